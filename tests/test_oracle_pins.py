@@ -1,0 +1,347 @@
+"""Pins of the fp64 oracle against closed forms, invariants and library routines.
+
+Each test is chosen so that a plausible slip in the oracle (a dropped term, a
+wrong sign or index, a transposed rotation, a wrong rounding mode) fails it.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+
+
+# --------------------------------------------------------------- rounding
+def _f16_nearest_even(x: float) -> float:
+    """RNE to binary16 by exact rational comparison of the two neighbours."""
+    h = np.float16(x)                      # a candidate; check it against its neighbours
+    cands = {float(h), float(np.nextafter(h, np.float16(np.inf))), float(np.nextafter(h, np.float16(-np.inf)))}
+    cands = {c for c in cands if np.isfinite(c)}
+    fx = Fraction(x)
+    best = sorted(cands, key=lambda c: (abs(Fraction(c) - fx),
+                                         int(np.array([c], np.float16).view(np.uint16)[0]) & 1))
+    return best[0]
+
+
+def test_meta_round_is_rne_from_double():
+    rng = np.random.default_rng(5)
+    xs = list(rng.standard_normal(400) * 10.0 ** rng.integers(-6, 4, 400))
+    # exact ties between fp16 neighbours (odd multiples of half a spacing) and
+    # values a hair off a tie, which a double->float->half path can misround
+    for e in (-3, 0, 2):
+        sp = 2.0 ** (e - 10)
+        for k in (1, 3, 5, 1023):
+            t = 2.0 ** e + (k + 0.5) * sp
+            xs += [t, np.nextafter(t, 0), np.nextafter(t, 10)]
+    xs += [2.0 ** -24 * 1.5, 2.0 ** -25, 65504.0, 6.1e-5]
+    got = O.meta_round(np.array(xs), "f16")
+    for x, g in zip(xs, got):
+        assert g == _f16_nearest_even(float(x)), x
+
+
+# ------------------------------------------------------------- least squares
+def test_alpha_is_least_squares_minimiser():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((50, 64))
+    ref = rng.standard_normal((50, 64)) * 3
+    a = O.ls_alpha(x, ref)
+    # normal equation: the residual is orthogonal to the reference
+    resid = x - a[:, None] * ref
+    dots = np.abs(np.sum(resid * ref, -1)) / (np.linalg.norm(x, axis=-1) * np.linalg.norm(ref, axis=-1))
+    assert dots.max() < 1e-12
+    # and any other scale is worse
+    err = lambda s: np.sum((x - s[:, None] * ref) ** 2, -1)
+    for eps in (1e-3, -1e-3, 0.1):
+        assert np.all(err(a + eps) > err(a))
+    # against a least-squares library solve, column by column
+    for i in range(5):
+        sol = np.linalg.lstsq(ref[i][:, None], x[i], rcond=None)[0][0]
+        assert abs(sol - a[i]) < 1e-13 * max(1, abs(sol))
+
+
+def test_alpha_special_cases():
+    ref = np.array([1.0, -2.0, 0.5, 4.0])
+    assert O.ls_alpha(0.75 * ref, ref) == 0.75
+    assert O.ls_alpha(ref, ref) == 1.0
+    assert O.ls_alpha(ref, np.zeros(4)) == 0.0
+
+
+def test_alpha_recovers_generator_scale():
+    w = W.get(1).replace(batch=2, context=64, heads=4)
+    st = W.structure(w)
+    kv = W.kv_numpy(w, batch=2, context=64, st=st)          # [L][2][B][N+1][H][D]
+    ref = kv[-1]
+    for l in range(w.loops - 1):
+        a = O.ls_alpha(kv[l], ref)                           # [2][B][N+1][H]
+        true = st["alpha"][l][:, None, None, :]
+        bound = 6 * st["sigma"][l] / np.linalg.norm(ref, axis=-1) + 2.0 ** -7
+        assert np.all(np.abs(a - true) <= bound)
+
+
+# ------------------------------------------------------------------ rotation
+def test_generator_rotations_orthogonal():
+    for key in (0, 1, 3):
+        st = W.structure(W.get(key).replace(heads=2))
+        R = st["rot64"]
+        I = np.eye(R.shape[-1])
+        for h in range(R.shape[0]):
+            for kv in range(2):
+                assert np.abs(R[h, kv].T @ R[h, kv] - I).max() <= 1e-12
+                assert np.abs(R[h, kv] @ R[h, kv].T - I).max() <= 1e-12
+        R32 = st["rot32"].astype(np.float64)
+        assert np.abs(np.einsum("hkji,hkjl->hkil", R32, R32) - I).max() < 1e-6
+
+
+# ----------------------------------------------------------------- quantizer
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("meta", ["f16", "f32"])
+def test_quantizer_levels_and_error(bits, meta):
+    rng = np.random.default_rng(bits)
+    y = rng.standard_normal((300, 128)) * np.exp(rng.standard_normal((300, 1)))
+    G = 32
+    q = O.quantize(y, bits, G, meta)
+    qmax = (1 << bits) - 1
+    cg = q.codes.reshape(300, 4, G)
+    yg = y.reshape(300, 4, G)
+    # min maps to code 0 and max to the top code in every group
+    imin, imax = yg.argmin(-1), yg.argmax(-1)
+    assert np.all(np.take_along_axis(cg, imin[..., None], -1) == 0)
+    assert np.all(np.take_along_axis(cg, imax[..., None], -1) == qmax)
+    # every level is used across the tensor
+    assert set(np.unique(q.codes)) == set(range(qmax + 1))
+    # per-element error: half a step, plus the rounding of step and zero
+    deq = O.dequantize(q.codes, q.scale, q.zero, G)
+    dt = np.float16 if meta == "f16" else np.float32
+    ulp = lambda v: np.spacing(np.abs(v).astype(dt)).astype(np.float64)
+    bound = (q.scale / 2 + (1 << bits) * ulp(q.scale) + ulp(q.zero))
+    err = np.abs(y - deq).reshape(300, 4, G)
+    assert np.all(err <= bound[..., None] * (1 + 1e-12))
+    # codes are the nearest level to (y - z)/s
+    inner = (q.u >= 0) & (q.u <= qmax)
+    assert np.all(np.abs(q.u[inner] - q.codes[inner]) <= 0.5)
+
+
+def test_quantizer_round_half_even_and_degenerate():
+    # group [0, 1, 2, 3] * 1/3 scale: u values exactly 0..3
+    y = np.array([[0.0, 0.5, 1.5, 3.0]])
+    q = O.quantize(y, 2, 4, "f32")                       # step 1.0, zero 0
+    assert q.scale[0, 0] == 1.0 and list(q.codes[0]) == [0, 0, 2, 3]   # 0.5 -> 0, 1.5 -> 2 (ties to even)
+    q = O.quantize(np.full((1, 8), 2.5), 4, 8, "f16")
+    assert q.scale[0, 0] == 0 and q.zero[0, 0] == 2.5 and not q.codes.any()
+    assert np.all(O.dequantize(q.codes, q.scale, q.zero, 8) == 2.5)
+
+
+def test_quantizer_group_independence():
+    # groups must not mix: changing one group leaves the others' codes alone
+    rng = np.random.default_rng(3)
+    y = rng.standard_normal((1, 128))
+    q1 = O.quantize(y, 2, 32, "f16")
+    y2 = y.copy()
+    y2[0, 40:64] *= 100
+    q2 = O.quantize(y2, 2, 32, "f16")
+    np.testing.assert_array_equal(q1.codes[0, :32], q2.codes[0, :32])
+    np.testing.assert_array_equal(q1.codes[0, 64:], q2.codes[0, 64:])
+    assert not np.array_equal(q1.codes[0, 32:64], q2.codes[0, 32:64])
+
+
+# ------------------------------------------------------------------- encode
+def _small(key, **kw):
+    w = W.get(key).replace(**kw)
+    st = W.structure(w)
+    kv = W.kv_numpy(w, st=st)                                 # [L][2][B][N+1][H][D]
+    L, _, B, N1, H, D = kv.shape
+    kvt = kv.reshape(L, 2, B * N1, H, D)
+    return w, st, kvt
+
+
+@pytest.mark.parametrize("key,kw", [(0, {}), (1, dict(batch=1, context=40, heads=3)),
+                                    (3, dict(batch=1, context=20, heads=2))])
+def test_reconstruction_bound(key, kw):
+    w, st, kv = _small(key, **kw)
+    enc = O.encode(kv, st["rot32"], w.res_bits, w.group_size, w.meta_dtype)
+    xh = O.reconstruct(enc, st["rot32"])
+    G = w.group_size
+    D = w.head_dim
+    eref = np.abs(xh[-1] - kv[-1])
+    sref = np.repeat(enc.ref.scale, G, axis=-1)
+    assert np.all(eref <= sref / 2 * (1 + 1e-3) + 1e-2 * sref)
+    R = st["rot32"].astype(np.float64)
+    for l in range(w.loops - 1):
+        q = enc.res[l]
+        a = enc.alpha[l]
+        d = kv[l] - a[..., None] * kv[-1]
+        r = np.einsum("hkij,kthj->kthi", R, d)
+        deq = O.dequantize(q.codes, q.scale, q.zero, G)
+        e_r = np.abs(deq - r).max(-1)
+        bound = np.abs(a) * eref.max(-1) + np.sqrt(D) * e_r * (1 + 1e-6) + 1e-6 * np.abs(d).max(-1) * D
+        err = np.abs(xh[l] - kv[l]).max(-1)
+        assert np.all(err <= bound + 1e-12)
+        # residual range is far below the raw range (the point of the method)
+        assert np.median(np.repeat(q.scale, G, -1)) < 0.5 * np.median(sref)
+
+
+def test_reconstruction_detects_transposed_rotation():
+    w, st, kv = _small(1, batch=1, context=16, heads=2)
+    enc = O.encode(kv, st["rot32"], (4, 4, 4), w.group_size, w.meta_dtype)
+    a = enc.alpha[0][..., None]
+    d = kv[0] - a * kv[-1]                       # what the rotated residual encodes
+
+    def part(rot):                               # residual part of the reconstruction
+        xh = O.reconstruct(enc, rot)
+        return xh[0] - a * xh[-1]
+    rms = lambda e: np.sqrt(np.mean(e ** 2))
+    good = rms(part(st["rot32"]) - d)
+    bad = rms(part(np.swapaxes(st["rot32"], -1, -2)) - d)
+    assert bad > 4 * good
+
+
+def test_identical_loops_give_zero_point_residual():
+    w, st, kv = _small(1, batch=1, context=24, heads=2)
+    kv = kv.copy()
+    kv[0] = kv[-1]
+    enc = O.encode(kv, st["rot32"], w.res_bits, w.group_size, w.meta_dtype)
+    assert np.all(enc.alpha64[0] == 1.0) and np.all(enc.alpha[0] == 1.0)
+    q = enc.res[0]
+    assert not q.codes.any() and not q.scale.any() and not q.zero.any()
+    xh = O.reconstruct(enc, st["rot32"])
+    np.testing.assert_array_equal(xh[0], xh[-1])
+
+
+def test_residual_rounding_exact_in_float64():
+    # d = x - alpha*ref is exact for bf16 x/ref and fp16 alpha: equals an fma
+    w, st, kv = _small(1, batch=1, context=30, heads=2)
+    enc = O.encode(kv, st["rot32"], w.res_bits, w.group_size, w.meta_dtype)
+    a = enc.alpha[0][..., None]
+    d = kv[0] - a * kv[-1]
+    exact = [Fraction(float(x)) - Fraction(float(al)) * Fraction(float(r))
+             for x, al, r in zip(kv[0].ravel()[:500], np.broadcast_to(a, kv[0].shape).ravel()[:500], kv[-1].ravel()[:500])]
+    assert all(Fraction(float(v)) == e for v, e in zip(d.ravel()[:500], exact))
+
+
+# ------------------------------------------------------------------ packing
+@pytest.mark.parametrize("bits", [2, 4])
+def test_pack_unpack_exhaustive(bits):
+    allb = np.arange(256, dtype=np.uint8)[:, None]
+    c = O.unpack_codes(allb, bits)
+    assert c.shape == (256, 8 // bits) and c.max() == (1 << bits) - 1
+    np.testing.assert_array_equal(O.pack_codes(c, bits), allb)
+
+
+def test_pack_spec_vectors():
+    assert list(O.pack_codes(np.array([1, 2, 3, 4, 15, 0, 7, 8]), 4)) == [0x21, 0x43, 0x0F, 0x87]
+    assert list(O.pack_codes(np.array([1, 2, 3, 0, 3, 3, 3, 3]), 2)) == [0x39, 0xFF]
+
+
+# ---------------------------------------------------------- pool and paging
+def test_pool_roundtrip_and_gather():
+    w = W.get(3).replace(batch=2, context=37, heads=3)
+    st = W.structure(w)
+    kv = W.kv_numpy(w, st=st)                                 # [L][2][B][N+1][H][D]
+    L, _, B, N1, H, D = kv.shape
+    table, nblk = W.block_table(w, shuffled=True)
+    lay = O.PoolLayout(H, D, w.group_size, L, w.res_bits, w.meta_dtype, nblk)
+    assert all(lay.rec_bytes(l) % 16 == 0 for l in range(L))
+    pool = np.zeros(lay.pool_bytes, np.uint8)
+    pos = np.tile(np.arange(N1), (B, 1))
+    slots = W.slot_mapping(table, pos).reshape(-1)
+    kvt = kv.reshape(L, 2, B * N1, H, D)
+    enc = O.encode(kvt, st["rot32"], w.res_bits, w.group_size, w.meta_dtype)
+    O.write_tokens(pool, lay, enc, slots)
+    for b in range(B):
+        for h in range(H):
+            for l in range(L):
+                for k in range(2):
+                    c, s, z, a = O.gather_sequence(pool, lay, table[b], N1, h, l, k)
+                    q = enc.ref if l == L - 1 else enc.res[l]
+                    sl = slice(b * N1, (b + 1) * N1)
+                    np.testing.assert_array_equal(c, q.codes[k, sl, h])
+                    np.testing.assert_array_equal(s, q.scale[k, sl, h])
+                    np.testing.assert_array_equal(z, q.zero[k, sl, h])
+                    if l < L - 1:
+                        np.testing.assert_array_equal(a, enc.alpha[l][k, sl, h])
+            xh = O.reconstruct(enc, st["rot32"])
+            for l in range(L):
+                Kh, Vh = O.reconstruct_sequence(pool, lay, table[b], N1, h, l, st["rot32"][h])
+                np.testing.assert_allclose(Kh, xh[l, 0, b * N1:(b + 1) * N1, h], rtol=0, atol=1e-12)
+                np.testing.assert_allclose(Vh, xh[l, 1, b * N1:(b + 1) * N1, h], rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------- attention
+def test_attention_against_library_softmax():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(9)
+    for n in (1, 2, 7, 300):
+        q = rng.standard_normal(64)
+        K = rng.standard_normal((n, 64)) * 3
+        V = rng.standard_normal((n, 64))
+        tau = 0.125
+        o = O.attention(q, K, V, tau)
+        t = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q)[None, None, None], torch.from_numpy(K)[None, None],
+            torch.from_numpy(V)[None, None], scale=tau)[0, 0, 0].numpy()
+        np.testing.assert_allclose(o, t, rtol=1e-12, atol=1e-12)
+
+
+def test_attention_invariants():
+    rng = np.random.default_rng(2)
+    K = rng.standard_normal((50, 16))
+    V = rng.standard_normal((50, 16))
+    q = rng.standard_normal(16)
+    np.testing.assert_allclose(O.attention(np.zeros(16), K, V, 0.25), V.mean(0), rtol=0, atol=1e-14)
+    np.testing.assert_array_equal(O.attention(q, K[:1], V[:1], 0.25), V[0])
+    perm = rng.permutation(50)
+    np.testing.assert_allclose(O.attention(q, K[perm], V[perm], 0.25), O.attention(q, K, V, 0.25), atol=1e-14)
+    assert not O.attention(q, K[:0], V[:0], 0.25).any()
+    # tail token is just one more key
+    np.testing.assert_allclose(O.attention(q, K[:-1], V[:-1], 0.25, K[-1], V[-1]),
+                               O.attention(q, K, V, 0.25), atol=1e-14)
+    # two keys: p1 = sigmoid(score difference)
+    o = O.attention(q, K[:2], V[:2], 0.25)
+    p1 = 1 / (1 + np.exp(-0.25 * (K[1] - K[0]) @ q))
+    np.testing.assert_allclose(o, (1 - p1) * V[0] + p1 * V[1], atol=1e-14)
+
+
+def test_decode_attention_matches_dense_on_reconstruction():
+    # attention over the pool equals attention over the reconstruction of the
+    # same encoded tokens (pool indexing, paging and per-loop reconstruction)
+    w = W.get(1).replace(batch=2, context=33, heads=2)
+    st = W.structure(w)
+    kv = W.kv_numpy(w, st=st)
+    L, _, B, N1, H, D = kv.shape
+    N = N1 - 1
+    table, nblk = W.block_table(w, shuffled=True)
+    lay = O.PoolLayout(H, D, w.group_size, L, w.res_bits, w.meta_dtype, nblk)
+    pool = np.zeros(lay.pool_bytes, np.uint8)
+    slots = W.slot_mapping(table, np.tile(np.arange(N), (B, 1))).reshape(-1)
+    enc = O.encode(kv[:, :, :, :N].reshape(L, 2, B * N, H, D), st["rot32"], w.res_bits, w.group_size, w.meta_dtype)
+    O.write_tokens(pool, lay, enc, slots)
+    xh = O.reconstruct(enc, st["rot32"]).reshape(L, 2, B, N, H, D)
+    qs = W.queries_numpy(w)
+    tau = 1 / np.sqrt(D)
+    for l in range(L):
+        out = O.decode_attention(pool, lay, l, qs[l], st["rot32"], table, [N] * B, tau,
+                                 kv[l, 0, :, N], kv[l, 1, :, N])
+        for b in range(B):
+            for h in range(H):
+                ref = O.attention(qs[l, b, h], xh[l, 0, b, :, h], xh[l, 1, b, :, h], tau,
+                                  kv[l, 0, b, N, h], kv[l, 1, b, N, h])
+                np.testing.assert_allclose(out[b, h], ref, rtol=0, atol=1e-12)
+
+
+def test_bf16_baseline_attention():
+    w = W.get(1).replace(batch=2, context=21, heads=2)
+    kv = W.kv_numpy(w)
+    L, _, B, N1, H, D = kv.shape
+    N = N1 - 1
+    table, nblk = W.block_table(w)
+    kc = np.zeros((nblk, H, 16, D))
+    vc = np.zeros((nblk, H, 16, D))
+    slots = W.slot_mapping(table, np.tile(np.arange(N), (B, 1))).reshape(-1)
+    O.bf16_pool_write(kc, vc, kv[1, :, :, :N].reshape(2, B * N, H, D), slots)
+    q = W.queries_numpy(w)[1]
+    out = O.bf16_decode_attention(kc, vc, q, table, [N] * B, 0.1)
+    for b in range(B):
+        for h in range(H):
+            ref = O.attention(q[b, h], kv[1, 0, b, :N, h], kv[1, 1, b, :N, h], 0.1)
+            np.testing.assert_allclose(out[b, h], ref, atol=1e-13)

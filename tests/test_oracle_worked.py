@@ -1,0 +1,94 @@
+"""Pins of the oracle against hand-derived worked examples (tests/golden/)."""
+import numpy as np
+
+import oracle as O
+
+
+def _f16(bits):
+    return float(np.array([bits], dtype=np.uint16).view(np.float16)[0])
+
+
+def _example(g, which):
+    x_ref = np.array(g["x_ref"], dtype=np.float64)
+    x0 = np.array(g["x_0"], dtype=np.float64)
+    # [L][2][T][H][D] with K = V, one token, one head
+    kv = np.stack([x0, x_ref])[:, None, None, None, :].repeat(2, axis=1)
+    R = np.array(g[which + "_rot"], dtype=np.float64).reshape(4, 4)
+    rot32 = np.stack([R, R])[None].astype(np.float32)          # [H=1][2][4][4]
+    return kv, rot32
+
+
+def test_worked_example_encode(golden):
+    g = golden("worked_example_d4.txt")
+    for which in ("A", "B"):
+        kv, rot32 = _example(g, which)
+        enc = O.encode(kv, rot32, res_bits=(2,), G=4, meta="f16")
+        for k in range(2):
+            assert list(enc.ref.codes[k, 0, 0]) == g["ref_codes"]
+            assert enc.ref.scale[k, 0, 0, 0] == _f16(g["ref_scale_f16"])
+            assert enc.ref.zero[k, 0, 0, 0] == _f16(g["ref_zero_f16"])
+            assert enc.alpha[0][k, 0, 0] == _f16(g["alpha_f16"])
+            assert list(enc.res[0].codes[k, 0, 0]) == g[which + "_res_codes"]
+            assert enc.res[0].scale[k, 0, 0, 0] == _f16(g[which + "_res_scale_f16"])
+            assert enc.res[0].zero[k, 0, 0, 0] == _f16(g[which + "_res_zero_f16"])
+        assert list(O.pack_codes(enc.ref.codes[0, 0, 0], 4)) == g["ref_packed"]
+        p = O.pack_codes(enc.res[0].codes[0, 0, 0], 2)
+        assert list(p) == [g[which + "_res_packed"]]
+
+
+def test_worked_example_reconstruct(golden):
+    g = golden("worked_example_d4.txt")
+    for which in ("A", "B"):
+        kv, rot32 = _example(g, which)
+        enc = O.encode(kv, rot32, res_bits=(2,), G=4, meta="f16")
+        xh = O.reconstruct(enc, rot32)
+        np.testing.assert_array_equal(xh[1, 0, 0, 0], g["x_ref_hat"])
+        np.testing.assert_allclose(xh[0, 0, 0, 0], g[which + "_x0_hat"], rtol=0, atol=1e-15)
+
+
+def test_worked_layout_bytes(golden):
+    g = golden("worked_example_d4.txt")
+    lg = golden("worked_layout_d4.txt")
+    kv, rot32 = _example(g, "A")
+    enc = O.encode(kv, rot32, res_bits=(2,), G=4, meta="f16")
+    lay = O.PoolLayout(H=1, D=4, G=4, L=2, res_bits=(2,), meta="f16", num_blocks=1, block_size=2)
+    assert lay.slab_bytes == lg["slab_bytes"][0]
+    assert [lay.rec_bytes(0), lay.rec_bytes(1)] == lg["rec_bytes"]
+    pool = np.zeros(lay.pool_bytes, dtype=np.uint8)
+    O.write_tokens(pool, lay, enc, np.array([1]))
+    want = bytes.fromhex("".join(h[0] for h in lg["hex"]))
+    assert pool.tobytes() == want
+    # and reading it back returns the encoded values
+    c, s, z, a = O.read_pages(pool, lay, [0], 0, 0, 1)
+    assert list(c[0, 1]) == g["A_res_codes"] and a[0, 1] == 2.0
+    assert s[0, 1, 0] == _f16(g["A_res_scale_f16"]) and z[0, 1, 0] == _f16(g["A_res_zero_f16"])
+
+
+def test_worked_attention_closed_form():
+    # scores 0, ln 2, ln 5 -> softmax 1/8, 2/8, 5/8 (tau = 1/sqrt(4) = 0.5, q = [2,0,0,0])
+    q = np.array([2.0, 0, 0, 0])
+    K = np.array([[0, 1, 2, 3], [np.log(2), -1, 0, 0], [np.log(5), 4, 4, 4]], dtype=np.float64)
+    V = np.array([[8.0, 0, 0, 1], [0, 8, 0, 1], [0, 0, 8, 1]])
+    o = O.attention(q, K[:2], V[:2], 0.5, tail_k=K[2], tail_v=V[2])
+    np.testing.assert_allclose(o, [1.0, 2.0, 5.0, 1.0], rtol=0, atol=1e-13)
+
+
+def test_worked_example_rounded_alpha(golden):
+    g = golden("worked_example_d4.txt")
+    x_ref = np.array(g["C_x_ref"], dtype=np.float64)
+    x0 = np.array(g["C_x_0"], dtype=np.float64)
+    kv = np.stack([x0, x_ref])[:, None, None, None, :].repeat(2, axis=1)
+    rot32 = np.stack([np.eye(4), np.eye(4)])[None].astype(np.float32)
+    enc = O.encode(kv, rot32, res_bits=(2,), G=4, meta="f16")
+    assert enc.alpha[0][0, 0, 0] == _f16(g["C_alpha_f16"])
+    assert list(enc.res[0].codes[0, 0, 0]) == g["C_res_codes"]
+    assert enc.res[0].scale[0, 0, 0, 0] == _f16(g["C_res_scale_f16"])
+    assert enc.res[0].zero[0, 0, 0, 0] == _f16(g["C_res_zero_f16"])
+
+
+def test_worked_layout_offsets(golden):
+    lg = golden("worked_layout_d4.txt")
+    lay = O.PoolLayout(H=2, D=4, G=4, L=2, res_bits=(2,), meta="f16", num_blocks=3, block_size=2)
+    assert lay.pool_bytes == lg["pool_bytes"][0]
+    for blk, head, loop, kv, off in lg["offset"]:
+        assert lay.record_offset(blk, head, loop, kv) == off
