@@ -1,0 +1,368 @@
+"""Decode-step benchmark of ResidualQuant attention over a packed INT4/INT2 KV
+cache on one MI355X.
+
+One step of the looped model's decode for one layer at the long-context
+Ouro-like shape (batch 16, context 32768, 16 heads x 128, 4 loops, 16-token
+pages): four decode-attention calls, one per loop, each over that loop's
+packed cache plus the current token's uncompressed K/V, then the deferred
+compression of the current token (all loops) into the paged pool. Inputs are
+seeded synthetic draws resident in HBM before timing starts.
+
+Prints one JSON line (see the keys below). Also measured: the in-library bf16
+baseline step at the same batch (append the token's 4 loops of bf16 K/V + 4
+decode calls), the dominant kernel's bandwidth against the 8 TB/s HBM peak
+(HIP events around each residual-loop split-K launch), and the fp64 oracle
+timed on the host on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+DEFAULT_WORKLOAD = "ouro_h16_d128_l4_b16_n32768"
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvent_t pairs for timing kernels launched inside the library."""
+
+    def __init__(self):
+        self.h = ctypes.CDLL("libamdhip64.so")
+        self.h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.h.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        e = ctypes.c_void_p()
+        assert self.h.hipEventCreate(ctypes.byref(e)) == 0
+        return e
+
+    def ms(self, a, b):
+        assert self.h.hipEventSynchronize(b) == 0
+        f = ctypes.c_float()
+        assert self.h.hipEventElapsedTime(ctypes.byref(f), a, b) == 0
+        return float(f.value)
+
+    def destroy(self, e):
+        self.h.hipEventDestroy(e)
+
+
+def token_head_bytes(w, loop):
+    """Algorithmic packed bytes one decode call reads per token-head: the
+    reference loop's record share (INT4 codes + scale/zero) for K and V, plus
+    for a residual loop its own record share (codes + scale/zero + alpha)."""
+    D, G = w.head_dim, w.group_size
+    m = 2 if w.meta_dtype == "f16" else 4
+    ref = 2 * (D * 4 // 8 + 2 * m * (D // G))
+    if loop == w.loops - 1:
+        return ref
+    b = w.res_bits[loop]
+    return ref + 2 * (D * b // 8 + 2 * m * (D // G) + m)
+
+
+def setup_rq(w, dev, split_pages):
+    import torch
+    import looped_transformer_decode_rq_amd as R
+    import workloads as W
+    B, N, H, D, L = w.batch, w.context, w.heads, w.head_dim, w.loops
+    st = W.structure(w, 0)
+    table, nblk = W.block_table(w)
+    lay = R.make_layout(H, D, w.group_size, L, w.res_bits, nblk, w.meta_dtype, w.kv_dtype)
+    pool = torch.zeros(R.pool_bytes(lay), dtype=torch.uint8, device=dev)
+    rot = torch.from_numpy(st["rot32"]).to(dev)
+    kvdt = torch.bfloat16 if w.kv_dtype == "bf16" else torch.float32
+    cur = torch.empty((L, 2, B, H, D), dtype=kvdt, device=dev)      # current token, all loops
+    pos = np.arange(N)
+    for b in range(B):
+        kvb = W.kv_torch(w, 0, b, st, dev)
+        slots = torch.from_numpy(table[b, pos // 16].astype(np.int64) * 16 + pos % 16).to(dev)
+        R.encode_pack(lay, pool, kvb[:, :, :N].contiguous(), rot, slots)
+        cur[:, :, b] = kvb[:, :, N]
+        del kvb
+    torch.cuda.synchronize()
+    q = W.queries_torch(w, 0, dev)
+    s = dict(lay=lay, pool=pool, rot=rot, cur=cur, q=q, table=table, nblk=nblk, st=st,
+             d_table=torch.from_numpy(table).to(dev), d_seq=torch.full((B,), N, dtype=torch.int32, device=dev),
+             slots_new=torch.from_numpy(table[:, N // 16].astype(np.int64) * 16 + N % 16).to(dev))
+    s["qs"] = [q[l:l + 1].contiguous() for l in range(L)]
+    s["tk"] = [cur[l, 0][None].contiguous() for l in range(L)]
+    s["tv"] = [cur[l, 1][None].contiguous() for l in range(L)]
+    s["kv_new"] = cur                                                  # [L][2][T=B][H][D]
+    s["out"] = torch.empty((L, 1, B, H, D), device=dev)
+    s["ws"] = torch.empty(R.decode_workspace_bytes(lay, 1, B, table.shape[1], split_pages), dtype=torch.uint8,
+                          device=dev)
+    return s
+
+
+def rq_step(w, s, split_pages, events=None):
+    import looped_transformer_decode_rq_amd as R
+    tau = 1.0 / np.sqrt(w.head_dim)
+    for l in range(w.loops):
+        ev = None if events is None else events[l]
+        R.decode_attention(s["lay"], s["pool"], [l], s["qs"][l], s["rot"], s["d_table"], s["d_seq"],
+                           s["tk"][l], s["tv"][l], tau, s["out"][l], s["ws"], split_pages=split_pages, events=ev)
+    R.encode_pack(s["lay"], s["pool"], s["kv_new"], s["rot"], s["slots_new"])
+
+
+def setup_bf16(w, dev, rq, split_pages):
+    import torch
+    import looped_transformer_decode_rq_amd as R
+    import workloads as W
+    B, N, H, D, L = w.batch, w.context, w.heads, w.head_dim, w.loops
+    table, nblk = rq["table"], rq["nblk"]
+    kc = [torch.zeros((nblk, H, 16, D), dtype=torch.bfloat16, device=dev) for _ in range(L)]
+    vc = [torch.zeros_like(kc[0]) for _ in range(L)]
+    pos = np.arange(N)
+    for b in range(B):
+        kvb = W.kv_torch(w, 0, b, rq["st"], dev)
+        slots = torch.from_numpy(table[b, pos // 16].astype(np.int64) * 16 + pos % 16).to(dev)
+        for l in range(L):
+            R.bf16_write(kc[l], vc[l], kvb[l, :, :N].contiguous(), slots)
+        del kvb
+    torch.cuda.synchronize()
+    return dict(kc=kc, vc=vc, out=torch.empty((B, H, D), device=dev),
+                ws=torch.empty(R.bf16_workspace_bytes(H, D, B, table.shape[1], split_pages), dtype=torch.uint8,
+                               device=dev),
+                q=[rq["q"][l].contiguous() for l in range(L)],
+                new=[rq["cur"][l].contiguous() for l in range(L)])
+
+
+def bf16_step(w, rq, b, split_pages, events=None):
+    import looped_transformer_decode_rq_amd as R
+    tau = 1.0 / np.sqrt(w.head_dim)
+    for l in range(w.loops):
+        R.bf16_decode_attention(b["kc"][l], b["vc"][l], b["q"][l], rq["d_table"], rq["d_seq"],
+                                rq["tk"][l][0], rq["tv"][l][0], tau, b["out"], b["ws"], split_pages=split_pages,
+                                events=None if events is None else events[l])
+        R.bf16_write(b["kc"][l], b["vc"][l], b["new"][l], rq["slots_new"])
+
+
+def timed(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn(None)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        fn(k)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def cpu_baseline(w, rq, budget_s=12.0):
+    """The fp64 oracle on a bounded sample: decode attention of one (sequence,
+    head) unit per loop, repeated over units until the budget is spent, plus
+    the oracle encode of one step's new tokens; extrapolated to a full step."""
+    import torch
+    import oracle as O
+    import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+    B, N, H, D, L = w.batch, w.context, w.heads, w.head_dim, w.loops
+    st = rq["st"]
+    tau = 1.0 / np.sqrt(D)
+    times = {l: [] for l in range(L)}
+    units = 0
+    t_start = time.perf_counter()
+    npages = -(-N // 16)
+    pos = np.arange(N)
+    mini = O.PoolLayout(1, D, w.group_size, L, w.res_bits, w.meta_dtype, npages)
+    q_h = rq["q"].float().cpu().numpy().astype(np.float64)
+    cur = rq["cur"].float().cpu().numpy().astype(np.float64)
+    for h in range(H):
+        kvb = W.kv_torch(w, 0, 0, st, torch.device("cuda:0"))
+        kvh = kvb[:, :, :N, h:h + 1].float().cpu().numpy().astype(np.float64)
+        del kvb
+        enc = O.encode(kvh, st["rot32"][h:h + 1], w.res_bits, w.group_size, w.meta_dtype)
+        opool = np.zeros(mini.pool_bytes, np.uint8)
+        O.write_tokens(opool, mini, enc, pos)
+        for l in range(L):
+            t0 = time.perf_counter()
+            O.decode_attention(opool, mini, l, q_h[l, 0:1, h:h + 1], st["rot32"][h:h + 1],
+                               np.arange(npages)[None], [N], tau, cur[l, 0, 0:1, h:h + 1], cur[l, 1, 0:1, h:h + 1])
+            times[l].append(time.perf_counter() - t0)
+        units += 1
+        if time.perf_counter() - t_start > budget_s:
+            break
+    t0 = time.perf_counter()
+    enc_new = O.encode(cur[:, :, :, :, :], st["rot32"], w.res_bits, w.group_size, w.meta_dtype)
+    t_enc = time.perf_counter() - t0
+    step = sum(B * H * float(np.mean(times[l])) for l in range(L)) + t_enc
+    del enc_new
+    return {"value": B / step, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{units} (sequence, head) units x {L} loops of fp64 decode attention over {N} packed tokens "
+                      f"+ fp64 encode of one step's {B} new tokens; step time extrapolated to {B}x{H} units "
+                      f"({step:.1f} s per step)"}
+
+
+def traffic_from_profiles(kernel_src_hash):
+    """HBM bytes per launch of the dominant kernel from committed rocprofv3
+    counter summaries, valid only for the kernel source they were taken on."""
+    p = os.path.join(ROOT, "profiles", "split_kernel_traffic.json")
+    try:
+        d = json.load(open(p))
+    except Exception:
+        return None
+    if d.get("kernel_src_sha256") != kernel_src_hash:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def kernel_src_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("rq_decode.hip", "rq_device.h", "rq_internal.h"):
+        h.update(open(os.path.join(ROOT, "looped_transformer_decode_rq_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--split-pages", type=int, default=0)
+    ap.add_argument("--no-bf16", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this path has no multi-GPU mode (asked for --gpus {args.gpus}); "
+              "run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import looped_transformer_decode_rq_amd as R
+    import workloads as W
+    R.lib()
+    w = W.get(args.workload)
+    dev = torch.device("cuda:0")
+    B, N, H, D, L = w.batch, w.context, w.heads, w.head_dim, w.loops
+    table_w = -(-(N + 1) // 16)
+    args.split_pages = args.split_pages or _auto_split(B * H, table_w)
+    log(f"workload {w.name}: setting up packed cache (split {args.split_pages} pages)")
+    rq = setup_rq(w, dev, args.split_pages)
+    ev = HipEvents()
+    res_loops = [l for l in range(L) if l != L - 1]
+    pairs = {(k, l): (ev.create(), ev.create()) for k in range(args.steps) for l in range(L)}
+
+    def rq_fn(k):
+        rq_step(w, rq, args.split_pages, None if k is None else [pairs[(k, l)] for l in range(L)])
+
+    log("timing packed step")
+    t_rq = timed(rq_fn, args.steps, args.warmup)
+    split_ms = {l: [] for l in range(L)}
+    for (k, l), (a, b) in pairs.items():
+        split_ms[l].append(ev.ms(a, b))
+        ev.destroy(a)
+        ev.destroy(b)
+    res_ms = float(np.mean([m for l in res_loops for m in split_ms[l]]))
+    ref_ms = float(np.mean(split_ms[L - 1]))
+    nsplit = -(-rq["table"].shape[1] // args.split_pages)
+    qp = 64 + 4 * D
+    res_bytes = (token_head_bytes(w, 0) * B * H * N + B * H * qp + B * N // 16 * 4
+                 + B * H * nsplit * (2 + 2 * D) * 4)
+    ref_bytes = (token_head_bytes(w, L - 1) * B * H * N + B * H * qp + B * N // 16 * 4
+                 + B * H * nsplit * (2 + 2 * D) * 4)
+    achieved = res_bytes / (res_ms * 1e-3) / 1e9
+    # whole step: packed reads of the 4 calls + q/out/tails + rotations + encode traffic
+    kvsz = 2 if w.kv_dtype == "bf16" else 4
+    step_bytes = sum(token_head_bytes(w, l) * B * H * N for l in range(L))
+    step_bytes += L * B * H * D * (kvsz * 3 + 4) + L * H * 2 * D * D * 4
+    ref_share = token_head_bytes(w, L - 1)
+    stored = ref_share + sum(token_head_bytes(w, l) - ref_share for l in range(L - 1))
+    step_bytes += L * 2 * B * H * D * kvsz + B * H * stored          # encode: read new K/V, write records
+    step_gbs = step_bytes / t_rq / 1e9
+    log(f"packed step {t_rq * 1e3:.3f} ms; residual split kernel {res_ms:.3f} ms ({achieved:.0f} GB/s)")
+
+    bf16 = None
+    if not args.no_bf16:
+        log("setting up bf16 baseline cache")
+        b16 = setup_bf16(w, dev, rq, args.split_pages)
+        bpairs = {k: [(ev.create(), ev.create()) for _ in range(L)] for k in range(args.steps)}
+
+        def bf_fn(k):
+            bf16_step(w, rq, b16, args.split_pages, None if k is None else bpairs[k])
+
+        t_bf = timed(bf_fn, args.steps, args.warmup)
+        bms = []
+        for k, evs in bpairs.items():
+            for a, b in evs:
+                bms.append(ev.ms(a, b))
+                ev.destroy(a)
+                ev.destroy(b)
+        bf_kernel_bytes = 2 * D * 2 * B * H * N
+        bf16 = {"tokens_per_s": B / t_bf, "ms_per_step": t_bf * 1e3,
+                "split_kernel_ms": float(np.mean(bms)),
+                "split_kernel_gbs": bf_kernel_bytes / (float(np.mean(bms)) * 1e-3) / 1e9,
+                "speedup_packed_vs_bf16": t_bf / t_rq}
+        log(f"bf16 step {t_bf * 1e3:.3f} ms; packed/bf16 speedup {t_bf / t_rq:.2f}x")
+        del b16
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu:
+        log("timing the fp64 oracle on the host")
+        cpu = cpu_baseline(w, rq)
+
+    traffic = traffic_from_profiles(kernel_src_hash())
+    line = {
+        "metric": "decode-attn tokens/s + effective HBM GB/s (% of peak) on packed INT4/INT2 KV",
+        "value": B / t_rq,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": t_rq * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4/int2 codes x fp32 (bf16 inputs, fp16 metadata)",
+        "data": "synthetic (seeded generator; no model weights)",
+        "config": {"workload": w.name, "layers": 1, "batch": B, "context": N, "heads": H, "head_dim": D,
+                   "loops": L, "group_size": w.group_size, "res_bits": list(w.res_bits), "block_size": 16,
+                   "split_pages": args.split_pages,
+                   "step": "4 per-loop decode calls (each + bf16 current token) + encode of 16 new tokens"},
+        "effective_hbm_gbs": step_gbs,
+        "effective_hbm_frac": step_gbs / HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": f"rq_split_kernel<{D},{w.res_bits[0]},{w.meta_dtype == 'f32'}> (residual loop)",
+                     "kernel_ms": res_ms, "bytes_per_launch": res_bytes},
+        "ref_loop_kernel": {"ms": ref_ms, "gbs": ref_bytes / (ref_ms * 1e-3) / 1e9, "bytes_per_launch": ref_bytes},
+        "bf16_baseline": bf16,
+        "cpu_baseline": cpu,
+        "context_from_pages": {"kv_storage_reduction": "80.7% (theoretical, mixed precision)",
+                               "fixed_batch_decode_speedup": "up to 2.73x on RTX 5090",
+                               "peak_throughput_speedup": "up to 4.15x on RTX 5090"},
+    }
+    print(json.dumps(line), flush=True)
+
+
+def _auto_split(units, max_blocks):
+    """Pages per split: the smallest power of two keeping ~16K waves per call."""
+    sp = 1
+    while sp < 1024 and units * (-(-max_blocks // sp)) > 16384:
+        sp *= 2
+    return sp
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,218 @@
+/*
+ * rq.h -- ResidualQuant decode attention over a looped Transformer's packed,
+ * paged INT4/INT2 KV cache, on AMD Instinct MI355X (gfx950).
+ *
+ * The method (ResidualQuant: KV Cache Quantization for Looped Transformers
+ * with 2-Bit Residuals, arXiv 2610.10381, abstract; rit.work summary of the
+ * paper, section on how each pass's KV cache is restored):
+ *   - the final loop's K/V of every token is the reference, stored as
+ *     asymmetric INT4;
+ *   - every other loop l stores r_l = R * (x_l - alpha_l * x_ref), with alpha_l
+ *     the least-squares scale of the reference and R an orthogonal rotation
+ *     per (layer, head, K|V) shared by all tokens and loops, quantized to INT2
+ *     (INT4 under loop-wise mixed precision) with a tunable step and offset;
+ *   - a token is compressed once, after its final loop; until then its K/V of
+ *     every loop stay uncompressed (bf16) and are attended as a "tail";
+ *   - attention rebuilds the reference and the loop's own residual on chip and
+ *     never writes decompressed K/V back to memory.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller. The library
+ *     never allocates, frees or synchronizes; scratch comes from the caller's
+ *     workspace. Work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *     stream) and the call returns at once.
+ *   - On any validation failure the call returns a negative rq_status before
+ *     touching memory or enqueuing work. RQ_ERR_HIP reports a failed launch.
+ *   - Tensor layouts are C-contiguous (row-major) in the stated index order.
+ *   - Device-side indices (block ids, slots, sequence lengths) are clamped
+ *     against the pool and table sizes: an out-of-range id never causes an
+ *     out-of-bounds access; the affected output is unspecified.
+ *
+ * Packed pool format (one layer). The pool is num_blocks * num_heads slabs,
+ * slab (block, head) at byte (block * num_heads + head) * slab_bytes. A slab
+ * holds, for l = 0 .. num_loops-1 in order and inside each loop K (kv=0) then
+ * V (kv=1), one page record of block_size tokens:
+ *     codes   block_size * head_dim * b_l / 8 bytes, token-major; channel i of
+ *             a token sits in byte i*b_l/8 at bit (i mod (8/b_l)) * b_l
+ *     meta    block_size * (head_dim/group_size) pairs (scale, zero), token-
+ *             major, meta dtype
+ *     alpha   block_size values, meta dtype (only for loops l < num_loops-1)
+ *     pad     zero bytes up to a multiple of 16
+ * with b_l = loop_bits[l] for l < num_loops-1 and 4 for the reference loop.
+ * A value decodes as code * scale + zero (per group of group_size channels);
+ * loop l reconstructs as alpha * ref_hat + R^T * residual_hat.
+ */
+#ifndef RQ_H
+#define RQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t rq_status;
+#define RQ_OK               0
+#define RQ_ERR_NULL        -1   /* a required pointer is NULL */
+#define RQ_ERR_SHAPE       -2   /* inconsistent or out-of-range sizes / indices */
+#define RQ_ERR_UNSUPPORTED -3   /* a valid request this build has no kernel for */
+#define RQ_ERR_WORKSPACE   -4   /* workspace smaller than the *_workspace_bytes figure */
+#define RQ_ERR_HIP         -5   /* a HIP runtime call or kernel launch failed */
+
+#define RQ_DTYPE_BF16 0
+#define RQ_DTYPE_F16  1
+#define RQ_DTYPE_F32  2
+
+#define RQ_MAX_LOOPS 16
+
+/* Geometry of one layer's packed cache.
+ *   num_heads   H >= 1
+ *   head_dim    D in {64, 96, 128}
+ *   group_size  G: channels per (scale, zero) group, contiguous inside a head.
+ *               Supported: D=128: 32, 64, 128; D=96: 96; D=64: 16, 32, 64.
+ *   num_loops   L in [1, 16]; loop L-1 is the reference
+ *   block_size  tokens per page; must be 16
+ *   num_blocks  pages in the pool (>= 1)
+ *   meta_dtype  RQ_DTYPE_F16 or RQ_DTYPE_F32 (scale, zero, alpha)
+ *   kv_dtype    RQ_DTYPE_BF16 or RQ_DTYPE_F32 (new K/V, queries, tails)
+ *   loop_bits   loop_bits[l] in {2, 4} for l < L-1 (the residual of loop l);
+ *               entries from L-1 on are ignored (the reference is INT4). */
+typedef struct rq_layout {
+    int32_t num_heads;
+    int32_t head_dim;
+    int32_t group_size;
+    int32_t num_loops;
+    int32_t block_size;
+    int32_t num_blocks;
+    int32_t meta_dtype;
+    int32_t kv_dtype;
+    uint8_t loop_bits[RQ_MAX_LOOPS];
+} rq_layout;
+
+/* Tuning and instrumentation for the decode calls (all fields optional).
+ *   split_pages       pages per split-K partial; 0 = chosen by the library
+ *   event_main_begin  hipEvent_t recorded on `stream` just before the split-K
+ *                     kernel of each loop, or NULL
+ *   event_main_end    hipEvent_t recorded just after it, or NULL
+ * With several loops in one call the events bracket the last loop's kernel. */
+typedef struct rq_decode_opts {
+    int32_t split_pages;
+    int32_t reserved;
+    void   *event_main_begin;
+    void   *event_main_end;
+} rq_decode_opts;
+
+/* Human-readable name of a status code (static string). */
+const char *rq_status_string(rq_status status);
+
+/* RQ_OK if `layout` is one the kernels support, else the reason. */
+rq_status rq_layout_check(const rq_layout *layout);
+
+/* Bytes of the packed pool of one layer (0 if the layout is invalid). */
+size_t rq_pool_bytes(const rq_layout *layout);
+
+/* Bytes of one page record of loop `loop` (0 if invalid). */
+size_t rq_record_bytes(const rq_layout *layout, int32_t loop);
+
+/* Byte offset of the record (block, head, loop, kv) inside the pool, or -1. */
+int64_t rq_record_offset(const rq_layout *layout, int32_t block, int32_t head,
+                         int32_t loop, int32_t kv);
+
+/* Compress new tokens once their final loop has run and write them into the
+ * paged pool (rit.work summary: deferred write after the final pass).
+ *   pool          packed pool of this layer (rq_pool_bytes), written in place
+ *   kv_new        [L][2][T][H][D] kv_dtype: every loop's K (kv=0) and V (kv=1)
+ *                 of the T tokens
+ *   rot           [H][2][D][D] fp32: R of (head, K|V), row-major, r = R * d.
+ *                 May be NULL when L == 1.
+ *   slot_mapping  [T] int64: page * 16 + offset of each token; a negative slot
+ *                 skips the token
+ * Per token-head and K|V, in float64: alpha = <x_l,x_ref>/<x_ref,x_ref>
+ * (0 if x_ref = 0) rounded to meta_dtype; d = x_l - alpha*x_ref;
+ * r = R*d; per group: scale = (max-min)/(2^b-1) and zero = min rounded to
+ * meta_dtype (nearest even); code = clamp(rint((y-zero)/scale), 0, 2^b-1),
+ * all codes 0 when scale == 0. Tokens of one call must have distinct slots. */
+rq_status rq_encode_pack(const rq_layout *layout, void *pool, const void *kv_new,
+                         const float *rot, const int64_t *slot_mapping,
+                         int32_t num_tokens, void *stream);
+
+/* Workspace bytes for rq_decode_attention(_ex) with these sizes. */
+size_t rq_decode_workspace_bytes(const rq_layout *layout, int32_t n_loops,
+                                 int32_t batch, int32_t max_blocks_per_seq,
+                                 int32_t split_pages);
+
+/* Decode attention of one query per (loop, sequence, head) over the packed
+ * cache plus the uncompressed current token (arXiv 2610.10381 abstract: the
+ * reduced KV traffic is what speeds up decoding; rit.work summary: reference
+ * and residual are rebuilt in small blocks inside attention).
+ *   loops        HOST array [n_loops] of loop indices in [0, L); each entry i
+ *                attends loop loops[i]'s cache with query q[i]
+ *   q            [n_loops][B][H][D] kv_dtype
+ *   rot          [H][2][D][D] fp32 (as in rq_encode_pack); may be NULL if every
+ *                requested loop is the reference
+ *   block_table  [B][max_blocks_per_seq] int32 physical page ids
+ *   seq_lens     [B] int32 cached tokens per sequence
+ *   tail_k/v     [n_loops][B][H][D] kv_dtype, the current token's K/V of that
+ *                loop, or both NULL
+ *   out          [n_loops][B][H][D] fp32
+ * out = softmax(tau * q.k_hat) v_hat over the seq_len cached tokens and the
+ * tail, with k_hat, v_hat the reconstruction above (tau = softmax_scale). A
+ * sequence with no cached token and no tail gets a zero row. */
+rq_status rq_decode_attention(const rq_layout *layout, const void *pool,
+                              const int32_t *loops, int32_t n_loops, const void *q,
+                              const float *rot, const int32_t *block_table,
+                              const int32_t *seq_lens, int32_t batch,
+                              int32_t max_blocks_per_seq, const void *tail_k,
+                              const void *tail_v, float softmax_scale, float *out,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+rq_status rq_decode_attention_ex(const rq_layout *layout, const void *pool,
+                                 const int32_t *loops, int32_t n_loops, const void *q,
+                                 const float *rot, const int32_t *block_table,
+                                 const int32_t *seq_lens, int32_t batch,
+                                 int32_t max_blocks_per_seq, const void *tail_k,
+                                 const void *tail_v, float softmax_scale, float *out,
+                                 void *workspace, size_t workspace_bytes,
+                                 const rq_decode_opts *opts, void *stream);
+
+/* Uncompressed baseline (for the speed ratio): the same decode attention over
+ * a paged bf16 cache of ONE loop.
+ *   k_cache, v_cache  [num_blocks][H][16][D] bf16
+ *   q, tail_k, tail_v [B][H][D] bf16 (tails may both be NULL); out [B][H][D] fp32
+ * head_dim in {64, 96, 128}; block_size must be 16. */
+size_t rq_bf16_workspace_bytes(int32_t num_heads, int32_t head_dim, int32_t batch,
+                               int32_t max_blocks_per_seq, int32_t split_pages);
+
+rq_status rq_bf16_decode_attention(int32_t num_heads, int32_t head_dim,
+                                   int32_t block_size, int32_t num_blocks,
+                                   const void *k_cache, const void *v_cache,
+                                   const void *q, const int32_t *block_table,
+                                   const int32_t *seq_lens, int32_t batch,
+                                   int32_t max_blocks_per_seq, const void *tail_k,
+                                   const void *tail_v, float softmax_scale, float *out,
+                                   void *workspace, size_t workspace_bytes, void *stream);
+
+rq_status rq_bf16_decode_attention_ex(int32_t num_heads, int32_t head_dim,
+                                      int32_t block_size, int32_t num_blocks,
+                                      const void *k_cache, const void *v_cache,
+                                      const void *q, const int32_t *block_table,
+                                      const int32_t *seq_lens, int32_t batch,
+                                      int32_t max_blocks_per_seq, const void *tail_k,
+                                      const void *tail_v, float softmax_scale, float *out,
+                                      void *workspace, size_t workspace_bytes,
+                                      const rq_decode_opts *opts, void *stream);
+
+/* Append tokens to a paged bf16 cache (the baseline's write step).
+ *   kv_new [2][T][H][D] bf16 (K then V of one loop); slot_mapping [T] int64,
+ *   negative = skip. */
+rq_status rq_bf16_write(int32_t num_heads, int32_t head_dim, int32_t block_size,
+                        int32_t num_blocks, void *k_cache, void *v_cache,
+                        const void *kv_new, const int64_t *slot_mapping,
+                        int32_t num_tokens, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RQ_H */

@@ -1,0 +1,251 @@
+"""ctypes binding of librq.so (argument marshalling only).
+
+Tensors are passed as raw device pointers (``tensor.data_ptr()``); the stream is
+torch's current HIP stream unless one is given. Shapes and dtypes are checked
+here only as far as needed to hand the library consistent sizes; the library
+validates again and returns a status, which is turned into ``RqError``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_float, c_int32, c_int64, c_size_t, c_uint8, c_void_p
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(HERE, "librq.so")
+
+RQ_DTYPE_BF16, RQ_DTYPE_F16, RQ_DTYPE_F32 = 0, 1, 2
+RQ_MAX_LOOPS = 16
+
+EXPORTED = [
+    "rq_status_string", "rq_layout_check", "rq_pool_bytes", "rq_record_bytes", "rq_record_offset",
+    "rq_encode_pack", "rq_decode_workspace_bytes", "rq_decode_attention", "rq_decode_attention_ex",
+    "rq_bf16_workspace_bytes", "rq_bf16_decode_attention", "rq_bf16_decode_attention_ex", "rq_bf16_write",
+]
+
+
+class RqError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn}: {status_string(status)} ({status})")
+
+
+class RqLayout(ctypes.Structure):
+    _fields_ = [("num_heads", c_int32), ("head_dim", c_int32), ("group_size", c_int32),
+                ("num_loops", c_int32), ("block_size", c_int32), ("num_blocks", c_int32),
+                ("meta_dtype", c_int32), ("kv_dtype", c_int32), ("loop_bits", c_uint8 * RQ_MAX_LOOPS)]
+
+
+class RqDecodeOpts(ctypes.Structure):
+    _fields_ = [("split_pages", c_int32), ("reserved", c_int32),
+                ("event_main_begin", c_void_p), ("event_main_end", c_void_p)]
+
+
+_LIB = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built (no fallback)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(library_path):
+            raise RuntimeError(f"librq.so not found at {library_path}; build it with "
+                               "python -m looped_transformer_decode_rq_amd.build")
+        L = ctypes.CDLL(library_path)
+        P = c_void_p
+        sig = {
+            "rq_status_string": (ctypes.c_char_p, [c_int32]),
+            "rq_layout_check": (c_int32, [POINTER(RqLayout)]),
+            "rq_pool_bytes": (c_size_t, [POINTER(RqLayout)]),
+            "rq_record_bytes": (c_size_t, [POINTER(RqLayout), c_int32]),
+            "rq_record_offset": (c_int64, [POINTER(RqLayout), c_int32, c_int32, c_int32, c_int32]),
+            "rq_encode_pack": (c_int32, [POINTER(RqLayout), P, P, P, P, c_int32, P]),
+            "rq_decode_workspace_bytes": (c_size_t, [POINTER(RqLayout), c_int32, c_int32, c_int32, c_int32]),
+            "rq_decode_attention": (c_int32, [POINTER(RqLayout), P, P, c_int32, P, P, P, P, c_int32, c_int32,
+                                              P, P, c_float, P, P, c_size_t, P]),
+            "rq_decode_attention_ex": (c_int32, [POINTER(RqLayout), P, P, c_int32, P, P, P, P, c_int32, c_int32,
+                                                 P, P, c_float, P, P, c_size_t, POINTER(RqDecodeOpts), P]),
+            "rq_bf16_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32]),
+            "rq_bf16_decode_attention": (c_int32, [c_int32, c_int32, c_int32, c_int32, P, P, P, P, P, c_int32,
+                                                   c_int32, P, P, c_float, P, P, c_size_t, P]),
+            "rq_bf16_decode_attention_ex": (c_int32, [c_int32, c_int32, c_int32, c_int32, P, P, P, P, P, c_int32,
+                                                      c_int32, P, P, c_float, P, P, c_size_t,
+                                                      POINTER(RqDecodeOpts), P]),
+            "rq_bf16_write": (c_int32, [c_int32, c_int32, c_int32, c_int32, P, P, P, P, c_int32, P]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _LIB = L
+    return _LIB
+
+
+def status_string(status: int) -> str:
+    return lib().rq_status_string(int(status)).decode()
+
+
+def _check(fn, status):
+    if status != 0:
+        raise RqError(fn, status)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not getattr(t, "is_cuda", False):
+        raise ValueError("librq takes device tensors only (got a host tensor)")
+    return c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is not None:
+        return c_void_p(int(stream))
+    import torch
+    return c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+_DT = {"bf16": RQ_DTYPE_BF16, "f16": RQ_DTYPE_F16, "f32": RQ_DTYPE_F32}
+
+
+def make_layout(num_heads, head_dim, group_size, num_loops, res_bits, num_blocks,
+                meta_dtype="f16", kv_dtype="bf16", block_size=16) -> RqLayout:
+    lay = RqLayout()
+    lay.num_heads, lay.head_dim, lay.group_size = num_heads, head_dim, group_size
+    lay.num_loops, lay.block_size, lay.num_blocks = num_loops, block_size, num_blocks
+    lay.meta_dtype = _DT[meta_dtype] if isinstance(meta_dtype, str) else meta_dtype
+    lay.kv_dtype = _DT[kv_dtype] if isinstance(kv_dtype, str) else kv_dtype
+    for i, b in enumerate(res_bits):
+        lay.loop_bits[i] = int(b)
+    return lay
+
+
+def layout_check(layout) -> int:
+    return lib().rq_layout_check(ctypes.byref(layout))
+
+
+def pool_bytes(layout) -> int:
+    return lib().rq_pool_bytes(ctypes.byref(layout))
+
+
+def record_bytes(layout, loop) -> int:
+    return lib().rq_record_bytes(ctypes.byref(layout), loop)
+
+
+def record_offset(layout, block, head, loop, kv) -> int:
+    return lib().rq_record_offset(ctypes.byref(layout), block, head, loop, kv)
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def _kv_bytes(layout):
+    return 4 if layout.kv_dtype == RQ_DTYPE_F32 else 2
+
+
+def _check_rot(layout, rot):
+    H, D = layout.num_heads, layout.head_dim
+    _need(tuple(rot.shape) == (H, 2, D, D) and rot.element_size() == 4 and rot.is_contiguous(),
+          f"rot must be contiguous fp32 [{H}][2][{D}][{D}]")
+
+
+def encode_pack(layout, pool, kv_new, rot, slot_mapping, stream=None):
+    """rq_encode_pack: kv_new [L][2][T][H][D], rot [H][2][D][D] fp32, slots [T] int64."""
+    T = 0 if kv_new is None else int(kv_new.shape[2])
+    if T:
+        L, H, D = layout.num_loops, layout.num_heads, layout.head_dim
+        _need(_nbytes(pool) >= pool_bytes(layout) > 0, "pool smaller than rq_pool_bytes(layout)")
+        _need(tuple(kv_new.shape) == (L, 2, T, H, D) and kv_new.element_size() == _kv_bytes(layout)
+              and kv_new.is_contiguous(), f"kv_new must be contiguous [{L}][2][T][{H}][{D}] in kv_dtype")
+        _need(slot_mapping.numel() == T and slot_mapping.element_size() == 8, "slot_mapping must be int64 [T]")
+        if L > 1:
+            _check_rot(layout, rot)
+    _check("rq_encode_pack", lib().rq_encode_pack(
+        ctypes.byref(layout), _ptr(pool), _ptr(kv_new), _ptr(rot), _ptr(slot_mapping), T, _stream(stream)))
+
+
+def decode_workspace_bytes(layout, n_loops, batch, max_blocks_per_seq, split_pages=0) -> int:
+    return lib().rq_decode_workspace_bytes(ctypes.byref(layout), n_loops, batch, max_blocks_per_seq, split_pages)
+
+
+def _opts(split_pages, events):
+    o = RqDecodeOpts()
+    o.split_pages = int(split_pages or 0)
+    if events is not None:
+        o.event_main_begin, o.event_main_end = events
+    return o
+
+
+def decode_attention(layout, pool, loops, q, rot, block_table, seq_lens, tail_k, tail_v,
+                     softmax_scale, out, workspace, split_pages=0, events=None, stream=None):
+    """rq_decode_attention_ex; loops is a host sequence of loop indices."""
+    n = len(loops)
+    arr = (c_int32 * max(n, 1))(*[int(x) for x in loops])
+    B, mb = int(block_table.shape[0]), int(block_table.shape[1])
+    ws_bytes = workspace.numel() * workspace.element_size()
+    H, D = layout.num_heads, layout.head_dim
+    _need(_nbytes(pool) >= pool_bytes(layout) > 0, "pool smaller than rq_pool_bytes(layout)")
+    shp = (n, B, H, D)
+    _need(tuple(q.shape) == shp and q.element_size() == _kv_bytes(layout) and q.is_contiguous(),
+          f"q must be contiguous {shp} in kv_dtype")
+    _need(tuple(out.shape) == shp and out.element_size() == 4 and out.is_contiguous(), f"out must be fp32 {shp}")
+    _need(block_table.element_size() == 4 and block_table.is_contiguous(), "block_table must be int32 [B][M]")
+    _need(seq_lens.numel() == B and seq_lens.element_size() == 4, "seq_lens must be int32 [B]")
+    _need((tail_k is None) == (tail_v is None), "tail_k and tail_v go together")
+    for t in (tail_k, tail_v):
+        if t is not None:
+            _need(tuple(t.shape) == shp and t.element_size() == _kv_bytes(layout) and t.is_contiguous(),
+                  f"tails must be contiguous {shp} in kv_dtype")
+    if any(int(l) != layout.num_loops - 1 for l in loops):
+        _check_rot(layout, rot)
+    o = _opts(split_pages, events)
+    _check("rq_decode_attention", lib().rq_decode_attention_ex(
+        ctypes.byref(layout), _ptr(pool), arr, n, _ptr(q), _ptr(rot), _ptr(block_table), _ptr(seq_lens),
+        B, mb, _ptr(tail_k), _ptr(tail_v), float(softmax_scale), _ptr(out), _ptr(workspace), ws_bytes,
+        ctypes.byref(o), _stream(stream)))
+
+
+def bf16_workspace_bytes(num_heads, head_dim, batch, max_blocks_per_seq, split_pages=0) -> int:
+    return lib().rq_bf16_workspace_bytes(num_heads, head_dim, batch, max_blocks_per_seq, split_pages)
+
+
+def bf16_decode_attention(k_cache, v_cache, q, block_table, seq_lens, tail_k, tail_v, softmax_scale, out,
+                          workspace, split_pages=0, events=None, stream=None):
+    nblk, H, bs, D = (int(x) for x in k_cache.shape)
+    B, mb = int(block_table.shape[0]), int(block_table.shape[1])
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _need(tuple(v_cache.shape) == tuple(k_cache.shape) and k_cache.element_size() == 2
+          and v_cache.element_size() == 2 and k_cache.is_contiguous() and v_cache.is_contiguous(),
+          "k_cache/v_cache must be contiguous bf16 [num_blocks][H][16][D]")
+    shp = (B, H, D)
+    _need(tuple(q.shape) == shp and q.element_size() == 2 and q.is_contiguous(), f"q must be bf16 {shp}")
+    _need(tuple(out.shape) == shp and out.element_size() == 4 and out.is_contiguous(), f"out must be fp32 {shp}")
+    _need(block_table.element_size() == 4 and block_table.is_contiguous(), "block_table must be int32 [B][M]")
+    _need(seq_lens.numel() == B and seq_lens.element_size() == 4, "seq_lens must be int32 [B]")
+    _need((tail_k is None) == (tail_v is None), "tail_k and tail_v go together")
+    for t in (tail_k, tail_v):
+        if t is not None:
+            _need(tuple(t.shape) == shp and t.element_size() == 2 and t.is_contiguous(), f"tails must be bf16 {shp}")
+    o = _opts(split_pages, events)
+    _check("rq_bf16_decode_attention", lib().rq_bf16_decode_attention_ex(
+        H, D, bs, nblk, _ptr(k_cache), _ptr(v_cache), _ptr(q), _ptr(block_table), _ptr(seq_lens), B, mb,
+        _ptr(tail_k), _ptr(tail_v), float(softmax_scale), _ptr(out), _ptr(workspace), ws_bytes,
+        ctypes.byref(o), _stream(stream)))
+
+
+def bf16_write(k_cache, v_cache, kv_new, slot_mapping, stream=None):
+    nblk, H, bs, D = (int(x) for x in k_cache.shape)
+    T = int(kv_new.shape[1])
+    _need(tuple(kv_new.shape) == (2, T, H, D) and kv_new.element_size() == 2 and kv_new.is_contiguous(),
+          f"kv_new must be contiguous bf16 [2][T][{H}][{D}]")
+    _need(tuple(v_cache.shape) == tuple(k_cache.shape), "k_cache/v_cache shapes differ")
+    _need(slot_mapping.numel() == T and slot_mapping.element_size() == 8, "slot_mapping must be int64 [T]")
+    _check("rq_bf16_write", lib().rq_bf16_write(
+        H, D, bs, nblk, _ptr(k_cache), _ptr(v_cache), _ptr(kv_new), _ptr(slot_mapping),
+        int(kv_new.shape[1]), _stream(stream)))

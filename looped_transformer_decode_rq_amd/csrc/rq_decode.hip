@@ -1,0 +1,619 @@
+// Decode attention over the packed, paged ResidualQuant cache.
+//
+// Reconstruction of loop l (ResidualQuant, arXiv 2610.10381 abstract; rit.work
+// summary, section on how each pass is restored): x_hat = alpha*ref_hat +
+// R^T res_hat, ref_hat = c*s + z (INT4), res_hat = c*s + z (INT2/INT4).
+// Attention never materializes x_hat (the summary: reference and differences
+// are rebuilt in small blocks inside attention, nothing decompressed is written
+// back). It uses two exact identities of that formula:
+//   q . x_hat = alpha*(q . ref_hat) + (R q) . res_hat
+//   sum_t p_t x_hat_t = sum_t p_t alpha_t ref_hat_t + R^T sum_t p_t res_hat_t
+// so the query is rotated once, V is accumulated in the rotated space, and
+// R_V^T is applied once per output row.
+//
+// Three kernels per request:
+//   rq_qprep     per (loop call, head, 16 sequences): q' = R_K q on the f32
+//                matrix cores; q and q' are turned into 16-bit fixed point split
+//                into four signed 4-bit limbs laid out for v_dot8_i32_i4.
+//   rq_split     per (split of pages, head, sequence) one wave: walks the
+//                block table, loads each page's packed codes and metadata with
+//                wide coalesced loads, scores tokens with integer dot products
+//                of codes x query limbs (exact integer sums), runs the online
+//                softmax, accumulates V in registers and writes a partial
+//                (m, l, acc_ref[D], acc_res[D]).
+//   rq_combine   per (head, loop call, 16 sequences): log-sum-exp merge of the
+//                partials and the uncompressed tail token, then
+//                out = acc_ref/l + R_V^T (acc_res/l) on the f32 matrix cores.
+#include "rq_device.h"
+#include "rq_internal.h"
+
+namespace rq {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr float kRescaleThresh = 8.0f;   // log2 units: rescale when a score beats m by 2^8
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kQmaxFixed = 30583;        // 7 * (1 + 16 + 256 + 4096): range of 4 balanced base-16 digits
+
+template <int D> struct Lanes {
+    static constexpr int LPT = (D == 96) ? 2 : 4;   // lanes per token
+    static constexpr int CPL = D / LPT;             // channels per lane
+    static constexpr int TPW = 64 / LPT;            // tokens per wave step
+    static constexpr int PPI = TPW / 16;            // pages per wave step
+    static constexpr int NDW = CPL / 8;             // limb dwords per lane per limb
+};
+
+// ---------------------------------------------------------------- qprep
+struct QPrepArgs {
+    const void *q;          // [n][B][H][D]
+    const float *rot;       // [H][2][D][D]
+    uint8_t *qpack;         // [n][B][H][qpack_bytes]
+    int B, H;
+    int rb[RQ_MAX_LOOPS];   // residual bits of call i, 0 = reference loop
+};
+
+// Channel covered by nibble n of limb dword (q4, k) in the order the split
+// kernel consumes codes: INT4 words hold 8 consecutive channels; an INT2 word
+// (16 channels) is consumed as its even then its odd channels.
+template <int D>
+__device__ __forceinline__ int limb_channel(int q4, int k, int n, int rb) {
+    constexpr int CPL = Lanes<D>::CPL;
+    if (rb == 2) return q4 * CPL + 16 * (k >> 1) + 2 * n + (k & 1);
+    return q4 * CPL + 8 * k + n;
+}
+
+template <int D, bool KV_F32>
+__global__ __launch_bounds__(256) void rq_qprep_kernel(QPrepArgs a) {
+    using Ln = Lanes<D>;
+    constexpr int QS = D + 1;
+    __shared__ float Q[16 * QS];
+    __shared__ float QR[16 * QS];
+    __shared__ int QI[kWaves][2][D];
+    __shared__ int8_t DG[kWaves][2][4][D];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int h = blockIdx.x, i = blockIdx.y, tile = blockIdx.z;
+    const int rb = a.rb[i];
+    const int B = a.B, H = a.H;
+
+    for (int e = threadIdx.x; e < 16 * D; e += 256) {
+        const int r = e / D, c = e % D;
+        const int b = tile * 16 + r;
+        Q[r * QS + c] = (b < B) ? load_kv<KV_F32>(a.q, (((int64_t)i * B + b) * H + h) * D + c) : 0.0f;
+    }
+    __syncthreads();
+    if (rb != 0) {
+        // q' = R_K q for the 16 rows: [16 x D] x R_K^T. v_mfma_f32_16x16x4f32:
+        // lane l supplies A[l%16][k0 + l/16], B[k0 + l/16][l%16] and receives
+        // D[4*(l/16)+v][l%16].
+        const float *RK = a.rot + ((int64_t)h * 2 + 0) * D * D;
+        for (int nt = wave; nt < D / 16; nt += kWaves) {
+            floatx4 c = {0.f, 0.f, 0.f, 0.f};
+            const int n = nt * 16 + (lane & 15);
+            for (int kk = 0; kk < D / 4; ++kk) {
+                const int k = 4 * kk + (lane >> 4);
+                c = __builtin_amdgcn_mfma_f32_16x16x4f32(Q[(lane & 15) * QS + k], RK[(int64_t)n * D + k], c, 0, 0, 0);
+            }
+            for (int v = 0; v < 4; ++v) QR[(4 * (lane >> 4) + v) * QS + n] = c[v];
+        }
+    }
+    __syncthreads();
+
+    for (int j = 0; j < 4; ++j) {
+        const int r = wave + 4 * j;
+        const int b = tile * 16 + r;
+        const bool row_ok = b < B;
+        int S[2] = {0, 0};
+        for (int which = 0; which < 2; ++which) {
+            const float *src = which == 0 ? Q : QR;
+            const bool on = which == 0 || rb != 0;
+            float x0 = 0.f, x1 = 0.f;
+            if (on) {
+                x0 = (lane < D) ? src[r * QS + lane] : 0.f;
+                x1 = (lane + 64 < D) ? src[r * QS + lane + 64] : 0.f;
+            }
+            const float amax = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
+            int s = 0;
+            if (amax > 0.f) {
+                int e;
+                frexpf(amax, &e);
+                s = 14 - e;
+                if (ldexpf(amax, s + 1) <= (float)kQmaxFixed) s += 1;
+            }
+            S[which] = s;
+            for (int half = 0; half < 2; ++half) {
+                const int c = lane + 64 * half;
+                if (c >= D) continue;
+                const int qi = (int)rintf(ldexpf(half ? x1 : x0, s));
+                QI[wave][which][c] = qi;
+                int rem = qi;
+                for (int d = 0; d < 4; ++d) {
+                    const int dig = ((rem + 8) & 15) - 8;
+                    DG[wave][which][d][c] = (int8_t)dig;
+                    rem = (rem - dig) / 16;
+                }
+            }
+        }
+        __syncthreads();
+        if (row_ok) {
+            uint8_t *qp = a.qpack + (((int64_t)i * B + b) * H + h) * qpack_bytes(D);
+            // limb dwords: [q4][k][limb], nibble n = channel limb_channel(q4,k,n)
+            for (int which = 0; which < 2; ++which) {
+                if (which == 1 && rb == 0) break;
+                const int order = which == 0 ? 4 : rb;
+                for (int dw = lane; dw < D / 2; dw += 64) {
+                    const int limb = dw & 3;
+                    const int k = (dw >> 2) % Ln::NDW;
+                    const int q4 = dw / (4 * Ln::NDW);
+                    uint32_t word = 0;
+                    for (int nn = 0; nn < 8; ++nn) {
+                        const int ch = limb_channel<D>(q4, k, nn, order);
+                        word |= ((uint32_t)DG[wave][which][limb][ch] & 15u) << (4 * nn);
+                    }
+                    ((uint32_t *)(qp + 64 + which * 2 * D))[dw] = word;
+                }
+            }
+            if (lane < 2 * Ln::LPT) {
+                const int which = lane / Ln::LPT, q4 = lane % Ln::LPT;
+                int sum = 0;
+                if (which == 0 || rb != 0)
+                    for (int c = q4 * Ln::CPL; c < (q4 + 1) * Ln::CPL; ++c) sum += QI[wave][which][c];
+                ((int *)(qp + 16 + 16 * which))[q4] = sum;
+            }
+            if (lane == 0) {
+                ((float *)qp)[0] = ldexpf(1.0f, -S[0]);
+                ((float *)qp)[1] = rb ? ldexpf(1.0f, -S[1]) : 0.0f;
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// ------------------------------------------------------------------ split
+struct SplitArgs {
+    const uint8_t *pool;
+    int64_t slab;
+    int H, nblk, G;
+    int ref_off, ref_rec, ref_code_bytes;
+    int res_off, res_rec, res_code_bytes;
+    int meta_bytes;
+    const int32_t *block_table;
+    int max_blocks;
+    const int32_t *seq_lens;
+    const uint8_t *qpack;   // this call: [B][H][qpack_bytes]
+    float *partials;        // this call: [B][H][nsplit][2 + 2D]
+    int nsplit, split_pages;
+    float score_scale;      // softmax_scale * log2(e)
+};
+
+template <int NB>
+__device__ __forceinline__ void load_bytes(const uint8_t *p, uint32_t *out) {
+    // NB bytes, 4-byte granules; widest aligned vector loads the offsets allow
+    static_assert(NB % 4 == 0, "");
+    if constexpr (NB % 16 == 0) {
+#pragma unroll
+        for (int i = 0; i < NB / 16; ++i) {
+            uint4 v = ((const uint4 *)p)[i];
+            out[4 * i] = v.x; out[4 * i + 1] = v.y; out[4 * i + 2] = v.z; out[4 * i + 3] = v.w;
+        }
+    } else if constexpr (NB % 8 == 0) {
+#pragma unroll
+        for (int i = 0; i < NB / 8; ++i) {
+            uint2 v = ((const uint2 *)p)[i];
+            out[2 * i] = v.x; out[2 * i + 1] = v.y;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < NB / 4; ++i) out[i] = ((const uint32_t *)p)[i];
+    }
+}
+
+template <bool META_F32>
+__device__ __forceinline__ void load_sz(const uint8_t *p, float &s, float &z) {
+    if constexpr (META_F32) {
+        const float2 v = *(const float2 *)p;
+        s = v.x; z = v.y;
+    } else {
+        const uint32_t v = *(const uint32_t *)p;
+        s = f16_to_f32((uint16_t)(v & 0xFFFF));
+        z = f16_to_f32((uint16_t)(v >> 16));
+    }
+}
+
+template <bool META_F32>
+__device__ __forceinline__ float load_meta1(const uint8_t *p) {
+    if constexpr (META_F32) return *(const float *)p;
+    else return f16_to_f32(*(const uint16_t *)p);
+}
+
+__device__ __forceinline__ float ubyte(uint32_t x, int j) { return (float)((x >> (8 * j)) & 0xFFu); }
+
+// Integer dot of 4-bit codes (XOR 8 turns 0..15 into signed -8..7) with the
+// four query limbs; returns sum_i q_int_i * (c_i - 8).
+template <int NW>
+__device__ __forceinline__ int dot_int4(const uint32_t *codes, const uint32_t (*limb)[4]) {
+    int a0 = 0, a1 = 0, a2 = 0, a3 = 0;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+        const int w = (int)(codes[k] ^ 0x88888888u);
+        a0 = __builtin_amdgcn_sdot8((int)limb[k][0], w, a0, false);
+        a1 = __builtin_amdgcn_sdot8((int)limb[k][1], w, a1, false);
+        a2 = __builtin_amdgcn_sdot8((int)limb[k][2], w, a2, false);
+        a3 = __builtin_amdgcn_sdot8((int)limb[k][3], w, a3, false);
+    }
+    return a0 + 16 * a1 + 256 * a2 + 4096 * a3;
+}
+
+// Same for 2-bit codes: a word of 16 crumbs is split into its even and odd
+// channels, each widened to nibbles (values 0..3 need no offset).
+template <int NW>
+__device__ __forceinline__ int dot_int2(const uint32_t *codes, const uint32_t (*limb)[4]) {
+    int a0 = 0, a1 = 0, a2 = 0, a3 = 0;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+        const int ev = (int)(codes[k] & 0x33333333u);
+        const int od = (int)((codes[k] >> 2) & 0x33333333u);
+        a0 = __builtin_amdgcn_sdot8((int)limb[2 * k][0], ev, a0, false);
+        a1 = __builtin_amdgcn_sdot8((int)limb[2 * k][1], ev, a1, false);
+        a2 = __builtin_amdgcn_sdot8((int)limb[2 * k][2], ev, a2, false);
+        a3 = __builtin_amdgcn_sdot8((int)limb[2 * k][3], ev, a3, false);
+        a0 = __builtin_amdgcn_sdot8((int)limb[2 * k + 1][0], od, a0, false);
+        a1 = __builtin_amdgcn_sdot8((int)limb[2 * k + 1][1], od, a1, false);
+        a2 = __builtin_amdgcn_sdot8((int)limb[2 * k + 1][2], od, a2, false);
+        a3 = __builtin_amdgcn_sdot8((int)limb[2 * k + 1][3], od, a3, false);
+    }
+    return a0 + 16 * a1 + 256 * a2 + 4096 * a3;
+}
+
+// acc[8k + 2j (+1)] += w * code for INT4 words
+template <int NW>
+__device__ __forceinline__ void axpy_int4(float *acc, const uint32_t *codes, float w) {
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+        const uint32_t lo = codes[k] & 0x0F0F0F0Fu, hi = (codes[k] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            acc[8 * k + 2 * j] = fmaf(w, ubyte(lo, j), acc[8 * k + 2 * j]);
+            acc[8 * k + 2 * j + 1] = fmaf(w, ubyte(hi, j), acc[8 * k + 2 * j + 1]);
+        }
+    }
+}
+
+// acc[16k + 4j + i] += w * code for INT2 words
+template <int NW>
+__device__ __forceinline__ void axpy_int2(float *acc, const uint32_t *codes, float w) {
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t c = (codes[k] >> (2 * i)) & 0x03030303u;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[16 * k + 4 * j + i] = fmaf(w, ubyte(c, j), acc[16 * k + 4 * j + i]);
+        }
+    }
+}
+
+template <int D, int RB, bool META_F32>
+__global__ __launch_bounds__(256) void rq_split_kernel(SplitArgs a) {
+    using Ln = Lanes<D>;
+    constexpr int LPT = Ln::LPT, CPL = Ln::CPL, PPI = Ln::PPI;
+    constexpr int REF_NB = CPL / 2;                 // INT4 code bytes per lane
+    constexpr int RES_NB = RB ? CPL * RB / 8 : 4;   // residual code bytes per lane
+    constexpr int REF_NW = REF_NB / 4, RES_NW = RES_NB / 4;
+    constexpr int msz = META_F32 ? 4 : 2;
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int split = blockIdx.x * kWaves + wave;
+    const int h = blockIdx.y, b = blockIdx.z;
+    if (split >= a.nsplit) return;
+    const int H = a.H;
+    int seq = a.seq_lens[b];
+    seq = seq < 0 ? 0 : (seq > a.max_blocks * 16 ? a.max_blocks * 16 : seq);
+    const int npages = (seq + 15) >> 4;
+    const int p0 = split * a.split_pages;
+    const int p1 = min(npages, p0 + a.split_pages);
+    if (p0 >= p1) return;
+
+    const int tok_i = lane / LPT, q4 = lane % LPT;
+    const int page_in_step = tok_i >> 4, tok = tok_i & 15;
+    const int ng = D / a.G;
+    const int g = (q4 * CPL) / a.G;
+
+    // query record of (b, h)
+    const uint8_t *qp = a.qpack + ((int64_t)b * H + h) * qpack_bytes(D);
+    const float sc_ref = ((const float *)qp)[0];
+    const float sc_res = ((const float *)qp)[1];
+    const int qs_ref = ((const int *)(qp + 16))[q4];
+    const int qs_res = ((const int *)(qp + 32))[q4];
+    uint32_t lref[Ln::NDW][4], lres[Ln::NDW][4];
+    load_bytes<Ln::NDW * 16>(qp + 64 + q4 * Ln::NDW * 16, &lref[0][0]);
+    if constexpr (RB != 0) load_bytes<Ln::NDW * 16>(qp + 64 + 2 * D + q4 * Ln::NDW * 16, &lres[0][0]);
+
+    const int32_t *table = a.block_table + (int64_t)b * a.max_blocks;
+    const int ref_meta = a.ref_code_bytes + (tok * ng + g) * 2 * msz;
+    const int res_meta = a.res_code_bytes + (tok * ng + g) * 2 * msz;
+    const int res_alpha = a.res_code_bytes + a.meta_bytes + tok * msz;
+    const int ref_codes = tok * (D / 2) + q4 * REF_NB;
+    const int res_codes = tok * (D * RB / 8) + q4 * RES_NB;
+
+    float m = kNegInf, lsum = 0.f, zr = 0.f, zs = 0.f;
+    float accr[CPL], accs[RB ? CPL : 1];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) accr[i] = 0.f;
+#pragma unroll
+    for (int i = 0; i < (RB ? CPL : 1); ++i) accs[i] = 0.f;
+
+    for (int p = p0; p < p1; p += PPI) {
+        const int pp = p + page_in_step;
+        bool valid = pp < p1;
+        int64_t blk = valid ? (int64_t)table[pp] : 0;
+        if (blk < 0 || blk >= a.nblk) { blk = 0; valid = false; }
+        valid = valid && (pp * 16 + tok < seq);
+        const uint8_t *slab = a.pool + (blk * H + h) * a.slab;
+        const uint8_t *kr = slab + a.ref_off;
+        const uint8_t *vr = kr + a.ref_rec;
+
+        uint32_t ck[REF_NW], cv[REF_NW];
+        load_bytes<REF_NB>(kr + ref_codes, ck);
+        load_bytes<REF_NB>(vr + ref_codes, cv);
+        float skr, zkr, svr, zvr;
+        load_sz<META_F32>(kr + ref_meta, skr, zkr);
+        load_sz<META_F32>(vr + ref_meta, svr, zvr);
+
+        uint32_t rk[RES_NW], rv[RES_NW];
+        float sks = 0.f, zks = 0.f, svs = 0.f, zvs = 0.f, ak = 1.f, av = 1.f;
+        if constexpr (RB != 0) {
+            const uint8_t *ks = slab + a.res_off;
+            const uint8_t *vs = ks + a.res_rec;
+            load_bytes<RES_NB>(ks + res_codes, rk);
+            load_bytes<RES_NB>(vs + res_codes, rv);
+            load_sz<META_F32>(ks + res_meta, sks, zks);
+            load_sz<META_F32>(vs + res_meta, svs, zvs);
+            ak = load_meta1<META_F32>(ks + res_alpha);
+            av = load_meta1<META_F32>(vs + res_alpha);
+        }
+
+        // ---- score: q.x_hat = alpha*(s*sum q c + z*sum q) + (s_r*sum q' c_r + z_r*sum q')
+        const int dref = dot_int4<REF_NW>(ck, lref) + 8 * qs_ref;
+        float part = (skr * (float)dref + zkr * (float)qs_ref) * sc_ref;
+        if constexpr (RB != 0) {
+            int dres = (RB == 2) ? dot_int2<RES_NW>(rk, lres) : dot_int4<RES_NW>(rk, lres) + 8 * qs_res;
+            part = ak * part + (sks * (float)dres + zks * (float)qs_res) * sc_res;
+        }
+        float score = group_sum<LPT>(part) * a.score_scale;
+        score = valid ? score : kNegInf;
+
+        // ---- online softmax, rescaled only when a score beats m by 2^8
+        if (__any(score > m + kRescaleThresh)) {
+            const float mn = fmaxf(m, wave_max(score));
+            const float f = fast_exp2(m - mn);
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) accr[i] *= f;
+#pragma unroll
+            for (int i = 0; i < (RB ? CPL : 1); ++i) accs[i] *= f;
+            zr *= f; zs *= f; lsum *= f;
+            m = mn;
+        }
+        const float pr = fast_exp2(score - m);
+        lsum += pr;
+
+        // ---- V: acc_ref += p*alpha*s*c (+ p*alpha*z per group), acc_res in rotated space
+        const float pa = pr * av;
+        const float wr = valid ? pa * svr : 0.f;
+        zr += valid ? pa * zvr : 0.f;
+        axpy_int4<REF_NW>(accr, cv, wr);
+        if constexpr (RB != 0) {
+            const float ws = valid ? pr * svs : 0.f;
+            zs += valid ? pr * zvs : 0.f;
+            if constexpr (RB == 2) axpy_int2<RES_NW>(accs, rv, ws);
+            else axpy_int4<RES_NW>(accs, rv, ws);
+        }
+    }
+
+    // ---- fold the per-group zero terms, reduce over the wave's token slots
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) accr[i] += zr;
+    if constexpr (RB != 0) {
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) accs[i] += zs;
+    }
+#pragma unroll
+    for (int off = LPT; off < 64; off <<= 1) {
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) accr[i] += __shfl_xor(accr[i], off, 64);
+        if constexpr (RB != 0) {
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) accs[i] += __shfl_xor(accs[i], off, 64);
+        }
+        lsum += __shfl_xor(lsum, off, 64);
+    }
+    if (lane < LPT) {
+        float *out = a.partials + (((int64_t)b * H + h) * a.nsplit + split) * partial_floats(D);
+        if (lane == 0) { out[0] = m; out[1] = lsum; }
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) out[2 + q4 * CPL + i] = accr[i];
+        if constexpr (RB != 0) {
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) out[2 + D + q4 * CPL + i] = accs[i];
+        }
+    }
+}
+
+// --------------------------------------------------------------- combine
+struct CombineArgs {
+    const float *partials;  // [n][B][H][nsplit][2 + 2D]
+    int nsplit, split_pages, max_blocks;
+    const int32_t *seq_lens;
+    const void *q, *tail_k, *tail_v;   // [n][B][H][D]
+    const float *rot;
+    float *out;                        // [n][B][H][D]
+    int B, H;
+    float score_scale;
+    int is_res[RQ_MAX_LOOPS];
+};
+
+template <int D, bool KV_F32>
+__global__ __launch_bounds__(256) void rq_combine_kernel(CombineArgs a) {
+    constexpr int QS = D + 1;
+    __shared__ float A[16 * QS];
+    __shared__ float O[16 * QS];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int h = blockIdx.x, i = blockIdx.y, tile = blockIdx.z;
+    const int B = a.B, H = a.H;
+    const bool has_res = a.is_res[i] != 0;
+    constexpr int PF = 2 + 2 * D;
+
+    for (int j = 0; j < 4; ++j) {
+        const int r = wave + 4 * j;
+        const int b = tile * 16 + r;
+        float ar0 = 0.f, ar1 = 0.f, as0 = 0.f, as1 = 0.f;
+        const int c0 = lane, c1 = lane + 64;
+        if (b < B) {
+            int seq = a.seq_lens[b];
+            seq = seq < 0 ? 0 : (seq > a.max_blocks * 16 ? a.max_blocks * 16 : seq);
+            const int npages = (seq + 15) >> 4;
+            const int ns = (npages + a.split_pages - 1) / a.split_pages;
+            const int64_t row = ((int64_t)i * B + b) * H + h;
+            const float *P = a.partials + row * a.nsplit * PF;
+            float st = kNegInf;
+            if (a.tail_k) {
+                float d = 0.f;
+                if (c0 < D) d += load_kv<KV_F32>(a.q, row * D + c0) * load_kv<KV_F32>(a.tail_k, row * D + c0);
+                if (c1 < D) d += load_kv<KV_F32>(a.q, row * D + c1) * load_kv<KV_F32>(a.tail_k, row * D + c1);
+                st = wave_sum(d) * a.score_scale;
+            }
+            float mloc = kNegInf;
+            for (int s = lane; s < ns; s += 64) mloc = fmaxf(mloc, P[(int64_t)s * PF]);
+            const float M = fmaxf(wave_max(mloc), st);
+            if (M != kNegInf) {
+                float lloc = 0.f;
+                for (int s = lane; s < ns; s += 64) lloc += fast_exp2(P[(int64_t)s * PF] - M) * P[(int64_t)s * PF + 1];
+                float lsum = wave_sum(lloc);
+                for (int s = 0; s < ns; ++s) {
+                    const float *ps = P + (int64_t)s * PF;
+                    const float e = fast_exp2(ps[0] - M);
+                    if (c0 < D) ar0 = fmaf(e, ps[2 + c0], ar0);
+                    if (c1 < D) ar1 = fmaf(e, ps[2 + c1], ar1);
+                    if (has_res) {
+                        if (c0 < D) as0 = fmaf(e, ps[2 + D + c0], as0);
+                        if (c1 < D) as1 = fmaf(e, ps[2 + D + c1], as1);
+                    }
+                }
+                if (a.tail_k) {
+                    const float pt = fast_exp2(st - M);
+                    lsum += pt;
+                    if (c0 < D) ar0 = fmaf(pt, load_kv<KV_F32>(a.tail_v, row * D + c0), ar0);
+                    if (c1 < D) ar1 = fmaf(pt, load_kv<KV_F32>(a.tail_v, row * D + c1), ar1);
+                }
+                const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+                ar0 *= inv; ar1 *= inv; as0 *= inv; as1 *= inv;
+            }
+        }
+        if (c0 < D) { O[r * QS + c0] = ar0; A[r * QS + c0] = as0; }
+        if (c1 < D) { O[r * QS + c1] = ar1; A[r * QS + c1] = as1; }
+    }
+    __syncthreads();
+
+    if (has_res) {
+        // out = O + A * R_V  (row vector times R_V = R_V^T applied to the column)
+        const float *RV = a.rot + ((int64_t)h * 2 + 1) * D * D;
+        for (int nt = wave; nt < D / 16; nt += kWaves) {
+            floatx4 c = {0.f, 0.f, 0.f, 0.f};
+            const int n = nt * 16 + (lane & 15);
+            for (int kk = 0; kk < D / 4; ++kk) {
+                const int k = 4 * kk + (lane >> 4);
+                c = __builtin_amdgcn_mfma_f32_16x16x4f32(A[(lane & 15) * QS + k], RV[(int64_t)k * D + n], c, 0, 0, 0);
+            }
+            for (int v = 0; v < 4; ++v) {
+                const int r = 4 * (lane >> 4) + v;
+                const int b = tile * 16 + r;
+                if (b < B) a.out[(((int64_t)i * B + b) * H + h) * D + n] = c[v] + O[r * QS + n];
+            }
+        }
+    } else {
+        for (int e = threadIdx.x; e < 16 * D; e += 256) {
+            const int r = e / D, c = e % D;
+            const int b = tile * 16 + r;
+            if (b < B) a.out[(((int64_t)i * B + b) * H + h) * D + c] = O[r * QS + c];
+        }
+    }
+}
+
+// ------------------------------------------------------------- dispatch
+template <int D>
+hipError_t launch_split_d(const SplitArgs &s, int rb, bool mf, dim3 grid, hipStream_t st) {
+#define RQ_SPLIT(RB_, MF_) hipLaunchKernelGGL((rq_split_kernel<D, RB_, MF_>), grid, dim3(256), 0, st, s)
+    if (mf) {
+        if (rb == 0) RQ_SPLIT(0, true); else if (rb == 2) RQ_SPLIT(2, true); else RQ_SPLIT(4, true);
+    } else {
+        if (rb == 0) RQ_SPLIT(0, false); else if (rb == 2) RQ_SPLIT(2, false); else RQ_SPLIT(4, false);
+    }
+#undef RQ_SPLIT
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_decode_d(const DecodeCall &c) {
+    const Geom &g = *c.g;
+    const bool kvf = g.kvdt == RQ_DTYPE_F32, mf = g.meta == RQ_DTYPE_F32;
+    const int tiles = (c.B + 15) / 16;
+
+    QPrepArgs qa;
+    qa.q = c.q; qa.rot = c.rot; qa.qpack = c.qpack; qa.B = c.B; qa.H = g.H;
+    CombineArgs ca;
+    for (int i = 0; i < RQ_MAX_LOOPS; ++i) {
+        const bool res = i < c.n && c.loops[i] != g.L - 1;
+        qa.rb[i] = res ? g.bits[c.loops[i]] : 0;
+        ca.is_res[i] = res ? 1 : 0;
+    }
+    dim3 pgrid(g.H, c.n, tiles);
+    if (kvf) hipLaunchKernelGGL((rq_qprep_kernel<D, true>), pgrid, dim3(256), 0, c.stream, qa);
+    else hipLaunchKernelGGL((rq_qprep_kernel<D, false>), pgrid, dim3(256), 0, c.stream, qa);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+
+    const float score_scale = c.softmax_scale * kLog2e;
+    const int ref = g.L - 1;
+    for (int i = 0; i < c.n; ++i) {
+        const int l = c.loops[i];
+        SplitArgs s;
+        s.pool = c.pool; s.slab = g.slab; s.H = g.H; s.nblk = g.nblk; s.G = g.G;
+        s.ref_off = (int)g.loop_off[ref]; s.ref_rec = g.rec[ref]; s.ref_code_bytes = g.code_bytes[ref];
+        s.res_off = (int)g.loop_off[l]; s.res_rec = g.rec[l]; s.res_code_bytes = g.code_bytes[l];
+        s.meta_bytes = g.meta_bytes;
+        s.block_table = c.block_table; s.max_blocks = c.max_blocks; s.seq_lens = c.seq_lens;
+        s.qpack = c.qpack + (int64_t)i * c.B * g.H * qpack_bytes(D);
+        s.partials = c.partials + (int64_t)i * c.B * g.H * c.nsplit * partial_floats(D);
+        s.nsplit = c.nsplit; s.split_pages = c.split_pages;
+        s.score_scale = score_scale;
+        const int rb = (l == ref) ? 0 : g.bits[l];
+        dim3 grid((c.nsplit + kWaves - 1) / kWaves, g.H, c.B);
+        const bool last = i == c.n - 1;
+        if (last && c.ev_begin && hipEventRecord(c.ev_begin, c.stream) != hipSuccess) return hipErrorInvalidHandle;
+        err = launch_split_d<D>(s, rb, mf, grid, c.stream);
+        if (err != hipSuccess) return err;
+        if (last && c.ev_end && hipEventRecord(c.ev_end, c.stream) != hipSuccess) return hipErrorInvalidHandle;
+    }
+
+    ca.partials = c.partials; ca.nsplit = c.nsplit; ca.split_pages = c.split_pages;
+    ca.max_blocks = c.max_blocks; ca.seq_lens = c.seq_lens;
+    ca.q = c.q; ca.tail_k = c.tail_k; ca.tail_v = c.tail_v; ca.rot = c.rot; ca.out = c.out;
+    ca.B = c.B; ca.H = g.H; ca.score_scale = score_scale;
+    if (kvf) hipLaunchKernelGGL((rq_combine_kernel<D, true>), pgrid, dim3(256), 0, c.stream, ca);
+    else hipLaunchKernelGGL((rq_combine_kernel<D, false>), pgrid, dim3(256), 0, c.stream, ca);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeCall &c) {
+    if (c.B <= 0 || c.n <= 0) return hipSuccess;
+    switch (c.g->D) {
+        case 64: return launch_decode_d<64>(c);
+        case 96: return launch_decode_d<96>(c);
+        case 128: return launch_decode_d<128>(c);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace rq

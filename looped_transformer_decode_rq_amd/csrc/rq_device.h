@@ -1,0 +1,94 @@
+// Device helpers for the gfx950 kernels (wave64, CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rq {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef double doublex4 __attribute__((ext_vector_type(4)));
+
+constexpr float kNegInf = -__builtin_inff();
+
+// ------------------------------------------------------------ dtype access
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(((uint32_t)b) << 16);
+}
+__device__ __forceinline__ float f16_to_f32(uint16_t b) {
+    return (float)__builtin_bit_cast(_Float16, b);
+}
+
+// Element i of a [.. D] row whose dtype is bf16 (IS_F32 = false) or fp32.
+template <bool IS_F32>
+__device__ __forceinline__ float load_kv(const void *base, int64_t i) {
+    if constexpr (IS_F32) return ((const float *)base)[i];
+    else return bf16_to_f32(((const uint16_t *)base)[i]);
+}
+
+// Round a float64 to IEEE binary16, nearest-even, directly from the double
+// (a float64 -> float32 -> float16 chain can round twice).
+__device__ __forceinline__ uint16_t f64_to_f16_bits(double x) {
+    uint64_t u = (uint64_t)__double_as_longlong(x);
+    uint32_t sign = (uint32_t)(u >> 48) & 0x8000u;
+    int e = (int)((u >> 52) & 0x7FF);
+    uint64_t m = u & 0xFFFFFFFFFFFFFull;
+    if (e == 0x7FF) return (uint16_t)(sign | 0x7C00u | (m ? 0x200u : 0u));
+    if (e == 0) return (uint16_t)sign;                 // |x| < 2^-1022
+    int E = e - 1023;
+    if (E >= 16) return (uint16_t)(sign | 0x7C00u);    // |x| >= 2^16
+    uint64_t sig = m | (1ull << 52);
+    int Q = (E < -14 ? -14 : E) - 10;                  // exponent of one fp16 quantum
+    int shift = 52 + Q - E;                            // >= 42
+    if (shift >= 64) return (uint16_t)sign;            // below half the smallest subnormal
+    uint64_t k = sig >> shift;
+    uint64_t rem = sig & ((1ull << shift) - 1);
+    uint64_t half = 1ull << (shift - 1);
+    if (rem > half || (rem == half && (k & 1))) k++;
+    uint32_t bits = (E < -14) ? (uint32_t)k                               // subnormal (1024 = min normal)
+                              : (uint32_t)(((E + 15) << 10) + (int)(k - 1024));  // carry moves the exponent
+    if (bits >= 0x7C00u) bits = 0x7C00u;
+    return (uint16_t)(sign | bits);
+}
+
+__device__ __forceinline__ double f16_bits_to_f64(uint16_t b) {
+    return (double)__builtin_bit_cast(_Float16, b);
+}
+
+// --------------------------------------------------------- cross-lane ops
+// DPP quad permutations: xor 1 and xor 2 inside each group of 4 lanes.
+__device__ __forceinline__ float dpp_quad_xor1(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_quad_xor2(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
+
+// Sum over groups of LPT consecutive lanes (LPT in {1, 2, 4}); every lane of
+// the group gets the sum.
+template <int LPT>
+__device__ __forceinline__ float group_sum(float v) {
+    if constexpr (LPT >= 2) v += dpp_quad_xor1(v);
+    if constexpr (LPT >= 4) v += dpp_quad_xor2(v);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace rq

@@ -1,0 +1,89 @@
+// Internal declarations shared by the C-ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rq.h"
+
+namespace rq {
+
+// Derived geometry of one layer's packed pool (see the format in rq.h).
+struct Geom {
+    int H, D, G, L, bs, nblk, meta, kvdt, msz;
+    int bits[RQ_MAX_LOOPS];
+    int code_bytes[RQ_MAX_LOOPS];   // per record
+    int rec[RQ_MAX_LOOPS];          // record bytes (16-aligned)
+    int64_t loop_off[RQ_MAX_LOOPS + 1];
+    int meta_bytes;                 // per record: bs * (D/G) * 2 * msz
+    int64_t slab;                   // bytes per (block, head)
+};
+
+// Fills g from a layout; returns RQ_OK or the validation failure.
+rq_status make_geom(const rq_layout *layout, Geom *g);
+
+// Lanes per token used by the split-K kernels for a head dim.
+inline int lanes_per_token(int D) { return D == 96 ? 2 : 4; }
+
+// Per-(loop call, sequence, head) query record written by the query prep kernel.
+__host__ __device__ constexpr int qpack_bytes(int D) { return 64 + 4 * D; }
+__host__ __device__ constexpr int partial_floats(int D) { return 2 + 2 * D; }
+
+int auto_split_pages(int units, int max_blocks);
+
+// ------------------------------------------------------------------ launchers
+struct DecodeCall {
+    const Geom *g;
+    const uint8_t *pool;
+    int n;                        // loop calls in this request
+    int loops[RQ_MAX_LOOPS];
+    const void *q;
+    const float *rot;
+    const int32_t *block_table;
+    const int32_t *seq_lens;
+    int B, max_blocks;
+    const void *tail_k, *tail_v;
+    float softmax_scale;
+    float *out;
+    uint8_t *qpack;               // workspace: [n][B][H][qpack_bytes]
+    float *partials;              // workspace: [n][B][H][nsplit][partial_floats]
+    int split_pages, nsplit;
+    hipEvent_t ev_begin, ev_end;
+    hipStream_t stream;
+};
+
+hipError_t launch_decode(const DecodeCall &c);
+
+struct EncodeCall {
+    const Geom *g;
+    uint8_t *pool;
+    const void *kv_new;
+    const float *rot;
+    const int64_t *slots;
+    int T;
+    hipStream_t stream;
+};
+
+hipError_t launch_encode(const EncodeCall &c);
+
+struct Bf16Call {
+    int H, D, nblk;
+    const uint16_t *kc, *vc;
+    const uint16_t *q;
+    const int32_t *block_table, *seq_lens;
+    int B, max_blocks;
+    const uint16_t *tail_k, *tail_v;
+    float softmax_scale;
+    float *out;
+    float *partials;              // [B][H][nsplit][2 + D]
+    int split_pages, nsplit;
+    hipEvent_t ev_begin, ev_end;
+    hipStream_t stream;
+};
+
+hipError_t launch_bf16_decode(const Bf16Call &c);
+hipError_t launch_bf16_write(int H, int D, int nblk, uint16_t *kc, uint16_t *vc,
+                             const uint16_t *kv_new, const int64_t *slots, int T,
+                             hipStream_t stream);
+
+}  // namespace rq

@@ -83,6 +83,8 @@ class Quantized:
     zero: np.ndarray    # float64 [..., D/G]
     u: np.ndarray       # float64 [..., D]  pre-rounding code values (NaN where scale == 0)
     bits: int
+    step64: np.ndarray = None   # float64 [..., D/G] (max-min)/(2^b-1) before rounding
+    lo64: np.ndarray = None     # float64 [..., D/G] group minimum before rounding
 
 
 def quantize(y: np.ndarray, bits: int, G: int, meta: str) -> Quantized:
@@ -100,7 +102,8 @@ def quantize(y: np.ndarray, bits: int, G: int, meta: str) -> Quantized:
     lo = yg.min(axis=-1)
     hi = yg.max(axis=-1)
     qmax = (1 << bits) - 1
-    s = meta_round((hi - lo) / qmax, meta)
+    step64 = (hi - lo) / qmax
+    s = meta_round(step64, meta)
     z = meta_round(lo, meta)
     degenerate = s == 0
     with np.errstate(invalid="ignore", divide="ignore"):
@@ -108,7 +111,8 @@ def quantize(y: np.ndarray, bits: int, G: int, meta: str) -> Quantized:
     c = np.clip(np.rint(u), 0, qmax)
     c = np.where(degenerate[..., None], 0, c).astype(np.uint8)
     u = np.where(degenerate[..., None], np.nan, u)
-    return Quantized(codes=c.reshape(y.shape), scale=s, zero=z, u=u.reshape(y.shape), bits=bits)
+    return Quantized(codes=c.reshape(y.shape), scale=s, zero=z, u=u.reshape(y.shape), bits=bits,
+                     step64=step64, lo64=lo)
 
 
 def dequantize(codes: np.ndarray, scale: np.ndarray, zero: np.ndarray, G: int) -> np.ndarray:

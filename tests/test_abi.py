@@ -1,0 +1,187 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/rq.h declares, its host-side pool geometry matches the oracle's own
+implementation of the format, and invalid calls are rejected with the
+documented status before any device work is enqueued."""
+import ctypes
+import os
+import re
+from ctypes import c_float, c_void_p
+
+import numpy as np
+import pytest
+
+import oracle as O
+from conftest import ROOT
+
+import looped_transformer_decode_rq_amd as R
+from looped_transformer_decode_rq_amd import build as B
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(R.library_path):
+        B.build_library()
+    return R.lib()
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "rq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(rq_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(R.EXPORTED)
+
+
+LAYOUTS = [
+    dict(H=1, D=64, G=32, L=2, bits=(2,), meta="f32", kv="f32", nblk=17),
+    dict(H=16, D=128, G=128, L=4, bits=(2, 2, 2), meta="f16", kv="bf16", nblk=300),
+    dict(H=55, D=96, G=96, L=8, bits=(4, 4, 2, 2, 2, 2, 2), meta="f16", kv="bf16", nblk=5),
+    dict(H=3, D=128, G=32, L=3, bits=(4, 2), meta="f32", kv="bf16", nblk=9),
+    dict(H=2, D=64, G=16, L=1, bits=(), meta="f16", kv="f32", nblk=4),
+]
+
+
+def _lay(d):
+    return R.make_layout(d["H"], d["D"], d["G"], d["L"], d["bits"], d["nblk"], d["meta"], d["kv"])
+
+
+@pytest.mark.parametrize("d", LAYOUTS)
+def test_pool_geometry_matches_oracle(L, d):
+    lay = _lay(d)
+    assert R.layout_check(lay) == 0
+    ol = O.PoolLayout(d["H"], d["D"], d["G"], d["L"], d["bits"], d["meta"], d["nblk"])
+    assert R.pool_bytes(lay) == ol.pool_bytes
+    for l in range(d["L"]):
+        assert R.record_bytes(lay, l) == ol.rec_bytes(l)
+    rng = np.random.default_rng(0)
+    for _ in range(50):
+        blk, h, l, kv = (int(rng.integers(0, d["nblk"])), int(rng.integers(0, d["H"])),
+                         int(rng.integers(0, d["L"])), int(rng.integers(0, 2)))
+        assert R.record_offset(lay, blk, h, l, kv) == int(ol.record_offset(blk, h, l, kv))
+    assert R.record_offset(lay, d["nblk"], 0, 0, 0) == -1
+    assert R.record_offset(lay, 0, 0, d["L"], 0) == -1
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("head_dim", 256, -3), ("head_dim", 80, -2), ("head_dim", 0, -2), ("group_size", 16, -3), ("group_size", 48, -2),
+    ("num_loops", 17, -2), ("num_loops", 0, -2), ("block_size", 32, -3), ("num_blocks", 0, -2),
+    ("meta_dtype", 0, -3), ("kv_dtype", 1, -3), ("num_heads", 0, -2),
+])
+def test_layout_rejections(L, field, value, status):
+    lay = _lay(LAYOUTS[1])
+    setattr(lay, field, value)
+    assert R.layout_check(lay) == status
+    assert R.pool_bytes(lay) == 0
+
+
+def test_bits_rejection(L):
+    lay = _lay(LAYOUTS[1])
+    lay.loop_bits[1] = 3
+    assert R.layout_check(lay) == -3
+    lay.loop_bits[1] = 2
+    lay.loop_bits[3] = 7          # entry of the reference loop is ignored
+    assert R.layout_check(lay) == 0
+
+
+def test_status_strings(L):
+    for s in (0, -1, -2, -3, -4, -5, 99):
+        assert isinstance(R.status_string(s), str) and R.status_string(s)
+
+
+def _fake(i):
+    return c_void_p(0x100000 * (i + 1))     # 16-aligned non-null; never dereferenced on these paths
+
+
+def test_decode_validation(L):
+    lay = _lay(LAYOUTS[1])
+    loops = (ctypes.c_int32 * 1)(1)
+    ws_need = R.decode_workspace_bytes(lay, 1, 4, 10)
+    assert ws_need > 0
+    base = [ctypes.byref(lay), _fake(0), loops, 1, _fake(1), _fake(2), _fake(3), _fake(4), 4, 10,
+            None, None, c_float(0.1), _fake(5), _fake(6), ws_need, None, None]
+
+    def call(**kw):
+        a = list(base)
+        idx = dict(pool=1, loops=2, n=3, q=4, rot=5, table=6, seq=7, batch=8, mb=9, tk=10, tv=11,
+                   scale=12, out=13, ws=14, wsb=15)
+        for k, v in kw.items():
+            a[idx[k]] = v
+        return L.rq_decode_attention_ex(*a)
+
+    assert call(wsb=ws_need - 1) == -4
+    assert call(pool=None) == -1
+    assert call(q=None) == -1
+    assert call(out=None) == -1
+    assert call(ws=None) == -1
+    assert call(loops=None) == -1
+    assert call(tk=_fake(7)) == -1             # one tail without the other
+    assert call(n=0) == -2
+    assert call(n=17) == -2
+    assert call(loops=(ctypes.c_int32 * 1)(4)) == -2
+    assert call(loops=(ctypes.c_int32 * 1)(-1)) == -2
+    assert call(mb=0) == -2
+    assert call(batch=-1) == -2
+    assert call(scale=c_float(float("inf"))) == -2
+    assert call(pool=c_void_p(0x100008)) == -2  # misaligned pool
+    assert call(batch=0) == 0                   # nothing to do, nothing launched
+    # rot may be NULL only when every requested loop is the reference
+    assert call(rot=None) == -1
+    assert call(rot=None, loops=(ctypes.c_int32 * 1)(3), wsb=0) == -4
+    bad = R.make_layout(16, 80, 80, 4, (2, 2, 2), 300)
+    a = list(base)
+    a[0] = ctypes.byref(bad)
+    assert L.rq_decode_attention_ex(*a) == -3
+
+
+def test_encode_validation(L):
+    lay = _lay(LAYOUTS[1])
+    f = L.rq_encode_pack
+    assert f(ctypes.byref(lay), _fake(0), _fake(1), _fake(2), _fake(3), -1, None) == -2
+    assert f(ctypes.byref(lay), _fake(0), _fake(1), _fake(2), _fake(3), 0, None) == 0
+    assert f(ctypes.byref(lay), None, _fake(1), _fake(2), _fake(3), 5, None) == -1
+    assert f(ctypes.byref(lay), _fake(0), None, _fake(2), _fake(3), 5, None) == -1
+    assert f(ctypes.byref(lay), _fake(0), _fake(1), None, _fake(3), 5, None) == -1
+    assert f(ctypes.byref(lay), _fake(0), _fake(1), _fake(2), None, 5, None) == -1
+    assert f(None, _fake(0), _fake(1), _fake(2), _fake(3), 5, None) == -1
+
+
+def test_bf16_validation(L):
+    f = L.rq_bf16_decode_attention_ex
+    need = R.bf16_workspace_bytes(16, 128, 4, 10)
+    base = [16, 128, 16, 100, _fake(0), _fake(1), _fake(2), _fake(3), _fake(4), 4, 10, None, None,
+            c_float(0.1), _fake(5), _fake(6), need, None, None]
+    assert f(*base[:16], need - 4, None, None) == -4
+    a = list(base); a[1] = 100
+    assert f(*a) == -3
+    a = list(base); a[2] = 8
+    assert f(*a) == -3
+    a = list(base); a[4] = None
+    assert f(*a) == -1
+    a = list(base); a[9] = 0
+    assert f(*a) == 0
+    assert L.rq_bf16_write(16, 128, 16, 100, _fake(0), _fake(1), _fake(2), None, 3, None) == -1
+    assert L.rq_bf16_write(16, 128, 16, 100, _fake(0), _fake(1), _fake(2), _fake(3), 0, None) == 0
+
+
+def test_workspace_sizes_monotone(L):
+    lay = _lay(LAYOUTS[1])
+    a = R.decode_workspace_bytes(lay, 1, 16, 2049)
+    b = R.decode_workspace_bytes(lay, 4, 16, 2049)
+    assert 0 < a < b
+    assert R.decode_workspace_bytes(lay, 1, 16, 2049, 8) > R.decode_workspace_bytes(lay, 1, 16, 2049, 64)
+    assert R.decode_workspace_bytes(lay, 0, 16, 2049) == 0
+
+
+def test_binding_refuses_host_tensors(L):
+    torch = pytest.importorskip("torch")
+    lay = _lay(LAYOUTS[0])
+    with pytest.raises(ValueError):
+        R.encode_pack(lay, torch.zeros(R.pool_bytes(lay), dtype=torch.uint8),
+                      torch.zeros(2, 2, 1, 1, 64), torch.zeros(1, 2, 64, 64),
+                      torch.zeros(1, dtype=torch.int64))

@@ -1,0 +1,95 @@
+"""Full-size parity: every workload at its real shape (the 24-layer workload:
+one layer at its full batch and context, shuffled block table), inputs drawn
+on the device by the seeded generator, the whole cache packed by the HIP
+encoder, decode run in the split configuration the benchmark uses. A seeded
+sample of (sequence, head) pairs is then recomputed by the oracle one by one
+from the same generator draws: their packed records must match the oracle's
+encoding (exemption rule of gpu_util) and their attention outputs must match
+the oracle's attention over the oracle's own packed bytes."""
+import time
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+from gpu_util import (check_attention, check_caps, compare_pool_tokens, dev, lib_layout, to_host64, torch)
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(f"[full {time.strftime('%H:%M:%S')}] {msg}", flush=True)
+
+
+@pytest.mark.parametrize("key", [1, 2, 3, 4])
+def test_full_size_sampled(key):
+    import looped_transformer_decode_rq_amd as R
+    T = torch()
+    w = W.get(key)
+    B, N, H, D, L = w.batch, w.context, w.heads, w.head_dim, w.loops
+    _log(f"{w.name}: B{B} N{N} H{H} D{D} L{L}")
+    st = W.structure(w, 0)
+    table, nblk = W.block_table(w)
+    lay = lib_layout(w, nblk)
+    pool = T.zeros(R.pool_bytes(lay), dtype=T.uint8, device=dev())
+    rot = T.from_numpy(st["rot32"]).to(dev())
+    d_table = T.from_numpy(table).to(dev())
+    d_seq = T.full((B,), N, dtype=T.int32, device=dev())
+    rng = np.random.default_rng([w.seed, 1234])
+    samples = sorted({(int(rng.integers(0, B)), int(rng.integers(0, H))) for _ in range(3)})
+    kvdt = T.bfloat16 if w.kv_dtype == "bf16" else T.float32
+    tail_k = T.empty((L, B, H, D), dtype=kvdt, device=dev())
+    tail_v = T.empty_like(tail_k)
+    host = {}
+    pos = np.arange(N)
+    for b in range(B):
+        kvb = W.kv_torch(w, 0, b, st, dev())                       # [L][2][N+1][H][D]
+        slots = T.from_numpy(table[b, pos // 16].astype(np.int64) * 16 + pos % 16).to(dev())
+        R.encode_pack(lay, pool, kvb[:, :, :N].contiguous(), rot, slots)
+        tail_k[:, b] = kvb[:, 0, N]
+        tail_v[:, b] = kvb[:, 1, N]
+        for hb, hh in samples:
+            if hb == b:
+                host[(b, hh)] = to_host64(kvb[:, :, :N, hh:hh + 1])  # [L][2][N][1][D]
+        del kvb
+    T.cuda.synchronize()
+    _log("cache packed")
+    q = W.queries_torch(w, 0, dev())                                 # [L][B][H][D]
+    tau = 1.0 / np.sqrt(D)
+    outs = []
+    for l in range(L):
+        out = T.empty((1, B, H, D), device=dev())
+        ws = T.empty(R.decode_workspace_bytes(lay, 1, B, table.shape[1]), dtype=T.uint8, device=dev())
+        R.decode_attention(lay, pool, [l], q[l:l + 1].contiguous(), rot, d_table, d_seq,
+                           tail_k[l:l + 1].contiguous(), tail_v[l:l + 1].contiguous(), tau, out, ws)
+        outs.append(out[0])
+    T.cuda.synchronize()
+    _log("decode done")
+    npages = -(-N // 16)
+    slab = R.pool_bytes(lay) // (nblk * H)
+    pool3 = pool.view(nblk, H, slab)
+    q_h = to_host64(q)
+    tk_h, tv_h = to_host64(tail_k), to_host64(tail_v)
+    stats = {}
+    for b, h in samples:
+        kvh = host[(b, h)]
+        rot_h = st["rot32"][h:h + 1]
+        enc = O.encode(kvh, rot_h, w.res_bits, w.group_size, w.meta_dtype)
+        mini = O.PoolLayout(1, D, w.group_size, L, w.res_bits, w.meta_dtype, npages)
+        pages = T.from_numpy(table[b, :npages].astype(np.int64)).to(dev())
+        got_bytes = pool3[pages, h].contiguous().cpu().numpy().reshape(-1)
+        compare_pool_tokens(f"{w.name} b{b} h{h}", got_bytes, mini, enc, pos, stats)
+        ref_pool = np.zeros(mini.pool_bytes, np.uint8)
+        O.write_tokens(ref_pool, mini, enc, pos)
+        mtable = np.arange(npages, dtype=np.int64)[None]
+        for l in range(L):
+            want = O.decode_attention(ref_pool, mini, l, q_h[l, b:b + 1, h:h + 1], rot_h, mtable, [N], tau,
+                                      tk_h[l, b:b + 1, h:h + 1], tv_h[l, b:b + 1, h:h + 1])[0, 0]
+            got = outs[l][b, h].cpu().numpy()
+            e, r = check_attention(f"{w.name} b{b} h{h} loop {l}", got, want)
+            _log(f"b{b} h{h} loop {l}: max-abs {e:.2e} rel-L2 {r:.2e}")
+    check_caps(stats)
+    _log(f"encode stats {stats}")
+    for l in range(L):
+        assert T.isfinite(outs[l]).all()
