@@ -24,6 +24,8 @@
 //   rq_combine   per (head, loop call, 16 sequences): log-sum-exp merge of the
 //                partials and the uncompressed tail token, then
 //                out = acc_ref/l + R_V^T (acc_res/l) on the f32 matrix cores.
+#include <type_traits>
+
 #include "rq_device.h"
 #include "rq_internal.h"
 
@@ -62,110 +64,102 @@ __device__ __forceinline__ int limb_channel(int q4, int k, int n, int rb) {
     return q4 * CPL + 8 * k + n;
 }
 
+// One workgroup per (head, loop call, 16 sequences); one wave per sequence.
 template <int D, bool KV_F32>
-__global__ __launch_bounds__(256) void rq_qprep_kernel(QPrepArgs a) {
+__global__ __launch_bounds__(1024) void rq_qprep_kernel(QPrepArgs a) {
     using Ln = Lanes<D>;
     constexpr int QS = D + 1;
     __shared__ float Q[16 * QS];
     __shared__ float QR[16 * QS];
-    __shared__ int QI[kWaves][2][D];
-    __shared__ int8_t DG[kWaves][2][4][D];
+    __shared__ int QI[16][2][D];
+    __shared__ int8_t DG[16][2][4][D];
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, r = threadIdx.x >> 6;
     const int h = blockIdx.x, i = blockIdx.y, tile = blockIdx.z;
     const int rb = a.rb[i];
     const int B = a.B, H = a.H;
+    const int b = tile * 16 + r;
+    const bool row_ok = b < B;
 
-    for (int e = threadIdx.x; e < 16 * D; e += 256) {
-        const int r = e / D, c = e % D;
-        const int b = tile * 16 + r;
-        Q[r * QS + c] = (b < B) ? load_kv<KV_F32>(a.q, (((int64_t)i * B + b) * H + h) * D + c) : 0.0f;
-    }
+    for (int c = lane; c < D; c += 64)
+        Q[r * QS + c] = row_ok ? load_kv<KV_F32>(a.q, (((int64_t)i * B + b) * H + h) * D + c) : 0.0f;
     __syncthreads();
-    if (rb != 0) {
+    if (rb != 0 && r < D / 16) {
         // q' = R_K q for the 16 rows: [16 x D] x R_K^T. v_mfma_f32_16x16x4f32:
         // lane l supplies A[l%16][k0 + l/16], B[k0 + l/16][l%16] and receives
-        // D[4*(l/16)+v][l%16].
+        // D[4*(l/16)+v][l%16]; wave r computes columns 16r..16r+15.
         const float *RK = a.rot + ((int64_t)h * 2 + 0) * D * D;
-        for (int nt = wave; nt < D / 16; nt += kWaves) {
-            floatx4 c = {0.f, 0.f, 0.f, 0.f};
-            const int n = nt * 16 + (lane & 15);
-            for (int kk = 0; kk < D / 4; ++kk) {
-                const int k = 4 * kk + (lane >> 4);
-                c = __builtin_amdgcn_mfma_f32_16x16x4f32(Q[(lane & 15) * QS + k], RK[(int64_t)n * D + k], c, 0, 0, 0);
-            }
-            for (int v = 0; v < 4; ++v) QR[(4 * (lane >> 4) + v) * QS + n] = c[v];
+        floatx4 c = {0.f, 0.f, 0.f, 0.f};
+        const int n = r * 16 + (lane & 15);
+        for (int kk = 0; kk < D / 4; ++kk) {
+            const int k = 4 * kk + (lane >> 4);
+            c = __builtin_amdgcn_mfma_f32_16x16x4f32(Q[(lane & 15) * QS + k], RK[(int64_t)n * D + k], c, 0, 0, 0);
         }
+        for (int v = 0; v < 4; ++v) QR[(4 * (lane >> 4) + v) * QS + n] = c[v];
     }
     __syncthreads();
 
-    for (int j = 0; j < 4; ++j) {
-        const int r = wave + 4 * j;
-        const int b = tile * 16 + r;
-        const bool row_ok = b < B;
-        int S[2] = {0, 0};
-        for (int which = 0; which < 2; ++which) {
-            const float *src = which == 0 ? Q : QR;
-            const bool on = which == 0 || rb != 0;
-            float x0 = 0.f, x1 = 0.f;
-            if (on) {
-                x0 = (lane < D) ? src[r * QS + lane] : 0.f;
-                x1 = (lane + 64 < D) ? src[r * QS + lane + 64] : 0.f;
-            }
-            const float amax = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
-            int s = 0;
-            if (amax > 0.f) {
-                int e;
-                frexpf(amax, &e);
-                s = 14 - e;
-                if (ldexpf(amax, s + 1) <= (float)kQmaxFixed) s += 1;
-            }
-            S[which] = s;
-            for (int half = 0; half < 2; ++half) {
-                const int c = lane + 64 * half;
-                if (c >= D) continue;
-                const int qi = (int)rintf(ldexpf(half ? x1 : x0, s));
-                QI[wave][which][c] = qi;
-                int rem = qi;
-                for (int d = 0; d < 4; ++d) {
-                    const int dig = ((rem + 8) & 15) - 8;
-                    DG[wave][which][d][c] = (int8_t)dig;
-                    rem = (rem - dig) / 16;
-                }
+    // 16-bit fixed point per row, split into four balanced base-16 digits
+    int S[2] = {0, 0};
+    for (int which = 0; which < 2; ++which) {
+        const float *src = which == 0 ? Q : QR;
+        const bool on = which == 0 || rb != 0;
+        float x0 = 0.f, x1 = 0.f;
+        if (on) {
+            x0 = (lane < D) ? src[r * QS + lane] : 0.f;
+            x1 = (lane + 64 < D) ? src[r * QS + lane + 64] : 0.f;
+        }
+        const float amax = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
+        int s = 0;
+        if (amax > 0.f) {
+            int e;
+            frexpf(amax, &e);
+            s = 14 - e;
+            if (ldexpf(amax, s + 1) <= (float)kQmaxFixed) s += 1;
+        }
+        S[which] = s;
+        for (int half = 0; half < 2; ++half) {
+            const int c = lane + 64 * half;
+            if (c >= D) continue;
+            const int qi = (int)rintf(ldexpf(half ? x1 : x0, s));
+            QI[r][which][c] = qi;
+            int rem = qi;
+            for (int d = 0; d < 4; ++d) {
+                const int dig = ((rem + 8) & 15) - 8;
+                DG[r][which][d][c] = (int8_t)dig;
+                rem = (rem - dig) / 16;
             }
         }
-        __syncthreads();
-        if (row_ok) {
-            uint8_t *qp = a.qpack + (((int64_t)i * B + b) * H + h) * qpack_bytes(D);
-            // limb dwords: [q4][k][limb], nibble n = channel limb_channel(q4,k,n)
-            for (int which = 0; which < 2; ++which) {
-                if (which == 1 && rb == 0) break;
-                const int order = which == 0 ? 4 : rb;
-                for (int dw = lane; dw < D / 2; dw += 64) {
-                    const int limb = dw & 3;
-                    const int k = (dw >> 2) % Ln::NDW;
-                    const int q4 = dw / (4 * Ln::NDW);
-                    uint32_t word = 0;
-                    for (int nn = 0; nn < 8; ++nn) {
-                        const int ch = limb_channel<D>(q4, k, nn, order);
-                        word |= ((uint32_t)DG[wave][which][limb][ch] & 15u) << (4 * nn);
-                    }
-                    ((uint32_t *)(qp + 64 + which * 2 * D))[dw] = word;
-                }
+    }
+    __syncthreads();
+    if (!row_ok) return;
+    uint8_t *qp = a.qpack + (((int64_t)i * B + b) * H + h) * qpack_bytes(D);
+    // limb dwords: [q4][k][limb], nibble n = channel limb_channel(q4,k,n)
+    for (int which = 0; which < 2; ++which) {
+        if (which == 1 && rb == 0) break;
+        const int order = which == 0 ? 4 : rb;
+        for (int dw = lane; dw < D / 2; dw += 64) {
+            const int limb = dw & 3;
+            const int k = (dw >> 2) % Ln::NDW;
+            const int q4 = dw / (4 * Ln::NDW);
+            uint32_t word = 0;
+            for (int nn = 0; nn < 8; ++nn) {
+                const int ch = limb_channel<D>(q4, k, nn, order);
+                word |= ((uint32_t)DG[r][which][limb][ch] & 15u) << (4 * nn);
             }
-            if (lane < 2 * Ln::LPT) {
-                const int which = lane / Ln::LPT, q4 = lane % Ln::LPT;
-                int sum = 0;
-                if (which == 0 || rb != 0)
-                    for (int c = q4 * Ln::CPL; c < (q4 + 1) * Ln::CPL; ++c) sum += QI[wave][which][c];
-                ((int *)(qp + 16 + 16 * which))[q4] = sum;
-            }
-            if (lane == 0) {
-                ((float *)qp)[0] = ldexpf(1.0f, -S[0]);
-                ((float *)qp)[1] = rb ? ldexpf(1.0f, -S[1]) : 0.0f;
-            }
+            ((uint32_t *)(qp + 64 + which * 2 * D))[dw] = word;
         }
-        __syncthreads();
+    }
+    if (lane < 2 * Ln::LPT) {
+        const int which = lane / Ln::LPT, q4 = lane % Ln::LPT;
+        int sum = 0;
+        if (which == 0 || rb != 0)
+            for (int c = q4 * Ln::CPL; c < (q4 + 1) * Ln::CPL; ++c) sum += QI[r][which][c];
+        ((int *)(qp + 16 + 16 * which))[q4] = sum;
+    }
+    if (lane == 0) {
+        ((float *)qp)[0] = ldexpf(1.0f, -S[0]);
+        ((float *)qp)[1] = rb ? ldexpf(1.0f, -S[1]) : 0.0f;
     }
 }
 
@@ -181,7 +175,7 @@ struct SplitArgs {
     int max_blocks;
     const int32_t *seq_lens;
     const uint8_t *qpack;   // this call: [B][H][qpack_bytes]
-    float *partials;        // this call: [B][H][nsplit][2 + 2D]
+    float *partials;        // this call: [B][H][nwg][2 + 2D]
     int nsplit, split_pages;
     float score_scale;      // softmax_scale * log2(e)
 };
@@ -231,15 +225,16 @@ __device__ __forceinline__ float ubyte(uint32_t x, int j) { return (float)((x >>
 // Integer dot of 4-bit codes (XOR 8 turns 0..15 into signed -8..7) with the
 // four query limbs; returns sum_i q_int_i * (c_i - 8).
 template <int NW>
-__device__ __forceinline__ int dot_int4(const uint32_t *codes, const uint32_t (*limb)[4]) {
+__device__ __forceinline__ int dot_int4(const uint32_t *codes, const uint4 *limb) {
     int a0 = 0, a1 = 0, a2 = 0, a3 = 0;
 #pragma unroll
     for (int k = 0; k < NW; ++k) {
         const int w = (int)(codes[k] ^ 0x88888888u);
-        a0 = __builtin_amdgcn_sdot8((int)limb[k][0], w, a0, false);
-        a1 = __builtin_amdgcn_sdot8((int)limb[k][1], w, a1, false);
-        a2 = __builtin_amdgcn_sdot8((int)limb[k][2], w, a2, false);
-        a3 = __builtin_amdgcn_sdot8((int)limb[k][3], w, a3, false);
+        const uint4 q = limb[k];
+        a0 = __builtin_amdgcn_sdot8((int)q.x, w, a0, false);
+        a1 = __builtin_amdgcn_sdot8((int)q.y, w, a1, false);
+        a2 = __builtin_amdgcn_sdot8((int)q.z, w, a2, false);
+        a3 = __builtin_amdgcn_sdot8((int)q.w, w, a3, false);
     }
     return a0 + 16 * a1 + 256 * a2 + 4096 * a3;
 }
@@ -247,20 +242,21 @@ __device__ __forceinline__ int dot_int4(const uint32_t *codes, const uint32_t (*
 // Same for 2-bit codes: a word of 16 crumbs is split into its even and odd
 // channels, each widened to nibbles (values 0..3 need no offset).
 template <int NW>
-__device__ __forceinline__ int dot_int2(const uint32_t *codes, const uint32_t (*limb)[4]) {
+__device__ __forceinline__ int dot_int2(const uint32_t *codes, const uint4 *limb) {
     int a0 = 0, a1 = 0, a2 = 0, a3 = 0;
 #pragma unroll
     for (int k = 0; k < NW; ++k) {
         const int ev = (int)(codes[k] & 0x33333333u);
         const int od = (int)((codes[k] >> 2) & 0x33333333u);
-        a0 = __builtin_amdgcn_sdot8((int)limb[2 * k][0], ev, a0, false);
-        a1 = __builtin_amdgcn_sdot8((int)limb[2 * k][1], ev, a1, false);
-        a2 = __builtin_amdgcn_sdot8((int)limb[2 * k][2], ev, a2, false);
-        a3 = __builtin_amdgcn_sdot8((int)limb[2 * k][3], ev, a3, false);
-        a0 = __builtin_amdgcn_sdot8((int)limb[2 * k + 1][0], od, a0, false);
-        a1 = __builtin_amdgcn_sdot8((int)limb[2 * k + 1][1], od, a1, false);
-        a2 = __builtin_amdgcn_sdot8((int)limb[2 * k + 1][2], od, a2, false);
-        a3 = __builtin_amdgcn_sdot8((int)limb[2 * k + 1][3], od, a3, false);
+        const uint4 qe = limb[2 * k], qo = limb[2 * k + 1];
+        a0 = __builtin_amdgcn_sdot8((int)qe.x, ev, a0, false);
+        a1 = __builtin_amdgcn_sdot8((int)qe.y, ev, a1, false);
+        a2 = __builtin_amdgcn_sdot8((int)qe.z, ev, a2, false);
+        a3 = __builtin_amdgcn_sdot8((int)qe.w, ev, a3, false);
+        a0 = __builtin_amdgcn_sdot8((int)qo.x, od, a0, false);
+        a1 = __builtin_amdgcn_sdot8((int)qo.y, od, a1, false);
+        a2 = __builtin_amdgcn_sdot8((int)qo.z, od, a2, false);
+        a3 = __builtin_amdgcn_sdot8((int)qo.w, od, a3, false);
     }
     return a0 + 16 * a1 + 256 * a2 + 4096 * a3;
 }
@@ -293,41 +289,68 @@ __device__ __forceinline__ void axpy_int2(float *acc, const uint32_t *codes, flo
     }
 }
 
+// Raw loads of one page step (16 or 32 tokens) for one lane; converted only
+// when consumed, so that the next step's loads stay in flight meanwhile.
+template <int D, int RB, bool META_F32>
+struct PageRegs {
+    using Ln = Lanes<D>;
+    static constexpr int REF_NW = Ln::CPL / 8;
+    static constexpr int RES_NW = RB ? Ln::CPL * RB / 32 : 1;
+    using SZ = typename std::conditional<META_F32, float2, uint32_t>::type;
+    using AL = typename std::conditional<META_F32, float, uint32_t>::type;
+    uint32_t ck[REF_NW], cv[REF_NW], rk[RES_NW], rv[RES_NW];
+    SZ mkr, mvr, mks, mvs;
+    AL ak, av;
+};
+
+__device__ __forceinline__ void sz_of(float2 v, float &s, float &z) { s = v.x; z = v.y; }
+__device__ __forceinline__ void sz_of(uint32_t v, float &s, float &z) {
+    s = f16_to_f32((uint16_t)(v & 0xFFFF));
+    z = f16_to_f32((uint16_t)(v >> 16));
+}
+__device__ __forceinline__ float al_of(float v) { return v; }
+__device__ __forceinline__ float al_of(uint32_t v) { return f16_to_f32((uint16_t)v); }
+
 template <int D, int RB, bool META_F32>
 __global__ __launch_bounds__(256) void rq_split_kernel(SplitArgs a) {
     using Ln = Lanes<D>;
+    using PR = PageRegs<D, RB, META_F32>;
     constexpr int LPT = Ln::LPT, CPL = Ln::CPL, PPI = Ln::PPI;
     constexpr int REF_NB = CPL / 2;                 // INT4 code bytes per lane
     constexpr int RES_NB = RB ? CPL * RB / 8 : 4;   // residual code bytes per lane
-    constexpr int REF_NW = REF_NB / 4, RES_NW = RES_NB / 4;
+    constexpr int REF_NW = PR::REF_NW, RES_NW = PR::RES_NW;
     constexpr int msz = META_F32 ? 4 : 2;
+    constexpr int PF = partial_floats(D);
+    __shared__ float wp[kWaves][PF];
+    __shared__ __attribute__((aligned(16))) uint32_t limbs[D];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int split = blockIdx.x * kWaves + wave;
     const int h = blockIdx.y, b = blockIdx.z;
-    if (split >= a.nsplit) return;
     const int H = a.H;
     int seq = a.seq_lens[b];
     seq = seq < 0 ? 0 : (seq > a.max_blocks * 16 ? a.max_blocks * 16 : seq);
     const int npages = (seq + 15) >> 4;
     const int p0 = split * a.split_pages;
-    const int p1 = min(npages, p0 + a.split_pages);
-    if (p0 >= p1) return;
+    const int p1 = min(npages, p0 + a.split_pages);   // p0 >= p1: this wave has no pages
 
     const int tok_i = lane / LPT, q4 = lane % LPT;
     const int page_in_step = tok_i >> 4, tok = tok_i & 15;
     const int ng = D / a.G;
     const int g = (q4 * CPL) / a.G;
 
-    // query record of (b, h)
+    // query record of (b, h), shared by the workgroup's waves: the limbs live
+    // in LDS (read once per page step), the scalars in registers
     const uint8_t *qp = a.qpack + ((int64_t)b * H + h) * qpack_bytes(D);
     const float sc_ref = ((const float *)qp)[0];
     const float sc_res = ((const float *)qp)[1];
     const int qs_ref = ((const int *)(qp + 16))[q4];
     const int qs_res = ((const int *)(qp + 32))[q4];
-    uint32_t lref[Ln::NDW][4], lres[Ln::NDW][4];
-    load_bytes<Ln::NDW * 16>(qp + 64 + q4 * Ln::NDW * 16, &lref[0][0]);
-    if constexpr (RB != 0) load_bytes<Ln::NDW * 16>(qp + 64 + 2 * D + q4 * Ln::NDW * 16, &lres[0][0]);
+    constexpr int NLIMB = (RB ? 2 : 1) * D / 2;       // dwords: ref limbs (+ residual limbs)
+    for (int i = threadIdx.x; i < NLIMB; i += 256) limbs[i] = ((const uint32_t *)(qp + 64))[i];
+    __syncthreads();
+    const uint4 *lref = (const uint4 *)&limbs[q4 * Ln::NDW * 4];
+    const uint4 *lres = (const uint4 *)&limbs[D / 2 + q4 * Ln::NDW * 4];
 
     const int32_t *table = a.block_table + (int64_t)b * a.max_blocks;
     const int ref_meta = a.ref_code_bytes + (tok * ng + g) * 2 * msz;
@@ -343,47 +366,64 @@ __global__ __launch_bounds__(256) void rq_split_kernel(SplitArgs a) {
 #pragma unroll
     for (int i = 0; i < (RB ? CPL : 1); ++i) accs[i] = 0.f;
 
-    for (int p = p0; p < p1; p += PPI) {
-        const int pp = p + page_in_step;
-        bool valid = pp < p1;
-        int64_t blk = valid ? (int64_t)table[pp] : 0;
-        if (blk < 0 || blk >= a.nblk) { blk = 0; valid = false; }
-        valid = valid && (pp * 16 + tok < seq);
-        const uint8_t *slab = a.pool + (blk * H + h) * a.slab;
+    // block id of this lane's page in step `it` of a chunk whose table entries
+    // sit one per lane in `tbl` (-1 = no page / invalid id)
+    auto page_blk = [&](int tbl, int it) -> int {
+        if constexpr (PPI == 1) {
+            return __builtin_amdgcn_readlane(tbl, it);
+        } else {
+            const int lo = __builtin_amdgcn_readlane(tbl, 2 * it);
+            const int hi = __builtin_amdgcn_readlane(tbl, 2 * it + 1);
+            return page_in_step ? hi : lo;
+        }
+    };
+    auto load_page = [&](int blk, PR &r) {
+        const uint8_t *slab = a.pool + ((int64_t)(blk < 0 ? 0 : blk) * H + h) * a.slab;
         const uint8_t *kr = slab + a.ref_off;
         const uint8_t *vr = kr + a.ref_rec;
-
-        uint32_t ck[REF_NW], cv[REF_NW];
-        load_bytes<REF_NB>(kr + ref_codes, ck);
-        load_bytes<REF_NB>(vr + ref_codes, cv);
-        float skr, zkr, svr, zvr;
-        load_sz<META_F32>(kr + ref_meta, skr, zkr);
-        load_sz<META_F32>(vr + ref_meta, svr, zvr);
-
-        uint32_t rk[RES_NW], rv[RES_NW];
-        float sks = 0.f, zks = 0.f, svs = 0.f, zvs = 0.f, ak = 1.f, av = 1.f;
+        load_bytes<REF_NB>(kr + ref_codes, r.ck);
+        load_bytes<REF_NB>(vr + ref_codes, r.cv);
+        r.mkr = *(const typename PR::SZ *)(kr + ref_meta);
+        r.mvr = *(const typename PR::SZ *)(vr + ref_meta);
         if constexpr (RB != 0) {
             const uint8_t *ks = slab + a.res_off;
             const uint8_t *vs = ks + a.res_rec;
-            load_bytes<RES_NB>(ks + res_codes, rk);
-            load_bytes<RES_NB>(vs + res_codes, rv);
-            load_sz<META_F32>(ks + res_meta, sks, zks);
-            load_sz<META_F32>(vs + res_meta, svs, zvs);
-            ak = load_meta1<META_F32>(ks + res_alpha);
-            av = load_meta1<META_F32>(vs + res_alpha);
+            load_bytes<RES_NB>(ks + res_codes, r.rk);
+            load_bytes<RES_NB>(vs + res_codes, r.rv);
+            r.mks = *(const typename PR::SZ *)(ks + res_meta);
+            r.mvs = *(const typename PR::SZ *)(vs + res_meta);
+            if constexpr (META_F32) {
+                r.ak = *(const float *)(ks + res_alpha);
+                r.av = *(const float *)(vs + res_alpha);
+            } else {
+                r.ak = *(const uint16_t *)(ks + res_alpha);
+                r.av = *(const uint16_t *)(vs + res_alpha);
+            }
         }
-
-        // ---- score: q.x_hat = alpha*(s*sum q c + z*sum q) + (s_r*sum q' c_r + z_r*sum q')
-        const int dref = dot_int4<REF_NW>(ck, lref) + 8 * qs_ref;
+    };
+    auto process = [&](const PR &r, bool valid) {
+        // keep the LDS limb reads inside the loop (re-read per step) instead
+        // of letting them be hoisted into 32 more registers
+        __asm__ volatile("" ::: "memory");
+        float skr, zkr, svr, zvr;
+        sz_of(r.mkr, skr, zkr);
+        sz_of(r.mvr, svr, zvr);
+        // score: q.x_hat = alpha*(s*sum q c + z*sum q) + (s_r*sum q' c_r + z_r*sum q')
+        const int dref = dot_int4<REF_NW>(r.ck, lref) + 8 * qs_ref;
         float part = (skr * (float)dref + zkr * (float)qs_ref) * sc_ref;
+        float av = 1.f, svs = 0.f, zvs = 0.f;
         if constexpr (RB != 0) {
-            int dres = (RB == 2) ? dot_int2<RES_NW>(rk, lres) : dot_int4<RES_NW>(rk, lres) + 8 * qs_res;
+            float sks, zks;
+            sz_of(r.mks, sks, zks);
+            sz_of(r.mvs, svs, zvs);
+            const float ak = al_of(r.ak);
+            av = al_of(r.av);
+            const int dres = (RB == 2) ? dot_int2<RES_NW>(r.rk, lres) : dot_int4<RES_NW>(r.rk, lres) + 8 * qs_res;
             part = ak * part + (sks * (float)dres + zks * (float)qs_res) * sc_res;
         }
         float score = group_sum<LPT>(part) * a.score_scale;
         score = valid ? score : kNegInf;
-
-        // ---- online softmax, rescaled only when a score beats m by 2^8
+        // online softmax, rescaled only when a score beats m by 2^8
         if (__any(score > m + kRescaleThresh)) {
             const float mn = fmaxf(m, wave_max(score));
             const float f = fast_exp2(m - mn);
@@ -396,17 +436,46 @@ __global__ __launch_bounds__(256) void rq_split_kernel(SplitArgs a) {
         }
         const float pr = fast_exp2(score - m);
         lsum += pr;
-
-        // ---- V: acc_ref += p*alpha*s*c (+ p*alpha*z per group), acc_res in rotated space
+        // V: acc_ref += p*alpha*s*c (+ p*alpha*z per group), acc_res in rotated space
         const float pa = pr * av;
         const float wr = valid ? pa * svr : 0.f;
         zr += valid ? pa * zvr : 0.f;
-        axpy_int4<REF_NW>(accr, cv, wr);
+        axpy_int4<REF_NW>(accr, r.cv, wr);
         if constexpr (RB != 0) {
             const float ws = valid ? pr * svs : 0.f;
             zs += valid ? pr * zvs : 0.f;
-            if constexpr (RB == 2) axpy_int2<RES_NW>(accs, rv, ws);
-            else axpy_int4<RES_NW>(accs, rv, ws);
+            if constexpr (RB == 2) axpy_int2<RES_NW>(accs, r.rv, ws);
+            else axpy_int4<RES_NW>(accs, r.rv, ws);
+        }
+    };
+
+    for (int cbase = p0; cbase < p1; cbase += 64) {
+        const int cnt = min(64, p1 - cbase);
+        int tbl = -1;
+        if (lane < cnt) {
+            tbl = table[cbase + lane];
+            if (tbl < 0 || tbl >= a.nblk) tbl = -1;
+        }
+        const int steps = (cnt + PPI - 1) / PPI;
+        auto valid_of = [&](int it, int blk) {
+            const int pp = cbase + it * PPI + page_in_step;
+            return blk >= 0 && pp < p1 && pp * 16 + tok < seq;
+        };
+        // two page steps in flight: the loads of step it+1 are issued before
+        // step it is consumed. Loads are issued unconditionally (past the last
+        // step they re-read the last page, a cache hit) so that the wait
+        // counters stay exact on every path.
+        PR A, Bq;
+        int blkA = page_blk(tbl, 0), blkB;
+        load_page(blkA, A);
+        for (int it = 0; it < steps; it += 2) {
+            blkB = page_blk(tbl, min(it + 1, steps - 1));
+            load_page(blkB, Bq);
+            process(A, valid_of(it, blkA));
+            if (it + 1 >= steps) break;
+            blkA = page_blk(tbl, min(it + 2, steps - 1));
+            load_page(blkA, A);
+            process(Bq, valid_of(it + 1, blkB));
         }
     }
 
@@ -427,22 +496,45 @@ __global__ __launch_bounds__(256) void rq_split_kernel(SplitArgs a) {
         }
         lsum += __shfl_xor(lsum, off, 64);
     }
+    // ---- merge the workgroup's 4 wave partials (log-sum-exp), one partial per workgroup
     if (lane < LPT) {
-        float *out = a.partials + (((int64_t)b * H + h) * a.nsplit + split) * partial_floats(D);
-        if (lane == 0) { out[0] = m; out[1] = lsum; }
+        if (lane == 0) { wp[wave][0] = m; wp[wave][1] = lsum; }
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) out[2 + q4 * CPL + i] = accr[i];
+        for (int i = 0; i < CPL; ++i) wp[wave][2 + q4 * CPL + i] = accr[i];
         if constexpr (RB != 0) {
 #pragma unroll
-            for (int i = 0; i < CPL; ++i) out[2 + D + q4 * CPL + i] = accs[i];
+            for (int i = 0; i < CPL; ++i) wp[wave][2 + D + q4 * CPL + i] = accs[i];
         }
+    }
+    __syncthreads();
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wp[w][0]);
+    if (M == kNegInf) return;                      // no page in this workgroup
+    float e[kWaves];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) e[w] = fast_exp2(wp[w][0] - M);
+    float *out = a.partials + (((int64_t)b * H + h) * gridDim.x + blockIdx.x) * PF;
+    constexpr int NV = RB ? 2 * D : D;
+    for (int v = threadIdx.x; v < NV; v += 256) {
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) s = fmaf(e[w], wp[w][2 + v], s);
+        out[2 + v] = s;
+    }
+    if (threadIdx.x == 0) {
+        float l = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) l = fmaf(e[w], wp[w][1], l);
+        out[0] = M;
+        out[1] = l;
     }
 }
 
 // --------------------------------------------------------------- combine
 struct CombineArgs {
-    const float *partials;  // [n][B][H][nsplit][2 + 2D]
-    int nsplit, split_pages, max_blocks;
+    const float *partials;  // [n][B][H][nwg][2 + 2D], one partial per split workgroup
+    int nwg, split_pages, max_blocks;
     const int32_t *seq_lens;
     const void *q, *tail_k, *tail_v;   // [n][B][H][D]
     const float *rot;
@@ -452,46 +544,53 @@ struct CombineArgs {
     int is_res[RQ_MAX_LOOPS];
 };
 
+__device__ __forceinline__ float readlane_f(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// One workgroup per (head, loop call, 16 sequences); one wave per sequence.
 template <int D, bool KV_F32>
-__global__ __launch_bounds__(256) void rq_combine_kernel(CombineArgs a) {
+__global__ __launch_bounds__(1024) void rq_combine_kernel(CombineArgs a) {
     constexpr int QS = D + 1;
+    constexpr int PF = partial_floats(D);
     __shared__ float A[16 * QS];
     __shared__ float O[16 * QS];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, r = threadIdx.x >> 6;
     const int h = blockIdx.x, i = blockIdx.y, tile = blockIdx.z;
     const int B = a.B, H = a.H;
     const bool has_res = a.is_res[i] != 0;
-    constexpr int PF = 2 + 2 * D;
-
-    for (int j = 0; j < 4; ++j) {
-        const int r = wave + 4 * j;
-        const int b = tile * 16 + r;
-        float ar0 = 0.f, ar1 = 0.f, as0 = 0.f, as1 = 0.f;
-        const int c0 = lane, c1 = lane + 64;
-        if (b < B) {
-            int seq = a.seq_lens[b];
-            seq = seq < 0 ? 0 : (seq > a.max_blocks * 16 ? a.max_blocks * 16 : seq);
-            const int npages = (seq + 15) >> 4;
-            const int ns = (npages + a.split_pages - 1) / a.split_pages;
-            const int64_t row = ((int64_t)i * B + b) * H + h;
-            const float *P = a.partials + row * a.nsplit * PF;
-            float st = kNegInf;
-            if (a.tail_k) {
-                float d = 0.f;
-                if (c0 < D) d += load_kv<KV_F32>(a.q, row * D + c0) * load_kv<KV_F32>(a.tail_k, row * D + c0);
-                if (c1 < D) d += load_kv<KV_F32>(a.q, row * D + c1) * load_kv<KV_F32>(a.tail_k, row * D + c1);
-                st = wave_sum(d) * a.score_scale;
-            }
-            float mloc = kNegInf;
-            for (int s = lane; s < ns; s += 64) mloc = fmaxf(mloc, P[(int64_t)s * PF]);
-            const float M = fmaxf(wave_max(mloc), st);
-            if (M != kNegInf) {
-                float lloc = 0.f;
-                for (int s = lane; s < ns; s += 64) lloc += fast_exp2(P[(int64_t)s * PF] - M) * P[(int64_t)s * PF + 1];
-                float lsum = wave_sum(lloc);
-                for (int s = 0; s < ns; ++s) {
-                    const float *ps = P + (int64_t)s * PF;
-                    const float e = fast_exp2(ps[0] - M);
+    const int b = tile * 16 + r;
+    const int c0 = lane, c1 = lane + 64;
+    float ar0 = 0.f, ar1 = 0.f, as0 = 0.f, as1 = 0.f;
+    if (b < B) {
+        int seq = a.seq_lens[b];
+        seq = seq < 0 ? 0 : (seq > a.max_blocks * 16 ? a.max_blocks * 16 : seq);
+        const int npages = (seq + 15) >> 4;
+        const int nsw = (npages + a.split_pages - 1) / a.split_pages;   // wave splits with pages
+        const int ns = (nsw + kWaves - 1) / kWaves;                      // workgroup partials
+        const int64_t row = ((int64_t)i * B + b) * H + h;
+        const float *P = a.partials + row * a.nwg * PF;
+        float st = kNegInf;
+        if (a.tail_k) {
+            float d = 0.f;
+            if (c0 < D) d += load_kv<KV_F32>(a.q, row * D + c0) * load_kv<KV_F32>(a.tail_k, row * D + c0);
+            if (c1 < D) d += load_kv<KV_F32>(a.q, row * D + c1) * load_kv<KV_F32>(a.tail_k, row * D + c1);
+            st = wave_sum(d) * a.score_scale;
+        }
+        float mloc = kNegInf;
+        for (int s = lane; s < ns; s += 64) mloc = fmaxf(mloc, P[(int64_t)s * PF]);
+        const float M = fmaxf(wave_max(mloc), st);
+        if (M != kNegInf) {
+            float lloc = 0.f;
+            for (int cb = 0; cb < ns; cb += 64) {
+                const int s = cb + lane;
+                const float e_l = s < ns ? fast_exp2(P[(int64_t)s * PF] - M) : 0.f;
+                if (s < ns) lloc = fmaf(e_l, P[(int64_t)s * PF + 1], lloc);
+                const int cnt = min(64, ns - cb);
+#pragma unroll 8
+                for (int j = 0; j < cnt; ++j) {
+                    const float e = readlane_f(e_l, j);
+                    const float *ps = P + (int64_t)(cb + j) * PF;
                     if (c0 < D) ar0 = fmaf(e, ps[2 + c0], ar0);
                     if (c1 < D) ar1 = fmaf(e, ps[2 + c1], ar1);
                     if (has_res) {
@@ -499,43 +598,43 @@ __global__ __launch_bounds__(256) void rq_combine_kernel(CombineArgs a) {
                         if (c1 < D) as1 = fmaf(e, ps[2 + D + c1], as1);
                     }
                 }
-                if (a.tail_k) {
-                    const float pt = fast_exp2(st - M);
-                    lsum += pt;
-                    if (c0 < D) ar0 = fmaf(pt, load_kv<KV_F32>(a.tail_v, row * D + c0), ar0);
-                    if (c1 < D) ar1 = fmaf(pt, load_kv<KV_F32>(a.tail_v, row * D + c1), ar1);
-                }
-                const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
-                ar0 *= inv; ar1 *= inv; as0 *= inv; as1 *= inv;
             }
+            float lsum = wave_sum(lloc);
+            if (a.tail_k) {
+                const float pt = fast_exp2(st - M);
+                lsum += pt;
+                if (c0 < D) ar0 = fmaf(pt, load_kv<KV_F32>(a.tail_v, row * D + c0), ar0);
+                if (c1 < D) ar1 = fmaf(pt, load_kv<KV_F32>(a.tail_v, row * D + c1), ar1);
+            }
+            const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+            ar0 *= inv; ar1 *= inv; as0 *= inv; as1 *= inv;
         }
-        if (c0 < D) { O[r * QS + c0] = ar0; A[r * QS + c0] = as0; }
-        if (c1 < D) { O[r * QS + c1] = ar1; A[r * QS + c1] = as1; }
     }
+    if (c0 < D) { O[r * QS + c0] = ar0; A[r * QS + c0] = as0; }
+    if (c1 < D) { O[r * QS + c1] = ar1; A[r * QS + c1] = as1; }
     __syncthreads();
 
     if (has_res) {
-        // out = O + A * R_V  (row vector times R_V = R_V^T applied to the column)
-        const float *RV = a.rot + ((int64_t)h * 2 + 1) * D * D;
-        for (int nt = wave; nt < D / 16; nt += kWaves) {
+        // out = O + A * R_V (row vector times R_V = R_V^T applied to the column),
+        // v_mfma_f32_16x16x4f32: lane l supplies A[l%16][k0 + l/16], B[k0 + l/16][l%16]
+        // and receives D[4*(l/16)+v][l%16]; wave r computes output columns 16r..16r+15.
+        if (r < D / 16) {
+            const float *RV = a.rot + ((int64_t)h * 2 + 1) * D * D;
             floatx4 c = {0.f, 0.f, 0.f, 0.f};
-            const int n = nt * 16 + (lane & 15);
+            const int n = r * 16 + (lane & 15);
             for (int kk = 0; kk < D / 4; ++kk) {
                 const int k = 4 * kk + (lane >> 4);
                 c = __builtin_amdgcn_mfma_f32_16x16x4f32(A[(lane & 15) * QS + k], RV[(int64_t)k * D + n], c, 0, 0, 0);
             }
             for (int v = 0; v < 4; ++v) {
-                const int r = 4 * (lane >> 4) + v;
-                const int b = tile * 16 + r;
-                if (b < B) a.out[(((int64_t)i * B + b) * H + h) * D + n] = c[v] + O[r * QS + n];
+                const int rr = 4 * (lane >> 4) + v;
+                const int bb = tile * 16 + rr;
+                if (bb < B) a.out[(((int64_t)i * B + bb) * H + h) * D + n] = c[v] + O[rr * QS + n];
             }
         }
-    } else {
-        for (int e = threadIdx.x; e < 16 * D; e += 256) {
-            const int r = e / D, c = e % D;
-            const int b = tile * 16 + r;
-            if (b < B) a.out[(((int64_t)i * B + b) * H + h) * D + c] = O[r * QS + c];
-        }
+    } else if (b < B) {
+        if (c0 < D) a.out[(((int64_t)i * B + b) * H + h) * D + c0] = O[r * QS + c0];
+        if (c1 < D) a.out[(((int64_t)i * B + b) * H + h) * D + c1] = O[r * QS + c1];
     }
 }
 
@@ -567,8 +666,8 @@ hipError_t launch_decode_d(const DecodeCall &c) {
         ca.is_res[i] = res ? 1 : 0;
     }
     dim3 pgrid(g.H, c.n, tiles);
-    if (kvf) hipLaunchKernelGGL((rq_qprep_kernel<D, true>), pgrid, dim3(256), 0, c.stream, qa);
-    else hipLaunchKernelGGL((rq_qprep_kernel<D, false>), pgrid, dim3(256), 0, c.stream, qa);
+    if (kvf) hipLaunchKernelGGL((rq_qprep_kernel<D, true>), pgrid, dim3(1024), 0, c.stream, qa);
+    else hipLaunchKernelGGL((rq_qprep_kernel<D, false>), pgrid, dim3(1024), 0, c.stream, qa);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
 
@@ -583,7 +682,7 @@ hipError_t launch_decode_d(const DecodeCall &c) {
         s.meta_bytes = g.meta_bytes;
         s.block_table = c.block_table; s.max_blocks = c.max_blocks; s.seq_lens = c.seq_lens;
         s.qpack = c.qpack + (int64_t)i * c.B * g.H * qpack_bytes(D);
-        s.partials = c.partials + (int64_t)i * c.B * g.H * c.nsplit * partial_floats(D);
+        s.partials = c.partials + (int64_t)i * c.B * g.H * c.nwg * partial_floats(D);
         s.nsplit = c.nsplit; s.split_pages = c.split_pages;
         s.score_scale = score_scale;
         const int rb = (l == ref) ? 0 : g.bits[l];
@@ -595,12 +694,12 @@ hipError_t launch_decode_d(const DecodeCall &c) {
         if (last && c.ev_end && hipEventRecord(c.ev_end, c.stream) != hipSuccess) return hipErrorInvalidHandle;
     }
 
-    ca.partials = c.partials; ca.nsplit = c.nsplit; ca.split_pages = c.split_pages;
+    ca.partials = c.partials; ca.nwg = c.nwg; ca.split_pages = c.split_pages;
     ca.max_blocks = c.max_blocks; ca.seq_lens = c.seq_lens;
     ca.q = c.q; ca.tail_k = c.tail_k; ca.tail_v = c.tail_v; ca.rot = c.rot; ca.out = c.out;
     ca.B = c.B; ca.H = g.H; ca.score_scale = score_scale;
-    if (kvf) hipLaunchKernelGGL((rq_combine_kernel<D, true>), pgrid, dim3(256), 0, c.stream, ca);
-    else hipLaunchKernelGGL((rq_combine_kernel<D, false>), pgrid, dim3(256), 0, c.stream, ca);
+    if (kvf) hipLaunchKernelGGL((rq_combine_kernel<D, true>), pgrid, dim3(1024), 0, c.stream, ca);
+    else hipLaunchKernelGGL((rq_combine_kernel<D, false>), pgrid, dim3(1024), 0, c.stream, ca);
     return hipGetLastError();
 }
 

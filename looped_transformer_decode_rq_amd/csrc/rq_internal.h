@@ -31,6 +31,8 @@ __host__ __device__ constexpr int partial_floats(int D) { return 2 + 2 * D; }
 
 int auto_split_pages(int units, int max_blocks);
 
+constexpr int kSplitWaves = 4;   // waves (splits) per split-K workgroup
+
 // ------------------------------------------------------------------ launchers
 struct DecodeCall {
     const Geom *g;
@@ -46,8 +48,8 @@ struct DecodeCall {
     float softmax_scale;
     float *out;
     uint8_t *qpack;               // workspace: [n][B][H][qpack_bytes]
-    float *partials;              // workspace: [n][B][H][nsplit][partial_floats]
-    int split_pages, nsplit;
+    float *partials;              // workspace: [n][B][H][nwg][partial_floats]
+    int split_pages, nsplit, nwg;  // wave splits and split workgroups (4 waves each)
     hipEvent_t ev_begin, ev_end;
     hipStream_t stream;
 };
