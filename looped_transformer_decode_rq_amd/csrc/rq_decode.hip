@@ -91,6 +91,7 @@ __global__ __launch_bounds__(1024) void rq_qprep_kernel(QPrepArgs a) {
         const float *RK = a.rot + ((int64_t)h * 2 + 0) * D * D;
         floatx4 c = {0.f, 0.f, 0.f, 0.f};
         const int n = r * 16 + (lane & 15);
+#pragma unroll
         for (int kk = 0; kk < D / 4; ++kk) {
             const int k = 4 * kk + (lane >> 4);
             c = __builtin_amdgcn_mfma_f32_16x16x4f32(Q[(lane & 15) * QS + k], RK[(int64_t)n * D + k], c, 0, 0, 0);
@@ -622,6 +623,7 @@ __global__ __launch_bounds__(1024) void rq_combine_kernel(CombineArgs a) {
             const float *RV = a.rot + ((int64_t)h * 2 + 1) * D * D;
             floatx4 c = {0.f, 0.f, 0.f, 0.f};
             const int n = r * 16 + (lane & 15);
+#pragma unroll
             for (int kk = 0; kk < D / 4; ++kk) {
                 const int k = 4 * kk + (lane >> 4);
                 c = __builtin_amdgcn_mfma_f32_16x16x4f32(A[(lane & 15) * QS + k], RV[(int64_t)k * D + n], c, 0, 0, 0);

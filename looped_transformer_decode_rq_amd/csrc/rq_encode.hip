@@ -13,8 +13,9 @@
 // d = fma(-alpha_stored, ref, x), r = R d on the f64 matrix cores, group
 // min/max, step = (max-min)/(2^b-1), all casts round-to-nearest-even.
 //
-// One workgroup (4 waves) per (tile of 16 tokens, head, K|V). Lanes own two
-// adjacent channels. The rotation of the 16 residual rows of one loop is a
+// One workgroup (4 waves) per (tile of 16 tokens, head, K|V, residual loop);
+// the workgroup of residual loop 0 also writes the reference record. Lanes
+// own two adjacent channels. The rotation of the 16 residual rows is a
 // [16 x D] x [D x D]^T product on v_mfma_f64_16x16x4f64; R is read from
 // global memory (L2-resident), the rows live in LDS.
 #include "rq_device.h"
@@ -120,7 +121,9 @@ __global__ __launch_bounds__(kThreads) void rq_encode_pack_kernel(EncArgs a) {
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int tile = blockIdx.x, h = blockIdx.y, kv = blockIdx.z;
+    const int tile = blockIdx.x, h = blockIdx.y;
+    const int nres = a.L > 1 ? a.L - 1 : 1;
+    const int kv = blockIdx.z / nres, l = blockIdx.z % nres;   // l: this workgroup's residual loop
     const int D = a.D, L = a.L, H = a.H;
     const int c0 = 2 * lane, c1 = 2 * lane + 1;
     const bool active = c0 < D;
@@ -145,12 +148,12 @@ __global__ __launch_bounds__(kThreads) void rq_encode_pack_kernel(EncArgs a) {
         const double sq = wave_sum_f64(x0 * x0 + x1 * x1);
         if (lane == 0) refsq[t] = sq;
         uint8_t *rec = a.pool + (blk * H + h) * a.slab + a.loop_off[L - 1] + (int64_t)kv * a.rec[L - 1];
-        quantize_row<META_F32>(x0, x1, active, lane, D, a.G, 4, rec, a.code_bytes[L - 1], off, write);
+        quantize_row<META_F32>(x0, x1, active, lane, D, a.G, 4, rec, a.code_bytes[L - 1], off, write && l == 0);
     }
     __syncthreads();
 
-    // ---- residual loops
-    for (int l = 0; l < L - 1; ++l) {
+    // ---- residual loop l
+    if (L > 1) {
         // alpha (least squares), rounded to the meta dtype; d = x_l - alpha*x_ref
         for (int t = wave; t < kTT; t += 4) {
             const int tg = tile * kTT + t;
@@ -184,6 +187,7 @@ __global__ __launch_bounds__(kThreads) void rq_encode_pack_kernel(EncArgs a) {
         for (int nt = wave; nt < D / 16; nt += 4) {
             doublex4 c = {0.0, 0.0, 0.0, 0.0};
             const int n = nt * 16 + (lane & 15);
+#pragma unroll 8
             for (int kk = 0; kk < D / 4; ++kk) {
                 const int k = 4 * kk + (lane >> 4);
                 const double av = rows[(lane & 15) * kRowStride + k];
@@ -243,7 +247,7 @@ hipError_t launch_encode(const EncodeCall &c) {
     a.rot = c.rot;
     a.slots = c.slots;
     a.T = c.T;
-    dim3 grid((c.T + kTT - 1) / kTT, g.H, 2);
+    dim3 grid((c.T + kTT - 1) / kTT, g.H, 2 * (g.L > 1 ? g.L - 1 : 1));
     const bool kvf = g.kvdt == RQ_DTYPE_F32, mf = g.meta == RQ_DTYPE_F32;
     if (kvf && mf) hipLaunchKernelGGL((rq_encode_pack_kernel<true, true>), grid, dim3(kThreads), 0, c.stream, a);
     else if (kvf) hipLaunchKernelGGL((rq_encode_pack_kernel<true, false>), grid, dim3(kThreads), 0, c.stream, a);
