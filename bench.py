@@ -276,11 +276,12 @@ def main():
     res_ms = float(np.mean([m for l in res_loops for m in split_ms[l]]))
     ref_ms = float(np.mean(split_ms[L - 1]))
     nsplit = -(-rq["table"].shape[1] // args.split_pages)
+    nwg = -(-nsplit // 4)                       # one partial per 4-wave split workgroup
     qp = 64 + 4 * D
     res_bytes = (token_head_bytes(w, 0) * B * H * N + B * H * qp + B * N // 16 * 4
-                 + B * H * nsplit * (2 + 2 * D) * 4)
+                 + B * H * nwg * (2 + 2 * D) * 4)
     ref_bytes = (token_head_bytes(w, L - 1) * B * H * N + B * H * qp + B * N // 16 * 4
-                 + B * H * nsplit * (2 + 2 * D) * 4)
+                 + B * H * nwg * (2 + D) * 4)
     achieved = res_bytes / (res_ms * 1e-3) / 1e9
     # whole step: packed reads of the 4 calls + q/out/tails + rotations + encode traffic
     kvsz = 2 if w.kv_dtype == "bf16" else 4
