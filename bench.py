@@ -242,6 +242,9 @@ def main():
     ap.add_argument("--split-pages", type=int, default=0)
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after setup, copy a buffer of this many MiB device to device (a plain copy of known "
+                         "size, used to calibrate HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this path has no multi-GPU mode (asked for --gpus {args.gpus}); "
@@ -259,6 +262,13 @@ def main():
     args.split_pages = args.split_pages or _auto_split(B * H, table_w)
     log(f"workload {w.name}: setting up packed cache (split {args.split_pages} pages)")
     rq = setup_rq(w, dev, args.split_pages)
+    if args.copy_probe_mib:
+        src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     ev = HipEvents()
     res_loops = [l for l in range(L) if l != L - 1]
     pairs = {(k, l): (ev.create(), ev.create()) for k in range(args.steps) for l in range(L)}
