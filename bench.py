@@ -370,7 +370,7 @@ def main():
 def _auto_split(units, max_blocks):
     """Pages per split: the smallest power of two keeping ~16K waves per call."""
     sp = 1
-    while sp < 1024 and units * (-(-max_blocks // sp)) > 16384:
+    while sp < 64 and units * (-(-max_blocks // sp)) > 16384:
         sp *= 2
     return sp
 

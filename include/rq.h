@@ -91,7 +91,8 @@ typedef struct rq_layout {
 } rq_layout;
 
 /* Tuning and instrumentation for the decode calls (all fields optional).
- *   split_pages       pages per split-K partial; 0 = chosen by the library
+ *   split_pages       pages per split-K wave, 1..64 (packed decode; larger is
+ *                     RQ_ERR_UNSUPPORTED); 0 = chosen by the library
  *   event_main_begin  hipEvent_t recorded on `stream` just before the split-K
  *                     kernel of each loop, or NULL
  *   event_main_end    hipEvent_t recorded just after it, or NULL

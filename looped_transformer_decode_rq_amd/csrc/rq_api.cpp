@@ -50,7 +50,7 @@ rq_status make_geom(const rq_layout *lay, Geom *g) {
 int auto_split_pages(int units, int max_blocks) {
     // aim for at most ~16K waves in flight per loop call, pages per split a power of two
     int sp = 1;
-    while (sp < 1024 && (int64_t)units * ((max_blocks + sp - 1) / sp) > 16384) sp *= 2;
+    while (sp < kMaxSplitPages && (int64_t)units * ((max_blocks + sp - 1) / sp) > 16384) sp *= 2;
     return sp;
 }
 
@@ -130,7 +130,8 @@ rq_status rq_encode_pack(const rq_layout *layout, void *pool, const void *kv_new
 size_t rq_decode_workspace_bytes(const rq_layout *layout, int32_t n_loops, int32_t batch,
                                  int32_t max_blocks_per_seq, int32_t split_pages) {
     Geom g;
-    if (make_geom(layout, &g) != RQ_OK || n_loops < 1 || batch < 0 || max_blocks_per_seq < 1 || split_pages < 0)
+    if (make_geom(layout, &g) != RQ_OK || n_loops < 1 || batch < 0 || max_blocks_per_seq < 1 || split_pages < 0 ||
+        split_pages > kMaxSplitPages)
         return 0;
     const int sp = split_pages > 0 ? split_pages : auto_split_pages(batch * g.H, max_blocks_per_seq);
     return decode_ws(g, n_loops, batch, max_blocks_per_seq, sp);
@@ -157,6 +158,7 @@ rq_status rq_decode_attention_ex(const rq_layout *layout, const void *pool, cons
     if ((tail_k == nullptr) != (tail_v == nullptr)) return RQ_ERR_NULL;
     const int sp_req = opts ? opts->split_pages : 0;
     if (sp_req < 0) return RQ_ERR_SHAPE;
+    if (sp_req > kMaxSplitPages) return RQ_ERR_UNSUPPORTED;
     if (batch == 0) return RQ_OK;
     if (!pool || !q || !block_table || !seq_lens || !out || (any_res && !rot)) return RQ_ERR_NULL;
     if (!aligned(pool, 16)) return RQ_ERR_SHAPE;

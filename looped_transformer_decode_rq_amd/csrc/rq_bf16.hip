@@ -37,7 +37,7 @@ template <int D>
 __global__ __launch_bounds__(256) void rq_bf16_split_kernel(Bf16SplitArgs a) {
     constexpr int LPT = (D == 96) ? 2 : 4, CPL = D / LPT, PPI = (64 / LPT) / 16;
     constexpr int NW = CPL / 2;   // 32-bit words (bf16 pairs) per lane
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int split = blockIdx.x * kWaves + wave, h = blockIdx.y, b = blockIdx.z;
     if (split >= a.nsplit) return;
     const int H = a.H;

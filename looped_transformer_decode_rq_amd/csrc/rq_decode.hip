@@ -290,42 +290,83 @@ __device__ __forceinline__ void axpy_int2(float *acc, const uint32_t *codes, flo
     }
 }
 
-// Raw loads of one page step (16 or 32 tokens) for one lane; converted only
-// when consumed, so that the next step's loads stay in flight meanwhile.
-template <int D, int RB, bool META_F32>
-struct PageRegs {
-    using Ln = Lanes<D>;
-    static constexpr int REF_NW = Ln::CPL / 8;
-    static constexpr int RES_NW = RB ? Ln::CPL * RB / 32 : 1;
-    using SZ = typename std::conditional<META_F32, float2, uint32_t>::type;
-    using AL = typename std::conditional<META_F32, float, uint32_t>::type;
-    uint32_t ck[REF_NW], cv[REF_NW], rk[RES_NW], rv[RES_NW];
-    SZ mkr, mvr, mks, mvs;
-    AL ak, av;
-};
-
 __device__ __forceinline__ void sz_of(float2 v, float &s, float &z) { s = v.x; z = v.y; }
 __device__ __forceinline__ void sz_of(uint32_t v, float &s, float &z) {
     s = f16_to_f32((uint16_t)(v & 0xFFFF));
     z = f16_to_f32((uint16_t)(v >> 16));
 }
-__device__ __forceinline__ float al_of(float v) { return v; }
-__device__ __forceinline__ float al_of(uint32_t v) { return f16_to_f32((uint16_t)v); }
 
-template <int D, int RB, bool META_F32>
+// One LDS stage holds one page step's packed bytes exactly as stored, in the
+// order [ref K codes][ref V codes][res K codes][res V codes] (each for the
+// step's PPI pages) and then, per page, [ref K meta][ref V meta][res K meta +
+// alpha][res V meta + alpha]. It is filled by direct-to-LDS loads
+// (global_load_lds_dwordx4): each instruction moves 64 pieces of 16 bytes,
+// lane i's piece landing at m0 + 16*i.
+template <int D, int RB, bool META_F32, int G>
+struct StageGeom {
+    static constexpr int PPI = Lanes<D>::PPI;
+    static constexpr int MSZ = META_F32 ? 4 : 2;
+    static constexpr int NG = D / G;
+    static constexpr int CB_REF = 16 * D / 2;           // codes of one reference record
+    static constexpr int CB_RES = 16 * D * RB / 8;      // codes of one residual record
+    static constexpr int MB = 16 * NG * 2 * MSZ;        // (scale, zero) of one record
+    static constexpr int AB = RB ? 16 * MSZ : 0;        // alpha of one residual record
+    static constexpr int MP = 2 * MB + (RB ? 2 * (MB + AB) : 0);   // metadata of one page
+    static constexpr int O_RK = 0;
+    static constexpr int O_RV = PPI * CB_REF;
+    static constexpr int O_SK = 2 * PPI * CB_REF;
+    static constexpr int O_SV = O_SK + PPI * CB_RES;
+    static constexpr int O_M = O_SV + PPI * CB_RES;
+    static constexpr int BYTES = O_M + PPI * MP;
+    static constexpr int NP = BYTES / 16;               // 16-byte pieces
+    static constexpr int NI = (NP + 63) / 64;           // direct-to-LDS instructions per stage
+    static constexpr int LIVE_LAST = NP - 64 * (NI - 1);
+    // ring depth per wave: three stages when three 4-wave workgroups (stages
+    // plus the merge buffer) still fit in the CU's 160 KB of LDS, else two
+    static constexpr int NST =
+        3 * (kWaves * 3 * BYTES + kWaves * partial_floats(D) * 4) <= 160 * 1024 ? 3 : 2;
+    static_assert(BYTES % 16 == 0, "stage pieces are 16 bytes");
+};
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Wait until at most `ahead` page steps of NI loads each are still in flight
+// (ahead is wave-uniform, 0 <= ahead <= K).
+template <int K, int NI>
+__device__ __forceinline__ void wait_steps(int ahead) {
+    if constexpr (K == 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (ahead >= K) wait_vmcnt<K * NI>();
+        else wait_steps<K - 1, NI>(ahead);
+    }
+}
+
+// Split-K decode over packed pages. One wave per split (4 per workgroup, the
+// same (sequence, head)); each wave streams its pages through a ring of NST
+// LDS stages with NST-1 page steps in flight while one is consumed. The
+// direct-to-LDS loads and their wait counts are issued explicitly (the data
+// never occupies registers while in flight, and no wait is more conservative
+// than the ring needs).
+template <int D, int RB, bool META_F32, int G>
 __global__ __launch_bounds__(256) void rq_split_kernel(SplitArgs a) {
     using Ln = Lanes<D>;
-    using PR = PageRegs<D, RB, META_F32>;
+    using SG = StageGeom<D, RB, META_F32, G>;
     constexpr int LPT = Ln::LPT, CPL = Ln::CPL, PPI = Ln::PPI;
     constexpr int REF_NB = CPL / 2;                 // INT4 code bytes per lane
     constexpr int RES_NB = RB ? CPL * RB / 8 : 4;   // residual code bytes per lane
-    constexpr int REF_NW = PR::REF_NW, RES_NW = PR::RES_NW;
-    constexpr int msz = META_F32 ? 4 : 2;
+    constexpr int REF_NW = REF_NB / 4, RES_NW = RES_NB / 4;
+    constexpr int MSZ = SG::MSZ, NG = SG::NG, NST = SG::NST, NI = SG::NI;
     constexpr int PF = partial_floats(D);
+    using SZ = typename std::conditional<META_F32, float2, uint32_t>::type;
+    __shared__ __attribute__((aligned(16))) uint8_t stage[kWaves][NST][SG::BYTES];
     __shared__ float wp[kWaves][PF];
-    __shared__ __attribute__((aligned(16))) uint32_t limbs[D];
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // wave index made provably wave-uniform, so the page loop is a scalar loop
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int split = blockIdx.x * kWaves + wave;
     const int h = blockIdx.y, b = blockIdx.z;
     const int H = a.H;
@@ -334,31 +375,86 @@ __global__ __launch_bounds__(256) void rq_split_kernel(SplitArgs a) {
     const int npages = (seq + 15) >> 4;
     const int p0 = split * a.split_pages;
     const int p1 = min(npages, p0 + a.split_pages);   // p0 >= p1: this wave has no pages
+    const int cnt = p1 - p0;
+    const int steps = cnt > 0 ? (cnt + PPI - 1) / PPI : 0;
 
     const int tok_i = lane / LPT, q4 = lane % LPT;
     const int page_in_step = tok_i >> 4, tok = tok_i & 15;
-    const int ng = D / a.G;
-    const int g = (q4 * CPL) / a.G;
+    const int g = (q4 * CPL) / G;
 
-    // query record of (b, h), shared by the workgroup's waves: the limbs live
-    // in LDS (read once per page step), the scalars in registers
+    // query record of (b, h): scalars and this lane's limbs in registers
     const uint8_t *qp = a.qpack + ((int64_t)b * H + h) * qpack_bytes(D);
     const float sc_ref = ((const float *)qp)[0];
     const float sc_res = ((const float *)qp)[1];
     const int qs_ref = ((const int *)(qp + 16))[q4];
     const int qs_res = ((const int *)(qp + 32))[q4];
-    constexpr int NLIMB = (RB ? 2 : 1) * D / 2;       // dwords: ref limbs (+ residual limbs)
-    for (int i = threadIdx.x; i < NLIMB; i += 256) limbs[i] = ((const uint32_t *)(qp + 64))[i];
-    __syncthreads();
-    const uint4 *lref = (const uint4 *)&limbs[q4 * Ln::NDW * 4];
-    const uint4 *lres = (const uint4 *)&limbs[D / 2 + q4 * Ln::NDW * 4];
+    uint4 lrv[Ln::NDW], lsv[RB ? Ln::NDW : 1];
+    {
+        const uint4 *gq = (const uint4 *)(qp + 64);
+#pragma unroll
+        for (int k = 0; k < Ln::NDW; ++k) lrv[k] = gq[q4 * Ln::NDW + k];
+        if constexpr (RB != 0) {
+#pragma unroll
+            for (int k = 0; k < Ln::NDW; ++k) lsv[k] = gq[D / 8 + q4 * Ln::NDW + k];
+        }
+    }
 
-    const int32_t *table = a.block_table + (int64_t)b * a.max_blocks;
-    const int ref_meta = a.ref_code_bytes + (tok * ng + g) * 2 * msz;
-    const int res_meta = a.res_code_bytes + (tok * ng + g) * 2 * msz;
-    const int res_alpha = a.res_code_bytes + a.meta_bytes + tok * msz;
-    const int ref_codes = tok * (D / 2) + q4 * REF_NB;
-    const int res_codes = tok * (D * RB / 8) + q4 * RES_NB;
+    // Make the compiler complete these loads here: its wait-count tracking
+    // does not see the direct-to-LDS loads issued below, so a wait it placed at
+    // a first use inside the page loop would also drain the ring.
+#pragma unroll
+    for (int k = 0; k < Ln::NDW; ++k) __asm__ volatile("" ::"v"(lrv[k].x), "v"(lrv[k].y), "v"(lrv[k].z), "v"(lrv[k].w));
+    if constexpr (RB != 0) {
+#pragma unroll
+        for (int k = 0; k < Ln::NDW; ++k) __asm__ volatile("" ::"v"(lsv[k].x), "v"(lsv[k].y), "v"(lsv[k].z), "v"(lsv[k].w));
+    }
+    __asm__ volatile("" ::"v"(qs_ref), "v"(qs_res), "v"(sc_ref), "v"(sc_res));
+
+    // the split's block-table entries, one per lane (at most 64 pages per split)
+    int tbl = -1;
+    if (lane < cnt) {
+        tbl = a.block_table[(int64_t)b * a.max_blocks + p0 + lane];
+        if (tbl < 0 || tbl >= a.nblk) tbl = -1;
+    }
+
+    // this lane's piece of each direct-to-LDS instruction: (page of the step, byte offset in the slab)
+    int doff[NI], dpg[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int byte = 16 * (64 * i + lane);
+        int off = 0, pg = 0;
+        if (byte < SG::O_RV) {
+            pg = byte / SG::CB_REF; off = a.ref_off + byte % SG::CB_REF;
+        } else if (byte < SG::O_SK) {
+            const int w = byte - SG::O_RV; pg = w / SG::CB_REF; off = a.ref_off + a.ref_rec + w % SG::CB_REF;
+        } else if (RB != 0 && byte < SG::O_SV) {
+            const int w = byte - SG::O_SK; pg = w / SG::CB_RES; off = a.res_off + w % SG::CB_RES;
+        } else if (RB != 0 && byte < SG::O_M) {
+            const int w = byte - SG::O_SV; pg = w / SG::CB_RES; off = a.res_off + a.res_rec + w % SG::CB_RES;
+        } else if (byte < SG::BYTES) {
+            const int w0 = byte - SG::O_M; pg = w0 / SG::MP;
+            const int w = w0 % SG::MP;
+            if (w < SG::MB) off = a.ref_off + SG::CB_REF + w;
+            else if (w < 2 * SG::MB) off = a.ref_off + a.ref_rec + SG::CB_REF + (w - SG::MB);
+            else if (w < 3 * SG::MB + SG::AB) off = a.res_off + SG::CB_RES + (w - 2 * SG::MB);
+            else off = a.res_off + a.res_rec + SG::CB_RES + (w - 3 * SG::MB - SG::AB);
+        }
+        doff[i] = off;
+        dpg[i] = pg;
+    }
+
+    // this lane's reads inside a stage
+    const int o_ck = SG::O_RK + tok_i * (D / 2) + q4 * REF_NB;
+    const int o_cv = SG::O_RV + tok_i * (D / 2) + q4 * REF_NB;
+    const int o_rk = SG::O_SK + tok_i * (D * RB / 8) + q4 * RES_NB;
+    const int o_rv = SG::O_SV + tok_i * (D * RB / 8) + q4 * RES_NB;
+    const int o_m = SG::O_M + page_in_step * SG::MP;
+    const int o_mkr = o_m + (tok * NG + g) * 2 * MSZ;
+    const int o_mvr = o_mkr + SG::MB;
+    const int o_mks = o_mkr + 2 * SG::MB;
+    const int o_aks = o_m + 3 * SG::MB + tok * MSZ;
+    const int o_mvs = o_mkr + 3 * SG::MB + SG::AB;
+    const int o_avs = o_m + 4 * SG::MB + SG::AB + tok * MSZ;
 
     float m = kNegInf, lsum = 0.f, zr = 0.f, zs = 0.f;
     float accr[CPL], accs[RB ? CPL : 1];
@@ -367,59 +463,56 @@ __global__ __launch_bounds__(256) void rq_split_kernel(SplitArgs a) {
 #pragma unroll
     for (int i = 0; i < (RB ? CPL : 1); ++i) accs[i] = 0.f;
 
-    // block id of this lane's page in step `it` of a chunk whose table entries
-    // sit one per lane in `tbl` (-1 = no page / invalid id)
-    auto page_blk = [&](int tbl, int it) -> int {
-        if constexpr (PPI == 1) {
-            return __builtin_amdgcn_readlane(tbl, it);
-        } else {
-            const int lo = __builtin_amdgcn_readlane(tbl, 2 * it);
-            const int hi = __builtin_amdgcn_readlane(tbl, 2 * it + 1);
-            return page_in_step ? hi : lo;
-        }
-    };
-    auto load_page = [&](int blk, PR &r) {
-        const uint8_t *slab = a.pool + ((int64_t)(blk < 0 ? 0 : blk) * H + h) * a.slab;
-        const uint8_t *kr = slab + a.ref_off;
-        const uint8_t *vr = kr + a.ref_rec;
-        load_bytes<REF_NB>(kr + ref_codes, r.ck);
-        load_bytes<REF_NB>(vr + ref_codes, r.cv);
-        r.mkr = *(const typename PR::SZ *)(kr + ref_meta);
-        r.mvr = *(const typename PR::SZ *)(vr + ref_meta);
-        if constexpr (RB != 0) {
-            const uint8_t *ks = slab + a.res_off;
-            const uint8_t *vs = ks + a.res_rec;
-            load_bytes<RES_NB>(ks + res_codes, r.rk);
-            load_bytes<RES_NB>(vs + res_codes, r.rv);
-            r.mks = *(const typename PR::SZ *)(ks + res_meta);
-            r.mvs = *(const typename PR::SZ *)(vs + res_meta);
-            if constexpr (META_F32) {
-                r.ak = *(const float *)(ks + res_alpha);
-                r.av = *(const float *)(vs + res_alpha);
-            } else {
-                r.ak = *(const uint16_t *)(ks + res_alpha);
-                r.av = *(const uint16_t *)(vs + res_alpha);
+    auto blk_of = [&](int st, int pg) -> int { return __builtin_amdgcn_readlane(tbl, st * PPI + pg); };
+
+    // issue the NI direct-to-LDS loads of page step `st` into ring slot `slot`
+    // (a missing page reads block 0; its tokens are masked)
+    auto issue = [&](int st, int slot) {
+        // the slot's previous contents must have been read out before the
+        // loads can land on it
+        __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const int b0 = max(blk_of(st, 0), 0);
+        const uint8_t *base0 = a.pool + ((int64_t)b0 * H + h) * a.slab;
+        const uint8_t *base1 = base0;
+        if constexpr (PPI == 2) base1 = a.pool + ((int64_t)max(blk_of(st, 1), 0) * H + h) * a.slab;
+        const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&stage[wave][slot][0]);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const uint32_t m0v = lds + 1024u * i;
+            if (i < NI - 1 || SG::LIVE_LAST == 64 || lane < SG::LIVE_LAST) {
+                if constexpr (PPI == 1) {
+                    __asm__ volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                                     ::"s"(m0v), "v"((uint32_t)doff[i]), "s"(base0) : "memory", "m0");
+                } else {
+                    const uint8_t *src = (dpg[i] ? base1 : base0) + doff[i];
+                    __asm__ volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                                     ::"s"(m0v), "v"(src) : "memory", "m0");
+                }
             }
         }
     };
-    auto process = [&](const PR &r, bool valid) {
-        // keep the LDS limb reads inside the loop (re-read per step) instead
-        // of letting them be hoisted into 32 more registers
-        __asm__ volatile("" ::: "memory");
+
+    auto process = [&](int slot, bool valid) {
+        const uint8_t *S = &stage[wave][slot][0];
+        uint32_t ck[REF_NW], cv[REF_NW], rk[RES_NW], rv[RES_NW];
+        load_bytes<REF_NB>(S + o_ck, ck);
+        load_bytes<REF_NB>(S + o_cv, cv);
         float skr, zkr, svr, zvr;
-        sz_of(r.mkr, skr, zkr);
-        sz_of(r.mvr, svr, zvr);
+        sz_of(*(const SZ *)(S + o_mkr), skr, zkr);
+        sz_of(*(const SZ *)(S + o_mvr), svr, zvr);
         // score: q.x_hat = alpha*(s*sum q c + z*sum q) + (s_r*sum q' c_r + z_r*sum q')
-        const int dref = dot_int4<REF_NW>(r.ck, lref) + 8 * qs_ref;
+        const int dref = dot_int4<REF_NW>(ck, lrv) + 8 * qs_ref;
         float part = (skr * (float)dref + zkr * (float)qs_ref) * sc_ref;
         float av = 1.f, svs = 0.f, zvs = 0.f;
         if constexpr (RB != 0) {
+            load_bytes<RES_NB>(S + o_rk, rk);
+            load_bytes<RES_NB>(S + o_rv, rv);
             float sks, zks;
-            sz_of(r.mks, sks, zks);
-            sz_of(r.mvs, svs, zvs);
-            const float ak = al_of(r.ak);
-            av = al_of(r.av);
-            const int dres = (RB == 2) ? dot_int2<RES_NW>(r.rk, lres) : dot_int4<RES_NW>(r.rk, lres) + 8 * qs_res;
+            sz_of(*(const SZ *)(S + o_mks), sks, zks);
+            sz_of(*(const SZ *)(S + o_mvs), svs, zvs);
+            const float ak = load_meta1<META_F32>(S + o_aks);
+            av = load_meta1<META_F32>(S + o_avs);
+            const int dres = (RB == 2) ? dot_int2<RES_NW>(rk, lsv) : dot_int4<RES_NW>(rk, lsv) + 8 * qs_res;
             part = ak * part + (sks * (float)dres + zks * (float)qs_res) * sc_res;
         }
         float score = group_sum<LPT>(part) * a.score_scale;
@@ -441,42 +534,27 @@ __global__ __launch_bounds__(256) void rq_split_kernel(SplitArgs a) {
         const float pa = pr * av;
         const float wr = valid ? pa * svr : 0.f;
         zr += valid ? pa * zvr : 0.f;
-        axpy_int4<REF_NW>(accr, r.cv, wr);
+        axpy_int4<REF_NW>(accr, cv, wr);
         if constexpr (RB != 0) {
             const float ws = valid ? pr * svs : 0.f;
             zs += valid ? pr * zvs : 0.f;
-            if constexpr (RB == 2) axpy_int2<RES_NW>(accs, r.rv, ws);
-            else axpy_int4<RES_NW>(accs, r.rv, ws);
+            if constexpr (RB == 2) axpy_int2<RES_NW>(accs, rv, ws);
+            else axpy_int4<RES_NW>(accs, rv, ws);
         }
     };
 
-    for (int cbase = p0; cbase < p1; cbase += 64) {
-        const int cnt = min(64, p1 - cbase);
-        int tbl = -1;
-        if (lane < cnt) {
-            tbl = table[cbase + lane];
-            if (tbl < 0 || tbl >= a.nblk) tbl = -1;
-        }
-        const int steps = (cnt + PPI - 1) / PPI;
-        auto valid_of = [&](int it, int blk) {
-            const int pp = cbase + it * PPI + page_in_step;
-            return blk >= 0 && pp < p1 && pp * 16 + tok < seq;
-        };
-        // two page steps in flight: the loads of step it+1 are issued before
-        // step it is consumed. Loads are issued unconditionally (past the last
-        // step they re-read the last page, a cache hit) so that the wait
-        // counters stay exact on every path.
-        PR A, Bq;
-        int blkA = page_blk(tbl, 0), blkB;
-        load_page(blkA, A);
-        for (int it = 0; it < steps; it += 2) {
-            blkB = page_blk(tbl, min(it + 1, steps - 1));
-            load_page(blkB, Bq);
-            process(A, valid_of(it, blkA));
-            if (it + 1 >= steps) break;
-            blkA = page_blk(tbl, min(it + 2, steps - 1));
-            load_page(blkA, A);
-            process(Bq, valid_of(it + 1, blkB));
+    if (steps > 0) {
+#pragma unroll
+        for (int j = 0; j < NST - 1; ++j)
+            if (j < steps) issue(j, j);
+        for (int cur = 0; cur < steps; ++cur) {
+            if (cur + NST - 1 < steps) issue(cur + NST - 1, (cur + NST - 1) % NST);
+            wait_steps<NST - 1, NI>(min(NST - 1, steps - 1 - cur));
+            const int pp = p0 + cur * PPI + page_in_step;
+            int blk = blk_of(cur, 0);
+            if constexpr (PPI == 2) blk = page_in_step ? blk_of(cur, 1) : blk;
+            const bool valid = blk >= 0 && pp < p1 && pp * 16 + tok < seq;
+            process(cur % NST, valid);
         }
     }
 
@@ -643,12 +721,28 @@ __global__ __launch_bounds__(1024) void rq_combine_kernel(CombineArgs a) {
 // ------------------------------------------------------------- dispatch
 template <int D>
 hipError_t launch_split_d(const SplitArgs &s, int rb, bool mf, dim3 grid, hipStream_t st) {
-#define RQ_SPLIT(RB_, MF_) hipLaunchKernelGGL((rq_split_kernel<D, RB_, MF_>), grid, dim3(256), 0, st, s)
-    if (mf) {
-        if (rb == 0) RQ_SPLIT(0, true); else if (rb == 2) RQ_SPLIT(2, true); else RQ_SPLIT(4, true);
+#define RQ_SPLIT(RB_, MF_, G_) hipLaunchKernelGGL((rq_split_kernel<D, RB_, MF_, G_>), grid, dim3(256), 0, st, s)
+#define RQ_SPLIT_RB(MF_, G_)                          \
+    do {                                              \
+        if (rb == 0) RQ_SPLIT(0, MF_, G_);            \
+        else if (rb == 2) RQ_SPLIT(2, MF_, G_);       \
+        else RQ_SPLIT(4, MF_, G_);                    \
+    } while (0)
+#define RQ_SPLIT_G(G_)                                \
+    do {                                              \
+        if (mf) RQ_SPLIT_RB(true, G_);                \
+        else RQ_SPLIT_RB(false, G_);                  \
+    } while (0)
+    // group sizes per head dim as accepted by the layout check
+    if constexpr (D == 128) {
+        if (s.G == 32) RQ_SPLIT_G(32); else if (s.G == 64) RQ_SPLIT_G(64); else RQ_SPLIT_G(128);
+    } else if constexpr (D == 96) {
+        RQ_SPLIT_G(96);
     } else {
-        if (rb == 0) RQ_SPLIT(0, false); else if (rb == 2) RQ_SPLIT(2, false); else RQ_SPLIT(4, false);
+        if (s.G == 16) RQ_SPLIT_G(16); else if (s.G == 32) RQ_SPLIT_G(32); else RQ_SPLIT_G(64);
     }
+#undef RQ_SPLIT_G
+#undef RQ_SPLIT_RB
 #undef RQ_SPLIT
     return hipGetLastError();
 }

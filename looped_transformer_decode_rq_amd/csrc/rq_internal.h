@@ -32,6 +32,7 @@ __host__ __device__ constexpr int partial_floats(int D) { return 2 + 2 * D; }
 int auto_split_pages(int units, int max_blocks);
 
 constexpr int kSplitWaves = 4;   // waves (splits) per split-K workgroup
+constexpr int kMaxSplitPages = 64; // pages per split: one block-table entry per lane
 
 // ------------------------------------------------------------------ launchers
 struct DecodeCall {

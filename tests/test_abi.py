@@ -15,6 +15,7 @@ from conftest import ROOT
 
 import looped_transformer_decode_rq_amd as R
 from looped_transformer_decode_rq_amd import build as B
+from looped_transformer_decode_rq_amd._lib import RqDecodeOpts
 
 
 @pytest.fixture(scope="module")
@@ -137,6 +138,11 @@ def test_decode_validation(L):
     a = list(base)
     a[0] = ctypes.byref(bad)
     assert L.rq_decode_attention_ex(*a) == -3
+    # at most 64 pages per split wave: one block-table entry per lane
+    for sp, want in ((-1, -2), (65, -3)):
+        a = list(base)
+        a[16] = ctypes.byref(RqDecodeOpts(sp, 0, None, None))
+        assert L.rq_decode_attention_ex(*a) == want
 
 
 def test_encode_validation(L):
@@ -176,6 +182,7 @@ def test_workspace_sizes_monotone(L):
     assert 0 < a < b
     assert R.decode_workspace_bytes(lay, 1, 16, 2049, 8) > R.decode_workspace_bytes(lay, 1, 16, 2049, 64)
     assert R.decode_workspace_bytes(lay, 0, 16, 2049) == 0
+    assert R.decode_workspace_bytes(lay, 1, 16, 2049, 65) == 0      # at most 64 pages per split
 
 
 def test_binding_refuses_host_tensors(L):
