@@ -56,11 +56,15 @@ int auto_split_pages(int units, int max_blocks) {
 
 static int nsplit_of(int max_blocks, int sp) { return (max_blocks + sp - 1) / sp; }
 
-static int nwg_of(int max_blocks, int sp) { return (nsplit_of(max_blocks, sp) + kSplitWaves - 1) / kSplitWaves; }
+int partials_per_row(int n, int max_blocks, int sp) {
+    const int ns = nsplit_of(max_blocks, sp);
+    return n >= 2 ? ns : (ns + kSplitWaves - 1) / kSplitWaves;
+}
 
 static size_t decode_ws(const Geom &g, int n, int B, int max_blocks, int sp) {
     const size_t qp = round_up((size_t)n * B * g.H * qpack_bytes(g.D), 256);
-    const size_t parts = (size_t)n * B * g.H * nwg_of(max_blocks, sp) * partial_floats(g.D) * sizeof(float);
+    const size_t parts =
+        (size_t)n * B * g.H * partials_per_row(n, max_blocks, sp) * partial_floats(g.D) * sizeof(float);
     return qp + parts;
 }
 
@@ -177,7 +181,8 @@ rq_status rq_decode_attention_ex(const rq_layout *layout, const void *pool, cons
     c.softmax_scale = softmax_scale; c.out = out;
     c.qpack = (uint8_t *)workspace;
     c.partials = (float *)((uint8_t *)workspace + round_up((size_t)n_loops * batch * g.H * qpack_bytes(g.D), 256));
-    c.split_pages = sp; c.nsplit = nsplit_of(max_blocks_per_seq, sp); c.nwg = nwg_of(max_blocks_per_seq, sp);
+    c.split_pages = sp; c.nsplit = nsplit_of(max_blocks_per_seq, sp);
+    c.nparts = partials_per_row(n_loops, max_blocks_per_seq, sp);
     c.ev_begin = opts ? (hipEvent_t)opts->event_main_begin : nullptr;
     c.ev_end = opts ? (hipEvent_t)opts->event_main_end : nullptr;
     c.stream = (hipStream_t)stream;

@@ -24,6 +24,7 @@
 //   rq_combine   per (head, loop call, 16 sequences): log-sum-exp merge of the
 //                partials and the uncompressed tail token, then
 //                out = acc_ref/l + R_V^T (acc_res/l) on the f32 matrix cores.
+#include <algorithm>
 #include <type_traits>
 
 #include "rq_device.h"
@@ -296,12 +297,192 @@ __device__ __forceinline__ void sz_of(uint32_t v, float &s, float &z) {
     z = f16_to_f32((uint16_t)(v >> 16));
 }
 
+// ---- shared per-token arithmetic of the split kernels
+
+// Query state of one (loop call, sequence, head) held by each lane: the
+// fixed-point scales, the limb sums of the lane's channels and its limbs.
+template <int D>
+struct QueryRegs {
+    float sc_ref, sc_res;
+    int qs_ref, qs_res;
+    uint4 lrv[Lanes<D>::NDW], lsv[Lanes<D>::NDW];
+};
+
+// Online-softmax state of one lane: running max (log2 units), sum of weights,
+// the per-group zero terms and the V accumulators (reference, rotated residual).
+template <int D>
+struct SplitState {
+    float m, lsum, zr, zs;
+    float accr[Lanes<D>::CPL], accs[Lanes<D>::CPL];
+};
+
+template <int D, bool RES>
+__device__ __forceinline__ void load_query(const uint8_t *qp, int q4, QueryRegs<D> &q) {
+    using Ln = Lanes<D>;
+    q.sc_ref = ((const float *)qp)[0];
+    q.sc_res = ((const float *)qp)[1];
+    q.qs_ref = ((const int *)(qp + 16))[q4];
+    q.qs_res = ((const int *)(qp + 32))[q4];
+    const uint4 *gq = (const uint4 *)(qp + 64);
+#pragma unroll
+    for (int k = 0; k < Ln::NDW; ++k) q.lrv[k] = gq[q4 * Ln::NDW + k];
+    if constexpr (RES) {
+#pragma unroll
+        for (int k = 0; k < Ln::NDW; ++k) q.lsv[k] = gq[D / 8 + q4 * Ln::NDW + k];
+    }
+    // Make the compiler complete these loads here: its wait-count tracking
+    // does not see the direct-to-LDS loads issued later, so a wait it placed
+    // at a first use inside the page loop would also drain the ring.
+#pragma unroll
+    for (int k = 0; k < Ln::NDW; ++k)
+        __asm__ volatile("" ::"v"(q.lrv[k].x), "v"(q.lrv[k].y), "v"(q.lrv[k].z), "v"(q.lrv[k].w));
+    if constexpr (RES) {
+#pragma unroll
+        for (int k = 0; k < Ln::NDW; ++k)
+            __asm__ volatile("" ::"v"(q.lsv[k].x), "v"(q.lsv[k].y), "v"(q.lsv[k].z), "v"(q.lsv[k].w));
+    }
+    __asm__ volatile("" ::"v"(q.qs_ref), "v"(q.qs_res), "v"(q.sc_ref), "v"(q.sc_res));
+}
+
+template <int D>
+__device__ __forceinline__ void init_state(SplitState<D> &s) {
+    s.m = kNegInf; s.lsum = 0.f; s.zr = 0.f; s.zs = 0.f;
+#pragma unroll
+    for (int i = 0; i < Lanes<D>::CPL; ++i) { s.accr[i] = 0.f; s.accs[i] = 0.f; }
+}
+
+// One token slot of one lane (LPT lanes per token): score it from the codes in
+// LDS and fold it into the online softmax and both V accumulators.
+//   ck, cv      this lane's reference K / V code bytes
+//   mkr, mvr    the token's reference K / V (scale, zero) of this lane's group
+//   rk, rv      this lane's residual K / V code bytes (RB != 0)
+//   mks, mvs    residual (scale, zero); aks, avs residual alphas (RB != 0)
+template <int D, int RB, bool META_F32>
+__device__ __forceinline__ void token_step(const uint8_t *ck, const uint8_t *cv, const uint8_t *mkr,
+                                           const uint8_t *mvr, const uint8_t *rk, const uint8_t *rv,
+                                           const uint8_t *mks, const uint8_t *aks, const uint8_t *mvs,
+                                           const uint8_t *avs, bool valid, float score_scale,
+                                           const QueryRegs<D> &q, SplitState<D> &s) {
+    using Ln = Lanes<D>;
+    constexpr int LPT = Ln::LPT, CPL = Ln::CPL;
+    constexpr int REF_NB = CPL / 2;                 // INT4 code bytes per lane
+    constexpr int RES_NB = RB ? CPL * RB / 8 : 4;   // residual code bytes per lane
+    constexpr int REF_NW = REF_NB / 4, RES_NW = RES_NB / 4;
+    using SZ = typename std::conditional<META_F32, float2, uint32_t>::type;
+    uint32_t ckw[REF_NW], cvw[REF_NW], rkw[RES_NW], rvw[RES_NW];
+    load_bytes<REF_NB>(ck, ckw);
+    load_bytes<REF_NB>(cv, cvw);
+    float skr, zkr, svr, zvr;
+    sz_of(*(const SZ *)mkr, skr, zkr);
+    sz_of(*(const SZ *)mvr, svr, zvr);
+    // score: q.x_hat = alpha*(s*sum q c + z*sum q) + (s_r*sum q' c_r + z_r*sum q')
+    const int dref = dot_int4<REF_NW>(ckw, q.lrv) + 8 * q.qs_ref;
+    float part = (skr * (float)dref + zkr * (float)q.qs_ref) * q.sc_ref;
+    float av = 1.f, svs = 0.f, zvs = 0.f;
+    if constexpr (RB != 0) {
+        load_bytes<RES_NB>(rk, rkw);
+        load_bytes<RES_NB>(rv, rvw);
+        float sks, zks;
+        sz_of(*(const SZ *)mks, sks, zks);
+        sz_of(*(const SZ *)mvs, svs, zvs);
+        const float ak = load_meta1<META_F32>(aks);
+        av = load_meta1<META_F32>(avs);
+        const int dres = (RB == 2) ? dot_int2<RES_NW>(rkw, q.lsv) : dot_int4<RES_NW>(rkw, q.lsv) + 8 * q.qs_res;
+        part = ak * part + (sks * (float)dres + zks * (float)q.qs_res) * q.sc_res;
+    }
+    float score = group_sum<LPT>(part) * score_scale;
+    score = valid ? score : kNegInf;
+    // online softmax, rescaled only when a score beats m by 2^8
+    if (__any(score > s.m + kRescaleThresh)) {
+        const float mn = fmaxf(s.m, wave_max(score));
+        const float f = fast_exp2(s.m - mn);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) s.accr[i] *= f;
+        if constexpr (RB != 0) {
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) s.accs[i] *= f;
+        }
+        s.zr *= f; s.zs *= f; s.lsum *= f;
+        s.m = mn;
+    }
+    const float pr = fast_exp2(score - s.m);
+    s.lsum += pr;
+    // V: acc_ref += p*alpha*s*c (+ p*alpha*z per group), acc_res in rotated space
+    const float pa = pr * av;
+    const float wr = valid ? pa * svr : 0.f;
+    s.zr += valid ? pa * zvr : 0.f;
+    axpy_int4<REF_NW>(s.accr, cvw, wr);
+    if constexpr (RB != 0) {
+        const float ws = valid ? pr * svs : 0.f;
+        s.zs += valid ? pr * zvs : 0.f;
+        if constexpr (RB == 2) axpy_int2<RES_NW>(s.accs, rvw, ws);
+        else axpy_int4<RES_NW>(s.accs, rvw, ws);
+    }
+}
+
+// Fold the per-group zero terms into the accumulators and sum them (and the
+// weights) over the wave's token slots; lanes q4 = 0..LPT-1 then hold the
+// wave's totals for their channels.
+template <int D, bool RES>
+__device__ __forceinline__ void reduce_slots(SplitState<D> &s) {
+    constexpr int LPT = Lanes<D>::LPT, CPL = Lanes<D>::CPL;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) s.accr[i] += s.zr;
+    if constexpr (RES) {
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) s.accs[i] += s.zs;
+    }
+#pragma unroll
+    for (int off = LPT; off < 64; off <<= 1) {
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) s.accr[i] += __shfl_xor(s.accr[i], off, 64);
+        if constexpr (RES) {
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) s.accs[i] += __shfl_xor(s.accs[i], off, 64);
+        }
+        s.lsum += __shfl_xor(s.lsum, off, 64);
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Wait until at most `ahead` page steps of NI loads each are still in flight
+// (ahead is wave-uniform, 0 <= ahead <= K).
+template <int K, int NI>
+__device__ __forceinline__ void wait_steps(int ahead) {
+    if constexpr (K == 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (ahead >= K) wait_vmcnt<K * NI>();
+        else wait_steps<K - 1, NI>(ahead);
+    }
+}
+
+// One direct-to-LDS load of 16 bytes per active lane: lane i's bytes land at
+// lds + 16*i (lds is wave-uniform).
+__device__ __forceinline__ void dma16(uint32_t lds, const uint8_t *base, uint32_t off) {
+    __asm__ volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                     ::"s"(lds), "v"(off), "s"(base) : "memory", "m0");
+}
+__device__ __forceinline__ void dma16(uint32_t lds, const uint8_t *src) {
+    __asm__ volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                     ::"s"(lds), "v"(src) : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
+}
+
+// ---- per-loop split kernel
+
 // One LDS stage holds one page step's packed bytes exactly as stored, in the
 // order [ref K codes][ref V codes][res K codes][res V codes] (each for the
 // step's PPI pages) and then, per page, [ref K meta][ref V meta][res K meta +
 // alpha][res V meta + alpha]. It is filled by direct-to-LDS loads
-// (global_load_lds_dwordx4): each instruction moves 64 pieces of 16 bytes,
-// lane i's piece landing at m0 + 16*i.
+// (global_load_lds_dwordx4): each instruction moves 64 pieces of 16 bytes.
 template <int D, int RB, bool META_F32, int G>
 struct StageGeom {
     static constexpr int PPI = Lanes<D>::PPI;
@@ -328,40 +509,21 @@ struct StageGeom {
     static_assert(BYTES % 16 == 0, "stage pieces are 16 bytes");
 };
 
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// Wait until at most `ahead` page steps of NI loads each are still in flight
-// (ahead is wave-uniform, 0 <= ahead <= K).
-template <int K, int NI>
-__device__ __forceinline__ void wait_steps(int ahead) {
-    if constexpr (K == 0) {
-        wait_vmcnt<0>();
-    } else {
-        if (ahead >= K) wait_vmcnt<K * NI>();
-        else wait_steps<K - 1, NI>(ahead);
-    }
-}
-
-// Split-K decode over packed pages. One wave per split (4 per workgroup, the
-// same (sequence, head)); each wave streams its pages through a ring of NST
-// LDS stages with NST-1 page steps in flight while one is consumed. The
-// direct-to-LDS loads and their wait counts are issued explicitly (the data
-// never occupies registers while in flight, and no wait is more conservative
-// than the ring needs).
+// Split-K decode of one loop over packed pages. One wave per split (4 per
+// workgroup, the same (sequence, head)); each wave streams its pages through
+// a ring of NST LDS stages with NST-1 page steps in flight while one is
+// consumed. The direct-to-LDS loads and their wait counts are issued
+// explicitly (the data never occupies registers while in flight, and no wait
+// is more conservative than the ring needs).
 template <int D, int RB, bool META_F32, int G>
 __global__ __launch_bounds__(256) void rq_split_kernel(SplitArgs a) {
     using Ln = Lanes<D>;
     using SG = StageGeom<D, RB, META_F32, G>;
     constexpr int LPT = Ln::LPT, CPL = Ln::CPL, PPI = Ln::PPI;
-    constexpr int REF_NB = CPL / 2;                 // INT4 code bytes per lane
-    constexpr int RES_NB = RB ? CPL * RB / 8 : 4;   // residual code bytes per lane
-    constexpr int REF_NW = REF_NB / 4, RES_NW = RES_NB / 4;
+    constexpr int REF_NB = CPL / 2;
+    constexpr int RES_NB = RB ? CPL * RB / 8 : 4;
     constexpr int MSZ = SG::MSZ, NG = SG::NG, NST = SG::NST, NI = SG::NI;
     constexpr int PF = partial_floats(D);
-    using SZ = typename std::conditional<META_F32, float2, uint32_t>::type;
     __shared__ __attribute__((aligned(16))) uint8_t stage[kWaves][NST][SG::BYTES];
     __shared__ float wp[kWaves][PF];
 
@@ -373,6 +535,9 @@ __global__ __launch_bounds__(256) void rq_split_kernel(SplitArgs a) {
     int seq = a.seq_lens[b];
     seq = seq < 0 ? 0 : (seq > a.max_blocks * 16 ? a.max_blocks * 16 : seq);
     const int npages = (seq + 15) >> 4;
+    // a workgroup none of whose splits has a page writes nothing (the combine
+    // reads only the partials of workgroups that have pages)
+    if (blockIdx.x * kWaves * a.split_pages >= npages) return;
     const int p0 = split * a.split_pages;
     const int p1 = min(npages, p0 + a.split_pages);   // p0 >= p1: this wave has no pages
     const int cnt = p1 - p0;
@@ -382,33 +547,8 @@ __global__ __launch_bounds__(256) void rq_split_kernel(SplitArgs a) {
     const int page_in_step = tok_i >> 4, tok = tok_i & 15;
     const int g = (q4 * CPL) / G;
 
-    // query record of (b, h): scalars and this lane's limbs in registers
-    const uint8_t *qp = a.qpack + ((int64_t)b * H + h) * qpack_bytes(D);
-    const float sc_ref = ((const float *)qp)[0];
-    const float sc_res = ((const float *)qp)[1];
-    const int qs_ref = ((const int *)(qp + 16))[q4];
-    const int qs_res = ((const int *)(qp + 32))[q4];
-    uint4 lrv[Ln::NDW], lsv[RB ? Ln::NDW : 1];
-    {
-        const uint4 *gq = (const uint4 *)(qp + 64);
-#pragma unroll
-        for (int k = 0; k < Ln::NDW; ++k) lrv[k] = gq[q4 * Ln::NDW + k];
-        if constexpr (RB != 0) {
-#pragma unroll
-            for (int k = 0; k < Ln::NDW; ++k) lsv[k] = gq[D / 8 + q4 * Ln::NDW + k];
-        }
-    }
-
-    // Make the compiler complete these loads here: its wait-count tracking
-    // does not see the direct-to-LDS loads issued below, so a wait it placed at
-    // a first use inside the page loop would also drain the ring.
-#pragma unroll
-    for (int k = 0; k < Ln::NDW; ++k) __asm__ volatile("" ::"v"(lrv[k].x), "v"(lrv[k].y), "v"(lrv[k].z), "v"(lrv[k].w));
-    if constexpr (RB != 0) {
-#pragma unroll
-        for (int k = 0; k < Ln::NDW; ++k) __asm__ volatile("" ::"v"(lsv[k].x), "v"(lsv[k].y), "v"(lsv[k].z), "v"(lsv[k].w));
-    }
-    __asm__ volatile("" ::"v"(qs_ref), "v"(qs_res), "v"(sc_ref), "v"(sc_res));
+    QueryRegs<D> q;
+    load_query<D, RB != 0>(a.qpack + ((int64_t)b * H + h) * qpack_bytes(D), q4, q);
 
     // the split's block-table entries, one per lane (at most 64 pages per split)
     int tbl = -1;
@@ -456,12 +596,8 @@ __global__ __launch_bounds__(256) void rq_split_kernel(SplitArgs a) {
     const int o_mvs = o_mkr + 3 * SG::MB + SG::AB;
     const int o_avs = o_m + 4 * SG::MB + SG::AB + tok * MSZ;
 
-    float m = kNegInf, lsum = 0.f, zr = 0.f, zs = 0.f;
-    float accr[CPL], accs[RB ? CPL : 1];
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) accr[i] = 0.f;
-#pragma unroll
-    for (int i = 0; i < (RB ? CPL : 1); ++i) accs[i] = 0.f;
+    SplitState<D> s;
+    init_state<D>(s);
 
     auto blk_of = [&](int st, int pg) -> int { return __builtin_amdgcn_readlane(tbl, st * PPI + pg); };
 
@@ -475,71 +611,13 @@ __global__ __launch_bounds__(256) void rq_split_kernel(SplitArgs a) {
         const uint8_t *base0 = a.pool + ((int64_t)b0 * H + h) * a.slab;
         const uint8_t *base1 = base0;
         if constexpr (PPI == 2) base1 = a.pool + ((int64_t)max(blk_of(st, 1), 0) * H + h) * a.slab;
-        const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&stage[wave][slot][0]);
+        const uint32_t lds = lds_addr(&stage[wave][slot][0]);
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-            const uint32_t m0v = lds + 1024u * i;
             if (i < NI - 1 || SG::LIVE_LAST == 64 || lane < SG::LIVE_LAST) {
-                if constexpr (PPI == 1) {
-                    __asm__ volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-                                     ::"s"(m0v), "v"((uint32_t)doff[i]), "s"(base0) : "memory", "m0");
-                } else {
-                    const uint8_t *src = (dpg[i] ? base1 : base0) + doff[i];
-                    __asm__ volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-                                     ::"s"(m0v), "v"(src) : "memory", "m0");
-                }
+                if constexpr (PPI == 1) dma16(lds + 1024u * i, base0, (uint32_t)doff[i]);
+                else dma16(lds + 1024u * i, (dpg[i] ? base1 : base0) + doff[i]);
             }
-        }
-    };
-
-    auto process = [&](int slot, bool valid) {
-        const uint8_t *S = &stage[wave][slot][0];
-        uint32_t ck[REF_NW], cv[REF_NW], rk[RES_NW], rv[RES_NW];
-        load_bytes<REF_NB>(S + o_ck, ck);
-        load_bytes<REF_NB>(S + o_cv, cv);
-        float skr, zkr, svr, zvr;
-        sz_of(*(const SZ *)(S + o_mkr), skr, zkr);
-        sz_of(*(const SZ *)(S + o_mvr), svr, zvr);
-        // score: q.x_hat = alpha*(s*sum q c + z*sum q) + (s_r*sum q' c_r + z_r*sum q')
-        const int dref = dot_int4<REF_NW>(ck, lrv) + 8 * qs_ref;
-        float part = (skr * (float)dref + zkr * (float)qs_ref) * sc_ref;
-        float av = 1.f, svs = 0.f, zvs = 0.f;
-        if constexpr (RB != 0) {
-            load_bytes<RES_NB>(S + o_rk, rk);
-            load_bytes<RES_NB>(S + o_rv, rv);
-            float sks, zks;
-            sz_of(*(const SZ *)(S + o_mks), sks, zks);
-            sz_of(*(const SZ *)(S + o_mvs), svs, zvs);
-            const float ak = load_meta1<META_F32>(S + o_aks);
-            av = load_meta1<META_F32>(S + o_avs);
-            const int dres = (RB == 2) ? dot_int2<RES_NW>(rk, lsv) : dot_int4<RES_NW>(rk, lsv) + 8 * qs_res;
-            part = ak * part + (sks * (float)dres + zks * (float)qs_res) * sc_res;
-        }
-        float score = group_sum<LPT>(part) * a.score_scale;
-        score = valid ? score : kNegInf;
-        // online softmax, rescaled only when a score beats m by 2^8
-        if (__any(score > m + kRescaleThresh)) {
-            const float mn = fmaxf(m, wave_max(score));
-            const float f = fast_exp2(m - mn);
-#pragma unroll
-            for (int i = 0; i < CPL; ++i) accr[i] *= f;
-#pragma unroll
-            for (int i = 0; i < (RB ? CPL : 1); ++i) accs[i] *= f;
-            zr *= f; zs *= f; lsum *= f;
-            m = mn;
-        }
-        const float pr = fast_exp2(score - m);
-        lsum += pr;
-        // V: acc_ref += p*alpha*s*c (+ p*alpha*z per group), acc_res in rotated space
-        const float pa = pr * av;
-        const float wr = valid ? pa * svr : 0.f;
-        zr += valid ? pa * zvr : 0.f;
-        axpy_int4<REF_NW>(accr, cv, wr);
-        if constexpr (RB != 0) {
-            const float ws = valid ? pr * svs : 0.f;
-            zs += valid ? pr * zvs : 0.f;
-            if constexpr (RB == 2) axpy_int2<RES_NW>(accs, rv, ws);
-            else axpy_int4<RES_NW>(accs, rv, ws);
         }
     };
 
@@ -554,52 +632,39 @@ __global__ __launch_bounds__(256) void rq_split_kernel(SplitArgs a) {
             int blk = blk_of(cur, 0);
             if constexpr (PPI == 2) blk = page_in_step ? blk_of(cur, 1) : blk;
             const bool valid = blk >= 0 && pp < p1 && pp * 16 + tok < seq;
-            process(cur % NST, valid);
+            const uint8_t *S = &stage[wave][cur % NST][0];
+            token_step<D, RB, META_F32>(S + o_ck, S + o_cv, S + o_mkr, S + o_mvr, S + o_rk, S + o_rv,
+                                        S + o_mks, S + o_aks, S + o_mvs, S + o_avs, valid, a.score_scale,
+                                        q, s);
         }
     }
 
-    // ---- fold the per-group zero terms, reduce over the wave's token slots
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) accr[i] += zr;
-    if constexpr (RB != 0) {
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) accs[i] += zs;
-    }
-#pragma unroll
-    for (int off = LPT; off < 64; off <<= 1) {
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) accr[i] += __shfl_xor(accr[i], off, 64);
-        if constexpr (RB != 0) {
-#pragma unroll
-            for (int i = 0; i < CPL; ++i) accs[i] += __shfl_xor(accs[i], off, 64);
-        }
-        lsum += __shfl_xor(lsum, off, 64);
-    }
+    reduce_slots<D, RB != 0>(s);
     // ---- merge the workgroup's 4 wave partials (log-sum-exp), one partial per workgroup
     if (lane < LPT) {
-        if (lane == 0) { wp[wave][0] = m; wp[wave][1] = lsum; }
+        if (lane == 0) { wp[wave][0] = s.m; wp[wave][1] = s.lsum; }
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) wp[wave][2 + q4 * CPL + i] = accr[i];
+        for (int i = 0; i < CPL; ++i) wp[wave][2 + q4 * CPL + i] = s.accr[i];
         if constexpr (RB != 0) {
 #pragma unroll
-            for (int i = 0; i < CPL; ++i) wp[wave][2 + D + q4 * CPL + i] = accs[i];
+            for (int i = 0; i < CPL; ++i) wp[wave][2 + D + q4 * CPL + i] = s.accs[i];
         }
     }
     __syncthreads();
     float M = kNegInf;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wp[w][0]);
-    if (M == kNegInf) return;                      // no page in this workgroup
+    // every token of the workgroup masked (invalid block ids): an empty partial
     float e[kWaves];
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) e[w] = fast_exp2(wp[w][0] - M);
+    for (int w = 0; w < kWaves; ++w) e[w] = M == kNegInf ? 0.f : fast_exp2(wp[w][0] - M);
     float *out = a.partials + (((int64_t)b * H + h) * gridDim.x + blockIdx.x) * PF;
     constexpr int NV = RB ? 2 * D : D;
     for (int v = threadIdx.x; v < NV; v += 256) {
-        float s = 0.f;
+        float acc = 0.f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) s = fmaf(e[w], wp[w][2 + v], s);
-        out[2 + v] = s;
+        for (int w = 0; w < kWaves; ++w) acc = fmaf(e[w], wp[w][2 + v], acc);
+        out[2 + v] = acc;
     }
     if (threadIdx.x == 0) {
         float l = 0.f;
@@ -610,10 +675,251 @@ __global__ __launch_bounds__(256) void rq_split_kernel(SplitArgs a) {
     }
 }
 
+// ---- multi-loop split kernel
+
+struct MultiArgs {
+    const uint8_t *pool;
+    int64_t slab;
+    int H, nblk;
+    int ref_off, ref_rec;
+    int nl;                                   // loop calls of this group = waves per workgroup
+    int res_off[kMaxMultiLoops], res_rec[kMaxMultiLoops], rb[kMaxMultiLoops];   // rb 0: reference loop
+    const int32_t *block_table;
+    int max_blocks;
+    const int32_t *seq_lens;
+    const uint8_t *qpack;     // group's first call: [nl][B][H][qpack_bytes]
+    float *partials;          // group's first call: [nl][B][H][nsplit][2 + 2D]
+    int B, nsplit, split_pages, nst;
+    float score_scale;
+};
+
+// Stage layout of the multi-loop kernel. The reference stage is shared by the
+// workgroup: [ref K codes][ref V codes] for the step's PPI pages, then per
+// page [ref K meta][ref V meta]. Each wave has a private residual stage for
+// its own loop's bits rb: [res K codes][res V codes], then per page
+// [res K meta][K alpha][res V meta][V alpha] (each record's tail as stored).
+template <int D, bool META_F32, int G, int RBMAX>
+struct MultiGeom {
+    static constexpr int PPI = Lanes<D>::PPI;
+    static constexpr int MSZ = META_F32 ? 4 : 2;
+    static constexpr int NG = D / G;
+    static constexpr int CB_REF = 16 * D / 2;
+    static constexpr int MB = 16 * NG * 2 * MSZ;
+    static constexpr int AB = 16 * MSZ;
+    static constexpr int R_CV = PPI * CB_REF;
+    static constexpr int R_M = 2 * PPI * CB_REF;
+    static constexpr int REF_BYTES = R_M + PPI * 2 * MB;
+    static constexpr int P_REF = REF_BYTES / 16;
+    __host__ __device__ static constexpr int cb_res(int rb) { return 16 * D * rb / 8; }
+    __host__ __device__ static constexpr int smp() { return 2 * (MB + AB); }
+    __host__ __device__ static constexpr int res_bytes(int rb) { return rb ? 2 * PPI * cb_res(rb) + PPI * smp() : 0; }
+    static constexpr int RES_MAX = 2 * PPI * (16 * D * RBMAX / 8) + PPI * 2 * (MB + AB);
+    // loads per wave and step: the wave's share of the reference (at least
+    // two waves share it) and its residual, padded to fixed counts
+    static constexpr int NIR = ((P_REF + 1) / 2 + 63) / 64;
+    static constexpr int NIS = (RES_MAX / 16 + 63) / 64;
+    static constexpr int NIW = NIR + NIS;
+    static_assert(REF_BYTES % 16 == 0 && RES_MAX % 16 == 0, "stage pieces are 16 bytes");
+};
+
+// Split-K decode of several loops at once (the same sequences and heads, one
+// query per loop): one workgroup per (split, head, sequence) with one wave per
+// loop call. Each reference page is loaded once into the shared stage and
+// scored by every wave; each wave adds its own loop's residual. The ring has
+// nst stages; every wave issues exactly NIW direct-to-LDS loads per step
+// (short shares are padded with a one-lane load into the wave's scratch
+// slot), so its waits are fixed counts, and one barrier per step publishes
+// the landed stage to all waves and frees the slot for reuse.
+template <int D, bool META_F32, int G, int RBMAX>
+__global__ __launch_bounds__(64 * kMaxMultiLoops) void rq_multi_kernel(MultiArgs a) {
+    using Ln = Lanes<D>;
+    using MG = MultiGeom<D, META_F32, G, RBMAX>;
+    constexpr int LPT = Ln::LPT, CPL = Ln::CPL, PPI = Ln::PPI;
+    constexpr int REF_NB = CPL / 2;
+    constexpr int MSZ = MG::MSZ, NG = MG::NG, NIR = MG::NIR, NIS = MG::NIS, NIW = MG::NIW;
+    constexpr int PF = partial_floats(D);
+    constexpr int NST_MAX = 8;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int H = a.H, nl = a.nl, nst = a.nst;
+    int seq = a.seq_lens[b];
+    seq = seq < 0 ? 0 : (seq > a.max_blocks * 16 ? a.max_blocks * 16 : seq);
+    const int npages = (seq + 15) >> 4;
+    const int p0 = split * a.split_pages;
+    if (p0 >= npages) return;                     // the whole workgroup: no page in this split
+    const int p1 = min(npages, p0 + a.split_pages);
+    const int cnt = p1 - p0;
+    const int steps = (cnt + PPI - 1) / PPI;
+
+    const int rb = __builtin_amdgcn_readfirstlane(a.rb[wave]);
+    const int res_off = a.res_off[wave], res_rec = a.res_rec[wave];
+    const int tok_i = lane / LPT, q4 = lane % LPT;
+    const int page_in_step = tok_i >> 4, tok = tok_i & 15;
+    const int g = (q4 * CPL) / G;
+
+    QueryRegs<D> q;
+    load_query<D, true>(a.qpack + (((int64_t)wave * a.B + b) * H + h) * qpack_bytes(D), q4, q);
+
+    int tbl = -1;
+    if (lane < cnt) {
+        tbl = a.block_table[(int64_t)b * a.max_blocks + p0 + lane];
+        if (tbl < 0 || tbl >= a.nblk) tbl = -1;
+    }
+
+    // LDS: nst shared reference stages, then nst private residual stages per
+    // wave, then one 16-byte scratch slot per wave for the padding loads
+    const int ref_stage = MG::REF_BYTES, res_stage = MG::RES_MAX;
+    uint8_t *ref_base = smem;
+    uint8_t *res_base = smem + nst * ref_stage + wave * nst * res_stage;
+    const uint32_t junk = lds_addr(smem + nst * (ref_stage + nl * res_stage) + 16 * wave);
+
+    // this wave's share of the reference pieces [r0, r0 + rcount)
+    const int rq = (MG::P_REF + nl - 1) / nl;
+    const int r0 = wave * rq;
+    const int rcount = max(0, min(MG::P_REF, r0 + rq) - r0);
+    const int cbr = MG::cb_res(rb);
+    const int pres = MG::res_bytes(rb) / 16;
+
+    // per instruction: destination offset in the stage (-1: padding), and
+    // this lane's (page of the step, byte offset in the slab)
+    int rdst[NIR], rdoff[NIR], rdpg[NIR];
+    bool rlive[NIR];
+#pragma unroll
+    for (int j = 0; j < NIR; ++j) {
+        const bool pad = 64 * j >= rcount;
+        rdst[j] = pad ? -1 : 16 * (r0 + 64 * j);
+        rlive[j] = pad ? lane == 0 : 64 * j + lane < rcount;
+        const int byte = 16 * (r0 + 64 * j + lane);
+        int off = 0, pg = 0;
+        if (!pad && rlive[j]) {
+            if (byte < MG::R_CV) {
+                pg = byte / MG::CB_REF; off = a.ref_off + byte % MG::CB_REF;
+            } else if (byte < MG::R_M) {
+                const int w = byte - MG::R_CV; pg = w / MG::CB_REF; off = a.ref_off + a.ref_rec + w % MG::CB_REF;
+            } else {
+                const int w0 = byte - MG::R_M; pg = w0 / (2 * MG::MB);
+                const int w = w0 % (2 * MG::MB);
+                off = w < MG::MB ? a.ref_off + MG::CB_REF + w : a.ref_off + a.ref_rec + MG::CB_REF + (w - MG::MB);
+            }
+        }
+        rdoff[j] = off; rdpg[j] = pg;
+    }
+    int sdst[NIS], sdoff[NIS], sdpg[NIS];
+    bool slive[NIS];
+#pragma unroll
+    for (int j = 0; j < NIS; ++j) {
+        const bool pad = 64 * j >= pres;
+        sdst[j] = pad ? -1 : 16 * 64 * j;
+        slive[j] = pad ? lane == 0 : 64 * j + lane < pres;
+        const int byte = 16 * (64 * j + lane);
+        int off = 0, pg = 0;
+        if (!pad && slive[j]) {
+            const int s_cv = PPI * cbr, s_m = 2 * PPI * cbr;
+            if (byte < s_cv) {
+                pg = byte / cbr; off = res_off + byte % cbr;
+            } else if (byte < s_m) {
+                const int w = byte - s_cv; pg = w / cbr; off = res_off + res_rec + w % cbr;
+            } else {
+                const int w0 = byte - s_m; pg = w0 / MG::smp();
+                const int w = w0 % MG::smp();
+                off = w < MG::MB + MG::AB ? res_off + cbr + w : res_off + res_rec + cbr + (w - MG::MB - MG::AB);
+            }
+        }
+        sdoff[j] = off; sdpg[j] = pg;
+    }
+
+    // this lane's reads inside the stages
+    const int o_ck = tok_i * (D / 2) + q4 * REF_NB;
+    const int o_cv = MG::R_CV + o_ck;
+    const int o_mkr = MG::R_M + page_in_step * 2 * MG::MB + (tok * NG + g) * 2 * MSZ;
+    const int o_mvr = o_mkr + MG::MB;
+    const int res_nb = CPL * rb / 8;
+    const int o_rk = tok_i * (D * rb / 8) + q4 * res_nb;
+    const int o_rv = PPI * cbr + o_rk;
+    const int o_m = 2 * PPI * cbr + page_in_step * MG::smp();
+    const int o_mks = o_m + (tok * NG + g) * 2 * MSZ;
+    const int o_aks = o_m + MG::MB + tok * MSZ;
+    const int o_mvs = o_mks + MG::MB + MG::AB;
+    const int o_avs = o_aks + MG::MB + MG::AB;
+
+    SplitState<D> s;
+    init_state<D>(s);
+
+    auto blk_of = [&](int st, int pg) -> int { return __builtin_amdgcn_readlane(tbl, st * PPI + pg); };
+
+    auto issue = [&](int st, int slot) {
+        const int b0 = max(blk_of(st, 0), 0);
+        const uint8_t *base0 = a.pool + ((int64_t)b0 * H + h) * a.slab;
+        const uint8_t *base1 = base0;
+        if constexpr (PPI == 2) base1 = a.pool + ((int64_t)max(blk_of(st, 1), 0) * H + h) * a.slab;
+        const uint32_t rl = lds_addr(ref_base + slot * ref_stage);
+        const uint32_t sl = lds_addr(res_base + slot * res_stage);
+#pragma unroll
+        for (int j = 0; j < NIR; ++j) {
+            const uint32_t dst = rdst[j] < 0 ? junk : rl + (uint32_t)rdst[j];
+            if (rlive[j]) {
+                if constexpr (PPI == 1) dma16(dst, base0, (uint32_t)rdoff[j]);
+                else dma16(dst, (rdpg[j] ? base1 : base0) + rdoff[j]);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NIS; ++j) {
+            const uint32_t dst = sdst[j] < 0 ? junk : sl + (uint32_t)sdst[j];
+            if (slive[j]) {
+                if constexpr (PPI == 1) dma16(dst, base0, (uint32_t)sdoff[j]);
+                else dma16(dst, (sdpg[j] ? base1 : base0) + sdoff[j]);
+            }
+        }
+    };
+
+    for (int j = 0; j < nst - 1; ++j)
+        if (j < steps) issue(j, j);
+    for (int cur = 0; cur < steps; ++cur) {
+        // this wave's loads of step `cur` have landed ...
+        wait_steps<NST_MAX - 2, NIW>(min(nst - 2, steps - 1 - cur));
+        // ... and so have every other wave's; all waves are done with step cur-1
+        __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (cur + nst - 1 < steps) issue(cur + nst - 1, (cur + nst - 1) % nst);
+        const int slot = cur % nst;
+        const int pp = p0 + cur * PPI + page_in_step;
+        int blk = blk_of(cur, 0);
+        if constexpr (PPI == 2) blk = page_in_step ? blk_of(cur, 1) : blk;
+        const bool valid = blk >= 0 && pp < p1 && pp * 16 + tok < seq;
+        const uint8_t *R = ref_base + slot * ref_stage;
+        const uint8_t *S = res_base + slot * res_stage;
+        if (rb == 2) {
+            token_step<D, 2, META_F32>(R + o_ck, R + o_cv, R + o_mkr, R + o_mvr, S + o_rk, S + o_rv, S + o_mks,
+                                       S + o_aks, S + o_mvs, S + o_avs, valid, a.score_scale, q, s);
+        } else if (RBMAX == 4 && rb == 4) {
+            token_step<D, RBMAX, META_F32>(R + o_ck, R + o_cv, R + o_mkr, R + o_mvr, S + o_rk, S + o_rv,
+                                           S + o_mks, S + o_aks, S + o_mvs, S + o_avs, valid, a.score_scale,
+                                           q, s);
+        } else {
+            token_step<D, 0, META_F32>(R + o_ck, R + o_cv, R + o_mkr, R + o_mvr, S, S, S, S, S, S, valid,
+                                       a.score_scale, q, s);
+        }
+    }
+
+    reduce_slots<D, true>(s);
+    if (lane < LPT) {
+        float *out = a.partials + ((((int64_t)wave * a.B + b) * H + h) * a.nsplit + split) * PF;
+        if (lane == 0) { out[0] = s.m; out[1] = s.lsum; }
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) out[2 + q4 * CPL + i] = s.accr[i];
+        if (rb != 0) {
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) out[2 + D + q4 * CPL + i] = s.accs[i];
+        }
+    }
+}
+
 // --------------------------------------------------------------- combine
 struct CombineArgs {
-    const float *partials;  // [n][B][H][nwg][2 + 2D], one partial per split workgroup
-    int nwg, split_pages, max_blocks;
+    const float *partials;  // [n][B][H][nparts][2 + 2D]
+    int nparts, spp;        // partials per row; splits merged into one partial (4, or 1 for multi-loop)
+    int split_pages, max_blocks;
     const int32_t *seq_lens;
     const void *q, *tail_k, *tail_v;   // [n][B][H][D]
     const float *rot;
@@ -645,10 +951,10 @@ __global__ __launch_bounds__(1024) void rq_combine_kernel(CombineArgs a) {
         int seq = a.seq_lens[b];
         seq = seq < 0 ? 0 : (seq > a.max_blocks * 16 ? a.max_blocks * 16 : seq);
         const int npages = (seq + 15) >> 4;
-        const int nsw = (npages + a.split_pages - 1) / a.split_pages;   // wave splits with pages
-        const int ns = (nsw + kWaves - 1) / kWaves;                      // workgroup partials
+        const int nsw = (npages + a.split_pages - 1) / a.split_pages;   // splits with pages
+        const int ns = (nsw + a.spp - 1) / a.spp;                        // their partials
         const int64_t row = ((int64_t)i * B + b) * H + h;
-        const float *P = a.partials + row * a.nwg * PF;
+        const float *P = a.partials + row * a.nparts * PF;
         float st = kNegInf;
         if (a.tail_k) {
             float d = 0.f;
@@ -747,6 +1053,47 @@ hipError_t launch_split_d(const SplitArgs &s, int rb, bool mf, dim3 grid, hipStr
     return hipGetLastError();
 }
 
+template <int D, bool MF, int G, int RBMAX>
+hipError_t launch_multi_k(const MultiArgs &m, dim3 grid, size_t lds, hipStream_t st) {
+    hipLaunchKernelGGL((rq_multi_kernel<D, MF, G, RBMAX>), grid, dim3(64 * m.nl), lds, st, m);
+    return hipGetLastError();
+}
+
+template <int D, bool MF, int RBMAX>
+hipError_t launch_multi_g(const MultiArgs &m, int G, dim3 grid, size_t lds, hipStream_t st) {
+    if constexpr (D == 128) {
+        if (G == 32) return launch_multi_k<D, MF, 32, RBMAX>(m, grid, lds, st);
+        if (G == 64) return launch_multi_k<D, MF, 64, RBMAX>(m, grid, lds, st);
+        return launch_multi_k<D, MF, 128, RBMAX>(m, grid, lds, st);
+    } else if constexpr (D == 96) {
+        return launch_multi_k<D, MF, 96, RBMAX>(m, grid, lds, st);
+    } else {
+        if (G == 16) return launch_multi_k<D, MF, 16, RBMAX>(m, grid, lds, st);
+        if (G == 32) return launch_multi_k<D, MF, 32, RBMAX>(m, grid, lds, st);
+        return launch_multi_k<D, MF, 64, RBMAX>(m, grid, lds, st);
+    }
+}
+
+// LDS bytes of one multi-loop ring slot (shared reference stage plus one
+// residual stage per wave)
+template <int D, bool MF, int RBMAX>
+int multi_slot_bytes(int G, int nl) {
+    const int msz = MF ? 4 : 2, ppi = Lanes<D>::PPI;
+    const int mb = 16 * (D / G) * 2 * msz, ab = 16 * msz;
+    const int ref = 2 * ppi * (16 * D / 2) + ppi * 2 * mb;
+    const int res = 2 * ppi * (16 * D * RBMAX / 8) + ppi * 2 * (mb + ab);
+    return ref + nl * res;
+}
+
+// Ring depth of the multi-loop kernel: as deep as the workgroup's LDS share
+// allows (three workgroups per CU up to 4 waves each, else one 64 KB
+// workgroup), at most 8.
+template <int D, bool MF, int RBMAX>
+int multi_ring_depth(int G, int nl) {
+    const int budget = nl <= 4 ? 53 * 1024 : 64 * 1024;
+    return std::min(8, (budget - 16 * nl) / multi_slot_bytes<D, MF, RBMAX>(G, nl));
+}
+
 template <int D>
 hipError_t launch_decode_d(const DecodeCall &c) {
     const Geom &g = *c.g;
@@ -769,7 +1116,62 @@ hipError_t launch_decode_d(const DecodeCall &c) {
 
     const float score_scale = c.softmax_scale * kLog2e;
     const int ref = g.L - 1;
-    for (int i = 0; i < c.n; ++i) {
+    if (c.n >= 2) {
+        // multi-loop mode: loop calls in balanced groups of at least 2 and at
+        // most nl_max waves, each group reading every reference page once
+        bool any4 = false;
+        for (int i = 0; i < c.n; ++i) any4 = any4 || (c.loops[i] != ref && g.bits[c.loops[i]] == 4);
+        auto depth = [&](int nl) {
+            if (mf) return any4 ? multi_ring_depth<D, true, 4>(g.G, nl) : multi_ring_depth<D, true, 2>(g.G, nl);
+            return any4 ? multi_ring_depth<D, false, 4>(g.G, nl) : multi_ring_depth<D, false, 2>(g.G, nl);
+        };
+        int nl_max = 3;
+        for (int nl = std::min(c.n, kMaxMultiLoops); nl > 3; --nl)
+            if (depth(nl) >= 3) { nl_max = nl; break; }
+        const int ngroups = (c.n + nl_max - 1) / nl_max;
+        int first = 0;
+        for (int k = 0; k < ngroups; ++k) {
+            const int nl = c.n / ngroups + (k < c.n % ngroups ? 1 : 0);
+            MultiArgs m;
+            m.pool = c.pool; m.slab = g.slab; m.H = g.H; m.nblk = g.nblk;
+            m.ref_off = (int)g.loop_off[ref]; m.ref_rec = g.rec[ref];
+            m.nl = nl;
+            bool g4 = false;
+            for (int w = 0; w < kMaxMultiLoops; ++w) {
+                const int l = w < nl ? c.loops[first + w] : ref;
+                m.rb[w] = (l == ref) ? 0 : g.bits[l];
+                m.res_off[w] = (int)g.loop_off[l];
+                m.res_rec[w] = g.rec[l];
+                g4 = g4 || m.rb[w] == 4;
+            }
+            m.block_table = c.block_table; m.max_blocks = c.max_blocks; m.seq_lens = c.seq_lens;
+            m.qpack = c.qpack + (int64_t)first * c.B * g.H * qpack_bytes(D);
+            m.partials = c.partials + (int64_t)first * c.B * g.H * c.nparts * partial_floats(D);
+            m.B = c.B; m.nsplit = c.nsplit; m.split_pages = c.split_pages;
+            m.score_scale = score_scale;
+            int slot;
+            if (mf) {
+                m.nst = g4 ? multi_ring_depth<D, true, 4>(g.G, nl) : multi_ring_depth<D, true, 2>(g.G, nl);
+                slot = g4 ? multi_slot_bytes<D, true, 4>(g.G, nl) : multi_slot_bytes<D, true, 2>(g.G, nl);
+            } else {
+                m.nst = g4 ? multi_ring_depth<D, false, 4>(g.G, nl) : multi_ring_depth<D, false, 2>(g.G, nl);
+                slot = g4 ? multi_slot_bytes<D, false, 4>(g.G, nl) : multi_slot_bytes<D, false, 2>(g.G, nl);
+            }
+            if (m.nst < 2) return hipErrorInvalidConfiguration;
+            const size_t lds = (size_t)m.nst * slot + 16 * nl;
+            dim3 grid(c.nsplit, g.H, c.B);
+            const bool last = k == ngroups - 1;
+            if (last && c.ev_begin && hipEventRecord(c.ev_begin, c.stream) != hipSuccess) return hipErrorInvalidHandle;
+            if (mf) err = g4 ? launch_multi_g<D, true, 4>(m, g.G, grid, lds, c.stream)
+                             : launch_multi_g<D, true, 2>(m, g.G, grid, lds, c.stream);
+            else err = g4 ? launch_multi_g<D, false, 4>(m, g.G, grid, lds, c.stream)
+                          : launch_multi_g<D, false, 2>(m, g.G, grid, lds, c.stream);
+            if (err != hipSuccess) return err;
+            if (last && c.ev_end && hipEventRecord(c.ev_end, c.stream) != hipSuccess) return hipErrorInvalidHandle;
+            first += nl;
+        }
+    }
+    for (int i = 0; i < (c.n >= 2 ? 0 : c.n); ++i) {
         const int l = c.loops[i];
         SplitArgs s;
         s.pool = c.pool; s.slab = g.slab; s.H = g.H; s.nblk = g.nblk; s.G = g.G;
@@ -778,7 +1180,7 @@ hipError_t launch_decode_d(const DecodeCall &c) {
         s.meta_bytes = g.meta_bytes;
         s.block_table = c.block_table; s.max_blocks = c.max_blocks; s.seq_lens = c.seq_lens;
         s.qpack = c.qpack + (int64_t)i * c.B * g.H * qpack_bytes(D);
-        s.partials = c.partials + (int64_t)i * c.B * g.H * c.nwg * partial_floats(D);
+        s.partials = c.partials + (int64_t)i * c.B * g.H * c.nparts * partial_floats(D);
         s.nsplit = c.nsplit; s.split_pages = c.split_pages;
         s.score_scale = score_scale;
         const int rb = (l == ref) ? 0 : g.bits[l];
@@ -790,7 +1192,8 @@ hipError_t launch_decode_d(const DecodeCall &c) {
         if (last && c.ev_end && hipEventRecord(c.ev_end, c.stream) != hipSuccess) return hipErrorInvalidHandle;
     }
 
-    ca.partials = c.partials; ca.nwg = c.nwg; ca.split_pages = c.split_pages;
+    ca.partials = c.partials; ca.nparts = c.nparts; ca.spp = c.n >= 2 ? 1 : kWaves;
+    ca.split_pages = c.split_pages;
     ca.max_blocks = c.max_blocks; ca.seq_lens = c.seq_lens;
     ca.q = c.q; ca.tail_k = c.tail_k; ca.tail_v = c.tail_v; ca.rot = c.rot; ca.out = c.out;
     ca.B = c.B; ca.H = g.H; ca.score_scale = score_scale;

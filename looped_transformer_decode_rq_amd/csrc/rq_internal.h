@@ -31,8 +31,14 @@ __host__ __device__ constexpr int partial_floats(int D) { return 2 + 2 * D; }
 
 int auto_split_pages(int units, int max_blocks);
 
-constexpr int kSplitWaves = 4;   // waves (splits) per split-K workgroup
+constexpr int kSplitWaves = 4;     // waves (splits) per split-K workgroup
 constexpr int kMaxSplitPages = 64; // pages per split: one block-table entry per lane
+constexpr int kMaxMultiLoops = 8;  // loop calls (waves) per multi-loop workgroup
+
+// Partials per (loop call, sequence, head) row: one per split workgroup of 4
+// waves for a single loop call, one per split when several loops are decoded
+// together (the multi-loop kernel).
+int partials_per_row(int n_loops, int max_blocks, int split_pages);
 
 // ------------------------------------------------------------------ launchers
 struct DecodeCall {
@@ -49,8 +55,8 @@ struct DecodeCall {
     float softmax_scale;
     float *out;
     uint8_t *qpack;               // workspace: [n][B][H][qpack_bytes]
-    float *partials;              // workspace: [n][B][H][nwg][partial_floats]
-    int split_pages, nsplit, nwg;  // wave splits and split workgroups (4 waves each)
+    float *partials;              // workspace: [n][B][H][nparts][partial_floats]
+    int split_pages, nsplit, nparts;   // pages per split, splits, partials per row
     hipEvent_t ev_begin, ev_end;
     hipStream_t stream;
 };

@@ -4,8 +4,9 @@ on the device by the seeded generator, the whole cache packed by the HIP
 encoder, decode run in the split configuration the benchmark uses. A seeded
 sample of (sequence, head) pairs is then recomputed by the oracle one by one
 from the same generator draws: their packed records must match the oracle's
-encoding (exemption rule of gpu_util) and their attention outputs must match
-the oracle's attention over the oracle's own packed bytes."""
+encoding (exemption rule of gpu_util) and their attention outputs, per-loop
+calls and one multi-loop call, must match the oracle's attention over the
+oracle's own packed bytes."""
 import time
 
 import numpy as np
@@ -64,8 +65,17 @@ def test_full_size_sampled(key):
         R.decode_attention(lay, pool, [l], q[l:l + 1].contiguous(), rot, d_table, d_seq,
                            tail_k[l:l + 1].contiguous(), tail_v[l:l + 1].contiguous(), tau, out, ws)
         outs.append(out[0])
+    # multi-loop mode: every loop's query in one call
+    multi = T.empty((L, B, H, D), device=dev())
+    ws = T.empty(R.decode_workspace_bytes(lay, L, B, table.shape[1]), dtype=T.uint8, device=dev())
+    R.decode_attention(lay, pool, list(range(L)), q.contiguous(), rot, d_table, d_seq, tail_k, tail_v, tau,
+                       multi, ws)
     T.cuda.synchronize()
     _log("decode done")
+    for l in range(L):
+        d = (multi[l] - outs[l]).abs().max().item()
+        _log(f"multi-loop vs single call, loop {l}: max-abs {d:.2e}")
+        assert d <= 5e-5
     npages = -(-N // 16)
     slab = R.pool_bytes(lay) // (nblk * H)
     pool3 = pool.view(nblk, H, slab)
@@ -88,7 +98,8 @@ def test_full_size_sampled(key):
                                       tk_h[l, b:b + 1, h:h + 1], tv_h[l, b:b + 1, h:h + 1])[0, 0]
             got = outs[l][b, h].cpu().numpy()
             e, r = check_attention(f"{w.name} b{b} h{h} loop {l}", got, want)
-            _log(f"b{b} h{h} loop {l}: max-abs {e:.2e} rel-L2 {r:.2e}")
+            em, rm = check_attention(f"{w.name} b{b} h{h} loop {l} multi", multi[l, b, h].cpu().numpy(), want)
+            _log(f"b{b} h{h} loop {l}: max-abs {e:.2e} rel-L2 {r:.2e}; multi-loop {em:.2e} {rm:.2e}")
     check_caps(stats)
     _log(f"encode stats {stats}")
     for l in range(L):
