@@ -105,6 +105,13 @@ def setup_rq(w, dev, split_pages):
     s["out"] = torch.empty((L, 1, B, H, D), device=dev)
     s["ws"] = torch.empty(R.decode_workspace_bytes(lay, 1, B, table.shape[1], split_pages), dtype=torch.uint8,
                           device=dev)
+    # multi-loop mode: all loops' queries and current tokens in one call
+    s["q_all"] = q.contiguous()
+    s["tk_all"] = cur[:, 0].contiguous()
+    s["tv_all"] = cur[:, 1].contiguous()
+    s["out_all"] = torch.empty((L, B, H, D), device=dev)
+    s["ws_all"] = torch.empty(R.decode_workspace_bytes(lay, L, B, table.shape[1], split_pages),
+                              dtype=torch.uint8, device=dev)
     return s
 
 
@@ -115,6 +122,15 @@ def rq_step(w, s, split_pages, events=None):
         ev = None if events is None else events[l]
         R.decode_attention(s["lay"], s["pool"], [l], s["qs"][l], s["rot"], s["d_table"], s["d_seq"],
                            s["tk"][l], s["tv"][l], tau, s["out"][l], s["ws"], split_pages=split_pages, events=ev)
+    R.encode_pack(s["lay"], s["pool"], s["kv_new"], s["rot"], s["slots_new"])
+
+
+def rq_multi_step(w, s, split_pages, events=None):
+    import looped_transformer_decode_rq_amd as R
+    tau = 1.0 / np.sqrt(w.head_dim)
+    R.decode_attention(s["lay"], s["pool"], list(range(w.loops)), s["q_all"], s["rot"], s["d_table"], s["d_seq"],
+                       s["tk_all"], s["tv_all"], tau, s["out_all"], s["ws_all"], split_pages=split_pages,
+                       events=events)
     R.encode_pack(s["lay"], s["pool"], s["kv_new"], s["rot"], s["slots_new"])
 
 
@@ -303,6 +319,25 @@ def main():
     step_gbs = step_bytes / t_rq / 1e9
     log(f"packed step {t_rq * 1e3:.3f} ms; residual split kernel {res_ms:.3f} ms ({achieved:.0f} GB/s)")
 
+    # multi-loop mode: the same step with the 4 loops' queries in one call
+    mpairs = {k: (ev.create(), ev.create()) for k in range(args.steps)}
+
+    def multi_fn(k):
+        rq_multi_step(w, rq, args.split_pages, None if k is None else mpairs[k])
+
+    log("timing packed multi-loop step")
+    t_multi = timed(multi_fn, args.steps, args.warmup)
+    mk = []
+    for k, (a, b) in mpairs.items():
+        mk.append(ev.ms(a, b))
+        ev.destroy(a)
+        ev.destroy(b)
+    multi_ms = float(np.mean(mk))
+    multi_bytes = (stored * B * H * N + L * B * H * qp + B * N // 16 * 4
+                   + (L - 1) * B * H * nsplit * (2 + 2 * D) * 4 + B * H * nsplit * (2 + D) * 4)
+    multi_gbs = multi_bytes / (multi_ms * 1e-3) / 1e9
+    log(f"multi-loop step {t_multi * 1e3:.3f} ms; multi-loop kernel {multi_ms:.3f} ms ({multi_gbs:.0f} GB/s)")
+
     bf16 = None
     if not args.no_bf16:
         log("setting up bf16 baseline cache")
@@ -323,7 +358,8 @@ def main():
         bf16 = {"tokens_per_s": B / t_bf, "ms_per_step": t_bf * 1e3,
                 "split_kernel_ms": float(np.mean(bms)),
                 "split_kernel_gbs": bf_kernel_bytes / (float(np.mean(bms)) * 1e-3) / 1e9,
-                "speedup_packed_vs_bf16": t_bf / t_rq}
+                "speedup_packed_vs_bf16": t_bf / t_rq,
+                "speedup_multi_loop_vs_bf16": t_bf / t_multi}
         log(f"bf16 step {t_bf * 1e3:.3f} ms; packed/bf16 speedup {t_bf / t_rq:.2f}x")
         del b16
         torch.cuda.empty_cache()
@@ -358,6 +394,12 @@ def main():
                      "kernel": f"rq_split_kernel<{D},{w.res_bits[0]},{w.meta_dtype == 'f32'}> (residual loop)",
                      "kernel_ms": res_ms, "bytes_per_launch": res_bytes},
         "ref_loop_kernel": {"ms": ref_ms, "gbs": ref_bytes / (ref_ms * 1e-3) / 1e9, "bytes_per_launch": ref_bytes},
+        "multi_loop": {"tokens_per_s": B / t_multi, "ms_per_step": t_multi * 1e3,
+                       "step": f"one decode call with all {L} loops' queries (each reference page read once) "
+                               f"+ encode of {B} new tokens",
+                       "kernel": f"rq_multi_kernel<{D}> ({L} waves per split workgroup)",
+                       "kernel_ms": multi_ms, "bytes_per_launch": multi_bytes, "kernel_gbs": multi_gbs,
+                       "kernel_frac_of_peak": multi_gbs / HBM_PEAK_GBS},
         "bf16_baseline": bf16,
         "cpu_baseline": cpu,
         "context_from_pages": {"kv_storage_reduction": "80.7% (theoretical, mixed precision)",

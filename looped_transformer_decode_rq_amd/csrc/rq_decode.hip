@@ -263,21 +263,35 @@ __device__ __forceinline__ int dot_int2(const uint32_t *codes, const uint4 *limb
     return a0 + 16 * a1 + 256 * a2 + 4096 * a3;
 }
 
-// acc[8k + 2j (+1)] += w * code for INT4 words
+// Byte J of x as a float: one v_cvt_f32_ubyteJ, which selects the byte
+// itself (written out because the compiler otherwise re-extracts each masked
+// field with a separate bit-field extract first).
+template <int J>
+__device__ __forceinline__ float cvt_ubyte(uint32_t x) {
+    float r;
+    __asm__("v_cvt_f32_ubyte%c1 %0, %2" : "=v"(r) : "n"(J), "v"(x));
+    return r;
+}
+
+// acc[8k + 2j (+1)] += w * code for INT4 words: the even channels of a word
+// are the low nibbles of its bytes, the odd ones the high nibbles
 template <int NW>
 __device__ __forceinline__ void axpy_int4(float *acc, const uint32_t *codes, float w) {
 #pragma unroll
     for (int k = 0; k < NW; ++k) {
         const uint32_t lo = codes[k] & 0x0F0F0F0Fu, hi = (codes[k] >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            acc[8 * k + 2 * j] = fmaf(w, ubyte(lo, j), acc[8 * k + 2 * j]);
-            acc[8 * k + 2 * j + 1] = fmaf(w, ubyte(hi, j), acc[8 * k + 2 * j + 1]);
-        }
+        acc[8 * k + 0] = fmaf(w, cvt_ubyte<0>(lo), acc[8 * k + 0]);
+        acc[8 * k + 1] = fmaf(w, cvt_ubyte<0>(hi), acc[8 * k + 1]);
+        acc[8 * k + 2] = fmaf(w, cvt_ubyte<1>(lo), acc[8 * k + 2]);
+        acc[8 * k + 3] = fmaf(w, cvt_ubyte<1>(hi), acc[8 * k + 3]);
+        acc[8 * k + 4] = fmaf(w, cvt_ubyte<2>(lo), acc[8 * k + 4]);
+        acc[8 * k + 5] = fmaf(w, cvt_ubyte<2>(hi), acc[8 * k + 5]);
+        acc[8 * k + 6] = fmaf(w, cvt_ubyte<3>(lo), acc[8 * k + 6]);
+        acc[8 * k + 7] = fmaf(w, cvt_ubyte<3>(hi), acc[8 * k + 7]);
     }
 }
 
-// acc[16k + 4j + i] += w * code for INT2 words
+// acc[16k + 4j + i] += w * code for INT2 words: crumb i of byte j
 template <int NW>
 __device__ __forceinline__ void axpy_int2(float *acc, const uint32_t *codes, float w) {
 #pragma unroll
@@ -285,8 +299,10 @@ __device__ __forceinline__ void axpy_int2(float *acc, const uint32_t *codes, flo
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const uint32_t c = (codes[k] >> (2 * i)) & 0x03030303u;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[16 * k + 4 * j + i] = fmaf(w, ubyte(c, j), acc[16 * k + 4 * j + i]);
+            acc[16 * k + 0 + i] = fmaf(w, cvt_ubyte<0>(c), acc[16 * k + 0 + i]);
+            acc[16 * k + 4 + i] = fmaf(w, cvt_ubyte<1>(c), acc[16 * k + 4 + i]);
+            acc[16 * k + 8 + i] = fmaf(w, cvt_ubyte<2>(c), acc[16 * k + 8 + i]);
+            acc[16 * k + 12 + i] = fmaf(w, cvt_ubyte<3>(c), acc[16 * k + 12 + i]);
         }
     }
 }
