@@ -39,16 +39,21 @@ def log(msg):
 class HipEvents:
     """hipEvent_t pairs for timing kernels launched inside the library."""
 
+    # timing-only events: no system-scope fence (cache write-back and
+    # invalidate) when they are recorded, which would otherwise stall the
+    # stream between the kernels they bracket
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
     def __init__(self):
         self.h = ctypes.CDLL("libamdhip64.so")
-        self.h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.h.hipEventDestroy.argtypes = [ctypes.c_void_p]
         self.h.hipEventSynchronize.argtypes = [ctypes.c_void_p]
 
     def create(self):
         e = ctypes.c_void_p()
-        assert self.h.hipEventCreate(ctypes.byref(e)) == 0
+        assert self.h.hipEventCreateWithFlags(ctypes.byref(e), self.DISABLE_SYSTEM_FENCE) == 0
         return e
 
     def ms(self, a, b):

@@ -82,20 +82,28 @@ __global__ __launch_bounds__(1024) void rq_qprep_kernel(QPrepArgs a) {
     const int b = tile * 16 + r;
     const bool row_ok = b < B;
 
+    // q' = R_K q for the 16 rows: [16 x D] x R_K^T. v_mfma_f32_16x16x4f32:
+    // lane l supplies A[l%16][k0 + l/16], B[k0 + l/16][l%16] and receives
+    // D[4*(l/16)+v][l%16]; wave r computes columns 16r..16r+15. This lane's
+    // B operands (a column slice of R_K) are loaded first, so that their
+    // latency overlaps the query loads.
+    const bool rot_wave = rb != 0 && r < D / 16;
+    const int n = r * 16 + (lane & 15);
+    float rk[D / 4];
+    if (rot_wave) {
+        const float *RK = a.rot + ((int64_t)h * 2 + 0) * D * D + (int64_t)n * D + (lane >> 4);
+#pragma unroll
+        for (int kk = 0; kk < D / 4; ++kk) rk[kk] = RK[4 * kk];
+    }
     for (int c = lane; c < D; c += 64)
         Q[r * QS + c] = row_ok ? load_kv<KV_F32>(a.q, (((int64_t)i * B + b) * H + h) * D + c) : 0.0f;
     __syncthreads();
-    if (rb != 0 && r < D / 16) {
-        // q' = R_K q for the 16 rows: [16 x D] x R_K^T. v_mfma_f32_16x16x4f32:
-        // lane l supplies A[l%16][k0 + l/16], B[k0 + l/16][l%16] and receives
-        // D[4*(l/16)+v][l%16]; wave r computes columns 16r..16r+15.
-        const float *RK = a.rot + ((int64_t)h * 2 + 0) * D * D;
+    if (rot_wave) {
         floatx4 c = {0.f, 0.f, 0.f, 0.f};
-        const int n = r * 16 + (lane & 15);
 #pragma unroll
         for (int kk = 0; kk < D / 4; ++kk) {
             const int k = 4 * kk + (lane >> 4);
-            c = __builtin_amdgcn_mfma_f32_16x16x4f32(Q[(lane & 15) * QS + k], RK[(int64_t)n * D + k], c, 0, 0, 0);
+            c = __builtin_amdgcn_mfma_f32_16x16x4f32(Q[(lane & 15) * QS + k], rk[kk], c, 0, 0, 0);
         }
         for (int v = 0; v < 4; ++v) QR[(4 * (lane >> 4) + v) * QS + n] = c[v];
     }
@@ -963,6 +971,16 @@ __global__ __launch_bounds__(1024) void rq_combine_kernel(CombineArgs a) {
     const int b = tile * 16 + r;
     const int c0 = lane, c1 = lane + 64;
     float ar0 = 0.f, ar1 = 0.f, as0 = 0.f, as1 = 0.f;
+    // this lane's R_V operands of the output rotation, loaded before the
+    // partials so that the two latencies overlap (see the MFMA below)
+    const bool rot_wave = has_res && r < D / 16;
+    const int n = r * 16 + (lane & 15);
+    float rv[D / 4];
+    if (rot_wave) {
+        const float *RV = a.rot + ((int64_t)h * 2 + 1) * D * D + (int64_t)(lane >> 4) * D + n;
+#pragma unroll
+        for (int kk = 0; kk < D / 4; ++kk) rv[kk] = RV[(int64_t)4 * kk * D];
+    }
     if (b < B) {
         int seq = a.seq_lens[b];
         seq = seq < 0 ? 0 : (seq > a.max_blocks * 16 ? a.max_blocks * 16 : seq);
@@ -983,20 +1001,35 @@ __global__ __launch_bounds__(1024) void rq_combine_kernel(CombineArgs a) {
         const float M = fmaxf(wave_max(mloc), st);
         if (M != kNegInf) {
             float lloc = 0.f;
+            // columns c0 and c1 of this lane (clamped: the weight of a column
+            // beyond D is never used)
+            const int k0 = min(c0, D - 1), k1 = min(c1, D - 1);
             for (int cb = 0; cb < ns; cb += 64) {
                 const int s = cb + lane;
                 const float e_l = s < ns ? fast_exp2(P[(int64_t)s * PF] - M) : 0.f;
                 if (s < ns) lloc = fmaf(e_l, P[(int64_t)s * PF + 1], lloc);
                 const int cnt = min(64, ns - cb);
-#pragma unroll 8
-                for (int j = 0; j < cnt; ++j) {
-                    const float e = readlane_f(e_l, j);
-                    const float *ps = P + (int64_t)(cb + j) * PF;
-                    if (c0 < D) ar0 = fmaf(e, ps[2 + c0], ar0);
-                    if (c1 < D) ar1 = fmaf(e, ps[2 + c1], ar1);
-                    if (has_res) {
-                        if (c0 < D) as0 = fmaf(e, ps[2 + D + c0], as0);
-                        if (c1 < D) as1 = fmaf(e, ps[2 + D + c1], as1);
+                // groups of 8 partials with unconditional loads (indices past
+                // the last partial re-read it with weight 0), so that all the
+                // group's loads are in flight together
+                for (int j0 = 0; j0 < cnt; j0 += 8) {
+                    float e[8], v0[8], v1[8], w0[8], w1[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const int jj = min(j0 + j, cnt - 1);
+                        e[j] = j0 + j < cnt ? readlane_f(e_l, j0 + j) : 0.f;
+                        const float *ps = P + (int64_t)(cb + jj) * PF + 2;
+                        v0[j] = ps[k0];
+                        v1[j] = ps[k1];
+                        w0[j] = has_res ? ps[D + k0] : 0.f;
+                        w1[j] = has_res ? ps[D + k1] : 0.f;
+                    }
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        ar0 = fmaf(e[j], v0[j], ar0);
+                        ar1 = fmaf(e[j], v1[j], ar1);
+                        as0 = fmaf(e[j], w0[j], as0);
+                        as1 = fmaf(e[j], w1[j], as1);
                     }
                 }
             }
@@ -1019,14 +1052,12 @@ __global__ __launch_bounds__(1024) void rq_combine_kernel(CombineArgs a) {
         // out = O + A * R_V (row vector times R_V = R_V^T applied to the column),
         // v_mfma_f32_16x16x4f32: lane l supplies A[l%16][k0 + l/16], B[k0 + l/16][l%16]
         // and receives D[4*(l/16)+v][l%16]; wave r computes output columns 16r..16r+15.
-        if (r < D / 16) {
-            const float *RV = a.rot + ((int64_t)h * 2 + 1) * D * D;
+        if (rot_wave) {
             floatx4 c = {0.f, 0.f, 0.f, 0.f};
-            const int n = r * 16 + (lane & 15);
 #pragma unroll
             for (int kk = 0; kk < D / 4; ++kk) {
                 const int k = 4 * kk + (lane >> 4);
-                c = __builtin_amdgcn_mfma_f32_16x16x4f32(A[(lane & 15) * QS + k], RV[(int64_t)k * D + n], c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x4f32(A[(lane & 15) * QS + k], rv[kk], c, 0, 0, 0);
             }
             for (int v = 0; v < 4; ++v) {
                 const int rr = 4 * (lane >> 4) + v;
