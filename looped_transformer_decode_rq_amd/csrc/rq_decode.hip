@@ -232,19 +232,37 @@ __device__ __forceinline__ float load_meta1(const uint8_t *p) {
 
 __device__ __forceinline__ float ubyte(uint32_t x, int j) { return (float)((x >> (8 * j)) & 0xFFu); }
 
+// sum of the 8 products of signed nibbles of a and b, plus c: the
+// three-operand v_dot8_i32_i4, written out so that a chain can start from
+// the inline constant 0 (the builtin is lowered to the accumulate-in-place
+// form, which needs a register zeroed first)
+__device__ __forceinline__ int sdot8(int a, int b, int c) {
+    int r;
+    __asm__("v_dot8_i32_i4 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+__device__ __forceinline__ int sdot8_0(int a, int b) {
+    int r;
+    __asm__("v_dot8_i32_i4 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
 // Integer dot of 4-bit codes (XOR 8 turns 0..15 into signed -8..7) with the
 // four query limbs; returns sum_i q_int_i * (c_i - 8).
 template <int NW>
 __device__ __forceinline__ int dot_int4(const uint32_t *codes, const uint4 *limb) {
-    int a0 = 0, a1 = 0, a2 = 0, a3 = 0;
+    int a0, a1, a2, a3;
 #pragma unroll
     for (int k = 0; k < NW; ++k) {
         const int w = (int)(codes[k] ^ 0x88888888u);
         const uint4 q = limb[k];
-        a0 = __builtin_amdgcn_sdot8((int)q.x, w, a0, false);
-        a1 = __builtin_amdgcn_sdot8((int)q.y, w, a1, false);
-        a2 = __builtin_amdgcn_sdot8((int)q.z, w, a2, false);
-        a3 = __builtin_amdgcn_sdot8((int)q.w, w, a3, false);
+        if (k == 0) {
+            a0 = sdot8_0((int)q.x, w); a1 = sdot8_0((int)q.y, w);
+            a2 = sdot8_0((int)q.z, w); a3 = sdot8_0((int)q.w, w);
+        } else {
+            a0 = sdot8((int)q.x, w, a0); a1 = sdot8((int)q.y, w, a1);
+            a2 = sdot8((int)q.z, w, a2); a3 = sdot8((int)q.w, w, a3);
+        }
     }
     return a0 + 16 * a1 + 256 * a2 + 4096 * a3;
 }
@@ -253,22 +271,41 @@ __device__ __forceinline__ int dot_int4(const uint32_t *codes, const uint4 *limb
 // channels, each widened to nibbles (values 0..3 need no offset).
 template <int NW>
 __device__ __forceinline__ int dot_int2(const uint32_t *codes, const uint4 *limb) {
-    int a0 = 0, a1 = 0, a2 = 0, a3 = 0;
+    int a0, a1, a2, a3;
 #pragma unroll
     for (int k = 0; k < NW; ++k) {
         const int ev = (int)(codes[k] & 0x33333333u);
         const int od = (int)((codes[k] >> 2) & 0x33333333u);
         const uint4 qe = limb[2 * k], qo = limb[2 * k + 1];
-        a0 = __builtin_amdgcn_sdot8((int)qe.x, ev, a0, false);
-        a1 = __builtin_amdgcn_sdot8((int)qe.y, ev, a1, false);
-        a2 = __builtin_amdgcn_sdot8((int)qe.z, ev, a2, false);
-        a3 = __builtin_amdgcn_sdot8((int)qe.w, ev, a3, false);
-        a0 = __builtin_amdgcn_sdot8((int)qo.x, od, a0, false);
-        a1 = __builtin_amdgcn_sdot8((int)qo.y, od, a1, false);
-        a2 = __builtin_amdgcn_sdot8((int)qo.z, od, a2, false);
-        a3 = __builtin_amdgcn_sdot8((int)qo.w, od, a3, false);
+        if (k == 0) {
+            a0 = sdot8_0((int)qe.x, ev); a1 = sdot8_0((int)qe.y, ev);
+            a2 = sdot8_0((int)qe.z, ev); a3 = sdot8_0((int)qe.w, ev);
+        } else {
+            a0 = sdot8((int)qe.x, ev, a0); a1 = sdot8((int)qe.y, ev, a1);
+            a2 = sdot8((int)qe.z, ev, a2); a3 = sdot8((int)qe.w, ev, a3);
+        }
+        a0 = sdot8((int)qo.x, od, a0); a1 = sdot8((int)qo.y, od, a1);
+        a2 = sdot8((int)qo.z, od, a2); a3 = sdot8((int)qo.w, od, a3);
     }
     return a0 + 16 * a1 + 256 * a2 + 4096 * a3;
+}
+
+// Sum over each group of LPT consecutive lanes (LPT = 2 or 4, all lanes
+// active), with the DPP swizzle on the add's first operand. The s_nop covers
+// the wait states a DPP read needs after the VALU write of its source.
+template <int LPT>
+__device__ __forceinline__ float lane_group_sum(float v) {
+    static_assert(LPT == 2 || LPT == 4, "");
+    float r;
+    __asm__("s_nop 1\n\tv_add_f32_dpp %0, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
+            : "=v"(r) : "v"(v));
+    if constexpr (LPT == 4) {
+        float t;
+        __asm__("s_nop 1\n\tv_add_f32_dpp %0, %1, %1 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"
+                : "=v"(t) : "v"(r));
+        r = t;
+    }
+    return r;
 }
 
 // Byte J of x as a float: one v_cvt_f32_ubyteJ, which selects the byte
@@ -381,12 +418,13 @@ __device__ __forceinline__ void init_state(SplitState<D> &s) {
 //   mkr, mvr    the token's reference K / V (scale, zero) of this lane's group
 //   rk, rv      this lane's residual K / V code bytes (RB != 0)
 //   mks, mvs    residual (scale, zero); aks, avs residual alphas (RB != 0)
+//   lsv         this lane's residual query limbs (registers or LDS)
 template <int D, int RB, bool META_F32>
 __device__ __forceinline__ void token_step(const uint8_t *ck, const uint8_t *cv, const uint8_t *mkr,
                                            const uint8_t *mvr, const uint8_t *rk, const uint8_t *rv,
                                            const uint8_t *mks, const uint8_t *aks, const uint8_t *mvs,
                                            const uint8_t *avs, bool valid, float score_scale,
-                                           const QueryRegs<D> &q, SplitState<D> &s) {
+                                           const QueryRegs<D> &q, const uint4 *lsv, SplitState<D> &s) {
     using Ln = Lanes<D>;
     constexpr int LPT = Ln::LPT, CPL = Ln::CPL;
     constexpr int REF_NB = CPL / 2;                 // INT4 code bytes per lane
@@ -411,10 +449,10 @@ __device__ __forceinline__ void token_step(const uint8_t *ck, const uint8_t *cv,
         sz_of(*(const SZ *)mvs, svs, zvs);
         const float ak = load_meta1<META_F32>(aks);
         av = load_meta1<META_F32>(avs);
-        const int dres = (RB == 2) ? dot_int2<RES_NW>(rkw, q.lsv) : dot_int4<RES_NW>(rkw, q.lsv) + 8 * q.qs_res;
+        const int dres = (RB == 2) ? dot_int2<RES_NW>(rkw, lsv) : dot_int4<RES_NW>(rkw, lsv) + 8 * q.qs_res;
         part = ak * part + (sks * (float)dres + zks * (float)q.qs_res) * q.sc_res;
     }
-    float score = group_sum<LPT>(part) * score_scale;
+    float score = lane_group_sum<LPT>(part) * score_scale;
     score = valid ? score : kNegInf;
     // online softmax, rescaled only when a score beats m by 2^8
     if (__any(score > s.m + kRescaleThresh)) {
@@ -526,11 +564,12 @@ struct StageGeom {
     static constexpr int NP = BYTES / 16;               // 16-byte pieces
     static constexpr int NI = (NP + 63) / 64;           // direct-to-LDS instructions per stage
     static constexpr int LIVE_LAST = NP - 64 * (NI - 1);
-    // ring depth per wave: three stages when three 4-wave workgroups (stages
-    // plus the merge buffer) still fit in the CU's 160 KB of LDS, else two
-    static constexpr int NST =
-        3 * (kWaves * 3 * BYTES + kWaves * partial_floats(D) * 4) <= 160 * 1024 ? 3 : 2;
+    // ring depth per wave: three stages when three 4-wave workgroups still
+    // fit in the CU's 160 KB of LDS, else two; the end-of-loop merge reuses
+    // each wave's own stages
+    static constexpr int NST = 3 * kWaves * 3 * BYTES <= 160 * 1024 ? 3 : 2;
     static_assert(BYTES % 16 == 0, "stage pieces are 16 bytes");
+    static_assert(NST * BYTES >= partial_floats(D) * 4, "a wave's partial fits in its stages");
 };
 
 // Split-K decode of one loop over packed pages. One wave per split (4 per
@@ -549,7 +588,8 @@ __global__ __launch_bounds__(256) void rq_split_kernel(SplitArgs a) {
     constexpr int MSZ = SG::MSZ, NG = SG::NG, NST = SG::NST, NI = SG::NI;
     constexpr int PF = partial_floats(D);
     __shared__ __attribute__((aligned(16))) uint8_t stage[kWaves][NST][SG::BYTES];
-    __shared__ float wp[kWaves][PF];
+    // after the page loop: wave w's partial (m, l, acc_ref, acc_res) in its own stages
+    auto wp = [&](int w) -> float * { return (float *)&stage[w][0][0]; };
 
     // wave index made provably wave-uniform, so the page loop is a scalar loop
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -572,7 +612,8 @@ __global__ __launch_bounds__(256) void rq_split_kernel(SplitArgs a) {
     const int g = (q4 * CPL) / G;
 
     QueryRegs<D> q;
-    load_query<D, RB != 0>(a.qpack + ((int64_t)b * H + h) * qpack_bytes(D), q4, q);
+    const uint8_t *qp = a.qpack + ((int64_t)b * H + h) * qpack_bytes(D);
+    load_query<D, RB != 0>(qp, q4, q);
 
     // the split's block-table entries, one per lane (at most 64 pages per split)
     int tbl = -1;
@@ -607,18 +648,12 @@ __global__ __launch_bounds__(256) void rq_split_kernel(SplitArgs a) {
         dpg[i] = pg;
     }
 
-    // this lane's reads inside a stage
-    const int o_ck = SG::O_RK + tok_i * (D / 2) + q4 * REF_NB;
-    const int o_cv = SG::O_RV + tok_i * (D / 2) + q4 * REF_NB;
-    const int o_rk = SG::O_SK + tok_i * (D * RB / 8) + q4 * RES_NB;
-    const int o_rv = SG::O_SV + tok_i * (D * RB / 8) + q4 * RES_NB;
-    const int o_m = SG::O_M + page_in_step * SG::MP;
-    const int o_mkr = o_m + (tok * NG + g) * 2 * MSZ;
-    const int o_mvr = o_mkr + SG::MB;
-    const int o_mks = o_mkr + 2 * SG::MB;
-    const int o_aks = o_m + 3 * SG::MB + tok * MSZ;
-    const int o_mvs = o_mkr + 3 * SG::MB + SG::AB;
-    const int o_avs = o_m + 4 * SG::MB + SG::AB + tok * MSZ;
+    // this lane's reads inside a stage: four lane offsets; the other reads
+    // sit at compile-time distances from them (immediate LDS offsets)
+    const int o_ck = tok_i * (D / 2) + q4 * REF_NB;                  // + O_RK / O_RV
+    const int o_rk = tok_i * (D * RB / 8) + q4 * RES_NB;             // + O_SK / O_SV
+    const int o_mkr = page_in_step * SG::MP + (tok * NG + g) * 2 * MSZ;   // + O_M (+ MB, ...)
+    const int o_aks = page_in_step * SG::MP + tok * MSZ;             // + O_M + 3 MB (+ MB + AB)
 
     SplitState<D> s;
     init_state<D>(s);
@@ -657,43 +692,44 @@ __global__ __launch_bounds__(256) void rq_split_kernel(SplitArgs a) {
             if constexpr (PPI == 2) blk = page_in_step ? blk_of(cur, 1) : blk;
             const bool valid = blk >= 0 && pp < p1 && pp * 16 + tok < seq;
             const uint8_t *S = &stage[wave][cur % NST][0];
-            token_step<D, RB, META_F32>(S + o_ck, S + o_cv, S + o_mkr, S + o_mvr, S + o_rk, S + o_rv,
-                                        S + o_mks, S + o_aks, S + o_mvs, S + o_avs, valid, a.score_scale,
-                                        q, s);
+            const uint8_t *C = S + o_ck, *R = S + o_rk, *M = S + SG::O_M + o_mkr, *A = S + SG::O_M + o_aks;
+            token_step<D, RB, META_F32>(C + SG::O_RK, C + SG::O_RV, M, M + SG::MB, R + SG::O_SK, R + SG::O_SV,
+                                        M + 2 * SG::MB, A + 3 * SG::MB, M + 3 * SG::MB + SG::AB,
+                                        A + 4 * SG::MB + SG::AB, valid, a.score_scale, q, q.lsv, s);
         }
     }
 
     reduce_slots<D, RB != 0>(s);
     // ---- merge the workgroup's 4 wave partials (log-sum-exp), one partial per workgroup
     if (lane < LPT) {
-        if (lane == 0) { wp[wave][0] = s.m; wp[wave][1] = s.lsum; }
+        if (lane == 0) { wp(wave)[0] = s.m; wp(wave)[1] = s.lsum; }
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) wp[wave][2 + q4 * CPL + i] = s.accr[i];
+        for (int i = 0; i < CPL; ++i) wp(wave)[2 + q4 * CPL + i] = s.accr[i];
         if constexpr (RB != 0) {
 #pragma unroll
-            for (int i = 0; i < CPL; ++i) wp[wave][2 + D + q4 * CPL + i] = s.accs[i];
+            for (int i = 0; i < CPL; ++i) wp(wave)[2 + D + q4 * CPL + i] = s.accs[i];
         }
     }
     __syncthreads();
     float M = kNegInf;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wp[w][0]);
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wp(w)[0]);
     // every token of the workgroup masked (invalid block ids): an empty partial
     float e[kWaves];
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) e[w] = M == kNegInf ? 0.f : fast_exp2(wp[w][0] - M);
+    for (int w = 0; w < kWaves; ++w) e[w] = M == kNegInf ? 0.f : fast_exp2(wp(w)[0] - M);
     float *out = a.partials + (((int64_t)b * H + h) * gridDim.x + blockIdx.x) * PF;
     constexpr int NV = RB ? 2 * D : D;
     for (int v = threadIdx.x; v < NV; v += 256) {
         float acc = 0.f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) acc = fmaf(e[w], wp[w][2 + v], acc);
+        for (int w = 0; w < kWaves; ++w) acc = fmaf(e[w], wp(w)[2 + v], acc);
         out[2 + v] = acc;
     }
     if (threadIdx.x == 0) {
         float l = 0.f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) l = fmaf(e[w], wp[w][1], l);
+        for (int w = 0; w < kWaves; ++w) l = fmaf(e[w], wp(w)[1], l);
         out[0] = M;
         out[1] = l;
     }
@@ -915,14 +951,14 @@ __global__ __launch_bounds__(64 * kMaxMultiLoops) void rq_multi_kernel(MultiArgs
         const uint8_t *S = res_base + slot * res_stage;
         if (rb == 2) {
             token_step<D, 2, META_F32>(R + o_ck, R + o_cv, R + o_mkr, R + o_mvr, S + o_rk, S + o_rv, S + o_mks,
-                                       S + o_aks, S + o_mvs, S + o_avs, valid, a.score_scale, q, s);
+                                       S + o_aks, S + o_mvs, S + o_avs, valid, a.score_scale, q, q.lsv, s);
         } else if (RBMAX == 4 && rb == 4) {
             token_step<D, RBMAX, META_F32>(R + o_ck, R + o_cv, R + o_mkr, R + o_mvr, S + o_rk, S + o_rv,
                                            S + o_mks, S + o_aks, S + o_mvs, S + o_avs, valid, a.score_scale,
-                                           q, s);
+                                           q, q.lsv, s);
         } else {
             token_step<D, 0, META_F32>(R + o_ck, R + o_cv, R + o_mkr, R + o_mvr, S, S, S, S, S, S, valid,
-                                       a.score_scale, q, s);
+                                       a.score_scale, q, q.lsv, s);
         }
     }
 
