@@ -93,10 +93,12 @@ typedef struct rq_layout {
 /* Tuning and instrumentation for the decode calls (all fields optional).
  *   split_pages       pages per split-K wave, 1..64 (packed decode; larger is
  *                     RQ_ERR_UNSUPPORTED); 0 = chosen by the library
- *   event_main_begin  hipEvent_t recorded on `stream` just before the split-K
- *                     kernel of each loop, or NULL
- *   event_main_end    hipEvent_t recorded just after it, or NULL
- * With several loops in one call the events bracket the last loop's kernel. */
+ *   event_main_begin  hipEvent_t stamped when the split-K kernel starts, or NULL
+ *   event_main_end    hipEvent_t stamped when it completes, or NULL
+ * The events are recorded by the kernel's own dispatch (hipExtLaunchKernel),
+ * so they add no separate packets to `stream`. With several loops decoded one
+ * kernel per loop they bracket the last loop's kernel; in multi-loop mode,
+ * the last group's kernel. */
 typedef struct rq_decode_opts {
     int32_t split_pages;
     int32_t reserved;

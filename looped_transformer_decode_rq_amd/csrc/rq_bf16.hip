@@ -4,6 +4,8 @@
 // lanes per token, scores with v_dot2_f32_bf16 (exact bf16 products), online
 // softmax, V accumulated in fp32 registers, log-sum-exp combine with the
 // current token.
+#include <hip/hip_ext.h>
+
 #include "rq_device.h"
 #include "rq_internal.h"
 
@@ -181,11 +183,10 @@ hipError_t launch_bf16_d(const Bf16Call &c) {
     s.score_scale = c.softmax_scale * kLog2e;
     s.partials = c.partials;
     dim3 grid((c.nsplit + kWaves - 1) / kWaves, c.H, c.B);
-    if (c.ev_begin && hipEventRecord(c.ev_begin, c.stream) != hipSuccess) return hipErrorInvalidHandle;
-    hipLaunchKernelGGL((rq_bf16_split_kernel<D>), grid, dim3(256), 0, c.stream, s);
+    // the optional events are stamped by the kernel's own dispatch
+    hipExtLaunchKernelGGL((rq_bf16_split_kernel<D>), grid, dim3(256), 0, c.stream, c.ev_begin, c.ev_end, 0, s);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    if (c.ev_end && hipEventRecord(c.ev_end, c.stream) != hipSuccess) return hipErrorInvalidHandle;
     Bf16CombineArgs ca;
     ca.partials = c.partials; ca.nsplit = c.nsplit; ca.split_pages = c.split_pages; ca.max_blocks = c.max_blocks;
     ca.H = c.H; ca.seq_lens = c.seq_lens; ca.q = c.q; ca.tail_k = c.tail_k; ca.tail_v = c.tail_v;

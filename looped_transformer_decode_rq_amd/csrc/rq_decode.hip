@@ -27,6 +27,8 @@
 #include <algorithm>
 #include <type_traits>
 
+#include <hip/hip_ext.h>
+
 #include "rq_device.h"
 #include "rq_internal.h"
 
@@ -1108,9 +1110,13 @@ __global__ __launch_bounds__(1024) void rq_combine_kernel(CombineArgs a) {
 }
 
 // ------------------------------------------------------------- dispatch
+// ev0 / ev1 (may be null) are stamped by the kernel's own dispatch at its
+// start and end (no separate event packets in the stream)
 template <int D>
-hipError_t launch_split_d(const SplitArgs &s, int rb, bool mf, dim3 grid, hipStream_t st) {
-#define RQ_SPLIT(RB_, MF_, G_) hipLaunchKernelGGL((rq_split_kernel<D, RB_, MF_, G_>), grid, dim3(256), 0, st, s)
+hipError_t launch_split_d(const SplitArgs &s, int rb, bool mf, dim3 grid, hipStream_t st, hipEvent_t ev0,
+                          hipEvent_t ev1) {
+#define RQ_SPLIT(RB_, MF_, G_) \
+    hipExtLaunchKernelGGL((rq_split_kernel<D, RB_, MF_, G_>), grid, dim3(256), 0, st, ev0, ev1, 0, s)
 #define RQ_SPLIT_RB(MF_, G_)                          \
     do {                                              \
         if (rb == 0) RQ_SPLIT(0, MF_, G_);            \
@@ -1137,23 +1143,24 @@ hipError_t launch_split_d(const SplitArgs &s, int rb, bool mf, dim3 grid, hipStr
 }
 
 template <int D, bool MF, int G, int RBMAX>
-hipError_t launch_multi_k(const MultiArgs &m, dim3 grid, size_t lds, hipStream_t st) {
-    hipLaunchKernelGGL((rq_multi_kernel<D, MF, G, RBMAX>), grid, dim3(64 * m.nl), lds, st, m);
+hipError_t launch_multi_k(const MultiArgs &m, dim3 grid, size_t lds, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+    hipExtLaunchKernelGGL((rq_multi_kernel<D, MF, G, RBMAX>), grid, dim3(64 * m.nl), (uint32_t)lds, st, ev0, ev1, 0, m);
     return hipGetLastError();
 }
 
 template <int D, bool MF, int RBMAX>
-hipError_t launch_multi_g(const MultiArgs &m, int G, dim3 grid, size_t lds, hipStream_t st) {
+hipError_t launch_multi_g(const MultiArgs &m, int G, dim3 grid, size_t lds, hipStream_t st, hipEvent_t ev0,
+                          hipEvent_t ev1) {
     if constexpr (D == 128) {
-        if (G == 32) return launch_multi_k<D, MF, 32, RBMAX>(m, grid, lds, st);
-        if (G == 64) return launch_multi_k<D, MF, 64, RBMAX>(m, grid, lds, st);
-        return launch_multi_k<D, MF, 128, RBMAX>(m, grid, lds, st);
+        if (G == 32) return launch_multi_k<D, MF, 32, RBMAX>(m, grid, lds, st, ev0, ev1);
+        if (G == 64) return launch_multi_k<D, MF, 64, RBMAX>(m, grid, lds, st, ev0, ev1);
+        return launch_multi_k<D, MF, 128, RBMAX>(m, grid, lds, st, ev0, ev1);
     } else if constexpr (D == 96) {
-        return launch_multi_k<D, MF, 96, RBMAX>(m, grid, lds, st);
+        return launch_multi_k<D, MF, 96, RBMAX>(m, grid, lds, st, ev0, ev1);
     } else {
-        if (G == 16) return launch_multi_k<D, MF, 16, RBMAX>(m, grid, lds, st);
-        if (G == 32) return launch_multi_k<D, MF, 32, RBMAX>(m, grid, lds, st);
-        return launch_multi_k<D, MF, 64, RBMAX>(m, grid, lds, st);
+        if (G == 16) return launch_multi_k<D, MF, 16, RBMAX>(m, grid, lds, st, ev0, ev1);
+        if (G == 32) return launch_multi_k<D, MF, 32, RBMAX>(m, grid, lds, st, ev0, ev1);
+        return launch_multi_k<D, MF, 64, RBMAX>(m, grid, lds, st, ev0, ev1);
     }
 }
 
@@ -1244,13 +1251,12 @@ hipError_t launch_decode_d(const DecodeCall &c) {
             const size_t lds = (size_t)m.nst * slot + 16 * nl;
             dim3 grid(c.nsplit, g.H, c.B);
             const bool last = k == ngroups - 1;
-            if (last && c.ev_begin && hipEventRecord(c.ev_begin, c.stream) != hipSuccess) return hipErrorInvalidHandle;
-            if (mf) err = g4 ? launch_multi_g<D, true, 4>(m, g.G, grid, lds, c.stream)
-                             : launch_multi_g<D, true, 2>(m, g.G, grid, lds, c.stream);
-            else err = g4 ? launch_multi_g<D, false, 4>(m, g.G, grid, lds, c.stream)
-                          : launch_multi_g<D, false, 2>(m, g.G, grid, lds, c.stream);
+            hipEvent_t e0 = last ? c.ev_begin : nullptr, e1 = last ? c.ev_end : nullptr;
+            if (mf) err = g4 ? launch_multi_g<D, true, 4>(m, g.G, grid, lds, c.stream, e0, e1)
+                             : launch_multi_g<D, true, 2>(m, g.G, grid, lds, c.stream, e0, e1);
+            else err = g4 ? launch_multi_g<D, false, 4>(m, g.G, grid, lds, c.stream, e0, e1)
+                          : launch_multi_g<D, false, 2>(m, g.G, grid, lds, c.stream, e0, e1);
             if (err != hipSuccess) return err;
-            if (last && c.ev_end && hipEventRecord(c.ev_end, c.stream) != hipSuccess) return hipErrorInvalidHandle;
             first += nl;
         }
     }
@@ -1269,10 +1275,8 @@ hipError_t launch_decode_d(const DecodeCall &c) {
         const int rb = (l == ref) ? 0 : g.bits[l];
         dim3 grid((c.nsplit + kWaves - 1) / kWaves, g.H, c.B);
         const bool last = i == c.n - 1;
-        if (last && c.ev_begin && hipEventRecord(c.ev_begin, c.stream) != hipSuccess) return hipErrorInvalidHandle;
-        err = launch_split_d<D>(s, rb, mf, grid, c.stream);
+        err = launch_split_d<D>(s, rb, mf, grid, c.stream, last ? c.ev_begin : nullptr, last ? c.ev_end : nullptr);
         if (err != hipSuccess) return err;
-        if (last && c.ev_end && hipEventRecord(c.ev_end, c.stream) != hipSuccess) return hipErrorInvalidHandle;
     }
 
     ca.partials = c.partials; ca.nparts = c.nparts; ca.spp = c.n >= 2 ? 1 : kWaves;
