@@ -8,11 +8,15 @@ packed cache plus the current token's uncompressed K/V, then the deferred
 compression of the current token (all loops) into the paged pool. Inputs are
 seeded synthetic draws resident in HBM before timing starts.
 
-Prints one JSON line (see the keys below). Also measured: the in-library bf16
-baseline step at the same batch (append the token's 4 loops of bf16 K/V + 4
-decode calls), the dominant kernel's bandwidth against the 8 TB/s HBM peak
-(HIP events around each residual-loop split-K launch), and the fp64 oracle
-timed on the host on a bounded sample.
+Prints one JSON line (see the keys below). `value` is this per-loop step (the
+loops of a looped model run one after another). Also measured: the same step
+with the 4 loops' queries in one multi-loop call (each reference page read
+once; `multi_loop`), the in-library bf16 baseline step at the same batch
+(append the token's 4 loops of bf16 K/V + 4 decode calls), the dominant
+kernel's bandwidth against the 8 TB/s HBM peak (HIP events stamped by each
+residual-loop split-K dispatch during the timed steps), measured HBM traffic
+from committed rocprofv3 counter summaries when they match the kernel source,
+and the fp64 oracle timed on the host on a bounded sample.
 """
 from __future__ import annotations
 
@@ -234,8 +238,9 @@ def cpu_baseline(w, rq, budget_s=12.0):
 
 
 def traffic_from_profiles(kernel_src_hash):
-    """HBM bytes per launch of the dominant kernel from committed rocprofv3
-    counter summaries, valid only for the kernel source they were taken on."""
+    """HBM bytes per launch of the decode kernels (residual loop, reference
+    loop, multi-loop) from committed rocprofv3 counter summaries, valid only
+    for the kernel source they were taken on (else None)."""
     p = os.path.join(ROOT, "profiles", "split_kernel_traffic.json")
     try:
         d = json.load(open(p))
@@ -243,7 +248,7 @@ def traffic_from_profiles(kernel_src_hash):
         return None
     if d.get("kernel_src_sha256") != kernel_src_hash:
         return None
-    return d.get("hbm_bytes_per_launch")
+    return d
 
 
 def kernel_src_hash():
@@ -374,7 +379,10 @@ def main():
         log("timing the fp64 oracle on the host")
         cpu = cpu_baseline(w, rq)
 
-    traffic = traffic_from_profiles(kernel_src_hash())
+    traffic = traffic_from_profiles(kernel_src_hash()) if w.name == DEFAULT_WORKLOAD else None
+
+    def measured(key):
+        return None if traffic is None else traffic.get(key, {}).get("hbm_bytes_per_launch")
     line = {
         "metric": "decode-attn tokens/s + effective HBM GB/s (% of peak) on packed INT4/INT2 KV",
         "value": B / t_rq,
@@ -395,15 +403,17 @@ def main():
         "effective_hbm_gbs": step_gbs,
         "effective_hbm_frac": step_gbs / HBM_PEAK_GBS,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured("residual"),
                      "kernel": f"rq_split_kernel<{D},{w.res_bits[0]},{w.meta_dtype == 'f32'}> (residual loop)",
                      "kernel_ms": res_ms, "bytes_per_launch": res_bytes},
-        "ref_loop_kernel": {"ms": ref_ms, "gbs": ref_bytes / (ref_ms * 1e-3) / 1e9, "bytes_per_launch": ref_bytes},
+        "ref_loop_kernel": {"ms": ref_ms, "gbs": ref_bytes / (ref_ms * 1e-3) / 1e9, "bytes_per_launch": ref_bytes,
+                            "traffic": measured("reference")},
         "multi_loop": {"tokens_per_s": B / t_multi, "ms_per_step": t_multi * 1e3,
                        "step": f"one decode call with all {L} loops' queries (each reference page read once) "
                                f"+ encode of {B} new tokens",
                        "kernel": f"rq_multi_kernel<{D}> ({L} waves per split workgroup)",
-                       "kernel_ms": multi_ms, "bytes_per_launch": multi_bytes, "kernel_gbs": multi_gbs,
+                       "kernel_ms": multi_ms, "bytes_per_launch": multi_bytes, "traffic": measured("multi_loop"),
+                       "kernel_gbs": multi_gbs,
                        "kernel_frac_of_peak": multi_gbs / HBM_PEAK_GBS},
         "bf16_baseline": bf16,
         "cpu_baseline": cpu,
