@@ -124,23 +124,31 @@ def setup_rq(w, dev, split_pages):
     return s
 
 
-def rq_step(w, s, split_pages, events=None):
+def rq_step(w, s, split_pages, events=None, fused=True):
+    """One decode step: the loops' attention calls in order; the new tokens'
+    compression rides in the reference-loop call (fused) or follows it."""
     import looped_transformer_decode_rq_amd as R
     tau = 1.0 / np.sqrt(w.head_dim)
+    ref = w.loops - 1
     for l in range(w.loops):
         ev = None if events is None else events[l]
+        enc = dict(kv_new=s["kv_new"], slot_mapping=s["slots_new"]) if fused and l == ref else {}
         R.decode_attention(s["lay"], s["pool"], [l], s["qs"][l], s["rot"], s["d_table"], s["d_seq"],
-                           s["tk"][l], s["tv"][l], tau, s["out"][l], s["ws"], split_pages=split_pages, events=ev)
-    R.encode_pack(s["lay"], s["pool"], s["kv_new"], s["rot"], s["slots_new"])
+                           s["tk"][l], s["tv"][l], tau, s["out"][l], s["ws"], split_pages=split_pages, events=ev,
+                           **enc)
+    if not fused:
+        R.encode_pack(s["lay"], s["pool"], s["kv_new"], s["rot"], s["slots_new"])
 
 
-def rq_multi_step(w, s, split_pages, events=None):
+def rq_multi_step(w, s, split_pages, events=None, fused=True):
     import looped_transformer_decode_rq_amd as R
     tau = 1.0 / np.sqrt(w.head_dim)
+    enc = dict(kv_new=s["kv_new"], slot_mapping=s["slots_new"]) if fused else {}
     R.decode_attention(s["lay"], s["pool"], list(range(w.loops)), s["q_all"], s["rot"], s["d_table"], s["d_seq"],
                        s["tk_all"], s["tv_all"], tau, s["out_all"], s["ws_all"], split_pages=split_pages,
-                       events=events)
-    R.encode_pack(s["lay"], s["pool"], s["kv_new"], s["rot"], s["slots_new"])
+                       events=events, **enc)
+    if not fused:
+        R.encode_pack(s["lay"], s["pool"], s["kv_new"], s["rot"], s["slots_new"])
 
 
 def setup_bf16(w, dev, rq, split_pages):
@@ -268,6 +276,9 @@ def main():
     ap.add_argument("--split-pages", type=int, default=0)
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--separate-encode", action="store_true",
+                    help="compress the new tokens in a launch of their own after the attention calls "
+                         "instead of in the reference-loop call's launch")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after setup, copy a buffer of this many MiB device to device (a plain copy of known "
                          "size, used to calibrate HBM byte counters)")
@@ -300,7 +311,8 @@ def main():
     pairs = {(k, l): (ev.create(), ev.create()) for k in range(args.steps) for l in range(L)}
 
     def rq_fn(k):
-        rq_step(w, rq, args.split_pages, None if k is None else [pairs[(k, l)] for l in range(L)])
+        rq_step(w, rq, args.split_pages, None if k is None else [pairs[(k, l)] for l in range(L)],
+                fused=not args.separate_encode)
 
     log("timing packed step")
     t_rq = timed(rq_fn, args.steps, args.warmup)
@@ -333,7 +345,7 @@ def main():
     mpairs = {k: (ev.create(), ev.create()) for k in range(args.steps)}
 
     def multi_fn(k):
-        rq_multi_step(w, rq, args.split_pages, None if k is None else mpairs[k])
+        rq_multi_step(w, rq, args.split_pages, None if k is None else mpairs[k], fused=not args.separate_encode)
 
     log("timing packed multi-loop step")
     t_multi = timed(multi_fn, args.steps, args.warmup)
@@ -345,6 +357,8 @@ def main():
     multi_ms = float(np.mean(mk))
     multi_bytes = (stored * B * H * N + L * B * H * qp + B * N // 16 * 4
                    + (L - 1) * B * H * nsplit * (2 + 2 * D) * 4 + B * H * nsplit * (2 + D) * 4)
+    if not args.separate_encode:                 # the new tokens' encode runs in this launch
+        multi_bytes += L * 2 * B * H * D * kvsz + B * H * stored
     multi_gbs = multi_bytes / (multi_ms * 1e-3) / 1e9
     log(f"multi-loop step {t_multi * 1e3:.3f} ms; multi-loop kernel {multi_ms:.3f} ms ({multi_gbs:.0f} GB/s)")
 
@@ -399,7 +413,8 @@ def main():
         "config": {"workload": w.name, "layers": 1, "batch": B, "context": N, "heads": H, "head_dim": D,
                    "loops": L, "group_size": w.group_size, "res_bits": list(w.res_bits), "block_size": 16,
                    "split_pages": args.split_pages,
-                   "step": "4 per-loop decode calls (each + bf16 current token) + encode of 16 new tokens"},
+                   "step": "4 per-loop decode calls (each + bf16 current token) + encode of 16 new tokens "
+                           + ("(own launch)" if args.separate_encode else "(in the reference-loop call's launch)")},
         "effective_hbm_gbs": step_gbs,
         "effective_hbm_frac": step_gbs / HBM_PEAK_GBS,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -410,7 +425,7 @@ def main():
                             "traffic": measured("reference")},
         "multi_loop": {"tokens_per_s": B / t_multi, "ms_per_step": t_multi * 1e3,
                        "step": f"one decode call with all {L} loops' queries (each reference page read once) "
-                               f"+ encode of {B} new tokens",
+                               f"+ encode of {B} new tokens in the same launch",
                        "kernel": f"rq_multi_kernel<{D}> ({L} waves per split workgroup)",
                        "kernel_ms": multi_ms, "bytes_per_launch": multi_bytes, "traffic": measured("multi_loop"),
                        "kernel_gbs": multi_gbs,

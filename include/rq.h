@@ -179,6 +179,30 @@ rq_status rq_decode_attention_ex(const rq_layout *layout, const void *pool,
                                  void *workspace, size_t workspace_bytes,
                                  const rq_decode_opts *opts, void *stream);
 
+/* Decode attention and the deferred compression of the current tokens in the
+ * same launches (rit.work summary: a token is compressed once, after its final
+ * pass; here that write runs beside the final-loop attention instead of after
+ * it). Equivalent to rq_decode_attention_ex(...) followed by
+ * rq_encode_pack(layout, pool, kv_new, rot, slot_mapping, num_tokens, stream),
+ * with bit-identical outputs and pool bytes, provided that no new token's slot
+ * holds one of the cached tokens this call attends (the new tokens are the
+ * current ones, attended through tail_k/tail_v; a slot at position seq_len of
+ * its sequence satisfies this). The encode's workgroups join the launch of the
+ * reference loop's split kernel (per-loop calls) or of the last multi-loop
+ * kernel; without a reference-loop call and with n_loops == 1 they get a launch
+ * of their own after it.
+ *   pool, kv_new, slot_mapping, num_tokens  as in rq_encode_pack (pool is
+ *                written); num_tokens == 0 makes this rq_decode_attention_ex
+ *   other arguments as in rq_decode_attention_ex. */
+rq_status rq_decode_attention_encode(const rq_layout *layout, void *pool, const int32_t *loops,
+                                     int32_t n_loops, const void *q, const float *rot,
+                                     const int32_t *block_table, const int32_t *seq_lens, int32_t batch,
+                                     int32_t max_blocks_per_seq, const void *tail_k, const void *tail_v,
+                                     float softmax_scale, float *out, void *workspace,
+                                     size_t workspace_bytes, const void *kv_new,
+                                     const int64_t *slot_mapping, int32_t num_tokens,
+                                     const rq_decode_opts *opts, void *stream);
+
 /* Uncompressed baseline (for the speed ratio): the same decode attention over
  * a paged bf16 cache of ONE loop.
  *   k_cache, v_cache  [num_blocks][H][16][D] bf16

@@ -20,7 +20,7 @@ RQ_MAX_LOOPS = 16
 EXPORTED = [
     "rq_status_string", "rq_layout_check", "rq_pool_bytes", "rq_record_bytes", "rq_record_offset",
     "rq_encode_pack", "rq_decode_workspace_bytes", "rq_decode_attention", "rq_decode_attention_ex",
-    "rq_bf16_workspace_bytes", "rq_bf16_decode_attention", "rq_bf16_decode_attention_ex", "rq_bf16_write",
+    "rq_decode_attention_encode", "rq_bf16_workspace_bytes", "rq_bf16_decode_attention", "rq_bf16_decode_attention_ex", "rq_bf16_write",
 ]
 
 
@@ -65,6 +65,9 @@ def lib():
                                               P, P, c_float, P, P, c_size_t, P]),
             "rq_decode_attention_ex": (c_int32, [POINTER(RqLayout), P, P, c_int32, P, P, P, P, c_int32, c_int32,
                                                  P, P, c_float, P, P, c_size_t, POINTER(RqDecodeOpts), P]),
+            "rq_decode_attention_encode": (c_int32, [POINTER(RqLayout), P, P, c_int32, P, P, P, P, c_int32, c_int32,
+                                                     P, P, c_float, P, P, c_size_t, P, P, c_int32,
+                                                     POINTER(RqDecodeOpts), P]),
             "rq_bf16_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32]),
             "rq_bf16_decode_attention": (c_int32, [c_int32, c_int32, c_int32, c_int32, P, P, P, P, P, c_int32,
                                                    c_int32, P, P, c_float, P, P, c_size_t, P]),
@@ -183,8 +186,11 @@ def _opts(split_pages, events):
 
 
 def decode_attention(layout, pool, loops, q, rot, block_table, seq_lens, tail_k, tail_v,
-                     softmax_scale, out, workspace, split_pages=0, events=None, stream=None):
-    """rq_decode_attention_ex; loops is a host sequence of loop indices."""
+                     softmax_scale, out, workspace, split_pages=0, events=None, stream=None,
+                     kv_new=None, slot_mapping=None):
+    """rq_decode_attention_ex; loops is a host sequence of loop indices. With
+    kv_new / slot_mapping (as in encode_pack) it is rq_decode_attention_encode:
+    the current tokens are also compressed into `pool`, in the same launches."""
     n = len(loops)
     arr = (c_int32 * max(n, 1))(*[int(x) for x in loops])
     B, mb = int(block_table.shape[0]), int(block_table.shape[1])
@@ -205,10 +211,24 @@ def decode_attention(layout, pool, loops, q, rot, block_table, seq_lens, tail_k,
     if any(int(l) != layout.num_loops - 1 for l in loops):
         _check_rot(layout, rot)
     o = _opts(split_pages, events)
-    _check("rq_decode_attention", lib().rq_decode_attention_ex(
+    if kv_new is None and slot_mapping is None:
+        _check("rq_decode_attention", lib().rq_decode_attention_ex(
+            ctypes.byref(layout), _ptr(pool), arr, n, _ptr(q), _ptr(rot), _ptr(block_table), _ptr(seq_lens),
+            B, mb, _ptr(tail_k), _ptr(tail_v), float(softmax_scale), _ptr(out), _ptr(workspace), ws_bytes,
+            ctypes.byref(o), _stream(stream)))
+        return
+    _need(kv_new is not None and slot_mapping is not None, "kv_new and slot_mapping go together")
+    L = layout.num_loops
+    T = int(kv_new.shape[2])
+    _need(tuple(kv_new.shape) == (L, 2, T, H, D) and kv_new.element_size() == _kv_bytes(layout)
+          and kv_new.is_contiguous(), f"kv_new must be contiguous [{L}][2][T][{H}][{D}] in kv_dtype")
+    _need(slot_mapping.numel() == T and slot_mapping.element_size() == 8, "slot_mapping must be int64 [T]")
+    if L > 1:
+        _check_rot(layout, rot)
+    _check("rq_decode_attention_encode", lib().rq_decode_attention_encode(
         ctypes.byref(layout), _ptr(pool), arr, n, _ptr(q), _ptr(rot), _ptr(block_table), _ptr(seq_lens),
         B, mb, _ptr(tail_k), _ptr(tail_v), float(softmax_scale), _ptr(out), _ptr(workspace), ws_bytes,
-        ctypes.byref(o), _stream(stream)))
+        _ptr(kv_new), _ptr(slot_mapping), T, ctypes.byref(o), _stream(stream)))
 
 
 def bf16_workspace_bytes(num_heads, head_dim, batch, max_blocks_per_seq, split_pages=0) -> int:

@@ -141,15 +141,17 @@ size_t rq_decode_workspace_bytes(const rq_layout *layout, int32_t n_loops, int32
     return decode_ws(g, n_loops, batch, max_blocks_per_seq, sp);
 }
 
-rq_status rq_decode_attention_ex(const rq_layout *layout, const void *pool, const int32_t *loops,
-                                 int32_t n_loops, const void *q, const float *rot,
-                                 const int32_t *block_table, const int32_t *seq_lens, int32_t batch,
-                                 int32_t max_blocks_per_seq, const void *tail_k, const void *tail_v,
-                                 float softmax_scale, float *out, void *workspace, size_t workspace_bytes,
-                                 const rq_decode_opts *opts, void *stream) {
+static rq_status decode_impl(const rq_layout *layout, const void *pool, const int32_t *loops, int32_t n_loops,
+                             const void *q, const float *rot, const int32_t *block_table, const int32_t *seq_lens,
+                             int32_t batch, int32_t max_blocks_per_seq, const void *tail_k, const void *tail_v,
+                             float softmax_scale, float *out, void *workspace, size_t workspace_bytes,
+                             const rq_decode_opts *opts, void *stream, void *enc_pool, const void *kv_new,
+                             const int64_t *slot_mapping, int32_t num_tokens) {
     Geom g;
     rq_status st = make_geom(layout, &g);
     if (st != RQ_OK) return st;
+    if (num_tokens < 0 || num_tokens > (1 << 30) / 16) return RQ_ERR_SHAPE;
+    if (num_tokens > 0 && (!kv_new || !slot_mapping || !enc_pool || (g.L > 1 && !rot))) return RQ_ERR_NULL;
     if (!loops) return RQ_ERR_NULL;
     if (n_loops < 1 || n_loops > RQ_MAX_LOOPS || batch < 0 || batch > 65535 || max_blocks_per_seq < 1)
         return RQ_ERR_SHAPE;
@@ -186,7 +188,31 @@ rq_status rq_decode_attention_ex(const rq_layout *layout, const void *pool, cons
     c.ev_begin = opts ? (hipEvent_t)opts->event_main_begin : nullptr;
     c.ev_end = opts ? (hipEvent_t)opts->event_main_end : nullptr;
     c.stream = (hipStream_t)stream;
+    c.enc_pool = (uint8_t *)enc_pool; c.enc_kv = kv_new; c.enc_slots = slot_mapping; c.enc_T = num_tokens;
     return launch_decode(c) == hipSuccess ? RQ_OK : RQ_ERR_HIP;
+}
+
+rq_status rq_decode_attention_ex(const rq_layout *layout, const void *pool, const int32_t *loops,
+                                 int32_t n_loops, const void *q, const float *rot,
+                                 const int32_t *block_table, const int32_t *seq_lens, int32_t batch,
+                                 int32_t max_blocks_per_seq, const void *tail_k, const void *tail_v,
+                                 float softmax_scale, float *out, void *workspace, size_t workspace_bytes,
+                                 const rq_decode_opts *opts, void *stream) {
+    return decode_impl(layout, pool, loops, n_loops, q, rot, block_table, seq_lens, batch, max_blocks_per_seq,
+                       tail_k, tail_v, softmax_scale, out, workspace, workspace_bytes, opts, stream, nullptr,
+                       nullptr, nullptr, 0);
+}
+
+rq_status rq_decode_attention_encode(const rq_layout *layout, void *pool, const int32_t *loops, int32_t n_loops,
+                                     const void *q, const float *rot, const int32_t *block_table,
+                                     const int32_t *seq_lens, int32_t batch, int32_t max_blocks_per_seq,
+                                     const void *tail_k, const void *tail_v, float softmax_scale, float *out,
+                                     void *workspace, size_t workspace_bytes, const void *kv_new,
+                                     const int64_t *slot_mapping, int32_t num_tokens, const rq_decode_opts *opts,
+                                     void *stream) {
+    return decode_impl(layout, pool, loops, n_loops, q, rot, block_table, seq_lens, batch, max_blocks_per_seq,
+                       tail_k, tail_v, softmax_scale, out, workspace, workspace_bytes, opts, stream, pool, kv_new,
+                       slot_mapping, num_tokens);
 }
 
 rq_status rq_decode_attention(const rq_layout *layout, const void *pool, const int32_t *loops, int32_t n_loops,

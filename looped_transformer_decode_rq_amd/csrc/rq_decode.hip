@@ -30,6 +30,7 @@
 #include <hip/hip_ext.h>
 
 #include "rq_device.h"
+#include "rq_encode_body.h"
 #include "rq_internal.h"
 
 namespace rq {
@@ -189,7 +190,13 @@ struct SplitArgs {
     const uint8_t *qpack;   // this call: [B][H][qpack_bytes]
     float *partials;        // this call: [B][H][nwg][2 + 2D]
     int nsplit, split_pages;
+    int nwg;                // split workgroups per (sequence, head): the partials' row stride
     float score_scale;      // softmax_scale * log2(e)
+    // encode work items riding in this launch (reference-loop kernel only):
+    // workgroups with blockIdx.x >= enc_x0 run item (blockIdx.x - enc_x0) *
+    // gridDim.z + blockIdx.z of enc_items, for head blockIdx.y
+    int enc_x0, enc_items, enc_kvf;
+    enc::EncArgs enc;
 };
 
 template <int NB>
@@ -589,10 +596,26 @@ __global__ __launch_bounds__(256) void rq_split_kernel(SplitArgs a) {
     constexpr int RES_NB = RB ? CPL * RB / 8 : 4;
     constexpr int MSZ = SG::MSZ, NG = SG::NG, NST = SG::NST, NI = SG::NI;
     constexpr int PF = partial_floats(D);
-    __shared__ __attribute__((aligned(16))) uint8_t stage[kWaves][NST][SG::BYTES];
+    // the LDS stages; in the reference-loop kernel also the scratch of an encode work item
+    constexpr int STAGE_BYTES = kWaves * NST * SG::BYTES;
+    constexpr int LDS_BYTES = (RB == 0 && enc::kEncLdsBytes > STAGE_BYTES) ? enc::kEncLdsBytes : STAGE_BYTES;
+    __shared__ __attribute__((aligned(16))) uint8_t stage_mem[LDS_BYTES];
+    auto stage = reinterpret_cast<uint8_t (*)[NST][SG::BYTES]>(stage_mem);
     // after the page loop: wave w's partial (m, l, acc_ref, acc_res) in its own stages
     auto wp = [&](int w) -> float * { return (float *)&stage[w][0][0]; };
 
+    if constexpr (RB == 0) {
+        if ((int)blockIdx.x >= a.enc_x0) {
+            // an encode work item of the current tokens, run in the LDS stages
+            const int e = ((int)blockIdx.x - a.enc_x0) * (int)gridDim.z + (int)blockIdx.z;
+            if (e < a.enc_items) {
+                const int nz = 2 * (a.enc.L > 1 ? a.enc.L - 1 : 1);
+                if (a.enc_kvf) enc::encode_item<true, META_F32>(a.enc, e / nz, blockIdx.y, e % nz, stage_mem, kWaves);
+                else enc::encode_item<false, META_F32>(a.enc, e / nz, blockIdx.y, e % nz, stage_mem, kWaves);
+            }
+            return;
+        }
+    }
     // wave index made provably wave-uniform, so the page loop is a scalar loop
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int split = blockIdx.x * kWaves + wave;
@@ -720,7 +743,7 @@ __global__ __launch_bounds__(256) void rq_split_kernel(SplitArgs a) {
     float e[kWaves];
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) e[w] = M == kNegInf ? 0.f : fast_exp2(wp(w)[0] - M);
-    float *out = a.partials + (((int64_t)b * H + h) * gridDim.x + blockIdx.x) * PF;
+    float *out = a.partials + (((int64_t)b * H + h) * a.nwg + blockIdx.x) * PF;
     constexpr int NV = RB ? 2 * D : D;
     for (int v = threadIdx.x; v < NV; v += 256) {
         float acc = 0.f;
@@ -753,6 +776,8 @@ struct MultiArgs {
     float *partials;          // group's first call: [nl][B][H][nsplit][2 + 2D]
     int B, nsplit, split_pages, nst;
     float score_scale;
+    int enc_x0, enc_items, enc_kvf;   // encode work items riding in this launch (as in SplitArgs)
+    enc::EncArgs enc;
 };
 
 // Stage layout of the multi-loop kernel. The reference stage is shared by the
@@ -803,6 +828,16 @@ __global__ __launch_bounds__(64 * kMaxMultiLoops) void rq_multi_kernel(MultiArgs
     constexpr int NST_MAX = 8;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
+    if ((int)blockIdx.x >= a.enc_x0) {
+        // an encode work item of the current tokens (LDS sized for it by the host)
+        const int e = ((int)blockIdx.x - a.enc_x0) * (int)gridDim.z + (int)blockIdx.z;
+        if (e < a.enc_items) {
+            const int nz = 2 * (a.enc.L > 1 ? a.enc.L - 1 : 1);
+            if (a.enc_kvf) enc::encode_item<true, META_F32>(a.enc, e / nz, blockIdx.y, e % nz, smem, a.nl);
+            else enc::encode_item<false, META_F32>(a.enc, e / nz, blockIdx.y, e % nz, smem, a.nl);
+        }
+        return;
+    }
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int H = a.H, nl = a.nl, nst = a.nst;
@@ -815,14 +850,20 @@ __global__ __launch_bounds__(64 * kMaxMultiLoops) void rq_multi_kernel(MultiArgs
     const int cnt = p1 - p0;
     const int steps = (cnt + PPI - 1) / PPI;
 
-    const int rb = __builtin_amdgcn_readfirstlane(a.rb[wave]);
-    const int res_off = a.res_off[wave], res_rec = a.res_rec[wave];
+    // Loop call of this wave. The calls do unequal work (the reference loop has
+    // no residual), so the wave -> call assignment rotates from workgroup to
+    // workgroup: the waves a SIMD hosts from different workgroups then carry a
+    // mix of calls instead of always the same one.
+    const uint32_t lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    const int call = __builtin_amdgcn_readfirstlane((int)((wave + (lin ^ (lin >> 8))) % (uint32_t)nl));
+    const int rb = __builtin_amdgcn_readfirstlane(a.rb[call]);
+    const int res_off = a.res_off[call], res_rec = a.res_rec[call];
     const int tok_i = lane / LPT, q4 = lane % LPT;
     const int page_in_step = tok_i >> 4, tok = tok_i & 15;
     const int g = (q4 * CPL) / G;
 
     QueryRegs<D> q;
-    load_query<D, true>(a.qpack + (((int64_t)wave * a.B + b) * H + h) * qpack_bytes(D), q4, q);
+    load_query<D, true>(a.qpack + (((int64_t)call * a.B + b) * H + h) * qpack_bytes(D), q4, q);
 
     int tbl = -1;
     if (lane < cnt) {
@@ -966,7 +1007,7 @@ __global__ __launch_bounds__(64 * kMaxMultiLoops) void rq_multi_kernel(MultiArgs
 
     reduce_slots<D, true>(s);
     if (lane < LPT) {
-        float *out = a.partials + ((((int64_t)wave * a.B + b) * H + h) * a.nsplit + split) * PF;
+        float *out = a.partials + ((((int64_t)call * a.B + b) * H + h) * a.nsplit + split) * PF;
         if (lane == 0) { out[0] = s.m; out[1] = s.lsum; }
 #pragma unroll
         for (int i = 0; i < CPL; ++i) out[2 + q4 * CPL + i] = s.accr[i];
@@ -1248,9 +1289,18 @@ hipError_t launch_decode_d(const DecodeCall &c) {
                 slot = g4 ? multi_slot_bytes<D, false, 4>(g.G, nl) : multi_slot_bytes<D, false, 2>(g.G, nl);
             }
             if (m.nst < 2) return hipErrorInvalidConfiguration;
-            const size_t lds = (size_t)m.nst * slot + 16 * nl;
-            dim3 grid(c.nsplit, g.H, c.B);
+            size_t lds = (size_t)m.nst * slot + 16 * nl;
             const bool last = k == ngroups - 1;
+            // the current tokens' encode rides in the last group's launch
+            m.enc_x0 = c.nsplit; m.enc_items = 0; m.enc_kvf = kvf ? 1 : 0;
+            int ex = 0;
+            if (last && c.enc_T > 0) {
+                enc::fill_args(m.enc, g, c.enc_pool, c.enc_kv, c.rot, c.enc_slots, c.enc_T);
+                m.enc_items = (c.enc_T + enc::kTT - 1) / enc::kTT * 2 * (g.L > 1 ? g.L - 1 : 1);
+                ex = (m.enc_items + c.B - 1) / c.B;
+                lds = std::max(lds, (size_t)enc::kEncLdsBytes);
+            }
+            dim3 grid(c.nsplit + ex, g.H, c.B);
             hipEvent_t e0 = last ? c.ev_begin : nullptr, e1 = last ? c.ev_end : nullptr;
             if (mf) err = g4 ? launch_multi_g<D, true, 4>(m, g.G, grid, lds, c.stream, e0, e1)
                              : launch_multi_g<D, true, 2>(m, g.G, grid, lds, c.stream, e0, e1);
@@ -1260,6 +1310,7 @@ hipError_t launch_decode_d(const DecodeCall &c) {
             first += nl;
         }
     }
+    bool enc_done = c.n >= 2;   // multi-loop mode: attached to the last group above
     for (int i = 0; i < (c.n >= 2 ? 0 : c.n); ++i) {
         const int l = c.loops[i];
         SplitArgs s;
@@ -1273,12 +1324,31 @@ hipError_t launch_decode_d(const DecodeCall &c) {
         s.nsplit = c.nsplit; s.split_pages = c.split_pages;
         s.score_scale = score_scale;
         const int rb = (l == ref) ? 0 : g.bits[l];
-        dim3 grid((c.nsplit + kWaves - 1) / kWaves, g.H, c.B);
+        const int nwg = (c.nsplit + kWaves - 1) / kWaves;
+        s.nwg = nwg;
+        // the current tokens' encode rides in the first reference-loop launch
+        s.enc_x0 = nwg; s.enc_items = 0; s.enc_kvf = kvf ? 1 : 0;
+        int ex = 0;
+        if (l == ref && c.enc_T > 0 && !enc_done) {
+            enc::fill_args(s.enc, g, c.enc_pool, c.enc_kv, c.rot, c.enc_slots, c.enc_T);
+            s.enc_items = (c.enc_T + enc::kTT - 1) / enc::kTT * 2 * (g.L > 1 ? g.L - 1 : 1);
+            ex = (s.enc_items + c.B - 1) / c.B;
+            enc_done = true;
+        }
+        dim3 grid(nwg + ex, g.H, c.B);
         const bool last = i == c.n - 1;
         err = launch_split_d<D>(s, rb, mf, grid, c.stream, last ? c.ev_begin : nullptr, last ? c.ev_end : nullptr);
         if (err != hipSuccess) return err;
     }
 
+    if (c.enc_T > 0 && !enc_done) {
+        // no reference-loop call to ride in: the encoder's own launch
+        EncodeCall ec;
+        ec.g = &g; ec.pool = c.enc_pool; ec.kv_new = c.enc_kv; ec.rot = c.rot; ec.slots = c.enc_slots;
+        ec.T = c.enc_T; ec.stream = c.stream;
+        err = launch_encode(ec);
+        if (err != hipSuccess) return err;
+    }
     ca.partials = c.partials; ca.nparts = c.nparts; ca.spp = c.n >= 2 ? 1 : kWaves;
     ca.split_pages = c.split_pages;
     ca.max_blocks = c.max_blocks; ca.seq_lens = c.seq_lens;

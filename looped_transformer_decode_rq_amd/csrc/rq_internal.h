@@ -59,6 +59,11 @@ struct DecodeCall {
     int split_pages, nsplit, nparts;   // pages per split, splits, partials per row
     hipEvent_t ev_begin, ev_end;
     hipStream_t stream;
+    // optional encode of the current tokens in the same launches (enc_T = 0: none)
+    uint8_t *enc_pool;
+    const void *enc_kv;
+    const int64_t *enc_slots;
+    int enc_T;
 };
 
 hipError_t launch_decode(const DecodeCall &c);

@@ -145,6 +145,27 @@ def test_decode_validation(L):
         assert L.rq_decode_attention_ex(*a) == want
 
 
+def test_decode_encode_validation(L):
+    lay = _lay(LAYOUTS[1])
+    loops = (ctypes.c_int32 * 1)(3)
+    ws = R.decode_workspace_bytes(lay, 1, 4, 10)
+    base = [ctypes.byref(lay), _fake(0), loops, 1, _fake(1), _fake(2), _fake(3), _fake(4), 4, 10,
+            None, None, c_float(0.1), _fake(5), _fake(6), ws, _fake(7), _fake(8), 4, None, None]
+
+    def call(**kw):
+        a = list(base)
+        idx = dict(pool=1, rot=5, kv=16, slots=17, T=18)
+        for k, v in kw.items():
+            a[idx[k]] = v
+        return L.rq_decode_attention_encode(*a)
+
+    assert call(kv=None) == -1
+    assert call(slots=None) == -1
+    assert call(pool=None) == -1
+    assert call(rot=None) == -1                # L > 1: the encode needs R
+    assert call(T=-1) == -2
+
+
 def test_encode_validation(L):
     lay = _lay(LAYOUTS[1])
     f = L.rq_encode_pack
