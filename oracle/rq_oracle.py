@@ -21,6 +21,10 @@ R11 little-endian packing: element i sits in the low bits first.
 R12 softmax scale 1/sqrt(D) by default, attention over every cached token plus
     the current (uncompressed) token.
 R13 reconstruction of loop l: alpha * xref_hat + R^T dequant(residual).
+R14 the direct per-loop baseline (the "quantize every loop on its own"
+    approach the pages compare against): loop l's K/V quantized with the
+    quantizer of R6-R10 at its own bit width, no reference, no alpha, no
+    rotation; stored in the same paged record format without the alpha field.
 """
 from __future__ import annotations
 
@@ -33,7 +37,7 @@ __all__ = [
     "Encoded", "encode", "reconstruct", "pack_codes", "unpack_codes",
     "PoolLayout", "write_tokens", "read_pages", "gather_sequence",
     "reconstruct_sequence", "attention", "decode_attention",
-    "bf16_pool_write", "bf16_decode_attention",
+    "bf16_pool_write", "bf16_decode_attention", "DirectEncoded", "encode_direct",
 ]
 
 
@@ -183,6 +187,20 @@ def reconstruct(enc: Encoded, rot32: np.ndarray) -> np.ndarray:
     return np.stack(out)
 
 
+@dataclass
+class DirectEncoded:
+    q: list                   # per loop l: Quantized of x_l itself [2][T][H][D]
+    G: int
+    meta: str
+
+
+def encode_direct(kv: np.ndarray, bits, G: int, meta: str) -> DirectEncoded:
+    """The direct per-loop baseline (reading R14): every loop's K/V quantized
+    on its own, with loop l at bits[l] (2 or 4)."""
+    kv = np.asarray(kv, dtype=np.float64)
+    return DirectEncoded(q=[quantize(kv[l], int(bits[l]), G, meta) for l in range(kv.shape[0])], G=G, meta=meta)
+
+
 # ------------------------------------------------------------------ packing
 def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
     """Pack codes along the last axis, little-endian inside each byte (R11).
@@ -225,18 +243,30 @@ class PoolLayout:
     cache management itself (block table, slots) is the usual one; the pages
     only change what is stored per token (rit.work summary: scheduler and paged
     management stay as they are).
+
+    Direct mode (``direct_bits`` given, reading R14): every loop's record holds
+    its own codes at ``direct_bits[l]`` bits and the (scale, zero) pairs, with
+    no alpha field; ``res_bits`` is then unused.
     """
 
-    def __init__(self, H, D, G, L, res_bits, meta, num_blocks, block_size=16):
+    def __init__(self, H, D, G, L, res_bits, meta, num_blocks, block_size=16, direct_bits=None):
         self.H, self.D, self.G, self.L = int(H), int(D), int(G), int(L)
-        self.res_bits = tuple(int(b) for b in res_bits)
-        assert len(self.res_bits) == self.L - 1
+        self.direct = direct_bits is not None
+        if self.direct:
+            self.dbits = tuple(int(b) for b in direct_bits)
+            assert len(self.dbits) == self.L
+            self.res_bits = ()
+        else:
+            self.res_bits = tuple(int(b) for b in res_bits)
+            assert len(self.res_bits) == self.L - 1
         self.meta = meta
         self.msz = 2 if meta == "f16" else 4
         self.num_blocks = int(num_blocks)
         self.bs = int(block_size)
 
     def bits(self, l):
+        if self.direct:
+            return self.dbits[l]
         return 4 if l == self.L - 1 else self.res_bits[l]
 
     def code_bytes(self, l):
@@ -246,7 +276,7 @@ class PoolLayout:
         return self.bs * 2 * (self.D // self.G) * self.msz
 
     def alpha_bytes(self, l):
-        return self.bs * self.msz if l < self.L - 1 else 0
+        return self.bs * self.msz if (l < self.L - 1 and not self.direct) else 0
 
     def rec_bytes(self, l):
         n = self.code_bytes(l) + self.meta_bytes() + self.alpha_bytes(l)
@@ -279,8 +309,10 @@ def write_tokens(pool: np.ndarray, lay: PoolLayout, enc: Encoded, slots: np.ndar
     page, off = slots // lay.bs, slots % lay.bs
     mdt = _meta_np(lay.meta)
     ng = lay.D // lay.G
+    direct = isinstance(enc, DirectEncoded)
+    assert direct == lay.direct
     for l in range(lay.L):
-        q = enc.ref if l == lay.L - 1 else enc.res[l]
+        q = enc.q[l] if direct else (enc.ref if l == lay.L - 1 else enc.res[l])
         b = lay.bits(l)
         tb = lay.D * b // 8
         packed = pack_codes(q.codes, b)                     # [2][T][H][tb]
@@ -293,7 +325,7 @@ def write_tokens(pool: np.ndarray, lay: PoolLayout, enc: Encoded, slots: np.ndar
                 mb = np.ascontiguousarray(meta.astype(mdt)).view(np.uint8).reshape(len(slots), -1)
                 midx = (base + lay.code_bytes(l) + off * (2 * ng * lay.msz))[:, None] + np.arange(mb.shape[1])
                 pool[midx] = mb
-                if l < lay.L - 1:
+                if lay.alpha_bytes(l):
                     ab = np.ascontiguousarray(enc.alpha[l][kv, :, h].astype(mdt)).view(np.uint8).reshape(len(slots), -1)
                     aidx = (base + lay.code_bytes(l) + lay.meta_bytes() + off * lay.msz)[:, None] + np.arange(lay.msz)
                     pool[aidx] = ab
@@ -316,7 +348,7 @@ def read_pages(pool: np.ndarray, lay: PoolLayout, pages, head: int, l: int, kv: 
     mbytes = raw[:, lay.code_bytes(l): lay.code_bytes(l) + lay.meta_bytes()]
     meta = np.ascontiguousarray(mbytes).view(mdt).astype(np.float64).reshape(len(pages), lay.bs, lay.D // lay.G, 2)
     alpha = None
-    if l < lay.L - 1:
+    if lay.alpha_bytes(l):
         a0 = lay.code_bytes(l) + lay.meta_bytes()
         alpha = np.ascontiguousarray(raw[:, a0: a0 + lay.alpha_bytes(l)]).view(mdt).astype(np.float64).reshape(len(pages), lay.bs)
     return codes, meta[..., 0], meta[..., 1], alpha
@@ -339,6 +371,12 @@ def reconstruct_sequence(pool, lay: PoolLayout, table_row, n_tokens: int, head: 
     and its own residual). rot32_h is [2][D][D] for this head.
     """
     out = []
+    if lay.direct:
+        # direct baseline (R14): loop l's own record, nothing else
+        for kv in range(2):
+            c, s, z, _ = gather_sequence(pool, lay, table_row, n_tokens, head, l, kv)
+            out.append(dequantize(c, s, z, lay.G))
+        return out[0], out[1]
     R = np.asarray(rot32_h, dtype=np.float32).astype(np.float64)
     for kv in range(2):
         c, s, z, _ = gather_sequence(pool, lay, table_row, n_tokens, head, lay.L - 1, kv)
@@ -387,7 +425,7 @@ def decode_attention(pool, lay: PoolLayout, l: int, q, rot32, table, seq_lens, t
     todo = pairs if pairs is not None else [(b, h) for b in range(B) for h in range(H)]
     for b, h in todo:
         n = int(seq_lens[b])
-        K, V = reconstruct_sequence(pool, lay, table[b], n, h, l, rot32[h])
+        K, V = reconstruct_sequence(pool, lay, table[b], n, h, l, None if rot32 is None else rot32[h])
         tk = None if tail_k is None else tail_k[b, h]
         tv = None if tail_v is None else tail_v[b, h]
         out[b, h] = attention(q[b, h], K, V, tau, tk, tv)

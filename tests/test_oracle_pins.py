@@ -345,3 +345,61 @@ def test_bf16_baseline_attention():
         for h in range(H):
             ref = O.attention(q[b, h], kv[1, 0, b, :N, h], kv[1, 1, b, :N, h], 0.1)
             np.testing.assert_allclose(out[b, h], ref, atol=1e-13)
+
+
+# ------------------------------------------------ direct per-loop baseline
+def test_direct_layout_hand_derived():
+    """Direct mode record bytes derived by hand: D=4, G=4, loops (INT2, INT4),
+    fp16 metadata, one block, one head. Loop 0 record: 16 tokens x 1 B codes +
+    16 x (scale, zero) x 2 B = 80 B (no alpha); loop 1: 16 x 2 B + 64 = 96 B.
+    Token at slot 5 of loop 0, K = [0, 1, 2, 3]: scale 1, zero 0, codes
+    0,1,2,3 -> one byte 0b11_10_01_00 = 0xE4 at record byte 5; scale 1.0 is
+    f16 0x3C00 and zero 0x0000 at record bytes 16 + 5*4 .. +3 (little
+    endian: 00 3C 00 00)."""
+    lay = O.PoolLayout(1, 4, 4, 2, (), "f16", 1, direct_bits=(2, 4))
+    assert (lay.rec_bytes(0), lay.rec_bytes(1), lay.slab_bytes) == (80, 96, 352)
+    assert lay.record_offset(0, 0, 0, 1) == 80 and lay.record_offset(0, 0, 1, 0) == 160
+    kv = np.zeros((2, 2, 1, 1, 4))
+    kv[0, 0, 0, 0] = [0.0, 1.0, 2.0, 3.0]
+    kv[0, 1, 0, 0] = [5.0, 5.0, 5.0, 5.0]          # constant group: scale 0, zero 5 (0x4500)
+    kv[1, 0, 0, 0] = [0.0, 15.0, 3.0, 7.0]         # INT4: scale 1, codes 0, 15, 3, 7
+    enc = O.encode_direct(kv, (2, 4), 4, "f16")
+    pool = np.zeros(lay.pool_bytes, np.uint8)
+    O.write_tokens(pool, lay, enc, np.array([5]))
+    assert pool[5] == 0xE4
+    assert list(pool[16 + 20: 16 + 24]) == [0x00, 0x3C, 0x00, 0x00]
+    assert pool[80 + 5] == 0x00                               # V: all codes 0
+    assert list(pool[80 + 16 + 20: 80 + 16 + 24]) == [0x00, 0x00, 0x00, 0x45]
+    assert list(pool[160 + 10: 160 + 12]) == [0xF0, 0x73]     # codes (0,15),(3,7) low nibble first
+    assert list(pool[160 + 32 + 20: 160 + 32 + 24]) == [0x00, 0x3C, 0x00, 0x00]
+    # nothing else written
+    touched = {5, 36, 37, 38, 39, 85, 116, 117, 118, 119, 170, 171, 212, 213, 214, 215}
+    assert all(pool[i] == 0 for i in range(lay.pool_bytes) if i not in touched)
+
+
+def test_direct_reconstruction_and_attention_by_hand():
+    """Values on the quantization grid (INT2 steps 1 and 2, fp16-exact)
+    reconstruct exactly in direct mode, and decode attention over them is the
+    softmax of the hand-computed scores."""
+    D, L = 4, 2
+    lay = O.PoolLayout(1, D, 4, L, (), "f16", 2, direct_bits=(2, 2))
+    K = np.array([[0.0, 1.0, 2.0, 3.0], [3.0, 2.0, 1.0, 0.0], [1.0, 1.0, 4.0, 4.0]])
+    V = np.array([[2.0, 0.0, 0.0, 6.0], [0.0, 2.0, 4.0, 6.0], [6.0, 6.0, 0.0, 0.0]])
+    # loop 0 holds K/V, the final loop something else: loop 0 must read only its own record
+    kv = np.random.default_rng(3).normal(size=(L, 2, 3, 1, D))
+    kv[0, 0, :, 0] = K
+    kv[0, 1, :, 0] = V
+    enc = O.encode_direct(kv, (2, 2), 4, "f16")
+    pool = np.zeros(lay.pool_bytes, np.uint8)
+    table = np.array([[1, 0]])
+    O.write_tokens(pool, lay, enc, table[0, 0] * 16 + np.arange(3))
+    Kh, Vh = O.reconstruct_sequence(pool, lay, table[0], 3, 0, 0, None)
+    np.testing.assert_array_equal(Kh, K)
+    np.testing.assert_array_equal(Vh, V)
+    q = np.array([[[0.5, -1.0, 0.25, 1.0]]])
+    tau = 0.5
+    s = tau * np.array([0.0 - 1.0 + 0.5 + 3.0, 1.5 - 2.0 + 0.25 + 0.0, 0.5 - 1.0 + 1.0 + 4.0])
+    p = np.exp(s - s.max())
+    want = (p[:, None] * V).sum(0) / p.sum()
+    got = O.decode_attention(pool, lay, 0, q, None, table, [3], tau)[0, 0]
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-14)
