@@ -66,6 +66,9 @@ typedef int32_t rq_status;
 
 #define RQ_MAX_LOOPS 16
 
+#define RQ_MODE_RESIDUAL 0   /* ResidualQuant: INT4 reference + rotated residuals (default) */
+#define RQ_MODE_DIRECT   1   /* baseline: every loop quantized on its own */
+
 /* Geometry of one layer's packed cache.
  *   num_heads   H >= 1
  *   head_dim    D in {64, 96, 128}
@@ -77,7 +80,14 @@ typedef int32_t rq_status;
  *   meta_dtype  RQ_DTYPE_F16 or RQ_DTYPE_F32 (scale, zero, alpha)
  *   kv_dtype    RQ_DTYPE_BF16 or RQ_DTYPE_F32 (new K/V, queries, tails)
  *   loop_bits   loop_bits[l] in {2, 4} for l < L-1 (the residual of loop l);
- *               entries from L-1 on are ignored (the reference is INT4). */
+ *               entries from L-1 on are ignored (the reference is INT4).
+ *   mode        RQ_MODE_RESIDUAL (0), or RQ_MODE_DIRECT (1): the per-loop
+ *               quantization the pages compare against (arXiv 2610.10381
+ *               abstract: quantizing each loop's cache separately). Every loop
+ *               l < L, the last included, stores its own K/V at loop_bits[l]
+ *               bits with the same quantizer and record format but no alpha
+ *               field; there is no reference, alpha or rotation (rot may be
+ *               NULL), and loop l's decode reads loop l's records only. */
 typedef struct rq_layout {
     int32_t num_heads;
     int32_t head_dim;
@@ -88,6 +98,7 @@ typedef struct rq_layout {
     int32_t meta_dtype;
     int32_t kv_dtype;
     uint8_t loop_bits[RQ_MAX_LOOPS];
+    int32_t mode;
 } rq_layout;
 
 /* Tuning and instrumentation for the decode calls (all fields optional).

@@ -16,6 +16,7 @@ library_path = os.path.join(HERE, "librq.so")
 
 RQ_DTYPE_BF16, RQ_DTYPE_F16, RQ_DTYPE_F32 = 0, 1, 2
 RQ_MAX_LOOPS = 16
+RQ_MODE_RESIDUAL, RQ_MODE_DIRECT = 0, 1
 
 EXPORTED = [
     "rq_status_string", "rq_layout_check", "rq_pool_bytes", "rq_record_bytes", "rq_record_offset",
@@ -33,7 +34,8 @@ class RqError(RuntimeError):
 class RqLayout(ctypes.Structure):
     _fields_ = [("num_heads", c_int32), ("head_dim", c_int32), ("group_size", c_int32),
                 ("num_loops", c_int32), ("block_size", c_int32), ("num_blocks", c_int32),
-                ("meta_dtype", c_int32), ("kv_dtype", c_int32), ("loop_bits", c_uint8 * RQ_MAX_LOOPS)]
+                ("meta_dtype", c_int32), ("kv_dtype", c_int32), ("loop_bits", c_uint8 * RQ_MAX_LOOPS),
+                ("mode", c_int32)]
 
 
 class RqDecodeOpts(ctypes.Structure):
@@ -112,8 +114,11 @@ _DT = {"bf16": RQ_DTYPE_BF16, "f16": RQ_DTYPE_F16, "f32": RQ_DTYPE_F32}
 
 
 def make_layout(num_heads, head_dim, group_size, num_loops, res_bits, num_blocks,
-                meta_dtype="f16", kv_dtype="bf16", block_size=16) -> RqLayout:
+                meta_dtype="f16", kv_dtype="bf16", block_size=16, mode=0) -> RqLayout:
+    """rq_layout. mode 0 (RQ_MODE_RESIDUAL): res_bits are the L-1 residual
+    widths; mode 1 (RQ_MODE_DIRECT): res_bits are the L per-loop widths."""
     lay = RqLayout()
+    lay.mode = int(mode)
     lay.num_heads, lay.head_dim, lay.group_size = num_heads, head_dim, group_size
     lay.num_loops, lay.block_size, lay.num_blocks = num_loops, block_size, num_blocks
     lay.meta_dtype = _DT[meta_dtype] if isinstance(meta_dtype, str) else meta_dtype
@@ -167,7 +172,7 @@ def encode_pack(layout, pool, kv_new, rot, slot_mapping, stream=None):
         _need(tuple(kv_new.shape) == (L, 2, T, H, D) and kv_new.element_size() == _kv_bytes(layout)
               and kv_new.is_contiguous(), f"kv_new must be contiguous [{L}][2][T][{H}][{D}] in kv_dtype")
         _need(slot_mapping.numel() == T and slot_mapping.element_size() == 8, "slot_mapping must be int64 [T]")
-        if L > 1:
+        if L > 1 and layout.mode == RQ_MODE_RESIDUAL:
             _check_rot(layout, rot)
     _check("rq_encode_pack", lib().rq_encode_pack(
         ctypes.byref(layout), _ptr(pool), _ptr(kv_new), _ptr(rot), _ptr(slot_mapping), T, _stream(stream)))
@@ -208,7 +213,7 @@ def decode_attention(layout, pool, loops, q, rot, block_table, seq_lens, tail_k,
         if t is not None:
             _need(tuple(t.shape) == shp and t.element_size() == _kv_bytes(layout) and t.is_contiguous(),
                   f"tails must be contiguous {shp} in kv_dtype")
-    if any(int(l) != layout.num_loops - 1 for l in loops):
+    if layout.mode == RQ_MODE_RESIDUAL and any(int(l) != layout.num_loops - 1 for l in loops):
         _check_rot(layout, rot)
     o = _opts(split_pages, events)
     if kv_new is None and slot_mapping is None:
@@ -223,7 +228,7 @@ def decode_attention(layout, pool, loops, q, rot, block_table, seq_lens, tail_k,
     _need(tuple(kv_new.shape) == (L, 2, T, H, D) and kv_new.element_size() == _kv_bytes(layout)
           and kv_new.is_contiguous(), f"kv_new must be contiguous [{L}][2][T][{H}][{D}] in kv_dtype")
     _need(slot_mapping.numel() == T and slot_mapping.element_size() == 8, "slot_mapping must be int64 [T]")
-    if L > 1:
+    if L > 1 and layout.mode == RQ_MODE_RESIDUAL:
         _check_rot(layout, rot)
     _check("rq_decode_attention_encode", lib().rq_decode_attention_encode(
         ctypes.byref(layout), _ptr(pool), arr, n, _ptr(q), _ptr(rot), _ptr(block_table), _ptr(seq_lens),

@@ -24,6 +24,8 @@ rq_status make_geom(const rq_layout *lay, Geom *g) {
     if (!g_ok) return RQ_ERR_UNSUPPORTED;
     if (lay->meta_dtype != RQ_DTYPE_F16 && lay->meta_dtype != RQ_DTYPE_F32) return RQ_ERR_UNSUPPORTED;
     if (lay->kv_dtype != RQ_DTYPE_BF16 && lay->kv_dtype != RQ_DTYPE_F32) return RQ_ERR_UNSUPPORTED;
+    if (lay->mode != RQ_MODE_RESIDUAL && lay->mode != RQ_MODE_DIRECT) return RQ_ERR_UNSUPPORTED;
+    g->direct = lay->mode == RQ_MODE_DIRECT;
     g->H = H; g->D = D; g->G = G; g->L = L; g->bs = 16; g->nblk = lay->num_blocks;
     g->meta = lay->meta_dtype; g->kvdt = lay->kv_dtype;
     g->msz = lay->meta_dtype == RQ_DTYPE_F16 ? 2 : 4;
@@ -33,11 +35,11 @@ rq_status make_geom(const rq_layout *lay, Geom *g) {
         g->bits[l] = 0; g->code_bytes[l] = 0; g->rec[l] = 0; g->loop_off[l] = 0;
     }
     for (int l = 0; l < L; ++l) {
-        const int b = (l == L - 1) ? 4 : (int)lay->loop_bits[l];
+        const int b = (l == L - 1 && !g->direct) ? 4 : (int)lay->loop_bits[l];
         if (b != 2 && b != 4) return RQ_ERR_UNSUPPORTED;
         g->bits[l] = b;
         g->code_bytes[l] = g->bs * D * b / 8;
-        const int alpha = (l < L - 1) ? g->bs * g->msz : 0;
+        const int alpha = (l < L - 1 && !g->direct) ? g->bs * g->msz : 0;
         g->rec[l] = (int)round_up((size_t)(g->code_bytes[l] + g->meta_bytes + alpha), 16);
         g->loop_off[l] = off;
         off += 2 * (int64_t)g->rec[l];
@@ -122,7 +124,7 @@ rq_status rq_encode_pack(const rq_layout *layout, void *pool, const void *kv_new
     if (st != RQ_OK) return st;
     if (num_tokens < 0) return RQ_ERR_SHAPE;
     if (num_tokens == 0) return RQ_OK;
-    if (!pool || !kv_new || !slot_mapping || (g.L > 1 && !rot)) return RQ_ERR_NULL;
+    if (!pool || !kv_new || !slot_mapping || (g.L > 1 && !g.direct && !rot)) return RQ_ERR_NULL;
     if (!aligned(pool, 16)) return RQ_ERR_SHAPE;
     if (num_tokens > (1 << 30) / 16) return RQ_ERR_SHAPE;
     EncodeCall c;
@@ -151,14 +153,15 @@ static rq_status decode_impl(const rq_layout *layout, const void *pool, const in
     rq_status st = make_geom(layout, &g);
     if (st != RQ_OK) return st;
     if (num_tokens < 0 || num_tokens > (1 << 30) / 16) return RQ_ERR_SHAPE;
-    if (num_tokens > 0 && (!kv_new || !slot_mapping || !enc_pool || (g.L > 1 && !rot))) return RQ_ERR_NULL;
+    if (num_tokens > 0 && (!kv_new || !slot_mapping || !enc_pool || (g.L > 1 && !g.direct && !rot)))
+        return RQ_ERR_NULL;
     if (!loops) return RQ_ERR_NULL;
     if (n_loops < 1 || n_loops > RQ_MAX_LOOPS || batch < 0 || batch > 65535 || max_blocks_per_seq < 1)
         return RQ_ERR_SHAPE;
     bool any_res = false;
     for (int i = 0; i < n_loops; ++i) {
         if (loops[i] < 0 || loops[i] >= g.L) return RQ_ERR_SHAPE;
-        any_res = any_res || loops[i] != g.L - 1;
+        any_res = any_res || (loops[i] != g.L - 1 && !g.direct);
     }
     if (!isfinite(softmax_scale)) return RQ_ERR_SHAPE;
     if ((tail_k == nullptr) != (tail_v == nullptr)) return RQ_ERR_NULL;
@@ -184,7 +187,8 @@ static rq_status decode_impl(const rq_layout *layout, const void *pool, const in
     c.qpack = (uint8_t *)workspace;
     c.partials = (float *)((uint8_t *)workspace + round_up((size_t)n_loops * batch * g.H * qpack_bytes(g.D), 256));
     c.split_pages = sp; c.nsplit = nsplit_of(max_blocks_per_seq, sp);
-    c.nparts = partials_per_row(n_loops, max_blocks_per_seq, sp);
+    // direct mode decodes loop calls one kernel each (nothing shared between loops)
+    c.nparts = g.direct ? partials_per_row(1, max_blocks_per_seq, sp) : partials_per_row(n_loops, max_blocks_per_seq, sp);
     c.ev_begin = opts ? (hipEvent_t)opts->event_main_begin : nullptr;
     c.ev_end = opts ? (hipEvent_t)opts->event_main_end : nullptr;
     c.stream = (hipStream_t)stream;

@@ -56,6 +56,7 @@ struct QPrepArgs {
     uint8_t *qpack;         // [n][B][H][qpack_bytes]
     int B, H;
     int rb[RQ_MAX_LOOPS];   // residual bits of call i, 0 = reference loop
+    int ro[RQ_MAX_LOOPS];   // limb order of q itself for call i: 4, or 2 for a direct INT2 loop
 };
 
 // Channel covered by nibble n of limb dword (q4, k) in the order the split
@@ -150,7 +151,7 @@ __global__ __launch_bounds__(1024) void rq_qprep_kernel(QPrepArgs a) {
     // limb dwords: [q4][k][limb], nibble n = channel limb_channel(q4,k,n)
     for (int which = 0; which < 2; ++which) {
         if (which == 1 && rb == 0) break;
-        const int order = which == 0 ? 4 : rb;
+        const int order = which == 0 ? a.ro[i] : rb;
         for (int dw = lane; dw < D / 2; dw += 64) {
             const int limb = dw & 3;
             const int k = (dw >> 2) % Ln::NDW;
@@ -428,7 +429,7 @@ __device__ __forceinline__ void init_state(SplitState<D> &s) {
 //   rk, rv      this lane's residual K / V code bytes (RB != 0)
 //   mks, mvs    residual (scale, zero); aks, avs residual alphas (RB != 0)
 //   lsv         this lane's residual query limbs (registers or LDS)
-template <int D, int RB, bool META_F32>
+template <int D, int RB, bool META_F32, int REFB = 4>
 __device__ __forceinline__ void token_step(const uint8_t *ck, const uint8_t *cv, const uint8_t *mkr,
                                            const uint8_t *mvr, const uint8_t *rk, const uint8_t *rv,
                                            const uint8_t *mks, const uint8_t *aks, const uint8_t *mvs,
@@ -436,7 +437,7 @@ __device__ __forceinline__ void token_step(const uint8_t *ck, const uint8_t *cv,
                                            const QueryRegs<D> &q, const uint4 *lsv, SplitState<D> &s) {
     using Ln = Lanes<D>;
     constexpr int LPT = Ln::LPT, CPL = Ln::CPL;
-    constexpr int REF_NB = CPL / 2;                 // INT4 code bytes per lane
+    constexpr int REF_NB = CPL * REFB / 8;          // first record's code bytes per lane (INT4, or INT2 direct)
     constexpr int RES_NB = RB ? CPL * RB / 8 : 4;   // residual code bytes per lane
     constexpr int REF_NW = REF_NB / 4, RES_NW = RES_NB / 4;
     using SZ = typename std::conditional<META_F32, float2, uint32_t>::type;
@@ -447,7 +448,7 @@ __device__ __forceinline__ void token_step(const uint8_t *ck, const uint8_t *cv,
     sz_of(*(const SZ *)mkr, skr, zkr);
     sz_of(*(const SZ *)mvr, svr, zvr);
     // score: q.x_hat = alpha*(s*sum q c + z*sum q) + (s_r*sum q' c_r + z_r*sum q')
-    const int dref = dot_int4<REF_NW>(ckw, q.lrv) + 8 * q.qs_ref;
+    const int dref = (REFB == 4) ? dot_int4<REF_NW>(ckw, q.lrv) + 8 * q.qs_ref : dot_int2<REF_NW>(ckw, q.lrv);
     float part = (skr * (float)dref + zkr * (float)q.qs_ref) * q.sc_ref;
     float av = 1.f, svs = 0.f, zvs = 0.f;
     if constexpr (RB != 0) {
@@ -482,7 +483,8 @@ __device__ __forceinline__ void token_step(const uint8_t *ck, const uint8_t *cv,
     const float pa = pr * av;
     const float wr = valid ? pa * svr : 0.f;
     s.zr += valid ? pa * zvr : 0.f;
-    axpy_int4<REF_NW>(s.accr, cvw, wr);
+    if constexpr (REFB == 4) axpy_int4<REF_NW>(s.accr, cvw, wr);
+    else axpy_int2<REF_NW>(s.accr, cvw, wr);
     if constexpr (RB != 0) {
         const float ws = valid ? pr * svs : 0.f;
         s.zs += valid ? pr * zvs : 0.f;
@@ -554,12 +556,12 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 // step's PPI pages) and then, per page, [ref K meta][ref V meta][res K meta +
 // alpha][res V meta + alpha]. It is filled by direct-to-LDS loads
 // (global_load_lds_dwordx4): each instruction moves 64 pieces of 16 bytes.
-template <int D, int RB, bool META_F32, int G>
+template <int D, int RB, bool META_F32, int G, int REFB = 4>
 struct StageGeom {
     static constexpr int PPI = Lanes<D>::PPI;
     static constexpr int MSZ = META_F32 ? 4 : 2;
     static constexpr int NG = D / G;
-    static constexpr int CB_REF = 16 * D / 2;           // codes of one reference record
+    static constexpr int CB_REF = 16 * D * REFB / 8;    // codes of one reference (or direct) record
     static constexpr int CB_RES = 16 * D * RB / 8;      // codes of one residual record
     static constexpr int MB = 16 * NG * 2 * MSZ;        // (scale, zero) of one record
     static constexpr int AB = RB ? 16 * MSZ : 0;        // alpha of one residual record
@@ -587,12 +589,12 @@ struct StageGeom {
 // consumed. The direct-to-LDS loads and their wait counts are issued
 // explicitly (the data never occupies registers while in flight, and no wait
 // is more conservative than the ring needs).
-template <int D, int RB, bool META_F32, int G>
+template <int D, int RB, bool META_F32, int G, int REFB = 4>
 __global__ __launch_bounds__(256) void rq_split_kernel(SplitArgs a) {
     using Ln = Lanes<D>;
-    using SG = StageGeom<D, RB, META_F32, G>;
+    using SG = StageGeom<D, RB, META_F32, G, REFB>;
     constexpr int LPT = Ln::LPT, CPL = Ln::CPL, PPI = Ln::PPI;
-    constexpr int REF_NB = CPL / 2;
+    constexpr int REF_NB = CPL * REFB / 8;
     constexpr int RES_NB = RB ? CPL * RB / 8 : 4;
     constexpr int MSZ = SG::MSZ, NG = SG::NG, NST = SG::NST, NI = SG::NI;
     constexpr int PF = partial_floats(D);
@@ -675,7 +677,7 @@ __global__ __launch_bounds__(256) void rq_split_kernel(SplitArgs a) {
 
     // this lane's reads inside a stage: four lane offsets; the other reads
     // sit at compile-time distances from them (immediate LDS offsets)
-    const int o_ck = tok_i * (D / 2) + q4 * REF_NB;                  // + O_RK / O_RV
+    const int o_ck = tok_i * (D * REFB / 8) + q4 * REF_NB;           // + O_RK / O_RV
     const int o_rk = tok_i * (D * RB / 8) + q4 * RES_NB;             // + O_SK / O_SV
     const int o_mkr = page_in_step * SG::MP + (tok * NG + g) * 2 * MSZ;   // + O_M (+ MB, ...)
     const int o_aks = page_in_step * SG::MP + tok * MSZ;             // + O_M + 3 MB (+ MB + AB)
@@ -718,7 +720,7 @@ __global__ __launch_bounds__(256) void rq_split_kernel(SplitArgs a) {
             const bool valid = blk >= 0 && pp < p1 && pp * 16 + tok < seq;
             const uint8_t *S = &stage[wave][cur % NST][0];
             const uint8_t *C = S + o_ck, *R = S + o_rk, *M = S + SG::O_M + o_mkr, *A = S + SG::O_M + o_aks;
-            token_step<D, RB, META_F32>(C + SG::O_RK, C + SG::O_RV, M, M + SG::MB, R + SG::O_SK, R + SG::O_SV,
+            token_step<D, RB, META_F32, REFB>(C + SG::O_RK, C + SG::O_RV, M, M + SG::MB, R + SG::O_SK, R + SG::O_SV,
                                         M + 2 * SG::MB, A + 3 * SG::MB, M + 3 * SG::MB + SG::AB,
                                         A + 4 * SG::MB + SG::AB, valid, a.score_scale, q, q.lsv, s);
         }
@@ -1153,16 +1155,19 @@ __global__ __launch_bounds__(1024) void rq_combine_kernel(CombineArgs a) {
 // ------------------------------------------------------------- dispatch
 // ev0 / ev1 (may be null) are stamped by the kernel's own dispatch at its
 // start and end (no separate event packets in the stream)
+// rb: residual bits (0: one record only); refb: bits of the first record
+// (4: the INT4 reference; 2: a direct INT2 loop, with rb == 0)
 template <int D>
-hipError_t launch_split_d(const SplitArgs &s, int rb, bool mf, dim3 grid, hipStream_t st, hipEvent_t ev0,
+hipError_t launch_split_d(const SplitArgs &s, int rb, int refb, bool mf, dim3 grid, hipStream_t st, hipEvent_t ev0,
                           hipEvent_t ev1) {
-#define RQ_SPLIT(RB_, MF_, G_) \
-    hipExtLaunchKernelGGL((rq_split_kernel<D, RB_, MF_, G_>), grid, dim3(256), 0, st, ev0, ev1, 0, s)
+#define RQ_SPLIT(RB_, MF_, G_, REFB_) \
+    hipExtLaunchKernelGGL((rq_split_kernel<D, RB_, MF_, G_, REFB_>), grid, dim3(256), 0, st, ev0, ev1, 0, s)
 #define RQ_SPLIT_RB(MF_, G_)                          \
     do {                                              \
-        if (rb == 0) RQ_SPLIT(0, MF_, G_);            \
-        else if (rb == 2) RQ_SPLIT(2, MF_, G_);       \
-        else RQ_SPLIT(4, MF_, G_);                    \
+        if (rb == 0 && refb == 2) RQ_SPLIT(0, MF_, G_, 2); \
+        else if (rb == 0) RQ_SPLIT(0, MF_, G_, 4);    \
+        else if (rb == 2) RQ_SPLIT(2, MF_, G_, 4);    \
+        else RQ_SPLIT(4, MF_, G_, 4);                 \
     } while (0)
 #define RQ_SPLIT_G(G_)                                \
     do {                                              \
@@ -1235,8 +1240,9 @@ hipError_t launch_decode_d(const DecodeCall &c) {
     qa.q = c.q; qa.rot = c.rot; qa.qpack = c.qpack; qa.B = c.B; qa.H = g.H;
     CombineArgs ca;
     for (int i = 0; i < RQ_MAX_LOOPS; ++i) {
-        const bool res = i < c.n && c.loops[i] != g.L - 1;
+        const bool res = i < c.n && c.loops[i] != g.L - 1 && !g.direct;
         qa.rb[i] = res ? g.bits[c.loops[i]] : 0;
+        qa.ro[i] = (g.direct && i < c.n) ? g.bits[c.loops[i]] : 4;
         ca.is_res[i] = res ? 1 : 0;
     }
     dim3 pgrid(g.H, c.n, tiles);
@@ -1247,7 +1253,8 @@ hipError_t launch_decode_d(const DecodeCall &c) {
 
     const float score_scale = c.softmax_scale * kLog2e;
     const int ref = g.L - 1;
-    if (c.n >= 2) {
+    const bool multi = c.n >= 2 && !g.direct;   // direct loops share nothing: one kernel per call
+    if (multi) {
         // multi-loop mode: loop calls in balanced groups of at least 2 and at
         // most nl_max waves, each group reading every reference page once
         bool any4 = false;
@@ -1310,12 +1317,13 @@ hipError_t launch_decode_d(const DecodeCall &c) {
             first += nl;
         }
     }
-    bool enc_done = c.n >= 2;   // multi-loop mode: attached to the last group above
-    for (int i = 0; i < (c.n >= 2 ? 0 : c.n); ++i) {
+    bool enc_done = multi;   // multi-loop mode: attached to the last group above
+    for (int i = 0; i < (multi ? 0 : c.n); ++i) {
         const int l = c.loops[i];
         SplitArgs s;
         s.pool = c.pool; s.slab = g.slab; s.H = g.H; s.nblk = g.nblk; s.G = g.G;
-        s.ref_off = (int)g.loop_off[ref]; s.ref_rec = g.rec[ref]; s.ref_code_bytes = g.code_bytes[ref];
+        const int first = g.direct ? l : ref;   // the record read in full: the reference, or loop l itself
+        s.ref_off = (int)g.loop_off[first]; s.ref_rec = g.rec[first]; s.ref_code_bytes = g.code_bytes[first];
         s.res_off = (int)g.loop_off[l]; s.res_rec = g.rec[l]; s.res_code_bytes = g.code_bytes[l];
         s.meta_bytes = g.meta_bytes;
         s.block_table = c.block_table; s.max_blocks = c.max_blocks; s.seq_lens = c.seq_lens;
@@ -1323,13 +1331,14 @@ hipError_t launch_decode_d(const DecodeCall &c) {
         s.partials = c.partials + (int64_t)i * c.B * g.H * c.nparts * partial_floats(D);
         s.nsplit = c.nsplit; s.split_pages = c.split_pages;
         s.score_scale = score_scale;
-        const int rb = (l == ref) ? 0 : g.bits[l];
+        const int rb = (l == ref || g.direct) ? 0 : g.bits[l];
+        const int refb = g.direct ? g.bits[l] : 4;
         const int nwg = (c.nsplit + kWaves - 1) / kWaves;
         s.nwg = nwg;
         // the current tokens' encode rides in the first reference-loop launch
         s.enc_x0 = nwg; s.enc_items = 0; s.enc_kvf = kvf ? 1 : 0;
         int ex = 0;
-        if (l == ref && c.enc_T > 0 && !enc_done) {
+        if (l == ref && c.enc_T > 0 && !enc_done && !g.direct) {
             enc::fill_args(s.enc, g, c.enc_pool, c.enc_kv, c.rot, c.enc_slots, c.enc_T);
             s.enc_items = (c.enc_T + enc::kTT - 1) / enc::kTT * 2 * (g.L > 1 ? g.L - 1 : 1);
             ex = (s.enc_items + c.B - 1) / c.B;
@@ -1337,7 +1346,7 @@ hipError_t launch_decode_d(const DecodeCall &c) {
         }
         dim3 grid(nwg + ex, g.H, c.B);
         const bool last = i == c.n - 1;
-        err = launch_split_d<D>(s, rb, mf, grid, c.stream, last ? c.ev_begin : nullptr, last ? c.ev_end : nullptr);
+        err = launch_split_d<D>(s, rb, refb, mf, grid, c.stream, last ? c.ev_begin : nullptr, last ? c.ev_end : nullptr);
         if (err != hipSuccess) return err;
     }
 
@@ -1349,7 +1358,7 @@ hipError_t launch_decode_d(const DecodeCall &c) {
         err = launch_encode(ec);
         if (err != hipSuccess) return err;
     }
-    ca.partials = c.partials; ca.nparts = c.nparts; ca.spp = c.n >= 2 ? 1 : kWaves;
+    ca.partials = c.partials; ca.nparts = c.nparts; ca.spp = multi ? 1 : kWaves;
     ca.split_pages = c.split_pages;
     ca.max_blocks = c.max_blocks; ca.seq_lens = c.seq_lens;
     ca.q = c.q; ca.tail_k = c.tail_k; ca.tail_v = c.tail_v; ca.rot = c.rot; ca.out = c.out;

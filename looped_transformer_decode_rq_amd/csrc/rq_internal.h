@@ -11,6 +11,7 @@ namespace rq {
 // Derived geometry of one layer's packed pool (see the format in rq.h).
 struct Geom {
     int H, D, G, L, bs, nblk, meta, kvdt, msz;
+    bool direct;                    // RQ_MODE_DIRECT: every loop on its own, no alpha
     int bits[RQ_MAX_LOOPS];
     int code_bytes[RQ_MAX_LOOPS];   // per record
     int rec[RQ_MAX_LOOPS];          // record bytes (16-aligned)

@@ -69,6 +69,20 @@ def test_pool_geometry_matches_oracle(L, d):
     assert R.record_offset(lay, 0, 0, d["L"], 0) == -1
 
 
+@pytest.mark.parametrize("bits", [(2, 2, 2, 2), (4, 2, 4, 2), (4, 4, 4, 4)])
+def test_direct_pool_geometry_matches_oracle(L, bits):
+    lay = R.make_layout(16, 128, 128, 4, bits, 37, "f16", "bf16", mode=R.RQ_MODE_DIRECT)
+    assert R.layout_check(lay) == 0
+    ol = O.PoolLayout(16, 128, 128, 4, (), "f16", 37, direct_bits=bits)
+    assert R.pool_bytes(lay) == ol.pool_bytes
+    for l in range(4):
+        assert R.record_bytes(lay, l) == ol.rec_bytes(l)
+        for blk, h, kv in ((0, 0, 0), (36, 15, 1), (7, 3, 0)):
+            assert R.record_offset(lay, blk, h, l, kv) == int(ol.record_offset(blk, h, l, kv))
+    bad = R.make_layout(16, 128, 128, 4, bits, 37, "f16", "bf16", mode=2)
+    assert R.layout_check(bad) == -3
+
+
 @pytest.mark.parametrize("field,value,status", [
     ("head_dim", 256, -3), ("head_dim", 80, -2), ("head_dim", 0, -2), ("group_size", 16, -3), ("group_size", 48, -2),
     ("num_loops", 17, -2), ("num_loops", 0, -2), ("block_size", 32, -3), ("num_blocks", 0, -2),
