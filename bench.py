@@ -151,6 +151,47 @@ def rq_multi_step(w, s, split_pages, events=None, fused=True):
         R.encode_pack(s["lay"], s["pool"], s["kv_new"], s["rot"], s["slots_new"])
 
 
+def direct_baseline(w, dev, rq, bits, split_pages, steps, warmup):
+    """The direct per-loop quantization baseline on the same synthetic K/V:
+    every loop quantized on its own at `bits[l]` (no reference, alpha or
+    rotation). Times the same step (one decode call per loop + compression of
+    the new tokens) and returns its outputs for the error comparison."""
+    import torch
+    import looped_transformer_decode_rq_amd as R
+    import workloads as W
+    B, N, H, D, L = w.batch, w.context, w.heads, w.head_dim, w.loops
+    table, nblk = rq["table"], rq["nblk"]
+    lay = R.make_layout(H, D, w.group_size, L, bits, nblk, w.meta_dtype, w.kv_dtype, mode=R.RQ_MODE_DIRECT)
+    pool = torch.zeros(R.pool_bytes(lay), dtype=torch.uint8, device=dev)
+    pos = np.arange(N)
+    for b in range(B):
+        kvb = W.kv_torch(w, 0, b, rq["st"], dev)
+        slots = torch.from_numpy(table[b, pos // 16].astype(np.int64) * 16 + pos % 16).to(dev)
+        R.encode_pack(lay, pool, kvb[:, :, :N].contiguous(), None, slots)
+        del kvb
+    out = torch.empty((L, 1, B, H, D), device=dev)
+    ws = torch.empty(R.decode_workspace_bytes(lay, 1, B, table.shape[1], split_pages), dtype=torch.uint8,
+                     device=dev)
+    tau = 1.0 / np.sqrt(D)
+
+    def step(k):
+        for l in range(L):
+            R.decode_attention(lay, pool, [l], rq["qs"][l], None, rq["d_table"], rq["d_seq"], rq["tk"][l],
+                               rq["tv"][l], tau, out[l], ws, split_pages=split_pages)
+        R.encode_pack(lay, pool, rq["kv_new"], None, rq["slots_new"])
+
+    t = timed(step, steps, warmup)
+    stored = sum(2 * (D * b // 8 + 2 * (2 if w.meta_dtype == "f16" else 4) * (D // w.group_size)) for b in bits)
+    res = {"bits": list(bits), "ms_per_step": t * 1e3, "tokens_per_s": B / t,
+           "stored_bytes_per_token_head": stored}
+    del pool
+    return res, out[:, 0].clone()
+
+
+def rel_l2(a, b):
+    return float((a.double() - b.double()).norm() / b.double().norm())
+
+
 def setup_bf16(w, dev, rq, split_pages):
     import torch
     import looped_transformer_decode_rq_amd as R
@@ -276,6 +317,7 @@ def main():
     ap.add_argument("--split-pages", type=int, default=0)
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-direct", action="store_true", help="skip the direct per-loop quantization baselines")
     ap.add_argument("--separate-encode", action="store_true",
                     help="compress the new tokens in a launch of their own after the attention calls "
                          "instead of in the reference-loop call's launch")
@@ -362,6 +404,15 @@ def main():
     multi_gbs = multi_bytes / (multi_ms * 1e-3) / 1e9
     log(f"multi-loop step {t_multi * 1e3:.3f} ms; multi-loop kernel {multi_ms:.3f} ms ({multi_gbs:.0f} GB/s)")
 
+    direct, direct_outs, errors = {}, {}, {}
+    if not args.no_direct:
+        for name, bits in (("direct_int2", (2,) * L), ("direct_int4", (4,) * L)):
+            log(f"timing the {name} baseline")
+            direct[name], direct_outs[name] = direct_baseline(w, dev, rq, bits, args.split_pages, args.steps,
+                                                              args.warmup)
+            log(f"{name} step {direct[name]['ms_per_step']:.3f} ms")
+        torch.cuda.empty_cache()
+
     bf16 = None
     if not args.no_bf16:
         log("setting up bf16 baseline cache")
@@ -385,6 +436,19 @@ def main():
                 "speedup_packed_vs_bf16": t_bf / t_rq,
                 "speedup_multi_loop_vs_bf16": t_bf / t_multi}
         log(f"bf16 step {t_bf * 1e3:.3f} ms; packed/bf16 speedup {t_bf / t_rq:.2f}x")
+        # exact attention over the bf16 cache, per loop: the reference for the error comparison
+        tau = 1.0 / np.sqrt(D)
+        exact = []
+        for l in range(L):
+            R.bf16_decode_attention(b16["kc"][l], b16["vc"][l], b16["q"][l], rq["d_table"], rq["d_seq"],
+                                    rq["tk"][l][0], rq["tv"][l][0], tau, b16["out"], b16["ws"],
+                                    split_pages=args.split_pages)
+            exact.append(b16["out"].clone())
+        errors["rq_per_loop"] = [rel_l2(rq["out"][l, 0], exact[l]) for l in range(L)]
+        errors["rq_multi_loop"] = [rel_l2(rq["out_all"][l], exact[l]) for l in range(L)]
+        for key, o in direct_outs.items():
+            errors[key] = [rel_l2(o[l], exact[l]) for l in range(L)]
+        log("attention rel-L2 vs bf16: " + ", ".join(f"{k} {max(v):.2e}" for k, v in errors.items()))
         del b16
         torch.cuda.empty_cache()
 
@@ -431,6 +495,9 @@ def main():
                        "kernel_gbs": multi_gbs,
                        "kernel_frac_of_peak": multi_gbs / HBM_PEAK_GBS},
         "bf16_baseline": bf16,
+        "direct_baselines": direct or None,
+        "attention_rel_l2_vs_bf16": errors or None,
+        "stored_bytes_per_token_head": {"rq": stored, "bf16": 2 * D * 2 * L},
         "cpu_baseline": cpu,
         "context_from_pages": {"kv_storage_reduction": "80.7% (theoretical, mixed precision)",
                                "fixed_batch_decode_speedup": "up to 2.73x on RTX 5090",
