@@ -21,6 +21,12 @@ R11 little-endian packing: element i sits in the low bits first.
 R12 softmax scale 1/sqrt(D) by default, attention over every cached token plus
     the current (uncompressed) token.
 R13 reconstruction of loop l: alpha * xref_hat + R^T dequant(residual).
+R15 rotation fitting (a stand-in for calibration; the pages fix no fitting
+    rule): alternate (1) quantize the rotated residual samples with the
+    quantizer above and (2) the orthogonal Procrustes step, the orthogonal R
+    closest to mapping the samples onto their quantized values, R = U V^T for
+    M = Yhat D^T = U S V^T; keep the R with the lowest mean squared
+    quantization error seen (the starting R included).
 R14 the direct per-loop baseline (the "quantize every loop on its own"
     approach the pages compare against): loop l's K/V quantized with the
     quantizer of R6-R10 at its own bit width, no reference, no alpha, no
@@ -38,6 +44,7 @@ __all__ = [
     "PoolLayout", "write_tokens", "read_pages", "gather_sequence",
     "reconstruct_sequence", "attention", "decode_attention",
     "bf16_pool_write", "bf16_decode_attention", "DirectEncoded", "encode_direct",
+    "rotation_quant_error", "procrustes", "fit_rotation",
 ]
 
 
@@ -462,3 +469,37 @@ def bf16_decode_attention(kcache, vcache, q, table, seq_lens, tau, tail_k=None, 
         tv = None if tail_v is None else tail_v[b, h]
         out[b, h] = attention(q[b, h], K, V, tau, tk, tv)
     return out
+
+
+# ---------------------------------------------------------- rotation fitting
+def rotation_quant_error(samples: np.ndarray, R: np.ndarray, bits: int, G: int, meta: str) -> float:
+    """Mean over samples of ||Q(R d) - R d||^2 (reading R15); samples [n][D]."""
+    Y = np.asarray(samples, dtype=np.float64) @ np.asarray(R, dtype=np.float64).T      # rows: (R d)^T
+    q = quantize(Y, bits, G, meta)
+    Yh = dequantize(q.codes, q.scale, q.zero, G)
+    return float(((Yh - Y) ** 2).sum() / Y.shape[0])
+
+
+def procrustes(M: np.ndarray) -> np.ndarray:
+    """argmax_R trace(R^T M) over orthogonal R (= argmin ||R D - Yhat|| for
+    M = Yhat D^T): R = U V^T from the SVD M = U S V^T."""
+    U, _, Vt = np.linalg.svd(np.asarray(M, dtype=np.float64))
+    return U @ Vt
+
+
+def fit_rotation(samples: np.ndarray, R0: np.ndarray, bits: int, G: int, meta: str, iters: int):
+    """Reading R15. Returns (best R, objective of R0 and of every iterate)."""
+    Dm = np.asarray(samples, dtype=np.float64)                 # [n][D]
+    R = np.asarray(R0, dtype=np.float32).astype(np.float64)
+    best, best_err = R.copy(), rotation_quant_error(Dm, R, bits, G, meta)
+    hist = [best_err]
+    for _ in range(iters):
+        Y = Dm @ R.T
+        q = quantize(Y, bits, G, meta)
+        Yh = dequantize(q.codes, q.scale, q.zero, G)           # [n][D]
+        R = procrustes(Yh.T @ Dm)                              # sum_i yhat_i d_i^T
+        err = rotation_quant_error(Dm, R, bits, G, meta)
+        hist.append(err)
+        if err < best_err:
+            best, best_err = R.copy(), err
+    return best, hist

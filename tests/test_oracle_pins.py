@@ -403,3 +403,40 @@ def test_direct_reconstruction_and_attention_by_hand():
     want = (p[:, None] * V).sum(0) / p.sum()
     got = O.decode_attention(pool, lay, 0, q, None, table, [3], tau)[0, 0]
     np.testing.assert_allclose(got, want, rtol=0, atol=1e-14)
+
+
+# ---------------------------------------------------------- rotation fitting
+def test_procrustes_matches_brute_force_in_2d():
+    """The Procrustes step against a search over every 2-D orthogonal matrix
+    (rotations and reflections by angle): both maximize trace(R^T M)."""
+    rng = np.random.default_rng(11)
+    for _ in range(20):
+        M = rng.normal(size=(2, 2))
+        R = O.procrustes(M)
+        th = np.linspace(0, 2 * np.pi, 2000001)
+        c, s_ = np.cos(th), np.sin(th)
+        # trace(Q^T M) for Q = [[c, -s], [s, c]] and for the reflection [[c, s], [s, -c]]
+        rot = c * M[0, 0] + s_ * M[1, 0] - s_ * M[0, 1] + c * M[1, 1]
+        ref = c * M[0, 0] + s_ * M[1, 0] + s_ * M[0, 1] - c * M[1, 1]
+        best = float(max(rot.max(), ref.max()))
+        assert abs(float(np.trace(R.T @ M)) - best) < 1e-8
+        np.testing.assert_allclose(R @ R.T, np.eye(2), atol=1e-12)
+
+
+def test_fit_rotation_orthogonal_and_never_worse():
+    """The fitted R is orthogonal to 1e-12 and its error is the minimum of
+    the trajectory, no larger than the starting rotation's; on residuals with
+    outlier channels the fit lowers the error."""
+    w = W.get(1)
+    st = W.structure(w)
+    rng = np.random.default_rng(5)
+    D = w.head_dim
+    scale = np.ones(D)
+    scale[rng.permutation(D)[:3]] = 10.0
+    samples = rng.normal(size=(1024, D)) * scale * 0.1
+    R0 = st["rot32"][0, 0]
+    R, hist = O.fit_rotation(samples, R0, 2, D, "f16", 8)
+    np.testing.assert_allclose(R @ R.T, np.eye(D), atol=1e-12)
+    err = O.rotation_quant_error(samples, R, 2, D, "f16")
+    assert err == min(hist) and err <= hist[0]
+    assert err < hist[0]
