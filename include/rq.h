@@ -214,6 +214,27 @@ rq_status rq_decode_attention_encode(const rq_layout *layout, void *pool, const 
                                      const int64_t *slot_mapping, int32_t num_tokens,
                                      const rq_decode_opts *opts, void *stream);
 
+/* Fit a residual rotation on calibration samples (HOST memory; runs on the
+ * host, not on the decode path). The pages give the rotation's role (a channel
+ * rotation of each loop's residual before its low-bit quantization, per
+ * layer, head and K|V: arXiv 2610.10381 abstract; rit.work summary, section on
+ * how each pass is restored) but no fitting rule; this one alternates the
+ * method's group quantization of the rotated samples with an orthogonal
+ * Procrustes step (R = U V^T for M = sum_i yhat_i d_i^T = U S V^T) and returns
+ * the rotation with the lowest mean squared quantization error seen, the
+ * starting one included. All arithmetic in float64.
+ *   samples     [n][head_dim] float32: residual rows d = x_l - alpha * x_ref
+ *   bits, group_size, meta_dtype  the quantizer (as in rq_layout)
+ *   rot0        [head_dim][head_dim] float32 starting rotation (row-major, r = R d)
+ *   iters       alternations, >= 0
+ *   rot_out     [head_dim][head_dim] float32: the fitted rotation (may alias rot0)
+ *   objective   [iters + 1] float64 or NULL: the mean squared error of rot0
+ *               and of every iterate
+ * head_dim <= 128 and a multiple of group_size; bits 2 or 4. */
+rq_status rq_fit_rotation(const float *samples, int64_t n, int32_t head_dim, int32_t bits,
+                          int32_t group_size, int32_t meta_dtype, const float *rot0, int32_t iters,
+                          float *rot_out, double *objective);
+
 /* Uncompressed baseline (for the speed ratio): the same decode attention over
  * a paged bf16 cache of ONE loop.
  *   k_cache, v_cache  [num_blocks][H][16][D] bf16

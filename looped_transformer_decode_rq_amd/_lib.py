@@ -21,7 +21,7 @@ RQ_MODE_RESIDUAL, RQ_MODE_DIRECT = 0, 1
 EXPORTED = [
     "rq_status_string", "rq_layout_check", "rq_pool_bytes", "rq_record_bytes", "rq_record_offset",
     "rq_encode_pack", "rq_decode_workspace_bytes", "rq_decode_attention", "rq_decode_attention_ex",
-    "rq_decode_attention_encode", "rq_bf16_workspace_bytes", "rq_bf16_decode_attention", "rq_bf16_decode_attention_ex", "rq_bf16_write",
+    "rq_decode_attention_encode", "rq_fit_rotation", "rq_bf16_workspace_bytes", "rq_bf16_decode_attention", "rq_bf16_decode_attention_ex", "rq_bf16_write",
 ]
 
 
@@ -70,6 +70,7 @@ def lib():
             "rq_decode_attention_encode": (c_int32, [POINTER(RqLayout), P, P, c_int32, P, P, P, P, c_int32, c_int32,
                                                      P, P, c_float, P, P, c_size_t, P, P, c_int32,
                                                      POINTER(RqDecodeOpts), P]),
+            "rq_fit_rotation": (c_int32, [P, c_int64, c_int32, c_int32, c_int32, c_int32, P, c_int32, P, P]),
             "rq_bf16_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32]),
             "rq_bf16_decode_attention": (c_int32, [c_int32, c_int32, c_int32, c_int32, P, P, P, P, P, c_int32,
                                                    c_int32, P, P, c_float, P, P, c_size_t, P]),
@@ -274,3 +275,21 @@ def bf16_write(k_cache, v_cache, kv_new, slot_mapping, stream=None):
     _check("rq_bf16_write", lib().rq_bf16_write(
         H, D, bs, nblk, _ptr(k_cache), _ptr(v_cache), _ptr(kv_new), _ptr(slot_mapping),
         int(kv_new.shape[1]), _stream(stream)))
+
+
+def fit_rotation(samples, rot0, bits, group_size, meta_dtype="f16", iters=10):
+    """rq_fit_rotation on HOST arrays (calibration, not the decode path):
+    samples [n][D] float32, rot0 [D][D] float32 -> (fitted R [D][D] float32,
+    objective [iters + 1] float64)."""
+    import numpy as np
+    x = np.ascontiguousarray(samples, dtype=np.float32)
+    r0 = np.ascontiguousarray(rot0, dtype=np.float32)
+    n, D = x.shape
+    _need(r0.shape == (D, D), "rot0 must be [D][D]")
+    out = np.empty((D, D), np.float32)
+    obj = np.empty(int(iters) + 1, np.float64)
+    md = _DT[meta_dtype] if isinstance(meta_dtype, str) else meta_dtype
+    _check("rq_fit_rotation", lib().rq_fit_rotation(
+        x.ctypes.data_as(c_void_p), n, D, int(bits), int(group_size), md, r0.ctypes.data_as(c_void_p),
+        int(iters), out.ctypes.data_as(c_void_p), obj.ctypes.data_as(c_void_p)))
+    return out, obj

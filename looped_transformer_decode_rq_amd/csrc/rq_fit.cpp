@@ -1,0 +1,171 @@
+// Rotation fitting on calibration residuals (host code; an offline step, not
+// part of the decode path).
+//
+// The pages give the rotation's role -- a per-(layer, head, K|V) channel
+// rotation of the residual before its low-bit quantization (ResidualQuant,
+// arXiv 2610.10381 abstract; rit.work summary, section on how each pass is
+// restored) -- but no rule for choosing it. This fits one by alternating
+//   (1) quantize the rotated samples with the method's group quantizer
+//       (step (max-min)/(2^b-1) and offset min rounded to the metadata dtype,
+//       codes rounded to nearest even and clamped), and
+//   (2) the orthogonal Procrustes step: the orthogonal R that best maps the
+//       samples onto their quantized values, R = U V^T for the SVD
+//       M = sum_i yhat_i d_i^T = U S V^T,
+// keeping the R with the lowest mean squared quantization error seen (the
+// starting rotation included). Everything is float64; the SVD is a one-sided
+// (Hestenes) Jacobi iteration.
+#include <math.h>
+#include <string.h>
+
+#include <vector>
+
+#include "rq_internal.h"
+
+namespace rq {
+namespace {
+
+// float64 -> float16 -> float64, round to nearest even: the value is scaled
+// by a power of two onto the fp16 grid of its binade (exact), rounded with
+// rint (nearest even in the default rounding mode) and scaled back.
+double round_f16(double x) {
+    if (!isfinite(x) || x == 0.0) return x;
+    const double ax = fabs(x);
+    if (ax >= 65520.0) return copysign(INFINITY, x);   // rounds past the largest fp16
+    int e;
+    frexp(ax, &e);                                      // ax in [2^(e-1), 2^e)
+    int q = e - 1 - 10;                                 // exponent of the fp16 quantum in this binade
+    if (q < -24) q = -24;                               // subnormal quantum 2^-24
+    const double r = rint(ldexp(ax, -q));
+    return copysign(ldexp(r, q), x);
+}
+
+double meta_round(double x, int meta) { return meta == RQ_DTYPE_F32 ? (double)(float)x : round_f16(x); }
+
+// y [D] -> its quantized reconstruction yh [D]
+void quantize_row(const double *y, double *yh, int D, int G, int bits, int meta) {
+    const double qmax = (double)((1 << bits) - 1);
+    for (int g0 = 0; g0 < D; g0 += G) {
+        double lo = y[g0], hi = y[g0];
+        for (int c = g0 + 1; c < g0 + G; ++c) {
+            lo = fmin(lo, y[c]);
+            hi = fmax(hi, y[c]);
+        }
+        const double s = meta_round((hi - lo) / qmax, meta);
+        const double z = meta_round(lo, meta);
+        for (int c = g0; c < g0 + G; ++c) {
+            double code = 0.0;
+            if (s != 0.0) code = fmin(fmax(rint((y[c] - z) / s), 0.0), qmax);
+            yh[c] = code * s + z;
+        }
+    }
+}
+
+// Y = rows of samples rotated by R (row-major R, y_i = R d_i); returns the mean
+// squared quantization error and, if M is given, accumulates M += yhat_i d_i^T.
+double quant_error(const std::vector<double> &X, int64_t n, int D, const std::vector<double> &R, int G, int bits,
+                   int meta, std::vector<double> *M) {
+    std::vector<double> y(D), yh(D);
+    double err = 0.0;
+    if (M) M->assign((size_t)D * D, 0.0);
+    for (int64_t i = 0; i < n; ++i) {
+        const double *d = &X[(size_t)i * D];
+        for (int r = 0; r < D; ++r) {
+            double acc = 0.0;
+            for (int c = 0; c < D; ++c) acc += R[(size_t)r * D + c] * d[c];
+            y[r] = acc;
+        }
+        quantize_row(y.data(), yh.data(), D, G, bits, meta);
+        for (int r = 0; r < D; ++r) err += (yh[r] - y[r]) * (yh[r] - y[r]);
+        if (M)
+            for (int r = 0; r < D; ++r)
+                for (int c = 0; c < D; ++c) (*M)[(size_t)r * D + c] += yh[r] * d[c];
+    }
+    return err / (double)n;
+}
+
+// Orthogonal polar factor R = U V^T of M (row-major D x D) by one-sided Jacobi:
+// rotate column pairs of W = M V until they are mutually orthogonal; then
+// W = U S and R = U V^T.
+void procrustes(const std::vector<double> &M, int D, std::vector<double> &R) {
+    std::vector<double> W(M), V((size_t)D * D, 0.0);
+    for (int i = 0; i < D; ++i) V[(size_t)i * D + i] = 1.0;
+    auto col = [&](std::vector<double> &A, int r, int c) -> double & { return A[(size_t)r * D + c]; };
+    for (int sweep = 0; sweep < 60; ++sweep) {
+        double off = 0.0;
+        for (int p = 0; p < D - 1; ++p) {
+            for (int q = p + 1; q < D; ++q) {
+                double a = 0.0, b = 0.0, g = 0.0;
+                for (int r = 0; r < D; ++r) {
+                    const double wp = col(W, r, p), wq = col(W, r, q);
+                    a += wp * wp;
+                    b += wq * wq;
+                    g += wp * wq;
+                }
+                if (a == 0.0 || b == 0.0) continue;
+                const double rel = fabs(g) / sqrt(a * b);
+                off = fmax(off, rel);
+                if (rel < 1e-15) continue;
+                const double zeta = (b - a) / (2.0 * g);
+                const double t = (zeta >= 0 ? 1.0 : -1.0) / (fabs(zeta) + sqrt(1.0 + zeta * zeta));
+                const double cs = 1.0 / sqrt(1.0 + t * t), sn = cs * t;
+                for (int r = 0; r < D; ++r) {
+                    const double wp = col(W, r, p), wq = col(W, r, q);
+                    col(W, r, p) = cs * wp - sn * wq;
+                    col(W, r, q) = sn * wp + cs * wq;
+                    const double vp = col(V, r, p), vq = col(V, r, q);
+                    col(V, r, p) = cs * vp - sn * vq;
+                    col(V, r, q) = sn * vp + cs * vq;
+                }
+            }
+        }
+        if (off < 1e-15) break;
+    }
+    // U = W S^-1 column by column; R = U V^T
+    for (int c = 0; c < D; ++c) {
+        double nrm = 0.0;
+        for (int r = 0; r < D; ++r) nrm += col(W, r, c) * col(W, r, c);
+        nrm = sqrt(nrm);
+        const double inv = nrm > 0.0 ? 1.0 / nrm : 0.0;
+        for (int r = 0; r < D; ++r) col(W, r, c) *= inv;
+    }
+    R.assign((size_t)D * D, 0.0);
+    for (int r = 0; r < D; ++r)
+        for (int c = 0; c < D; ++c) {
+            double acc = 0.0;
+            for (int k = 0; k < D; ++k) acc += col(W, r, k) * col(V, c, k);
+            R[(size_t)r * D + c] = acc;
+        }
+}
+
+}  // namespace
+}  // namespace rq
+
+using namespace rq;
+
+extern "C" rq_status rq_fit_rotation(const float *samples, int64_t n, int32_t head_dim, int32_t bits,
+                                     int32_t group_size, int32_t meta_dtype, const float *rot0, int32_t iters,
+                                     float *rot_out, double *objective) {
+    if (!samples || !rot0 || !rot_out) return RQ_ERR_NULL;
+    const int D = head_dim, G = group_size;
+    if (n < 1 || D < 1 || D > 128 || G < 1 || D % G != 0 || iters < 0 || iters > 10000) return RQ_ERR_SHAPE;
+    if (bits != 2 && bits != 4) return RQ_ERR_UNSUPPORTED;
+    if (meta_dtype != RQ_DTYPE_F16 && meta_dtype != RQ_DTYPE_F32) return RQ_ERR_UNSUPPORTED;
+    std::vector<double> X((size_t)n * D), R((size_t)D * D), M;
+    for (size_t i = 0; i < X.size(); ++i) X[i] = (double)samples[i];
+    for (size_t i = 0; i < R.size(); ++i) R[i] = (double)rot0[i];
+    std::vector<double> best(R);
+    double best_err = quant_error(X, n, D, R, G, bits, meta_dtype, nullptr);
+    if (objective) objective[0] = best_err;
+    for (int it = 0; it < iters; ++it) {
+        quant_error(X, n, D, R, G, bits, meta_dtype, &M);
+        procrustes(M, D, R);
+        const double err = quant_error(X, n, D, R, G, bits, meta_dtype, nullptr);
+        if (objective) objective[it + 1] = err;
+        if (err < best_err) {
+            best_err = err;
+            best = R;
+        }
+    }
+    for (size_t i = 0; i < best.size(); ++i) rot_out[i] = (float)best[i];
+    return RQ_OK;
+}
