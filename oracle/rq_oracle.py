@@ -21,13 +21,13 @@ R11 little-endian packing: element i sits in the low bits first.
 R12 softmax scale 1/sqrt(D) by default, attention over every cached token plus
     the current (uncompressed) token.
 R13 reconstruction of loop l: alpha * xref_hat + R^T dequant(residual).
-R15 rotation fitting (a stand-in for calibration; the pages fix no fitting
+R18 rotation fitting (a stand-in for calibration; the pages fix no fitting
     rule): alternate (1) quantize the rotated residual samples with the
     quantizer above and (2) the orthogonal Procrustes step, the orthogonal R
     closest to mapping the samples onto their quantized values, R = U V^T for
     M = Yhat D^T = U S V^T; keep the R with the lowest mean squared
     quantization error seen (the starting R included).
-R14 the direct per-loop baseline (the "quantize every loop on its own"
+R17 the direct per-loop baseline (the "quantize every loop on its own"
     approach the pages compare against): loop l's K/V quantized with the
     quantizer of R6-R10 at its own bit width, no reference, no alpha, no
     rotation; stored in the same paged record format without the alpha field.
@@ -202,7 +202,7 @@ class DirectEncoded:
 
 
 def encode_direct(kv: np.ndarray, bits, G: int, meta: str) -> DirectEncoded:
-    """The direct per-loop baseline (reading R14): every loop's K/V quantized
+    """The direct per-loop baseline (reading R17): every loop's K/V quantized
     on its own, with loop l at bits[l] (2 or 4)."""
     kv = np.asarray(kv, dtype=np.float64)
     return DirectEncoded(q=[quantize(kv[l], int(bits[l]), G, meta) for l in range(kv.shape[0])], G=G, meta=meta)
@@ -251,7 +251,7 @@ class PoolLayout:
     only change what is stored per token (rit.work summary: scheduler and paged
     management stay as they are).
 
-    Direct mode (``direct_bits`` given, reading R14): every loop's record holds
+    Direct mode (``direct_bits`` given, reading R17): every loop's record holds
     its own codes at ``direct_bits[l]`` bits and the (scale, zero) pairs, with
     no alpha field; ``res_bits`` is then unused.
     """
@@ -379,7 +379,7 @@ def reconstruct_sequence(pool, lay: PoolLayout, table_row, n_tokens: int, head: 
     """
     out = []
     if lay.direct:
-        # direct baseline (R14): loop l's own record, nothing else
+        # direct baseline (R17): loop l's own record, nothing else
         for kv in range(2):
             c, s, z, _ = gather_sequence(pool, lay, table_row, n_tokens, head, l, kv)
             out.append(dequantize(c, s, z, lay.G))
@@ -473,7 +473,7 @@ def bf16_decode_attention(kcache, vcache, q, table, seq_lens, tau, tail_k=None, 
 
 # ---------------------------------------------------------- rotation fitting
 def rotation_quant_error(samples: np.ndarray, R: np.ndarray, bits: int, G: int, meta: str) -> float:
-    """Mean over samples of ||Q(R d) - R d||^2 (reading R15); samples [n][D]."""
+    """Mean over samples of ||Q(R d) - R d||^2 (reading R18); samples [n][D]."""
     Y = np.asarray(samples, dtype=np.float64) @ np.asarray(R, dtype=np.float64).T      # rows: (R d)^T
     q = quantize(Y, bits, G, meta)
     Yh = dequantize(q.codes, q.scale, q.zero, G)
@@ -488,7 +488,7 @@ def procrustes(M: np.ndarray) -> np.ndarray:
 
 
 def fit_rotation(samples: np.ndarray, R0: np.ndarray, bits: int, G: int, meta: str, iters: int):
-    """Reading R15. Returns (best R, objective of R0 and of every iterate)."""
+    """Reading R18. Returns (best R, objective of R0 and of every iterate)."""
     Dm = np.asarray(samples, dtype=np.float64)                 # [n][D]
     R = np.asarray(R0, dtype=np.float32).astype(np.float64)
     best, best_err = R.copy(), rotation_quant_error(Dm, R, bits, G, meta)
