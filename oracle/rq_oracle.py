@@ -27,6 +27,12 @@ R18 rotation fitting (a stand-in for calibration; the pages fix no fitting
     closest to mapping the samples onto their quantized values, R = U V^T for
     M = Yhat D^T = U S V^T; keep the R with the lowest mean squared
     quantization error seen (the starting R included).
+R19 storage order of V codes inside a page record (the pages fix no storage
+    layout; this is the library's format): tokens in quads, channels in
+    column groups of J = min(16, D), one "lane" per (quad, column) holding
+    that column's codes of the quad's four tokens for every column group,
+    split into 32-bit words and stored word-plane by word-plane (see
+    v_code_bits). K codes stay token-major (pack_codes per token).
 R17 the direct per-loop baseline (the "quantize every loop on its own"
     approach the pages compare against): loop l's K/V quantized with the
     quantizer of R6-R10 at its own bit width, no reference, no alpha, no
@@ -41,7 +47,7 @@ import numpy as np
 __all__ = [
     "meta_round", "ls_alpha", "Quantized", "quantize", "dequantize",
     "Encoded", "encode", "reconstruct", "pack_codes", "unpack_codes",
-    "PoolLayout", "write_tokens", "read_pages", "gather_sequence",
+    "v_code_bits", "PoolLayout", "write_tokens", "read_pages", "gather_sequence",
     "reconstruct_sequence", "attention", "decode_attention",
     "bf16_pool_write", "bf16_decode_attention", "DirectEncoded", "encode_direct",
     "rotation_quant_error", "procrustes", "fit_rotation",
@@ -235,13 +241,53 @@ def unpack_codes(packed: np.ndarray, bits: int) -> np.ndarray:
 
 
 # ------------------------------------------------------------------- layout
+def v_code_bits(bs: int, D: int, bits: int) -> np.ndarray:
+    """Bit offset of the code of (token t, channel c) inside the V code block
+    of one page record, [bs][D] int64 (reading R19).
+
+    Tokens: quad u = t // 4, position v = t % 4 (bs a multiple of 4).
+    Channels: column group m = c // J, column j = c % J, J = min(16, D),
+    M = D / J groups. Lane lam = J*u + j holds, for m = 0..M-1, the codes of
+    (token 4u+v, channel J*m+j), v = 0..3. With W = 8 // bits groups per
+    32-bit word, word p of a lane holds groups W*p .. W*p + W_p - 1 where
+    W_p = min(W, M - W*p) (the last word may be partial), and inside word p
+    the code (group W*p + i, position v) is field
+        f = 2*W_p*(v % 2) + W_p*(v // 2) + i,
+    i.e. bits [f*bits, (f+1)*bits) of the word, little-endian. Word p of every
+    lane forms plane p (lanes in order, W_p*bits/2 bytes each); the planes
+    follow one another from plane 0.
+    """
+    assert bs % 4 == 0 and bits in (2, 4)
+    J = min(16, D)
+    assert D % J == 0
+    M = D // J
+    W = 8 // bits
+    nlanes = (bs // 4) * J
+    wp = [min(W, M - W * p) for p in range(-(-M // W))]
+    plane_start = [0]
+    for w in wp:
+        plane_start.append(plane_start[-1] + nlanes * w * bits // 2)
+    pos = np.zeros((bs, D), dtype=np.int64)
+    for t in range(bs):
+        u, v = divmod(t, 4)
+        for c in range(D):
+            m, j = divmod(c, J)
+            lam = J * u + j
+            p, i = divmod(m, W)
+            f = 2 * wp[p] * (v % 2) + wp[p] * (v // 2) + i
+            byte0 = plane_start[p] + lam * wp[p] * bits // 2
+            pos[t, c] = 8 * byte0 + f * bits
+    return pos
+
+
 class PoolLayout:
     """Byte layout of one layer's packed, paged cache (the library's format).
 
     The pool is [num_blocks][H] slabs; a slab holds, for loops l = 0..L-1 and
     then K (kv=0) before V (kv=1), one page record of ``block_size`` tokens:
 
-        codes  block_size * D*b_l/8 bytes, token-major (pack_codes per token)
+        codes  block_size * D*b_l/8 bytes: K token-major (pack_codes per
+               token), V in the order of v_code_bits (reading R19)
         meta   block_size * (D/G) pairs (scale, zero), token-major, meta dtype
         alpha  block_size values, meta dtype          (residual loops only)
         pad    to a multiple of 16 bytes
@@ -323,11 +369,22 @@ def write_tokens(pool: np.ndarray, lay: PoolLayout, enc: Encoded, slots: np.ndar
         b = lay.bits(l)
         tb = lay.D * b // 8
         packed = pack_codes(q.codes, b)                     # [2][T][H][tb]
+        vpos = v_code_bits(lay.bs, lay.D, b)[off]           # [T][D] bit offsets of V codes
+        vmask = (1 << b) - 1
         for kv in range(2):
             for h in range(lay.H):
                 base = lay.record_offset(page, h, l, kv)    # [T]
-                cidx = (base + off * tb)[:, None] + np.arange(tb)
-                pool[cidx] = packed[kv, :, h, :]
+                if kv == 0:
+                    cidx = (base + off * tb)[:, None] + np.arange(tb)
+                    pool[cidx] = packed[kv, :, h, :]
+                else:
+                    # codes of several tokens can share a byte: clear then set
+                    # each code's bits with unbuffered (repeat-safe) updates
+                    byte = base[:, None] + vpos // 8
+                    sh = (vpos % 8).astype(np.uint8)
+                    code = q.codes[kv, :, h, :].astype(np.uint8)
+                    np.bitwise_and.at(pool, byte.ravel(), (~(np.uint8(vmask) << sh)).ravel().astype(np.uint8))
+                    np.bitwise_or.at(pool, byte.ravel(), (code << sh).ravel().astype(np.uint8))
                 meta = np.stack([q.scale[kv, :, h, :], q.zero[kv, :, h, :]], axis=-1)
                 mb = np.ascontiguousarray(meta.astype(mdt)).view(np.uint8).reshape(len(slots), -1)
                 midx = (base + lay.code_bytes(l) + off * (2 * ng * lay.msz))[:, None] + np.arange(mb.shape[1])
@@ -350,7 +407,11 @@ def read_pages(pool: np.ndarray, lay: PoolLayout, pages, head: int, l: int, kv: 
     raw = pool[idx]                                          # [P][rec]
     b = lay.bits(l)
     tb = lay.D * b // 8
-    codes = unpack_codes(raw[:, : lay.bs * tb].reshape(len(pages), lay.bs, tb), b)
+    if kv == 0:
+        codes = unpack_codes(raw[:, : lay.bs * tb].reshape(len(pages), lay.bs, tb), b)
+    else:
+        vpos = v_code_bits(lay.bs, lay.D, b)                 # [bs][D]
+        codes = ((raw[:, vpos // 8] >> (vpos % 8).astype(np.uint8)) & ((1 << b) - 1)).astype(np.uint8)
     mdt = _meta_np(lay.meta)
     mbytes = raw[:, lay.code_bytes(l): lay.code_bytes(l) + lay.meta_bytes()]
     meta = np.ascontiguousarray(mbytes).view(mdt).astype(np.float64).reshape(len(pages), lay.bs, lay.D // lay.G, 2)

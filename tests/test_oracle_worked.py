@@ -47,21 +47,64 @@ def test_worked_example_reconstruct(golden):
 
 
 def test_worked_layout_bytes(golden):
-    g = golden("worked_example_d4.txt")
-    lg = golden("worked_layout_d4.txt")
-    kv, rot32 = _example(g, "A")
-    enc = O.encode(kv, rot32, res_bits=(2,), G=4, meta="f16")
-    lay = O.PoolLayout(H=1, D=4, G=4, L=2, res_bits=(2,), meta="f16", num_blocks=1, block_size=2)
+    """Every byte of a slab holding one hand-derived token (D = 16, K = V,
+    R = I; worked_layout_d16.txt): token-major K codes, V codes in their
+    column-lane order, metadata and alpha."""
+    lg = golden("worked_layout_d16.txt")
+    x_ref = np.arange(16, dtype=np.float64)
+    k = np.array([3, 2, 1, 0, 0, 1, 2, 3, 3, 2, 1, 0, 0, 1, 2, 3], dtype=np.float64)
+    x0 = x_ref + (k - 1.5)
+    kv = np.stack([x0, x_ref])[:, None, None, None, :].repeat(2, axis=1)     # [L][2][T][H][D]
+    rot32 = np.stack([np.eye(16), np.eye(16)])[None].astype(np.float32)
+    enc = O.encode(kv, rot32, res_bits=(2,), G=16, meta="f16")
+    lay = O.PoolLayout(H=1, D=16, G=16, L=2, res_bits=(2,), meta="f16", num_blocks=1)
     assert lay.slab_bytes == lg["slab_bytes"][0]
     assert [lay.rec_bytes(0), lay.rec_bytes(1)] == lg["rec_bytes"]
     pool = np.zeros(lay.pool_bytes, dtype=np.uint8)
-    O.write_tokens(pool, lay, enc, np.array([1]))
-    want = bytes.fromhex("".join(h[0] for h in lg["hex"]))
-    assert pool.tobytes() == want
+    O.write_tokens(pool, lay, enc, np.array([5]))
+    want = np.zeros(lay.pool_bytes, dtype=np.uint8)
+    for off, val in lg["nz"]:
+        want[off] = val
+    np.testing.assert_array_equal(pool, want)
     # and reading it back returns the encoded values
-    c, s, z, a = O.read_pages(pool, lay, [0], 0, 0, 1)
-    assert list(c[0, 1]) == g["A_res_codes"] and a[0, 1] == 2.0
-    assert s[0, 1, 0] == _f16(g["A_res_scale_f16"]) and z[0, 1, 0] == _f16(g["A_res_zero_f16"])
+    for kvi in range(2):
+        c, s_, z, a = O.read_pages(pool, lay, [0], 0, 0, kvi)
+        assert list(c[0, 5]) == list(k) and a[0, 5] == 1.0
+        assert s_[0, 5, 0] == 1.0 and z[0, 5, 0] == -1.5
+        c, s_, z, a = O.read_pages(pool, lay, [0], 0, 1, kvi)
+        assert list(c[0, 5]) == list(range(16)) and a is None
+
+
+def test_v_code_order_hand_derived(golden):
+    """Single V code positions derived by hand from the storage order,
+    including a partial last word (D = 96, INT2)."""
+    for D, bits, t, c, byte, bit in golden("v_code_order.txt")["pos"]:
+        p = O.v_code_bits(16, D, bits)[t, c]
+        assert (p // 8, p % 8) == (byte, bit), (D, bits, t, c)
+
+
+def test_v_code_order_is_a_packing():
+    """Every code of a page gets its own aligned field, the fields tile the
+    code block exactly, and writing tokens in any slot order over stale bytes
+    then reading the page returns every code (every supported width, and the
+    tiny D used by hand examples)."""
+    rng = np.random.default_rng(0)
+    for D in (4, 16, 64, 96, 128):
+        for bits in (2, 4):
+            p = O.v_code_bits(16, D, bits)
+            assert np.unique(p).size == p.size and (p % bits == 0).all()
+            assert p.min() == 0 and p.max() == 16 * D * bits - bits
+            lay = O.PoolLayout(H=1, D=D, G=D, L=1, res_bits=(), meta="f16", num_blocks=2, direct_bits=(bits,))
+            codes = rng.integers(0, 1 << bits, size=(2, 16, 1, D)).astype(np.uint8)
+            q = O.Quantized(codes=codes, scale=np.ones((2, 16, 1, 1)), zero=np.zeros((2, 16, 1, 1)),
+                            u=codes.astype(np.float64), bits=bits)
+            enc = O.DirectEncoded(q=[q], G=D, meta="f16")
+            pool = np.full(lay.pool_bytes, 0xA5, dtype=np.uint8)          # stale bytes get overwritten
+            slots = 16 + rng.permutation(16)                                # token i -> page 1, offset slots[i]-16
+            O.write_tokens(pool, lay, enc, slots)
+            for kvi in range(2):
+                c, *_ = O.read_pages(pool, lay, [1], 0, 0, kvi)
+                np.testing.assert_array_equal(c[0, slots - 16], codes[kvi, :, 0])
 
 
 def test_worked_attention_closed_form():
@@ -87,8 +130,8 @@ def test_worked_example_rounded_alpha(golden):
 
 
 def test_worked_layout_offsets(golden):
-    lg = golden("worked_layout_d4.txt")
-    lay = O.PoolLayout(H=2, D=4, G=4, L=2, res_bits=(2,), meta="f16", num_blocks=3, block_size=2)
+    lg = golden("worked_layout_d16.txt")
+    lay = O.PoolLayout(H=2, D=16, G=16, L=2, res_bits=(2,), meta="f16", num_blocks=3)
     assert lay.pool_bytes == lg["pool_bytes"][0]
     for blk, head, loop, kv, off in lg["offset"]:
         assert lay.record_offset(blk, head, loop, kv) == off
