@@ -83,7 +83,7 @@ def token_head_bytes(w, loop):
     return ref + 2 * (D * b // 8 + 2 * m * (D // G) + m)
 
 
-def setup_rq(w, dev, split_pages):
+def setup_rq(w, dev, split_pages, split_pages_multi):
     import torch
     import looped_transformer_decode_rq_amd as R
     import workloads as W
@@ -119,7 +119,7 @@ def setup_rq(w, dev, split_pages):
     s["tk_all"] = cur[:, 0].contiguous()
     s["tv_all"] = cur[:, 1].contiguous()
     s["out_all"] = torch.empty((L, B, H, D), device=dev)
-    s["ws_all"] = torch.empty(R.decode_workspace_bytes(lay, L, B, table.shape[1], split_pages),
+    s["ws_all"] = torch.empty(R.decode_workspace_bytes(lay, L, B, table.shape[1], split_pages_multi),
                               dtype=torch.uint8, device=dev)
     return s
 
@@ -338,9 +338,14 @@ def main():
     dev = torch.device("cuda:0")
     B, N, H, D, L = w.batch, w.context, w.heads, w.head_dim, w.loops
     table_w = -(-(N + 1) // 16)
-    args.split_pages = args.split_pages or _auto_split(B * H, table_w)
-    log(f"workload {w.name}: setting up packed cache (split {args.split_pages} pages)")
-    rq = setup_rq(w, dev, args.split_pages)
+    # pages per split: the library's own choice for each mode unless forced
+    probe = R.make_layout(H, D, w.group_size, L, w.res_bits, 1, w.meta_dtype, w.kv_dtype)
+    sp_loop = args.split_pages or R.decode_auto_split_pages(probe, 1, B, table_w)
+    sp_multi = args.split_pages or R.decode_auto_split_pages(probe, L, B, table_w)
+    sp_bf16 = args.split_pages or R.bf16_auto_split_pages(H, B, table_w)
+    log(f"workload {w.name}: setting up packed cache (split pages: per-loop {sp_loop}, multi-loop {sp_multi}, "
+        f"bf16 {sp_bf16})")
+    rq = setup_rq(w, dev, sp_loop, sp_multi)
     if args.copy_probe_mib:
         src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
@@ -353,7 +358,7 @@ def main():
     pairs = {(k, l): (ev.create(), ev.create()) for k in range(args.steps) for l in range(L)}
 
     def rq_fn(k):
-        rq_step(w, rq, args.split_pages, None if k is None else [pairs[(k, l)] for l in range(L)],
+        rq_step(w, rq, sp_loop, None if k is None else [pairs[(k, l)] for l in range(L)],
                 fused=not args.separate_encode)
 
     log("timing packed step")
@@ -365,8 +370,8 @@ def main():
         ev.destroy(b)
     res_ms = float(np.mean([m for l in res_loops for m in split_ms[l]]))
     ref_ms = float(np.mean(split_ms[L - 1]))
-    nsplit = -(-rq["table"].shape[1] // args.split_pages)
-    nwg = -(-nsplit // 4)                       # one partial per 4-wave split workgroup
+    nwg = -(-rq["table"].shape[1] // (4 * sp_loop))     # one partial per 4-wave split workgroup
+    nsplit = -(-rq["table"].shape[1] // sp_multi)       # multi-loop: one partial per split and loop
     qp = 64 + 4 * D
     res_bytes = (token_head_bytes(w, 0) * B * H * N + B * H * qp + B * N // 16 * 4
                  + B * H * nwg * (2 + 2 * D) * 4)
@@ -387,7 +392,7 @@ def main():
     mpairs = {k: (ev.create(), ev.create()) for k in range(args.steps)}
 
     def multi_fn(k):
-        rq_multi_step(w, rq, args.split_pages, None if k is None else mpairs[k], fused=not args.separate_encode)
+        rq_multi_step(w, rq, sp_multi, None if k is None else mpairs[k], fused=not args.separate_encode)
 
     log("timing packed multi-loop step")
     t_multi = timed(multi_fn, args.steps, args.warmup)
@@ -416,11 +421,11 @@ def main():
     bf16 = None
     if not args.no_bf16:
         log("setting up bf16 baseline cache")
-        b16 = setup_bf16(w, dev, rq, args.split_pages)
+        b16 = setup_bf16(w, dev, rq, sp_bf16)
         bpairs = {k: [(ev.create(), ev.create()) for _ in range(L)] for k in range(args.steps)}
 
         def bf_fn(k):
-            bf16_step(w, rq, b16, args.split_pages, None if k is None else bpairs[k])
+            bf16_step(w, rq, b16, sp_bf16, None if k is None else bpairs[k])
 
         t_bf = timed(bf_fn, args.steps, args.warmup)
         bms = []
@@ -442,7 +447,7 @@ def main():
         for l in range(L):
             R.bf16_decode_attention(b16["kc"][l], b16["vc"][l], b16["q"][l], rq["d_table"], rq["d_seq"],
                                     rq["tk"][l][0], rq["tv"][l][0], tau, b16["out"], b16["ws"],
-                                    split_pages=args.split_pages)
+                                    split_pages=sp_bf16)
             exact.append(b16["out"].clone())
         errors["rq_per_loop"] = [rel_l2(rq["out"][l, 0], exact[l]) for l in range(L)]
         errors["rq_multi_loop"] = [rel_l2(rq["out_all"][l], exact[l]) for l in range(L)]
@@ -476,7 +481,7 @@ def main():
         "data": "synthetic (seeded generator; no model weights)",
         "config": {"workload": w.name, "layers": 1, "batch": B, "context": N, "heads": H, "head_dim": D,
                    "loops": L, "group_size": w.group_size, "res_bits": list(w.res_bits), "block_size": 16,
-                   "split_pages": args.split_pages,
+                   "split_pages": {"per_loop": sp_loop, "multi_loop": sp_multi, "bf16": sp_bf16},
                    "step": "4 per-loop decode calls (each + bf16 current token) + encode of 16 new tokens "
                            + ("(own launch)" if args.separate_encode else "(in the reference-loop call's launch)")},
         "effective_hbm_gbs": step_gbs,
@@ -504,14 +509,6 @@ def main():
                                "peak_throughput_speedup": "up to 4.15x on RTX 5090"},
     }
     print(json.dumps(line), flush=True)
-
-
-def _auto_split(units, max_blocks):
-    """Pages per split: the smallest power of two keeping ~16K waves per call."""
-    sp = 1
-    while sp < 64 and units * (-(-max_blocks // sp)) > 16384:
-        sp *= 2
-    return sp
 
 
 if __name__ == "__main__":

@@ -20,8 +20,9 @@ RQ_MODE_RESIDUAL, RQ_MODE_DIRECT = 0, 1
 
 EXPORTED = [
     "rq_status_string", "rq_layout_check", "rq_pool_bytes", "rq_record_bytes", "rq_record_offset",
-    "rq_encode_pack", "rq_decode_workspace_bytes", "rq_decode_attention", "rq_decode_attention_ex",
-    "rq_decode_attention_encode", "rq_fit_rotation", "rq_bf16_workspace_bytes", "rq_bf16_decode_attention", "rq_bf16_decode_attention_ex", "rq_bf16_write",
+    "rq_encode_pack", "rq_decode_workspace_bytes", "rq_decode_auto_split_pages", "rq_decode_attention",
+    "rq_decode_attention_ex", "rq_decode_attention_encode", "rq_fit_rotation", "rq_bf16_workspace_bytes",
+    "rq_bf16_auto_split_pages", "rq_bf16_decode_attention", "rq_bf16_decode_attention_ex", "rq_bf16_write",
 ]
 
 
@@ -63,6 +64,7 @@ def lib():
             "rq_record_offset": (c_int64, [POINTER(RqLayout), c_int32, c_int32, c_int32, c_int32]),
             "rq_encode_pack": (c_int32, [POINTER(RqLayout), P, P, P, P, c_int32, P]),
             "rq_decode_workspace_bytes": (c_size_t, [POINTER(RqLayout), c_int32, c_int32, c_int32, c_int32]),
+            "rq_decode_auto_split_pages": (c_int32, [POINTER(RqLayout), c_int32, c_int32, c_int32]),
             "rq_decode_attention": (c_int32, [POINTER(RqLayout), P, P, c_int32, P, P, P, P, c_int32, c_int32,
                                               P, P, c_float, P, P, c_size_t, P]),
             "rq_decode_attention_ex": (c_int32, [POINTER(RqLayout), P, P, c_int32, P, P, P, P, c_int32, c_int32,
@@ -72,6 +74,7 @@ def lib():
                                                      POINTER(RqDecodeOpts), P]),
             "rq_fit_rotation": (c_int32, [P, c_int64, c_int32, c_int32, c_int32, c_int32, P, c_int32, P, P]),
             "rq_bf16_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32]),
+            "rq_bf16_auto_split_pages": (c_int32, [c_int32, c_int32, c_int32]),
             "rq_bf16_decode_attention": (c_int32, [c_int32, c_int32, c_int32, c_int32, P, P, P, P, P, c_int32,
                                                    c_int32, P, P, c_float, P, P, c_size_t, P]),
             "rq_bf16_decode_attention_ex": (c_int32, [c_int32, c_int32, c_int32, c_int32, P, P, P, P, P, c_int32,
@@ -183,6 +186,11 @@ def decode_workspace_bytes(layout, n_loops, batch, max_blocks_per_seq, split_pag
     return lib().rq_decode_workspace_bytes(ctypes.byref(layout), n_loops, batch, max_blocks_per_seq, split_pages)
 
 
+def decode_auto_split_pages(layout, n_loops, batch, max_blocks_per_seq) -> int:
+    """Pages per split the decode call picks for split_pages=0 on the current device."""
+    return lib().rq_decode_auto_split_pages(ctypes.byref(layout), n_loops, batch, max_blocks_per_seq)
+
+
 def _opts(split_pages, events):
     o = RqDecodeOpts()
     o.split_pages = int(split_pages or 0)
@@ -239,6 +247,10 @@ def decode_attention(layout, pool, loops, q, rot, block_table, seq_lens, tail_k,
 
 def bf16_workspace_bytes(num_heads, head_dim, batch, max_blocks_per_seq, split_pages=0) -> int:
     return lib().rq_bf16_workspace_bytes(num_heads, head_dim, batch, max_blocks_per_seq, split_pages)
+
+
+def bf16_auto_split_pages(num_heads, batch, max_blocks_per_seq) -> int:
+    return lib().rq_bf16_auto_split_pages(num_heads, batch, max_blocks_per_seq)
 
 
 def bf16_decode_attention(k_cache, v_cache, q, block_table, seq_lens, tail_k, tail_v, softmax_scale, out,

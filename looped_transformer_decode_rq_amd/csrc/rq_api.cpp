@@ -3,6 +3,9 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
+#include <atomic>
+
 #include "rq_internal.h"
 
 namespace rq {
@@ -49,11 +52,35 @@ rq_status make_geom(const rq_layout *lay, Geom *g) {
     return RQ_OK;
 }
 
-int auto_split_pages(int units, int max_blocks) {
-    // aim for at most ~16K waves in flight per loop call, pages per split a power of two
-    int sp = 1;
-    while (sp < kMaxSplitPages && (int64_t)units * ((max_blocks + sp - 1) / sp) > 16384) sp *= 2;
-    return sp;
+// Compute units of the current device (queried once per device; 256 if the
+// query fails).
+static int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+int auto_split_pages(int units, int max_blocks, bool multi) {
+    // A split-K launch runs in rounds of resident workgroups (about three per
+    // CU for these kernels); the last round is partly empty. Enough
+    // workgroups for ~8 rounds (one split per 4-wave workgroup per loop) or
+    // ~14 rounds (multi-loop: one split per workgroup, each reading a page
+    // once for all its loops) keep that tail small without shrinking the
+    // splits to where per-split setup and partials dominate. The pages are
+    // then spread evenly over the splits of a row.
+    const int waves = multi ? 1 : kSplitWaves;
+    const int64_t target = (int64_t)(multi ? 14 : 8) * 3 * device_cus();
+    const int64_t wg_per_unit = std::max<int64_t>(1, (target + units - 1) / std::max(units, 1));
+    int64_t sp = ((int64_t)max_blocks + waves * wg_per_unit - 1) / (waves * wg_per_unit);
+    sp = std::min<int64_t>(kMaxSplitPages, std::max<int64_t>(kMinAutoSplitPages, sp));
+    const int64_t nwg = ((int64_t)max_blocks + waves * sp - 1) / (waves * sp);
+    sp = ((int64_t)max_blocks + waves * nwg - 1) / (waves * nwg);
+    return (int)std::max<int64_t>(1, sp);
 }
 
 static int nsplit_of(int max_blocks, int sp) { return (max_blocks + sp - 1) / sp; }
@@ -62,6 +89,10 @@ int partials_per_row(int n, int max_blocks, int sp) {
     const int ns = nsplit_of(max_blocks, sp);
     return n >= 2 ? ns : (ns + kSplitWaves - 1) / kSplitWaves;
 }
+
+// Several loop calls in one request share a multi-loop kernel (one split per
+// workgroup); direct-mode calls are decoded one kernel per loop.
+static bool multi_mode(const Geom &g, int n_loops) { return n_loops >= 2 && !g.direct; }
 
 static size_t decode_ws(const Geom &g, int n, int B, int max_blocks, int sp) {
     const size_t qp = round_up((size_t)n * B * g.H * qpack_bytes(g.D), 256);
@@ -139,8 +170,20 @@ size_t rq_decode_workspace_bytes(const rq_layout *layout, int32_t n_loops, int32
     if (make_geom(layout, &g) != RQ_OK || n_loops < 1 || batch < 0 || max_blocks_per_seq < 1 || split_pages < 0 ||
         split_pages > kMaxSplitPages)
         return 0;
-    const int sp = split_pages > 0 ? split_pages : auto_split_pages(batch * g.H, max_blocks_per_seq);
+    const int sp = split_pages > 0 ? split_pages : auto_split_pages(batch * g.H, max_blocks_per_seq, multi_mode(g, n_loops));
     return decode_ws(g, n_loops, batch, max_blocks_per_seq, sp);
+}
+
+int32_t rq_decode_auto_split_pages(const rq_layout *layout, int32_t n_loops, int32_t batch,
+                                   int32_t max_blocks_per_seq) {
+    Geom g;
+    if (make_geom(layout, &g) != RQ_OK || n_loops < 1 || batch < 1 || max_blocks_per_seq < 1) return 0;
+    return auto_split_pages(batch * g.H, max_blocks_per_seq, multi_mode(g, n_loops));
+}
+
+int32_t rq_bf16_auto_split_pages(int32_t num_heads, int32_t batch, int32_t max_blocks_per_seq) {
+    if (num_heads < 1 || batch < 1 || max_blocks_per_seq < 1) return 0;
+    return auto_split_pages(batch * num_heads, max_blocks_per_seq, false);
 }
 
 static rq_status decode_impl(const rq_layout *layout, const void *pool, const int32_t *loops, int32_t n_loops,
@@ -172,7 +215,7 @@ static rq_status decode_impl(const rq_layout *layout, const void *pool, const in
     if (!pool || !q || !block_table || !seq_lens || !out || (any_res && !rot)) return RQ_ERR_NULL;
     if (!aligned(pool, 16)) return RQ_ERR_SHAPE;
     if ((int64_t)max_blocks_per_seq * 16 > (int64_t)1 << 30) return RQ_ERR_SHAPE;
-    const int sp = sp_req > 0 ? sp_req : auto_split_pages(batch * g.H, max_blocks_per_seq);
+    const int sp = sp_req > 0 ? sp_req : auto_split_pages(batch * g.H, max_blocks_per_seq, multi_mode(g, n_loops));
     const size_t need = decode_ws(g, n_loops, batch, max_blocks_per_seq, sp);
     if (!workspace) return RQ_ERR_NULL;
     if (workspace_bytes < need) return RQ_ERR_WORKSPACE;
@@ -233,7 +276,7 @@ size_t rq_bf16_workspace_bytes(int32_t num_heads, int32_t head_dim, int32_t batc
                                int32_t split_pages) {
     if (num_heads < 1 || batch < 0 || max_blocks_per_seq < 1 || split_pages < 0) return 0;
     if (head_dim != 64 && head_dim != 96 && head_dim != 128) return 0;
-    const int sp = split_pages > 0 ? split_pages : auto_split_pages(batch * num_heads, max_blocks_per_seq);
+    const int sp = split_pages > 0 ? split_pages : auto_split_pages(batch * num_heads, max_blocks_per_seq, false);
     return bf16_ws(num_heads, head_dim, batch, max_blocks_per_seq, sp);
 }
 
@@ -254,7 +297,7 @@ rq_status rq_bf16_decode_attention_ex(int32_t num_heads, int32_t head_dim, int32
     if (!k_cache || !v_cache || !q || !block_table || !seq_lens || !out) return RQ_ERR_NULL;
     if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(q, 16)) return RQ_ERR_SHAPE;
     if ((int64_t)max_blocks_per_seq * 16 > (int64_t)1 << 30) return RQ_ERR_SHAPE;
-    const int sp = sp_req > 0 ? sp_req : auto_split_pages(batch * num_heads, max_blocks_per_seq);
+    const int sp = sp_req > 0 ? sp_req : auto_split_pages(batch * num_heads, max_blocks_per_seq, false);
     if (!workspace) return RQ_ERR_NULL;
     if (workspace_bytes < bf16_ws(num_heads, head_dim, batch, max_blocks_per_seq, sp)) return RQ_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return RQ_ERR_SHAPE;

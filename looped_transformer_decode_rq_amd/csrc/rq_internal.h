@@ -30,10 +30,14 @@ inline int lanes_per_token(int D) { return D == 96 ? 2 : 4; }
 __host__ __device__ constexpr int qpack_bytes(int D) { return 64 + 4 * D; }
 __host__ __device__ constexpr int partial_floats(int D) { return 2 + 2 * D; }
 
-int auto_split_pages(int units, int max_blocks);
+// Pages per split chosen when the caller passes 0: sized so that a launch
+// has several rounds of resident workgroups (units = sequences x heads,
+// multi = one split per workgroup for several loop calls at once).
+int auto_split_pages(int units, int max_blocks, bool multi);
 
 constexpr int kSplitWaves = 4;     // waves (splits) per split-K workgroup
 constexpr int kMaxSplitPages = 64; // pages per split: one block-table entry per lane
+constexpr int kMinAutoSplitPages = 16;  // smallest split the automatic choice aims for
 constexpr int kMaxMultiLoops = 8;  // loop calls (waves) per multi-loop workgroup
 
 // Partials per (loop call, sequence, head) row: one per split workgroup of 4

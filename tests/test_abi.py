@@ -227,3 +227,30 @@ def test_binding_refuses_host_tensors(L):
         R.encode_pack(lay, torch.zeros(R.pool_bytes(lay), dtype=torch.uint8),
                       torch.zeros(2, 2, 1, 1, 64), torch.zeros(1, 2, 64, 64),
                       torch.zeros(1, dtype=torch.int64))
+
+
+def test_auto_split_fills_several_rounds(L):
+    """The automatic split: pages spread evenly, several rounds of split
+    workgroups per launch, and the workspace query sized with the same rule.
+    Without a GPU the device query falls back to 256 compute units."""
+    lay = _lay(LAYOUTS[1])
+    units, mb = 16 * 16, 2049
+    sp1 = R.decode_auto_split_pages(lay, 1, 16, mb)
+    spm = R.decode_auto_split_pages(lay, 4, 16, mb)
+    assert 1 <= sp1 <= 64 and 1 <= spm <= 64
+    wg1 = -(-mb // (4 * sp1))
+    assert units * wg1 >= 8 * 3 * 256                     # >= 8 rounds of 3 workgroups per CU
+    assert -(-mb // (4 * wg1)) == sp1                      # pages spread evenly over the splits
+    assert units * -(-mb // spm) >= 14 * 3 * 256 or spm == 64 or -(-mb // 64) == -(-mb // spm)
+    assert (sp1, spm) == (22, 49)
+    assert R.decode_workspace_bytes(lay, 1, 16, mb, 0) == R.decode_workspace_bytes(lay, 1, 16, mb, sp1)
+    assert R.decode_workspace_bytes(lay, 4, 16, mb, 0) == R.decode_workspace_bytes(lay, 4, 16, mb, spm)
+    assert R.bf16_auto_split_pages(16, 16, mb) == sp1
+    assert R.bf16_workspace_bytes(16, 128, 16, mb, 0) == R.bf16_workspace_bytes(16, 128, 16, mb, sp1)
+    # small problems keep at least one page per split and never exceed 64
+    for B_, mb_ in ((1, 1), (1, 17), (2, 257), (128, 513), (8, 513)):
+        for n in (1, 4):
+            sp = R.decode_auto_split_pages(lay, n, B_, mb_)
+            assert 1 <= sp <= 64, (B_, mb_, n, sp)
+    assert R.decode_auto_split_pages(lay, 0, 16, mb) == 0
+    assert R.bf16_auto_split_pages(0, 16, mb) == 0
