@@ -32,8 +32,20 @@
  * slab (block, head) at byte (block * num_heads + head) * slab_bytes. A slab
  * holds, for l = 0 .. num_loops-1 in order and inside each loop K (kv=0) then
  * V (kv=1), one page record of block_size tokens:
- *     codes   block_size * head_dim * b_l / 8 bytes, token-major; channel i of
- *             a token sits in byte i*b_l/8 at bit (i mod (8/b_l)) * b_l
+ *     codes   block_size * head_dim * b_l / 8 bytes. K records: token-major;
+ *             channel i of a token sits in byte i*b_l/8 at bit
+ *             (i mod (8/b_l)) * b_l. V records: ordered for the B operand of
+ *             a 16x16x16 matrix instruction (tokens along k). Token t is
+ *             position v = t%4 of quad u = t/4; channel c is column j = c%16
+ *             of group m = c/16. "Lane" 16u + j (0..63) holds the codes
+ *             (t = 4u+v, c = 16m+j) for every m and v. W = 8/b_l groups
+ *             share a 32-bit word: word p holds groups W*p .. W*p+W_p-1
+ *             (W_p = min(W, head_dim/16 - W*p)), with code (m = W*p+i, v) in
+ *             bits [f*b_l, (f+1)*b_l), f = 2*W_p*(v%2) + W_p*(v/2) + i.
+ *             Word p of all 64 lanes forms plane p (lane order,
+ *             W_p*b_l/2 bytes per lane); the planes follow one another.
+ *             Every plane is 256 bytes except the last one of
+ *             head_dim = 96 INT2, which has 16-bit units (128 bytes).
  *     meta    block_size * (head_dim/group_size) pairs (scale, zero), token-
  *             major, meta dtype
  *     alpha   block_size values, meta dtype (only for loops l < num_loops-1)
@@ -146,7 +158,11 @@ int64_t rq_record_offset(const rq_layout *layout, int32_t block, int32_t head,
  * (0 if x_ref = 0) rounded to meta_dtype; d = x_l - alpha*x_ref;
  * r = R*d; per group: scale = (max-min)/(2^b-1) and zero = min rounded to
  * meta_dtype (nearest even); code = clamp(rint((y-zero)/scale), 0, 2^b-1),
- * all codes 0 when scale == 0. Tokens of one call must have distinct slots. */
+ * all codes 0 when scale == 0. Tokens of one call must have distinct slots.
+ * V codes of the four tokens of a quad share 32-bit words; each token's codes
+ * are written with atomic and/or on those words, so writes of different
+ * tokens of one page (in one call or in calls running at once) never clobber
+ * each other. */
 rq_status rq_encode_pack(const rq_layout *layout, void *pool, const void *kv_new,
                          const float *rot, const int64_t *slot_mapping,
                          int32_t num_tokens, void *stream);
@@ -155,6 +171,18 @@ rq_status rq_encode_pack(const rq_layout *layout, void *pool, const void *kv_new
 size_t rq_decode_workspace_bytes(const rq_layout *layout, int32_t n_loops,
                                  int32_t batch, int32_t max_blocks_per_seq,
                                  int32_t split_pages);
+
+/* Pages per split that rq_decode_attention(_ex) uses when split_pages is 0,
+ * for these sizes on the current device: enough split workgroups for several
+ * rounds of resident workgroups on the device's compute units, the pages
+ * spread evenly over the splits (per-loop calls: about 8 rounds of 4-split
+ * workgroups; several non-direct loops in one call: about 14 rounds of
+ * one-split workgroups), clamped to 16..64 before the even spread. The same
+ * rule sizes rq_decode_workspace_bytes(..., 0), so a workspace sized on one
+ * device may be too small on a device with more compute units
+ * (RQ_ERR_WORKSPACE). Returns 0 for invalid arguments. */
+int32_t rq_decode_auto_split_pages(const rq_layout *layout, int32_t n_loops,
+                                   int32_t batch, int32_t max_blocks_per_seq);
 
 /* Decode attention of one query per (loop, sequence, head) over the packed
  * cache plus the uncompressed current token (arXiv 2610.10381 abstract: the
@@ -242,6 +270,11 @@ rq_status rq_fit_rotation(const float *samples, int64_t n, int32_t head_dim, int
  * head_dim in {64, 96, 128}; block_size must be 16. */
 size_t rq_bf16_workspace_bytes(int32_t num_heads, int32_t head_dim, int32_t batch,
                                int32_t max_blocks_per_seq, int32_t split_pages);
+
+/* Pages per split of the bf16 baseline when split_pages is 0: the per-loop
+ * rule of rq_decode_auto_split_pages. Returns 0 for invalid arguments. */
+int32_t rq_bf16_auto_split_pages(int32_t num_heads, int32_t batch,
+                                 int32_t max_blocks_per_seq);
 
 rq_status rq_bf16_decode_attention(int32_t num_heads, int32_t head_dim,
                                    int32_t block_size, int32_t num_blocks,

@@ -318,48 +318,98 @@ __device__ __forceinline__ float lane_group_sum(float v) {
     return r;
 }
 
-// Byte J of x as a float: one v_cvt_f32_ubyteJ, which selects the byte
-// itself (written out because the compiler otherwise re-extracts each masked
-// field with a separate bit-field extract first).
-template <int J>
-__device__ __forceinline__ float cvt_ubyte(uint32_t x) {
-    float r;
-    __asm__("v_cvt_f32_ubyte%c1 %0, %2" : "=v"(r) : "n"(J), "v"(x));
-    return r;
+// ---- V on the matrix cores
+//
+// The V codes of a page record are stored for the B operand of
+// v_mfma_f32_16x16x16_f16 (the record format in rq.h): lane l = 16u + j
+// holds, for column group m = 0..D/16-1, the codes of tokens 4u..4u+3 at
+// channel 16m + j, packed in 32-bit word planes (plane p of lane l at byte
+// 256p + 4l of the code block; the one partial word, D = 96 INT2, is a 16-bit
+// unit at 256p + 2l). Inside word p, the code of (group W*p + i, token 4u+v)
+// is field 2W(v%2) + W(v/2) + i (W = 8/bits groups per word; W_p for the
+// partial word), so one shift and one and-or turn two codes of the same group
+// into the fp16 pair (16 + c_v, 16 + c_{v+1}): 16 + c is exact in fp16 as
+// 0x4C00 | c << 6.
+//
+// The per-token weights (p*alpha*s for the reference, p*s for the residual)
+// form the A operand: rows 4g + r of group g hold (reference hi, lo, residual
+// hi, lo) of the weight split into two fp16 terms (hi = RNE(w), lo = RNE(w -
+// hi): relative error <= 2^-22 while w is a normal fp16 number, absolute
+// <= 2^-25 below; w <= 256*alpha*s by the lazy softmax rescale), tokens
+// along k. Row 4g+r of the product is then sum_t w_t (16 + c_t) for every
+// column, lanes 16g..16g+15 receiving the rows of group g. The offset 16 is
+// taken out again with the same rounded weights, in the zero term:
+// value sum = sum_t w_t (16 + c_t) + sum_t (p alpha z_t - 16 w_t).
+typedef _Float16 halfx4 __attribute__((ext_vector_type(4)));
+typedef _Float16 halfx2 __attribute__((ext_vector_type(2)));
+
+// fp16 pair (16 + c, 16 + c') of the BITS-bit fields at bit SH and at bit
+// SH + 16 of w: one shift to bit 6, then (x & mask) | 0x4C004C00. The mask and
+// the exponent bits come in as opaque registers (vmask: SGPR, exp16: VGPR),
+// so that the compiler selects a single v_and_or_b32 (a VOP3 takes no literal
+// and reads at most one scalar operand) and still tracks its hazards.
+template <int SH>
+__device__ __forceinline__ uint32_t vpair(uint32_t w, uint32_t vmask, uint32_t exp16) {
+    const uint32_t x = SH == 6 ? w : (SH > 6 ? (w >> (SH - 6)) : (w << (6 - SH)));
+    return (x & vmask) | exp16;
 }
 
-// acc[8k + 2j (+1)] += w * code for INT4 words: the even channels of a word
-// are the low nibbles of its bytes, the odd ones the high nibbles
-template <int NW>
-__device__ __forceinline__ void axpy_int4(float *acc, const uint32_t *codes, float w) {
+// The opaque operands of vpair for BITS-bit codes.
+template <int BITS>
+__device__ __forceinline__ void vpair_consts(uint32_t &vmask, uint32_t &exp16) {
+    if constexpr (BITS == 4) __asm__("s_mov_b32 %0, 0x03c003c0" : "=s"(vmask));
+    else __asm__("s_mov_b32 %0, 0x00c000c0" : "=s"(vmask));
+    __asm__("v_mov_b32 %0, 0x4c004c00" : "=v"(exp16));
+}
+
+__device__ __forceinline__ floatx4 mfma_f16(uint2 a, uint32_t b0, uint32_t b1, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(halfx4, a),
+                                                 __builtin_bit_cast(halfx4, make_uint2(b0, b1)), c, 0, 0, 0);
+}
+
+// This lane's words of one page's V code block `vb` (BITS-bit codes, D
+// channels): the full 32-bit words, then the 16-bit partial unit (D = 96
+// INT2) with its upper fields moved 8 bits up so that every word is read the
+// same way
+template <int D, int BITS>
+struct VWords {
+    static constexpr int NM = D / 16, W = 8 / BITS;
+    static constexpr int NFULL = NM / W, REM = NM - NFULL * W;
+    static constexpr int N = NFULL + (REM > 0 ? 1 : 0);
+    uint32_t w[N];
+};
+
+template <int D, int BITS>
+__device__ __forceinline__ void load_v(VWords<D, BITS> &v, const uint8_t *vb, int lane) {
+    using V = VWords<D, BITS>;
 #pragma unroll
-    for (int k = 0; k < NW; ++k) {
-        const uint32_t lo = codes[k] & 0x0F0F0F0Fu, hi = (codes[k] >> 4) & 0x0F0F0F0Fu;
-        acc[8 * k + 0] = fmaf(w, cvt_ubyte<0>(lo), acc[8 * k + 0]);
-        acc[8 * k + 1] = fmaf(w, cvt_ubyte<0>(hi), acc[8 * k + 1]);
-        acc[8 * k + 2] = fmaf(w, cvt_ubyte<1>(lo), acc[8 * k + 2]);
-        acc[8 * k + 3] = fmaf(w, cvt_ubyte<1>(hi), acc[8 * k + 3]);
-        acc[8 * k + 4] = fmaf(w, cvt_ubyte<2>(lo), acc[8 * k + 4]);
-        acc[8 * k + 5] = fmaf(w, cvt_ubyte<2>(hi), acc[8 * k + 5]);
-        acc[8 * k + 6] = fmaf(w, cvt_ubyte<3>(lo), acc[8 * k + 6]);
-        acc[8 * k + 7] = fmaf(w, cvt_ubyte<3>(hi), acc[8 * k + 7]);
+    for (int p = 0; p < V::NFULL; ++p) v.w[p] = ((const uint32_t *)vb)[64 * p + lane];
+    if constexpr (V::REM > 0) {
+        const uint32_t u = ((const uint16_t *)(vb + 256 * V::NFULL))[lane];
+        v.w[V::NFULL] = u | (u << (16 - 2 * V::REM * BITS));
     }
 }
 
-// acc[16k + 4j + i] += w * code for INT2 words: crumb i of byte j
-template <int NW>
-__device__ __forceinline__ void axpy_int2(float *acc, const uint32_t *codes, float w) {
-#pragma unroll
-    for (int k = 0; k < NW; ++k) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t c = (codes[k] >> (2 * i)) & 0x03030303u;
-            acc[16 * k + 0 + i] = fmaf(w, cvt_ubyte<0>(c), acc[16 * k + 0 + i]);
-            acc[16 * k + 4 + i] = fmaf(w, cvt_ubyte<1>(c), acc[16 * k + 4 + i]);
-            acc[16 * k + 8 + i] = fmaf(w, cvt_ubyte<2>(c), acc[16 * k + 8 + i]);
-            acc[16 * k + 12 + i] = fmaf(w, cvt_ubyte<3>(c), acc[16 * k + 12 + i]);
-        }
+// acc[m] += A x B_m for every column group m of the page
+template <int WP, int BITS, int I>
+__device__ __forceinline__ void v_mfma_word(floatx4 *acc, uint32_t w, uint2 a, uint32_t vmask, uint32_t exp16) {
+    if constexpr (I < WP) {
+        const uint32_t b0 = vpair<BITS * I>(w, vmask, exp16);
+        const uint32_t b1 = vpair<BITS * (WP + I)>(w, vmask, exp16);
+        acc[I] = mfma_f16(a, b0, b1, acc[I]);
+        v_mfma_word<WP, BITS, I + 1>(acc, w, a, vmask, exp16);
     }
+}
+
+template <int D, int BITS>
+__device__ __forceinline__ void v_mfma(floatx4 *acc, const VWords<D, BITS> &v, uint2 a) {
+    using V = VWords<D, BITS>;
+    uint32_t vmask, exp16;
+    vpair_consts<BITS>(vmask, exp16);
+#pragma unroll
+    for (int p = 0; p < V::NFULL; ++p) v_mfma_word<V::W, BITS, 0>(acc + V::W * p, v.w[p], a, vmask, exp16);
+    if constexpr (V::REM > 0)
+        v_mfma_word<V::REM, BITS, 0>(acc + V::W * V::NFULL, v.w[V::NFULL], a, vmask, exp16);
 }
 
 __device__ __forceinline__ void sz_of(float2 v, float &s, float &z) { s = v.x; z = v.y; }
@@ -379,13 +429,20 @@ struct QueryRegs {
     uint4 lrv[Lanes<D>::NDW], lsv[Lanes<D>::NDW];
 };
 
-// Online-softmax state of one lane: running max (log2 units), sum of weights,
-// the per-group zero terms and the V accumulators (reference, rotated residual).
+// Online-softmax state of one wave: running max (log2 units) and, per lane,
+// its token slots' sum of weights and per-group zero terms; the V sums of
+// the whole wave in matrix accumulators: rows 4g, 4g+1 of column group m
+// sum the reference term, rows 4g+2, 4g+3 the rotated residual (the A
+// operand of the reference codes is zero in the residual rows and vice
+// versa, so both share one accumulator).
 template <int D>
 struct SplitState {
     float m, lsum, zr, zs;
-    float accr[Lanes<D>::CPL], accs[Lanes<D>::CPL];
+    floatx4 v[D / 16];
 };
+
+// Bytes of the per-wave weight scratch (A operand rows) of one page.
+constexpr int kWScratch = 16 * 16 * 2;
 
 template <int D, bool RES>
 __device__ __forceinline__ void load_query(const uint8_t *qp, int q4, QueryRegs<D> &q) {
@@ -419,31 +476,48 @@ template <int D>
 __device__ __forceinline__ void init_state(SplitState<D> &s) {
     s.m = kNegInf; s.lsum = 0.f; s.zr = 0.f; s.zs = 0.f;
 #pragma unroll
-    for (int i = 0; i < Lanes<D>::CPL; ++i) { s.accr[i] = 0.f; s.accs[i] = 0.f; }
+    for (int i = 0; i < D / 16; ++i) s.v[i] = floatx4{0.f, 0.f, 0.f, 0.f};
 }
 
-// One token slot of one lane (LPT lanes per token): score it from the codes in
-// LDS and fold it into the online softmax and both V accumulators.
-//   ck, cv      this lane's reference K / V code bytes
-//   mkr, mvr    the token's reference K / V (scale, zero) of this lane's group
-//   rk, rv      this lane's residual K / V code bytes (RB != 0)
-//   mks, mvs    residual (scale, zero); aks, avs residual alphas (RB != 0)
-//   lsv         this lane's residual query limbs (registers or LDS)
-template <int D, int RB, bool META_F32, int REFB = 4>
-__device__ __forceinline__ void token_step(const uint8_t *ck, const uint8_t *cv, const uint8_t *mkr,
-                                           const uint8_t *mvr, const uint8_t *rk, const uint8_t *rv,
-                                           const uint8_t *mks, const uint8_t *aks, const uint8_t *mvs,
-                                           const uint8_t *avs, bool valid, float score_scale,
-                                           const QueryRegs<D> &q, const uint4 *lsv, SplitState<D> &s) {
+// One page step of one wave (LPT lanes per token, PPI pages): score this
+// lane's token from the K codes in LDS, fold it into the online softmax, and
+// add every token's V to the matrix accumulators.
+//   ck, mkr, mvr  this lane's reference K code bytes and (scale, zero) of K / V
+//   rk            this lane's residual K code bytes (RB != 0)
+//   mks, mvs      residual (scale, zero); aks, avs residual alphas (RB != 0)
+//   vref, vres    V code blocks of page 0 of the step (page pg at + pg*stride)
+//   wsc           this wave's weight scratch (PPI pages of kWScratch bytes);
+//                 may alias the step's code bytes, which are all read first
+//   lsv           this lane's residual query limbs (registers or LDS)
+template <int D, int RB, bool META_F32, int G, int REFB = 4>
+__device__ __forceinline__ void token_step(const uint8_t *ck, const uint8_t *mkr, const uint8_t *mvr,
+                                           const uint8_t *rk, const uint8_t *mks, const uint8_t *aks,
+                                           const uint8_t *mvs, const uint8_t *avs, const uint8_t *vref,
+                                           const uint8_t *vres, uint8_t *wsc, int lane, bool valid,
+                                           float score_scale, const QueryRegs<D> &q, const uint4 *lsv,
+                                           SplitState<D> &s) {
     using Ln = Lanes<D>;
-    constexpr int LPT = Ln::LPT, CPL = Ln::CPL;
-    constexpr int REF_NB = CPL * REFB / 8;          // first record's code bytes per lane (INT4, or INT2 direct)
-    constexpr int RES_NB = RB ? CPL * RB / 8 : 4;   // residual code bytes per lane
+    constexpr int LPT = Ln::LPT, CPL = Ln::CPL, PPI = Ln::PPI;
+    constexpr int REF_NB = CPL * REFB / 8;          // first record's K code bytes per lane (INT4, or INT2 direct)
+    constexpr int RES_NB = RB ? CPL * RB / 8 : 4;   // residual K code bytes per lane
     constexpr int REF_NW = REF_NB / 4, RES_NW = RES_NB / 4;
+    constexpr int NPG = G / CPL;                    // lanes of one token in one group
+    constexpr int VREF_STRIDE = 16 * D * REFB / 8, VRES_STRIDE = 16 * D * (RB ? RB : 2) / 8;
     using SZ = typename std::conditional<META_F32, float2, uint32_t>::type;
-    uint32_t ckw[REF_NW], cvw[REF_NW], rkw[RES_NW], rvw[RES_NW];
+    const int tok_i = lane / LPT, q4 = lane % LPT;
+    uint32_t ckw[REF_NW], rkw[RES_NW];
     load_bytes<REF_NB>(ck, ckw);
-    load_bytes<REF_NB>(cv, cvw);
+    if constexpr (RB != 0) load_bytes<RES_NB>(rk, rkw);
+    VWords<D, REFB> vw_ref[PPI];
+    VWords<D, RB ? RB : 2> vw_res[PPI];
+#pragma unroll
+    for (int pg = 0; pg < PPI; ++pg) {
+        load_v<D, REFB>(vw_ref[pg], vref + pg * VREF_STRIDE, lane);
+        if constexpr (RB != 0) load_v<D, RB>(vw_res[pg], vres + pg * VRES_STRIDE, lane);
+    }
+    // every code byte of the step is read before the weight scratch (which
+    // may overlap them) is written
+    __asm__ volatile("" ::: "memory");
     float skr, zkr, svr, zvr;
     sz_of(*(const SZ *)mkr, skr, zkr);
     sz_of(*(const SZ *)mvr, svr, zvr);
@@ -452,8 +526,6 @@ __device__ __forceinline__ void token_step(const uint8_t *ck, const uint8_t *cv,
     float part = (skr * (float)dref + zkr * (float)q.qs_ref) * q.sc_ref;
     float av = 1.f, svs = 0.f, zvs = 0.f;
     if constexpr (RB != 0) {
-        load_bytes<RES_NB>(rk, rkw);
-        load_bytes<RES_NB>(rv, rvw);
         float sks, zks;
         sz_of(*(const SZ *)mks, sks, zks);
         sz_of(*(const SZ *)mvs, svs, zvs);
@@ -469,51 +541,78 @@ __device__ __forceinline__ void token_step(const uint8_t *ck, const uint8_t *cv,
         const float mn = fmaxf(s.m, wave_max(score));
         const float f = fast_exp2(s.m - mn);
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) s.accr[i] *= f;
-        if constexpr (RB != 0) {
-#pragma unroll
-            for (int i = 0; i < CPL; ++i) s.accs[i] *= f;
-        }
+        for (int i = 0; i < D / 16; ++i) s.v[i] *= f;
         s.zr *= f; s.zs *= f; s.lsum *= f;
         s.m = mn;
     }
     const float pr = fast_exp2(score - s.m);
     s.lsum += pr;
-    // V: acc_ref += p*alpha*s*c (+ p*alpha*z per group), acc_res in rotated space
+    // weights of this token (group of this lane); the zero terms carry z - 16 s
     const float pa = pr * av;
     const float wr = valid ? pa * svr : 0.f;
-    s.zr += valid ? pa * zvr : 0.f;
-    if constexpr (REFB == 4) axpy_int4<REF_NW>(s.accr, cvw, wr);
-    else axpy_int2<REF_NW>(s.accr, cvw, wr);
-    if constexpr (RB != 0) {
-        const float ws = valid ? pr * svs : 0.f;
-        s.zs += valid ? pr * zvs : 0.f;
-        if constexpr (RB == 2) axpy_int2<RES_NW>(s.accs, rvw, ws);
-        else axpy_int4<RES_NW>(s.accs, rvw, ws);
+    const float ws = valid ? pr * svs : 0.f;
+    const halfx2 hi = {(_Float16)wr, (_Float16)ws};
+    const halfx2 lo = {(_Float16)(wr - (float)hi.x), (_Float16)(ws - (float)hi.y)};
+    const uint32_t hib = __builtin_bit_cast(uint32_t, hi), lob = __builtin_bit_cast(uint32_t, lo);
+    // zero terms: p*alpha*z minus the offset 16 times the weight as the matrix cores see it
+    s.zr += valid ? fmaf(pa, zvr, -16.f * ((float)hi.x + (float)lo.x)) : 0.f;
+    if constexpr (RB != 0) s.zs += valid ? fmaf(pr, zvs, -16.f * ((float)hi.y + (float)lo.y)) : 0.f;
+    // rows 4g + r of this token's column: lane k of the group's NPG lanes writes rows k, k + NPG, ...
+    {
+        const int g = (q4 * CPL) / G, k = q4 % NPG;
+        uint16_t *wrow = (uint16_t *)(wsc + (tok_i >> 4) * kWScratch) + (tok_i & 15);
+#pragma unroll
+        for (int e = 0; e < 4 / NPG; ++e) {
+            const int r = k + NPG * e;
+            if (RB != 0 || r < 2) {
+                const uint32_t pair = (r & 1) ? lob : hib;
+                wrow[(4 * g + r) * 16] = (uint16_t)((r >> 1) ? pair >> 16 : pair);
+            }
+        }
     }
+    // the rows are read back by other lanes of this wave: LDS keeps one wave's
+    // accesses in order; keep the compiler from reordering them
+    __asm__ volatile("" ::: "memory");
+    // A row of this lane: 4g + r with r = lane%4; the reference codes take
+    // rows r < 2, the residual codes rows r >= 2 (unwritten rows are masked)
+    const bool ref_row = (lane & 2) == 0;
+#pragma unroll
+    for (int pg = 0; pg < PPI; ++pg) {
+        const uint2 a2 = *(const uint2 *)(wsc + pg * kWScratch + (lane & 15) * 32 + (lane >> 4) * 8);
+        const uint2 ar = make_uint2(ref_row ? a2.x : 0u, ref_row ? a2.y : 0u);
+        v_mfma<D, REFB>(s.v, vw_ref[pg], ar);
+        if constexpr (RB != 0) {
+            const uint2 as = make_uint2(ref_row ? 0u : a2.x, ref_row ? 0u : a2.y);
+            v_mfma<D, RB>(s.v, vw_res[pg], as);
+        }
+    }
+    __asm__ volatile("" ::: "memory");
 }
 
-// Fold the per-group zero terms into the accumulators and sum them (and the
-// weights) over the wave's token slots; lanes q4 = 0..LPT-1 then hold the
-// wave's totals for their channels.
-template <int D, bool RES>
-__device__ __forceinline__ void reduce_slots(SplitState<D> &s) {
-    constexpr int LPT = Lanes<D>::LPT, CPL = Lanes<D>::CPL;
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) s.accr[i] += s.zr;
-    if constexpr (RES) {
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) s.accs[i] += s.zs;
-    }
+// End of a split: sum the weights and zero terms over the wave's token slots
+// and write (m, l, acc_ref[D], acc_res[D]) of the wave to `out` (acc_res
+// only when RES). Lanes 16g..16g+15 hold rows 4g..4g+3 of the products of the
+// column groups of group g.
+template <int D, bool RES, int G>
+__device__ __forceinline__ void finish_split(SplitState<D> &s, int lane, float *out) {
+    constexpr int LPT = Lanes<D>::LPT, CPL = Lanes<D>::CPL, NPG = G / CPL;
 #pragma unroll
     for (int off = LPT; off < 64; off <<= 1) {
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) s.accr[i] += __shfl_xor(s.accr[i], off, 64);
-        if constexpr (RES) {
-#pragma unroll
-            for (int i = 0; i < CPL; ++i) s.accs[i] += __shfl_xor(s.accs[i], off, 64);
-        }
+        s.zr += __shfl_xor(s.zr, off, 64);
+        if constexpr (RES) s.zs += __shfl_xor(s.zs, off, 64);
         s.lsum += __shfl_xor(s.lsum, off, 64);
+    }
+    // lane q4 = g*NPG (token slot 0) holds group g's zero terms
+    const int gl = lane >> 4, col = lane & 15;
+    const float zr = __shfl(s.zr, gl * NPG, 64);
+    const float zs = RES ? __shfl(s.zs, gl * NPG, 64) : 0.f;
+    if (lane == 0) { out[0] = s.m; out[1] = s.lsum; }
+#pragma unroll
+    for (int m = 0; m < D / 16; ++m) {
+        if (gl == (16 * m) / G) {
+            out[2 + 16 * m + col] = s.v[m][0] + s.v[m][1] + zr;
+            if constexpr (RES) out[2 + D + 16 * m + col] = s.v[m][2] + s.v[m][3] + zs;
+        }
     }
 }
 
@@ -579,6 +678,9 @@ struct StageGeom {
     // fit in the CU's 160 KB of LDS, else two; the end-of-loop merge reuses
     // each wave's own stages
     static constexpr int NST = 3 * kWaves * 3 * BYTES <= 160 * 1024 ? 3 : 2;
+    // the step's weight scratch reuses the start of its own slot (the code
+    // bytes, read into registers first)
+    static_assert(PPI * kWScratch <= O_M, "weight scratch fits in the slot's code bytes");
     static_assert(BYTES % 16 == 0, "stage pieces are 16 bytes");
     static_assert(NST * BYTES >= partial_floats(D) * 4, "a wave's partial fits in its stages");
 };
@@ -590,7 +692,8 @@ struct StageGeom {
 // explicitly (the data never occupies registers while in flight, and no wait
 // is more conservative than the ring needs).
 template <int D, int RB, bool META_F32, int G, int REFB = 4>
-__global__ __launch_bounds__(256) void rq_split_kernel(SplitArgs a) {
+// (at most 128 registers: four waves per SIMD, four workgroups per CU)
+__global__ __launch_bounds__(256, 4) void rq_split_kernel(SplitArgs a) {
     using Ln = Lanes<D>;
     using SG = StageGeom<D, RB, META_F32, G, REFB>;
     constexpr int LPT = Ln::LPT, CPL = Ln::CPL, PPI = Ln::PPI;
@@ -718,25 +821,17 @@ __global__ __launch_bounds__(256) void rq_split_kernel(SplitArgs a) {
             int blk = blk_of(cur, 0);
             if constexpr (PPI == 2) blk = page_in_step ? blk_of(cur, 1) : blk;
             const bool valid = blk >= 0 && pp < p1 && pp * 16 + tok < seq;
-            const uint8_t *S = &stage[wave][cur % NST][0];
-            const uint8_t *C = S + o_ck, *R = S + o_rk, *M = S + SG::O_M + o_mkr, *A = S + SG::O_M + o_aks;
-            token_step<D, RB, META_F32, REFB>(C + SG::O_RK, C + SG::O_RV, M, M + SG::MB, R + SG::O_SK, R + SG::O_SV,
-                                        M + 2 * SG::MB, A + 3 * SG::MB, M + 3 * SG::MB + SG::AB,
-                                        A + 4 * SG::MB + SG::AB, valid, a.score_scale, q, q.lsv, s);
+            uint8_t *S = &stage[wave][cur % NST][0];
+            const uint8_t *M = S + SG::O_M + o_mkr, *A = S + SG::O_M + o_aks;
+            token_step<D, RB, META_F32, G, REFB>(S + SG::O_RK + o_ck, M, M + SG::MB, S + SG::O_SK + o_rk,
+                                                 M + 2 * SG::MB, A + 3 * SG::MB, M + 3 * SG::MB + SG::AB,
+                                                 A + 4 * SG::MB + SG::AB, S + SG::O_RV, S + SG::O_SV, S, lane,
+                                                 valid, a.score_scale, q, q.lsv, s);
         }
     }
 
-    reduce_slots<D, RB != 0>(s);
     // ---- merge the workgroup's 4 wave partials (log-sum-exp), one partial per workgroup
-    if (lane < LPT) {
-        if (lane == 0) { wp(wave)[0] = s.m; wp(wave)[1] = s.lsum; }
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) wp(wave)[2 + q4 * CPL + i] = s.accr[i];
-        if constexpr (RB != 0) {
-#pragma unroll
-            for (int i = 0; i < CPL; ++i) wp(wave)[2 + D + q4 * CPL + i] = s.accs[i];
-        }
-    }
+    finish_split<D, RB != 0, G>(s, lane, wp(wave));
     __syncthreads();
     float M = kNegInf;
 #pragma unroll
@@ -937,12 +1032,10 @@ __global__ __launch_bounds__(64 * kMaxMultiLoops) void rq_multi_kernel(MultiArgs
 
     // this lane's reads inside the stages
     const int o_ck = tok_i * (D / 2) + q4 * REF_NB;
-    const int o_cv = MG::R_CV + o_ck;
     const int o_mkr = MG::R_M + page_in_step * 2 * MG::MB + (tok * NG + g) * 2 * MSZ;
     const int o_mvr = o_mkr + MG::MB;
     const int res_nb = CPL * rb / 8;
     const int o_rk = tok_i * (D * rb / 8) + q4 * res_nb;
-    const int o_rv = PPI * cbr + o_rk;
     const int o_m = 2 * PPI * cbr + page_in_step * MG::smp();
     const int o_mks = o_m + (tok * NG + g) * 2 * MSZ;
     const int o_aks = o_m + MG::MB + tok * MSZ;
@@ -951,6 +1044,8 @@ __global__ __launch_bounds__(64 * kMaxMultiLoops) void rq_multi_kernel(MultiArgs
 
     SplitState<D> s;
     init_state<D>(s);
+    // this wave's weight scratch (after the padding slots)
+    uint8_t *wsc = smem + nst * (ref_stage + nl * res_stage) + 16 * nl + wave * PPI * kWScratch;
 
     auto blk_of = [&](int st, int pg) -> int { return __builtin_amdgcn_readlane(tbl, st * PPI + pg); };
 
@@ -995,29 +1090,20 @@ __global__ __launch_bounds__(64 * kMaxMultiLoops) void rq_multi_kernel(MultiArgs
         const uint8_t *R = ref_base + slot * ref_stage;
         const uint8_t *S = res_base + slot * res_stage;
         if (rb == 2) {
-            token_step<D, 2, META_F32>(R + o_ck, R + o_cv, R + o_mkr, R + o_mvr, S + o_rk, S + o_rv, S + o_mks,
-                                       S + o_aks, S + o_mvs, S + o_avs, valid, a.score_scale, q, q.lsv, s);
+            token_step<D, 2, META_F32, G>(R + o_ck, R + o_mkr, R + o_mvr, S + o_rk, S + o_mks, S + o_aks,
+                                          S + o_mvs, S + o_avs, R + MG::R_CV, S + PPI * MG::cb_res(2), wsc, lane,
+                                          valid, a.score_scale, q, q.lsv, s);
         } else if (RBMAX == 4 && rb == 4) {
-            token_step<D, RBMAX, META_F32>(R + o_ck, R + o_cv, R + o_mkr, R + o_mvr, S + o_rk, S + o_rv,
-                                           S + o_mks, S + o_aks, S + o_mvs, S + o_avs, valid, a.score_scale,
-                                           q, q.lsv, s);
+            token_step<D, RBMAX, META_F32, G>(R + o_ck, R + o_mkr, R + o_mvr, S + o_rk, S + o_mks, S + o_aks,
+                                              S + o_mvs, S + o_avs, R + MG::R_CV, S + PPI * MG::cb_res(RBMAX), wsc,
+                                              lane, valid, a.score_scale, q, q.lsv, s);
         } else {
-            token_step<D, 0, META_F32>(R + o_ck, R + o_cv, R + o_mkr, R + o_mvr, S, S, S, S, S, S, valid,
-                                       a.score_scale, q, q.lsv, s);
+            token_step<D, 0, META_F32, G>(R + o_ck, R + o_mkr, R + o_mvr, S, S, S, S, S, R + MG::R_CV, S, wsc, lane,
+                                          valid, a.score_scale, q, q.lsv, s);
         }
     }
 
-    reduce_slots<D, true>(s);
-    if (lane < LPT) {
-        float *out = a.partials + ((((int64_t)call * a.B + b) * H + h) * a.nsplit + split) * PF;
-        if (lane == 0) { out[0] = s.m; out[1] = s.lsum; }
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) out[2 + q4 * CPL + i] = s.accr[i];
-        if (rb != 0) {
-#pragma unroll
-            for (int i = 0; i < CPL; ++i) out[2 + D + q4 * CPL + i] = s.accs[i];
-        }
-    }
+    finish_split<D, true, G>(s, lane, a.partials + ((((int64_t)call * a.B + b) * H + h) * a.nsplit + split) * PF);
 }
 
 // --------------------------------------------------------------- combine
@@ -1221,13 +1307,18 @@ int multi_slot_bytes(int G, int nl) {
     return ref + nl * res;
 }
 
+// LDS bytes of the multi-loop kernel outside its ring: one 16-byte padding
+// slot and one weight scratch per wave
+template <int D>
+int multi_fixed_bytes(int nl) { return nl * (16 + Lanes<D>::PPI * kWScratch); }
+
 // Ring depth of the multi-loop kernel: as deep as the workgroup's LDS share
 // allows (three workgroups per CU up to 4 waves each, else one 64 KB
 // workgroup), at most 8.
 template <int D, bool MF, int RBMAX>
 int multi_ring_depth(int G, int nl) {
     const int budget = nl <= 4 ? 53 * 1024 : 64 * 1024;
-    return std::min(8, (budget - 16 * nl) / multi_slot_bytes<D, MF, RBMAX>(G, nl));
+    return std::min(8, (budget - multi_fixed_bytes<D>(nl)) / multi_slot_bytes<D, MF, RBMAX>(G, nl));
 }
 
 template <int D>
@@ -1296,7 +1387,7 @@ hipError_t launch_decode_d(const DecodeCall &c) {
                 slot = g4 ? multi_slot_bytes<D, false, 4>(g.G, nl) : multi_slot_bytes<D, false, 2>(g.G, nl);
             }
             if (m.nst < 2) return hipErrorInvalidConfiguration;
-            size_t lds = (size_t)m.nst * slot + 16 * nl;
+            size_t lds = (size_t)m.nst * slot + multi_fixed_bytes<D>(nl);
             const bool last = k == ngroups - 1;
             // the current tokens' encode rides in the last group's launch
             m.enc_x0 = c.nsplit; m.enc_items = 0; m.enc_kvf = kvf ? 1 : 0;

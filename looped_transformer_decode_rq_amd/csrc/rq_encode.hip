@@ -57,7 +57,7 @@ __global__ __launch_bounds__(kThreads) void rq_direct_encode_kernel(EncArgs a) {
             x1 = (double)load_kv<KV_F32>(a.kv, base + c1);
         }
         uint8_t *rec = a.pool + (blk * H + h) * a.slab + a.loop_off[l] + (int64_t)kv * a.rec[l];
-        quantize_row<META_F32>(x0, x1, active, lane, D, a.G, a.bits[l], rec, a.code_bytes[l], off, write);
+        quantize_row<META_F32>(x0, x1, active, lane, D, a.G, a.bits[l], rec, a.code_bytes[l], off, write, kv == 1);
     }
 }
 

@@ -51,12 +51,37 @@ __device__ __forceinline__ void group_minmax(double &lo, double &hi, int span) {
     }
 }
 
+// Place one V code of token offset `off` (0..15) and channel c into a V
+// record's code block (the record format in rq.h): lane 16*(off/4) + c%16,
+// word plane p = (c/16)/W (W = 8/bits column groups per 32-bit word, every
+// earlier plane full: 64 lanes x 4 bytes), field 2*W_p*(v%2) + W_p*(v/2) + i
+// with v = off%4, i = (c/16)%W and W_p the groups in word p (the last word
+// of D = 96 INT2 holds 2 and is a 16-bit unit). Codes of the four tokens of
+// a quad share words, and tokens are written by different waves and
+// launches, so the field is cleared and set with atomic and/or on the
+// aligned 32-bit word (other tokens' bits are untouched).
+__device__ __forceinline__ void put_v_code(uint8_t *rec, int D, int bits, int off, int c, uint32_t code) {
+    const int u = off >> 2, v = off & 3;
+    const int m = c >> 4, j = c & 15;
+    const int lam = 16 * u + j;
+    const int W = 8 / bits, M = D >> 4;
+    const int p = m / W, i = m % W;
+    const int wp = min(W, M - W * p);
+    const int f = 2 * wp * (v & 1) + wp * (v >> 1) + i;
+    const int byte = 256 * p + lam * wp * bits / 2;
+    uint32_t *word = (uint32_t *)(rec + (byte & ~3));
+    const int sh = (byte & 3) * 8 + f * bits;
+    atomicAnd(word, ~(((1u << bits) - 1u) << sh));
+    atomicOr(word, code << sh);
+}
+
 // Quantize the row held by this wave (two channels per lane) and write codes
-// and (scale, zero) into the record at `rec` for token offset `off`.
-// `write` is wave-uniform.
+// and (scale, zero) into the record at `rec` for token offset `off`: K
+// records token-major, V records (vorder) in the column-lane order of
+// put_v_code. `write` and `vorder` are wave-uniform.
 template <bool META_F32>
 __device__ void quantize_row(double y0, double y1, bool active, int lane, int D, int G, int bits,
-                             uint8_t *rec, int code_bytes, int off, bool write) {
+                             uint8_t *rec, int code_bytes, int off, bool write, bool vorder) {
     const int span = (G == D) ? 64 : G / 2;
     double lo = active ? fmin(y0, y1) : __builtin_inf();
     double hi = active ? fmax(y0, y1) : -__builtin_inf();
@@ -69,8 +94,14 @@ __device__ void quantize_row(double y0, double y1, bool active, int lane, int D,
         c0 = (uint32_t)fmin(fmax(rint((y0 - z) / s), 0.0), (double)qmax);
         c1 = (uint32_t)fmin(fmax(rint((y1 - z) / s), 0.0), (double)qmax);
     }
-    // pack: each lane contributes its two codes; OR-reduce inside the lanes
-    // that share one 32-bit word (4 lanes for INT4, 8 lanes for INT2)
+    if (vorder) {
+        if (write && active) {
+            put_v_code(rec, D, bits, off, 2 * lane, c0);
+            put_v_code(rec, D, bits, off, 2 * lane + 1, c1);
+        }
+    }
+    // pack (K records): each lane contributes its two codes; OR-reduce inside
+    // the lanes that share one 32-bit word (4 lanes for INT4, 8 lanes for INT2)
     uint32_t word;
     int lanes_per_word;
     if (bits == 4) {
@@ -83,7 +114,7 @@ __device__ void quantize_row(double y0, double y1, bool active, int lane, int D,
     for (int off2 = 1; off2 < lanes_per_word; off2 <<= 1) word |= __shfl_xor(word, off2, 64);
     if (!write) return;
     const int row_bytes = D * bits / 8;
-    if ((lane % lanes_per_word) == 0 && active) {
+    if (!vorder && (lane % lanes_per_word) == 0 && active) {
         const int w = lane / lanes_per_word;
         *(uint32_t *)(rec + (int64_t)off * row_bytes + 4 * w) = word;
     }
@@ -141,7 +172,8 @@ __device__ void encode_item(const EncArgs &a, int tile, int h, int z, uint8_t *l
         const double sq = wave_sum_f64(x0 * x0 + x1 * x1);
         if (lane == 0) refsq[t] = sq;
         uint8_t *rec = a.pool + (blk * H + h) * a.slab + a.loop_off[L - 1] + (int64_t)kv * a.rec[L - 1];
-        quantize_row<META_F32>(x0, x1, active, lane, D, a.G, 4, rec, a.code_bytes[L - 1], off, write && l == 0);
+        quantize_row<META_F32>(x0, x1, active, lane, D, a.G, 4, rec, a.code_bytes[L - 1], off, write && l == 0,
+                               kv == 1);
     }
     __syncthreads();
 
@@ -214,7 +246,8 @@ __device__ void encode_item(const EncArgs &a, int tile, int h, int z, uint8_t *l
             const double y0 = rows[t * kRowStride + c0];
             const double y1 = active ? rows[t * kRowStride + c1] : 0.0;
             uint8_t *rec = a.pool + (blk * H + h) * a.slab + a.loop_off[l] + (int64_t)kv * a.rec[l];
-            quantize_row<META_F32>(y0, y1, active, lane, D, a.G, a.bits[l], rec, a.code_bytes[l], off, write);
+            quantize_row<META_F32>(y0, y1, active, lane, D, a.G, a.bits[l], rec, a.code_bytes[l], off, write,
+                                   kv == 1);
             if (write && lane == 0)
                 store_meta<META_F32>(rec + a.code_bytes[l] + a.meta_bytes + (int64_t)off * msz, alph[t]);
         }
