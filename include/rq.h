@@ -271,8 +271,10 @@ rq_status rq_fit_rotation(const float *samples, int64_t n, int32_t head_dim, int
 size_t rq_bf16_workspace_bytes(int32_t num_heads, int32_t head_dim, int32_t batch,
                                int32_t max_blocks_per_seq, int32_t split_pages);
 
-/* Pages per split of the bf16 baseline when split_pages is 0: the per-loop
- * rule of rq_decode_auto_split_pages. Returns 0 for invalid arguments. */
+/* Pages per split of the bf16 baseline when split_pages is 0. Its split
+ * kernel writes one partial per split, so it takes the multi-loop rule of
+ * rq_decode_auto_split_pages (about 14 rounds of one-split units). Returns 0
+ * for invalid arguments. */
 int32_t rq_bf16_auto_split_pages(int32_t num_heads, int32_t batch,
                                  int32_t max_blocks_per_seq);
 

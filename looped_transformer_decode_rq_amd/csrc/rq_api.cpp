@@ -65,16 +65,18 @@ static int device_cus() {
     return n;
 }
 
-int auto_split_pages(int units, int max_blocks, bool multi) {
+int auto_split_pages(int units, int max_blocks, bool per_split) {
     // A split-K launch runs in rounds of resident workgroups (about three per
     // CU for these kernels); the last round is partly empty. Enough
-    // workgroups for ~8 rounds (one split per 4-wave workgroup per loop) or
-    // ~14 rounds (multi-loop: one split per workgroup, each reading a page
-    // once for all its loops) keep that tail small without shrinking the
-    // splits to where per-split setup and partials dominate. The pages are
-    // then spread evenly over the splits of a row.
-    const int waves = multi ? 1 : kSplitWaves;
-    const int64_t target = (int64_t)(multi ? 14 : 8) * 3 * device_cus();
+    // workgroups for ~8 rounds (per-loop packed calls: four splits per
+    // workgroup, merged into one partial) or ~14 rounds of one-split units
+    // (one partial per split: the multi-loop kernel, whose workgroup reads a
+    // page once for all its loops, and the bf16 baseline) keep that tail
+    // small without shrinking the splits to where per-split setup and the
+    // partials' merge dominate. The pages are then spread evenly over the
+    // splits of a row.
+    const int waves = per_split ? 1 : kSplitWaves;
+    const int64_t target = (int64_t)(per_split ? 14 : 8) * 3 * device_cus();
     const int64_t wg_per_unit = std::max<int64_t>(1, (target + units - 1) / std::max(units, 1));
     int64_t sp = ((int64_t)max_blocks + waves * wg_per_unit - 1) / (waves * wg_per_unit);
     sp = std::min<int64_t>(kMaxSplitPages, std::max<int64_t>(kMinAutoSplitPages, sp));
@@ -183,7 +185,7 @@ int32_t rq_decode_auto_split_pages(const rq_layout *layout, int32_t n_loops, int
 
 int32_t rq_bf16_auto_split_pages(int32_t num_heads, int32_t batch, int32_t max_blocks_per_seq) {
     if (num_heads < 1 || batch < 1 || max_blocks_per_seq < 1) return 0;
-    return auto_split_pages(batch * num_heads, max_blocks_per_seq, false);
+    return auto_split_pages(batch * num_heads, max_blocks_per_seq, true);
 }
 
 static rq_status decode_impl(const rq_layout *layout, const void *pool, const int32_t *loops, int32_t n_loops,
@@ -276,7 +278,7 @@ size_t rq_bf16_workspace_bytes(int32_t num_heads, int32_t head_dim, int32_t batc
                                int32_t split_pages) {
     if (num_heads < 1 || batch < 0 || max_blocks_per_seq < 1 || split_pages < 0) return 0;
     if (head_dim != 64 && head_dim != 96 && head_dim != 128) return 0;
-    const int sp = split_pages > 0 ? split_pages : auto_split_pages(batch * num_heads, max_blocks_per_seq, false);
+    const int sp = split_pages > 0 ? split_pages : auto_split_pages(batch * num_heads, max_blocks_per_seq, true);
     return bf16_ws(num_heads, head_dim, batch, max_blocks_per_seq, sp);
 }
 
@@ -297,7 +299,7 @@ rq_status rq_bf16_decode_attention_ex(int32_t num_heads, int32_t head_dim, int32
     if (!k_cache || !v_cache || !q || !block_table || !seq_lens || !out) return RQ_ERR_NULL;
     if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(q, 16)) return RQ_ERR_SHAPE;
     if ((int64_t)max_blocks_per_seq * 16 > (int64_t)1 << 30) return RQ_ERR_SHAPE;
-    const int sp = sp_req > 0 ? sp_req : auto_split_pages(batch * num_heads, max_blocks_per_seq, false);
+    const int sp = sp_req > 0 ? sp_req : auto_split_pages(batch * num_heads, max_blocks_per_seq, true);
     if (!workspace) return RQ_ERR_NULL;
     if (workspace_bytes < bf16_ws(num_heads, head_dim, batch, max_blocks_per_seq, sp)) return RQ_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return RQ_ERR_SHAPE;

@@ -31,9 +31,9 @@ __host__ __device__ constexpr int qpack_bytes(int D) { return 64 + 4 * D; }
 __host__ __device__ constexpr int partial_floats(int D) { return 2 + 2 * D; }
 
 // Pages per split chosen when the caller passes 0: sized so that a launch
-// has several rounds of resident workgroups (units = sequences x heads,
-// multi = one split per workgroup for several loop calls at once).
-int auto_split_pages(int units, int max_blocks, bool multi);
+// has several rounds of resident workgroups (units = sequences x heads;
+// per_split = one partial per split: multi-loop calls and the bf16 baseline).
+int auto_split_pages(int units, int max_blocks, bool per_split);
 
 constexpr int kSplitWaves = 4;     // waves (splits) per split-K workgroup
 constexpr int kMaxSplitPages = 64; // pages per split: one block-table entry per lane
