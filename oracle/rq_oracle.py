@@ -33,6 +33,11 @@ R19 storage order of V codes inside a page record (the pages fix no storage
     that column's codes of the quad's four tokens for every column group,
     split into 32-bit words and stored word-plane by word-plane (see
     v_code_bits). K codes stay token-major (pack_codes per token).
+R20 chunked prefill over the packed cache (the serving setting the pages
+    describe; they give no kernel-level definition): a chunk of C new tokens
+    per sequence, for one loop, attends all cached (packed) tokens of that
+    loop plus the chunk's own uncompressed K/V causally (query i sees chunk
+    tokens 0..i); softmax scale as in R12.
 R17 the direct per-loop baseline (the "quantize every loop on its own"
     approach the pages compare against): loop l's K/V quantized with the
     quantizer of R6-R10 at its own bit width, no reference, no alpha, no
@@ -48,7 +53,7 @@ __all__ = [
     "meta_round", "ls_alpha", "Quantized", "quantize", "dequantize",
     "Encoded", "encode", "reconstruct", "pack_codes", "unpack_codes",
     "v_code_bits", "PoolLayout", "write_tokens", "read_pages", "gather_sequence",
-    "reconstruct_sequence", "attention", "decode_attention",
+    "reconstruct_sequence", "attention", "decode_attention", "chunk_attention",
     "bf16_pool_write", "bf16_decode_attention", "DirectEncoded", "encode_direct",
     "rotation_quant_error", "procrustes", "fit_rotation",
 ]
@@ -497,6 +502,37 @@ def decode_attention(pool, lay: PoolLayout, l: int, q, rot32, table, seq_lens, t
         tk = None if tail_k is None else tail_k[b, h]
         tv = None if tail_v is None else tail_v[b, h]
         out[b, h] = attention(q[b, h], K, V, tau, tk, tv)
+    return out
+
+
+def chunk_attention(pool, lay: PoolLayout, l: int, q, rot32, table, seq_lens, tau,
+                    chunk_k=None, chunk_v=None, pairs=None) -> np.ndarray:
+    """Attention of a chunk of C queries per sequence over loop l's packed
+    cache and, causally, over the chunk itself; [B][C][H][D] float64 (reading
+    R20).
+
+    q [B][C][H][D]; chunk_k/chunk_v [B][C][H][D] (the chunk's own K/V of loop
+    l, uncompressed) or None. Query i of sequence b attends the seq_lens[b]
+    reconstructed cached tokens and chunk tokens 0..i, each key once, with
+    plain softmax (same brute force as ``attention``). The serving context of
+    the rit.work summary (a prefill chunk reading the compressed cache) gives
+    the setting; with C = 1 this is decode attention with the chunk token as
+    the uncompressed current token.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, C, H, D = q.shape
+    out = np.full((B, C, H, D), np.nan)
+    todo = pairs if pairs is not None else [(b, h) for b in range(B) for h in range(H)]
+    for b, h in todo:
+        n = int(seq_lens[b])
+        K, V = reconstruct_sequence(pool, lay, table[b], n, h, l, None if rot32 is None else rot32[h])
+        for i in range(C):
+            if chunk_k is not None:
+                Kc = np.concatenate([K, np.asarray(chunk_k[b, : i + 1, h], dtype=np.float64)], axis=0)
+                Vc = np.concatenate([V, np.asarray(chunk_v[b, : i + 1, h], dtype=np.float64)], axis=0)
+            else:
+                Kc, Vc = K, V
+            out[b, i, h] = attention(q[b, i, h], Kc, Vc, tau)
     return out
 
 

@@ -440,3 +440,75 @@ def test_fit_rotation_orthogonal_and_never_worse():
     err = O.rotation_quant_error(samples, R, 2, D, "f16")
     assert err == min(hist) and err <= hist[0]
     assert err < hist[0]
+
+
+# ----------------------------------------------------------- chunked prefill
+def test_chunk_attention_against_library_masked_softmax():
+    """Chunked attention over the packed cache equals torch's scaled-dot-
+    product attention (fp64, CPU) with an explicit mask: every cached token
+    visible, chunk tokens causally (query i sees chunk tokens 0..i)."""
+    import torch
+    w = W.get(1).replace(batch=2, heads=2, context=37)
+    st = W.structure(w)
+    kv = W.kv_numpy(w, st=st)                                 # [L][2][B][N+1][H][D]
+    L, _, B, N1, H, D = kv.shape
+    N = N1 - 1
+    table, nblk = W.block_table(w, shuffled=True)
+    lay = O.PoolLayout(H, D, w.group_size, L, w.res_bits, w.meta_dtype, nblk)
+    pool = np.zeros(lay.pool_bytes, np.uint8)
+    pos = np.tile(np.arange(N), (B, 1))
+    slots = W.slot_mapping(table, pos).reshape(-1)
+    enc = O.encode(kv[:, :, :, :N].reshape(L, 2, B * N, H, D), st["rot32"], w.res_bits, w.group_size, w.meta_dtype)
+    O.write_tokens(pool, lay, enc, slots)
+    rng = np.random.default_rng(5)
+    C = 5
+    q = rng.normal(size=(B, C, H, D)) / np.sqrt(D)
+    ck = rng.normal(size=(B, C, H, D))
+    cv = rng.normal(size=(B, C, H, D))
+    seq = [N, 11]
+    tau = 1 / np.sqrt(D)
+    for l in (0, L - 1):
+        got = O.chunk_attention(pool, lay, l, q, st["rot32"], table, seq, tau, ck, cv)
+        for b in range(B):
+            for h in range(H):
+                K, V = O.reconstruct_sequence(pool, lay, table[b], seq[b], h, l, st["rot32"][h])
+                Kall = torch.from_numpy(np.concatenate([K, ck[b, :, h]]))
+                Vall = torch.from_numpy(np.concatenate([V, cv[b, :, h]]))
+                n = seq[b]
+                mask = torch.zeros((C, n + C), dtype=torch.bool)
+                mask[:, :n] = True
+                mask[:, n:] = torch.tril(torch.ones((C, C), dtype=torch.bool))
+                want = torch.nn.functional.scaled_dot_product_attention(
+                    torch.from_numpy(q[b, :, h])[None], Kall[None], Vall[None], attn_mask=mask[None], scale=tau)[0]
+                np.testing.assert_allclose(got[b, :, h], want.numpy(), rtol=0, atol=1e-12)
+
+
+def test_chunk_attention_special_cases():
+    """C = 1 is decode attention with the chunk token as the current token;
+    with nothing cached, the first query returns the first chunk value
+    exactly and the last query sees every chunk token."""
+    w = W.get(0)
+    st = W.structure(w)
+    kv = W.kv_numpy(w, st=st)
+    L, _, B, N1, H, D = kv.shape
+    N = N1 - 1
+    table, nblk = W.block_table(w)
+    lay = O.PoolLayout(H, D, w.group_size, L, w.res_bits, w.meta_dtype, nblk)
+    pool = np.zeros(lay.pool_bytes, np.uint8)
+    enc = O.encode(kv[:, :, 0, :N], st["rot32"], w.res_bits, w.group_size, w.meta_dtype)
+    O.write_tokens(pool, lay, enc, np.arange(N))
+    q = W.queries_numpy(w)                                      # [L][B][H][D]
+    tau = 1 / np.sqrt(D)
+    for l in range(L):
+        want = O.decode_attention(pool, lay, l, q[l], st["rot32"], table, [N], tau, kv[l, 0, :, N], kv[l, 1, :, N])
+        got = O.chunk_attention(pool, lay, l, q[l][:, None], st["rot32"], table, [N], tau,
+                                kv[l, 0, :, N][:, None], kv[l, 1, :, N][:, None])
+        np.testing.assert_array_equal(got[:, 0], want)
+    rng = np.random.default_rng(2)
+    C = 4
+    qc, ck, cv = (rng.normal(size=(1, C, H, D)) for _ in range(3))
+    got = O.chunk_attention(pool, lay, 0, qc, st["rot32"], table, [0], tau, ck, cv)
+    np.testing.assert_array_equal(got[0, 0, 0], cv[0, 0, 0])
+    s = tau * ck[0, :, 0] @ qc[0, C - 1, 0]
+    p = np.exp(s - s.max())
+    np.testing.assert_allclose(got[0, C - 1, 0], p @ cv[0, :, 0] / p.sum(), rtol=0, atol=1e-14)
