@@ -303,7 +303,7 @@ def traffic_from_profiles(kernel_src_hash):
 def kernel_src_hash():
     import hashlib
     h = hashlib.sha256()
-    for f in ("rq_decode.hip", "rq_device.h", "rq_internal.h"):
+    for f in ("rq_decode.hip", "rq_device.h", "rq_internal.h", "rq_vmfma.h"):
         h.update(open(os.path.join(ROOT, "looped_transformer_decode_rq_amd", "csrc", f), "rb").read())
     return h.hexdigest()
 

@@ -263,6 +263,38 @@ rq_status rq_fit_rotation(const float *samples, int64_t n, int32_t head_dim, int
                           int32_t group_size, int32_t meta_dtype, const float *rot0, int32_t iters,
                           float *rot_out, double *objective);
 
+/* Chunked prefill over the packed cache: a chunk of `chunk` new tokens per
+ * sequence, for one loop, attends every cached token of that loop and,
+ * causally, the chunk's own uncompressed K/V (query i sees chunk tokens
+ * 0..i). This is the serving setting in which a prefill chunk reads the
+ * compressed cache (rit.work summary, section on the infrastructure plan;
+ * arXiv 2610.10381 abstract on reduced KV traffic). The queries of a chunk
+ * share every page read, and both products run on the matrix cores.
+ *   loop          loop index in [0, L); loop L-1 attends the reference alone
+ *   chunk         queries per sequence, 1..256 (RQ_ERR_UNSUPPORTED above)
+ *   q             [B][chunk][H][D] bf16
+ *   rot           as in rq_decode_attention (may be NULL for the reference loop)
+ *   block_table, seq_lens, batch, max_blocks_per_seq: as in rq_decode_attention;
+ *                 seq_lens[b] counts the cached tokens, without the chunk
+ *   chunk_k/v     [B][chunk][H][D] bf16: the chunk's own K/V of this loop, or
+ *                 both NULL (then only the cache is attended)
+ *   out           [B][chunk][H][D] fp32
+ * Supported layouts: RQ_MODE_RESIDUAL, group_size == head_dim, kv_dtype bf16;
+ * others return RQ_ERR_UNSUPPORTED. opts: split_pages (any size >= 1; 0 = the
+ * library's choice) and timing events bracketing the split kernel.
+ * q, chunk_k, chunk_v and the workspace must be 16-byte aligned. */
+size_t rq_chunk_workspace_bytes(const rq_layout *layout, int32_t chunk, int32_t batch,
+                                int32_t max_blocks_per_seq, int32_t split_pages);
+
+rq_status rq_chunk_attention(const rq_layout *layout, const void *pool, int32_t loop,
+                             int32_t chunk, const void *q, const float *rot,
+                             const int32_t *block_table, const int32_t *seq_lens,
+                             int32_t batch, int32_t max_blocks_per_seq,
+                             const void *chunk_k, const void *chunk_v,
+                             float softmax_scale, float *out, void *workspace,
+                             size_t workspace_bytes, const rq_decode_opts *opts,
+                             void *stream);
+
 /* Uncompressed baseline (for the speed ratio): the same decode attention over
  * a paged bf16 cache of ONE loop.
  *   k_cache, v_cache  [num_blocks][H][16][D] bf16

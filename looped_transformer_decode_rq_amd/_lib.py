@@ -23,6 +23,7 @@ EXPORTED = [
     "rq_encode_pack", "rq_decode_workspace_bytes", "rq_decode_auto_split_pages", "rq_decode_attention",
     "rq_decode_attention_ex", "rq_decode_attention_encode", "rq_fit_rotation", "rq_bf16_workspace_bytes",
     "rq_bf16_auto_split_pages", "rq_bf16_decode_attention", "rq_bf16_decode_attention_ex", "rq_bf16_write",
+    "rq_chunk_workspace_bytes", "rq_chunk_attention",
 ]
 
 
@@ -72,6 +73,9 @@ def lib():
             "rq_decode_attention_encode": (c_int32, [POINTER(RqLayout), P, P, c_int32, P, P, P, P, c_int32, c_int32,
                                                      P, P, c_float, P, P, c_size_t, P, P, c_int32,
                                                      POINTER(RqDecodeOpts), P]),
+            "rq_chunk_workspace_bytes": (c_size_t, [POINTER(RqLayout), c_int32, c_int32, c_int32, c_int32]),
+            "rq_chunk_attention": (c_int32, [POINTER(RqLayout), P, c_int32, c_int32, P, P, P, P, c_int32, c_int32,
+                                             P, P, c_float, P, P, c_size_t, POINTER(RqDecodeOpts), P]),
             "rq_fit_rotation": (c_int32, [P, c_int64, c_int32, c_int32, c_int32, c_int32, P, c_int32, P, P]),
             "rq_bf16_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32]),
             "rq_bf16_auto_split_pages": (c_int32, [c_int32, c_int32, c_int32]),
@@ -247,6 +251,36 @@ def decode_attention(layout, pool, loops, q, rot, block_table, seq_lens, tail_k,
 
 def bf16_workspace_bytes(num_heads, head_dim, batch, max_blocks_per_seq, split_pages=0) -> int:
     return lib().rq_bf16_workspace_bytes(num_heads, head_dim, batch, max_blocks_per_seq, split_pages)
+
+
+def chunk_workspace_bytes(layout, chunk, batch, max_blocks_per_seq, split_pages=0) -> int:
+    return lib().rq_chunk_workspace_bytes(ctypes.byref(layout), chunk, batch, max_blocks_per_seq, split_pages)
+
+
+def chunk_attention(layout, pool, loop, q, rot, block_table, seq_lens, chunk_k, chunk_v, softmax_scale, out,
+                    workspace, split_pages=0, events=None, stream=None):
+    """rq_chunk_attention: q, chunk_k, chunk_v [B][C][H][D] bf16 (chunk K/V may
+    both be None), out [B][C][H][D] fp32."""
+    B, C, H, D = (int(x) for x in q.shape)
+    _need(H == layout.num_heads and D == layout.head_dim and q.element_size() == 2 and q.is_contiguous(),
+          "q must be contiguous bf16 [B][C][H][D]")
+    _need(tuple(out.shape) == (B, C, H, D) and out.element_size() == 4 and out.is_contiguous(), "out must be fp32 [B][C][H][D]")
+    _need(int(block_table.shape[0]) == B and block_table.element_size() == 4 and block_table.is_contiguous(),
+          "block_table must be int32 [B][M]")
+    _need(seq_lens.numel() == B and seq_lens.element_size() == 4, "seq_lens must be int32 [B]")
+    _need((chunk_k is None) == (chunk_v is None), "chunk_k and chunk_v go together")
+    for t in (chunk_k, chunk_v):
+        if t is not None:
+            _need(tuple(t.shape) == (B, C, H, D) and t.element_size() == 2 and t.is_contiguous(),
+                  "chunk K/V must be contiguous bf16 [B][C][H][D]")
+    _need(_nbytes(pool) >= pool_bytes(layout) > 0, "pool smaller than rq_pool_bytes(layout)")
+    if int(loop) != layout.num_loops - 1:
+        _check_rot(layout, rot)
+    o = _opts(split_pages, events)
+    _check("rq_chunk_attention", lib().rq_chunk_attention(
+        ctypes.byref(layout), _ptr(pool), int(loop), C, _ptr(q), _ptr(rot), _ptr(block_table), _ptr(seq_lens), B,
+        int(block_table.shape[1]), _ptr(chunk_k), _ptr(chunk_v), float(softmax_scale), _ptr(out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), ctypes.byref(o), _stream(stream)))
 
 
 def bf16_auto_split_pages(num_heads, batch, max_blocks_per_seq) -> int:

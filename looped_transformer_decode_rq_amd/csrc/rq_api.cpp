@@ -103,6 +103,22 @@ static size_t decode_ws(const Geom &g, int n, int B, int max_blocks, int sp) {
     return qp + parts;
 }
 
+// Chunked prefill: each workgroup carries 64 queries over a long run of pages
+// (compute-heavy), so the launch aims for about two rounds of workgroups at
+// two per CU; a split is any number of pages.
+static int chunk_split_pages(int B, int H, int C, int max_blocks) {
+    const int64_t units = (int64_t)B * H * ((C + 63) / 64);
+    const int64_t target = 4LL * device_cus();
+    const int64_t ns = std::max<int64_t>(1, std::min<int64_t>(max_blocks, (target + units - 1) / std::max<int64_t>(units, 1)));
+    return (int)((max_blocks + ns - 1) / ns);
+}
+
+static size_t chunk_ws(const Geom &g, int B, int C, int max_blocks, int sp) {
+    const int64_t rows = (int64_t)B * C * g.H;
+    return round_up((size_t)rows * chunk_qrec_bytes(g.D), 256) +
+           (size_t)rows * nsplit_of(max_blocks, sp) * partial_floats(g.D) * sizeof(float);
+}
+
 static size_t bf16_ws(int H, int D, int B, int max_blocks, int sp) {
     return (size_t)B * H * nsplit_of(max_blocks, sp) * (2 + D) * sizeof(float);
 }
@@ -272,6 +288,61 @@ rq_status rq_decode_attention(const rq_layout *layout, const void *pool, const i
     return rq_decode_attention_ex(layout, pool, loops, n_loops, q, rot, block_table, seq_lens, batch,
                                   max_blocks_per_seq, tail_k, tail_v, softmax_scale, out, workspace,
                                   workspace_bytes, nullptr, stream);
+}
+
+// Layouts the chunked-prefill kernels support (RQ_OK) or the reason.
+static rq_status chunk_supported(const Geom &g) {
+    if (g.direct || g.G != g.D || g.kvdt != RQ_DTYPE_BF16) return RQ_ERR_UNSUPPORTED;
+    return RQ_OK;
+}
+
+size_t rq_chunk_workspace_bytes(const rq_layout *layout, int32_t chunk, int32_t batch, int32_t max_blocks_per_seq,
+                                int32_t split_pages) {
+    Geom g;
+    if (make_geom(layout, &g) != RQ_OK || chunk_supported(g) != RQ_OK || chunk < 1 || chunk > kMaxChunk ||
+        batch < 0 || max_blocks_per_seq < 1 || split_pages < 0)
+        return 0;
+    const int sp = split_pages > 0 ? split_pages : chunk_split_pages(batch, g.H, chunk, max_blocks_per_seq);
+    return chunk_ws(g, batch, chunk, max_blocks_per_seq, sp);
+}
+
+rq_status rq_chunk_attention(const rq_layout *layout, const void *pool, int32_t loop, int32_t chunk, const void *q,
+                             const float *rot, const int32_t *block_table, const int32_t *seq_lens, int32_t batch,
+                             int32_t max_blocks_per_seq, const void *chunk_k, const void *chunk_v,
+                             float softmax_scale, float *out, void *workspace, size_t workspace_bytes,
+                             const rq_decode_opts *opts, void *stream) {
+    Geom g;
+    rq_status st = make_geom(layout, &g);
+    if (st != RQ_OK) return st;
+    st = chunk_supported(g);
+    if (st != RQ_OK) return st;
+    if (loop < 0 || loop >= g.L || chunk < 1 || batch < 0 || batch > 65535 || max_blocks_per_seq < 1)
+        return RQ_ERR_SHAPE;
+    if (chunk > kMaxChunk) return RQ_ERR_UNSUPPORTED;
+    if (!isfinite(softmax_scale)) return RQ_ERR_SHAPE;
+    if ((chunk_k == nullptr) != (chunk_v == nullptr)) return RQ_ERR_NULL;
+    const int sp_req = opts ? opts->split_pages : 0;
+    if (sp_req < 0) return RQ_ERR_SHAPE;
+    if (batch == 0) return RQ_OK;
+    if (!pool || !q || !block_table || !seq_lens || !out || (loop != g.L - 1 && !rot)) return RQ_ERR_NULL;
+    if (!aligned(pool, 16) || !aligned(q, 16) || (chunk_k && (!aligned(chunk_k, 16) || !aligned(chunk_v, 16))))
+        return RQ_ERR_SHAPE;
+    if ((int64_t)max_blocks_per_seq * 16 > (int64_t)1 << 30) return RQ_ERR_SHAPE;
+    const int sp = sp_req > 0 ? sp_req : chunk_split_pages(batch, g.H, chunk, max_blocks_per_seq);
+    if (!workspace) return RQ_ERR_NULL;
+    if (workspace_bytes < chunk_ws(g, batch, chunk, max_blocks_per_seq, sp)) return RQ_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return RQ_ERR_SHAPE;
+    ChunkCall c;
+    c.g = &g; c.pool = (const uint8_t *)pool; c.loop = loop; c.B = batch; c.C = chunk;
+    c.max_blocks = max_blocks_per_seq; c.q = q; c.rot = rot; c.block_table = block_table; c.seq_lens = seq_lens;
+    c.chunk_k = chunk_k; c.chunk_v = chunk_v; c.softmax_scale = softmax_scale; c.out = out;
+    c.qrec = (uint8_t *)workspace;
+    c.partials = (float *)((uint8_t *)workspace + round_up((size_t)batch * chunk * g.H * chunk_qrec_bytes(g.D), 256));
+    c.split_pages = sp; c.nsplit = nsplit_of(max_blocks_per_seq, sp);
+    c.ev_begin = opts ? (hipEvent_t)opts->event_main_begin : nullptr;
+    c.ev_end = opts ? (hipEvent_t)opts->event_main_end : nullptr;
+    c.stream = (hipStream_t)stream;
+    return launch_chunk(c) == hipSuccess ? RQ_OK : RQ_ERR_HIP;
 }
 
 size_t rq_bf16_workspace_bytes(int32_t num_heads, int32_t head_dim, int32_t batch, int32_t max_blocks_per_seq,

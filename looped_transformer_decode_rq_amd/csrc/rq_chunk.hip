@@ -1,0 +1,616 @@
+// Chunked prefill attention over the packed, paged ResidualQuant cache.
+//
+// A chunk of C new tokens per sequence, for one loop, attends every cached
+// token of that loop (reconstructed from the INT4 reference and the loop's
+// rotated residual, arXiv 2610.10381 abstract; rit.work summary, section on
+// how each pass is restored: reference and differences rebuilt inside
+// attention, nothing decompressed written back) and, causally, the chunk's own
+// uncompressed K/V (query i sees chunk tokens 0..i).
+//
+// Unlike decode, sixteen queries share every page, so both products run on
+// the matrix cores (v_mfma_f32_16x16x16 with tokens as the 16 rows of one
+// operand):
+//   scores^T = Kcodes x Q: A = K codes of 16 tokens as bf16 (16 + c) (K
+//     records are token-major: a lane's 4 codes of one k-step are 16
+//     contiguous bits), B = the 16 bf16 queries (or the hi/lo bf16 terms of
+//     q' = R_K q for the residual); the output leaves each lane with four
+//     tokens of one query, which is exactly the A operand of the next
+//     product, so no transpose is needed;
+//   out = P x Vcodes: A = fp16 hi/lo of p * alpha * s (reference) and p * s
+//     (residual), B = the V codes in their stored operand order.
+// Per token and group: q . k_hat = alpha * (s * sum q (16 + c) + (z - 16 s) *
+// sum q) + (s_r * sum q' (16 + c_r) + (z_r - 16 s_r) * sum q'), one group per
+// token-head (group_size == head_dim).
+//
+// Three kernels per call:
+//   rq_chunk_qprep    per (head, 16 query rows): sum q; for a residual loop
+//                     q' = R_K q on the f32 matrix cores, split into bf16 hi/lo
+//   rq_chunk_split    per (head, split of pages, sequence x 64 queries): four
+//                     waves of 16 queries walk the split's pages, online
+//                     softmax per query, one partial per (split, query)
+//   rq_chunk_combine  per (head, 16 query rows): merge the partials, the
+//                     chunk's causal part in bf16, out = acc_ref/l + R_V^T
+//                     acc_res/l on the f32 matrix cores
+#include <hip/hip_ext.h>
+
+#include "rq_device.h"
+#include "rq_internal.h"
+#include "rq_vmfma.h"
+
+namespace rq {
+namespace {
+
+constexpr float kLog2eC = 1.4426950408889634f;
+constexpr float kThreshC = 8.0f;         // rescale when a score beats the running max by 2^8
+
+// bf16 round-to-nearest-even of a float, as its bits
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+    const bf16x2 v = {(__bf16)x, (__bf16)0.f};
+    return __builtin_bit_cast(uint32_t, v) & 0xFFFFu;
+}
+
+// ------------------------------------------------------------------ qprep
+struct ChunkPrepArgs {
+    const uint16_t *q;      // [R][H][D] bf16, R = B*C rows
+    const float *rot;       // [H][2][D][D]
+    uint8_t *qrec;          // [R][H][chunk_qrec_bytes]
+    int R, H, res;
+};
+
+// One workgroup per (head, 16 rows); one wave per row.
+template <int D>
+__global__ __launch_bounds__(1024) void rq_chunk_qprep_kernel(ChunkPrepArgs a) {
+    constexpr int QS = D + 1;
+    __shared__ float Q[16 * QS];
+    __shared__ float QR[16 * QS];
+    const int lane = threadIdx.x & 63, r = threadIdx.x >> 6;
+    const int h = blockIdx.x, tile = blockIdx.y;
+    const int row = tile * 16 + r;
+    const bool row_ok = row < a.R;
+    const bool rot_wave = a.res && r < D / 16;
+    const int n = r * 16 + (lane & 15);
+    float rk[D / 4];
+    if (rot_wave) {
+        const float *RK = a.rot + ((int64_t)h * 2 + 0) * D * D + (int64_t)n * D + (lane >> 4);
+#pragma unroll
+        for (int kk = 0; kk < D / 4; ++kk) rk[kk] = RK[4 * kk];
+    }
+    for (int c = lane; c < D; c += 64)
+        Q[r * QS + c] = row_ok ? bf16_to_f32(a.q[((int64_t)row * a.H + h) * D + c]) : 0.0f;
+    __syncthreads();
+    if (rot_wave) {
+        // q' = R_K q for the 16 rows: [16 x D] x R_K^T; v_mfma_f32_16x16x4f32:
+        // lane l supplies A[l%16][k0 + l/16], B[k0 + l/16][l%16], receives
+        // D[4*(l/16)+v][l%16]; wave r computes columns 16r..16r+15
+        floatx4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < D / 4; ++kk) {
+            const int k = 4 * kk + (lane >> 4);
+            c = __builtin_amdgcn_mfma_f32_16x16x4f32(Q[(lane & 15) * QS + k], rk[kk], c, 0, 0, 0);
+        }
+        for (int v = 0; v < 4; ++v) QR[(4 * (lane >> 4) + v) * QS + n] = c[v];
+    }
+    __syncthreads();
+    if (!row_ok) return;
+    uint8_t *rec = a.qrec + ((int64_t)row * a.H + h) * chunk_qrec_bytes(D);
+    float sq = 0.f, sr = 0.f;
+    uint16_t *hi = (uint16_t *)(rec + 16), *lo = hi + D;
+    for (int c = lane; c < D; c += 64) {
+        sq += Q[r * QS + c];
+        if (a.res) {
+            const float x = QR[r * QS + c];
+            const uint32_t hb = bf16_bits(x);
+            const uint32_t lb = bf16_bits(x - __uint_as_float(hb << 16));
+            hi[c] = (uint16_t)hb;
+            lo[c] = (uint16_t)lb;
+            sr += __uint_as_float(hb << 16) + __uint_as_float(lb << 16);   // q' as the matrix cores see it
+        }
+    }
+    sq = wave_sum(sq);
+    sr = wave_sum(sr);
+    if (lane == 0) {
+        ((float *)rec)[0] = sq;
+        ((float *)rec)[1] = sr;
+    }
+}
+
+// ------------------------------------------------------------------ split
+struct ChunkArgs {
+    const uint8_t *pool;
+    int64_t slab;
+    int H, nblk;
+    int ref_off, ref_rec, res_off, res_rec;   // slab offsets of the K records; V at + rec
+    int meta_bytes;                           // (scale, zero) bytes of one record
+    const int32_t *block_table;
+    int max_blocks;
+    const int32_t *seq_lens;
+    const uint16_t *q;                        // [B][C][H][D] bf16
+    const uint8_t *qrec;                      // [B*C][H][chunk_qrec_bytes]
+    float *partials;                          // [B*C][H][nsplit][2 + 2D]
+    int C, nqg, nsplit, split_pages;
+    float score_scale;                        // softmax_scale * log2(e)
+};
+
+// bf16 pairs (16 + c0, 16 + c1), (16 + c2, 16 + c3) of four BITS-bit codes in
+// the low 4*BITS bits of u (code e at bits e*BITS): spread the odd codes to
+// 16 bits above the even ones, then one shift and one and-or per pair
+template <int BITS>
+__device__ __forceinline__ uint2 kpairs(uint32_t u) {
+    constexpr uint32_t MASK = BITS == 4 ? 0x00780078u : 0x00180018u;
+    const uint32_t y = u | (u << (16 - BITS));
+    const uint32_t b0 = ((y << 3) & MASK) | 0x41804180u;
+    const uint32_t b1 = (BITS == 4 ? ((y >> 5) & MASK) : ((y >> 1) & MASK)) | 0x41804180u;
+    return make_uint2(b0, b1);
+}
+
+__device__ __forceinline__ floatx4 mfma_bf16k(uint2 a, uint2 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(shortx4, a), __builtin_bit_cast(shortx4, b),
+                                                     c, 0, 0, 0);
+}
+
+// This lane's K codes of one token: D*BITS/32 bytes (channels kb*D/4 ..
+// kb*D/4 + D/4 - 1), as 32-bit words (the last one partial for D = 96 INT2)
+template <int D, int BITS>
+struct KChunk {
+    static constexpr int NB = D * BITS / 32;
+    static constexpr int NW = (NB + 3) / 4;
+    uint32_t w[NW];
+};
+
+template <int D, int BITS>
+__device__ __forceinline__ void load_k(KChunk<D, BITS> &k, const uint8_t *p) {
+    using K = KChunk<D, BITS>;
+    if constexpr (K::NB % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < K::NW; ++i) k.w[i] = ((const uint32_t *)p)[i];
+    } else {
+        // 6 bytes (D = 96, INT2), 2-byte aligned
+        const uint16_t *h = (const uint16_t *)p;
+        k.w[0] = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+        k.w[1] = h[2];
+    }
+}
+
+// the four codes of k-step s
+template <int BITS>
+__device__ __forceinline__ uint32_t kstep(const uint32_t *w, int s) {
+    if constexpr (BITS == 4) return (w[s >> 1] >> (16 * (s & 1))) & 0xFFFFu;
+    else return (w[s >> 2] >> (8 * (s & 3))) & 0xFFu;
+}
+
+// (scale, zero) of four consecutive tokens of one record
+template <bool MF>
+__device__ __forceinline__ void load_sz4(const uint8_t *p, float *s, float *z) {
+    if constexpr (MF) {
+        const float4 a = ((const float4 *)p)[0], b = ((const float4 *)p)[1];
+        s[0] = a.x; z[0] = a.y; s[1] = a.z; z[1] = a.w; s[2] = b.x; z[2] = b.y; s[3] = b.z; z[3] = b.w;
+    } else {
+        const uint4 v = *(const uint4 *)p;
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            s[r] = f16_to_f32((uint16_t)(w[r] & 0xFFFF));
+            z[r] = f16_to_f32((uint16_t)(w[r] >> 16));
+        }
+    }
+}
+
+template <bool MF>
+__device__ __forceinline__ void load_a4(const uint8_t *p, float *al) {
+    if constexpr (MF) {
+        const float4 a = *(const float4 *)p;
+        al[0] = a.x; al[1] = a.y; al[2] = a.z; al[3] = a.w;
+    } else {
+        const uint2 v = *(const uint2 *)p;
+        al[0] = f16_to_f32((uint16_t)(v.x & 0xFFFF)); al[1] = f16_to_f32((uint16_t)(v.x >> 16));
+        al[2] = f16_to_f32((uint16_t)(v.y & 0xFFFF)); al[3] = f16_to_f32((uint16_t)(v.y >> 16));
+    }
+}
+
+// fp16 hi/lo of four weights as two A operands (token order 0..3). Each
+// weight is first pinned as an fp32 register value: otherwise the compiler
+// may fuse the product that forms it into some of the fp16 conversions and
+// not into others (one rounding against two), and the hi term the matrix
+// cores see would then differ from the one `used` and lo are formed with.
+__device__ __forceinline__ void split4(const float *win, uint2 &hi, uint2 &lo, float &used) {
+    float w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        w[i] = win[i];
+        __asm__ volatile("" : "+v"(w[i]));
+    }
+    halfx2 h01 = {(_Float16)w[0], (_Float16)w[1]}, h23 = {(_Float16)w[2], (_Float16)w[3]};
+    halfx2 l01 = {(_Float16)(w[0] - (float)h01.x), (_Float16)(w[1] - (float)h01.y)};
+    halfx2 l23 = {(_Float16)(w[2] - (float)h23.x), (_Float16)(w[3] - (float)h23.y)};
+    hi = make_uint2(__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23));
+    lo = make_uint2(__builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23));
+    used = ((float)h01.x + (float)l01.x) + ((float)h01.y + (float)l01.y) + ((float)h23.x + (float)l23.x) +
+           ((float)h23.y + (float)l23.y);
+}
+
+// acc[m] += Ahi x B_m + Alo x B_m for every column group m, one operand
+// expansion for both terms
+template <int WP, int BITS, int I>
+__device__ __forceinline__ void v_mfma2_word(floatx4 *acc, uint32_t w, uint2 ahi, uint2 alo, uint32_t vmask,
+                                             uint32_t exp16) {
+    if constexpr (I < WP) {
+        const uint32_t b0 = vpair<BITS * I>(w, vmask, exp16);
+        const uint32_t b1 = vpair<BITS * (WP + I)>(w, vmask, exp16);
+        acc[I] = mfma_f16(ahi, b0, b1, acc[I]);
+        acc[I] = mfma_f16(alo, b0, b1, acc[I]);
+        v_mfma2_word<WP, BITS, I + 1>(acc, w, ahi, alo, vmask, exp16);
+    }
+}
+
+template <int D, int BITS>
+__device__ __forceinline__ void v_mfma2(floatx4 *acc, const VWords<D, BITS> &v, uint2 ahi, uint2 alo) {
+    using V = VWords<D, BITS>;
+    uint32_t vmask, exp16;
+    vpair_consts<BITS>(vmask, exp16);
+#pragma unroll
+    for (int p = 0; p < V::NFULL; ++p) v_mfma2_word<V::W, BITS, 0>(acc + V::W * p, v.w[p], ahi, alo, vmask, exp16);
+    if constexpr (V::REM > 0)
+        v_mfma2_word<V::REM, BITS, 0>(acc + V::W * V::NFULL, v.w[V::NFULL], ahi, alo, vmask, exp16);
+}
+
+// One workgroup per (head, split, sequence x group of 64 queries); wave w
+// holds queries 16*(4*qg + w) + 0..15. Lane l = 16*kb + x: as the query
+// operand it holds query x's channels kb*D/4 + 4s..4s+3 of k-step s; as the
+// K operand token x's same channels; after the score product it holds tokens
+// 4*kb..4*kb+3 of query x; in the output accumulators queries 4*kb..4*kb+3
+// at channel 16m + x.
+template <int D, int RB, bool MF>
+__global__ __launch_bounds__(256) void rq_chunk_split_kernel(ChunkArgs a) {
+    constexpr int NK = D / 16;                 // k-steps of the score product = column groups of V
+    constexpr int PF = partial_floats(D);
+    constexpr int MSZ = MF ? 4 : 2;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int kb = lane >> 4, x = lane & 15;
+    const int h = blockIdx.x, split = blockIdx.y;
+    const int b = blockIdx.z / a.nqg, qg = blockIdx.z % a.nqg;
+    const int H = a.H, C = a.C;
+    const int q0 = 16 * (4 * qg + wave);       // first query row of this wave
+    if (q0 >= C) return;                       // no query of this wave (no barrier below)
+    int seq = a.seq_lens[b];
+    seq = seq < 0 ? 0 : (seq > a.max_blocks * 16 ? a.max_blocks * 16 : seq);
+    const int npages = (seq + 15) >> 4;
+    const int p0 = split * a.split_pages;
+    const int p1 = min(npages, p0 + a.split_pages);
+
+    // this lane's query (operand role): row q0 + x
+    const int qi = q0 + x;
+    const bool qok = qi < C;
+    const int64_t qrow = ((int64_t)b * C + (qok ? qi : 0)) * H + h;
+    uint2 qa[NK], qh[NK], ql[NK];
+    {
+        const uint16_t *qp = a.q + qrow * D + kb * (D / 4);
+        const uint16_t *hp = (const uint16_t *)(a.qrec + qrow * chunk_qrec_bytes(D) + 16) + kb * (D / 4);
+#pragma unroll
+        for (int s = 0; s < NK; ++s) {
+            qa[s] = qok ? *(const uint2 *)(qp + 4 * s) : make_uint2(0u, 0u);
+            if constexpr (RB != 0) {
+                qh[s] = qok ? *(const uint2 *)(hp + 4 * s) : make_uint2(0u, 0u);
+                ql[s] = qok ? *(const uint2 *)(hp + D + 4 * s) : make_uint2(0u, 0u);
+            }
+        }
+    }
+    const float sum_q = qok ? ((const float *)(a.qrec + qrow * chunk_qrec_bytes(D)))[0] : 0.f;
+    const float sum_r = qok ? ((const float *)(a.qrec + qrow * chunk_qrec_bytes(D)))[1] : 0.f;
+
+    float m = kNegInf, lsum = 0.f, zr = 0.f, zs = 0.f;
+    floatx4 vacc_r[NK], vacc_s[NK];
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+        vacc_r[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+        vacc_s[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+    const int code_ref = 16 * D / 2, code_res = 16 * D * (RB ? RB : 2) / 8;
+
+    for (int p = p0; p < p1; ++p) {
+        int blk = a.block_table[(int64_t)b * a.max_blocks + p];
+        const bool bok = blk >= 0 && blk < a.nblk;
+        blk = bok ? blk : 0;
+        const uint8_t *slab = a.pool + ((int64_t)blk * H + h) * a.slab;
+        const uint8_t *rk = slab + a.ref_off, *rv = rk + a.ref_rec;
+        const uint8_t *sk = slab + a.res_off, *sv = sk + a.res_rec;
+        // ---- loads: K codes of token x (operand role), metadata of tokens 4kb..4kb+3, V codes
+        KChunk<D, 4> kr;
+        load_k<D, 4>(kr, rk + x * (D / 2) + kb * (D / 8));
+        float skr[4], zkr[4], svr[4], zvr[4];
+        load_sz4<MF>(rk + code_ref + 4 * kb * 2 * MSZ, skr, zkr);
+        load_sz4<MF>(rv + code_ref + 4 * kb * 2 * MSZ, svr, zvr);
+        VWords<D, 4> vr;
+        load_v<D, 4>(vr, rv, lane);
+        KChunk<D, RB ? RB : 2> ks;
+        VWords<D, RB ? RB : 2> vs;
+        float sks[4], zks[4], aks[4], svs[4], zvs[4], avs[4];
+        if constexpr (RB != 0) {
+            load_k<D, RB>(ks, sk + x * (D * RB / 8) + kb * (D * RB / 32));
+            load_sz4<MF>(sk + code_res + 4 * kb * 2 * MSZ, sks, zks);
+            load_a4<MF>(sk + code_res + a.meta_bytes + 4 * kb * MSZ, aks);
+            load_sz4<MF>(sv + code_res + 4 * kb * 2 * MSZ, svs, zvs);
+            load_a4<MF>(sv + code_res + a.meta_bytes + 4 * kb * MSZ, avs);
+            load_v<D, RB>(vs, sv, lane);
+        }
+        // ---- scores^T: rows = tokens, columns = queries
+        floatx4 sr = {0.f, 0.f, 0.f, 0.f}, ss = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < NK; ++s) sr = mfma_bf16k(kpairs<4>(kstep<4>(kr.w, s)), qa[s], sr);
+        if constexpr (RB != 0) {
+#pragma unroll
+            for (int s = 0; s < NK; ++s) {
+                const uint2 kp = kpairs<RB>(kstep<RB>(ks.w, s));
+                ss = mfma_bf16k(kp, qh[s], ss);
+                ss = mfma_bf16k(kp, ql[s], ss);
+            }
+        }
+        float sc[4];
+        float pmax = kNegInf;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * p + 4 * kb + r;
+            float v = skr[r] * sr[r] + fmaf(-16.f, skr[r], zkr[r]) * sum_q;
+            if constexpr (RB != 0) v = aks[r] * v + (sks[r] * ss[r] + fmaf(-16.f, sks[r], zks[r]) * sum_r);
+            v *= a.score_scale;
+            sc[r] = (bok && t < seq && qok) ? v : kNegInf;
+            pmax = fmaxf(pmax, sc[r]);
+        }
+        // ---- online softmax per query (lanes x, x+16, x+32, x+48 share query x)
+        pmax = fmaxf(pmax, __shfl_xor(pmax, 16, 64));
+        pmax = fmaxf(pmax, __shfl_xor(pmax, 32, 64));
+        if (__any(pmax > m + kThreshC)) {
+            const float mn = fmaxf(m, pmax);
+            const float f = (mn == kNegInf) ? 1.f : fast_exp2(m - mn);
+            lsum *= f; zr *= f; zs *= f;
+            m = mn;
+            // accumulator rows are queries 4kb + v: their factors come from lanes 4kb + v
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const float fv = __shfl(f, 4 * kb + v, 64);
+#pragma unroll
+                for (int i = 0; i < NK; ++i) {
+                    vacc_r[i][v] *= fv;
+                    if constexpr (RB != 0) vacc_s[i][v] *= fv;
+                }
+            }
+        }
+        float wr[4], ws[4];
+        float zsum_r = 0.f, zsum_s = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float pr = (sc[r] == kNegInf) ? 0.f : fast_exp2(sc[r] - m);
+            lsum += pr;
+            const float av = RB != 0 ? avs[r] : 1.f;
+            wr[r] = pr * av * svr[r];
+            zsum_r = fmaf(pr * av, zvr[r], zsum_r);
+            if constexpr (RB != 0) {
+                ws[r] = pr * svs[r];
+                zsum_s = fmaf(pr, zvs[r], zsum_s);
+            }
+        }
+        uint2 ahi, alo;
+        float used;
+        split4(wr, ahi, alo, used);
+        zr += zsum_r - 16.f * used;
+        v_mfma2<D, 4>(vacc_r, vr, ahi, alo);
+        if constexpr (RB != 0) {
+            split4(ws, ahi, alo, used);
+            zs += zsum_s - 16.f * used;
+            v_mfma2<D, RB>(vacc_s, vs, ahi, alo);
+        }
+    }
+
+    // ---- partials: sums over the four token lanes of each query
+    lsum += __shfl_xor(lsum, 16, 64);
+    lsum += __shfl_xor(lsum, 32, 64);
+    zr += __shfl_xor(zr, 16, 64);
+    zr += __shfl_xor(zr, 32, 64);
+    zs += __shfl_xor(zs, 16, 64);
+    zs += __shfl_xor(zs, 32, 64);
+    if (kb == 0 && qok) {
+        float *o = a.partials + (qrow * a.nsplit + split) * PF;
+        o[0] = m;
+        o[1] = lsum;
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int qv = 4 * kb + v;                  // query of accumulator row v
+        const float zrv = __shfl(zr, qv, 64), zsv = __shfl(zs, qv, 64);
+        const int qiv = q0 + qv;
+        if (qiv < C) {
+            float *o = a.partials + ((((int64_t)b * C + qiv) * H + h) * a.nsplit + split) * PF;
+#pragma unroll
+            for (int i = 0; i < NK; ++i) {
+                o[2 + 16 * i + x] = vacc_r[i][v] + zrv;
+                if constexpr (RB != 0) o[2 + D + 16 * i + x] = vacc_s[i][v] + zsv;
+            }
+        }
+    }
+}
+
+// --------------------------------------------------------------- combine
+struct ChunkCombineArgs {
+    const float *partials;          // [R][H][nsplit][2 + 2D]
+    int nsplit, split_pages, max_blocks;
+    const int32_t *seq_lens;
+    const uint16_t *q, *chunk_k, *chunk_v;   // [B][C][H][D] bf16 (chunk K/V may be NULL)
+    const float *rot;
+    float *out;                     // [B][C][H][D]
+    int R, C, H, res;
+    float score_scale;
+};
+
+// One workgroup per (head, 16 query rows); one wave per row.
+template <int D>
+__global__ __launch_bounds__(1024) void rq_chunk_combine_kernel(ChunkCombineArgs a) {
+    constexpr int QS = D + 1;
+    constexpr int PF = partial_floats(D);
+    __shared__ float A[16 * QS];
+    __shared__ float O[16 * QS];
+    __shared__ float QV[16 * QS];
+    const int lane = threadIdx.x & 63, r = threadIdx.x >> 6;
+    const int h = blockIdx.x, tile = blockIdx.y;
+    const int row = tile * 16 + r;
+    const int H = a.H, C = a.C;
+    const int c0 = lane, c1 = lane + 64;
+    float ar0 = 0.f, ar1 = 0.f, as0 = 0.f, as1 = 0.f;
+    const bool rot_wave = a.res && r < D / 16;
+    const int n = r * 16 + (lane & 15);
+    float rv[D / 4];
+    if (rot_wave) {
+        const float *RV = a.rot + ((int64_t)h * 2 + 1) * D * D + (int64_t)(lane >> 4) * D + n;
+#pragma unroll
+        for (int kk = 0; kk < D / 4; ++kk) rv[kk] = RV[(int64_t)4 * kk * D];
+    }
+    if (row < a.R) {
+        const int b = row / C, i = row % C;
+        const int64_t qrow = (int64_t)row * H + h;
+        for (int c = lane; c < D; c += 64) QV[r * QS + c] = bf16_to_f32(a.q[qrow * D + c]);
+        int seq = a.seq_lens[b];
+        seq = seq < 0 ? 0 : (seq > a.max_blocks * 16 ? a.max_blocks * 16 : seq);
+        const int npages = (seq + 15) >> 4;
+        const int ns = (npages + a.split_pages - 1) / a.split_pages;     // splits with pages
+        const float *P = a.partials + qrow * a.nsplit * PF;
+        // chunk tokens 0..i: one lane per token (i < C), score over the whole row
+        const int nj = a.chunk_k ? i + 1 : 0;
+        float mloc = kNegInf;
+        for (int s = lane; s < ns; s += 64) mloc = fmaxf(mloc, P[(int64_t)s * PF]);
+        float sj[4];                                     // chunk scores of tokens lane + 64k (C <= 256)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int j = lane + 64 * k;
+            sj[k] = kNegInf;
+            if (j < nj) {
+                const uint16_t *kr = a.chunk_k + (((int64_t)b * C + j) * H + h) * D;
+                float d = 0.f;
+                for (int c = 0; c < D; c += 8) {
+                    const uint4 v = *(const uint4 *)(kr + c);
+                    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        d = fmaf(QV[r * QS + c + 2 * e], __uint_as_float(w[e] << 16), d);
+                        d = fmaf(QV[r * QS + c + 2 * e + 1], __uint_as_float(w[e] & 0xFFFF0000u), d);
+                    }
+                }
+                sj[k] = d * a.score_scale;
+                mloc = fmaxf(mloc, sj[k]);
+            }
+        }
+        const float M = wave_max(mloc);
+        if (M != kNegInf) {
+            float lloc = 0.f;
+            const int k0 = min(c0, D - 1), k1 = min(c1, D - 1);
+            for (int s = 0; s < ns; ++s) {
+                const float *ps = P + (int64_t)s * PF;
+                const float e = ps[0] == kNegInf ? 0.f : fast_exp2(ps[0] - M);
+                if (lane == 0) lloc = fmaf(e, ps[1], lloc);
+                ar0 = fmaf(e, ps[2 + k0], ar0);
+                ar1 = fmaf(e, ps[2 + k1], ar1);
+                if (a.res) {
+                    as0 = fmaf(e, ps[2 + D + k0], as0);
+                    as1 = fmaf(e, ps[2 + D + k1], as1);
+                }
+            }
+            // chunk part: weights of tokens lane + 64k, then the V rows token by token
+            float pj[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                pj[k] = sj[k] == kNegInf ? 0.f : fast_exp2(sj[k] - M);
+                lloc += pj[k];
+            }
+            for (int j = 0; j < nj; ++j) {
+                const float pw = __shfl(pj[j >> 6], j & 63, 64);
+                const uint16_t *vr = a.chunk_v + (((int64_t)b * C + j) * H + h) * D;
+                if (c0 < D) ar0 = fmaf(pw, bf16_to_f32(vr[c0]), ar0);
+                if (c1 < D) ar1 = fmaf(pw, bf16_to_f32(vr[c1]), ar1);
+            }
+            const float lsum = wave_sum(lloc);
+            const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+            ar0 *= inv; ar1 *= inv; as0 *= inv; as1 *= inv;
+        }
+    }
+    if (c0 < D) { O[r * QS + c0] = ar0; A[r * QS + c0] = as0; }
+    if (c1 < D) { O[r * QS + c1] = ar1; A[r * QS + c1] = as1; }
+    __syncthreads();
+    if (a.res) {
+        // out = O + A * R_V (R_V^T applied to each row's residual sum), as in decode
+        if (rot_wave) {
+            floatx4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < D / 4; ++kk) {
+                const int k = 4 * kk + (lane >> 4);
+                c = __builtin_amdgcn_mfma_f32_16x16x4f32(A[(lane & 15) * QS + k], rv[kk], c, 0, 0, 0);
+            }
+            for (int v = 0; v < 4; ++v) {
+                const int rr = 4 * (lane >> 4) + v;
+                const int rw = tile * 16 + rr;
+                if (rw < a.R) a.out[((int64_t)rw * H + h) * D + n] = c[v] + O[rr * QS + n];
+            }
+        }
+    } else if (row < a.R) {
+        if (c0 < D) a.out[((int64_t)row * H + h) * D + c0] = O[r * QS + c0];
+        if (c1 < D) a.out[((int64_t)row * H + h) * D + c1] = O[r * QS + c1];
+    }
+}
+
+template <int D, int RB>
+hipError_t launch_chunk_split(const ChunkArgs &s, bool mf, dim3 grid, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+    if (mf) hipExtLaunchKernelGGL((rq_chunk_split_kernel<D, RB, true>), grid, dim3(256), 0, st, e0, e1, 0, s);
+    else hipExtLaunchKernelGGL((rq_chunk_split_kernel<D, RB, false>), grid, dim3(256), 0, st, e0, e1, 0, s);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_chunk_d(const ChunkCall &c) {
+    const Geom &g = *c.g;
+    const int R = c.B * c.C;
+    const int ref = g.L - 1;
+    const bool res = c.loop != ref;
+    const int rb = res ? g.bits[c.loop] : 0;
+
+    ChunkPrepArgs pa;
+    pa.q = (const uint16_t *)c.q; pa.rot = c.rot; pa.qrec = c.qrec; pa.R = R; pa.H = g.H; pa.res = res ? 1 : 0;
+    const int tiles = (R + 15) / 16;
+    hipLaunchKernelGGL((rq_chunk_qprep_kernel<D>), dim3(g.H, tiles), dim3(1024), 0, c.stream, pa);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+
+    ChunkArgs s;
+    s.pool = c.pool; s.slab = g.slab; s.H = g.H; s.nblk = g.nblk;
+    s.ref_off = (int)g.loop_off[ref]; s.ref_rec = g.rec[ref];
+    s.res_off = (int)g.loop_off[c.loop]; s.res_rec = g.rec[c.loop];
+    s.meta_bytes = g.meta_bytes;
+    s.block_table = c.block_table; s.max_blocks = c.max_blocks; s.seq_lens = c.seq_lens;
+    s.q = (const uint16_t *)c.q; s.qrec = c.qrec; s.partials = c.partials;
+    s.C = c.C; s.nqg = (c.C + 63) / 64; s.nsplit = c.nsplit; s.split_pages = c.split_pages;
+    s.score_scale = c.softmax_scale * kLog2eC;
+    const bool mf = g.meta == RQ_DTYPE_F32;
+    dim3 grid(g.H, c.nsplit, c.B * s.nqg);
+    if (rb == 0) err = launch_chunk_split<D, 0>(s, mf, grid, c.stream, c.ev_begin, c.ev_end);
+    else if (rb == 2) err = launch_chunk_split<D, 2>(s, mf, grid, c.stream, c.ev_begin, c.ev_end);
+    else err = launch_chunk_split<D, 4>(s, mf, grid, c.stream, c.ev_begin, c.ev_end);
+    if (err != hipSuccess) return err;
+
+    ChunkCombineArgs ca;
+    ca.partials = c.partials; ca.nsplit = c.nsplit; ca.split_pages = c.split_pages; ca.max_blocks = c.max_blocks;
+    ca.seq_lens = c.seq_lens; ca.q = (const uint16_t *)c.q;
+    ca.chunk_k = (const uint16_t *)c.chunk_k; ca.chunk_v = (const uint16_t *)c.chunk_v;
+    ca.rot = c.rot; ca.out = c.out; ca.R = R; ca.C = c.C; ca.H = g.H; ca.res = res ? 1 : 0;
+    ca.score_scale = s.score_scale;
+    hipLaunchKernelGGL((rq_chunk_combine_kernel<D>), dim3(g.H, tiles), dim3(1024), 0, c.stream, ca);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_chunk(const ChunkCall &c) {
+    if (c.B <= 0 || c.C <= 0) return hipSuccess;
+    switch (c.g->D) {
+        case 64: return launch_chunk_d<64>(c);
+        case 96: return launch_chunk_d<96>(c);
+        case 128: return launch_chunk_d<128>(c);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace rq

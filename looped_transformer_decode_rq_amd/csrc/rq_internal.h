@@ -29,6 +29,9 @@ inline int lanes_per_token(int D) { return D == 96 ? 2 : 4; }
 // Per-(loop call, sequence, head) query record written by the query prep kernel.
 __host__ __device__ constexpr int qpack_bytes(int D) { return 64 + 4 * D; }
 __host__ __device__ constexpr int partial_floats(int D) { return 2 + 2 * D; }
+// Per-(query row, head) record of the chunked-prefill query prep: sum q, sum q'
+// (two floats, padded to 16 B), then q' = R_K q as bf16 hi[D] and lo[D].
+__host__ __device__ constexpr int chunk_qrec_bytes(int D) { return 16 + 4 * D; }
 
 // Pages per split chosen when the caller passes 0: sized so that a launch
 // has several rounds of resident workgroups (units = sequences x heads;
@@ -72,6 +75,28 @@ struct DecodeCall {
 };
 
 hipError_t launch_decode(const DecodeCall &c);
+
+// Chunked prefill over the packed cache: C queries per sequence of one loop.
+struct ChunkCall {
+    const Geom *g;
+    const uint8_t *pool;
+    int loop, B, C, max_blocks;
+    const void *q;                // [B][C][H][D] bf16
+    const float *rot;
+    const int32_t *block_table, *seq_lens;
+    const void *chunk_k, *chunk_v;    // [B][C][H][D] bf16 or NULL
+    float softmax_scale;
+    float *out;                   // [B][C][H][D]
+    uint8_t *qrec;                // workspace: [B*C][H][chunk_qrec_bytes]
+    float *partials;              // workspace: [B*C][H][nsplit][partial_floats]
+    int split_pages, nsplit;
+    hipEvent_t ev_begin, ev_end;
+    hipStream_t stream;
+};
+
+constexpr int kMaxChunk = 256;    // queries per sequence in one chunked call
+
+hipError_t launch_chunk(const ChunkCall &c);
 
 struct EncodeCall {
     const Geom *g;

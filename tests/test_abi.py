@@ -254,3 +254,44 @@ def test_auto_split_fills_several_rounds(L):
             assert 1 <= sp <= 64, (B_, mb_, n, sp)
     assert R.decode_auto_split_pages(lay, 0, 16, mb) == 0
     assert R.bf16_auto_split_pages(0, 16, mb) == 0
+
+
+def test_chunk_validation(L):
+    """rq_chunk_attention rejects bad calls with the documented status and
+    enqueues nothing (no GPU needed); unsupported layouts are refused."""
+    lay = _lay(LAYOUTS[1])                      # D128, G128, bf16 K/V: supported
+    C, B, mb = 8, 4, 10
+    ws = R.chunk_workspace_bytes(lay, C, B, mb)
+    assert ws > 0
+    base = [ctypes.byref(lay), _fake(0), 1, C, _fake(1), _fake(2), _fake(3), _fake(4), B, mb,
+            _fake(5), _fake(6), c_float(0.1), _fake(7), _fake(8), ws, None, None]
+
+    def call(**kw):
+        a = list(base)
+        idx = dict(pool=1, loop=2, C=3, q=4, rot=5, table=6, seq=7, batch=8, mb=9, ck=10, cv=11, scale=12,
+                   out=13, ws=14, wsb=15, opts=16)
+        for k, v in kw.items():
+            a[idx[k]] = v
+        return L.rq_chunk_attention(*a)
+
+    assert call(wsb=ws - 1) == -4
+    assert call(pool=None) == -1 and call(q=None) == -1 and call(out=None) == -1 and call(ws=None) == -1
+    assert call(ck=None) == -1                  # chunk K without V
+    assert call(ck=None, cv=None, wsb=0) == -4  # neither: allowed (then the workspace check fires)
+    assert call(loop=4) == -2 and call(loop=-1) == -2
+    assert call(C=0) == -2 and call(C=257) == -3
+    assert call(batch=-1) == -2 and call(mb=0) == -2
+    assert call(scale=c_float(float("nan"))) == -2
+    assert call(q=c_void_p(0x100008)) == -2     # misaligned query
+    assert call(rot=None) == -1                 # residual loop needs R
+    assert call(rot=None, loop=3, wsb=0) == -4  # the reference loop does not
+    assert call(batch=0) == 0
+    assert call(opts=ctypes.byref(RqDecodeOpts(-1, 0, None, None))) == -2
+    # supported layouts only: direct mode, groups smaller than the head, fp32 K/V
+    for bad in (R.make_layout(16, 128, 128, 4, (2, 2, 2), 300, "f16", "bf16", mode=R.RQ_MODE_DIRECT),
+                R.make_layout(16, 128, 32, 4, (2, 2, 2), 300, "f16", "bf16"),
+                R.make_layout(16, 128, 128, 4, (2, 2, 2), 300, "f16", "f32")):
+        a = list(base)
+        a[0] = ctypes.byref(bad)
+        assert L.rq_chunk_attention(*a) == -3
+        assert R.chunk_workspace_bytes(bad, C, B, mb) == 0
