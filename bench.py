@@ -151,6 +151,36 @@ def rq_multi_step(w, s, split_pages, events=None, fused=True):
         R.encode_pack(s["lay"], s["pool"], s["kv_new"], s["rot"], s["slots_new"])
 
 
+def setup_chunk(w, dev, rq, C):
+    """A prefill chunk of C new tokens per sequence after the cached context:
+    their queries and K/V of every loop (seeded, same recipe as the cache)."""
+    import torch
+    import looped_transformer_decode_rq_amd as R
+    import workloads as W
+    B, N, H, D, L = w.batch, w.context, w.heads, w.head_dim, w.loops
+    ck = torch.empty((L, B, C, H, D), dtype=torch.bfloat16, device=dev)
+    cv = torch.empty_like(ck)
+    for b in range(B):
+        kv = W.kv_torch(w, 0, b, rq["st"], dev, tok0=N, ntok=C)          # [L][2][C][H][D]
+        ck[:, b] = kv[:, 0]
+        cv[:, b] = kv[:, 1]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(int(np.random.SeedSequence([w.seed, 0, 11]).generate_state(1)[0]))
+    q = (torch.randn((L, B, C, H, D), generator=gen, device=dev) / float(np.sqrt(D))).to(torch.bfloat16)
+    ws = torch.empty(R.chunk_workspace_bytes(rq["lay"], C, B, rq["table"].shape[1]), dtype=torch.uint8, device=dev)
+    return dict(C=C, q=q, ck=ck, cv=cv, out=torch.empty((L, B, C, H, D), device=dev), ws=ws)
+
+
+def chunk_step(w, rq, ch, events=None):
+    """One chunked-prefill step: every loop's chunk over that loop's packed
+    cache plus the chunk itself (causal)."""
+    import looped_transformer_decode_rq_amd as R
+    tau = 1.0 / np.sqrt(w.head_dim)
+    for l in range(w.loops):
+        R.chunk_attention(rq["lay"], rq["pool"], l, ch["q"][l], rq["rot"], rq["d_table"], rq["d_seq"], ch["ck"][l],
+                          ch["cv"][l], tau, ch["out"][l], ch["ws"], events=None if events is None else events[l])
+
+
 def direct_baseline(w, dev, rq, bits, split_pages, steps, warmup):
     """The direct per-loop quantization baseline on the same synthetic K/V:
     every loop quantized on its own at `bits[l]` (no reference, alpha or
@@ -318,6 +348,8 @@ def main():
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-direct", action="store_true", help="skip the direct per-loop quantization baselines")
+    ap.add_argument("--chunk", type=int, default=64,
+                    help="queries per sequence of the chunked-prefill leg (0 skips it)")
     ap.add_argument("--separate-encode", action="store_true",
                     help="compress the new tokens in a launch of their own after the attention calls "
                          "instead of in the reference-loop call's launch")
@@ -409,6 +441,40 @@ def main():
     multi_gbs = multi_bytes / (multi_ms * 1e-3) / 1e9
     log(f"multi-loop step {t_multi * 1e3:.3f} ms; multi-loop kernel {multi_ms:.3f} ms ({multi_gbs:.0f} GB/s)")
 
+    chunked = None
+    if args.chunk > 0:
+        log(f"timing chunked prefill ({args.chunk} new tokens per sequence and loop)")
+        ch = setup_chunk(w, dev, rq, args.chunk)
+        cpairs = {k: [(ev.create(), ev.create()) for _ in range(L)] for k in range(args.steps)}
+
+        def ch_fn(k):
+            chunk_step(w, rq, ch, None if k is None else cpairs[k])
+
+        t_ch = timed(ch_fn, args.steps, args.warmup)
+        cms = {l: [] for l in range(L)}
+        for k, evs in cpairs.items():
+            for l, (a, b) in enumerate(evs):
+                cms[l].append(ev.ms(a, b))
+                ev.destroy(a)
+                ev.destroy(b)
+        ch_res_ms = float(np.mean([m for l in res_loops for m in cms[l]]))
+        C = args.chunk
+        ch_bytes = token_head_bytes(w, 0) * B * H * N
+        # attention-equivalent work: q.k and p.v, 2D flops each per (query, cached token); the packed
+        # residual loop does both for the reference and for the rotated residual
+        ch_flops = 2 * 2 * 2 * D * B * H * N * C
+        chunked = {"chunk": C, "ms_per_step": t_ch * 1e3, "new_tokens_per_s": B * C / t_ch,
+                   "step": f"{L} chunked-prefill calls (one per loop): {C} queries per sequence over its "
+                           f"{N} packed tokens + the chunk's own bf16 K/V, causal",
+                   "residual_split_kernel_ms": ch_res_ms,
+                   "residual_split_kernel_gbs": ch_bytes / (ch_res_ms * 1e-3) / 1e9,
+                   "residual_split_kernel_tflops": ch_flops / (ch_res_ms * 1e-3) / 1e12,
+                   "reference_split_kernel_ms": float(np.mean(cms[L - 1]))}
+        log(f"chunked prefill step {t_ch * 1e3:.3f} ms; residual chunk kernel {ch_res_ms:.3f} ms "
+            f"({chunked['residual_split_kernel_gbs']:.0f} GB/s packed, {chunked['residual_split_kernel_tflops']:.1f} TFLOP/s)")
+        del ch
+        torch.cuda.empty_cache()
+
     direct, direct_outs, errors = {}, {}, {}
     if not args.no_direct:
         for name, bits in (("direct_int2", (2,) * L), ("direct_int4", (4,) * L)):
@@ -499,6 +565,7 @@ def main():
                        "kernel_ms": multi_ms, "bytes_per_launch": multi_bytes, "traffic": measured("multi_loop"),
                        "kernel_gbs": multi_gbs,
                        "kernel_frac_of_peak": multi_gbs / HBM_PEAK_GBS},
+        "chunked_prefill": chunked,
         "bf16_baseline": bf16,
         "direct_baselines": direct or None,
         "attention_rel_l2_vs_bf16": errors or None,

@@ -280,8 +280,9 @@ rq_status rq_fit_rotation(const float *samples, int64_t n, int32_t head_dim, int
  *                 both NULL (then only the cache is attended)
  *   out           [B][chunk][H][D] fp32
  * Supported layouts: RQ_MODE_RESIDUAL, group_size == head_dim, kv_dtype bf16;
- * others return RQ_ERR_UNSUPPORTED. opts: split_pages (any size >= 1; 0 = the
- * library's choice) and timing events bracketing the split kernel.
+ * others return RQ_ERR_UNSUPPORTED. opts: split_pages (1..1024, larger is
+ * RQ_ERR_UNSUPPORTED; 0 = the library's choice) and timing events bracketing
+ * the split kernel.
  * q, chunk_k, chunk_v and the workspace must be 16-byte aligned. */
 size_t rq_chunk_workspace_bytes(const rq_layout *layout, int32_t chunk, int32_t batch,
                                 int32_t max_blocks_per_seq, int32_t split_pages);

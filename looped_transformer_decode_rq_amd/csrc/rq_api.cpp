@@ -109,7 +109,8 @@ static size_t decode_ws(const Geom &g, int n, int B, int max_blocks, int sp) {
 static int chunk_split_pages(int B, int H, int C, int max_blocks) {
     const int64_t units = (int64_t)B * H * ((C + 63) / 64);
     const int64_t target = 4LL * device_cus();
-    const int64_t ns = std::max<int64_t>(1, std::min<int64_t>(max_blocks, (target + units - 1) / std::max<int64_t>(units, 1)));
+    int64_t ns = std::max<int64_t>(1, std::min<int64_t>(max_blocks, (target + units - 1) / std::max<int64_t>(units, 1)));
+    ns = std::max<int64_t>(ns, (max_blocks + kMaxChunkSplit - 1) / kMaxChunkSplit);
     return (int)((max_blocks + ns - 1) / ns);
 }
 
@@ -323,6 +324,7 @@ rq_status rq_chunk_attention(const rq_layout *layout, const void *pool, int32_t 
     if ((chunk_k == nullptr) != (chunk_v == nullptr)) return RQ_ERR_NULL;
     const int sp_req = opts ? opts->split_pages : 0;
     if (sp_req < 0) return RQ_ERR_SHAPE;
+    if (sp_req > kMaxChunkSplit) return RQ_ERR_UNSUPPORTED;
     if (batch == 0) return RQ_OK;
     if (!pool || !q || !block_table || !seq_lens || !out || (loop != g.L - 1 && !rot)) return RQ_ERR_NULL;
     if (!aligned(pool, 16) || !aligned(q, 16) || (chunk_k && (!aligned(chunk_k, 16) || !aligned(chunk_v, 16))))

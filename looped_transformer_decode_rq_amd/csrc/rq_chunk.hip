@@ -129,7 +129,11 @@ struct ChunkArgs {
     float *partials;                          // [B*C][H][nsplit][2 + 2D]
     int C, nqg, nsplit, split_pages;
     float score_scale;                        // softmax_scale * log2(e)
+    int stage;                                // bytes of one ring stage: 2*ref_rec (+ 2*res_rec)
 };
+
+constexpr int kChunkStages = 4;               // ring depth: three pages in flight while one is used
+constexpr int kChunkMaxSplit = 1024;          // pages per split (block ids preloaded into LDS)
 
 // bf16 pairs (16 + c0, 16 + c1), (16 + c2, 16 + c3) of four BITS-bit codes in
 // the low 4*BITS bits of u (code e at bits e*BITS): spread the odd codes to
@@ -259,23 +263,68 @@ __device__ __forceinline__ void v_mfma2(floatx4 *acc, const VWords<D, BITS> &v, 
 // K operand token x's same channels; after the score product it holds tokens
 // 4*kb..4*kb+3 of query x; in the output accumulators queries 4*kb..4*kb+3
 // at channel 16m + x.
-template <int D, int RB, bool MF>
+//
+// The four waves share every page: each stage of an LDS ring holds the page's
+// reference K and V records and the loop's residual K and V records exactly
+// as stored (two runs of the slab), filled by direct-to-LDS loads that the
+// waves issue in equal shares kChunkStages-1 pages ahead; one barrier per
+// page publishes the landed stage and frees the oldest one. The split's block
+// ids are preloaded into LDS.
+template <int D, int RB, bool MF, int NI>
 __global__ __launch_bounds__(256) void rq_chunk_split_kernel(ChunkArgs a) {
     constexpr int NK = D / 16;                 // k-steps of the score product = column groups of V
     constexpr int PF = partial_floats(D);
     constexpr int MSZ = MF ? 4 : 2;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    constexpr int NST = kChunkStages;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int kb = lane >> 4, x = lane & 15;
     const int h = blockIdx.x, split = blockIdx.y;
     const int b = blockIdx.z / a.nqg, qg = blockIdx.z % a.nqg;
     const int H = a.H, C = a.C;
-    const int q0 = 16 * (4 * qg + wave);       // first query row of this wave
-    if (q0 >= C) return;                       // no query of this wave (no barrier below)
+    const int q0 = 16 * (4 * qg + wave);       // first query row of this wave (>= C: loads only)
     int seq = a.seq_lens[b];
     seq = seq < 0 ? 0 : (seq > a.max_blocks * 16 ? a.max_blocks * 16 : seq);
     const int npages = (seq + 15) >> 4;
     const int p0 = split * a.split_pages;
     const int p1 = min(npages, p0 + a.split_pages);
+    const int steps = p1 > p0 ? p1 - p0 : 0;
+
+    // LDS: ring of NST stages, one 16-byte padding slot per wave, block ids of the split
+    const int stage = a.stage;
+    uint8_t *ring = smem;
+    const uint32_t junk = lds_addr(smem + NST * stage + 16 * wave);
+    int *tbl = (int *)(smem + NST * stage + 64);
+    for (int i = threadIdx.x; i < steps; i += 256) {
+        int blk = a.block_table[(int64_t)b * a.max_blocks + p0 + i];
+        tbl[i] = (blk >= 0 && blk < a.nblk) ? blk : -1;
+    }
+    __syncthreads();
+
+    // this lane's pieces: instruction j of wave w covers pieces 64*(NI*w + j) + lane
+    const int np = stage >> 4, nref = a.ref_rec >> 3;          // 16-byte pieces; of them in the reference run
+    int doff[NI], live[NI], dst[NI];
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+        const int start = 64 * (NI * wave + j);
+        live[j] = max(0, min(64, np - start));
+        dst[j] = start * 16;
+        const int k = start + lane;
+        doff[j] = k < nref ? a.ref_off + 16 * k : a.res_off + 16 * (k - nref);
+    }
+    auto issue = [&](int st, int slot) {
+        const int blk = max(__builtin_amdgcn_readfirstlane(tbl[st]), 0);
+        const uint8_t *base = a.pool + ((int64_t)blk * H + h) * a.slab;
+        const uint32_t l0 = lds_addr(ring + slot * stage);
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            if (live[j] > 0) {
+                if (lane < live[j]) dma16(l0 + dst[j], base, (uint32_t)doff[j]);
+            } else if (lane == 0) {
+                dma16(junk, base, 0u);
+            }
+        }
+    };
 
     // this lane's query (operand role): row q0 + x
     const int qi = q0 + x;
@@ -296,6 +345,14 @@ __global__ __launch_bounds__(256) void rq_chunk_split_kernel(ChunkArgs a) {
     }
     const float sum_q = qok ? ((const float *)(a.qrec + qrow * chunk_qrec_bytes(D)))[0] : 0.f;
     const float sum_r = qok ? ((const float *)(a.qrec + qrow * chunk_qrec_bytes(D)))[1] : 0.f;
+    // the query registers are complete before the ring's loads are counted
+#pragma unroll
+    for (int s = 0; s < NK; ++s) {
+        __asm__ volatile("" ::"v"(qa[s].x), "v"(qa[s].y));
+        if constexpr (RB != 0) __asm__ volatile("" ::"v"(qh[s].x), "v"(qh[s].y), "v"(ql[s].x), "v"(ql[s].y));
+    }
+    __asm__ volatile("" ::"v"(sum_q), "v"(sum_r));
+    wait_vmcnt<0>();
 
     float m = kNegInf, lsum = 0.f, zr = 0.f, zs = 0.f;
     floatx4 vacc_r[NK], vacc_s[NK];
@@ -306,13 +363,21 @@ __global__ __launch_bounds__(256) void rq_chunk_split_kernel(ChunkArgs a) {
     }
     const int code_ref = 16 * D / 2, code_res = 16 * D * (RB ? RB : 2) / 8;
 
-    for (int p = p0; p < p1; ++p) {
-        int blk = a.block_table[(int64_t)b * a.max_blocks + p];
-        const bool bok = blk >= 0 && blk < a.nblk;
-        blk = bok ? blk : 0;
-        const uint8_t *slab = a.pool + ((int64_t)blk * H + h) * a.slab;
-        const uint8_t *rk = slab + a.ref_off, *rv = rk + a.ref_rec;
-        const uint8_t *sk = slab + a.res_off, *sv = sk + a.res_rec;
+#pragma unroll
+    for (int j = 0; j < NST - 1; ++j)
+        if (j < steps) issue(j, j);
+    for (int cur = 0; cur < steps; ++cur) {
+        // this wave's loads of page `cur` have landed ...
+        wait_steps<NST - 2, NI>(min(NST - 2, steps - 1 - cur));
+        // ... and every other wave's; all waves are done with page cur-1
+        __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (cur + NST - 1 < steps) issue(cur + NST - 1, (cur + NST - 1) % NST);
+        if (q0 >= C) continue;                 // a wave without queries only loads
+        const int p = p0 + cur;
+        const bool bok = tbl[cur] >= 0;
+        const uint8_t *S = ring + (cur % NST) * stage;
+        const uint8_t *rk = S, *rv = S + a.ref_rec;
+        const uint8_t *sk = S + 2 * a.ref_rec, *sv = sk + a.res_rec;
         // ---- loads: K codes of token x (operand role), metadata of tokens 4kb..4kb+3, V codes
         KChunk<D, 4> kr;
         load_k<D, 4>(kr, rk + x * (D / 2) + kb * (D / 8));
@@ -555,8 +620,16 @@ __global__ __launch_bounds__(1024) void rq_chunk_combine_kernel(ChunkCombineArgs
 
 template <int D, int RB>
 hipError_t launch_chunk_split(const ChunkArgs &s, bool mf, dim3 grid, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
-    if (mf) hipExtLaunchKernelGGL((rq_chunk_split_kernel<D, RB, true>), grid, dim3(256), 0, st, e0, e1, 0, s);
-    else hipExtLaunchKernelGGL((rq_chunk_split_kernel<D, RB, false>), grid, dim3(256), 0, st, e0, e1, 0, s);
+    // ring, padding slots, block ids of one split
+    const size_t lds = (size_t)kChunkStages * s.stage + 64 + 4 * (size_t)s.split_pages;
+    const bool two = s.stage > 4096;           // two direct-to-LDS instructions per wave and page
+    if (mf) {
+        if (two) hipExtLaunchKernelGGL((rq_chunk_split_kernel<D, RB, true, 2>), grid, dim3(256), (uint32_t)lds, st, e0, e1, 0, s);
+        else hipExtLaunchKernelGGL((rq_chunk_split_kernel<D, RB, true, 1>), grid, dim3(256), (uint32_t)lds, st, e0, e1, 0, s);
+    } else {
+        if (two) hipExtLaunchKernelGGL((rq_chunk_split_kernel<D, RB, false, 2>), grid, dim3(256), (uint32_t)lds, st, e0, e1, 0, s);
+        else hipExtLaunchKernelGGL((rq_chunk_split_kernel<D, RB, false, 1>), grid, dim3(256), (uint32_t)lds, st, e0, e1, 0, s);
+    }
     return hipGetLastError();
 }
 
@@ -584,6 +657,8 @@ hipError_t launch_chunk_d(const ChunkCall &c) {
     s.q = (const uint16_t *)c.q; s.qrec = c.qrec; s.partials = c.partials;
     s.C = c.C; s.nqg = (c.C + 63) / 64; s.nsplit = c.nsplit; s.split_pages = c.split_pages;
     s.score_scale = c.softmax_scale * kLog2eC;
+    s.stage = 2 * g.rec[ref] + (res ? 2 * g.rec[c.loop] : 0);
+    if (s.stage > 8192 || c.split_pages > kChunkMaxSplit) return hipErrorInvalidValue;
     const bool mf = g.meta == RQ_DTYPE_F32;
     dim3 grid(g.H, c.nsplit, c.B * s.nqg);
     if (rb == 0) err = launch_chunk_split<D, 0>(s, mf, grid, c.stream, c.ev_begin, c.ev_end);

@@ -91,4 +91,38 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ------------------------------------------- direct-to-LDS loads and waits
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Wait until at most `ahead` page steps of NI loads each are still in flight
+// (ahead is wave-uniform, 0 <= ahead <= K).
+template <int K, int NI>
+__device__ __forceinline__ void wait_steps(int ahead) {
+    if constexpr (K == 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (ahead >= K) wait_vmcnt<K * NI>();
+        else wait_steps<K - 1, NI>(ahead);
+    }
+}
+
+// One direct-to-LDS load of 16 bytes per active lane: lane i's bytes land at
+// lds + 16*i (lds is wave-uniform).
+__device__ __forceinline__ void dma16(uint32_t lds, const uint8_t *base, uint32_t off) {
+    __asm__ volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                     ::"s"(lds), "v"(off), "s"(base) : "memory", "m0");
+}
+__device__ __forceinline__ void dma16(uint32_t lds, const uint8_t *src) {
+    __asm__ volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                     ::"s"(lds), "v"(src) : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
+}
+
+
 }  // namespace rq

@@ -95,6 +95,7 @@ struct ChunkCall {
 };
 
 constexpr int kMaxChunk = 256;    // queries per sequence in one chunked call
+constexpr int kMaxChunkSplit = 1024;   // pages per split of a chunked call
 
 hipError_t launch_chunk(const ChunkCall &c);
 
