@@ -396,13 +396,20 @@ __device__ __forceinline__ void init_state(SplitState<D> &s) {
 //   wsc           this wave's weight scratch (PPI pages of kWScratch bytes);
 //                 may alias the step's code bytes, which are all read first
 //   lsv           this lane's residual query limbs (registers or LDS)
-template <int D, int RB, bool META_F32, int G, int REFB = 4>
+//   SHR           shared reference rows (multi-loop): the reference weights go
+//                 to rows 2*(sha_pair + g) + {hi, lo} of `sha` instead of the
+//                 wave's own product; the reference product and the rescale
+//                 of those rows are done by the wave that owns them, which
+//                 reads this step's factor from `fr` (1 without a rescale).
+//                 The accumulators are then rescaled only when RB != 0.
+template <int D, int RB, bool META_F32, int G, int REFB = 4, bool SHR = false>
 __device__ __forceinline__ void token_step(const uint8_t *ck, const uint8_t *mkr, const uint8_t *mvr,
                                            const uint8_t *rk, const uint8_t *mks, const uint8_t *aks,
                                            const uint8_t *mvs, const uint8_t *avs, const uint8_t *vref,
                                            const uint8_t *vres, uint8_t *wsc, int lane, bool valid,
                                            float score_scale, const QueryRegs<D> &q, const uint4 *lsv,
-                                           SplitState<D> &s) {
+                                           SplitState<D> &s, uint8_t *sha = nullptr, int sha_pair = 0,
+                                           float *fr = nullptr) {
     using Ln = Lanes<D>;
     constexpr int LPT = Ln::LPT, CPL = Ln::CPL, PPI = Ln::PPI;
     constexpr int REF_NB = CPL * REFB / 8;          // first record's K code bytes per lane (INT4, or INT2 direct)
@@ -419,7 +426,7 @@ __device__ __forceinline__ void token_step(const uint8_t *ck, const uint8_t *mkr
     VWords<D, RB ? RB : 2> vw_res[PPI];
 #pragma unroll
     for (int pg = 0; pg < PPI; ++pg) {
-        load_v<D, REFB>(vw_ref[pg], vref + pg * VREF_STRIDE, lane);
+        if constexpr (!SHR) load_v<D, REFB>(vw_ref[pg], vref + pg * VREF_STRIDE, lane);
         if constexpr (RB != 0) load_v<D, RB>(vw_res[pg], vres + pg * VRES_STRIDE, lane);
     }
     // every code byte of the step is read before the weight scratch (which
@@ -444,13 +451,20 @@ __device__ __forceinline__ void token_step(const uint8_t *ck, const uint8_t *mkr
     float score = lane_group_sum<LPT>(part) * score_scale;
     score = valid ? score : kNegInf;
     // online softmax, rescaled only when a score beats m by 2^8
+    float fstep = 1.f;
     if (__any(score > s.m + kRescaleThresh)) {
         const float mn = fmaxf(s.m, wave_max(score));
         const float f = fast_exp2(s.m - mn);
+        if constexpr (!SHR || RB != 0) {
 #pragma unroll
-        for (int i = 0; i < D / 16; ++i) s.v[i] *= f;
+            for (int i = 0; i < D / 16; ++i) s.v[i] *= f;
+        }
         s.zr *= f; s.zs *= f; s.lsum *= f;
         s.m = mn;
+        fstep = f;
+    }
+    if constexpr (SHR) {
+        if (lane == 0) *fr = fstep;
     }
     const float pr = fast_exp2(score - s.m);
     s.lsum += pr;
@@ -471,12 +485,16 @@ __device__ __forceinline__ void token_step(const uint8_t *ck, const uint8_t *mkr
     {
         const int g = (q4 * CPL) / G, k = q4 % NPG;
         uint16_t *wrow = (uint16_t *)(wsc + (tok_i >> 4) * kWScratch) + (tok_i & 15);
+        uint16_t *srow = nullptr;
+        if constexpr (SHR) srow = (uint16_t *)(sha + (tok_i >> 4) * kWScratch) + (tok_i & 15) + 32 * (sha_pair + g);
 #pragma unroll
         for (int e = 0; e < 4 / NPG; ++e) {
             const int r = k + NPG * e;
             if (RB != 0 || r < 2) {
                 const uint32_t pair = (r & 1) ? lob : hib;
-                wrow[(4 * g + r) * 16] = (uint16_t)((r >> 1) ? pair >> 16 : pair);
+                const uint16_t h16 = (uint16_t)((r >> 1) ? pair >> 16 : pair);
+                if (SHR && r < 2) srow[16 * r] = h16;
+                else wrow[(4 * g + r) * 16] = h16;
             }
         }
     }
@@ -489,8 +507,10 @@ __device__ __forceinline__ void token_step(const uint8_t *ck, const uint8_t *mkr
 #pragma unroll
     for (int pg = 0; pg < PPI; ++pg) {
         const uint2 a2 = *(const uint2 *)(wsc + pg * kWScratch + (lane & 15) * 32 + (lane >> 4) * 8);
-        const uint2 ar = make_uint2(ref_row ? a2.x : 0u, ref_row ? a2.y : 0u);
-        v_mfma<D, REFB>(s.v, vw_ref[pg], ar);
+        if constexpr (!SHR) {
+            const uint2 ar = make_uint2(ref_row ? a2.x : 0u, ref_row ? a2.y : 0u);
+            v_mfma<D, REFB>(s.v, vw_ref[pg], ar);
+        }
         if constexpr (RB != 0) {
             const uint2 as = make_uint2(ref_row ? 0u : a2.x, ref_row ? 0u : a2.y);
             v_mfma<D, RB>(s.v, vw_res[pg], as);
@@ -522,6 +542,87 @@ __device__ __forceinline__ void finish_split(SplitState<D> &s, int lane, float *
         if (gl == (16 * m) / G) {
             out[2 + 16 * m + col] = s.v[m][0] + s.v[m][1] + zr;
             if constexpr (RES) out[2 + D + 16 * m + col] = s.v[m][2] + s.v[m][3] + zs;
+        }
+    }
+}
+
+// ---- shared reference rows (multi-loop)
+//
+// The reference V codes of a page are the same B operand for every loop of a
+// multi-loop workgroup; only the weights differ. One wave (the reference
+// loop's, which has no residual of its own) therefore multiplies the
+// reference V codes by an A operand whose row pairs 2P, 2P+1 (P = call*NG +
+// g) hold the (hi, lo) weights that wave `call` wrote for group g, and keeps
+// every loop's reference sums in its accumulators. The rows of a step are
+// consumed one step later, after the workgroup barrier that publishes them.
+
+// Fold one step's shared rows into the owner's accumulators: rescale the
+// rows of each loop by the factor that loop applied at that step, then add
+// the products with the step's reference V codes.
+template <int D, int G>
+__device__ __forceinline__ void shared_ref_step(SplitState<D> &s, const uint8_t *sha, const float *fr,
+                                                const uint8_t *vref, int lane, int nl) {
+    constexpr int NG = D / G, PPI = Lanes<D>::PPI;
+    constexpr int VREF_STRIDE = 16 * D * 4 / 8;
+    // rows 4(lane/16) + i of this lane's accumulators: pairs P0 (i < 2), P0 + 1
+    const int p0 = 2 * (lane >> 4), c0 = p0 / NG, c1 = (p0 + 1) / NG;
+    const float f0 = c0 < nl ? fr[c0] : 1.f, f1 = c1 < nl ? fr[c1] : 1.f;
+    if (__any(f0 != 1.f || f1 != 1.f)) {
+#pragma unroll
+        for (int m = 0; m < D / 16; ++m) {
+            s.v[m][0] *= f0; s.v[m][1] *= f0;
+            s.v[m][2] *= f1; s.v[m][3] *= f1;
+        }
+    }
+#pragma unroll
+    for (int pg = 0; pg < PPI; ++pg) {
+        VWords<D, 4> vw;
+        load_v<D, 4>(vw, vref + pg * VREF_STRIDE, lane);
+        const uint2 a = *(const uint2 *)(sha + pg * kWScratch + (lane & 15) * 32 + (lane >> 4) * 8);
+        v_mfma<D, 4>(s.v, vw, a);
+    }
+}
+
+// The owner's reference sums of every loop into `gath` ([nl][D] floats):
+// pair P = call*NG + g of column group m belongs to call P/NG when g is the
+// group of m's channels.
+template <int D, int G>
+__device__ __forceinline__ void shared_ref_gather(const SplitState<D> &s, float *gath, int lane, int nl) {
+    constexpr int NG = D / G;
+    const int p0 = 2 * (lane >> 4), col = lane & 15;
+#pragma unroll
+    for (int m = 0; m < D / 16; ++m) {
+        const int gm = (16 * m) / G;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int P = p0 + j, c = P / NG;
+            if (c < nl && P % NG == gm) gath[c * D + 16 * m + col] = s.v[m][2 * j] + s.v[m][2 * j + 1];
+        }
+    }
+}
+
+// End of a split with shared reference rows: as finish_split, with the
+// reference sums of this wave's loop taken from `gref` (its row of the
+// gather area) and the residual sums from the wave's own accumulators (none
+// for the reference loop, RES = false).
+template <int D, bool RES, int G>
+__device__ __forceinline__ void finish_split_shared(SplitState<D> &s, int lane, const float *gref, float *out) {
+    constexpr int LPT = Lanes<D>::LPT, CPL = Lanes<D>::CPL, NPG = G / CPL;
+#pragma unroll
+    for (int off = LPT; off < 64; off <<= 1) {
+        s.zr += __shfl_xor(s.zr, off, 64);
+        if constexpr (RES) s.zs += __shfl_xor(s.zs, off, 64);
+        s.lsum += __shfl_xor(s.lsum, off, 64);
+    }
+    const int gl = lane >> 4, col = lane & 15;
+    const float zr = __shfl(s.zr, gl * NPG, 64);
+    const float zs = RES ? __shfl(s.zs, gl * NPG, 64) : 0.f;
+    if (lane == 0) { out[0] = s.m; out[1] = s.lsum; }
+#pragma unroll
+    for (int m = 0; m < D / 16; ++m) {
+        if (gl == (16 * m) / G) {
+            out[2 + 16 * m + col] = gref[16 * m + col] + zr;
+            out[2 + D + 16 * m + col] = RES ? s.v[m][2] + s.v[m][3] + zs : 0.f;
         }
     }
 }
@@ -792,7 +893,11 @@ struct MultiGeom {
 // (short shares are padded with a one-lane load into the wave's scratch
 // slot), so its waits are fixed counts, and one barrier per step publishes
 // the landed stage to all waves and frees the slot for reuse.
-template <int D, bool META_F32, int G, int RBMAX>
+// SH: the group holds the reference loop and its wave owns the reference
+// rows of every loop (shared_ref_step); the rows of step cur are consumed in
+// step cur + 1, so loads run nst - 2 steps ahead instead of nst - 1 and the
+// stage of step cur stays intact until then.
+template <int D, bool META_F32, int G, int RBMAX, bool SH>
 __global__ __launch_bounds__(64 * kMaxMultiLoops) void rq_multi_kernel(MultiArgs a) {
     using Ln = Lanes<D>;
     using MG = MultiGeom<D, META_F32, G, RBMAX>;
@@ -847,7 +952,9 @@ __global__ __launch_bounds__(64 * kMaxMultiLoops) void rq_multi_kernel(MultiArgs
     }
 
     // LDS: nst shared reference stages, then nst private residual stages per
-    // wave, then one 16-byte scratch slot per wave for the padding loads
+    // wave, then one 16-byte scratch slot per wave for the padding loads, the
+    // weight scratch of each wave and (SH) two buffers of shared reference
+    // rows and two of rescale factors
     const int ref_stage = MG::REF_BYTES, res_stage = MG::RES_MAX;
     uint8_t *ref_base = smem;
     uint8_t *res_base = smem + nst * ref_stage + wave * nst * res_stage;
@@ -924,6 +1031,14 @@ __global__ __launch_bounds__(64 * kMaxMultiLoops) void rq_multi_kernel(MultiArgs
     init_state<D>(s);
     // this wave's weight scratch (after the padding slots)
     uint8_t *wsc = smem + nst * (ref_stage + nl * res_stage) + 16 * nl + wave * PPI * kWScratch;
+    uint8_t *sha = smem + nst * (ref_stage + nl * res_stage) + nl * (16 + PPI * kWScratch);
+    float *fbuf = (float *)(sha + 2 * PPI * kWScratch);
+    if constexpr (SH) {
+        // rows past the last loop's pairs are never written: zero them once
+        // (visible to the owner after the first barrier)
+        for (int i = threadIdx.x; i < 2 * PPI * kWScratch / 4; i += 64 * nl) ((uint32_t *)sha)[i] = 0u;
+    }
+    const int la = SH ? nst - 2 : nst - 1;   // steps in flight ahead of the current one
 
     auto blk_of = [&](int st, int pg) -> int { return __builtin_amdgcn_readlane(tbl, st * PPI + pg); };
 
@@ -952,14 +1067,16 @@ __global__ __launch_bounds__(64 * kMaxMultiLoops) void rq_multi_kernel(MultiArgs
         }
     };
 
-    for (int j = 0; j < nst - 1; ++j)
+    for (int j = 0; j < la; ++j)
         if (j < steps) issue(j, j);
     for (int cur = 0; cur < steps; ++cur) {
         // this wave's loads of step `cur` have landed ...
-        wait_steps<NST_MAX - 2, NIW>(min(nst - 2, steps - 1 - cur));
-        // ... and so have every other wave's; all waves are done with step cur-1
+        wait_steps<NST_MAX - 2, NIW>(min(la - 1, steps - 1 - cur));
+        // ... and so have every other wave's; all waves are done with step
+        // cur-1 (SH: except the owner's use of its reference stage, which ends
+        // before the next barrier, and the stage is refilled only after it)
         __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        if (cur + nst - 1 < steps) issue(cur + nst - 1, (cur + nst - 1) % nst);
+        if (cur + la < steps) issue(cur + la, (cur + la) % nst);
         const int slot = cur % nst;
         const int pp = p0 + cur * PPI + page_in_step;
         int blk = blk_of(cur, 0);
@@ -967,6 +1084,31 @@ __global__ __launch_bounds__(64 * kMaxMultiLoops) void rq_multi_kernel(MultiArgs
         const bool valid = blk >= 0 && pp < p1 && pp * 16 + tok < seq;
         const uint8_t *R = ref_base + slot * ref_stage;
         const uint8_t *S = res_base + slot * res_stage;
+        if constexpr (SH) {
+            uint8_t *shc = sha + (cur & 1) * PPI * kWScratch;
+            float *fc = fbuf + (cur & 1) * kMaxMultiLoops + call;
+            if (rb == 2) {
+                token_step<D, 2, META_F32, G, 4, true>(R + o_ck, R + o_mkr, R + o_mvr, S + o_rk, S + o_mks,
+                                                       S + o_aks, S + o_mvs, S + o_avs, R + MG::R_CV,
+                                                       S + PPI * MG::cb_res(2), wsc, lane, valid, a.score_scale,
+                                                       q, q.lsv, s, shc, call * NG, fc);
+            } else if (RBMAX == 4 && rb == 4) {
+                token_step<D, RBMAX, META_F32, G, 4, true>(R + o_ck, R + o_mkr, R + o_mvr, S + o_rk, S + o_mks,
+                                                           S + o_aks, S + o_mvs, S + o_avs, R + MG::R_CV,
+                                                           S + PPI * MG::cb_res(RBMAX), wsc, lane, valid,
+                                                           a.score_scale, q, q.lsv, s, shc, call * NG, fc);
+            } else {
+                token_step<D, 0, META_F32, G, 4, true>(R + o_ck, R + o_mkr, R + o_mvr, S, S, S, S, S, R + MG::R_CV,
+                                                       S, wsc, lane, valid, a.score_scale, q, q.lsv, s, shc,
+                                                       call * NG, fc);
+                // the previous step's rows of every loop
+                if (cur > 0)
+                    shared_ref_step<D, G>(s, sha + ((cur - 1) & 1) * PPI * kWScratch,
+                                          fbuf + ((cur - 1) & 1) * kMaxMultiLoops,
+                                          ref_base + ((cur - 1) % nst) * ref_stage + MG::R_CV, lane, nl);
+            }
+            continue;
+        }
         if (rb == 2) {
             token_step<D, 2, META_F32, G>(R + o_ck, R + o_mkr, R + o_mvr, S + o_rk, S + o_mks, S + o_aks,
                                           S + o_mvs, S + o_avs, R + MG::R_CV, S + PPI * MG::cb_res(2), wsc, lane,
@@ -981,7 +1123,25 @@ __global__ __launch_bounds__(64 * kMaxMultiLoops) void rq_multi_kernel(MultiArgs
         }
     }
 
-    finish_split<D, true, G>(s, lane, a.partials + ((((int64_t)call * a.B + b) * H + h) * a.nsplit + split) * PF);
+    float *part = a.partials + ((((int64_t)call * a.B + b) * H + h) * a.nsplit + split) * PF;
+    if constexpr (SH) {
+        // the last step's rows, then every loop's reference sums through LDS
+        // (the ring is free: every load has landed and every read is done)
+        __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        float *gath = (float *)smem;
+        if (rb == 0) {
+            const int last = steps - 1;
+            shared_ref_step<D, G>(s, sha + (last & 1) * PPI * kWScratch, fbuf + (last & 1) * kMaxMultiLoops,
+                                  ref_base + (last % nst) * ref_stage + MG::R_CV, lane, nl);
+            __asm__ volatile("" ::: "memory");
+            shared_ref_gather<D, G>(s, gath, lane, nl);
+        }
+        __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (rb == 0) finish_split_shared<D, false, G>(s, lane, gath + call * D, part);
+        else finish_split_shared<D, true, G>(s, lane, gath + call * D, part);
+    } else {
+        finish_split<D, true, G>(s, lane, part);
+    }
 }
 
 // --------------------------------------------------------------- combine
@@ -1153,24 +1313,30 @@ hipError_t launch_split_d(const SplitArgs &s, int rb, int refb, bool mf, dim3 gr
 }
 
 template <int D, bool MF, int G, int RBMAX>
-hipError_t launch_multi_k(const MultiArgs &m, dim3 grid, size_t lds, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
-    hipExtLaunchKernelGGL((rq_multi_kernel<D, MF, G, RBMAX>), grid, dim3(64 * m.nl), (uint32_t)lds, st, ev0, ev1, 0, m);
+hipError_t launch_multi_k(const MultiArgs &m, bool sh, dim3 grid, size_t lds, hipStream_t st, hipEvent_t ev0,
+                          hipEvent_t ev1) {
+    if (sh)
+        hipExtLaunchKernelGGL((rq_multi_kernel<D, MF, G, RBMAX, true>), grid, dim3(64 * m.nl), (uint32_t)lds, st, ev0,
+                              ev1, 0, m);
+    else
+        hipExtLaunchKernelGGL((rq_multi_kernel<D, MF, G, RBMAX, false>), grid, dim3(64 * m.nl), (uint32_t)lds, st,
+                              ev0, ev1, 0, m);
     return hipGetLastError();
 }
 
 template <int D, bool MF, int RBMAX>
-hipError_t launch_multi_g(const MultiArgs &m, int G, dim3 grid, size_t lds, hipStream_t st, hipEvent_t ev0,
+hipError_t launch_multi_g(const MultiArgs &m, bool sh, int G, dim3 grid, size_t lds, hipStream_t st, hipEvent_t ev0,
                           hipEvent_t ev1) {
     if constexpr (D == 128) {
-        if (G == 32) return launch_multi_k<D, MF, 32, RBMAX>(m, grid, lds, st, ev0, ev1);
-        if (G == 64) return launch_multi_k<D, MF, 64, RBMAX>(m, grid, lds, st, ev0, ev1);
-        return launch_multi_k<D, MF, 128, RBMAX>(m, grid, lds, st, ev0, ev1);
+        if (G == 32) return launch_multi_k<D, MF, 32, RBMAX>(m, sh, grid, lds, st, ev0, ev1);
+        if (G == 64) return launch_multi_k<D, MF, 64, RBMAX>(m, sh, grid, lds, st, ev0, ev1);
+        return launch_multi_k<D, MF, 128, RBMAX>(m, sh, grid, lds, st, ev0, ev1);
     } else if constexpr (D == 96) {
-        return launch_multi_k<D, MF, 96, RBMAX>(m, grid, lds, st, ev0, ev1);
+        return launch_multi_k<D, MF, 96, RBMAX>(m, sh, grid, lds, st, ev0, ev1);
     } else {
-        if (G == 16) return launch_multi_k<D, MF, 16, RBMAX>(m, grid, lds, st, ev0, ev1);
-        if (G == 32) return launch_multi_k<D, MF, 32, RBMAX>(m, grid, lds, st, ev0, ev1);
-        return launch_multi_k<D, MF, 64, RBMAX>(m, grid, lds, st, ev0, ev1);
+        if (G == 16) return launch_multi_k<D, MF, 16, RBMAX>(m, sh, grid, lds, st, ev0, ev1);
+        if (G == 32) return launch_multi_k<D, MF, 32, RBMAX>(m, sh, grid, lds, st, ev0, ev1);
+        return launch_multi_k<D, MF, 64, RBMAX>(m, sh, grid, lds, st, ev0, ev1);
     }
 }
 
@@ -1186,17 +1352,20 @@ int multi_slot_bytes(int G, int nl) {
 }
 
 // LDS bytes of the multi-loop kernel outside its ring: one 16-byte padding
-// slot and one weight scratch per wave
+// slot and one weight scratch per wave, and with shared reference rows two
+// row buffers and two factor buffers
 template <int D>
-int multi_fixed_bytes(int nl) { return nl * (16 + Lanes<D>::PPI * kWScratch); }
+int multi_fixed_bytes(int nl, bool sh) {
+    return nl * (16 + Lanes<D>::PPI * kWScratch) + (sh ? 2 * Lanes<D>::PPI * kWScratch + 2 * kMaxMultiLoops * 4 : 0);
+}
 
 // Ring depth of the multi-loop kernel: as deep as the workgroup's LDS share
 // allows (three workgroups per CU up to 4 waves each, else one 64 KB
 // workgroup), at most 8.
 template <int D, bool MF, int RBMAX>
-int multi_ring_depth(int G, int nl) {
+int multi_ring_depth(int G, int nl, bool sh) {
     const int budget = nl <= 4 ? 53 * 1024 : 64 * 1024;
-    return std::min(8, (budget - multi_fixed_bytes<D>(nl)) / multi_slot_bytes<D, MF, RBMAX>(G, nl));
+    return std::min(8, (budget - multi_fixed_bytes<D>(nl, sh)) / multi_slot_bytes<D, MF, RBMAX>(G, nl));
 }
 
 template <int D>
@@ -1229,8 +1398,8 @@ hipError_t launch_decode_d(const DecodeCall &c) {
         bool any4 = false;
         for (int i = 0; i < c.n; ++i) any4 = any4 || (c.loops[i] != ref && g.bits[c.loops[i]] == 4);
         auto depth = [&](int nl) {
-            if (mf) return any4 ? multi_ring_depth<D, true, 4>(g.G, nl) : multi_ring_depth<D, true, 2>(g.G, nl);
-            return any4 ? multi_ring_depth<D, false, 4>(g.G, nl) : multi_ring_depth<D, false, 2>(g.G, nl);
+            if (mf) return any4 ? multi_ring_depth<D, true, 4>(g.G, nl, false) : multi_ring_depth<D, true, 2>(g.G, nl, false);
+            return any4 ? multi_ring_depth<D, false, 4>(g.G, nl, false) : multi_ring_depth<D, false, 2>(g.G, nl, false);
         };
         int nl_max = 3;
         for (int nl = std::min(c.n, kMaxMultiLoops); nl > 3; --nl)
@@ -1244,12 +1413,14 @@ hipError_t launch_decode_d(const DecodeCall &c) {
             m.ref_off = (int)g.loop_off[ref]; m.ref_rec = g.rec[ref];
             m.nl = nl;
             bool g4 = false;
+            int nref = 0;
             for (int w = 0; w < kMaxMultiLoops; ++w) {
                 const int l = w < nl ? c.loops[first + w] : ref;
                 m.rb[w] = (l == ref) ? 0 : g.bits[l];
                 m.res_off[w] = (int)g.loop_off[l];
                 m.res_rec[w] = g.rec[l];
                 g4 = g4 || m.rb[w] == 4;
+                nref += (w < nl && l == ref) ? 1 : 0;
             }
             m.block_table = c.block_table; m.max_blocks = c.max_blocks; m.seq_lens = c.seq_lens;
             m.qpack = c.qpack + (int64_t)first * c.B * g.H * qpack_bytes(D);
@@ -1257,15 +1428,20 @@ hipError_t launch_decode_d(const DecodeCall &c) {
             m.B = c.B; m.nsplit = c.nsplit; m.split_pages = c.split_pages;
             m.score_scale = score_scale;
             int slot;
-            if (mf) {
-                m.nst = g4 ? multi_ring_depth<D, true, 4>(g.G, nl) : multi_ring_depth<D, true, 2>(g.G, nl);
-                slot = g4 ? multi_slot_bytes<D, true, 4>(g.G, nl) : multi_slot_bytes<D, true, 2>(g.G, nl);
-            } else {
-                m.nst = g4 ? multi_ring_depth<D, false, 4>(g.G, nl) : multi_ring_depth<D, false, 2>(g.G, nl);
-                slot = g4 ? multi_slot_bytes<D, false, 4>(g.G, nl) : multi_slot_bytes<D, false, 2>(g.G, nl);
-            }
+            auto ring = [&](bool sh) {
+                if (mf) return g4 ? multi_ring_depth<D, true, 4>(g.G, nl, sh) : multi_ring_depth<D, true, 2>(g.G, nl, sh);
+                return g4 ? multi_ring_depth<D, false, 4>(g.G, nl, sh) : multi_ring_depth<D, false, 2>(g.G, nl, sh);
+            };
+            if (mf) slot = g4 ? multi_slot_bytes<D, true, 4>(g.G, nl) : multi_slot_bytes<D, true, 2>(g.G, nl);
+            else slot = g4 ? multi_slot_bytes<D, false, 4>(g.G, nl) : multi_slot_bytes<D, false, 2>(g.G, nl);
+            // shared reference rows: the group holds the reference loop (whose
+            // wave owns the rows), every (call, group) row pair fits the
+            // 16 rows of the A operand, and the ring keeps a stage in flight
+            // besides the current and the previous one
+            const bool sh = nref == 1 && nl * (D / g.G) <= 8 && ring(true) >= 3;
+            m.nst = ring(sh);
             if (m.nst < 2) return hipErrorInvalidConfiguration;
-            size_t lds = (size_t)m.nst * slot + multi_fixed_bytes<D>(nl);
+            size_t lds = (size_t)m.nst * slot + multi_fixed_bytes<D>(nl, sh);
             const bool last = k == ngroups - 1;
             // the current tokens' encode rides in the last group's launch
             m.enc_x0 = c.nsplit; m.enc_items = 0; m.enc_kvf = kvf ? 1 : 0;
@@ -1278,10 +1454,10 @@ hipError_t launch_decode_d(const DecodeCall &c) {
             }
             dim3 grid(c.nsplit + ex, g.H, c.B);
             hipEvent_t e0 = last ? c.ev_begin : nullptr, e1 = last ? c.ev_end : nullptr;
-            if (mf) err = g4 ? launch_multi_g<D, true, 4>(m, g.G, grid, lds, c.stream, e0, e1)
-                             : launch_multi_g<D, true, 2>(m, g.G, grid, lds, c.stream, e0, e1);
-            else err = g4 ? launch_multi_g<D, false, 4>(m, g.G, grid, lds, c.stream, e0, e1)
-                          : launch_multi_g<D, false, 2>(m, g.G, grid, lds, c.stream, e0, e1);
+            if (mf) err = g4 ? launch_multi_g<D, true, 4>(m, sh, g.G, grid, lds, c.stream, e0, e1)
+                             : launch_multi_g<D, true, 2>(m, sh, g.G, grid, lds, c.stream, e0, e1);
+            else err = g4 ? launch_multi_g<D, false, 4>(m, sh, g.G, grid, lds, c.stream, e0, e1)
+                          : launch_multi_g<D, false, 2>(m, sh, g.G, grid, lds, c.stream, e0, e1);
             if (err != hipSuccess) return err;
             first += nl;
         }
