@@ -1042,11 +1042,15 @@ __global__ __launch_bounds__(64 * kMaxMultiLoops) void rq_multi_kernel(MultiArgs
 
     auto blk_of = [&](int st, int pg) -> int { return __builtin_amdgcn_readlane(tbl, st * PPI + pg); };
 
+    // byte offset of slab (block, h): block * H + h and the slab size fit 32 bits
+    const uint32_t slab32 = (uint32_t)a.slab;
+    auto slab_at = [&](int blk) -> const uint8_t * {
+        return a.pool + (uint64_t)(uint32_t)(max(blk, 0) * H + h) * slab32;
+    };
     auto issue = [&](int st, int slot) {
-        const int b0 = max(blk_of(st, 0), 0);
-        const uint8_t *base0 = a.pool + ((int64_t)b0 * H + h) * a.slab;
+        const uint8_t *base0 = slab_at(blk_of(st, 0));
         const uint8_t *base1 = base0;
-        if constexpr (PPI == 2) base1 = a.pool + ((int64_t)max(blk_of(st, 1), 0) * H + h) * a.slab;
+        if constexpr (PPI == 2) base1 = slab_at(blk_of(st, 1));
         const uint32_t rl = lds_addr(ref_base + slot * ref_stage);
         const uint32_t sl = lds_addr(res_base + slot * res_stage);
 #pragma unroll
@@ -1069,6 +1073,9 @@ __global__ __launch_bounds__(64 * kMaxMultiLoops) void rq_multi_kernel(MultiArgs
 
     for (int j = 0; j < la; ++j)
         if (j < steps) issue(j, j);
+    // ring slots of the current, the previous and the issued step, kept as
+    // running counters (nst is a launch value: no division per step)
+    int slot = 0, pslot = nst - 1, islot = la;
     for (int cur = 0; cur < steps; ++cur) {
         // this wave's loads of step `cur` have landed ...
         wait_steps<NST_MAX - 2, NIW>(min(la - 1, steps - 1 - cur));
@@ -1076,8 +1083,7 @@ __global__ __launch_bounds__(64 * kMaxMultiLoops) void rq_multi_kernel(MultiArgs
         // cur-1 (SH: except the owner's use of its reference stage, which ends
         // before the next barrier, and the stage is refilled only after it)
         __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        if (cur + la < steps) issue(cur + la, (cur + la) % nst);
-        const int slot = cur % nst;
+        if (cur + la < steps) issue(cur + la, islot);
         const int pp = p0 + cur * PPI + page_in_step;
         int blk = blk_of(cur, 0);
         if constexpr (PPI == 2) blk = page_in_step ? blk_of(cur, 1) : blk;
@@ -1105,11 +1111,9 @@ __global__ __launch_bounds__(64 * kMaxMultiLoops) void rq_multi_kernel(MultiArgs
                 if (cur > 0)
                     shared_ref_step<D, G>(s, sha + ((cur - 1) & 1) * PPI * kWScratch,
                                           fbuf + ((cur - 1) & 1) * kMaxMultiLoops,
-                                          ref_base + ((cur - 1) % nst) * ref_stage + MG::R_CV, lane, nl);
+                                          ref_base + pslot * ref_stage + MG::R_CV, lane, nl);
             }
-            continue;
-        }
-        if (rb == 2) {
+        } else if (rb == 2) {
             token_step<D, 2, META_F32, G>(R + o_ck, R + o_mkr, R + o_mvr, S + o_rk, S + o_mks, S + o_aks,
                                           S + o_mvs, S + o_avs, R + MG::R_CV, S + PPI * MG::cb_res(2), wsc, lane,
                                           valid, a.score_scale, q, q.lsv, s);
@@ -1121,6 +1125,9 @@ __global__ __launch_bounds__(64 * kMaxMultiLoops) void rq_multi_kernel(MultiArgs
             token_step<D, 0, META_F32, G>(R + o_ck, R + o_mkr, R + o_mvr, S, S, S, S, S, R + MG::R_CV, S, wsc, lane,
                                           valid, a.score_scale, q, q.lsv, s);
         }
+        pslot = slot;
+        slot = slot + 1 == nst ? 0 : slot + 1;
+        islot = islot + 1 == nst ? 0 : islot + 1;
     }
 
     float *part = a.partials + ((((int64_t)call * a.B + b) * H + h) * a.nsplit + split) * PF;
@@ -1132,7 +1139,7 @@ __global__ __launch_bounds__(64 * kMaxMultiLoops) void rq_multi_kernel(MultiArgs
         if (rb == 0) {
             const int last = steps - 1;
             shared_ref_step<D, G>(s, sha + (last & 1) * PPI * kWScratch, fbuf + (last & 1) * kMaxMultiLoops,
-                                  ref_base + (last % nst) * ref_stage + MG::R_CV, lane, nl);
+                                  ref_base + pslot * ref_stage + MG::R_CV, lane, nl);
             __asm__ volatile("" ::: "memory");
             shared_ref_gather<D, G>(s, gath, lane, nl);
         }
