@@ -568,10 +568,14 @@ __device__ __forceinline__ void shared_ref_step(SplitState<D> &s, const uint8_t 
     const int p0 = 2 * (lane >> 4), c0 = p0 / NG, c1 = (p0 + 1) / NG;
     const float f0 = c0 < nl ? fr[c0] : 1.f, f1 = c1 < nl ? fr[c1] : 1.f;
     if (__any(f0 != 1.f || f1 != 1.f)) {
+        // in place (tied registers): a plain product lets the compiler move
+        // every accumulator into new registers on both paths of this branch
 #pragma unroll
         for (int m = 0; m < D / 16; ++m) {
-            s.v[m][0] *= f0; s.v[m][1] *= f0;
-            s.v[m][2] *= f1; s.v[m][3] *= f1;
+            __asm__("v_mul_f32 %0, %0, %1" : "+v"(s.v[m][0]) : "v"(f0));
+            __asm__("v_mul_f32 %0, %0, %1" : "+v"(s.v[m][1]) : "v"(f0));
+            __asm__("v_mul_f32 %0, %0, %1" : "+v"(s.v[m][2]) : "v"(f1));
+            __asm__("v_mul_f32 %0, %0, %1" : "+v"(s.v[m][3]) : "v"(f1));
         }
     }
 #pragma unroll
@@ -1076,59 +1080,49 @@ __global__ __launch_bounds__(64 * kMaxMultiLoops) void rq_multi_kernel(MultiArgs
     // ring slots of the current, the previous and the issued step, kept as
     // running counters (nst is a launch value: no division per step)
     int slot = 0, pslot = nst - 1, islot = la;
-    for (int cur = 0; cur < steps; ++cur) {
-        // this wave's loads of step `cur` have landed ...
-        wait_steps<NST_MAX - 2, NIW>(min(la - 1, steps - 1 - cur));
-        // ... and so have every other wave's; all waves are done with step
-        // cur-1 (SH: except the owner's use of its reference stage, which ends
-        // before the next barrier, and the stage is refilled only after it)
-        __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        if (cur + la < steps) issue(cur + la, islot);
-        const int pp = p0 + cur * PPI + page_in_step;
-        int blk = blk_of(cur, 0);
-        if constexpr (PPI == 2) blk = page_in_step ? blk_of(cur, 1) : blk;
-        const bool valid = blk >= 0 && pp < p1 && pp * 16 + tok < seq;
-        const uint8_t *R = ref_base + slot * ref_stage;
-        const uint8_t *S = res_base + slot * res_stage;
-        if constexpr (SH) {
+    // The page loop, one copy per residual width RBW of this wave's loop: the
+    // accumulators then stay in the same registers from step to step.
+    auto page_loop = [&](auto rbw_tag) {
+        constexpr int RBW = decltype(rbw_tag)::value;
+        for (int cur = 0; cur < steps; ++cur) {
+            // this wave's loads of step `cur` have landed ...
+            wait_steps<NST_MAX - 2, NIW>(min(la - 1, steps - 1 - cur));
+            // ... and so have every other wave's; all waves are done with step
+            // cur-1 (SH: except the owner's use of its reference stage, which
+            // ends before the next barrier, and the stage is refilled only after it)
+            __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            if (cur + la < steps) issue(cur + la, islot);
+            const int pp = p0 + cur * PPI + page_in_step;
+            int blk = blk_of(cur, 0);
+            if constexpr (PPI == 2) blk = page_in_step ? blk_of(cur, 1) : blk;
+            const bool valid = blk >= 0 && pp < p1 && pp * 16 + tok < seq;
+            const uint8_t *R = ref_base + slot * ref_stage;
+            const uint8_t *S = res_base + slot * res_stage;
             uint8_t *shc = sha + (cur & 1) * PPI * kWScratch;
             float *fc = fbuf + (cur & 1) * kMaxMultiLoops + call;
-            if (rb == 2) {
-                token_step<D, 2, META_F32, G, 4, true>(R + o_ck, R + o_mkr, R + o_mvr, S + o_rk, S + o_mks,
+            if constexpr (RBW != 0) {
+                token_step<D, RBW, META_F32, G, 4, SH>(R + o_ck, R + o_mkr, R + o_mvr, S + o_rk, S + o_mks,
                                                        S + o_aks, S + o_mvs, S + o_avs, R + MG::R_CV,
-                                                       S + PPI * MG::cb_res(2), wsc, lane, valid, a.score_scale,
+                                                       S + PPI * MG::cb_res(RBW), wsc, lane, valid, a.score_scale,
                                                        q, q.lsv, s, shc, call * NG, fc);
-            } else if (RBMAX == 4 && rb == 4) {
-                token_step<D, RBMAX, META_F32, G, 4, true>(R + o_ck, R + o_mkr, R + o_mvr, S + o_rk, S + o_mks,
-                                                           S + o_aks, S + o_mvs, S + o_avs, R + MG::R_CV,
-                                                           S + PPI * MG::cb_res(RBMAX), wsc, lane, valid,
-                                                           a.score_scale, q, q.lsv, s, shc, call * NG, fc);
             } else {
-                token_step<D, 0, META_F32, G, 4, true>(R + o_ck, R + o_mkr, R + o_mvr, S, S, S, S, S, R + MG::R_CV,
-                                                       S, wsc, lane, valid, a.score_scale, q, q.lsv, s, shc,
-                                                       call * NG, fc);
-                // the previous step's rows of every loop
-                if (cur > 0)
+                token_step<D, 0, META_F32, G, 4, SH>(R + o_ck, R + o_mkr, R + o_mvr, S, S, S, S, S, R + MG::R_CV, S,
+                                                     wsc, lane, valid, a.score_scale, q, q.lsv, s, shc, call * NG,
+                                                     fc);
+                // SH: the previous step's rows of every loop
+                if (SH && cur > 0)
                     shared_ref_step<D, G>(s, sha + ((cur - 1) & 1) * PPI * kWScratch,
                                           fbuf + ((cur - 1) & 1) * kMaxMultiLoops,
                                           ref_base + pslot * ref_stage + MG::R_CV, lane, nl);
             }
-        } else if (rb == 2) {
-            token_step<D, 2, META_F32, G>(R + o_ck, R + o_mkr, R + o_mvr, S + o_rk, S + o_mks, S + o_aks,
-                                          S + o_mvs, S + o_avs, R + MG::R_CV, S + PPI * MG::cb_res(2), wsc, lane,
-                                          valid, a.score_scale, q, q.lsv, s);
-        } else if (RBMAX == 4 && rb == 4) {
-            token_step<D, RBMAX, META_F32, G>(R + o_ck, R + o_mkr, R + o_mvr, S + o_rk, S + o_mks, S + o_aks,
-                                              S + o_mvs, S + o_avs, R + MG::R_CV, S + PPI * MG::cb_res(RBMAX), wsc,
-                                              lane, valid, a.score_scale, q, q.lsv, s);
-        } else {
-            token_step<D, 0, META_F32, G>(R + o_ck, R + o_mkr, R + o_mvr, S, S, S, S, S, R + MG::R_CV, S, wsc, lane,
-                                          valid, a.score_scale, q, q.lsv, s);
+            pslot = slot;
+            slot = slot + 1 == nst ? 0 : slot + 1;
+            islot = islot + 1 == nst ? 0 : islot + 1;
         }
-        pslot = slot;
-        slot = slot + 1 == nst ? 0 : slot + 1;
-        islot = islot + 1 == nst ? 0 : islot + 1;
-    }
+    };
+    if (rb == 2) page_loop(std::integral_constant<int, 2>{});
+    else if (RBMAX == 4 && rb == 4) page_loop(std::integral_constant<int, RBMAX>{});
+    else page_loop(std::integral_constant<int, 0>{});
 
     float *part = a.partials + ((((int64_t)call * a.B + b) * H + h) * a.nsplit + split) * PF;
     if constexpr (SH) {
