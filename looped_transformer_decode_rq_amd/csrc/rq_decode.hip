@@ -25,6 +25,7 @@
 //                partials and the uncompressed tail token, then
 //                out = acc_ref/l + R_V^T (acc_res/l) on the f32 matrix cores.
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include <hip/hip_ext.h>
@@ -1360,13 +1361,63 @@ int multi_fixed_bytes(int nl, bool sh) {
     return nl * (16 + Lanes<D>::PPI * kWScratch) + (sh ? 2 * Lanes<D>::PPI * kWScratch + 2 * kMaxMultiLoops * 4 : 0);
 }
 
-// Ring depth of the multi-loop kernel: as deep as the workgroup's LDS share
-// allows (three workgroups per CU up to 4 waves each, else one 64 KB
-// workgroup), at most 8.
+// LDS of one CU of the current device (queried once per device; 160 KB if
+// the query fails)
+static int lds_per_cu() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 160 * 1024;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess || n <= 0)
+        n = 160 * 1024;
+    cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+// Workgroups of one multi-loop kernel variant with nl waves that its
+// registers and wave slots let one CU hold (queried once per variant and nl)
+template <int D, bool MF, int G, int RBMAX, bool SH>
+int multi_occ_k(int nl) {
+    static std::atomic<int> cache[kMaxMultiLoops + 1];
+    int n = cache[nl].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, rq_multi_kernel<D, MF, G, RBMAX, SH>, 64 * nl, 0) !=
+            hipSuccess || n <= 0)
+        n = 1;
+    cache[nl].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+template <int D, bool MF, int RBMAX>
+int multi_occ(int G, int nl, bool sh) {
+    auto k = [&](auto gt) {
+        constexpr int GG = decltype(gt)::value;
+        return sh ? multi_occ_k<D, MF, GG, RBMAX, true>(nl) : multi_occ_k<D, MF, GG, RBMAX, false>(nl);
+    };
+    if constexpr (D == 128) {
+        if (G == 32) return k(std::integral_constant<int, 32>{});
+        if (G == 64) return k(std::integral_constant<int, 64>{});
+        return k(std::integral_constant<int, 128>{});
+    } else if constexpr (D == 96) {
+        return k(std::integral_constant<int, 96>{});
+    } else {
+        if (G == 16) return k(std::integral_constant<int, 16>{});
+        if (G == 32) return k(std::integral_constant<int, 32>{});
+        return k(std::integral_constant<int, 64>{});
+    }
+}
+
+// Ring depth of the multi-loop kernel, at most 8: as deep as the LDS share
+// of one workgroup allows when the CU holds as many workgroups as the
+// kernel's registers and wave slots admit (LDS then never lowers the
+// occupancy), at most 64 KB; a ring of fewer than 3 stages takes 64 KB.
 template <int D, bool MF, int RBMAX>
 int multi_ring_depth(int G, int nl, bool sh) {
-    const int budget = nl <= 4 ? 53 * 1024 : 64 * 1024;
-    return std::min(8, (budget - multi_fixed_bytes<D>(nl, sh)) / multi_slot_bytes<D, MF, RBMAX>(G, nl));
+    const int fixed = multi_fixed_bytes<D>(nl, sh), slot = multi_slot_bytes<D, MF, RBMAX>(G, nl);
+    const int budget = std::min(64 * 1024, lds_per_cu() / multi_occ<D, MF, RBMAX>(G, nl, sh));
+    const int d = (budget - fixed) / slot;
+    return std::min(8, d >= 3 ? d : (64 * 1024 - fixed) / slot);
 }
 
 template <int D>
