@@ -473,15 +473,19 @@ __device__ __forceinline__ void token_step(const uint8_t *ck, const uint8_t *mkr
     const float pa = pr * av;
     float wr = valid ? pa * svr : 0.f;
     float ws = valid ? pr * svs : 0.f;
-    // pin the weights as fp32 values, so that every fp16 conversion below
-    // (the A operand and the zero term's copy) rounds the same number
+    // pin the weights as fp32 values, so that the fp16 terms below and the
+    // zero terms split and use the same numbers
     __asm__ volatile("" : "+v"(wr), "+v"(ws));
+    // fp16 terms, both rounded to nearest (unbiased): hi = RNE(w), lo = RNE(w - hi)
     const halfx2 hi = {(_Float16)wr, (_Float16)ws};
     const halfx2 lo = {(_Float16)(wr - (float)hi.x), (_Float16)(ws - (float)hi.y)};
     const uint32_t hib = __builtin_bit_cast(uint32_t, hi), lob = __builtin_bit_cast(uint32_t, lo);
-    // zero terms: p*alpha*z minus the offset 16 times the weight as the matrix cores see it
-    s.zr += valid ? fmaf(pa, zvr, -16.f * ((float)hi.x + (float)lo.x)) : 0.f;
-    if constexpr (RB != 0) s.zs += valid ? fmaf(pr, zvs, -16.f * ((float)hi.y + (float)lo.y)) : 0.f;
+    // zero terms: p*alpha*z minus the offset 16 times the weight. The matrix
+    // cores see hi + lo instead of w: the offset then leaves 16 (hi + lo - w)
+    // per token, an unbiased rounding error of the same size as the one the
+    // split already makes on the code term (c (hi + lo - w), c <= 15).
+    s.zr += valid ? fmaf(pa, zvr, -16.f * wr) : 0.f;
+    if constexpr (RB != 0) s.zs += valid ? fmaf(pr, zvs, -16.f * ws) : 0.f;
     // rows 4g + r of this token's column: lane k of the group's NPG lanes writes rows k, k + NPG, ...
     {
         const int g = (q4 * CPL) / G, k = q4 % NPG;

@@ -26,8 +26,11 @@ namespace rq {
 // <= 2^-25 below; w <= 256*alpha*s by the lazy softmax rescale), tokens
 // along k. Row 4g+r of the product is then sum_t w_t (16 + c_t) for every
 // column, lanes 16g..16g+15 receiving the rows of group g. The offset 16 is
-// taken out again with the same rounded weights, in the zero term:
-// value sum = sum_t w_t (16 + c_t) + sum_t (p alpha z_t - 16 w_t).
+// taken out again in the zero term:
+// value sum = sum_t w_t (16 + c_t) + sum_t (p alpha z_t - 16 w'_t),
+// with w' the weight as the matrix cores see it (chunked prefill) or before
+// the split (decode: then 16 (w - w') joins the split's own error c (w - w'),
+// unbiased and of the same size).
 typedef _Float16 halfx4 __attribute__((ext_vector_type(4)));
 typedef _Float16 halfx2 __attribute__((ext_vector_type(2)));
 typedef short shortx4 __attribute__((ext_vector_type(4)));
