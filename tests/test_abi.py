@@ -230,19 +230,20 @@ def test_binding_refuses_host_tensors(L):
 
 
 def test_auto_split_fills_several_rounds(L):
-    """The automatic split: pages spread evenly, several rounds of split
-    workgroups per launch, and the workspace query sized with the same rule.
-    Without a GPU the device query falls back to 256 compute units."""
+    """The automatic split: pages spread evenly over enough split workgroups
+    for several rounds per launch, rounded up to a multiple of 8 pages, and
+    the workspace query sized with the same rule. Without a GPU the device
+    query falls back to 256 compute units."""
     lay = _lay(LAYOUTS[1])
     units, mb = 16 * 16, 2049
     sp1 = R.decode_auto_split_pages(lay, 1, 16, mb)
     spm = R.decode_auto_split_pages(lay, 4, 16, mb)
     assert 1 <= sp1 <= 64 and 1 <= spm <= 64
+    assert sp1 % 8 == 0 and spm % 8 == 0
     wg1 = -(-mb // (4 * sp1))
-    assert units * wg1 >= 8 * 3 * 256                     # >= 8 rounds of 3 workgroups per CU
-    assert -(-mb // (4 * wg1)) == sp1                      # pages spread evenly over the splits
-    assert units * -(-mb // spm) >= 14 * 3 * 256 or spm == 64 or -(-mb // 64) == -(-mb // spm)
-    assert (sp1, spm) == (22, 49)
+    assert units * wg1 >= 7 * 3 * 256                     # >= 7 rounds of 3 workgroups per CU
+    assert units * -(-mb // spm) >= 12 * 3 * 256          # one-split units: >= 12 rounds
+    assert (sp1, spm) == (24, 56)                          # 22 and 49 pages spread evenly, rounded up
     assert R.decode_workspace_bytes(lay, 1, 16, mb, 0) == R.decode_workspace_bytes(lay, 1, 16, mb, sp1)
     assert R.decode_workspace_bytes(lay, 4, 16, mb, 0) == R.decode_workspace_bytes(lay, 4, 16, mb, spm)
     assert R.bf16_auto_split_pages(16, 16, mb) == spm
