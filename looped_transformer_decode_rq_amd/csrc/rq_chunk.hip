@@ -211,11 +211,14 @@ __device__ __forceinline__ void load_a4(const uint8_t *p, float *al) {
     }
 }
 
-// fp16 hi/lo of four weights as two A operands (token order 0..3). Each
+// fp16 hi/lo of four weights as two A operands (token order 0..3), and their
+// sum before the split (`used`, for the zero term: the matrix cores see hi +
+// lo, and the offset then leaves 16 (hi + lo - w) per token, an unbiased
+// rounding error the size of the split's own error on the code term). Each
 // weight is first pinned as an fp32 register value: otherwise the compiler
 // may fuse the product that forms it into some of the fp16 conversions and
-// not into others (one rounding against two), and the hi term the matrix
-// cores see would then differ from the one `used` and lo are formed with.
+// not into others (one rounding against two), and lo would then be formed
+// against a different hi than the one the matrix cores see.
 __device__ __forceinline__ void split4(const float *win, uint2 &hi, uint2 &lo, float &used) {
     float w[4];
 #pragma unroll
@@ -228,8 +231,7 @@ __device__ __forceinline__ void split4(const float *win, uint2 &hi, uint2 &lo, f
     halfx2 l23 = {(_Float16)(w[2] - (float)h23.x), (_Float16)(w[3] - (float)h23.y)};
     hi = make_uint2(__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23));
     lo = make_uint2(__builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23));
-    used = ((float)h01.x + (float)l01.x) + ((float)h01.y + (float)l01.y) + ((float)h23.x + (float)l23.x) +
-           ((float)h23.y + (float)l23.y);
+    used = (w[0] + w[1]) + (w[2] + w[3]);
 }
 
 // acc[m] += Ahi x B_m + Alo x B_m for every column group m, one operand
