@@ -42,6 +42,7 @@ namespace {
 
 constexpr float kLog2eC = 1.4426950408889634f;
 constexpr float kThreshC = 8.0f;         // rescale when a score beats the running max by 2^8
+constexpr int kChunkFold = 16;           // pages between folds of the zero terms into the accumulators
 
 // bf16 round-to-nearest-even of a float, as its bits
 __device__ __forceinline__ uint32_t bf16_bits(float x) {
@@ -368,102 +369,133 @@ __global__ __launch_bounds__(256) void rq_chunk_split_kernel(ChunkArgs a) {
 #pragma unroll
     for (int j = 0; j < NST - 1; ++j)
         if (j < steps) issue(j, j);
-    for (int cur = 0; cur < steps; ++cur) {
-        // this wave's loads of page `cur` have landed ...
-        wait_steps<NST - 2, NI>(min(NST - 2, steps - 1 - cur));
-        // ... and every other wave's; all waves are done with page cur-1
-        __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        if (cur + NST - 1 < steps) issue(cur + NST - 1, (cur + NST - 1) % NST);
-        if (q0 >= C) continue;                 // a wave without queries only loads
-        const int p = p0 + cur;
-        const bool bok = tbl[cur] >= 0;
-        const uint8_t *S = ring + (cur % NST) * stage;
-        const uint8_t *rk = S, *rv = S + a.ref_rec;
-        const uint8_t *sk = S + 2 * a.ref_rec, *sv = sk + a.res_rec;
-        // ---- loads: K codes of token x (operand role), metadata of tokens 4kb..4kb+3, V codes
-        KChunk<D, 4> kr;
-        load_k<D, 4>(kr, rk + x * (D / 2) + kb * (D / 8));
-        float skr[4], zkr[4], svr[4], zvr[4];
-        load_sz4<MF>(rk + code_ref + 4 * kb * 2 * MSZ, skr, zkr);
-        load_sz4<MF>(rv + code_ref + 4 * kb * 2 * MSZ, svr, zvr);
-        VWords<D, 4> vr;
-        load_v<D, 4>(vr, rv, lane);
-        KChunk<D, RB ? RB : 2> ks;
-        VWords<D, RB ? RB : 2> vs;
-        float sks[4], zks[4], aks[4], svs[4], zvs[4], avs[4];
-        if constexpr (RB != 0) {
-            load_k<D, RB>(ks, sk + x * (D * RB / 8) + kb * (D * RB / 32));
-            load_sz4<MF>(sk + code_res + 4 * kb * 2 * MSZ, sks, zks);
-            load_a4<MF>(sk + code_res + a.meta_bytes + 4 * kb * MSZ, aks);
-            load_sz4<MF>(sv + code_res + 4 * kb * 2 * MSZ, svs, zvs);
-            load_a4<MF>(sv + code_res + a.meta_bytes + 4 * kb * MSZ, avs);
-            load_v<D, RB>(vs, sv, lane);
-        }
-        // ---- scores^T: rows = tokens, columns = queries
-        floatx4 sr = {0.f, 0.f, 0.f, 0.f}, ss = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < NK; ++s) sr = mfma_bf16k(kpairs<4>(kstep<4>(kr.w, s)), qa[s], sr);
-        if constexpr (RB != 0) {
-#pragma unroll
-            for (int s = 0; s < NK; ++s) {
-                const uint2 kp = kpairs<RB>(kstep<RB>(ks.w, s));
-                ss = mfma_bf16k(kp, qh[s], ss);
-                ss = mfma_bf16k(kp, ql[s], ss);
+    // pages in blocks of kChunkFold; the zero terms are folded into the
+    // accumulators after each block (see below)
+    for (int cb = 0; cb < steps; cb += kChunkFold) {
+        const int ce = min(steps, cb + kChunkFold);
+        for (int cur = cb; cur < ce; ++cur) {
+            // this wave's loads of page `cur` have landed ...
+            wait_steps<NST - 2, NI>(min(NST - 2, steps - 1 - cur));
+            // ... and every other wave's; all waves are done with page cur-1
+            __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            if (cur + NST - 1 < steps) issue(cur + NST - 1, (cur + NST - 1) % NST);
+            if (q0 >= C) continue;                 // a wave without queries only loads
+            const int p = p0 + cur;
+            const bool bok = tbl[cur] >= 0;
+            const uint8_t *S = ring + (cur % NST) * stage;
+            const uint8_t *rk = S, *rv = S + a.ref_rec;
+            const uint8_t *sk = S + 2 * a.ref_rec, *sv = sk + a.res_rec;
+            // ---- loads: K codes of token x (operand role), metadata of tokens 4kb..4kb+3, V codes
+            KChunk<D, 4> kr;
+            load_k<D, 4>(kr, rk + x * (D / 2) + kb * (D / 8));
+            float skr[4], zkr[4], svr[4], zvr[4];
+            load_sz4<MF>(rk + code_ref + 4 * kb * 2 * MSZ, skr, zkr);
+            load_sz4<MF>(rv + code_ref + 4 * kb * 2 * MSZ, svr, zvr);
+            VWords<D, 4> vr;
+            load_v<D, 4>(vr, rv, lane);
+            KChunk<D, RB ? RB : 2> ks;
+            VWords<D, RB ? RB : 2> vs;
+            float sks[4], zks[4], aks[4], svs[4], zvs[4], avs[4];
+            if constexpr (RB != 0) {
+                load_k<D, RB>(ks, sk + x * (D * RB / 8) + kb * (D * RB / 32));
+                load_sz4<MF>(sk + code_res + 4 * kb * 2 * MSZ, sks, zks);
+                load_a4<MF>(sk + code_res + a.meta_bytes + 4 * kb * MSZ, aks);
+                load_sz4<MF>(sv + code_res + 4 * kb * 2 * MSZ, svs, zvs);
+                load_a4<MF>(sv + code_res + a.meta_bytes + 4 * kb * MSZ, avs);
+                load_v<D, RB>(vs, sv, lane);
             }
-        }
-        float sc[4];
-        float pmax = kNegInf;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 16 * p + 4 * kb + r;
-            float v = skr[r] * sr[r] + fmaf(-16.f, skr[r], zkr[r]) * sum_q;
-            if constexpr (RB != 0) v = aks[r] * v + (sks[r] * ss[r] + fmaf(-16.f, sks[r], zks[r]) * sum_r);
-            v *= a.score_scale;
-            sc[r] = (bok && t < seq && qok) ? v : kNegInf;
-            pmax = fmaxf(pmax, sc[r]);
-        }
-        // ---- online softmax per query (lanes x, x+16, x+32, x+48 share query x)
-        pmax = fmaxf(pmax, __shfl_xor(pmax, 16, 64));
-        pmax = fmaxf(pmax, __shfl_xor(pmax, 32, 64));
-        if (__any(pmax > m + kThreshC)) {
-            const float mn = fmaxf(m, pmax);
-            const float f = (mn == kNegInf) ? 1.f : fast_exp2(m - mn);
-            lsum *= f; zr *= f; zs *= f;
-            m = mn;
-            // accumulator rows are queries 4kb + v: their factors come from lanes 4kb + v
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const float fv = __shfl(f, 4 * kb + v, 64);
-#pragma unroll
-                for (int i = 0; i < NK; ++i) {
-                    vacc_r[i][v] *= fv;
-                    if constexpr (RB != 0) vacc_s[i][v] *= fv;
+            // ---- scores^T: rows = tokens, columns = queries
+            floatx4 sr = {0.f, 0.f, 0.f, 0.f}, ss = {0.f, 0.f, 0.f, 0.f};
+    #pragma unroll
+            for (int s = 0; s < NK; ++s) sr = mfma_bf16k(kpairs<4>(kstep<4>(kr.w, s)), qa[s], sr);
+            if constexpr (RB != 0) {
+    #pragma unroll
+                for (int s = 0; s < NK; ++s) {
+                    const uint2 kp = kpairs<RB>(kstep<RB>(ks.w, s));
+                    ss = mfma_bf16k(kp, qh[s], ss);
+                    ss = mfma_bf16k(kp, ql[s], ss);
                 }
             }
-        }
-        float wr[4], ws[4];
-        float zsum_r = 0.f, zsum_s = 0.f;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float pr = (sc[r] == kNegInf) ? 0.f : fast_exp2(sc[r] - m);
-            lsum += pr;
-            const float av = RB != 0 ? avs[r] : 1.f;
-            wr[r] = pr * av * svr[r];
-            zsum_r = fmaf(pr * av, zvr[r], zsum_r);
+            float sc[4];
+            float pmax = kNegInf;
+    #pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * p + 4 * kb + r;
+                float v = skr[r] * sr[r] + fmaf(-16.f, skr[r], zkr[r]) * sum_q;
+                if constexpr (RB != 0) v = aks[r] * v + (sks[r] * ss[r] + fmaf(-16.f, sks[r], zks[r]) * sum_r);
+                v *= a.score_scale;
+                sc[r] = (bok && t < seq && qok) ? v : kNegInf;
+                pmax = fmaxf(pmax, sc[r]);
+            }
+            // ---- online softmax per query (lanes x, x+16, x+32, x+48 share query x)
+            pmax = fmaxf(pmax, __shfl_xor(pmax, 16, 64));
+            pmax = fmaxf(pmax, __shfl_xor(pmax, 32, 64));
+            if (__any(pmax > m + kThreshC)) {
+                const float mn = fmaxf(m, pmax);
+                const float f = (mn == kNegInf) ? 1.f : fast_exp2(m - mn);
+                lsum *= f; zr *= f; zs *= f;
+                m = mn;
+                // accumulator rows are queries 4kb + v: their factors come from lanes 4kb + v
+    #pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const float fv = __shfl(f, 4 * kb + v, 64);
+    #pragma unroll
+                    for (int i = 0; i < NK; ++i) {
+                        vacc_r[i][v] *= fv;
+                        if constexpr (RB != 0) vacc_s[i][v] *= fv;
+                    }
+                }
+            }
+            float wr[4], ws[4];
+            float zsum_r = 0.f, zsum_s = 0.f;
+    #pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float pr = (sc[r] == kNegInf) ? 0.f : fast_exp2(sc[r] - m);
+                lsum += pr;
+                const float av = RB != 0 ? avs[r] : 1.f;
+                wr[r] = pr * av * svr[r];
+                zsum_r = fmaf(pr * av, zvr[r], zsum_r);
+                if constexpr (RB != 0) {
+                    ws[r] = pr * svs[r];
+                    zsum_s = fmaf(pr, zvs[r], zsum_s);
+                }
+            }
+            uint2 ahi, alo;
+            float used;
+            split4(wr, ahi, alo, used);
+            zr += zsum_r - 16.f * used;
+            v_mfma2<D, 4>(vacc_r, vr, ahi, alo);
             if constexpr (RB != 0) {
-                ws[r] = pr * svs[r];
-                zsum_s = fmaf(pr, zvs[r], zsum_s);
+                split4(ws, ahi, alo, used);
+                zs += zsum_s - 16.f * used;
+                v_mfma2<D, RB>(vacc_s, vs, ahi, alo);
             }
         }
-        uint2 ahi, alo;
-        float used;
-        split4(wr, ahi, alo, used);
-        zr += zsum_r - 16.f * used;
-        v_mfma2<D, 4>(vacc_r, vr, ahi, alo);
-        if constexpr (RB != 0) {
-            split4(ws, ahi, alo, used);
-            zs += zsum_s - 16.f * used;
-            v_mfma2<D, RB>(vacc_s, vs, ahi, alo);
+        // After every block of kChunkFold pages the zero terms go into the
+        // accumulators. The products carry the offset 16 of every code, so the
+        // running sums grow (16 + c) s / |value| times faster than the result
+        // and their fp32 rounding would otherwise build up over the whole split
+        // (thousands of tokens); folded, it builds up over one block only.
+        if (q0 < C) {
+            float zq = zr + __shfl_xor(zr, 16, 64);
+            zq += __shfl_xor(zq, 32, 64);
+            float zsq = 0.f;
+            if constexpr (RB != 0) {
+                zsq = zs + __shfl_xor(zs, 16, 64);
+                zsq += __shfl_xor(zsq, 32, 64);
+            }
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const float zrv = __shfl(zq, 4 * kb + v, 64);       // accumulator row v: query 4kb + v
+                const float zsv = RB != 0 ? __shfl(zsq, 4 * kb + v, 64) : 0.f;
+#pragma unroll
+                for (int i = 0; i < NK; ++i) {
+                    vacc_r[i][v] += zrv;
+                    if constexpr (RB != 0) vacc_s[i][v] += zsv;
+                }
+            }
+            zr = 0.f;
+            zs = 0.f;
         }
     }
 

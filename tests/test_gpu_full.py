@@ -6,7 +6,10 @@ sample of (sequence, head) pairs is then recomputed by the oracle one by one
 from the same generator draws: their packed records must match the oracle's
 encoding (exemption rule of gpu_util) and their attention outputs, per-loop
 calls and one multi-loop call, must match the oracle's attention over the
-oracle's own packed bytes."""
+oracle's own packed bytes. Where chunked prefill is supported (group =
+head, bf16 K/V) a chunk of 64 new tokens per sequence (the benchmark's
+chunk) is run for every loop in the library's split configuration and the
+sampled pairs are checked against the oracle's chunk attention."""
 import time
 
 import numpy as np
@@ -76,6 +79,30 @@ def test_full_size_sampled(key):
         d = (multi[l] - outs[l]).abs().max().item()
         _log(f"multi-loop vs single call, loop {l}: max-abs {d:.2e}")
         assert d <= 5e-5
+    # chunked prefill over the same cache: C new tokens per sequence, every loop
+    chunk = None
+    if w.group_size == D and w.kv_dtype == "bf16":
+        C = 64
+        ck = T.empty((L, B, C, H, D), dtype=kvdt, device=dev())
+        cv = T.empty_like(ck)
+        for b in range(B):
+            kvc = W.kv_torch(w, 0, b, st, dev(), tok0=N, ntok=C)     # [L][2][C][H][D]
+            ck[:, b] = kvc[:, 0]
+            cv[:, b] = kvc[:, 1]
+            del kvc
+        gen = T.Generator(device=dev())
+        gen.manual_seed(int(np.random.SeedSequence([w.seed, 0, 11]).generate_state(1)[0]))
+        qc = (T.randn((L, B, C, H, D), generator=gen, device=dev()) / float(np.sqrt(D))).to(T.bfloat16)
+        wsc = T.empty(R.chunk_workspace_bytes(lay, C, B, table.shape[1]), dtype=T.uint8, device=dev())
+        couts = []
+        for l in range(L):
+            out = T.empty((B, C, H, D), device=dev())
+            R.chunk_attention(lay, pool, l, qc[l].contiguous(), rot, d_table, d_seq, ck[l].contiguous(),
+                              cv[l].contiguous(), tau, out, wsc)
+            couts.append(out)
+        T.cuda.synchronize()
+        chunk = (to_host64(qc), to_host64(ck), to_host64(cv), couts)
+        _log("chunked prefill done")
     npages = -(-N // 16)
     slab = R.pool_bytes(lay) // (nblk * H)
     pool3 = pool.view(nblk, H, slab)
@@ -100,6 +127,13 @@ def test_full_size_sampled(key):
             e, r = check_attention(f"{w.name} b{b} h{h} loop {l}", got, want)
             em, rm = check_attention(f"{w.name} b{b} h{h} loop {l} multi", multi[l, b, h].cpu().numpy(), want)
             _log(f"b{b} h{h} loop {l}: max-abs {e:.2e} rel-L2 {r:.2e}; multi-loop {em:.2e} {rm:.2e}")
+            if chunk is not None:
+                qc_h, ck_h, cv_h, couts = chunk
+                wc = O.chunk_attention(ref_pool, mini, l, qc_h[l, b:b + 1, :, h:h + 1], rot_h, mtable, [N], tau,
+                                       ck_h[l, b:b + 1, :, h:h + 1], cv_h[l, b:b + 1, :, h:h + 1])[0, :, 0]
+                gc = couts[l][b, :, h].cpu().numpy()
+                ec, rc = check_attention(f"{w.name} b{b} h{h} loop {l} chunk", gc, wc)
+                _log(f"b{b} h{h} loop {l}: chunk of {gc.shape[0]} max-abs {ec:.2e} rel-L2 {rc:.2e}")
     check_caps(stats)
     _log(f"encode stats {stats}")
     for l in range(L):
