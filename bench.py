@@ -267,6 +267,31 @@ def timed(fn, steps, warmup):
     return (time.perf_counter() - t0) / steps
 
 
+def graph_leg(w, rq, split_pages, layers, steps, warmup):
+    """The per-loop step of `layers` layers captured in one HIP graph and
+    replayed. Every layer's calls go to the one packed cache (each call streams
+    its full records, far beyond any cache), so the replay times the same work
+    as `layers` distinct layers."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(layers):
+            rq_step(w, rq, split_pages)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(layers):
+            rq_step(w, rq, split_pages)
+    torch.cuda.synchronize()
+    t = timed(lambda k: g.replay(), steps, warmup)
+    del g
+    return {"layers": layers, "ms_per_replay": t * 1e3, "ms_per_layer_step": t * 1e3 / layers,
+            "tokens_per_s_one_layer": w.batch / (t / layers),
+            "step": f"{layers} layers x (4 per-loop decode calls + encode of {w.batch} new tokens), one graph"}
+
+
 def cpu_baseline(w, rq, budget_s=12.0):
     """The fp64 oracle on a bounded sample: decode attention of one (sequence,
     head) unit per loop, repeated over units until the budget is spent, plus
@@ -350,6 +375,8 @@ def main():
     ap.add_argument("--no-direct", action="store_true", help="skip the direct per-loop quantization baselines")
     ap.add_argument("--chunk", type=int, default=64,
                     help="queries per sequence of the chunked-prefill leg (0 skips it)")
+    ap.add_argument("--graph-layers", type=int, default=4,
+                    help="layers of the per-loop step captured in one HIP graph for the graph leg (0 skips it)")
     ap.add_argument("--separate-encode", action="store_true",
                     help="compress the new tokens in a launch of their own after the attention calls "
                          "instead of in the reference-loop call's launch")
@@ -440,6 +467,17 @@ def main():
         multi_bytes += L * 2 * B * H * D * kvsz + B * H * stored
     multi_gbs = multi_bytes / (multi_ms * 1e-3) / 1e9
     log(f"multi-loop step {t_multi * 1e3:.3f} ms; multi-loop kernel {multi_ms:.3f} ms ({multi_gbs:.0f} GB/s)")
+
+    graph = None
+    if args.graph_layers > 0:
+        log(f"timing the per-loop step of {args.graph_layers} layers replayed from one HIP graph")
+        try:
+            graph = graph_leg(w, rq, sp_loop, args.graph_layers, args.steps, args.warmup)
+            graph["eager_ms_per_step"] = t_rq * 1e3
+            log(f"graph replay {graph['ms_per_layer_step']:.3f} ms per layer step (eager {t_rq * 1e3:.3f} ms)")
+        except Exception as e:          # graph capture unavailable: report it and go on
+            log(f"graph leg failed: {e}")
+            graph = {"error": str(e)[:300]}
 
     chunked = None
     if args.chunk > 0:
@@ -566,6 +604,7 @@ def main():
                        "kernel_gbs": multi_gbs,
                        "kernel_frac_of_peak": multi_gbs / HBM_PEAK_GBS},
         "chunked_prefill": chunked,
+        "graph": graph,
         "bf16_baseline": bf16,
         "direct_baselines": direct or None,
         "attention_rel_l2_vs_bf16": errors or None,
