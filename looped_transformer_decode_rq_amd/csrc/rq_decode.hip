@@ -89,17 +89,22 @@ __global__ __launch_bounds__(1024) void rq_qprep_kernel(QPrepArgs a) {
     const bool row_ok = b < B;
 
     // q' = R_K q for the 16 rows: [16 x D] x R_K^T. v_mfma_f32_16x16x4f32:
-    // lane l supplies A[l%16][k0 + l/16], B[k0 + l/16][l%16] and receives
-    // D[4*(l/16)+v][l%16]; wave r computes columns 16r..16r+15. This lane's
-    // B operands (a column slice of R_K) are loaded first, so that their
-    // latency overlaps the query loads.
+    // lane l supplies A[l%16][k], B[k][l%16] for its k-slot l/16 and receives
+    // D[4*(l/16)+v][l%16]; wave r computes columns 16r..16r+15. Step kk gives
+    // slot k0 = l/16 the channel k = (D/4) k0 + kk, so that a lane's B
+    // operands are D/4 consecutive floats of row n of R_K (vector loads).
+    // They are loaded first, so that their latency overlaps the query loads.
     const bool rot_wave = rb != 0 && r < D / 16;
     const int n = r * 16 + (lane & 15);
     float rk[D / 4];
     if (rot_wave) {
-        const float *RK = a.rot + ((int64_t)h * 2 + 0) * D * D + (int64_t)n * D + (lane >> 4);
+        const float4 *RK = (const float4 *)(a.rot + ((int64_t)h * 2 + 0) * D * D + (int64_t)n * D +
+                                            (lane >> 4) * (D / 4));
 #pragma unroll
-        for (int kk = 0; kk < D / 4; ++kk) rk[kk] = RK[4 * kk];
+        for (int k4 = 0; k4 < D / 16; ++k4) {
+            const float4 v = RK[k4];
+            rk[4 * k4] = v.x; rk[4 * k4 + 1] = v.y; rk[4 * k4 + 2] = v.z; rk[4 * k4 + 3] = v.w;
+        }
     }
     for (int c = lane; c < D; c += 64)
         Q[r * QS + c] = row_ok ? load_kv<KV_F32>(a.q, (((int64_t)i * B + b) * H + h) * D + c) : 0.0f;
@@ -108,7 +113,7 @@ __global__ __launch_bounds__(1024) void rq_qprep_kernel(QPrepArgs a) {
         floatx4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < D / 4; ++kk) {
-            const int k = 4 * kk + (lane >> 4);
+            const int k = (lane >> 4) * (D / 4) + kk;
             c = __builtin_amdgcn_mfma_f32_16x16x4f32(Q[(lane & 15) * QS + k], rk[kk], c, 0, 0, 0);
         }
         for (int v = 0; v < 4; ++v) QR[(4 * (lane >> 4) + v) * QS + n] = c[v];
@@ -150,6 +155,7 @@ __global__ __launch_bounds__(1024) void rq_qprep_kernel(QPrepArgs a) {
     __syncthreads();
     if (!row_ok) return;
     uint8_t *qp = a.qpack + (((int64_t)i * B + b) * H + h) * qpack_bytes(D);
+    const int c0q = lane;
     // limb dwords: [q4][k][limb], nibble n = channel limb_channel(q4,k,n)
     for (int which = 0; which < 2; ++which) {
         if (which == 1 && rb == 0) break;
@@ -166,12 +172,18 @@ __global__ __launch_bounds__(1024) void rq_qprep_kernel(QPrepArgs a) {
             ((uint32_t *)(qp + 64 + which * 2 * D))[dw] = word;
         }
     }
-    if (lane < 2 * Ln::LPT) {
-        const int which = lane / Ln::LPT, q4 = lane % Ln::LPT;
-        int sum = 0;
-        if (which == 0 || rb != 0)
-            for (int c = q4 * Ln::CPL; c < (q4 + 1) * Ln::CPL; ++c) sum += QI[r][which][c];
-        ((int *)(qp + 16 + 16 * which))[q4] = sum;
+    // per (which, q4): the sum of the fixed-point values of the q4 lanes'
+    // channels, as wave sums (|sum| < 2^24: exact in fp32)
+    for (int which = 0; which < 2; ++which) {
+        const bool on = which == 0 || rb != 0;
+        const int v0 = (on && c0q < D) ? QI[r][which][c0q] : 0;
+        const int v1 = (on && c0q + 64 < D) ? QI[r][which][c0q + 64] : 0;
+#pragma unroll
+        for (int t = 0; t < Ln::LPT; ++t) {
+            const float part = (float)((c0q / Ln::CPL == t ? v0 : 0) + ((c0q + 64) / Ln::CPL == t ? v1 : 0));
+            const float tot = wave_sum(part);
+            if (lane == 0) ((int *)(qp + 16 + 16 * which))[t] = (int)tot;
+        }
     }
     if (lane == 0) {
         ((float *)qp)[0] = ldexpf(1.0f, -S[0]);
