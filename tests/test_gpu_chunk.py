@@ -3,9 +3,10 @@ against the fp64 oracle's chunk_attention, on the oracle's packed bytes.
 
 Cases: an Ouro-like layer (D128, G128, INT2 residuals) with a ragged context
 and shuffled table, and a Huginn-like one (D96, G96, INT4 and INT2 residual
-loops); chunks of 1..100 queries, with and without the chunk's own K/V, split
-sizes chosen by the library and forced small; empty caches; C = 1 against
-decode attention; the supported-layout check.
+loops); chunks of 1..256 queries (256 is the largest chunk), with and without
+the chunk's own K/V, split sizes chosen by the library, forced small and the
+largest (1024 pages: one split); empty caches; C = 1 against decode attention;
+the supported-layout check.
 """
 import numpy as np
 import pytest
@@ -59,7 +60,7 @@ def run_chunk(c, pool, loop, q, ck, cv, split_pages=0):
 
 
 @pytest.mark.parametrize("name", list(CASES))
-@pytest.mark.parametrize("C,split_pages", [(1, 0), (16, 0), (37, 3), (64, 1), (100, 0)])
+@pytest.mark.parametrize("C,split_pages", [(1, 0), (16, 0), (37, 3), (64, 1), (100, 0), (256, 1024)])
 def test_chunk_matches_oracle(name, C, split_pages):
     c = case(name)
     pool = c.device_pool_from_oracle()
