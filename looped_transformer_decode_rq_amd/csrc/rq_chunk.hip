@@ -148,9 +148,20 @@ __device__ __forceinline__ uint2 kpairs(uint32_t u) {
     return make_uint2(b0, b1);
 }
 
-__device__ __forceinline__ floatx4 mfma_bf16k(uint2 a, uint2 b, floatx4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(shortx4, a), __builtin_bit_cast(shortx4, b),
-                                                     c, 0, 0, 0);
+// 16x16x32 products: a lane's eight k values of A and of B are two 16x16x16
+// operands side by side (the matrix cores pair element e of A with element e
+// of B within a lane group, so any split of k between the halves works)
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ floatx4 mfma_bf16k32(uint2 a0, uint2 a1, uint2 b0, uint2 b1, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, make_uint4(a0.x, a0.y, a1.x, a1.y)),
+                                                   __builtin_bit_cast(bf16x8, make_uint4(b0.x, b0.y, b1.x, b1.y)), c,
+                                                   0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mfma_f16k32(uint2 a0, uint2 a1, uint2 b0, uint2 b1, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(halfx8, make_uint4(a0.x, a0.y, a1.x, a1.y)),
+                                                  __builtin_bit_cast(halfx8, make_uint4(b0.x, b0.y, b1.x, b1.y)), c,
+                                                  0, 0, 0);
 }
 
 // This lane's K codes of one token: D*BITS/32 bytes (channels kb*D/4 ..
@@ -236,15 +247,15 @@ __device__ __forceinline__ void split4(const float *win, uint2 &hi, uint2 &lo, f
 }
 
 // acc[m] += Ahi x B_m + Alo x B_m for every column group m, one operand
-// expansion for both terms
+// expansion and one 16x16x32 product for both terms (k: the tokens' hi
+// weights, then their lo weights against the same codes)
 template <int WP, int BITS, int I>
 __device__ __forceinline__ void v_mfma2_word(floatx4 *acc, uint32_t w, uint2 ahi, uint2 alo, uint32_t vmask,
                                              uint32_t exp16) {
     if constexpr (I < WP) {
         const uint32_t b0 = vpair<BITS * I>(w, vmask, exp16);
         const uint32_t b1 = vpair<BITS * (WP + I)>(w, vmask, exp16);
-        acc[I] = mfma_f16(ahi, b0, b1, acc[I]);
-        acc[I] = mfma_f16(alo, b0, b1, acc[I]);
+        acc[I] = mfma_f16k32(ahi, alo, make_uint2(b0, b1), make_uint2(b0, b1), acc[I]);
         v_mfma2_word<WP, BITS, I + 1>(acc, w, ahi, alo, vmask, exp16);
     }
 }
@@ -407,13 +418,13 @@ __global__ __launch_bounds__(256) void rq_chunk_split_kernel(ChunkArgs a) {
             // ---- scores^T: rows = tokens, columns = queries
             floatx4 sr = {0.f, 0.f, 0.f, 0.f}, ss = {0.f, 0.f, 0.f, 0.f};
     #pragma unroll
-            for (int s = 0; s < NK; ++s) sr = mfma_bf16k(kpairs<4>(kstep<4>(kr.w, s)), qa[s], sr);
+            for (int s = 0; s < NK; s += 2)      // two k-steps per product
+                sr = mfma_bf16k32(kpairs<4>(kstep<4>(kr.w, s)), kpairs<4>(kstep<4>(kr.w, s + 1)), qa[s], qa[s + 1], sr);
             if constexpr (RB != 0) {
     #pragma unroll
                 for (int s = 0; s < NK; ++s) {
                     const uint2 kp = kpairs<RB>(kstep<RB>(ks.w, s));
-                    ss = mfma_bf16k(kp, qh[s], ss);
-                    ss = mfma_bf16k(kp, ql[s], ss);
+                    ss = mfma_bf16k32(kp, kp, qh[s], ql[s], ss);     // the hi and lo query terms
                 }
             }
             float sc[4];
