@@ -110,12 +110,14 @@ __global__ __launch_bounds__(1024) void rq_qprep_kernel(QPrepArgs a) {
         Q[r * QS + c] = row_ok ? load_kv<KV_F32>(a.q, (((int64_t)i * B + b) * H + h) * D + c) : 0.0f;
     __syncthreads();
     if (rot_wave) {
-        floatx4 c = {0.f, 0.f, 0.f, 0.f};
+        // four independent accumulation chains (the products' latency overlaps)
+        floatx4 c4[4] = {};
 #pragma unroll
         for (int kk = 0; kk < D / 4; ++kk) {
             const int k = (lane >> 4) * (D / 4) + kk;
-            c = __builtin_amdgcn_mfma_f32_16x16x4f32(Q[(lane & 15) * QS + k], rk[kk], c, 0, 0, 0);
+            c4[kk & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(Q[(lane & 15) * QS + k], rk[kk], c4[kk & 3], 0, 0, 0);
         }
+        const floatx4 c = (c4[0] + c4[1]) + (c4[2] + c4[3]);
         for (int v = 0; v < 4; ++v) QR[(4 * (lane >> 4) + v) * QS + n] = c[v];
     }
     __syncthreads();
@@ -1276,12 +1278,14 @@ __global__ __launch_bounds__(1024) void rq_combine_kernel(CombineArgs a) {
         // v_mfma_f32_16x16x4f32: lane l supplies A[l%16][k0 + l/16], B[k0 + l/16][l%16]
         // and receives D[4*(l/16)+v][l%16]; wave r computes output columns 16r..16r+15.
         if (rot_wave) {
-            floatx4 c = {0.f, 0.f, 0.f, 0.f};
+            // four independent accumulation chains (the products' latency overlaps)
+            floatx4 c4[4] = {};
 #pragma unroll
             for (int kk = 0; kk < D / 4; ++kk) {
                 const int k = 4 * kk + (lane >> 4);
-                c = __builtin_amdgcn_mfma_f32_16x16x4f32(A[(lane & 15) * QS + k], rv[kk], c, 0, 0, 0);
+                c4[kk & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(A[(lane & 15) * QS + k], rv[kk], c4[kk & 3], 0, 0, 0);
             }
+            const floatx4 c = (c4[0] + c4[1]) + (c4[2] + c4[3]);
             for (int v = 0; v < 4; ++v) {
                 const int rr = 4 * (lane >> 4) + v;
                 const int bb = tile * 16 + rr;
