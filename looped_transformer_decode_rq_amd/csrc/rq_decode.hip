@@ -867,6 +867,7 @@ struct MultiArgs {
     int H, nblk;
     int ref_off, ref_rec;
     int nl;                                   // loop calls of this group = waves per workgroup
+    int nres;                                 // calls with a residual (rb != 0): private residual rings
     int res_off[kMaxMultiLoops], res_rec[kMaxMultiLoops], rb[kMaxMultiLoops];   // rb 0: reference loop
     const int32_t *block_table;
     int max_blocks;
@@ -980,8 +981,12 @@ __global__ __launch_bounds__(64 * kMaxMultiLoops) void rq_multi_kernel(MultiArgs
     // rows and two of rescale factors
     const int ref_stage = MG::REF_BYTES, res_stage = MG::RES_MAX;
     uint8_t *ref_base = smem;
-    uint8_t *res_base = smem + nst * ref_stage + wave * nst * res_stage;
-    const uint32_t junk = lds_addr(smem + nst * (ref_stage + nl * res_stage) + 16 * wave);
+    // residual rings only for the calls with a residual (index ri among them)
+    int ri = 0;
+    for (int c = 0; c < call; ++c) ri += a.rb[c] != 0 ? 1 : 0;
+    uint8_t *res_base = smem + nst * ref_stage + ri * nst * res_stage;
+    const int ring_bytes = nst * (ref_stage + a.nres * res_stage);
+    const uint32_t junk = lds_addr(smem + ring_bytes + 16 * wave);
 
     // this wave's share of the reference pieces [r0, r0 + rcount)
     const int rq = (MG::P_REF + nl - 1) / nl;
@@ -1053,8 +1058,8 @@ __global__ __launch_bounds__(64 * kMaxMultiLoops) void rq_multi_kernel(MultiArgs
     SplitState<D> s;
     init_state<D>(s);
     // this wave's weight scratch (after the padding slots)
-    uint8_t *wsc = smem + nst * (ref_stage + nl * res_stage) + 16 * nl + wave * PPI * kWScratch;
-    uint8_t *sha = smem + nst * (ref_stage + nl * res_stage) + nl * (16 + PPI * kWScratch);
+    uint8_t *wsc = smem + ring_bytes + 16 * nl + wave * PPI * kWScratch;
+    uint8_t *sha = smem + ring_bytes + nl * (16 + PPI * kWScratch);
     float *fbuf = (float *)(sha + 2 * PPI * kWScratch);
     if constexpr (SH) {
         // rows past the last loop's pairs are never written: zero them once
@@ -1363,14 +1368,14 @@ hipError_t launch_multi_g(const MultiArgs &m, bool sh, int G, dim3 grid, size_t 
 }
 
 // LDS bytes of one multi-loop ring slot (shared reference stage plus one
-// residual stage per wave)
+// residual stage per call with a residual, nres of them)
 template <int D, bool MF, int RBMAX>
-int multi_slot_bytes(int G, int nl) {
+int multi_slot_bytes(int G, int nres) {
     const int msz = MF ? 4 : 2, ppi = Lanes<D>::PPI;
     const int mb = 16 * (D / G) * 2 * msz, ab = 16 * msz;
     const int ref = 2 * ppi * (16 * D / 2) + ppi * 2 * mb;
     const int res = 2 * ppi * (16 * D * RBMAX / 8) + ppi * 2 * (mb + ab);
-    return ref + nl * res;
+    return ref + nres * res;
 }
 
 // LDS bytes of the multi-loop kernel outside its ring: one 16-byte padding
@@ -1433,8 +1438,8 @@ int multi_occ(int G, int nl, bool sh) {
 // kernel's registers and wave slots admit (LDS then never lowers the
 // occupancy), at most 64 KB; a ring of fewer than 3 stages takes 64 KB.
 template <int D, bool MF, int RBMAX>
-int multi_ring_depth(int G, int nl, bool sh) {
-    const int fixed = multi_fixed_bytes<D>(nl, sh), slot = multi_slot_bytes<D, MF, RBMAX>(G, nl);
+int multi_ring_depth(int G, int nl, int nres, bool sh) {
+    const int fixed = multi_fixed_bytes<D>(nl, sh), slot = multi_slot_bytes<D, MF, RBMAX>(G, nres);
     const int budget = std::min(64 * 1024, lds_per_cu() / multi_occ<D, MF, RBMAX>(G, nl, sh));
     const int d = (budget - fixed) / slot;
     return std::min(8, d >= 3 ? d : (64 * 1024 - fixed) / slot);
@@ -1470,8 +1475,10 @@ hipError_t launch_decode_d(const DecodeCall &c) {
         bool any4 = false;
         for (int i = 0; i < c.n; ++i) any4 = any4 || (c.loops[i] != ref && g.bits[c.loops[i]] == 4);
         auto depth = [&](int nl) {
-            if (mf) return any4 ? multi_ring_depth<D, true, 4>(g.G, nl, false) : multi_ring_depth<D, true, 2>(g.G, nl, false);
-            return any4 ? multi_ring_depth<D, false, 4>(g.G, nl, false) : multi_ring_depth<D, false, 2>(g.G, nl, false);
+            if (mf) return any4 ? multi_ring_depth<D, true, 4>(g.G, nl, nl, false)
+                                : multi_ring_depth<D, true, 2>(g.G, nl, nl, false);
+            return any4 ? multi_ring_depth<D, false, 4>(g.G, nl, nl, false)
+                        : multi_ring_depth<D, false, 2>(g.G, nl, nl, false);
         };
         int nl_max = 3;
         for (int nl = std::min(c.n, kMaxMultiLoops); nl > 3; --nl)
@@ -1499,13 +1506,17 @@ hipError_t launch_decode_d(const DecodeCall &c) {
             m.partials = c.partials + (int64_t)first * c.B * g.H * c.nparts * partial_floats(D);
             m.B = c.B; m.nsplit = c.nsplit; m.split_pages = c.split_pages;
             m.score_scale = score_scale;
+            const int nres = nl - nref;
+            m.nres = nres;
             int slot;
             auto ring = [&](bool sh) {
-                if (mf) return g4 ? multi_ring_depth<D, true, 4>(g.G, nl, sh) : multi_ring_depth<D, true, 2>(g.G, nl, sh);
-                return g4 ? multi_ring_depth<D, false, 4>(g.G, nl, sh) : multi_ring_depth<D, false, 2>(g.G, nl, sh);
+                if (mf) return g4 ? multi_ring_depth<D, true, 4>(g.G, nl, nres, sh)
+                                  : multi_ring_depth<D, true, 2>(g.G, nl, nres, sh);
+                return g4 ? multi_ring_depth<D, false, 4>(g.G, nl, nres, sh)
+                          : multi_ring_depth<D, false, 2>(g.G, nl, nres, sh);
             };
-            if (mf) slot = g4 ? multi_slot_bytes<D, true, 4>(g.G, nl) : multi_slot_bytes<D, true, 2>(g.G, nl);
-            else slot = g4 ? multi_slot_bytes<D, false, 4>(g.G, nl) : multi_slot_bytes<D, false, 2>(g.G, nl);
+            if (mf) slot = g4 ? multi_slot_bytes<D, true, 4>(g.G, nres) : multi_slot_bytes<D, true, 2>(g.G, nres);
+            else slot = g4 ? multi_slot_bytes<D, false, 4>(g.G, nres) : multi_slot_bytes<D, false, 2>(g.G, nres);
             // shared reference rows: the group holds the reference loop (whose
             // wave owns the rows), every (call, group) row pair fits the
             // 16 rows of the A operand, and the ring keeps a stage in flight
