@@ -283,9 +283,11 @@ __device__ __forceinline__ void v_mfma2(floatx4 *acc, const VWords<D, BITS> &v, 
 // as stored (two runs of the slab), filled by direct-to-LDS loads that the
 // waves issue in equal shares kChunkStages-1 pages ahead; one barrier per
 // page publishes the landed stage and frees the oldest one. The split's block
-// ids are preloaded into LDS.
+// ids are preloaded into LDS. Three waves per SIMD (at most 168 registers):
+// with two, the per-page chains of loads, products and softmax left the SIMDs
+// idle; the residual widths then keep a few values in scratch.
 template <int D, int RB, bool MF, int NI>
-__global__ __launch_bounds__(256) void rq_chunk_split_kernel(ChunkArgs a) {
+__global__ __launch_bounds__(256, 3) void rq_chunk_split_kernel(ChunkArgs a) {
     constexpr int NK = D / 16;                 // k-steps of the score product = column groups of V
     constexpr int PF = partial_floats(D);
     constexpr int MSZ = MF ? 4 : 2;
