@@ -42,6 +42,11 @@ namespace {
 
 constexpr float kLog2eC = 1.4426950408889634f;
 constexpr float kThreshC = 8.0f;         // rescale when a score beats the running max by 2^8
+// LDS offset of the q' operand area: after the ring (ring_bytes), the padding
+// slots and the split's block ids, 16-byte aligned
+__host__ __device__ constexpr int chunk_qlds_offset(int ring_bytes, int split_pages) {
+    return (ring_bytes + 64 + 4 * split_pages + 15) & ~15;
+}
 constexpr int kChunkFold = 16;           // pages between folds of the zero terms into the accumulators
 
 // bf16 round-to-nearest-even of a float, as its bits
@@ -346,7 +351,10 @@ __global__ __launch_bounds__(256, 3) void rq_chunk_split_kernel(ChunkArgs a) {
     const int qi = q0 + x;
     const bool qok = qi < C;
     const int64_t qrow = ((int64_t)b * C + (qok ? qi : 0)) * H + h;
-    uint2 qa[NK], qh[NK], ql[NK];
+    // q in registers; the residual's hi/lo terms of q' in this wave's LDS area
+    // ([2][NK][64] operand pairs, read back per page: fewer registers)
+    uint2 qa[NK];
+    uint2 *qlds = (uint2 *)(smem + chunk_qlds_offset(NST * stage, a.split_pages)) + wave * 2 * NK * 64;
     {
         const uint16_t *qp = a.q + qrow * D + kb * (D / 4);
         const uint16_t *hp = (const uint16_t *)(a.qrec + qrow * chunk_qrec_bytes(D) + 16) + kb * (D / 4);
@@ -354,8 +362,8 @@ __global__ __launch_bounds__(256, 3) void rq_chunk_split_kernel(ChunkArgs a) {
         for (int s = 0; s < NK; ++s) {
             qa[s] = qok ? *(const uint2 *)(qp + 4 * s) : make_uint2(0u, 0u);
             if constexpr (RB != 0) {
-                qh[s] = qok ? *(const uint2 *)(hp + 4 * s) : make_uint2(0u, 0u);
-                ql[s] = qok ? *(const uint2 *)(hp + D + 4 * s) : make_uint2(0u, 0u);
+                qlds[s * 64 + lane] = qok ? *(const uint2 *)(hp + 4 * s) : make_uint2(0u, 0u);
+                qlds[(NK + s) * 64 + lane] = qok ? *(const uint2 *)(hp + D + 4 * s) : make_uint2(0u, 0u);
             }
         }
     }
@@ -363,10 +371,7 @@ __global__ __launch_bounds__(256, 3) void rq_chunk_split_kernel(ChunkArgs a) {
     const float sum_r = qok ? ((const float *)(a.qrec + qrow * chunk_qrec_bytes(D)))[1] : 0.f;
     // the query registers are complete before the ring's loads are counted
 #pragma unroll
-    for (int s = 0; s < NK; ++s) {
-        __asm__ volatile("" ::"v"(qa[s].x), "v"(qa[s].y));
-        if constexpr (RB != 0) __asm__ volatile("" ::"v"(qh[s].x), "v"(qh[s].y), "v"(ql[s].x), "v"(ql[s].y));
-    }
+    for (int s = 0; s < NK; ++s) __asm__ volatile("" ::"v"(qa[s].x), "v"(qa[s].y));
     __asm__ volatile("" ::"v"(sum_q), "v"(sum_r));
     wait_vmcnt<0>();
 
@@ -426,7 +431,7 @@ __global__ __launch_bounds__(256, 3) void rq_chunk_split_kernel(ChunkArgs a) {
     #pragma unroll
                 for (int s = 0; s < NK; ++s) {
                     const uint2 kp = kpairs<RB>(kstep<RB>(ks.w, s));
-                    ss = mfma_bf16k32(kp, kp, qh[s], ql[s], ss);     // the hi and lo query terms
+                    ss = mfma_bf16k32(kp, kp, qlds[s * 64 + lane], qlds[(NK + s) * 64 + lane], ss);  // hi, lo terms
                 }
             }
             float sc[4];
@@ -667,8 +672,10 @@ __global__ __launch_bounds__(1024) void rq_chunk_combine_kernel(ChunkCombineArgs
 
 template <int D, int RB>
 hipError_t launch_chunk_split(const ChunkArgs &s, bool mf, dim3 grid, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
-    // ring, padding slots, block ids of one split
-    const size_t lds = (size_t)kChunkStages * s.stage + 64 + 4 * (size_t)s.split_pages;
+    // ring, padding slots, block ids of one split, and for a residual loop the
+    // four waves' q' operands
+    const size_t lds = (size_t)chunk_qlds_offset(kChunkStages * s.stage, s.split_pages) +
+                       (RB != 0 ? 4 * 2 * (D / 16) * 64 * 8 : 0);
     const bool two = s.stage > 4096;           // two direct-to-LDS instructions per wave and page
     if (mf) {
         if (two) hipExtLaunchKernelGGL((rq_chunk_split_kernel<D, RB, true, 2>), grid, dim3(256), (uint32_t)lds, st, e0, e1, 0, s);
