@@ -23,6 +23,10 @@
  *     stream) and the call returns at once.
  *   - On any validation failure the call returns a negative rq_status before
  *     touching memory or enqueuing work. RQ_ERR_HIP reports a failed launch.
+ *   - Calls only enqueue kernels, so a sequence of them can be captured into a
+ *     HIP graph (stream capture) and replayed. The first call on a device also
+ *     queries device attributes (compute units, LDS per CU, kernel occupancy)
+ *     and caches them: make one call on the device before capturing.
  *   - Tensor layouts are C-contiguous (row-major) in the stated index order.
  *   - Device-side indices (block ids, slots, sequence lengths) are clamped
  *     against the pool and table sizes: an out-of-range id never causes an
