@@ -284,7 +284,9 @@ rq_status rq_fit_rotation(const float *samples, int64_t n, int32_t head_dim, int
  *                 both NULL (then only the cache is attended)
  *   out           [B][chunk][H][D] fp32
  * Supported layouts: RQ_MODE_RESIDUAL, group_size == head_dim, kv_dtype bf16;
- * others return RQ_ERR_UNSUPPORTED. opts: split_pages (1..1024, larger is
+ * others return RQ_ERR_UNSUPPORTED, and so do calls whose launch grids would
+ * exceed 65535 in a dimension (splits per sequence; batch * ceil(chunk/64);
+ * ceil(batch * chunk / 16)). opts: split_pages (1..1024, larger is
  * RQ_ERR_UNSUPPORTED; 0 = the library's choice) and timing events bracketing
  * the split kernel.
  * q, chunk_k, chunk_v and the workspace must be 16-byte aligned. */

@@ -288,6 +288,10 @@ def test_chunk_validation(L):
     assert call(rot=None, loop=3, wsb=0) == -4  # the reference loop does not
     assert call(batch=0) == 0
     assert call(opts=ctypes.byref(RqDecodeOpts(-1, 0, None, None))) == -2
+    # launch grids beyond 65535 blocks in a dimension: refused before any launch
+    assert call(batch=65535, C=256, wsb=1 << 62) == -3                     # batch x 64-query groups
+    assert call(batch=8192, C=256, wsb=1 << 62) == -3                      # 16-row tiles
+    assert call(mb=70000, opts=ctypes.byref(RqDecodeOpts(1, 0, None, None)), wsb=1 << 62) == -3   # splits
     # supported layouts only: direct mode, groups smaller than the head, fp32 K/V
     for bad in (R.make_layout(16, 128, 128, 4, (2, 2, 2), 300, "f16", "bf16", mode=R.RQ_MODE_DIRECT),
                 R.make_layout(16, 128, 32, 4, (2, 2, 2), 300, "f16", "bf16"),
