@@ -676,10 +676,14 @@ struct StageGeom {
     static constexpr int NP = BYTES / 16;               // 16-byte pieces
     static constexpr int NI = (NP + 63) / 64;           // direct-to-LDS instructions per stage
     static constexpr int LIVE_LAST = NP - 64 * (NI - 1);
-    // ring depth per wave: three stages when three 4-wave workgroups still
-    // fit in the CU's 160 KB of LDS, else two; the end-of-loop merge reuses
-    // each wave's own stages
-    static constexpr int NST = 3 * kWaves * 3 * BYTES <= 160 * 1024 ? 3 : 2;
+    // ring depth per wave: as deep as four 4-wave workgroups (the register
+    // bound's occupancy) allow in the CU's 160 KB of LDS, up to four stages,
+    // else three when three workgroups fit, else two; the end-of-loop merge
+    // reuses each wave's own stages
+    static constexpr int NST = 4 * kWaves * 4 * BYTES <= 160 * 1024   ? 4
+                               : 4 * kWaves * 3 * BYTES <= 160 * 1024 ? 3
+                               : 3 * kWaves * 3 * BYTES <= 160 * 1024 ? 3
+                                                                      : 2;
     // the step's weight scratch reuses the start of its own slot (the code
     // bytes, read into registers first)
     static_assert(PPI * kWScratch <= O_M, "weight scratch fits in the slot's code bytes");
