@@ -192,6 +192,34 @@ __device__ __forceinline__ void load_k(KChunk<D, BITS> &k, const uint8_t *p) {
     }
 }
 
+// Where the K codes of a page record sit in an LDS stage. The record is token
+// major (token t's D*BITS/8 bytes, then token t+1's), and the 16 lanes that
+// read one channel chunk of 16 tokens would address pieces one token record
+// apart (a 4-way LDS bank conflict for D = 128). The direct-to-LDS loads
+// therefore transpose the code area at 16-byte granularity on the way in:
+// piece c of token t lands at piece 16c + t, so those 16 lanes read 16
+// consecutive pieces. Only where a lane's chunk lies inside one piece (D = 64
+// and 128); for D = 96 the area is copied as stored.
+template <int D, int BITS>
+struct KSwz {
+    static constexpr int CB = D * BITS / 32;          // bytes of one lane's chunk
+    static constexpr int TB = D * BITS / 8;           // bytes of one token's codes
+    static constexpr bool ON = 16 % CB == 0 && TB % 16 == 0;
+    static constexpr int TP = TB / 16;                // pieces per token (when ON)
+    static constexpr int PIECES = ON ? 16 * TP : 0;   // pieces of the code area that move
+    // LDS byte offset of chunk kb of token x from the start of the codes
+    __device__ static int off(int x, int kb) {
+        if constexpr (ON) {
+            const int o = kb * CB;
+            return ((o >> 4) * 16 + x) * 16 + (o & 15);
+        } else {
+            return x * TB + kb * CB;
+        }
+    }
+    // the record's piece that LDS piece j (< PIECES) holds
+    __host__ __device__ static constexpr int src(int j) { return (j & 15) * TP + (j >> 4); }
+};
+
 // the four codes of k-step s
 template <int BITS>
 __device__ __forceinline__ uint32_t kstep(const uint32_t *w, int s) {
@@ -284,8 +312,9 @@ __device__ __forceinline__ void v_mfma2(floatx4 *acc, const VWords<D, BITS> &v, 
 // at channel 16m + x.
 //
 // The four waves share every page: each stage of an LDS ring holds the page's
-// reference K and V records and the loop's residual K and V records exactly
-// as stored (two runs of the slab), filled by direct-to-LDS loads that the
+// reference K and V records and the loop's residual K and V records as
+// stored (two runs of the slab; only the K code areas transposed, see KSwz),
+// filled by direct-to-LDS loads that the
 // waves issue in equal shares kChunkStages-1 pages ahead; one barrier per
 // page publishes the landed stage and frees the oldest one. The split's block
 // ids are preloaded into LDS. Three waves per SIMD (at most 168 registers):
@@ -324,6 +353,8 @@ __global__ __launch_bounds__(256, 3) void rq_chunk_split_kernel(ChunkArgs a) {
 
     // this lane's pieces: instruction j of wave w covers pieces 64*(NI*w + j) + lane
     const int np = stage >> 4, nref = a.ref_rec >> 3;          // 16-byte pieces; of them in the reference run
+    using KR = KSwz<D, 4>;
+    using KS = KSwz<D, RB ? RB : 2>;
     int doff[NI], live[NI], dst[NI];
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
@@ -331,7 +362,12 @@ __global__ __launch_bounds__(256, 3) void rq_chunk_split_kernel(ChunkArgs a) {
         live[j] = max(0, min(64, np - start));
         dst[j] = start * 16;
         const int k = start + lane;
-        doff[j] = k < nref ? a.ref_off + 16 * k : a.res_off + 16 * (k - nref);
+        if (k < nref) {
+            doff[j] = a.ref_off + 16 * (k < KR::PIECES ? KR::src(k) : k);
+        } else {
+            const int kk = k - nref;
+            doff[j] = a.res_off + 16 * (RB != 0 && kk < KS::PIECES ? KS::src(kk) : kk);
+        }
     }
     auto issue = [&](int st, int slot) {
         const int blk = max(__builtin_amdgcn_readfirstlane(tbl[st]), 0);
@@ -405,7 +441,7 @@ __global__ __launch_bounds__(256, 3) void rq_chunk_split_kernel(ChunkArgs a) {
             const uint8_t *sk = S + 2 * a.ref_rec, *sv = sk + a.res_rec;
             // ---- loads: K codes of token x (operand role), metadata of tokens 4kb..4kb+3, V codes
             KChunk<D, 4> kr;
-            load_k<D, 4>(kr, rk + x * (D / 2) + kb * (D / 8));
+            load_k<D, 4>(kr, rk + KR::off(x, kb));
             float skr[4], zkr[4], svr[4], zvr[4];
             load_sz4<MF>(rk + code_ref + 4 * kb * 2 * MSZ, skr, zkr);
             load_sz4<MF>(rv + code_ref + 4 * kb * 2 * MSZ, svr, zvr);
@@ -415,7 +451,7 @@ __global__ __launch_bounds__(256, 3) void rq_chunk_split_kernel(ChunkArgs a) {
             VWords<D, RB ? RB : 2> vs;
             float sks[4], zks[4], aks[4], svs[4], zvs[4], avs[4];
             if constexpr (RB != 0) {
-                load_k<D, RB>(ks, sk + x * (D * RB / 8) + kb * (D * RB / 32));
+                load_k<D, RB>(ks, sk + KS::off(x, kb));
                 load_sz4<MF>(sk + code_res + 4 * kb * 2 * MSZ, sks, zks);
                 load_a4<MF>(sk + code_res + a.meta_bytes + 4 * kb * MSZ, aks);
                 load_sz4<MF>(sv + code_res + 4 * kb * 2 * MSZ, svs, zvs);
