@@ -22,6 +22,12 @@ CASES = {
                                     seq_lens=[203, 17, 160]),
     "huginn_small": lambda: SmallCase(W.get(3).replace(batch=2, heads=3, context=95), shuffled=True,
                                       seq_lens=[95, 0]),
+    # layouts whose K code areas land in LDS transposed: D64 with INT4 and INT2
+    # residuals, and D128 with INT4 residuals
+    "d64_mixed": lambda: SmallCase(W.get(1).replace(batch=2, heads=2, context=70, head_dim=64, group_size=64,
+                                                    res_bits=(4, 2, 2)), shuffled=True, seq_lens=[70, 33]),
+    "d128_int4_res": lambda: SmallCase(W.get(1).replace(batch=2, heads=2, context=90, res_bits=(4, 4, 2)),
+                                       shuffled=True, seq_lens=[90, 41]),
 }
 _cache = {}
 
