@@ -653,15 +653,28 @@ __global__ __launch_bounds__(1024) void rq_chunk_combine_kernel(ChunkCombineArgs
         if (M != kNegInf) {
             float lloc = 0.f;
             const int k0 = min(c0, D - 1), k1 = min(c1, D - 1);
-            for (int s = 0; s < ns; ++s) {
-                const float *ps = P + (int64_t)s * PF;
-                const float e = ps[0] == kNegInf ? 0.f : fast_exp2(ps[0] - M);
-                if (lane == 0) lloc = fmaf(e, ps[1], lloc);
-                ar0 = fmaf(e, ps[2 + k0], ar0);
-                ar1 = fmaf(e, ps[2 + k1], ar1);
-                if (a.res) {
-                    as0 = fmaf(e, ps[2 + D + k0], as0);
-                    as1 = fmaf(e, ps[2 + D + k1], as1);
+            // four partials per round with their loads in flight together
+            // (indices past the last partial re-read it with weight 0)
+            for (int s0 = 0; s0 < ns; s0 += 4) {
+                float e[4], l[4], v0[4], v1[4], w0[4], w1[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const float *ps = P + (int64_t)min(s0 + u, ns - 1) * PF;
+                    const float mu = ps[0];
+                    e[u] = (s0 + u >= ns || mu == kNegInf) ? 0.f : fast_exp2(mu - M);
+                    l[u] = ps[1];
+                    v0[u] = ps[2 + k0];
+                    v1[u] = ps[2 + k1];
+                    w0[u] = a.res ? ps[2 + D + k0] : 0.f;
+                    w1[u] = a.res ? ps[2 + D + k1] : 0.f;
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    if (lane == 0) lloc = fmaf(e[u], l[u], lloc);
+                    ar0 = fmaf(e[u], v0[u], ar0);
+                    ar1 = fmaf(e[u], v1[u], ar1);
+                    as0 = fmaf(e[u], w0[u], as0);
+                    as1 = fmaf(e[u], w1[u], as1);
                 }
             }
             // chunk part: weights of tokens lane + 64k, then the V rows token by token
@@ -671,11 +684,26 @@ __global__ __launch_bounds__(1024) void rq_chunk_combine_kernel(ChunkCombineArgs
                 pj[k] = sj[k] == kNegInf ? 0.f : fast_exp2(sj[k] - M);
                 lloc += pj[k];
             }
-            for (int j = 0; j < nj; ++j) {
-                const float pw = __shfl(pj[j >> 6], j & 63, 64);
-                const uint16_t *vr = a.chunk_v + (((int64_t)b * C + j) * H + h) * D;
-                if (c0 < D) ar0 = fmaf(pw, bf16_to_f32(vr[c0]), ar0);
-                if (c1 < D) ar1 = fmaf(pw, bf16_to_f32(vr[c1]), ar1);
+            // eight tokens per round with their loads in flight together
+            // (indices past the last token re-read it with weight 0; columns
+            // beyond D read column D-1 and are never stored)
+            const int k0v = min(c0, D - 1), k1v = min(c1, D - 1);
+            for (int j0 = 0; j0 < nj; j0 += 8) {
+                float pw[8], v0[8], v1[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int j = min(j0 + u, nj - 1);
+                    const float p = __shfl(pj[j >> 6], j & 63, 64);
+                    pw[u] = j0 + u < nj ? p : 0.f;
+                    const uint16_t *vr = a.chunk_v + (((int64_t)b * C + j) * H + h) * D;
+                    v0[u] = bf16_to_f32(vr[k0v]);
+                    v1[u] = bf16_to_f32(vr[k1v]);
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    ar0 = fmaf(pw[u], v0[u], ar0);
+                    ar1 = fmaf(pw[u], v1[u], ar1);
+                }
             }
             const float lsum = wave_sum(lloc);
             const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
