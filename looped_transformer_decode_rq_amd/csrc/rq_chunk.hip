@@ -609,12 +609,6 @@ __global__ __launch_bounds__(1024) void rq_chunk_combine_kernel(ChunkCombineArgs
     float ar0 = 0.f, ar1 = 0.f, as0 = 0.f, as1 = 0.f;
     const bool rot_wave = a.res && r < D / 16;
     const int n = r * 16 + (lane & 15);
-    float rv[D / 4];
-    if (rot_wave) {
-        const float *RV = a.rot + ((int64_t)h * 2 + 1) * D * D + (int64_t)(lane >> 4) * D + n;
-#pragma unroll
-        for (int kk = 0; kk < D / 4; ++kk) rv[kk] = RV[(int64_t)4 * kk * D];
-    }
     if (row < a.R) {
         const int b = row / C, i = row % C;
         const int64_t qrow = (int64_t)row * H + h;
@@ -709,6 +703,15 @@ __global__ __launch_bounds__(1024) void rq_chunk_combine_kernel(ChunkCombineArgs
             const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
             ar0 *= inv; ar1 *= inv; as0 *= inv; as1 *= inv;
         }
+    }
+    // this lane's R_V operands of the output rotation: loaded after the
+    // merge (their registers would otherwise spill there), ahead of the
+    // barrier that their latency overlaps
+    float rv[D / 4];
+    if (rot_wave) {
+        const float *RV = a.rot + ((int64_t)h * 2 + 1) * D * D + (int64_t)(lane >> 4) * D + n;
+#pragma unroll
+        for (int kk = 0; kk < D / 4; ++kk) rv[kk] = RV[(int64_t)4 * kk * D];
     }
     if (c0 < D) { O[r * QS + c0] = ar0; A[r * QS + c0] = as0; }
     if (c1 < D) { O[r * QS + c1] = ar1; A[r * QS + c1] = as1; }
