@@ -75,25 +75,33 @@ __global__ __launch_bounds__(1024) void rq_chunk_qprep_kernel(ChunkPrepArgs a) {
     const bool row_ok = row < a.R;
     const bool rot_wave = a.res && r < D / 16;
     const int n = r * 16 + (lane & 15);
+    // this lane's B operands: D/4 consecutive floats of row n of R_K (vector
+    // loads); step kk gives k-slot l/16 the channel k = (D/4)(l/16) + kk
     float rk[D / 4];
     if (rot_wave) {
-        const float *RK = a.rot + ((int64_t)h * 2 + 0) * D * D + (int64_t)n * D + (lane >> 4);
+        const float4 *RK = (const float4 *)(a.rot + ((int64_t)h * 2 + 0) * D * D + (int64_t)n * D +
+                                            (lane >> 4) * (D / 4));
 #pragma unroll
-        for (int kk = 0; kk < D / 4; ++kk) rk[kk] = RK[4 * kk];
+        for (int k4 = 0; k4 < D / 16; ++k4) {
+            const float4 v = RK[k4];
+            rk[4 * k4] = v.x; rk[4 * k4 + 1] = v.y; rk[4 * k4 + 2] = v.z; rk[4 * k4 + 3] = v.w;
+        }
     }
     for (int c = lane; c < D; c += 64)
         Q[r * QS + c] = row_ok ? bf16_to_f32(a.q[((int64_t)row * a.H + h) * D + c]) : 0.0f;
     __syncthreads();
     if (rot_wave) {
         // q' = R_K q for the 16 rows: [16 x D] x R_K^T; v_mfma_f32_16x16x4f32:
-        // lane l supplies A[l%16][k0 + l/16], B[k0 + l/16][l%16], receives
-        // D[4*(l/16)+v][l%16]; wave r computes columns 16r..16r+15
-        floatx4 c = {0.f, 0.f, 0.f, 0.f};
+        // lane l supplies A[l%16][k], B[k][l%16] for its k-slot l/16, receives
+        // D[4*(l/16)+v][l%16]; wave r computes columns 16r..16r+15; four
+        // independent accumulation chains (the products' latency overlaps)
+        floatx4 c4[4] = {};
 #pragma unroll
         for (int kk = 0; kk < D / 4; ++kk) {
-            const int k = 4 * kk + (lane >> 4);
-            c = __builtin_amdgcn_mfma_f32_16x16x4f32(Q[(lane & 15) * QS + k], rk[kk], c, 0, 0, 0);
+            const int k = (lane >> 4) * (D / 4) + kk;
+            c4[kk & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(Q[(lane & 15) * QS + k], rk[kk], c4[kk & 3], 0, 0, 0);
         }
+        const floatx4 c = (c4[0] + c4[1]) + (c4[2] + c4[3]);
         for (int v = 0; v < 4; ++v) QR[(4 * (lane >> 4) + v) * QS + n] = c[v];
     }
     __syncthreads();
