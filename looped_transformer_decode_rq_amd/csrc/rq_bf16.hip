@@ -139,11 +139,25 @@ __global__ __launch_bounds__(64) void rq_bf16_combine_kernel(Bf16CombineArgs a) 
         float lloc = 0.f;
         for (int s = lane; s < ns; s += 64) lloc += fast_exp2(P[(int64_t)s * (2 + D)] - M) * P[(int64_t)s * (2 + D) + 1];
         float lsum = wave_sum(lloc);
-        for (int s = 0; s < ns; ++s) {
-            const float *ps = P + (int64_t)s * (2 + D);
-            const float e = fast_exp2(ps[0] - M);
-            if (c0 < D) o0 = fmaf(e, ps[2 + c0], o0);
-            if (c1 < D) o1 = fmaf(e, ps[2 + c1], o1);
+        // eight partials per round with their loads in flight together
+        // (indices past the last partial re-read it with weight 0; columns
+        // beyond D read column D-1 and are never stored)
+        const int k0 = min(c0, D - 1), k1 = min(c1, D - 1);
+        for (int s0 = 0; s0 < ns; s0 += 8) {
+            float e[8], v0[8], v1[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const float *ps = P + (int64_t)min(s0 + u, ns - 1) * (2 + D);
+                const float eu = fast_exp2(ps[0] - M);
+                e[u] = s0 + u < ns ? eu : 0.f;
+                v0[u] = ps[2 + k0];
+                v1[u] = ps[2 + k1];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                o0 = fmaf(e[u], v0[u], o0);
+                o1 = fmaf(e[u], v1[u], o1);
+            }
         }
         if (a.tail_k) {
             const float pt = fast_exp2(st - M);
