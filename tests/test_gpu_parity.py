@@ -151,10 +151,13 @@ def test_split_count_changes_only_rounding():
     np.testing.assert_array_equal(c.run_decode(pool, [0], split_pages=2), outs[1])
 
 
-def test_bf16_baseline_matches_oracle():
+# (head dim, pages per split): 1-page splits give up to 10 partials per row, more
+# than one round of the combine's loads, with a ragged last round
+@pytest.mark.parametrize("D,split_pages", [(128, 2), (128, 1), (96, 1), (64, 1)])
+def test_bf16_baseline_matches_oracle(D, split_pages):
     import looped_transformer_decode_rq_amd as R
     T = torch()
-    w = W.get(1).replace(batch=3, heads=3, context=150)
+    w = W.get(1).replace(batch=3, heads=3, context=150, head_dim=D, group_size=D)
     kv = W.kv_numpy(w)
     q = W.queries_numpy(w)
     table, nblk = W.block_table(w, spare_blocks=2, shuffled=True)
@@ -173,12 +176,12 @@ def test_bf16_baseline_matches_oracle():
         np.testing.assert_array_equal(kc.float().cpu().numpy(), okc)
         for tail in (True, False):
             out = T.full((B, H, D), float("nan"), device=dev())
-            ws = T.empty(R.bf16_workspace_bytes(H, D, B, table.shape[1], 2), dtype=T.uint8, device=dev())
+            ws = T.empty(R.bf16_workspace_bytes(H, D, B, table.shape[1], split_pages), dtype=T.uint8, device=dev())
             R.bf16_decode_attention(kc, vc, to_dev(q[l], "bf16"), T.from_numpy(table).to(dev()),
                                     T.from_numpy(seq).to(dev()),
                                     to_dev(kv[l, 0, :, N], "bf16") if tail else None,
                                     to_dev(kv[l, 1, :, N], "bf16") if tail else None,
-                                    1 / np.sqrt(D), out, ws, split_pages=2)
+                                    1 / np.sqrt(D), out, ws, split_pages=split_pages)
             want = O.bf16_decode_attention(okc, ovc, q[l], table, seq, 1 / np.sqrt(D),
                                            kv[l, 0, :, N] if tail else None, kv[l, 1, :, N] if tail else None)
-            check_attention(f"bf16 loop {l} tail {tail}", out.cpu().numpy(), want)
+            check_attention(f"bf16 D{D} sp{split_pages} loop {l} tail {tail}", out.cpu().numpy(), want)
