@@ -30,7 +30,10 @@
  *   - Tensor layouts are C-contiguous (row-major) in the stated index order.
  *   - Device-side indices (block ids, slots, sequence lengths) are clamped
  *     against the pool and table sizes: an out-of-range id never causes an
- *     out-of-bounds access; the affected output is unspecified.
+ *     out-of-bounds access. In the decode calls a block-table entry < 0 or
+ *     >= num_blocks masks its page: that page's tokens are not attended (the
+ *     output is attention over the remaining tokens). Elsewhere the affected
+ *     output is unspecified.
  *
  * Packed pool format (one layer). The pool is num_blocks * num_heads slabs,
  * slab (block, head) at byte (block * num_heads + head) * slab_bytes. A slab

@@ -82,9 +82,9 @@ __global__ __launch_bounds__(256) void rq_bf16_split_kernel(Bf16SplitArgs a) {
             lsum *= f;
             m = mn;
         }
-        const float pr = fast_exp2(score - m);
-        lsum += pr;
-        const float w = valid ? pr : 0.f;
+        // a masked token weighs 0 (also while m is still -inf)
+        const float w = valid ? fast_exp2(score - m) : 0.f;
+        lsum += w;
 #pragma unroll
         for (int k = 0; k < NW; ++k) {
             acc[2 * k] = fmaf(w, __uint_as_float(vw[k] << 16), acc[2 * k]);

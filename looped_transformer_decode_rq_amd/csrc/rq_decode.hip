@@ -13,8 +13,10 @@
 //
 // Three kernels per request:
 //   rq_qprep     per (loop call, head, 16 sequences): q' = R_K q on the f32
-//                matrix cores; q and q' are turned into 16-bit fixed point split
-//                into four signed 4-bit limbs laid out for v_dot8_i32_i4.
+//                matrix cores; q and q' are turned into fixed point with one
+//                power-of-two scale per lane slice of channels (24 bits for q,
+//                20 for q'), split into signed 4-bit limbs laid out for
+//                v_dot8_i32_i4.
 //   rq_split     per (split of pages, head, sequence) one wave: walks the
 //                block table, loads each page's packed codes and metadata with
 //                wide coalesced loads, scores tokens with integer dot products
@@ -41,7 +43,14 @@ namespace {
 constexpr int kWaves = 4;
 constexpr float kRescaleThresh = 8.0f;   // log2 units: rescale when a score beats m by 2^8
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kQmaxFixed = 30583;        // 7 * (1 + 16 + 256 + 4096): range of 4 balanced base-16 digits
+
+// Largest magnitude of nl balanced base-16 digits (each -8..7): 7 * (16^nl - 1) / 15.
+// A fixed-point value v is stored as the nibbles of v + 8 * (16^nl - 1) / 15
+// (every nibble u_d of that sum gives the digit u_d - 8, i.e. the 4-bit
+// two's-complement nibble u_d ^ 8).
+__host__ __device__ constexpr int qmax_fixed(int nl) { return 7 * (int)(((1u << (4 * nl)) - 1u) / 15u); }
+__host__ __device__ constexpr int digit_offset(int nl) { return 8 * (int)(((1u << (4 * nl)) - 1u) / 15u); }
+static_assert(kQueryLimbs == 6 && kRotLimbs == 5, "limb planes below: 4 + 2 (q) and 4 + 1 (q')");
 
 template <int D> struct Lanes {
     static constexpr int LPT = (D == 96) ? 2 : 4;   // lanes per token
@@ -79,7 +88,6 @@ __global__ __launch_bounds__(1024) void rq_qprep_kernel(QPrepArgs a) {
     __shared__ float Q[16 * QS];
     __shared__ float QR[16 * QS];
     __shared__ int QI[16][2][D];
-    __shared__ int8_t DG[16][2][4][D];
 
     const int lane = threadIdx.x & 63, r = threadIdx.x >> 6;
     const int h = blockIdx.x, i = blockIdx.y, tile = blockIdx.z;
@@ -122,74 +130,87 @@ __global__ __launch_bounds__(1024) void rq_qprep_kernel(QPrepArgs a) {
     }
     __syncthreads();
 
-    // 16-bit fixed point per row, split into four balanced base-16 digits
-    int S[2] = {0, 0};
+    // Fixed point per lane slice (the CPL channels one lane of the split
+    // kernels holds): v = rint(x * 2^s) with the largest s that keeps every
+    // |v| of the slice within the range of the limbs. A large channel then
+    // coarsens only its own slice, and 24 bits (q) / 20 bits (q') keep the
+    // small channels of that slice: bf16 values of q are exact down to
+    // 2^-15 of their slice's largest magnitude.
+    int S[2][4] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
     for (int which = 0; which < 2; ++which) {
         const float *src = which == 0 ? Q : QR;
         const bool on = which == 0 || rb != 0;
+        const int qmax = qmax_fixed(which == 0 ? kQueryLimbs : kRotLimbs);
         float x0 = 0.f, x1 = 0.f;
         if (on) {
             x0 = (lane < D) ? src[r * QS + lane] : 0.f;
             x1 = (lane + 64 < D) ? src[r * QS + lane + 64] : 0.f;
         }
-        const float amax = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
-        int s = 0;
-        if (amax > 0.f) {
-            int e;
-            frexpf(amax, &e);
-            s = 14 - e;
-            if (ldexpf(amax, s + 1) <= (float)kQmaxFixed) s += 1;
-        }
-        S[which] = s;
-        for (int half = 0; half < 2; ++half) {
-            const int c = lane + 64 * half;
-            if (c >= D) continue;
-            const int qi = (int)rintf(ldexpf(half ? x1 : x0, s));
-            QI[r][which][c] = qi;
-            int rem = qi;
-            for (int d = 0; d < 4; ++d) {
-                const int dig = ((rem + 8) & 15) - 8;
-                DG[r][which][d][c] = (int8_t)dig;
-                rem = (rem - dig) / 16;
+        const int t0 = lane / Ln::CPL, t1 = (lane + 64) / Ln::CPL;
+        int s0 = 0, s1 = 0;
+#pragma unroll
+        for (int t = 0; t < Ln::LPT; ++t) {
+            const float amax = wave_max(fmaxf(t0 == t ? fabsf(x0) : 0.f, t1 == t ? fabsf(x1) : 0.f));
+            int sh = 0;
+            if (amax > 0.f) {
+                int e;
+                frexpf(amax, &e);                       // amax in [2^(e-1), 2^e)
+                sh = 31 - __builtin_clz((unsigned)qmax) - e;   // amax * 2^sh < 2^floor(log2 qmax)
+                if (ldexpf(amax, sh + 1) <= (float)qmax) sh += 1;
             }
+            S[which][t] = sh;
+            s0 = t0 == t ? sh : s0;
+            s1 = t1 == t ? sh : s1;
         }
+        if (lane < D) QI[r][which][lane] = (int)rintf(ldexpf(x0, s0));
+        if (lane + 64 < D) QI[r][which][lane + 64] = (int)rintf(ldexpf(x1, s1));
     }
     __syncthreads();
     if (!row_ok) return;
     uint8_t *qp = a.qpack + (((int64_t)i * B + b) * H + h) * qpack_bytes(D);
-    const int c0q = lane;
-    // limb dwords: [q4][k][limb], nibble n = channel limb_channel(q4,k,n)
+    // Limb words. Per quantity (q, then q'), plane A holds limbs 0..3 as one
+    // 16-byte entry per (slice q4, dword k) and plane B the remaining limbs
+    // (2 for q, 1 for q') as one 8- or 4-byte entry per (q4, k). Nibble n of
+    // the word of (limb, q4, k) is the digit of channel limb_channel(q4, k, n).
     for (int which = 0; which < 2; ++which) {
         if (which == 1 && rb == 0) break;
+        const int nl = which == 0 ? kQueryLimbs : kRotLimbs;
         const int order = which == 0 ? a.ro[i] : rb;
-        for (int dw = lane; dw < D / 2; dw += 64) {
-            const int limb = dw & 3;
-            const int k = (dw >> 2) % Ln::NDW;
-            const int q4 = dw / (4 * Ln::NDW);
+        const int off = digit_offset(nl);
+        uint32_t *base = (uint32_t *)(qp + 64 + (which == 0 ? 0 : kQueryLimbs * D / 2));
+        for (int dw = lane; dw < nl * D / 8; dw += 64) {
+            int limb, e;
+            if (dw < D / 2) {
+                limb = dw & 3; e = dw >> 2;
+            } else {
+                const int nb = nl - 4, j = dw - D / 2;
+                limb = 4 + j % nb; e = j / nb;
+            }
+            const int k = e % Ln::NDW, q4 = e / Ln::NDW;
             uint32_t word = 0;
             for (int nn = 0; nn < 8; ++nn) {
-                const int ch = limb_channel<D>(q4, k, nn, order);
-                word |= ((uint32_t)DG[r][which][limb][ch] & 15u) << (4 * nn);
+                const uint32_t u = (uint32_t)(QI[r][which][limb_channel<D>(q4, k, nn, order)] + off);
+                word |= (((u >> (4 * limb)) & 15u) ^ 8u) << (4 * nn);
             }
-            ((uint32_t *)(qp + 64 + which * 2 * D))[dw] = word;
+            base[dw] = word;
         }
     }
-    // per (which, q4): the sum of the fixed-point values of the q4 lanes'
-    // channels, as wave sums (|sum| < 2^24: exact in fp32)
+    // per (which, slice): the sum of the slice's fixed-point values (|sum| <
+    // 2^31), and the slice's scale 2^-s
     for (int which = 0; which < 2; ++which) {
         const bool on = which == 0 || rb != 0;
-        const int v0 = (on && c0q < D) ? QI[r][which][c0q] : 0;
-        const int v1 = (on && c0q + 64 < D) ? QI[r][which][c0q + 64] : 0;
+        const int v0 = (on && lane < D) ? QI[r][which][lane] : 0;
+        const int v1 = (on && lane + 64 < D) ? QI[r][which][lane + 64] : 0;
 #pragma unroll
         for (int t = 0; t < Ln::LPT; ++t) {
-            const float part = (float)((c0q / Ln::CPL == t ? v0 : 0) + ((c0q + 64) / Ln::CPL == t ? v1 : 0));
-            const float tot = wave_sum(part);
-            if (lane == 0) ((int *)(qp + 16 + 16 * which))[t] = (int)tot;
+            int part = (lane / Ln::CPL == t ? v0 : 0) + ((lane + 64) / Ln::CPL == t ? v1 : 0);
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
+            if (lane == 0) {
+                ((int *)(qp + 16 + 16 * which))[t] = part;
+                ((float *)(qp + 48 * which))[t] = on ? ldexpf(1.0f, -S[which][t]) : 0.0f;
+            }
         }
-    }
-    if (lane == 0) {
-        ((float *)qp)[0] = ldexpf(1.0f, -S[0]);
-        ((float *)qp)[1] = rb ? ldexpf(1.0f, -S[1]) : 0.0f;
     }
 }
 
@@ -273,47 +294,74 @@ __device__ __forceinline__ int sdot8_0(int a, int b) {
     return r;
 }
 
-// Integer dot of 4-bit codes (XOR 8 turns 0..15 into signed -8..7) with the
-// four query limbs; returns sum_i q_int_i * (c_i - 8).
-template <int NW>
-__device__ __forceinline__ int dot_int4(const uint32_t *codes, const uint4 *limb) {
-    int a0, a1, a2, a3;
+// Query limbs of one lane slice as the split kernels hold them: per dword k
+// of channels, limbs 0..3 in `lo[k]` and the remaining NL - 4 limbs in
+// `hi[k]` (uint2 for the query, one uint for the rotated query).
+template <int NL> struct HiLimbs;
+template <> struct HiLimbs<6> { using T = uint2; };
+template <> struct HiLimbs<5> { using T = uint32_t; };
+
+__device__ __forceinline__ int hi_limb(uint2 v, int j) { return (int)(j == 0 ? v.x : v.y); }
+__device__ __forceinline__ int hi_limb(uint32_t v, int) { return (int)v; }
+
+// Sum of the digit sums a_d weighted by 16^d, as a float: exact in int32 up to
+// five limbs (|a_d| <= 8 * 8 * 48); six limbs are combined as two exact
+// three-limb halves (one fp32 rounding, relative 2^-24).
+template <int NL>
+__device__ __forceinline__ float combine_limbs(const int (&a)[NL]) {
+    if constexpr (NL == 6) {
+        const int lo = a[0] + 16 * a[1] + 256 * a[2];
+        const int hi = a[3] + 16 * a[4] + 256 * a[5];
+        return fmaf(4096.f, (float)hi, (float)lo);
+    } else {
+        return (float)(a[0] + 16 * a[1] + 256 * a[2] + 4096 * a[3] + 65536 * a[4]);
+    }
+}
+
+// Dot of 4-bit codes (XOR 8 turns 0..15 into signed -8..7) with the query
+// limbs: returns sum_i v_i * (c_i - 8) over the lane's channels, v_i the
+// fixed-point query.
+template <int NW, int NL>
+__device__ __forceinline__ float dot_int4(const uint32_t *codes, const uint4 *lo,
+                                          const typename HiLimbs<NL>::T *hi) {
+    int a[NL];
 #pragma unroll
     for (int k = 0; k < NW; ++k) {
         const int w = (int)(codes[k] ^ 0x88888888u);
-        const uint4 q = limb[k];
-        if (k == 0) {
-            a0 = sdot8_0((int)q.x, w); a1 = sdot8_0((int)q.y, w);
-            a2 = sdot8_0((int)q.z, w); a3 = sdot8_0((int)q.w, w);
-        } else {
-            a0 = sdot8((int)q.x, w, a0); a1 = sdot8((int)q.y, w, a1);
-            a2 = sdot8((int)q.z, w, a2); a3 = sdot8((int)q.w, w, a3);
+        const uint4 q = lo[k];
+        const int l4[4] = {(int)q.x, (int)q.y, (int)q.z, (int)q.w};
+#pragma unroll
+        for (int d = 0; d < NL; ++d) {
+            const int ql = d < 4 ? l4[d & 3] : hi_limb(hi[k], d - 4);
+            a[d] = k == 0 ? sdot8_0(ql, w) : sdot8(ql, w, a[d]);
         }
     }
-    return a0 + 16 * a1 + 256 * a2 + 4096 * a3;
+    return combine_limbs<NL>(a);
 }
 
 // Same for 2-bit codes: a word of 16 crumbs is split into its even and odd
-// channels, each widened to nibbles (values 0..3 need no offset).
-template <int NW>
-__device__ __forceinline__ int dot_int2(const uint32_t *codes, const uint4 *limb) {
-    int a0, a1, a2, a3;
+// channels, each widened to nibbles (values 0..3 need no offset); returns
+// sum_i v_i * c_i.
+template <int NW, int NL>
+__device__ __forceinline__ float dot_int2(const uint32_t *codes, const uint4 *lo,
+                                          const typename HiLimbs<NL>::T *hi) {
+    int a[NL];
 #pragma unroll
     for (int k = 0; k < NW; ++k) {
         const int ev = (int)(codes[k] & 0x33333333u);
         const int od = (int)((codes[k] >> 2) & 0x33333333u);
-        const uint4 qe = limb[2 * k], qo = limb[2 * k + 1];
-        if (k == 0) {
-            a0 = sdot8_0((int)qe.x, ev); a1 = sdot8_0((int)qe.y, ev);
-            a2 = sdot8_0((int)qe.z, ev); a3 = sdot8_0((int)qe.w, ev);
-        } else {
-            a0 = sdot8((int)qe.x, ev, a0); a1 = sdot8((int)qe.y, ev, a1);
-            a2 = sdot8((int)qe.z, ev, a2); a3 = sdot8((int)qe.w, ev, a3);
+        const uint4 qe = lo[2 * k], qo = lo[2 * k + 1];
+        const int le[4] = {(int)qe.x, (int)qe.y, (int)qe.z, (int)qe.w};
+        const int lodd[4] = {(int)qo.x, (int)qo.y, (int)qo.z, (int)qo.w};
+#pragma unroll
+        for (int d = 0; d < NL; ++d) {
+            const int qle = d < 4 ? le[d & 3] : hi_limb(hi[2 * k], d - 4);
+            const int qlo = d < 4 ? lodd[d & 3] : hi_limb(hi[2 * k + 1], d - 4);
+            a[d] = k == 0 ? sdot8_0(qle, ev) : sdot8(qle, ev, a[d]);
+            a[d] = sdot8(qlo, od, a[d]);
         }
-        a0 = sdot8((int)qo.x, od, a0); a1 = sdot8((int)qo.y, od, a1);
-        a2 = sdot8((int)qo.z, od, a2); a3 = sdot8((int)qo.w, od, a3);
     }
-    return a0 + 16 * a1 + 256 * a2 + 4096 * a3;
+    return combine_limbs<NL>(a);
 }
 
 // Sum over each group of LPT consecutive lanes (LPT = 2 or 4, all lanes
@@ -342,13 +390,16 @@ __device__ __forceinline__ void sz_of(uint32_t v, float &s, float &z) {
 
 // ---- shared per-token arithmetic of the split kernels
 
-// Query state of one (loop call, sequence, head) held by each lane: the
-// fixed-point scales, the limb sums of the lane's channels and its limbs.
+// Query state of one (loop call, sequence, head) held by each lane for its
+// slice of channels: the fixed-point scales and value sums of q and of
+// q' = R_K q, and their limbs (planes A and B of the query record).
 template <int D>
 struct QueryRegs {
     float sc_ref, sc_res;
     int qs_ref, qs_res;
     uint4 lrv[Lanes<D>::NDW], lsv[Lanes<D>::NDW];
+    uint2 lrh[Lanes<D>::NDW];
+    uint32_t lsh[Lanes<D>::NDW];
 };
 
 // Online-softmax state of one wave: running max (log2 units) and, per lane,
@@ -369,27 +420,38 @@ constexpr int kWScratch = 16 * 16 * 2;
 template <int D, bool RES>
 __device__ __forceinline__ void load_query(const uint8_t *qp, int q4, QueryRegs<D> &q) {
     using Ln = Lanes<D>;
-    q.sc_ref = ((const float *)qp)[0];
-    q.sc_res = ((const float *)qp)[1];
+    q.sc_ref = ((const float *)qp)[q4];
+    q.sc_res = ((const float *)(qp + 48))[q4];
     q.qs_ref = ((const int *)(qp + 16))[q4];
     q.qs_res = ((const int *)(qp + 32))[q4];
-    const uint4 *gq = (const uint4 *)(qp + 64);
+    const uint4 *qa = (const uint4 *)(qp + 64);
+    const uint2 *qb = (const uint2 *)(qp + 64 + 2 * D);
+    const uint4 *ra = (const uint4 *)(qp + 64 + kQueryLimbs * D / 2);
+    const uint32_t *rbp = (const uint32_t *)(qp + 64 + kQueryLimbs * D / 2 + 2 * D);
 #pragma unroll
-    for (int k = 0; k < Ln::NDW; ++k) q.lrv[k] = gq[q4 * Ln::NDW + k];
+    for (int k = 0; k < Ln::NDW; ++k) {
+        q.lrv[k] = qa[q4 * Ln::NDW + k];
+        q.lrh[k] = qb[q4 * Ln::NDW + k];
+    }
     if constexpr (RES) {
 #pragma unroll
-        for (int k = 0; k < Ln::NDW; ++k) q.lsv[k] = gq[D / 8 + q4 * Ln::NDW + k];
+        for (int k = 0; k < Ln::NDW; ++k) {
+            q.lsv[k] = ra[q4 * Ln::NDW + k];
+            q.lsh[k] = rbp[q4 * Ln::NDW + k];
+        }
     }
     // Make the compiler complete these loads here: its wait-count tracking
     // does not see the direct-to-LDS loads issued later, so a wait it placed
     // at a first use inside the page loop would also drain the ring.
 #pragma unroll
     for (int k = 0; k < Ln::NDW; ++k)
-        __asm__ volatile("" ::"v"(q.lrv[k].x), "v"(q.lrv[k].y), "v"(q.lrv[k].z), "v"(q.lrv[k].w));
+        __asm__ volatile("" ::"v"(q.lrv[k].x), "v"(q.lrv[k].y), "v"(q.lrv[k].z), "v"(q.lrv[k].w),
+                         "v"(q.lrh[k].x), "v"(q.lrh[k].y));
     if constexpr (RES) {
 #pragma unroll
         for (int k = 0; k < Ln::NDW; ++k)
-            __asm__ volatile("" ::"v"(q.lsv[k].x), "v"(q.lsv[k].y), "v"(q.lsv[k].z), "v"(q.lsv[k].w));
+            __asm__ volatile("" ::"v"(q.lsv[k].x), "v"(q.lsv[k].y), "v"(q.lsv[k].z), "v"(q.lsv[k].w),
+                             "v"(q.lsh[k]));
     }
     __asm__ volatile("" ::"v"(q.qs_ref), "v"(q.qs_res), "v"(q.sc_ref), "v"(q.sc_res));
 }
@@ -410,7 +472,6 @@ __device__ __forceinline__ void init_state(SplitState<D> &s) {
 //   vref, vres    V code blocks of page 0 of the step (page pg at + pg*stride)
 //   wsc           this wave's weight scratch (PPI pages of kWScratch bytes);
 //                 may alias the step's code bytes, which are all read first
-//   lsv           this lane's residual query limbs (registers or LDS)
 //   SHR           shared reference rows (multi-loop): the reference weights go
 //                 to rows 2*(sha_pair + g) + {hi, lo} of `sha` instead of the
 //                 wave's own product; the reference product and the rescale
@@ -422,8 +483,7 @@ __device__ __forceinline__ void token_step(const uint8_t *ck, const uint8_t *mkr
                                            const uint8_t *rk, const uint8_t *mks, const uint8_t *aks,
                                            const uint8_t *mvs, const uint8_t *avs, const uint8_t *vref,
                                            const uint8_t *vres, uint8_t *wsc, int lane, bool valid,
-                                           float score_scale, const QueryRegs<D> &q, const uint4 *lsv,
-                                           SplitState<D> &s, uint8_t *sha = nullptr, int sha_pair = 0,
+                                           float score_scale, const QueryRegs<D> &q, SplitState<D> &s, uint8_t *sha = nullptr, int sha_pair = 0,
                                            float *fr = nullptr) {
     using Ln = Lanes<D>;
     constexpr int LPT = Ln::LPT, CPL = Ln::CPL, PPI = Ln::PPI;
@@ -450,9 +510,15 @@ __device__ __forceinline__ void token_step(const uint8_t *ck, const uint8_t *mkr
     float skr, zkr, svr, zvr;
     sz_of(*(const SZ *)mkr, skr, zkr);
     sz_of(*(const SZ *)mvr, svr, zvr);
-    // score: q.x_hat = alpha*(s*sum q c + z*sum q) + (s_r*sum q' c_r + z_r*sum q')
-    const int dref = (REFB == 4) ? dot_int4<REF_NW>(ckw, q.lrv) + 8 * q.qs_ref : dot_int2<REF_NW>(ckw, q.lrv);
-    float part = (skr * (float)dref + zkr * (float)q.qs_ref) * q.sc_ref;
+    // score: q.x_hat = alpha*(s*sum q c + z*sum q) + (s_r*sum q' c_r + z_r*sum q'),
+    // per lane slice in its own fixed-point scale; INT4 codes are centred,
+    // s*sum q c + z*sum q = s*sum q (c - 8) + (8 s + z)*sum q
+    float part;
+    if constexpr (REFB == 4)
+        part = fmaf(skr, dot_int4<REF_NW, kQueryLimbs>(ckw, q.lrv, q.lrh), fmaf(8.f, skr, zkr) * (float)q.qs_ref);
+    else
+        part = fmaf(skr, dot_int2<REF_NW, kQueryLimbs>(ckw, q.lrv, q.lrh), zkr * (float)q.qs_ref);
+    part *= q.sc_ref;
     float av = 1.f, svs = 0.f, zvs = 0.f;
     if constexpr (RB != 0) {
         float sks, zks;
@@ -460,8 +526,12 @@ __device__ __forceinline__ void token_step(const uint8_t *ck, const uint8_t *mkr
         sz_of(*(const SZ *)mvs, svs, zvs);
         const float ak = load_meta1<META_F32>(aks);
         av = load_meta1<META_F32>(avs);
-        const int dres = (RB == 2) ? dot_int2<RES_NW>(rkw, lsv) : dot_int4<RES_NW>(rkw, lsv) + 8 * q.qs_res;
-        part = ak * part + (sks * (float)dres + zks * (float)q.qs_res) * q.sc_res;
+        float pres;
+        if constexpr (RB == 2)
+            pres = fmaf(sks, dot_int2<RES_NW, kRotLimbs>(rkw, q.lsv, q.lsh), zks * (float)q.qs_res);
+        else
+            pres = fmaf(sks, dot_int4<RES_NW, kRotLimbs>(rkw, q.lsv, q.lsh), fmaf(8.f, sks, zks) * (float)q.qs_res);
+        part = fmaf(ak, part, pres * q.sc_res);
     }
     float score = lane_group_sum<LPT>(part) * score_scale;
     score = valid ? score : kNegInf;
@@ -481,7 +551,9 @@ __device__ __forceinline__ void token_step(const uint8_t *ck, const uint8_t *mkr
     if constexpr (SHR) {
         if (lane == 0) *fr = fstep;
     }
-    const float pr = fast_exp2(score - s.m);
+    // a masked token weighs 0 (also while every score so far is masked and
+    // s.m is still -inf, where score - s.m would be NaN)
+    const float pr = valid ? fast_exp2(score - s.m) : 0.f;
     s.lsum += pr;
     // weights of this token (group of this lane); the zero terms carry z - 16 s
     const float pa = pr * av;
@@ -832,7 +904,7 @@ __global__ __launch_bounds__(256, 4) void rq_split_kernel(SplitArgs a) {
             token_step<D, RB, META_F32, G, REFB>(S + SG::O_RK + o_ck, M, M + SG::MB, S + SG::O_SK + o_rk,
                                                  M + 2 * SG::MB, A + 3 * SG::MB, M + 3 * SG::MB + SG::AB,
                                                  A + 4 * SG::MB + SG::AB, S + SG::O_RV, S + SG::O_SV, S, lane,
-                                                 valid, a.score_scale, q, q.lsv, s);
+                                                 valid, a.score_scale, q, s);
         }
     }
 
@@ -1132,10 +1204,10 @@ __global__ __launch_bounds__(64 * kMaxMultiLoops) void rq_multi_kernel(MultiArgs
                 token_step<D, RBW, META_F32, G, 4, SH>(R + o_ck, R + o_mkr, R + o_mvr, S + o_rk, S + o_mks,
                                                        S + o_aks, S + o_mvs, S + o_avs, R + MG::R_CV,
                                                        S + PPI * MG::cb_res(RBW), wsc, lane, valid, a.score_scale,
-                                                       q, q.lsv, s, shc, call * NG, fc);
+                                                       q, s, shc, call * NG, fc);
             } else {
                 token_step<D, 0, META_F32, G, 4, SH>(R + o_ck, R + o_mkr, R + o_mvr, S, S, S, S, S, R + MG::R_CV, S,
-                                                     wsc, lane, valid, a.score_scale, q, q.lsv, s, shc, call * NG,
+                                                     wsc, lane, valid, a.score_scale, q, s, shc, call * NG,
                                                      fc);
                 // SH: the previous step's rows of every loop
                 if (SH && cur > 0)

@@ -26,8 +26,13 @@ rq_status make_geom(const rq_layout *layout, Geom *g);
 // Lanes per token used by the split-K kernels for a head dim.
 inline int lanes_per_token(int D) { return D == 96 ? 2 : 4; }
 
-// Per-(loop call, sequence, head) query record written by the query prep kernel.
-__host__ __device__ constexpr int qpack_bytes(int D) { return 64 + 4 * D; }
+// Per-(loop call, sequence, head) query record written by the query prep kernel:
+// a 64-byte header (per lane slice: the fixed-point scale and the sum of the
+// fixed-point values, for q and q'), then the 4-bit limbs of q (kQueryLimbs
+// per channel: 24-bit fixed point) and of q' = R_K q (kRotLimbs: 20-bit).
+constexpr int kQueryLimbs = 6;
+constexpr int kRotLimbs = 5;
+__host__ __device__ constexpr int qpack_bytes(int D) { return 64 + (kQueryLimbs + kRotLimbs) * D / 2; }
 __host__ __device__ constexpr int partial_floats(int D) { return 2 + 2 * D; }
 // Per-(query row, head) record of the chunked-prefill query prep: sum q, sum q'
 // (two floats, padded to 16 B), then q' = R_K q as bf16 hi[D] and lo[D].

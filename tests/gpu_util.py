@@ -8,7 +8,9 @@ Comparison rules:
   all elements;
 * scale, zero and alpha are bit-exact, except where the oracle's value before
   rounding lies within 1e-6*step (alpha: 1e-6 relative) of a rounding boundary
-  of the metadata dtype; such groups are counted (cap 1e-4 of groups);
+  of the metadata dtype; such groups are counted (cap 1e-4 of groups), and
+  their codes are checked against the codes the oracle's values give under the
+  GPU's stored scale and zero, by the same rule and toward the same cap;
 * attention outputs: max-abs error <= 2e-3 and rel-L2 error <= 1e-3 against
   the oracle run on the same packed inputs.
 """
@@ -97,11 +99,24 @@ def compare_quantized(tag, codes_g, scale_g, zero_g, q: O.Quantized, meta: str, 
             ok = _near_boundary(alpha64, meta, CODE_BAND * np.abs(alpha64) + 1e-300)
             assert np.all(ok[abad]), f"{tag}: alpha differs off a rounding boundary"
         stats["meta_exempt"] = stats.get("meta_exempt", 0) + int(abad.sum())
-    # codes: compare where the group metadata agree
-    grp_ok = np.repeat(~meta_bad, G, axis=-1)
-    diff = (codes_g != q.codes) & grp_ok
+    # codes: where the group metadata agree, against the oracle's codes; in a
+    # metadata-exempt group, against the codes the oracle's pre-rounding
+    # values give under the GPU's stored scale and zero (same rounding rule)
+    u = np.array(q.u, dtype=np.float64)
+    want = np.array(q.codes)
+    if meta_bad.any():
+        s_o, z_o = np.repeat(q.scale, G, axis=-1), np.repeat(q.zero, G, axis=-1)
+        s_g, z_g = np.repeat(scale_g, G, axis=-1).astype(np.float64), np.repeat(zero_g, G, axis=-1).astype(np.float64)
+        bad = np.repeat(meta_bad, G, axis=-1)
+        y = np.where(np.isnan(u), z_o, u * s_o + z_o)   # a degenerate oracle group: every value ~ zero
+        with np.errstate(divide="ignore", invalid="ignore"):
+            u2 = np.where(s_g != 0, (y - z_g) / np.where(s_g != 0, s_g, 1.0), 0.0)
+        c2 = np.where(s_g != 0, np.clip(np.rint(u2), 0, 2 ** q.bits - 1), 0).astype(want.dtype)
+        u = np.where(bad, u2, u)
+        want = np.where(bad, c2, want)
+    diff = codes_g != want
     if diff.any():
-        assert np.all(_near_half(q.u[diff])), f"{tag}: {int(diff.sum())} codes differ off a rounding boundary"
+        assert np.all(_near_half(u[diff])), f"{tag}: {int(diff.sum())} codes differ off a rounding boundary"
     stats["codes"] = stats.get("codes", 0) + codes_g.size
     stats["code_exempt"] = stats.get("code_exempt", 0) + int(diff.sum())
 

@@ -185,3 +185,79 @@ def test_bf16_baseline_matches_oracle(D, split_pages):
             want = O.bf16_decode_attention(okc, ovc, q[l], table, seq, 1 / np.sqrt(D),
                                            kv[l, 0, :, N] if tail else None, kv[l, 1, :, N] if tail else None)
             check_attention(f"bf16 D{D} sp{split_pages} loop {l} tail {tail}", out.cpu().numpy(), want)
+
+
+# (pages masked in sequence 0, split size): a split whose pages are all masked,
+# one that starts with a masked page and continues with valid ones, one that
+# ends with a masked page
+@pytest.mark.parametrize("split_pages", [0, 1, 2, 3])
+def test_masked_block_ids_drop_their_tokens(split_pages):
+    """Block-table entries of -1 (or past the pool) mark pages whose tokens are
+    not attended: the output equals attention over the remaining tokens, for
+    per-loop and multi-loop calls, with and without the current token."""
+    import oracle as O
+    w = W.get(1).replace(batch=2, heads=2, context=190)
+    c = SmallCase(w, seq_lens=[190, 190])
+    pool = c.device_pool_from_oracle()
+    masked = {0: [0, 1, 2, 5], 1: [11]}          # sequence 1: its last (partial) page
+    table = c.table.copy()
+    for b, pages in masked.items():
+        table[b, pages] = -1
+    table[1, 3] = c.nblk + 7                      # an id past the pool is masked as well
+    masked[1].append(3)
+    T = torch()
+    c.d_table = T.from_numpy(table).to(dev())
+    L = w.loops
+    for tail in (True, False):
+        multi = c.run_decode(pool, list(range(L)), tail=tail, split_pages=split_pages)
+        for l in range(L):
+            want = np.zeros((w.batch, w.heads, w.head_dim))
+            for b in range(w.batch):
+                keep = np.ones(int(c.seq[b]), bool)
+                for p in masked[b]:
+                    keep[16 * p:16 * (p + 1)] = False
+                for h in range(w.heads):
+                    K, V = O.reconstruct_sequence(c.pool_o, c.olay, c.table[b], int(c.seq[b]), h, l,
+                                                  c.st["rot32"][h])
+                    want[b, h] = O.attention(c.q[l, b, h], K[keep], V[keep], c.tau,
+                                             c.tail_k[l, b, h] if tail else None,
+                                             c.tail_v[l, b, h] if tail else None)
+            got = c.run_decode(pool, [l], tail=tail, split_pages=split_pages)[0]
+            check_attention(f"masked pages loop {l} sp {split_pages} tail {tail}", got, want)
+            check_attention(f"masked pages multi-loop loop {l} sp {split_pages} tail {tail}", multi[l], want)
+
+
+def test_bf16_masked_block_ids_drop_their_tokens():
+    import looped_transformer_decode_rq_amd as R
+    import oracle as O
+    T = torch()
+    w = W.get(1).replace(batch=2, heads=2, context=150)
+    kv = W.kv_numpy(w)
+    q = W.queries_numpy(w)
+    table, nblk = W.block_table(w)
+    seq = np.array([150, 150], np.int32)
+    B, H, D, N = w.batch, w.heads, w.head_dim, w.context
+    kc = T.zeros((nblk, H, 16, D), dtype=T.bfloat16, device=dev())
+    vc = T.zeros_like(kc)
+    tb = np.concatenate([np.full(seq[b], b) for b in range(B)])
+    tp = np.concatenate([np.arange(seq[b]) for b in range(B)])
+    slots = table[tb, tp // 16].astype(np.int64) * 16 + tp % 16
+    R.bf16_write(kc, vc, to_dev(kv[0][:, tb, tp], "bf16"), T.from_numpy(slots).to(dev()))
+    mtable = table.copy()
+    mtable[0, [0, 1, 2, 6]] = -1
+    masked = {0: [0, 1, 2, 6], 1: []}
+    for sp in (1, 2, 3):
+        out = T.full((B, H, D), float("nan"), device=dev())
+        ws = T.empty(R.bf16_workspace_bytes(H, D, B, table.shape[1], sp), dtype=T.uint8, device=dev())
+        R.bf16_decode_attention(kc, vc, to_dev(q[0], "bf16"), T.from_numpy(mtable).to(dev()),
+                                T.from_numpy(seq).to(dev()), None, None, 1 / np.sqrt(D), out, ws, split_pages=sp)
+        want = np.zeros((B, H, D))
+        for b in range(B):
+            keep = np.ones(int(seq[b]), bool)
+            for p in masked[b]:
+                keep[16 * p:16 * (p + 1)] = False
+            for h in range(H):
+                K = kv[0, 0, b, :seq[b], h][keep]
+                V = kv[0, 1, b, :seq[b], h][keep]
+                want[b, h] = O.attention(q[0, b, h], K, V, 1 / np.sqrt(D))
+        check_attention(f"bf16 masked pages sp {sp}", out.cpu().numpy(), want)

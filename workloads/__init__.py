@@ -31,7 +31,7 @@ import numpy as np
 __all__ = [
     "Workload", "WORKLOADS", "get", "bf16_round", "bf16_bits",
     "structure", "kv_numpy", "queries_numpy", "block_table", "slot_mapping",
-    "kv_torch", "queries_torch",
+    "kv_torch", "queries_torch", "outlier_queries",
 ]
 
 
@@ -188,6 +188,22 @@ def queries_numpy(w: Workload, layer: int = 0, batch=None) -> np.ndarray:
     g = _rng(w, layer, 2)
     q = g.standard_normal((w.loops, B, w.heads, w.head_dim)) / np.sqrt(w.head_dim)
     return _store_round(w, q)
+
+
+def outlier_queries(w: Workload, q: np.ndarray, mult: float, zero_rows=(), seed: int = 0) -> np.ndarray:
+    """Queries with one large channel: per (loop, sequence, head) one seeded
+    channel of q is multiplied by ``mult`` (then rounded to the storage dtype);
+    the sequences in ``zero_rows`` get an all-zero query. q: [L][B][H][D]."""
+    q = np.array(q, dtype=np.float64)
+    L, B, H, D = q.shape
+    g = np.random.default_rng([w.seed, 31, seed])
+    ch = g.integers(0, D, size=(L, B, H))
+    li, bi, hi = np.meshgrid(np.arange(L), np.arange(B), np.arange(H), indexing="ij")
+    q[li, bi, hi, ch] *= mult
+    q = _store_round(w, q)
+    for b in zero_rows:
+        q[:, b] = 0.0
+    return q
 
 
 # ------------------------------------------------------------------- paging
