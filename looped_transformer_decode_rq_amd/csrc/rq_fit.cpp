@@ -120,13 +120,47 @@ void procrustes(const std::vector<double> &M, int D, std::vector<double> &R) {
         }
         if (off < 1e-15) break;
     }
-    // U = W S^-1 column by column; R = U V^T
+    // U = W S^-1 column by column. Columns whose singular value is zero (M of
+    // rank < D: fewer samples than channels, or channels that are zero in every
+    // sample) have no direction of their own; U is completed there with unit
+    // vectors orthogonal to every other column (Gram-Schmidt over the standard
+    // basis), so that R stays orthogonal. The samples have no component along
+    // the matching columns of V, so the completion does not change R d.
+    std::vector<double> nrm(D, 0.0);
+    double nmax = 0.0;
     for (int c = 0; c < D; ++c) {
-        double nrm = 0.0;
-        for (int r = 0; r < D; ++r) nrm += col(W, r, c) * col(W, r, c);
-        nrm = sqrt(nrm);
-        const double inv = nrm > 0.0 ? 1.0 / nrm : 0.0;
+        for (int r = 0; r < D; ++r) nrm[c] += col(W, r, c) * col(W, r, c);
+        nrm[c] = sqrt(nrm[c]);
+        nmax = fmax(nmax, nrm[c]);
+    }
+    std::vector<char> null_col(D, 0);
+    for (int c = 0; c < D; ++c) {
+        null_col[c] = !(nrm[c] > 1e-13 * nmax);
+        const double inv = null_col[c] ? 0.0 : 1.0 / nrm[c];
         for (int r = 0; r < D; ++r) col(W, r, c) *= inv;
+    }
+    // each null column: the standard basis vector with the largest component
+    // outside the span of the columns set so far (at least 1/sqrt(D) of it,
+    // since that span has dimension < D), projected out twice and normalized
+    std::vector<double> v(D), best_v(D);
+    for (int c = 0; c < D; ++c) {
+        if (!null_col[c]) continue;
+        double best_n = -1.0;
+        for (int k = 0; k < D; ++k) {
+            for (int r = 0; r < D; ++r) v[r] = r == k ? 1.0 : 0.0;
+            for (int pass = 0; pass < 2; ++pass)
+                for (int j = 0; j < D; ++j) {
+                    if (j == c) continue;      // unset null columns are zero and change nothing
+                    double dot = 0.0;
+                    for (int r = 0; r < D; ++r) dot += col(W, r, j) * v[r];
+                    for (int r = 0; r < D; ++r) v[r] -= dot * col(W, r, j);
+                }
+            double vn = 0.0;
+            for (int r = 0; r < D; ++r) vn += v[r] * v[r];
+            if (vn > best_n) { best_n = vn; best_v = v; }
+        }
+        const double inv = 1.0 / sqrt(best_n);
+        for (int r = 0; r < D; ++r) col(W, r, c) = best_v[r] * inv;
     }
     R.assign((size_t)D * D, 0.0);
     for (int r = 0; r < D; ++r)

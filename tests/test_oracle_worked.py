@@ -135,3 +135,46 @@ def test_worked_layout_offsets(golden):
     assert lay.pool_bytes == lg["pool_bytes"][0]
     for blk, head, loop, kv, off in lg["offset"]:
         assert lay.record_offset(blk, head, loop, kv) == off
+
+
+# ------------------------------------------------ rotation-fitting objective
+def test_rotation_objective_hand_derived(golden):
+    """Objective of a non-symmetric rotation on two rows, derived by hand
+    (tests/golden/rotation_objective_d4.txt): pins that the rows are rotated
+    as R d (not R^T d) before quantization."""
+    g = golden("rotation_objective_d4.txt")
+    S = np.array(g["S_rot"], dtype=np.float64).reshape(4, 4)
+    rows = np.array(g["obj_rows"], dtype=np.float64).reshape(2, 4)
+    assert O.rotation_quant_error(rows, S, 2, 4, "f16") == g["obj_value"][0]
+    # the per-row quantization behind it
+    q = O.quantize(rows @ S.T, 2, 4, "f16")
+    np.testing.assert_array_equal(q.codes[0], g["obj_row1_codes"])
+    np.testing.assert_array_equal(q.codes[1], g["obj_row2_codes"])
+    f16 = lambda v: np.array([v], np.uint16).view(np.float16).astype(np.float64)[0]
+    assert q.scale[0, 0] == f16(g["obj_row1_scale_f16"][0]) and q.zero[0, 0] == f16(g["obj_row1_zero_f16"][0])
+    assert q.scale[1, 0] == f16(g["obj_row2_scale_f16"][0]) and q.zero[1, 0] == f16(g["obj_row2_zero_f16"][0])
+    # the transposed rotation gives another value (the fixture discriminates)
+    assert O.rotation_quant_error(rows, S.T, 2, 4, "f16") != g["obj_value"][0]
+
+
+def test_one_procrustes_step_hand_derived(golden):
+    """One alternation step from R0 = S on rows S^T e_j: every rotated row is a
+    unit vector, quantized to (4095/4096) e_j, so M = (4095/4096) S and the
+    polar factor is S again; history [2^-24, 2^-24]."""
+    g = golden("rotation_objective_d4.txt")
+    S = np.array(g["S_rot"], dtype=np.float64).reshape(4, 4)
+    rows = np.array(g["step_rows"], dtype=np.float64).reshape(4, 4)
+    np.testing.assert_array_equal(rows, (S.T @ np.eye(4)).T)      # d_j = S^T e_j
+    Y = rows @ S.T
+    q = O.quantize(Y, 2, 4, "f16")
+    Yh = O.dequantize(q.codes, q.scale, q.zero, 4)
+    np.testing.assert_array_equal(Yh, g["step_yhat_scale"][0] * np.eye(4))
+    M = Yh.T @ rows
+    np.testing.assert_array_equal(M, g["step_M_scale"][0] * S)
+    np.testing.assert_allclose(O.procrustes(M), S, rtol=0, atol=1e-15)
+    R, hist = O.fit_rotation(rows, S, 2, 4, "f16", 1)
+    np.testing.assert_array_equal(hist, g["step_history"])
+    np.testing.assert_array_equal(R, S)
+    # a full-rank M = R_true * (symmetric positive definite) has polar factor R_true
+    P = np.diag([2.25, 9.0, 0.5625, 36.0])
+    np.testing.assert_allclose(O.procrustes(S @ P), S, rtol=0, atol=1e-15)

@@ -64,3 +64,24 @@ def test_fit_validation():
     assert L.rq_fit_rotation(p(x), 4, 64, 3, 64, 1, p(r), 1, p(r), None) == -3
     assert L.rq_fit_rotation(p(x), 4, 64, 2, 48, 1, p(r), 1, p(r), None) == -2
     assert L.rq_fit_rotation(p(x), 4, 256, 2, 64, 1, p(r), 1, p(r), None) == -2
+
+
+@pytest.mark.parametrize("n,zero_channels", [(512, 4), (40, 0), (40, 3)])
+def test_fit_rank_deficient_stays_orthogonal(n, zero_channels):
+    """Calibration rows with channels that are zero in every row, or fewer
+    rows than channels: M has rank < D, the polar factor is not unique there,
+    and the fit must still return an orthogonal rotation whose action on the
+    rows (hence every objective value) equals the oracle's."""
+    D = 64
+    x = _outlier_residuals(D, n, 11)
+    x[:, np.random.default_rng(3).permutation(D)[:zero_channels]] = 0.0
+    rng = np.random.default_rng(5)
+    q, r = np.linalg.qr(rng.normal(size=(D, D)))
+    R0 = (q * np.sign(np.diag(r))).astype(np.float32)
+    Rl, obj_l = R.fit_rotation(x, R0, 2, D, "f16", iters=3)
+    Ro, obj_o = O.fit_rotation(x.astype(np.float64), R0, 2, D, "f16", 3)
+    Rl64 = Rl.astype(np.float64)
+    np.testing.assert_allclose(Rl64 @ Rl64.T, np.eye(D), rtol=0, atol=1e-6)
+    np.testing.assert_allclose(obj_l, obj_o, rtol=1e-9, atol=0)
+    X = x.astype(np.float64)
+    np.testing.assert_allclose(X @ Rl64.T, X @ Ro.astype(np.float32).astype(np.float64).T, rtol=0, atol=2e-6)
