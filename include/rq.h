@@ -78,6 +78,11 @@ typedef int32_t rq_status;
 #define RQ_ERR_UNSUPPORTED -3   /* a valid request this build has no kernel for */
 #define RQ_ERR_WORKSPACE   -4   /* workspace smaller than the *_workspace_bytes figure */
 #define RQ_ERR_HIP         -5   /* a HIP runtime call or kernel launch failed */
+#define RQ_ERR_SCRATCH     -6   /* request needs more than RQ_NOALLOC_SCRATCH_BYTES */
+
+/* Size of the fixed device scratch of rq_decode_attention_noalloc (one array
+ * per GPU the library runs on, held until the process ends). */
+#define RQ_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
 #define RQ_DTYPE_BF16 0
 #define RQ_DTYPE_F16  1
@@ -224,6 +229,28 @@ rq_status rq_decode_attention_ex(const rq_layout *layout, const void *pool,
                                  const void *tail_v, float softmax_scale, float *out,
                                  void *workspace, size_t workspace_bytes,
                                  const rq_decode_opts *opts, void *stream);
+
+/* rq_decode_attention_ex without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). The query records and split partials go
+ * to a fixed library-owned device array of RQ_NOALLOC_SCRATCH_BYTES per GPU;
+ * the call itself allocates nothing. A request whose workspace
+ * (rq_decode_workspace_bytes with the same arguments and opts->split_pages)
+ * exceeds that size returns RQ_ERR_SCRATCH before touching memory; larger
+ * splits (opts->split_pages) or fewer loops per call shrink it. Every call on
+ * one GPU uses that GPU's one array: calls that can overlap on a GPU (several
+ * streams, several host threads) race on it and must be ordered by the
+ * caller. The array keeps the last call's contents; nothing in it needs to
+ * start at zero. The first call on a device looks up the array's address on
+ * that device (make one call before capturing a graph). Arguments otherwise as
+ * in rq_decode_attention_ex. */
+rq_status rq_decode_attention_noalloc(const rq_layout *layout, const void *pool,
+                                      const int32_t *loops, int32_t n_loops, const void *q,
+                                      const float *rot, const int32_t *block_table,
+                                      const int32_t *seq_lens, int32_t batch,
+                                      int32_t max_blocks_per_seq, const void *tail_k,
+                                      const void *tail_v, float softmax_scale, float *out,
+                                      const rq_decode_opts *opts, void *stream);
 
 /* Decode attention and the deferred compression of the current tokens in the
  * same launches (rit.work summary: a token is compressed once, after its final

@@ -23,8 +23,9 @@ EXPORTED = [
     "rq_encode_pack", "rq_decode_workspace_bytes", "rq_decode_auto_split_pages", "rq_decode_attention",
     "rq_decode_attention_ex", "rq_decode_attention_encode", "rq_fit_rotation", "rq_bf16_workspace_bytes",
     "rq_bf16_auto_split_pages", "rq_bf16_decode_attention", "rq_bf16_decode_attention_ex", "rq_bf16_write",
-    "rq_chunk_workspace_bytes", "rq_chunk_attention",
+    "rq_chunk_workspace_bytes", "rq_chunk_attention", "rq_decode_attention_noalloc",
 ]
+RQ_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class RqError(RuntimeError):
@@ -73,6 +74,8 @@ def lib():
             "rq_decode_attention_encode": (c_int32, [POINTER(RqLayout), P, P, c_int32, P, P, P, P, c_int32, c_int32,
                                                      P, P, c_float, P, P, c_size_t, P, P, c_int32,
                                                      POINTER(RqDecodeOpts), P]),
+            "rq_decode_attention_noalloc": (c_int32, [POINTER(RqLayout), P, P, c_int32, P, P, P, P, c_int32,
+                                                      c_int32, P, P, c_float, P, POINTER(RqDecodeOpts), P]),
             "rq_chunk_workspace_bytes": (c_size_t, [POINTER(RqLayout), c_int32, c_int32, c_int32, c_int32]),
             "rq_chunk_attention": (c_int32, [POINTER(RqLayout), P, c_int32, c_int32, P, P, P, P, c_int32, c_int32,
                                              P, P, c_float, P, P, c_size_t, POINTER(RqDecodeOpts), P]),
@@ -201,6 +204,34 @@ def _opts(split_pages, events):
     if events is not None:
         o.event_main_begin, o.event_main_end = events
     return o
+
+
+def decode_attention_noalloc(layout, pool, loops, q, rot, block_table, seq_lens, tail_k, tail_v,
+                             softmax_scale, out, split_pages=0, stream=None):
+    """rq_decode_attention_noalloc: decode attention with the library's fixed
+    device scratch instead of a caller workspace (nothing is allocated)."""
+    n = len(loops)
+    arr = (c_int32 * max(n, 1))(*[int(x) for x in loops])
+    B, mb = int(block_table.shape[0]), int(block_table.shape[1])
+    H, D = layout.num_heads, layout.head_dim
+    _need(_nbytes(pool) >= pool_bytes(layout) > 0, "pool smaller than rq_pool_bytes(layout)")
+    shp = (n, B, H, D)
+    _need(tuple(q.shape) == shp and q.element_size() == _kv_bytes(layout) and q.is_contiguous(),
+          f"q must be contiguous {shp} in kv_dtype")
+    _need(tuple(out.shape) == shp and out.element_size() == 4 and out.is_contiguous(), f"out must be fp32 {shp}")
+    _need(block_table.element_size() == 4 and block_table.is_contiguous(), "block_table must be int32 [B][M]")
+    _need(seq_lens.numel() == B and seq_lens.element_size() == 4, "seq_lens must be int32 [B]")
+    _need((tail_k is None) == (tail_v is None), "tail_k and tail_v go together")
+    for t in (tail_k, tail_v):
+        if t is not None:
+            _need(tuple(t.shape) == shp and t.element_size() == _kv_bytes(layout) and t.is_contiguous(),
+                  f"tails must be contiguous {shp} in kv_dtype")
+    if layout.mode == RQ_MODE_RESIDUAL and any(int(l) != layout.num_loops - 1 for l in loops):
+        _check_rot(layout, rot)
+    o = _opts(split_pages, None)
+    _check("rq_decode_attention_noalloc", lib().rq_decode_attention_noalloc(
+        ctypes.byref(layout), _ptr(pool), arr, n, _ptr(q), _ptr(rot), _ptr(block_table), _ptr(seq_lens),
+        B, mb, _ptr(tail_k), _ptr(tail_v), float(softmax_scale), _ptr(out), ctypes.byref(o), _stream(stream)))
 
 
 def decode_attention(layout, pool, loops, q, rot, block_table, seq_lens, tail_k, tail_v,

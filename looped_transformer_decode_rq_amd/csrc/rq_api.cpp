@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "rq_internal.h"
 
@@ -124,6 +125,32 @@ static size_t chunk_ws(const Geom &g, int B, int C, int max_blocks, int sp) {
            (size_t)rows * nsplit_of(max_blocks, sp) * partial_floats(g.D) * sizeof(float);
 }
 
+// Scratch of the allocation-free decode entry point: a file-scope device
+// array (one copy per GPU, held until the process ends). Host code never uses
+// the array's name as an address: the device address is looked up once per
+// device with hipGetSymbolAddress and kept.
+__device__ __align__(256) uint8_t scratch[RQ_NOALLOC_SCRATCH_BYTES];
+
+static void *scratch_address(hipError_t *err) {
+    static std::mutex mu;
+    static void *addr[64];
+    int dev = 0;
+    *err = hipGetDevice(&dev);
+    if (*err != hipSuccess) return nullptr;
+    if (dev < 0 || dev >= 64) {
+        *err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (*err != hipSuccess) return nullptr;
+        addr[dev] = p;
+    }
+    return addr[dev];
+}
+
 static size_t bf16_ws(int H, int D, int B, int max_blocks, int sp) {
     return (size_t)B * H * nsplit_of(max_blocks, sp) * (2 + D) * sizeof(float);
 }
@@ -142,6 +169,7 @@ const char *rq_status_string(rq_status s) {
         case RQ_ERR_UNSUPPORTED: return "unsupported configuration";
         case RQ_ERR_WORKSPACE: return "workspace too small";
         case RQ_ERR_HIP: return "HIP runtime or launch failure";
+        case RQ_ERR_SCRATCH: return "request needs more scratch than the allocation-free entry point holds";
         default: return "unknown status";
     }
 }
@@ -271,6 +299,20 @@ rq_status rq_decode_attention_ex(const rq_layout *layout, const void *pool, cons
     return decode_impl(layout, pool, loops, n_loops, q, rot, block_table, seq_lens, batch, max_blocks_per_seq,
                        tail_k, tail_v, softmax_scale, out, workspace, workspace_bytes, opts, stream, nullptr,
                        nullptr, nullptr, 0);
+}
+
+rq_status rq_decode_attention_noalloc(const rq_layout *layout, const void *pool, const int32_t *loops,
+                                      int32_t n_loops, const void *q, const float *rot,
+                                      const int32_t *block_table, const int32_t *seq_lens, int32_t batch,
+                                      int32_t max_blocks_per_seq, const void *tail_k, const void *tail_v,
+                                      float softmax_scale, float *out, const rq_decode_opts *opts, void *stream) {
+    hipError_t err = hipSuccess;
+    void *ws = scratch_address(&err);
+    if (!ws) return RQ_ERR_HIP;
+    const rq_status st = decode_impl(layout, pool, loops, n_loops, q, rot, block_table, seq_lens, batch,
+                                     max_blocks_per_seq, tail_k, tail_v, softmax_scale, out, ws,
+                                     RQ_NOALLOC_SCRATCH_BYTES, opts, stream, nullptr, nullptr, nullptr, 0);
+    return st == RQ_ERR_WORKSPACE ? RQ_ERR_SCRATCH : st;
 }
 
 rq_status rq_decode_attention_encode(const rq_layout *layout, void *pool, const int32_t *loops, int32_t n_loops,
