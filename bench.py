@@ -83,12 +83,12 @@ def token_head_bytes(w, loop):
     return ref + 2 * (D * b // 8 + 2 * m * (D // G) + m)
 
 
-def setup_rq(w, dev, split_pages, split_pages_multi):
+def setup_rq(w, dev, split_pages, split_pages_multi, layer=0, pool_only=False):
     import torch
     import looped_transformer_decode_rq_amd as R
     import workloads as W
     B, N, H, D, L = w.batch, w.context, w.heads, w.head_dim, w.loops
-    st = W.structure(w, 0)
+    st = W.structure(w, layer)
     table, nblk = W.block_table(w)
     lay = R.make_layout(H, D, w.group_size, L, w.res_bits, nblk, w.meta_dtype, w.kv_dtype)
     pool = torch.zeros(R.pool_bytes(lay), dtype=torch.uint8, device=dev)
@@ -97,13 +97,15 @@ def setup_rq(w, dev, split_pages, split_pages_multi):
     cur = torch.empty((L, 2, B, H, D), dtype=kvdt, device=dev)      # current token, all loops
     pos = np.arange(N)
     for b in range(B):
-        kvb = W.kv_torch(w, 0, b, st, dev)
+        kvb = W.kv_torch(w, layer, b, st, dev)
         slots = torch.from_numpy(table[b, pos // 16].astype(np.int64) * 16 + pos % 16).to(dev)
         R.encode_pack(lay, pool, kvb[:, :, :N].contiguous(), rot, slots)
         cur[:, :, b] = kvb[:, :, N]
         del kvb
     torch.cuda.synchronize()
-    q = W.queries_torch(w, 0, dev)
+    if pool_only:
+        return dict(pool=pool, rot=rot, cur=cur)
+    q = W.queries_torch(w, layer, dev)
     s = dict(lay=lay, pool=pool, rot=rot, cur=cur, q=q, table=table, nblk=nblk, st=st,
              d_table=torch.from_numpy(table).to(dev), d_seq=torch.full((B,), N, dtype=torch.int32, device=dev),
              slots_new=torch.from_numpy(table[:, N // 16].astype(np.int64) * 16 + N % 16).to(dev))
@@ -124,31 +126,34 @@ def setup_rq(w, dev, split_pages, split_pages_multi):
     return s
 
 
-def rq_step(w, s, split_pages, events=None, fused=True):
+def rq_step(w, s, split_pages, events=None, fused=True, pool=None):
     """One decode step: the loops' attention calls in order; the new tokens'
     compression rides in the reference-loop call (fused) or follows it."""
     import looped_transformer_decode_rq_amd as R
     tau = 1.0 / np.sqrt(w.head_dim)
     ref = w.loops - 1
+    # pool: one packed cache for every call, or a list with one per loop call
+    pools = pool if isinstance(pool, list) else [s["pool"] if pool is None else pool] * w.loops
     for l in range(w.loops):
         ev = None if events is None else events[l]
         enc = dict(kv_new=s["kv_new"], slot_mapping=s["slots_new"]) if fused and l == ref else {}
-        R.decode_attention(s["lay"], s["pool"], [l], s["qs"][l], s["rot"], s["d_table"], s["d_seq"],
+        R.decode_attention(s["lay"], pools[l], [l], s["qs"][l], s["rot"], s["d_table"], s["d_seq"],
                            s["tk"][l], s["tv"][l], tau, s["out"][l], s["ws"], split_pages=split_pages, events=ev,
                            **enc)
     if not fused:
-        R.encode_pack(s["lay"], s["pool"], s["kv_new"], s["rot"], s["slots_new"])
+        R.encode_pack(s["lay"], pools[ref], s["kv_new"], s["rot"], s["slots_new"])
 
 
-def rq_multi_step(w, s, split_pages, events=None, fused=True):
+def rq_multi_step(w, s, split_pages, events=None, fused=True, pool=None):
     import looped_transformer_decode_rq_amd as R
     tau = 1.0 / np.sqrt(w.head_dim)
+    pool = s["pool"] if pool is None else pool
     enc = dict(kv_new=s["kv_new"], slot_mapping=s["slots_new"]) if fused else {}
-    R.decode_attention(s["lay"], s["pool"], list(range(w.loops)), s["q_all"], s["rot"], s["d_table"], s["d_seq"],
+    R.decode_attention(s["lay"], pool, list(range(w.loops)), s["q_all"], s["rot"], s["d_table"], s["d_seq"],
                        s["tk_all"], s["tv_all"], tau, s["out_all"], s["ws_all"], split_pages=split_pages,
                        events=events, **enc)
     if not fused:
-        R.encode_pack(s["lay"], s["pool"], s["kv_new"], s["rot"], s["slots_new"])
+        R.encode_pack(s["lay"], pool, s["kv_new"], s["rot"], s["slots_new"])
 
 
 def setup_chunk(w, dev, rq, C):
@@ -179,6 +184,218 @@ def chunk_step(w, rq, ch, events=None):
     for l in range(w.loops):
         R.chunk_attention(rq["lay"], rq["pool"], l, ch["q"][l], rq["rot"], rq["d_table"], rq["d_seq"], ch["ck"][l],
                           ch["cv"][l], tau, ch["out"][l], ch["ws"], events=None if events is None else events[l])
+
+
+
+QUERY_RECORD = lambda D: 64 + 11 * D // 2        # per (call, sequence, head): header + 6 + 5 limb planes
+
+
+def split_kernel_bytes(w, loop, nparts):
+    """Algorithmic bytes of one per-loop split-K launch: the packed records of
+    every cached token-head, the query records, the block table and the
+    workgroup partials written."""
+    B, N, H, D = w.batch, w.context, w.heads, w.head_dim
+    res = loop != w.loops - 1
+    return (token_head_bytes(w, loop) * B * H * N + B * H * QUERY_RECORD(D) + B * (-(-N // 16)) * 4
+            + B * H * nparts * (2 + (2 * D if res else D)) * 4)
+
+
+def workload_leg(w, dev, steps, warmup, ev, copies):
+    """One layer of workload w: the per-loop step (one decode call per loop,
+    the new tokens' compression in the reference-loop launch), the multi-loop
+    step and the bf16 baseline step at the same batch. `copies` identical
+    packed layers are used in turn, call by call, so that no call finds the
+    records it reads in the 256 MB last-level cache (these layers are small:
+    a loop call reads 0.3-0.6 GB)."""
+    import torch
+    import looped_transformer_decode_rq_amd as R
+    B, N, H, D, L = w.batch, w.context, w.heads, w.head_dim, w.loops
+    table_w = -(-(N + 1) // 16)
+    probe = R.make_layout(H, D, w.group_size, L, w.res_bits, 1, w.meta_dtype, w.kv_dtype)
+    sp_loop = R.decode_auto_split_pages(probe, 1, B, table_w)
+    sp_multi = R.decode_auto_split_pages(probe, L, B, table_w)
+    sp_bf16 = R.bf16_auto_split_pages(H, B, table_w)
+    log(f"workload {w.name}: setting up {copies} packed layers")
+    rq = setup_rq(w, dev, sp_loop, sp_multi)
+    pools = [rq["pool"]] + [rq["pool"].clone() for _ in range(copies - 1)]
+    turn = [0]
+
+    def next_pools(n):
+        out = [pools[(turn[0] + i) % copies] for i in range(n)]
+        turn[0] += n
+        return out
+
+    pairs = {(k, l): (ev.create(), ev.create()) for k in range(steps) for l in range(L)}
+    t_rq = timed(lambda k: rq_step(w, rq, sp_loop, None if k is None else [pairs[(k, l)] for l in range(L)],
+                                   pool=next_pools(L)), steps, warmup)
+    kms = {l: [] for l in range(L)}
+    for (k, l), (a, b) in pairs.items():
+        kms[l].append(ev.ms(a, b))
+        ev.destroy(a)
+        ev.destroy(b)
+    mpairs = {k: (ev.create(), ev.create()) for k in range(steps)}
+    t_multi = timed(lambda k: rq_multi_step(w, rq, sp_multi, None if k is None else mpairs[k],
+                                            pool=next_pools(1)[0]), steps, warmup)
+    mms = []
+    for k, (a, b) in mpairs.items():
+        mms.append(ev.ms(a, b))
+        ev.destroy(a)
+        ev.destroy(b)
+    nwg = -(-table_w // (4 * sp_loop))
+    per_loop = []
+    for l in range(L):
+        ms = float(np.mean(kms[l]))
+        by = split_kernel_bytes(w, l, nwg)
+        per_loop.append({"loop": l, "bits": 4 if l == L - 1 else int(w.res_bits[l]), "kernel_ms": ms,
+                         "bytes_per_launch": by, "gbs": by / (ms * 1e-3) / 1e9,
+                         "frac_of_peak": by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS})
+    # the dominant kernel: the one with the most time per step (summed over its loops)
+    groups = {}
+    for r in per_loop:
+        key = "reference" if r["loop"] == L - 1 else f"int{r['bits']} residual"
+        groups.setdefault(key, []).append(r)
+    dom_key = max(groups, key=lambda k: sum(r["kernel_ms"] for r in groups[k]))
+    dom = groups[dom_key]
+    dom_ms = float(np.mean([r["kernel_ms"] for r in dom]))
+    dom_bytes = float(np.mean([r["bytes_per_launch"] for r in dom]))
+    stored = token_head_bytes(w, L - 1) + sum(token_head_bytes(w, l) - token_head_bytes(w, L - 1)
+                                              for l in range(L - 1))
+    nsplit = -(-table_w // sp_multi)
+    multi_bytes = (stored * B * H * N + L * B * H * QUERY_RECORD(D) + B * table_w * 4
+                   + (L - 1) * B * H * nsplit * (2 + 2 * D) * 4 + B * H * nsplit * (2 + D) * 4)
+    out = {"workload": w.name, "batch": B, "context": N, "heads": H, "head_dim": D, "loops": L,
+           "res_bits": list(w.res_bits), "group_size": w.group_size,
+           "packed_layers_in_turn": copies,
+           "per_loop_step": {"ms": t_rq * 1e3, "tokens_per_s": B / t_rq},
+           "multi_loop_step": {"ms": t_multi * 1e3, "tokens_per_s": B / t_multi, "kernel_ms": float(np.mean(mms)),
+                               "kernel_gbs": multi_bytes / (float(np.mean(mms)) * 1e-3) / 1e9},
+           "split_kernels": per_loop,
+           "roofline": {"bound": "hbm", "kernel": f"rq_split_kernel ({dom_key} loops)", "kernel_ms": dom_ms,
+                        "bytes_per_launch": dom_bytes, "achieved": dom_bytes / (dom_ms * 1e-3) / 1e9,
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": dom_bytes / (dom_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}}
+    out["multi_loop_step"]["kernel_frac_of_peak"] = out["multi_loop_step"]["kernel_gbs"] / HBM_PEAK_GBS
+    log(f"{w.name}: per-loop step {t_rq * 1e3:.3f} ms, multi-loop step {t_multi * 1e3:.3f} ms; "
+        f"{dom_key} split kernel {dom_ms:.3f} ms ({out['roofline']['frac']:.3f} of peak)")
+    del pools, rq["pool"]
+    b16 = setup_bf16(w, dev, rq, sp_bf16)
+    t_bf = timed(lambda k: bf16_step(w, rq, b16, sp_bf16), steps, warmup)
+    out["bf16_step"] = {"ms": t_bf * 1e3, "tokens_per_s": B / t_bf}
+    out["speedup_per_loop_vs_bf16"] = t_bf / t_rq
+    out["speedup_multi_loop_vs_bf16"] = t_bf / t_multi
+    log(f"{w.name}: bf16 step {t_bf * 1e3:.3f} ms; per-loop {t_bf / t_rq:.2f}x, multi-loop {t_bf / t_multi:.2f}x")
+    del b16, rq
+    torch.cuda.empty_cache()
+    return out
+
+
+def peak_batch_leg(w, dev, steps, warmup):
+    """The 24-layer peak-batch decode step: every layer's packed pool resident
+    (generated layer by layer from the workload recipe), timed as the KV path
+    of a full model step (per layer: one decode call per loop with the new
+    tokens' compression in the reference-loop launch; also the multi-loop
+    form); then the bf16 baseline at the largest batch whose 24 layers of
+    bf16 cache fit in the memory left, timed the same way."""
+    import torch
+    import looped_transformer_decode_rq_amd as R
+    import workloads as W
+    B, N, H, D, L, NL = w.batch, w.context, w.heads, w.head_dim, w.loops, w.layers
+    table_w = -(-(N + 1) // 16)
+    probe = R.make_layout(H, D, w.group_size, L, w.res_bits, 1, w.meta_dtype, w.kv_dtype)
+    sp_loop = R.decode_auto_split_pages(probe, 1, B, table_w)
+    sp_multi = R.decode_auto_split_pages(probe, L, B, table_w)
+    t0 = time.perf_counter()
+    base = setup_rq(w, dev, sp_loop, sp_multi, layer=0)
+    layers = [dict(pool=base["pool"], rot=base["rot"], cur=base["cur"])]
+    for layer in range(1, NL):
+        layers.append(setup_rq(w, dev, sp_loop, sp_multi, layer=layer, pool_only=True))
+        log(f"{w.name}: {layer + 1} of {NL} layers packed")
+    torch.cuda.synchronize()
+    packed_bytes = sum(int(x["pool"].numel()) for x in layers)
+    log(f"{w.name}: {NL} packed layers resident, {packed_bytes / 1e9:.1f} GB ({time.perf_counter() - t0:.0f} s)")
+    tau = 1.0 / np.sqrt(D)
+
+    def rq_full(k, multi):
+        for x in layers:
+            s = dict(base, pool=x["pool"], rot=x["rot"], kv_new=x["cur"])
+            if multi:
+                rq_multi_step(w, s, sp_multi)
+            else:
+                rq_step(w, s, sp_loop)
+
+    t_rq = timed(lambda k: rq_full(k, False), steps, warmup)
+    t_multi = timed(lambda k: rq_full(k, True), steps, warmup)
+    step_bytes = NL * sum(token_head_bytes(w, l) for l in range(L)) * B * H * N
+    out = {"workload": w.name, "layers": NL, "batch": B, "context": N, "packed_bytes_resident": packed_bytes,
+           "per_loop_step": {"ms": t_rq * 1e3, "tokens_per_s": B / t_rq,
+                             "effective_gbs": step_bytes / t_rq / 1e9},
+           "multi_loop_step": {"ms": t_multi * 1e3, "tokens_per_s": B / t_multi},
+           "step": f"{NL} layers x ({L} per-loop decode calls + compression of {B} new tokens); "
+                   "the KV path only (no projections or MLP: no model weights)"}
+    log(f"{w.name}: packed {NL}-layer step {t_rq * 1e3:.2f} ms per-loop, {t_multi * 1e3:.2f} ms multi-loop")
+    del layers, base
+    torch.cuda.empty_cache()
+    # bf16 baseline: 24 layers x L loops x K|V caches of [pages][H][16][D] bf16
+    per_seq = NL * L * 2 * table_w * 16 * H * D * 2
+    free, total = torch.cuda.mem_get_info()
+    reserve = 6 << 30
+    bmax = int(min(B, (free - reserve) // per_seq))
+    out["rq_largest_batch_that_fits"] = int((total - reserve) // (NL * table_w * H * int(
+        R.pool_bytes(probe) // H)))
+    out["bf16_bytes_per_sequence_all_layers"] = per_seq
+    if bmax < 1:
+        out["bf16_baseline"] = {"error": "no bf16 batch fits"}
+        return out
+    wb = w.replace(batch=bmax)
+    table, nblk = W.block_table(wb)
+    d_table = torch.from_numpy(table).to(dev)
+    d_seq = torch.full((bmax,), N, dtype=torch.int32, device=dev)
+    sp_bf16 = R.bf16_auto_split_pages(H, bmax, table_w)
+    ws = torch.empty(R.bf16_workspace_bytes(H, D, bmax, table_w, sp_bf16), dtype=torch.uint8, device=dev)
+    t0 = time.perf_counter()
+    caches = []
+    pos = np.arange(N)
+    for layer in range(NL):
+        st = W.structure(w, layer)
+        kc = [torch.empty((nblk, H, 16, D), dtype=torch.bfloat16, device=dev) for _ in range(L)]
+        vc = [torch.empty_like(kc[0]) for _ in range(L)]
+        cur = torch.empty((L, 2, bmax, H, D), dtype=torch.bfloat16, device=dev)
+        for b in range(bmax):
+            kvb = W.kv_torch(wb, layer, b, st, dev)
+            slots = torch.from_numpy(table[b, pos // 16].astype(np.int64) * 16 + pos % 16).to(dev)
+            for l in range(L):
+                R.bf16_write(kc[l], vc[l], kvb[l, :, :N].contiguous(), slots)
+            cur[:, :, b] = kvb[:, :, N]
+            del kvb
+        caches.append((kc, vc, cur))
+        log(f"{w.name}: bf16 layer {layer + 1} of {NL} written")
+    torch.cuda.synchronize()
+    log(f"{w.name}: bf16 caches of {NL} layers at batch {bmax} resident, "
+        f"{bmax * per_seq / 1e9:.1f} GB ({time.perf_counter() - t0:.0f} s)")
+    q = W.queries_torch(wb, 0, dev)
+    qs = [q[l].contiguous() for l in range(L)]
+    outb = torch.empty((bmax, H, D), device=dev)
+    slots_new = torch.from_numpy(table[:, N // 16].astype(np.int64) * 16 + N % 16).to(dev)
+    tails = [[(c[2][l, 0].contiguous(), c[2][l, 1].contiguous(), c[2][l].contiguous()) for l in range(L)]
+             for c in caches]
+
+    def bf_full(k):
+        for (kc, vc, _), tl in zip(caches, tails):
+            for l in range(L):
+                R.bf16_decode_attention(kc[l], vc[l], qs[l], d_table, d_seq, tl[l][0], tl[l][1], tau, outb, ws,
+                                        split_pages=sp_bf16)
+                R.bf16_write(kc[l], vc[l], tl[l][2], slots_new)
+
+    t_bf = timed(bf_full, steps, warmup)
+    out["bf16_baseline"] = {"batch": bmax, "ms_per_step": t_bf * 1e3, "tokens_per_s": bmax / t_bf,
+                            "cache_bytes_resident": bmax * per_seq}
+    out["peak_throughput_ratio_per_loop"] = (B / t_rq) / (bmax / t_bf)
+    out["peak_throughput_ratio_multi_loop"] = (B / t_multi) / (bmax / t_bf)
+    log(f"{w.name}: bf16 {NL}-layer step at batch {bmax}: {t_bf * 1e3:.2f} ms; peak-throughput ratio "
+        f"{out['peak_throughput_ratio_per_loop']:.2f}x per-loop, {out['peak_throughput_ratio_multi_loop']:.2f}x multi-loop")
+    del caches, tails
+    torch.cuda.empty_cache()
+    return out
 
 
 def direct_baseline(w, dev, rq, bits, split_pages, steps, warmup):
@@ -292,53 +509,109 @@ def graph_leg(w, rq, split_pages, layers, steps, warmup):
             "step": f"{layers} layers x (4 per-loop decode calls + encode of {w.batch} new tokens), one graph"}
 
 
-def cpu_baseline(w, rq, budget_s=12.0):
-    """The fp64 oracle on a bounded sample: decode attention of one (sequence,
-    head) unit per loop, repeated over units until the budget is spent, plus
-    the oracle encode of one step's new tokens; extrapolated to a full step."""
-    import torch
+def _oracle_unit(task):
+    """One (sequence, head) unit of a workload's decode step in the fp64
+    oracle, in a worker process: draw the unit's K/V and query with the
+    workload's recipe (batch 1, one head, the unit's own seed), pack its
+    cache with the oracle encoder (not timed: the cache exists before the
+    step), then time the oracle's decode attention of every loop over it."""
     import oracle as O
     import workloads as W
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = 1
-    B, N, H, D, L = w.batch, w.context, w.heads, w.head_dim, w.loops
-    st = rq["st"]
-    tau = 1.0 / np.sqrt(D)
-    times = {l: [] for l in range(L)}
-    units = 0
-    t_start = time.perf_counter()
+    name, seed = task
+    w = W.get(name).replace(batch=1, heads=1, seed=seed)
+    N, D, L = w.context, w.head_dim, w.loops
+    st = W.structure(w)
+    kv = W.kv_numpy(w, st=st)                                   # [L][2][1][N+1][1][D]
+    q = W.queries_numpy(w)                                      # [L][1][1][D]
     npages = -(-N // 16)
-    pos = np.arange(N)
-    mini = O.PoolLayout(1, D, w.group_size, L, w.res_bits, w.meta_dtype, npages)
-    q_h = rq["q"].float().cpu().numpy().astype(np.float64)
-    cur = rq["cur"].float().cpu().numpy().astype(np.float64)
-    for h in range(H):
-        kvb = W.kv_torch(w, 0, 0, st, torch.device("cuda:0"))
-        kvh = kvb[:, :, :N, h:h + 1].float().cpu().numpy().astype(np.float64)
-        del kvb
-        enc = O.encode(kvh, st["rot32"][h:h + 1], w.res_bits, w.group_size, w.meta_dtype)
-        opool = np.zeros(mini.pool_bytes, np.uint8)
-        O.write_tokens(opool, mini, enc, pos)
-        for l in range(L):
-            t0 = time.perf_counter()
-            O.decode_attention(opool, mini, l, q_h[l, 0:1, h:h + 1], st["rot32"][h:h + 1],
-                               np.arange(npages)[None], [N], tau, cur[l, 0, 0:1, h:h + 1], cur[l, 1, 0:1, h:h + 1])
-            times[l].append(time.perf_counter() - t0)
-        units += 1
-        if time.perf_counter() - t_start > budget_s:
-            break
+    lay = O.PoolLayout(1, D, w.group_size, L, w.res_bits, w.meta_dtype, npages)
+    enc = O.encode(kv[:, :, 0, :N], st["rot32"], w.res_bits, w.group_size, w.meta_dtype)
+    pool = np.zeros(lay.pool_bytes, np.uint8)
+    O.write_tokens(pool, lay, enc, np.arange(N))
+    tau = 1.0 / np.sqrt(D)
     t0 = time.perf_counter()
-    enc_new = O.encode(cur[:, :, :, :, :], st["rot32"], w.res_bits, w.group_size, w.meta_dtype)
-    t_enc = time.perf_counter() - t0
-    step = sum(B * H * float(np.mean(times[l])) for l in range(L)) + t_enc
-    del enc_new
-    return {"value": B / step, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{units} (sequence, head) units x {L} loops of fp64 decode attention over {N} packed tokens "
-                      f"+ fp64 encode of one step's {B} new tokens; step time extrapolated to {B}x{H} units "
-                      f"({step:.1f} s per step)"}
+    for l in range(L):
+        O.decode_attention(pool, lay, l, q[l], st["rot32"], np.arange(npages)[None], [N], tau,
+                           kv[l, 0, :, N], kv[l, 1, :, N])
+    return time.perf_counter() - t0
+
+
+def start_oracle_pools():
+    """Spawn-started worker pools for the oracle timing, created before this
+    process touches the GPU (the workers are fresh interpreters that never do):
+    one single-threaded worker per core of this process's CPU share (at most
+    16), and one more single worker for the 1-core figure."""
+    import multiprocessing as mp
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    saved = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
+    for k in saved:
+        os.environ[k] = "1"
+    try:
+        ctx = mp.get_context("spawn")
+        return cores, ctx.Pool(cores), ctx.Pool(1)
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+
+
+def _oracle_encode_step(w):
+    """Oracle time of one step's compression: every sequence's new token, all
+    loops and heads (one vectorized encode)."""
+    import oracle as O
+    import workloads as W
+    st = W.structure(w)
+    kv = W.kv_numpy(w.replace(context=0), st=st)[:, :, :, 0]     # [L][2][B][H][D]: one token per sequence
+    t0 = time.perf_counter()
+    O.encode(kv, st["rot32"], w.res_bits, w.group_size, w.meta_dtype)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(w, pools, budget_s=12.0):
+    """The fp64 oracle timed on the host's cores.
+
+    The decode step's (sequence, head) units are independent: they run in a
+    pool of single-threaded worker processes, one per core of this process's
+    CPU share. For the benchmark workload, waves of one unit per worker run
+    until the time budget is spent and the step time is extrapolated from the
+    mean unit time; the tiny and the Ouro-like 4096-token workloads run in
+    full. A single worker gives the 1-core figure."""
+    import workloads as W
+    cores, pool, pool1 = pools
+    B, H = w.batch, w.heads
+    out = {"unit": "tokens/s", "cores": cores, "kind": "oracle", "threads_per_core": 1}
+    t_enc = _oracle_encode_step(w)
+    times = []
+    t0 = time.perf_counter()
+    seed = 1000
+    while len(times) < B * H and (not times or time.perf_counter() - t0 < budget_s):
+        n = min(cores, B * H - len(times))
+        times += pool.map(_oracle_unit, [(w.name, seed + i) for i in range(n)])
+        seed += n
+    step = B * H * float(np.mean(times)) / cores + t_enc
+    out["value"] = B / step
+    out["sample"] = (f"{len(times)} of {B * H} (sequence, head) units of {w.name} (each drawn with the workload's "
+                     f"recipe under its own seed; fp64 decode attention of all {w.loops} loops over its "
+                     f"{w.context} packed tokens) on {cores} single-threaded worker processes, plus the fp64 "
+                     f"encode of one step's {B} new tokens; step time {step:.1f} s extrapolated to all units")
+    one = pool1.map(_oracle_unit, [(w.name, 7)])
+    step1 = B * H * float(np.mean(one)) + t_enc
+    out["one_core"] = {"value": B / step1, "ms_per_step": step1 * 1e3,
+                       "sample": f"1 unit on one single-threaded worker, extrapolated to {B * H} units"}
+    full = {}
+    for key in (0, 1):
+        wf = W.get(key)
+        te = _oracle_encode_step(wf)
+        t0 = time.perf_counter()
+        ut = pool.map(_oracle_unit, [(wf.name, 2000 + i) for i in range(wf.batch * wf.heads)])
+        wall = time.perf_counter() - t0
+        full[wf.name] = {"units": len(ut), "decode_s_sum": float(np.sum(ut)), "wall_s_with_packing": wall,
+                         "step_s_on_cores": float(np.sum(ut)) / cores + te,
+                         "tokens_per_s": wf.batch / (float(np.sum(ut)) / cores + te)}
+    out["full_workloads"] = full
+    return out
 
 
 def traffic_from_profiles(kernel_src_hash):
@@ -373,6 +646,10 @@ def main():
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-direct", action="store_true", help="skip the direct per-loop quantization baselines")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the per-layer legs of the 4096-token Ouro-like and the Huginn-like workloads")
+    ap.add_argument("--no-peak-batch", action="store_true",
+                    help="skip the 24-layer peak-batch leg (146.6 GB of packed cache resident)")
     ap.add_argument("--chunk", type=int, default=64,
                     help="queries per sequence of the chunked-prefill leg (0 skips it)")
     ap.add_argument("--graph-layers", type=int, default=4,
@@ -388,6 +665,8 @@ def main():
         print(f"bench.py measures one GPU: this path has no multi-GPU mode (asked for --gpus {args.gpus}); "
               "run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    # the oracle's worker processes start before anything touches the GPU
+    pools = None if args.no_cpu else start_oracle_pools()
 
     import torch
     import looped_transformer_decode_rq_amd as R
@@ -561,10 +840,22 @@ def main():
         del b16
         torch.cuda.empty_cache()
 
+    others = {}
+    if not args.no_other_workloads:
+        for key, copies in (("ouro_h16_d128_l4_b32_n4096", 3), ("huginn_h55_d96_l8_b8_n8192_mixed", 2)):
+            others[key] = workload_leg(W.get(key), dev, args.steps, args.warmup, ev, copies)
+    peak = None
+    if not args.no_peak_batch:
+        peak = peak_batch_leg(W.get("ouro_24layer_h16_d128_l4_b128_n8192"), dev, max(3, args.steps // 4),
+                              min(args.warmup, 2))
+
     cpu = None
     if not args.no_cpu:
         log("timing the fp64 oracle on the host")
-        cpu = cpu_baseline(w, rq)
+        cpu = cpu_baseline(w, pools)
+        for p in pools[1:]:
+            p.close()
+            p.join()
 
     traffic = traffic_from_profiles(kernel_src_hash()) if w.name == DEFAULT_WORKLOAD else None
 
@@ -581,7 +872,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4/int2 codes x fp32 (bf16 inputs, fp16 metadata)",
+        "dtype": ("int4/int2 codes; scores: exact int32 dot products (v_dot8_i32_i4) of the codes with a "
+                  "per-slice fixed-point query (24-bit q, 20-bit q' = R_K q); fp32 softmax; V on f16 matrix cores "
+                  "(weights split into fp16 hi+lo, codes exact) with fp32 accumulation; bf16 inputs, fp16 "
+                  "metadata, fp32 output"),
         "data": "synthetic (seeded generator; no model weights)",
         "config": {"workload": w.name, "layers": 1, "batch": B, "context": N, "heads": H, "head_dim": D,
                    "loops": L, "group_size": w.group_size, "res_bits": list(w.res_bits), "block_size": 16,
@@ -597,6 +891,8 @@ def main():
         "ref_loop_kernel": {"ms": ref_ms, "gbs": ref_bytes / (ref_ms * 1e-3) / 1e9, "bytes_per_launch": ref_bytes,
                             "traffic": measured("reference")},
         "multi_loop": {"tokens_per_s": B / t_multi, "ms_per_step": t_multi * 1e3,
+                       "note": "needs every loop's query of a layer at once; a looped model produces them one "
+                               "after another, so its decode step is the per-loop step (value)",
                        "step": f"one decode call with all {L} loops' queries (each reference page read once) "
                                f"+ encode of {B} new tokens in the same launch",
                        "kernel": f"rq_multi_kernel<{D}> ({L} waves per split workgroup)",
@@ -609,6 +905,8 @@ def main():
         "direct_baselines": direct or None,
         "attention_rel_l2_vs_bf16": errors or None,
         "stored_bytes_per_token_head": {"rq": stored, "bf16": 2 * D * 2 * L},
+        "other_workloads": others or None,
+        "peak_batch": peak,
         "cpu_baseline": cpu,
         "context_from_pages": {"kv_storage_reduction": "80.7% (theoretical, mixed precision)",
                                "fixed_batch_decode_speedup": "up to 2.73x on RTX 5090",
