@@ -710,11 +710,9 @@ def main():
     ref_ms = float(np.mean(split_ms[L - 1]))
     nwg = -(-rq["table"].shape[1] // (4 * sp_loop))     # one partial per 4-wave split workgroup
     nsplit = -(-rq["table"].shape[1] // sp_multi)       # multi-loop: one partial per split and loop
-    qp = 64 + 11 * D // 2                              # query record: header + 6 + 5 limb planes
-    res_bytes = (token_head_bytes(w, 0) * B * H * N + B * H * qp + B * N // 16 * 4
-                 + B * H * nwg * (2 + 2 * D) * 4)
-    ref_bytes = (token_head_bytes(w, L - 1) * B * H * N + B * H * qp + B * N // 16 * 4
-                 + B * H * nwg * (2 + D) * 4)
+    qp = QUERY_RECORD(D)
+    res_bytes = split_kernel_bytes(w, 0, nwg)
+    ref_bytes = split_kernel_bytes(w, L - 1, nwg)
     achieved = res_bytes / (res_ms * 1e-3) / 1e9
     # whole step: packed reads of the 4 calls + q/out/tails + rotations + encode traffic
     kvsz = 2 if w.kv_dtype == "bf16" else 4
