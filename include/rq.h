@@ -297,6 +297,28 @@ rq_status rq_fit_rotation(const float *samples, int64_t n, int32_t head_dim, int
                           int32_t group_size, int32_t meta_dtype, const float *rot0, int32_t iters,
                           float *rot_out, double *objective);
 
+/* The same fit with the calibration rows in DEVICE memory: every pass of the
+ * alternation (rotate each row, quantize it with the group quantizer,
+ * accumulate the squared error and M = sum_i yhat_i d_i^T) runs in float64 on
+ * the GPU with a fixed summation order (deterministic); the polar factor of M
+ * is taken on the host as in rq_fit_rotation. Unlike the decode calls this
+ * one synchronizes `stream` once per pass (it reads M back each iteration);
+ * it is a calibration step, not part of the decode path.
+ *   samples     [n][head_dim] float32, DEVICE, 4-byte aligned
+ *   rot0, iters, rot_out, objective: HOST, as in rq_fit_rotation
+ *   workspace   DEVICE, 256-byte aligned, rq_fit_workspace_bytes(head_dim)
+ *               bytes (RQ_ERR_WORKSPACE if smaller)
+ * head_dim 64, 96 or 128 (RQ_ERR_UNSUPPORTED otherwise), a multiple of
+ * group_size; bits 2 or 4; meta_dtype RQ_DTYPE_F16 or RQ_DTYPE_F32. Results
+ * equal rq_fit_rotation's up to the summation order of float64 sums. */
+rq_status rq_fit_rotation_device(const float *samples, int64_t n, int32_t head_dim, int32_t bits,
+                                 int32_t group_size, int32_t meta_dtype, const float *rot0,
+                                 int32_t iters, float *rot_out, double *objective, void *workspace,
+                                 size_t workspace_bytes, void *stream);
+
+/* Workspace bytes of rq_fit_rotation_device for a head dim (0 if unsupported). */
+size_t rq_fit_workspace_bytes(int32_t head_dim);
+
 /* Chunked prefill over the packed cache: a chunk of `chunk` new tokens per
  * sequence, for one loop, attends every cached token of that loop and,
  * causally, the chunk's own uncompressed K/V (query i sees chunk tokens

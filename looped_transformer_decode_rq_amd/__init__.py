@@ -11,5 +11,6 @@ from ._lib import (  # noqa: F401
     encode_pack, decode_workspace_bytes, decode_auto_split_pages, decode_attention, decode_attention_noalloc,
     RQ_NOALLOC_SCRATCH_BYTES, bf16_workspace_bytes,
     bf16_auto_split_pages, chunk_workspace_bytes, chunk_attention,
-    bf16_decode_attention, bf16_write, status_string, fit_rotation, EXPORTED,
+    bf16_decode_attention, bf16_write, status_string, fit_rotation, fit_rotation_device, fit_workspace_bytes,
+    EXPORTED,
 )

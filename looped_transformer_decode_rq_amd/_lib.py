@@ -24,6 +24,7 @@ EXPORTED = [
     "rq_decode_attention_ex", "rq_decode_attention_encode", "rq_fit_rotation", "rq_bf16_workspace_bytes",
     "rq_bf16_auto_split_pages", "rq_bf16_decode_attention", "rq_bf16_decode_attention_ex", "rq_bf16_write",
     "rq_chunk_workspace_bytes", "rq_chunk_attention", "rq_decode_attention_noalloc",
+    "rq_fit_rotation_device", "rq_fit_workspace_bytes",
 ]
 RQ_NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -80,6 +81,9 @@ def lib():
             "rq_chunk_attention": (c_int32, [POINTER(RqLayout), P, c_int32, c_int32, P, P, P, P, c_int32, c_int32,
                                              P, P, c_float, P, P, c_size_t, POINTER(RqDecodeOpts), P]),
             "rq_fit_rotation": (c_int32, [P, c_int64, c_int32, c_int32, c_int32, c_int32, P, c_int32, P, P]),
+            "rq_fit_rotation_device": (c_int32, [P, c_int64, c_int32, c_int32, c_int32, c_int32, P, c_int32, P, P,
+                                                 P, c_size_t, P]),
+            "rq_fit_workspace_bytes": (c_size_t, [c_int32]),
             "rq_bf16_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32]),
             "rq_bf16_auto_split_pages": (c_int32, [c_int32, c_int32, c_int32]),
             "rq_bf16_decode_attention": (c_int32, [c_int32, c_int32, c_int32, c_int32, P, P, P, P, P, c_int32,
@@ -369,4 +373,28 @@ def fit_rotation(samples, rot0, bits, group_size, meta_dtype="f16", iters=10):
     _check("rq_fit_rotation", lib().rq_fit_rotation(
         x.ctypes.data_as(c_void_p), n, D, int(bits), int(group_size), md, r0.ctypes.data_as(c_void_p),
         int(iters), out.ctypes.data_as(c_void_p), obj.ctypes.data_as(c_void_p)))
+    return out, obj
+
+
+def fit_workspace_bytes(head_dim) -> int:
+    return lib().rq_fit_workspace_bytes(int(head_dim))
+
+
+def fit_rotation_device(samples, rot0, bits, group_size, workspace, meta_dtype="f16", iters=10, stream=None):
+    """rq_fit_rotation_device: samples a DEVICE tensor [n][D] float32, rot0 a
+    host array [D][D] float32, workspace a device uint8 tensor of
+    fit_workspace_bytes(D) -> (fitted R [D][D] float32, objective
+    [iters + 1] float64), both on the host."""
+    import numpy as np
+    n, D = (int(v) for v in samples.shape)
+    _need(samples.element_size() == 4 and samples.is_contiguous(), "samples must be contiguous float32 [n][D]")
+    r0 = np.ascontiguousarray(rot0, dtype=np.float32)
+    _need(r0.shape == (D, D), "rot0 must be [D][D]")
+    out = np.empty((D, D), np.float32)
+    obj = np.empty(int(iters) + 1, np.float64)
+    md = _DT[meta_dtype] if isinstance(meta_dtype, str) else meta_dtype
+    _check("rq_fit_rotation_device", lib().rq_fit_rotation_device(
+        _ptr(samples), n, D, int(bits), int(group_size), md, r0.ctypes.data_as(c_void_p), int(iters),
+        out.ctypes.data_as(c_void_p), obj.ctypes.data_as(c_void_p), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
     return out, obj

@@ -176,6 +176,79 @@ void procrustes(const std::vector<double> &M, int D, std::vector<double> &R) {
 
 using namespace rq;
 
+namespace rq {
+namespace {
+
+// Workspace of the device fit: R, M and the error, then the per-workgroup
+// partials (float64 throughout).
+size_t fit_ws_off_m(int D) { return (size_t)D * D * 8; }
+size_t fit_ws_off_err(int D) { return 2 * (size_t)D * D * 8; }
+size_t fit_ws_off_mpart(int D) { return 2 * (size_t)D * D * 8 + 256; }
+size_t fit_ws_off_epart(int D) { return fit_ws_off_mpart(D) + (size_t)kFitBlocks * D * D * 8; }
+size_t fit_ws_bytes(int D) { return fit_ws_off_epart(D) + (size_t)kFitBlocks * 8; }
+
+}  // namespace
+}  // namespace rq
+
+extern "C" size_t rq_fit_workspace_bytes(int32_t head_dim) {
+    if (head_dim != 64 && head_dim != 96 && head_dim != 128) return 0;
+    return rq::fit_ws_bytes(head_dim);
+}
+
+extern "C" rq_status rq_fit_rotation_device(const float *samples, int64_t n, int32_t head_dim, int32_t bits,
+                                            int32_t group_size, int32_t meta_dtype, const float *rot0,
+                                            int32_t iters, float *rot_out, double *objective, void *workspace,
+                                            size_t workspace_bytes, void *stream) {
+    using namespace rq;
+    if (!samples || !rot0 || !rot_out || !workspace) return RQ_ERR_NULL;
+    const int D = head_dim, G = group_size;
+    if (n < 1 || G < 1 || D % G != 0 || iters < 0 || iters > 10000) return RQ_ERR_SHAPE;
+    if (D != 64 && D != 96 && D != 128) return RQ_ERR_UNSUPPORTED;
+    if (bits != 2 && bits != 4) return RQ_ERR_UNSUPPORTED;
+    if (meta_dtype != RQ_DTYPE_F16 && meta_dtype != RQ_DTYPE_F32) return RQ_ERR_UNSUPPORTED;
+    if (workspace_bytes < fit_ws_bytes(D)) return RQ_ERR_WORKSPACE;
+    if (((uintptr_t)workspace & 255) != 0 || ((uintptr_t)samples & 3) != 0) return RQ_ERR_SHAPE;
+    uint8_t *ws = (uint8_t *)workspace;
+    const hipStream_t st = (hipStream_t)stream;
+    FitPass p;
+    p.x = samples; p.n = n; p.D = D; p.bits = bits; p.G = G; p.meta = meta_dtype;
+    p.r = (const double *)ws;
+    p.m = (double *)(ws + fit_ws_off_m(D));
+    p.err = (double *)(ws + fit_ws_off_err(D));
+    p.mpart = (double *)(ws + fit_ws_off_mpart(D));
+    p.epart = (double *)(ws + fit_ws_off_epart(D));
+    p.stream = st;
+    std::vector<double> R((size_t)D * D), M((size_t)D * D);
+    for (size_t i = 0; i < R.size(); ++i) R[i] = (double)rot0[i];
+    std::vector<double> best(R);
+    double best_err = 0.0;
+    // one pass per rotation: its error, and M for the next Procrustes step
+    auto pass = [&](double *err) -> bool {
+        double e = 0.0;
+        if (hipMemcpyAsync((void *)p.r, R.data(), R.size() * 8, hipMemcpyHostToDevice, st) != hipSuccess) return false;
+        if (launch_fit_pass(p) != hipSuccess) return false;
+        if (hipMemcpyAsync(M.data(), p.m, M.size() * 8, hipMemcpyDeviceToHost, st) != hipSuccess) return false;
+        if (hipMemcpyAsync(&e, p.err, 8, hipMemcpyDeviceToHost, st) != hipSuccess) return false;
+        if (hipStreamSynchronize(st) != hipSuccess) return false;
+        *err = e / (double)n;
+        return true;
+    };
+    if (!pass(&best_err)) return RQ_ERR_HIP;
+    if (objective) objective[0] = best_err;
+    for (int it = 0; it < iters; ++it) {
+        procrustes(M, D, R);
+        double err = 0.0;
+        if (!pass(&err)) return RQ_ERR_HIP;
+        if (objective) objective[it + 1] = err;
+        if (err < best_err) {
+            best_err = err;
+            best = R;
+        }
+    }
+    for (size_t i = 0; i < best.size(); ++i) rot_out[i] = (float)best[i];
+    return RQ_OK;
+}
+
 extern "C" rq_status rq_fit_rotation(const float *samples, int64_t n, int32_t head_dim, int32_t bits,
                                      int32_t group_size, int32_t meta_dtype, const float *rot0, int32_t iters,
                                      float *rot_out, double *objective) {

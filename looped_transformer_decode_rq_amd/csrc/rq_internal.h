@@ -116,6 +116,20 @@ struct EncodeCall {
 
 hipError_t launch_encode(const EncodeCall &c);
 
+// One pass of the rotation fit over device-resident calibration rows (float64):
+// y = R d per row, its group quantization, the squared error and M = sum yhat d^T.
+constexpr int kFitBlocks = 64;     // workgroups of a pass (one partial M each)
+struct FitPass {
+    const float *x;                // [n][D] device
+    int64_t n;
+    int D, bits, G, meta;
+    const double *r;               // [D][D] device
+    double *mpart, *epart;         // workspace: [kFitBlocks][D][D], [kFitBlocks]
+    double *m, *err;               // workspace: [D][D], [1]
+    hipStream_t stream;
+};
+hipError_t launch_fit_pass(const FitPass &p);
+
 struct Bf16Call {
     int H, D, nblk;
     const uint16_t *kc, *vc;

@@ -85,3 +85,22 @@ def test_fit_rank_deficient_stays_orthogonal(n, zero_channels):
     np.testing.assert_allclose(obj_l, obj_o, rtol=1e-9, atol=0)
     X = x.astype(np.float64)
     np.testing.assert_allclose(X @ Rl64.T, X @ Ro.astype(np.float32).astype(np.float64).T, rtol=0, atol=2e-6)
+
+
+def test_fit_device_validation():
+    """Argument checks of the device fit that return before any GPU work."""
+    import ctypes
+    L = R.lib()
+    r = np.eye(64, dtype=np.float32)
+    p = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    assert R.fit_workspace_bytes(64) > 64 * 64 * 8 * 64
+    assert R.fit_workspace_bytes(80) == 0
+    fake = ctypes.c_void_p(256)          # never dereferenced: every call below fails validation first
+    ws = ctypes.c_void_p(4096)
+    big = R.fit_workspace_bytes(64)
+    assert L.rq_fit_rotation_device(None, 4, 64, 2, 64, 1, p(r), 1, p(r), None, ws, big, None) == -1
+    assert L.rq_fit_rotation_device(fake, 0, 64, 2, 64, 1, p(r), 1, p(r), None, ws, big, None) == -2
+    assert L.rq_fit_rotation_device(fake, 4, 64, 3, 64, 1, p(r), 1, p(r), None, ws, big, None) == -3
+    assert L.rq_fit_rotation_device(fake, 4, 80, 2, 16, 1, p(r), 1, p(r), None, ws, big, None) == -3
+    assert L.rq_fit_rotation_device(fake, 4, 64, 2, 48, 1, p(r), 1, p(r), None, ws, big, None) == -2
+    assert L.rq_fit_rotation_device(fake, 4, 64, 2, 64, 1, p(r), 1, p(r), None, ws, big - 8, None) == -4
