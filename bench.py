@@ -724,6 +724,31 @@ def main():
     step_gbs = step_bytes / t_rq / 1e9
     log(f"packed step {t_rq * 1e3:.3f} ms; residual split kernel {res_ms:.3f} ms ({achieved:.0f} GB/s)")
 
+    # the streaming reference of the per-loop split kernel: the same grid, ring
+    # and loads over the same page records, no attention arithmetic
+    stream_ref = {}
+    for key, l in (("residual", 0), ("reference", L - 1)):
+        sp_ev = [(ev.create(), ev.create()) for _ in range(args.steps)]
+
+        def probe_fn(k, l=l, sp_ev=sp_ev):
+            R.decode_stream_probe(rq["lay"], rq["pool"], l, rq["d_table"], rq["d_seq"], rq["ws"],
+                                  split_pages=sp_loop, events=None if k is None else sp_ev[k])
+
+        timed(probe_fn, args.steps, args.warmup)
+        pms = float(np.mean([ev.ms(a, b) for a, b in sp_ev]))
+        for a, b in sp_ev:
+            ev.destroy(a)
+            ev.destroy(b)
+        pbytes = token_head_bytes(w, l) * B * H * N + B * (-(-N // 16)) * 4
+        stream_ref[key] = {"kernel_ms": pms, "bytes_per_launch": pbytes, "gbs": pbytes / (pms * 1e-3) / 1e9,
+                           "frac_of_peak": pbytes / (pms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    stream_ref["split_kernel_frac_of_reference"] = {
+        "residual": (res_bytes / (res_ms * 1e-3) / 1e9) / stream_ref["residual"]["gbs"],
+        "reference": (ref_bytes / (ref_ms * 1e-3) / 1e9) / stream_ref["reference"]["gbs"]}
+    log(f"streaming reference (same loads, no arithmetic): residual {stream_ref['residual']['kernel_ms']:.3f} ms "
+        f"({stream_ref['residual']['gbs']:.0f} GB/s), reference {stream_ref['reference']['kernel_ms']:.3f} ms "
+        f"({stream_ref['reference']['gbs']:.0f} GB/s)")
+
     # multi-loop mode: the same step with the 4 loops' queries in one call
     mpairs = {k: (ev.create(), ev.create()) for k in range(args.steps)}
 
@@ -886,6 +911,7 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured("residual"),
                      "kernel": f"rq_split_kernel<{D},{w.res_bits[0]},{w.meta_dtype == 'f32'}> (residual loop)",
                      "kernel_ms": res_ms, "bytes_per_launch": res_bytes},
+        "stream_reference": stream_ref,
         "ref_loop_kernel": {"ms": ref_ms, "gbs": ref_bytes / (ref_ms * 1e-3) / 1e9, "bytes_per_launch": ref_bytes,
                             "traffic": measured("reference")},
         "multi_loop": {"tokens_per_s": B / t_multi, "ms_per_step": t_multi * 1e3,

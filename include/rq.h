@@ -230,6 +230,25 @@ rq_status rq_decode_attention_ex(const rq_layout *layout, const void *pool,
                                  void *workspace, size_t workspace_bytes,
                                  const rq_decode_opts *opts, void *stream);
 
+/* Bandwidth reference of the decode call of one loop: runs the per-loop split
+ * kernel's grid, ring, block-table walk and direct-to-LDS loads over the same
+ * page records (reference and, for a residual loop, the loop's own records)
+ * with no attention arithmetic -- every landed stage is folded into a
+ * per-workgroup checksum -- so its duration is the rate at which this access
+ * pattern streams the packed cache from HBM (the ceiling of the decode
+ * kernel's bandwidth, ResidualQuant being bound by the bytes it reads: arXiv
+ * 2610.10381 abstract). No query prep, merge or output. The checksums go to
+ * the start of the workspace as uint32 [batch][H][workgroups per sequence][4
+ * waves] (workgroups per sequence = ceil(max_blocks_per_seq / (4 *
+ * split_pages))); the workspace is sized as for rq_decode_attention_ex with
+ * one loop (rq_decode_workspace_bytes(layout, 1, batch, max_blocks_per_seq,
+ * opts->split_pages)); opts as in rq_decode_attention_ex (split_pages, timing
+ * events around the kernel). Nothing is written to the pool. */
+rq_status rq_decode_stream_probe(const rq_layout *layout, const void *pool, int32_t loop,
+                                 const int32_t *block_table, const int32_t *seq_lens, int32_t batch,
+                                 int32_t max_blocks_per_seq, void *workspace, size_t workspace_bytes,
+                                 const rq_decode_opts *opts, void *stream);
+
 /* rq_decode_attention_ex without a caller workspace, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation). The query records and split partials go

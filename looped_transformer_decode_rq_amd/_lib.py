@@ -24,7 +24,7 @@ EXPORTED = [
     "rq_decode_attention_ex", "rq_decode_attention_encode", "rq_fit_rotation", "rq_bf16_workspace_bytes",
     "rq_bf16_auto_split_pages", "rq_bf16_decode_attention", "rq_bf16_decode_attention_ex", "rq_bf16_write",
     "rq_chunk_workspace_bytes", "rq_chunk_attention", "rq_decode_attention_noalloc",
-    "rq_fit_rotation_device", "rq_fit_workspace_bytes",
+    "rq_fit_rotation_device", "rq_fit_workspace_bytes", "rq_decode_stream_probe",
 ]
 RQ_NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -84,6 +84,8 @@ def lib():
             "rq_fit_rotation_device": (c_int32, [P, c_int64, c_int32, c_int32, c_int32, c_int32, P, c_int32, P, P,
                                                  P, c_size_t, P]),
             "rq_fit_workspace_bytes": (c_size_t, [c_int32]),
+            "rq_decode_stream_probe": (c_int32, [POINTER(RqLayout), P, c_int32, P, P, c_int32, c_int32, P, c_size_t,
+                                                 POINTER(RqDecodeOpts), P]),
             "rq_bf16_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32]),
             "rq_bf16_auto_split_pages": (c_int32, [c_int32, c_int32, c_int32]),
             "rq_bf16_decode_attention": (c_int32, [c_int32, c_int32, c_int32, c_int32, P, P, P, P, P, c_int32,
@@ -398,3 +400,17 @@ def fit_rotation_device(samples, rot0, bits, group_size, workspace, meta_dtype="
         out.ctypes.data_as(c_void_p), obj.ctypes.data_as(c_void_p), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
     return out, obj
+
+
+def decode_stream_probe(layout, pool, loop, block_table, seq_lens, workspace, split_pages=0, events=None,
+                        stream=None):
+    """rq_decode_stream_probe: the per-loop decode kernel's loads of loop
+    `loop` with no attention arithmetic (an HBM-rate reference)."""
+    B, mb = int(block_table.shape[0]), int(block_table.shape[1])
+    _need(_nbytes(pool) >= pool_bytes(layout) > 0, "pool smaller than rq_pool_bytes(layout)")
+    _need(block_table.element_size() == 4 and block_table.is_contiguous(), "block_table must be int32 [B][M]")
+    _need(seq_lens.numel() == B and seq_lens.element_size() == 4, "seq_lens must be int32 [B]")
+    o = _opts(split_pages, events)
+    _check("rq_decode_stream_probe", lib().rq_decode_stream_probe(
+        ctypes.byref(layout), _ptr(pool), int(loop), _ptr(block_table), _ptr(seq_lens), B, mb, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), ctypes.byref(o), _stream(stream)))

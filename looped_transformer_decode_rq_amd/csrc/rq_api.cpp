@@ -242,7 +242,7 @@ static rq_status decode_impl(const rq_layout *layout, const void *pool, const in
                              int32_t batch, int32_t max_blocks_per_seq, const void *tail_k, const void *tail_v,
                              float softmax_scale, float *out, void *workspace, size_t workspace_bytes,
                              const rq_decode_opts *opts, void *stream, void *enc_pool, const void *kv_new,
-                             const int64_t *slot_mapping, int32_t num_tokens) {
+                             const int64_t *slot_mapping, int32_t num_tokens, bool stream_probe = false) {
     Geom g;
     rq_status st = make_geom(layout, &g);
     if (st != RQ_OK) return st;
@@ -263,7 +263,8 @@ static rq_status decode_impl(const rq_layout *layout, const void *pool, const in
     if (sp_req < 0) return RQ_ERR_SHAPE;
     if (sp_req > kMaxSplitPages) return RQ_ERR_UNSUPPORTED;
     if (batch == 0) return RQ_OK;
-    if (!pool || !q || !block_table || !seq_lens || !out || (any_res && !rot)) return RQ_ERR_NULL;
+    if (!pool || !block_table || !seq_lens) return RQ_ERR_NULL;
+    if (!stream_probe && (!q || !out || (any_res && !rot))) return RQ_ERR_NULL;
     if (!aligned(pool, 16)) return RQ_ERR_SHAPE;
     if ((int64_t)max_blocks_per_seq * 16 > (int64_t)1 << 30) return RQ_ERR_SHAPE;
     const int sp = sp_req > 0 ? sp_req : auto_split_pages(batch * g.H, max_blocks_per_seq, multi_mode(g, n_loops));
@@ -287,6 +288,8 @@ static rq_status decode_impl(const rq_layout *layout, const void *pool, const in
     c.ev_end = opts ? (hipEvent_t)opts->event_main_end : nullptr;
     c.stream = (hipStream_t)stream;
     c.enc_pool = (uint8_t *)enc_pool; c.enc_kv = kv_new; c.enc_slots = slot_mapping; c.enc_T = num_tokens;
+    c.stream_probe = stream_probe;
+    if (stream_probe) c.partials = (float *)workspace;   // the checksums, at the start of the workspace
     return launch_decode(c) == hipSuccess ? RQ_OK : RQ_ERR_HIP;
 }
 
@@ -313,6 +316,19 @@ rq_status rq_decode_attention_noalloc(const rq_layout *layout, const void *pool,
                                      max_blocks_per_seq, tail_k, tail_v, softmax_scale, out, ws,
                                      RQ_NOALLOC_SCRATCH_BYTES, opts, stream, nullptr, nullptr, nullptr, 0);
     return st == RQ_ERR_WORKSPACE ? RQ_ERR_SCRATCH : st;
+}
+
+rq_status rq_decode_stream_probe(const rq_layout *layout, const void *pool, int32_t loop, const int32_t *block_table,
+                                 const int32_t *seq_lens, int32_t batch, int32_t max_blocks_per_seq,
+                                 void *workspace, size_t workspace_bytes, const rq_decode_opts *opts, void *stream) {
+    Geom g;
+    const rq_status st = make_geom(layout, &g);
+    if (st != RQ_OK) return st;
+    if (loop < 0 || loop >= g.L) return RQ_ERR_SHAPE;
+    const int32_t loops[1] = {loop};
+    return decode_impl(layout, pool, loops, 1, nullptr, nullptr, block_table, seq_lens, batch, max_blocks_per_seq,
+                       nullptr, nullptr, 1.0f, nullptr, workspace, workspace_bytes, opts, stream, nullptr, nullptr,
+                       nullptr, 0, true);
 }
 
 rq_status rq_decode_attention_encode(const rq_layout *layout, void *pool, const int32_t *loops, int32_t n_loops,

@@ -763,6 +763,35 @@ struct StageGeom {
     static_assert(NST * BYTES >= partial_floats(D) * 4, "a wave's partial fits in its stages");
 };
 
+// This lane's piece of each of a stage's direct-to-LDS instructions: the page
+// of the step it belongs to and its byte offset in that page's slab.
+template <class SG, int RB>
+__device__ __forceinline__ void stage_pieces(const SplitArgs &a, int lane, int *doff, int *dpg) {
+#pragma unroll
+    for (int i = 0; i < SG::NI; ++i) {
+        const int byte = 16 * (64 * i + lane);
+        int off = 0, pg = 0;
+        if (byte < SG::O_RV) {
+            pg = byte / SG::CB_REF; off = a.ref_off + byte % SG::CB_REF;
+        } else if (byte < SG::O_SK) {
+            const int w = byte - SG::O_RV; pg = w / SG::CB_REF; off = a.ref_off + a.ref_rec + w % SG::CB_REF;
+        } else if (RB != 0 && byte < SG::O_SV) {
+            const int w = byte - SG::O_SK; pg = w / SG::CB_RES; off = a.res_off + w % SG::CB_RES;
+        } else if (RB != 0 && byte < SG::O_M) {
+            const int w = byte - SG::O_SV; pg = w / SG::CB_RES; off = a.res_off + a.res_rec + w % SG::CB_RES;
+        } else if (byte < SG::BYTES) {
+            const int w0 = byte - SG::O_M; pg = w0 / SG::MP;
+            const int w = w0 % SG::MP;
+            if (w < SG::MB) off = a.ref_off + SG::CB_REF + w;
+            else if (w < 2 * SG::MB) off = a.ref_off + a.ref_rec + SG::CB_REF + (w - SG::MB);
+            else if (w < 3 * SG::MB + SG::AB) off = a.res_off + SG::CB_RES + (w - 2 * SG::MB);
+            else off = a.res_off + a.res_rec + SG::CB_RES + (w - 3 * SG::MB - SG::AB);
+        }
+        doff[i] = off;
+        dpg[i] = pg;
+    }
+}
+
 // Split-K decode of one loop over packed pages. One wave per split (4 per
 // workgroup, the same (sequence, head)); each wave streams its pages through
 // a ring of NST LDS stages with NST-1 page steps in flight while one is
@@ -832,29 +861,7 @@ __global__ __launch_bounds__(256, 4) void rq_split_kernel(SplitArgs a) {
 
     // this lane's piece of each direct-to-LDS instruction: (page of the step, byte offset in the slab)
     int doff[NI], dpg[NI];
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-        const int byte = 16 * (64 * i + lane);
-        int off = 0, pg = 0;
-        if (byte < SG::O_RV) {
-            pg = byte / SG::CB_REF; off = a.ref_off + byte % SG::CB_REF;
-        } else if (byte < SG::O_SK) {
-            const int w = byte - SG::O_RV; pg = w / SG::CB_REF; off = a.ref_off + a.ref_rec + w % SG::CB_REF;
-        } else if (RB != 0 && byte < SG::O_SV) {
-            const int w = byte - SG::O_SK; pg = w / SG::CB_RES; off = a.res_off + w % SG::CB_RES;
-        } else if (RB != 0 && byte < SG::O_M) {
-            const int w = byte - SG::O_SV; pg = w / SG::CB_RES; off = a.res_off + a.res_rec + w % SG::CB_RES;
-        } else if (byte < SG::BYTES) {
-            const int w0 = byte - SG::O_M; pg = w0 / SG::MP;
-            const int w = w0 % SG::MP;
-            if (w < SG::MB) off = a.ref_off + SG::CB_REF + w;
-            else if (w < 2 * SG::MB) off = a.ref_off + a.ref_rec + SG::CB_REF + (w - SG::MB);
-            else if (w < 3 * SG::MB + SG::AB) off = a.res_off + SG::CB_RES + (w - 2 * SG::MB);
-            else off = a.res_off + a.res_rec + SG::CB_RES + (w - 3 * SG::MB - SG::AB);
-        }
-        doff[i] = off;
-        dpg[i] = pg;
-    }
+    stage_pieces<SG, RB>(a, lane, doff, dpg);
 
     // this lane's reads inside a stage: four lane offsets; the other reads
     // sit at compile-time distances from them (immediate LDS offsets)
@@ -933,6 +940,73 @@ __global__ __launch_bounds__(256, 4) void rq_split_kernel(SplitArgs a) {
         out[0] = M;
         out[1] = l;
     }
+}
+
+// ---- streaming reference of the per-loop split kernel
+//
+// The same grid, ring, block-table walk and direct-to-LDS loads as
+// rq_split_kernel, with no attention arithmetic: each lane folds one word of
+// every landed stage into a checksum (one per workgroup, written to
+// a.partials as uint32). Its duration is the rate at which this access
+// pattern streams the page records from HBM, the reference the split
+// kernel's bandwidth is measured against.
+template <int D, int RB, bool META_F32, int G, int REFB = 4>
+__global__ __launch_bounds__(256, 4) void rq_stream_kernel(SplitArgs a) {
+    using Ln = Lanes<D>;
+    using SG = StageGeom<D, RB, META_F32, G, REFB>;
+    constexpr int PPI = Ln::PPI, NST = SG::NST, NI = SG::NI;
+    __shared__ __attribute__((aligned(16))) uint8_t stage_mem[kWaves * NST * SG::BYTES];
+    auto stage = reinterpret_cast<uint8_t (*)[NST][SG::BYTES]>(stage_mem);
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int split = blockIdx.x * kWaves + wave;
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int H = a.H;
+    int seq = a.seq_lens[b];
+    seq = seq < 0 ? 0 : (seq > a.max_blocks * 16 ? a.max_blocks * 16 : seq);
+    const int npages = (seq + 15) >> 4;
+    if (blockIdx.x * kWaves * a.split_pages >= npages) return;
+    const int p0 = split * a.split_pages;
+    const int p1 = min(npages, p0 + a.split_pages);
+    const int cnt = p1 - p0;
+    const int steps = cnt > 0 ? (cnt + PPI - 1) / PPI : 0;
+    int tbl = -1;
+    if (lane < cnt) {
+        tbl = a.block_table[(int64_t)b * a.max_blocks + p0 + lane];
+        if (tbl < 0 || tbl >= a.nblk) tbl = -1;
+    }
+    int doff[NI], dpg[NI];
+    stage_pieces<SG, RB>(a, lane, doff, dpg);
+    auto blk_of = [&](int st, int pg) -> int { return __builtin_amdgcn_readlane(tbl, st * PPI + pg); };
+    auto issue = [&](int st, int slot) {
+        __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const int b0 = max(blk_of(st, 0), 0);
+        const uint8_t *base0 = a.pool + ((int64_t)b0 * H + h) * a.slab;
+        const uint8_t *base1 = base0;
+        if constexpr (PPI == 2) base1 = a.pool + ((int64_t)max(blk_of(st, 1), 0) * H + h) * a.slab;
+        const uint32_t lds = lds_addr(&stage[wave][slot][0]);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            if (i < NI - 1 || SG::LIVE_LAST == 64 || lane < SG::LIVE_LAST) {
+                if constexpr (PPI == 1) dma16(lds + 1024u * i, base0, (uint32_t)doff[i]);
+                else dma16(lds + 1024u * i, (dpg[i] ? base1 : base0) + doff[i]);
+            }
+        }
+    };
+    uint32_t sum = 0;
+    if (steps > 0) {
+#pragma unroll
+        for (int j = 0; j < NST - 1; ++j)
+            if (j < steps) issue(j, j);
+        for (int cur = 0; cur < steps; ++cur) {
+            if (cur + NST - 1 < steps) issue(cur + NST - 1, (cur + NST - 1) % NST);
+            wait_steps<NST - 1, NI>(min(NST - 1, steps - 1 - cur));
+            sum ^= ((const uint32_t *)&stage[wave][cur % NST][0])[lane] + (uint32_t)cur;
+            __asm__ volatile("" ::: "memory");
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) sum ^= (uint32_t)__shfl_xor((int)sum, o, 64);
+    if (lane == 0) ((uint32_t *)a.partials)[(((int64_t)b * H + h) * a.nwg + blockIdx.x) * kWaves + wave] = sum;
 }
 
 // ---- multi-loop split kernel
@@ -1415,6 +1489,37 @@ hipError_t launch_split_d(const SplitArgs &s, int rb, int refb, bool mf, dim3 gr
     return hipGetLastError();
 }
 
+// The streaming reference of launch_split_d's kernel (same variants).
+template <int D>
+hipError_t launch_stream_d(const SplitArgs &s, int rb, int refb, bool mf, dim3 grid, hipStream_t st, hipEvent_t ev0,
+                           hipEvent_t ev1) {
+#define RQ_STREAM(RB_, MF_, G_, REFB_) \
+    hipExtLaunchKernelGGL((rq_stream_kernel<D, RB_, MF_, G_, REFB_>), grid, dim3(256), 0, st, ev0, ev1, 0, s)
+#define RQ_STREAM_RB(MF_, G_)                          \
+    do {                                               \
+        if (rb == 0 && refb == 2) RQ_STREAM(0, MF_, G_, 2); \
+        else if (rb == 0) RQ_STREAM(0, MF_, G_, 4);    \
+        else if (rb == 2) RQ_STREAM(2, MF_, G_, 4);    \
+        else RQ_STREAM(4, MF_, G_, 4);                 \
+    } while (0)
+#define RQ_STREAM_G(G_)                                \
+    do {                                               \
+        if (mf) RQ_STREAM_RB(true, G_);                \
+        else RQ_STREAM_RB(false, G_);                  \
+    } while (0)
+    if constexpr (D == 128) {
+        if (s.G == 32) RQ_STREAM_G(32); else if (s.G == 64) RQ_STREAM_G(64); else RQ_STREAM_G(128);
+    } else if constexpr (D == 96) {
+        RQ_STREAM_G(96);
+    } else {
+        if (s.G == 16) RQ_STREAM_G(16); else if (s.G == 32) RQ_STREAM_G(32); else RQ_STREAM_G(64);
+    }
+#undef RQ_STREAM_G
+#undef RQ_STREAM_RB
+#undef RQ_STREAM
+    return hipGetLastError();
+}
+
 template <int D, bool MF, int G, int RBMAX>
 hipError_t launch_multi_k(const MultiArgs &m, bool sh, dim3 grid, size_t lds, hipStream_t st, hipEvent_t ev0,
                           hipEvent_t ev1) {
@@ -1537,10 +1642,13 @@ hipError_t launch_decode_d(const DecodeCall &c) {
         ca.is_res[i] = res ? 1 : 0;
     }
     dim3 pgrid(g.H, c.n, tiles);
-    if (kvf) hipLaunchKernelGGL((rq_qprep_kernel<D, true>), pgrid, dim3(1024), 0, c.stream, qa);
-    else hipLaunchKernelGGL((rq_qprep_kernel<D, false>), pgrid, dim3(1024), 0, c.stream, qa);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
+    hipError_t err = hipSuccess;
+    if (!c.stream_probe) {
+        if (kvf) hipLaunchKernelGGL((rq_qprep_kernel<D, true>), pgrid, dim3(1024), 0, c.stream, qa);
+        else hipLaunchKernelGGL((rq_qprep_kernel<D, false>), pgrid, dim3(1024), 0, c.stream, qa);
+        err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
 
     const float score_scale = c.softmax_scale * kLog2e;
     const int ref = g.L - 1;
@@ -1622,6 +1730,7 @@ hipError_t launch_decode_d(const DecodeCall &c) {
         }
     }
     bool enc_done = multi;   // multi-loop mode: attached to the last group above
+    if (c.stream_probe && (multi || c.n != 1)) return hipErrorInvalidValue;
     for (int i = 0; i < (multi ? 0 : c.n); ++i) {
         const int l = c.loops[i];
         SplitArgs s;
@@ -1650,6 +1759,8 @@ hipError_t launch_decode_d(const DecodeCall &c) {
         }
         dim3 grid(nwg + ex, g.H, c.B);
         const bool last = i == c.n - 1;
+        if (c.stream_probe)   // the streaming reference alone: no query prep, merge or encode
+            return launch_stream_d<D>(s, rb, refb, mf, dim3(nwg, g.H, c.B), c.stream, c.ev_begin, c.ev_end);
         err = launch_split_d<D>(s, rb, refb, mf, grid, c.stream, last ? c.ev_begin : nullptr, last ? c.ev_end : nullptr);
         if (err != hipSuccess) return err;
     }

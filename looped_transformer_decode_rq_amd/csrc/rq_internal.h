@@ -77,6 +77,9 @@ struct DecodeCall {
     const void *enc_kv;
     const int64_t *enc_slots;
     int enc_T;
+    // run the per-loop split kernel's streaming reference instead of the call
+    // (one loop call; its per-workgroup checksums go to `partials`)
+    bool stream_probe = false;
 };
 
 hipError_t launch_decode(const DecodeCall &c);

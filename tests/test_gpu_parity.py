@@ -261,3 +261,41 @@ def test_bf16_masked_block_ids_drop_their_tokens():
                 V = kv[0, 1, b, :seq[b], h][keep]
                 want[b, h] = O.attention(q[0, b, h], K, V, 1 / np.sqrt(D))
         check_attention(f"bf16 masked pages sp {sp}", out.cpu().numpy(), want)
+
+
+def test_stream_probe_reads_the_decode_pages():
+    """The streaming reference of the per-loop decode kernel (no attention
+    arithmetic) walks the same pages: its per-wave checksum (XOR over the
+    wave's page steps of the first 64 words of each landed stage, the page's
+    reference K codes, plus the step index) equals the same fold computed on
+    the host from the pool and the block table; the pool is left untouched."""
+    import looped_transformer_decode_rq_amd as R
+    T = torch()
+    w = W.get(1).replace(batch=2, heads=3, context=300)
+    c = SmallCase(w, shuffled=True, seq_lens=[300, 77])
+    pool = c.device_pool_from_oracle()
+    sp = 2
+    mb = c.table.shape[1]
+    nwg = -(-mb // (4 * sp))
+    for l in (0, w.loops - 1):
+        ws = T.zeros(R.decode_workspace_bytes(c.lay, 1, w.batch, mb, sp), dtype=T.uint8, device=dev())
+        R.decode_stream_probe(c.lay, pool, l, c.d_table, c.d_seq, ws, split_pages=sp)
+        T.cuda.synchronize()
+        got = ws.cpu().numpy().view(np.uint32)
+        for b in range(w.batch):
+            npg = -(-int(c.seq[b]) // 16)
+            for h in range(w.heads):
+                for x in range(nwg):
+                    if x * 4 * sp >= npg:
+                        continue
+                    for wv in range(4):
+                        p0 = (4 * x + wv) * sp
+                        acc = 0
+                        for cur, p in enumerate(range(p0, min(npg, p0 + sp))):
+                            blk = int(c.table[b, p])
+                            base = c.olay.record_offset(blk, h, w.loops - 1, 0)
+                            words = c.pool_o[base:base + 256].view(np.uint32).astype(np.uint64)
+                            for v in (words + cur) & 0xFFFFFFFF:
+                                acc ^= int(v)
+                        assert got[((b * w.heads + h) * nwg + x) * 4 + wv] == acc, (l, b, h, x, wv)
+    assert np.array_equal(pool.cpu().numpy(), c.pool_o)
