@@ -8,23 +8,28 @@
 // uncompressed K/V (query i sees chunk tokens 0..i).
 //
 // Unlike decode, sixteen queries share every page, so both products run on
-// the matrix cores (v_mfma_f32_16x16x16 with tokens as the 16 rows of one
-// operand):
-//   scores^T = Kcodes x Q: A = K codes of 16 tokens as bf16 (16 + c) (K
-//     records are token-major: a lane's 4 codes of one k-step are 16
-//     contiguous bits), B = the 16 bf16 queries (or the hi/lo bf16 terms of
-//     q' = R_K q for the residual); the output leaves each lane with four
-//     tokens of one query, which is exactly the A operand of the next
-//     product, so no transpose is needed;
-//   out = P x Vcodes: A = fp16 hi/lo of p * alpha * s (reference) and p * s
-//     (residual), B = the V codes in their stored operand order.
-// Per token and group: q . k_hat = alpha * (s * sum q (16 + c) + (z - 16 s) *
-// sum q) + (s_r * sum q' (16 + c_r) + (z_r - 16 s_r) * sum q'), one group per
-// token-head (group_size == head_dim).
+// the matrix cores, with tokens as the 16 rows of one operand:
+//   scores^T = Kcodes x Q on the int8 matrix cores (v_mfma_i32_16x16x64_i8):
+//     A = the K codes of 16 tokens, one code per byte (K records are
+//     token-major: a lane's codes of one step are one or two words, unpacked
+//     by two masks and a shift per word, in the order that leaves them);
+//     B = a fixed-point copy of each query, round(q 2^e) with one power of
+//     two per query row and |round(q 2^e)| < 2^22, as three signed base-256
+//     digits in the same channel order (q' = R_K q likewise for the
+//     residual): exact integer dot products per digit, joined in fp32. The
+//     output leaves each lane with four tokens of one query, which is exactly
+//     the A operand of the next product, so no transpose is needed;
+//   out = P x Vcodes on the fp16 matrix cores (v_mfma_f32_16x16x32_f16):
+//     A = fp16 hi/lo of p * alpha * s (reference) and p * s (residual),
+//     B = the V codes as fp16 (16 + c) in their stored operand order.
+// Per token and group: q . k_hat = alpha * (s * sum q c + z * sum q) +
+// (s_r * sum q' c_r + z_r * sum q'), one group per token-head (group_size ==
+// head_dim).
 //
 // Three kernels per call:
-//   rq_chunk_qprep    per (head, 16 query rows): sum q; for a residual loop
-//                     q' = R_K q on the f32 matrix cores, split into bf16 hi/lo
+//   rq_chunk_qprep    per (head, 16 query rows): the digits and scale of q
+//                     and sum q; for a residual loop likewise for q' = R_K q
+//                     (computed on the f32 matrix cores)
 //   rq_chunk_split    per (head, split of pages, sequence x 64 queries): four
 //                     waves of 16 queries walk the split's pages, online
 //                     softmax per query, one partial per (split, query)
@@ -49,10 +54,75 @@ __host__ __device__ constexpr int chunk_qlds_offset(int ring_bytes, int split_pa
 }
 constexpr int kChunkFold = 16;           // pages between folds of the zero terms into the accumulators
 
-// bf16 round-to-nearest-even of a float, as its bits
-__device__ __forceinline__ uint32_t bf16_bits(float x) {
-    const bf16x2 v = {(__bf16)x, (__bf16)0.f};
-    return __builtin_bit_cast(uint32_t, v) & 0xFFFFu;
+// ---------------------------------------------------- int8 score operands
+// A lane of the score product holds one token's (K) or one query's (B)
+// channels kb*D/4 .. kb*D/4 + D/4 - 1; step s of the 16x16x64 product takes
+// sixteen of them, as bytes in the order the unpacking of the stored codes
+// leaves them (byte e of the operand's four words):
+//   4-bit codes, words w0, w1 = channels 16s + 0..7, 16s + 8..15 (nibble j =
+//   channel j): operand (w0 & M, w0 >> 4 & M, w1 & M, w1 >> 4 & M), so byte
+//   i of word d is channel 16s + 8 (d / 2) + 2 i + d % 2;
+//   2-bit codes, word w = channels 16s + 0..15: operand (w >> 2d & M), byte i
+//   of word d is channel 16s + 4 i + d.
+// Channels past D/4 (the second step of D = 96) are zero in the query.
+template <int D>
+__host__ __device__ constexpr int chunk_steps8() { return (D / 4 + 15) / 16; }
+
+template <int BITS>
+__device__ __forceinline__ int chunk_byte_channel(int s, int e) {
+    const int d = e >> 2, i = e & 3;
+    return BITS == 4 ? 16 * s + 8 * (d >> 1) + 2 * i + (d & 1) : 16 * s + 4 * i + d;
+}
+
+template <int D, int BITS>
+__device__ __forceinline__ uint4 chunk_kbytes(const uint32_t *w, int s) {
+    if constexpr (BITS == 4) {
+        constexpr int NW = (D * 4 / 32 + 3) / 4;
+        const uint32_t w0 = w[2 * s], w1 = 2 * s + 1 < NW ? w[2 * s + 1] : 0u;
+        return make_uint4(w0 & 0x0F0F0F0Fu, (w0 >> 4) & 0x0F0F0F0Fu, w1 & 0x0F0F0F0Fu, (w1 >> 4) & 0x0F0F0F0Fu);
+    } else {
+        const uint32_t v = w[s];
+        return make_uint4(v & 0x03030303u, (v >> 2) & 0x03030303u, (v >> 4) & 0x03030303u, (v >> 6) & 0x03030303u);
+    }
+}
+
+typedef int intx4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ intx4 mfma_i8(uint4 a, uint4 b, intx4 c) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(intx4, a), __builtin_bit_cast(intx4, b), c, 0, 0,
+                                                 0);
+}
+
+// Fixed point of a query row: exponent e with |round(x 2^e)| < 2^22 for
+// every |x| <= mx (clamped so that 2^-e stays a normal float), the rounded
+// integer, and its signed base-256 digits d0 + 256 d1 + 65536 d2 (d0, d1 in
+// -128..127; |d2| <= 64)
+__device__ __forceinline__ int fix_exp(float mx) {
+    if (!(mx > 0.f)) return 0;
+    const int e = 21 - ilogbf(mx);
+    return e < -126 ? -126 : (e > 126 ? 126 : e);
+}
+__device__ __forceinline__ int fix_int(float x, int e) {
+    const float y = rintf(ldexpf(x, e));
+    return (int)fminf(fmaxf(y, -4194303.f), 4194303.f);
+}
+__device__ __forceinline__ int fix_digit(int v, int l) {
+    const int d0 = ((v + 128) & 255) - 128;
+    const int v1 = (v - d0) >> 8;
+    const int d1 = ((v1 + 128) & 255) - 128;
+    return l == 0 ? d0 : (l == 1 ? d1 : (v1 - d1) >> 8);
+}
+
+// word d of digit l, step s, lane slot kb of a row's operand
+template <int D, int BITS>
+__device__ __forceinline__ uint32_t digit_word(const float *row, int e, int s, int l, int kb, int d) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int ch = chunk_byte_channel<BITS>(s, 4 * d + i);
+        const int v = ch < D / 4 ? fix_digit(fix_int(row[kb * (D / 4) + ch], e), l) : 0;
+        w |= (uint32_t)(v & 0xFF) << (8 * i);
+    }
+    return w;
 }
 
 // ------------------------------------------------------------------ qprep
@@ -60,7 +130,7 @@ struct ChunkPrepArgs {
     const uint16_t *q;      // [R][H][D] bf16, R = B*C rows
     const float *rot;       // [H][2][D][D]
     uint8_t *qrec;          // [R][H][chunk_qrec_bytes]
-    int R, H, res;
+    int R, H, res;          // res: bits of the residual codes (0: reference loop)
 };
 
 // One workgroup per (head, 16 rows); one wave per row.
@@ -106,25 +176,41 @@ __global__ __launch_bounds__(1024) void rq_chunk_qprep_kernel(ChunkPrepArgs a) {
     }
     __syncthreads();
     if (!row_ok) return;
+    // record: sum q, sum q', 2^-e, 2^-e' (floats), then the digit words of q
+    // and of q' in operand order [step][digit][lane slot kb][4 words]
     uint8_t *rec = a.qrec + ((int64_t)row * a.H + h) * chunk_qrec_bytes(D);
-    float sq = 0.f, sr = 0.f;
-    uint16_t *hi = (uint16_t *)(rec + 16), *lo = hi + D;
+    const float *qrow = Q + r * QS, *rrow = QR + r * QS;
+    float mq = 0.f, mr = 0.f;
     for (int c = lane; c < D; c += 64) {
-        sq += Q[r * QS + c];
-        if (a.res) {
-            const float x = QR[r * QS + c];
-            const uint32_t hb = bf16_bits(x);
-            const uint32_t lb = bf16_bits(x - __uint_as_float(hb << 16));
-            hi[c] = (uint16_t)hb;
-            lo[c] = (uint16_t)lb;
-            sr += __uint_as_float(hb << 16) + __uint_as_float(lb << 16);   // q' as the matrix cores see it
-        }
+        mq = fmaxf(mq, fabsf(qrow[c]));
+        if (a.res) mr = fmaxf(mr, fabsf(rrow[c]));
     }
-    sq = wave_sum(sq);
-    sr = wave_sum(sr);
+    const int eq = fix_exp(wave_max(mq)), er = fix_exp(wave_max(mr));
+    // sums of the fixed-point values the products see (exact: |sum| < 2^29)
+    int sq = 0, sr = 0;
+    for (int c = lane; c < D; c += 64) {
+        sq += fix_int(qrow[c], eq);
+        if (a.res) sr += fix_int(rrow[c], er);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        sq += __shfl_xor(sq, o, 64);
+        sr += __shfl_xor(sr, o, 64);
+    }
+    constexpr int NS = chunk_steps8<D>();
+    uint32_t *wq = (uint32_t *)(rec + 16), *wr = wq + NS * 48;
+    for (int j = lane; j < NS * 48; j += 64) {
+        const int s = j / 48, l = (j / 16) % 3, kb = (j / 4) % 4, d = j % 4;
+        wq[j] = digit_word<D, 4>(qrow, eq, s, l, kb, d);
+        if (a.res == 4) wr[j] = digit_word<D, 4>(rrow, er, s, l, kb, d);
+        else if (a.res) wr[j] = digit_word<D, 2>(rrow, er, s, l, kb, d);
+    }
     if (lane == 0) {
-        ((float *)rec)[0] = sq;
-        ((float *)rec)[1] = sr;
+        float *hd = (float *)rec;
+        hd[0] = ldexpf((float)sq, -eq);
+        hd[1] = ldexpf((float)sr, -er);
+        hd[2] = ldexpf(1.f, -eq);
+        hd[3] = ldexpf(1.f, -er);
     }
 }
 
@@ -149,28 +235,10 @@ struct ChunkArgs {
 constexpr int kChunkStages = 4;               // ring depth: three pages in flight while one is used
 constexpr int kChunkMaxSplit = 1024;          // pages per split (block ids preloaded into LDS)
 
-// bf16 pairs (16 + c0, 16 + c1), (16 + c2, 16 + c3) of four BITS-bit codes in
-// the low 4*BITS bits of u (code e at bits e*BITS): spread the odd codes to
-// 16 bits above the even ones, then one shift and one and-or per pair
-template <int BITS>
-__device__ __forceinline__ uint2 kpairs(uint32_t u) {
-    constexpr uint32_t MASK = BITS == 4 ? 0x00780078u : 0x00180018u;
-    const uint32_t y = u | (u << (16 - BITS));
-    const uint32_t b0 = ((y << 3) & MASK) | 0x41804180u;
-    const uint32_t b1 = (BITS == 4 ? ((y >> 5) & MASK) : ((y >> 1) & MASK)) | 0x41804180u;
-    return make_uint2(b0, b1);
-}
-
 // 16x16x32 products: a lane's eight k values of A and of B are two 16x16x16
 // operands side by side (the matrix cores pair element e of A with element e
 // of B within a lane group, so any split of k between the halves works)
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
-__device__ __forceinline__ floatx4 mfma_bf16k32(uint2 a0, uint2 a1, uint2 b0, uint2 b1, floatx4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, make_uint4(a0.x, a0.y, a1.x, a1.y)),
-                                                   __builtin_bit_cast(bf16x8, make_uint4(b0.x, b0.y, b1.x, b1.y)), c,
-                                                   0, 0, 0);
-}
 __device__ __forceinline__ floatx4 mfma_f16k32(uint2 a0, uint2 a1, uint2 b0, uint2 b1, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(halfx8, make_uint4(a0.x, a0.y, a1.x, a1.y)),
                                                   __builtin_bit_cast(halfx8, make_uint4(b0.x, b0.y, b1.x, b1.y)), c,
@@ -227,13 +295,6 @@ struct KSwz {
     // the record's piece that LDS piece j (< PIECES) holds
     __host__ __device__ static constexpr int src(int j) { return (j & 15) * TP + (j >> 4); }
 };
-
-// the four codes of k-step s
-template <int BITS>
-__device__ __forceinline__ uint32_t kstep(const uint32_t *w, int s) {
-    if constexpr (BITS == 4) return (w[s >> 1] >> (16 * (s & 1))) & 0xFFFFu;
-    else return (w[s >> 2] >> (8 * (s & 3))) & 0xFFu;
-}
 
 // (scale, zero) of four consecutive tokens of one record
 template <bool MF>
@@ -314,10 +375,10 @@ __device__ __forceinline__ void v_mfma2(floatx4 *acc, const VWords<D, BITS> &v, 
 
 // One workgroup per (head, split, sequence x group of 64 queries); wave w
 // holds queries 16*(4*qg + w) + 0..15. Lane l = 16*kb + x: as the query
-// operand it holds query x's channels kb*D/4 + 4s..4s+3 of k-step s; as the
-// K operand token x's same channels; after the score product it holds tokens
-// 4*kb..4*kb+3 of query x; in the output accumulators queries 4*kb..4*kb+3
-// at channel 16m + x.
+// operand it holds the digits of query x's channels kb*D/4 + 16s + 0..15 of
+// step s; as the K operand token x's codes of the same channels; after the
+// score product it holds tokens 4*kb..4*kb+3 of query x; in the output
+// accumulators queries 4*kb..4*kb+3 at channel 16m + x.
 //
 // The four waves share every page: each stage of an LDS ring holds the page's
 // reference K and V records and the loop's residual K and V records as
@@ -395,28 +456,32 @@ __global__ __launch_bounds__(256, 3) void rq_chunk_split_kernel(ChunkArgs a) {
     const int qi = q0 + x;
     const bool qok = qi < C;
     const int64_t qrow = ((int64_t)b * C + (qok ? qi : 0)) * H + h;
-    // q in registers; the residual's hi/lo terms of q' in this wave's LDS area
-    // ([2][NK][64] operand pairs, read back per page: fewer registers)
-    uint2 qa[NK];
-    uint2 *qlds = (uint2 *)(smem + chunk_qlds_offset(NST * stage, a.split_pages)) + wave * 2 * NK * 64;
+    // the digits of q in registers; those of q' in this wave's LDS area
+    // ([step][digit][64 lanes], read back per page: fewer registers)
+    constexpr int NS = chunk_steps8<D>();
+    uint4 qd[NS][3];
+    uint4 *qlds = (uint4 *)(smem + chunk_qlds_offset(NST * stage, a.split_pages)) + wave * NS * 3 * 64;
+    const uint8_t *qr = a.qrec + qrow * chunk_qrec_bytes(D);
     {
-        const uint16_t *qp = a.q + qrow * D + kb * (D / 4);
-        const uint16_t *hp = (const uint16_t *)(a.qrec + qrow * chunk_qrec_bytes(D) + 16) + kb * (D / 4);
+        const uint4 *dq = (const uint4 *)(qr + 16) + kb, *dr = dq + NS * 12;
 #pragma unroll
-        for (int s = 0; s < NK; ++s) {
-            qa[s] = qok ? *(const uint2 *)(qp + 4 * s) : make_uint2(0u, 0u);
-            if constexpr (RB != 0) {
-                qlds[s * 64 + lane] = qok ? *(const uint2 *)(hp + 4 * s) : make_uint2(0u, 0u);
-                qlds[(NK + s) * 64 + lane] = qok ? *(const uint2 *)(hp + D + 4 * s) : make_uint2(0u, 0u);
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int l = 0; l < 3; ++l) {
+                qd[s][l] = qok ? dq[(s * 3 + l) * 4] : make_uint4(0u, 0u, 0u, 0u);
+                if constexpr (RB != 0) qlds[(s * 3 + l) * 64 + lane] = qok ? dr[(s * 3 + l) * 4] : make_uint4(0u, 0u, 0u, 0u);
             }
-        }
     }
-    const float sum_q = qok ? ((const float *)(a.qrec + qrow * chunk_qrec_bytes(D)))[0] : 0.f;
-    const float sum_r = qok ? ((const float *)(a.qrec + qrow * chunk_qrec_bytes(D)))[1] : 0.f;
+    // softmax scale (log2 domain) times: sum q, sum q', 2^-e, 2^-e'
+    const float4 hd = qok ? *(const float4 *)qr : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float tsq = a.score_scale * hd.x, tsr = a.score_scale * hd.y;
+    const float teq = a.score_scale * hd.z, ter = a.score_scale * hd.w;
     // the query registers are complete before the ring's loads are counted
 #pragma unroll
-    for (int s = 0; s < NK; ++s) __asm__ volatile("" ::"v"(qa[s].x), "v"(qa[s].y));
-    __asm__ volatile("" ::"v"(sum_q), "v"(sum_r));
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int l = 0; l < 3; ++l) __asm__ volatile("" ::"v"(qd[s][l].x), "v"(qd[s][l].y), "v"(qd[s][l].z), "v"(qd[s][l].w));
+    __asm__ volatile("" ::"v"(tsq), "v"(tsr), "v"(teq), "v"(ter));
     wait_vmcnt<0>();
 
     float m = kNegInf, lsum = 0.f, zr = 0.f, zs = 0.f;
@@ -466,16 +531,21 @@ __global__ __launch_bounds__(256, 3) void rq_chunk_split_kernel(ChunkArgs a) {
                 load_a4<MF>(sv + code_res + a.meta_bytes + 4 * kb * MSZ, avs);
                 load_v<D, RB>(vs, sv, lane);
             }
-            // ---- scores^T: rows = tokens, columns = queries
-            floatx4 sr = {0.f, 0.f, 0.f, 0.f}, ss = {0.f, 0.f, 0.f, 0.f};
+            // ---- scores^T: rows = tokens, columns = queries; one integer
+            // accumulator per digit
+            intx4 dr[3] = {}, ds[3] = {};
     #pragma unroll
-            for (int s = 0; s < NK; s += 2)      // two k-steps per product
-                sr = mfma_bf16k32(kpairs<4>(kstep<4>(kr.w, s)), kpairs<4>(kstep<4>(kr.w, s + 1)), qa[s], qa[s + 1], sr);
+            for (int s = 0; s < NS; ++s) {
+                const uint4 kk = chunk_kbytes<D, 4>(kr.w, s);
+    #pragma unroll
+                for (int l = 0; l < 3; ++l) dr[l] = mfma_i8(kk, qd[s][l], dr[l]);
+            }
             if constexpr (RB != 0) {
     #pragma unroll
-                for (int s = 0; s < NK; ++s) {
-                    const uint2 kp = kpairs<RB>(kstep<RB>(ks.w, s));
-                    ss = mfma_bf16k32(kp, kp, qlds[s * 64 + lane], qlds[(NK + s) * 64 + lane], ss);  // hi, lo terms
+                for (int s = 0; s < NS; ++s) {
+                    const uint4 kk = chunk_kbytes<D, RB>(ks.w, s);
+    #pragma unroll
+                    for (int l = 0; l < 3; ++l) ds[l] = mfma_i8(kk, qlds[(s * 3 + l) * 64 + lane], ds[l]);
                 }
             }
             float sc[4];
@@ -483,9 +553,13 @@ __global__ __launch_bounds__(256, 3) void rq_chunk_split_kernel(ChunkArgs a) {
     #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 16 * p + 4 * kb + r;
-                float v = skr[r] * sr[r] + fmaf(-16.f, skr[r], zkr[r]) * sum_q;
-                if constexpr (RB != 0) v = aks[r] * v + (sks[r] * ss[r] + fmaf(-16.f, sks[r], zks[r]) * sum_r);
-                v *= a.score_scale;
+                // sum q c = 65536 S2 + 256 S1 + S0 (256 S2 + S1 is exact in int32)
+                const float sr = fmaf((float)((dr[2][r] << 8) + dr[1][r]), 256.f, (float)dr[0][r]);
+                float v = fmaf(skr[r] * teq, sr, zkr[r] * tsq);
+                if constexpr (RB != 0) {
+                    const float ss = fmaf((float)((ds[2][r] << 8) + ds[1][r]), 256.f, (float)ds[0][r]);
+                    v = fmaf(aks[r], v, fmaf(sks[r] * ter, ss, zks[r] * tsr));
+                }
                 sc[r] = (bok && t < seq && qok) ? v : kNegInf;
                 pmax = fmaxf(pmax, sc[r]);
             }
@@ -750,7 +824,7 @@ hipError_t launch_chunk_split(const ChunkArgs &s, bool mf, dim3 grid, hipStream_
     // ring, padding slots, block ids of one split, and for a residual loop the
     // four waves' q' operands
     const size_t lds = (size_t)chunk_qlds_offset(kChunkStages * s.stage, s.split_pages) +
-                       (RB != 0 ? 4 * 2 * (D / 16) * 64 * 8 : 0);
+                       (RB != 0 ? 4 * chunk_steps8<D>() * 3 * 64 * 16 : 0);
     const bool two = s.stage > 4096;           // two direct-to-LDS instructions per wave and page
     if (mf) {
         if (two) hipExtLaunchKernelGGL((rq_chunk_split_kernel<D, RB, true, 2>), grid, dim3(256), (uint32_t)lds, st, e0, e1, 0, s);
@@ -771,7 +845,7 @@ hipError_t launch_chunk_d(const ChunkCall &c) {
     const int rb = res ? g.bits[c.loop] : 0;
 
     ChunkPrepArgs pa;
-    pa.q = (const uint16_t *)c.q; pa.rot = c.rot; pa.qrec = c.qrec; pa.R = R; pa.H = g.H; pa.res = res ? 1 : 0;
+    pa.q = (const uint16_t *)c.q; pa.rot = c.rot; pa.qrec = c.qrec; pa.R = R; pa.H = g.H; pa.res = rb;
     const int tiles = (R + 15) / 16;
     hipLaunchKernelGGL((rq_chunk_qprep_kernel<D>), dim3(g.H, tiles), dim3(1024), 0, c.stream, pa);
     hipError_t err = hipGetLastError();

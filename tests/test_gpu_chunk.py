@@ -6,7 +6,9 @@ and shuffled table, and a Huginn-like one (D96, G96, INT4 and INT2 residual
 loops); chunks of 1..256 queries (256 is the largest chunk), with and without
 the chunk's own K/V, split sizes chosen by the library, forced small and the
 largest (1024 pages: one split); empty caches; C = 1 against decode attention;
-the supported-layout check.
+queries with one channel x100 / x1000 and all-zero queries (the scores use a
+fixed-point copy of each query, one power of two per row); the
+supported-layout check.
 """
 import numpy as np
 import pytest
@@ -76,6 +78,29 @@ def test_chunk_matches_oracle(name, C, split_pages):
         want = O.chunk_attention(c.pool_o, c.olay, l, q, c.st["rot32"], c.table, c.seq, c.tau, ck, cv)
         e, r = check_attention(f"chunk {name} C{C} sp{split_pages} loop {l}", got, want)
         print(f"[chunk {name} C={C} sp={split_pages} loop {l}] max-abs {e:.2e} rel-L2 {r:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+@pytest.mark.parametrize("mult", [100.0, 1000.0])
+def test_chunk_outlier_query_channel(name, mult):
+    """One seeded channel of every query scaled by mult (it sets the row's
+    fixed-point scale); the first queries of sequence 0 all zero."""
+    c = case(name)
+    pool = c.device_pool_from_oracle()
+    q, ck, cv = chunk_inputs(c, 24, seed=11)
+    rng = np.random.default_rng([int(mult), 5])
+    B, C, H, D = q.shape
+    ch = rng.integers(0, D, size=(B, C, H))
+    bi, ci, hi = np.meshgrid(np.arange(B), np.arange(C), np.arange(H), indexing="ij")
+    q = q.copy()
+    q[bi, ci, hi, ch] *= mult
+    q = W.bf16_round(q)
+    q[0, :5] = 0.0
+    for l in range(c.w.loops):
+        got = run_chunk(c, pool, l, q, ck, cv)
+        want = O.chunk_attention(c.pool_o, c.olay, l, q, c.st["rot32"], c.table, c.seq, c.tau, ck, cv)
+        e, r = check_attention(f"chunk {name} x{mult:g} loop {l}", got, want)
+        print(f"[chunk {name} x{mult:g} loop {l}] max-abs {e:.2e} rel-L2 {r:.2e}", flush=True)
 
 
 @pytest.mark.parametrize("name", list(CASES))
