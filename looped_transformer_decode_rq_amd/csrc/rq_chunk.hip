@@ -232,17 +232,16 @@ struct ChunkArgs {
     int stage;                                // bytes of one ring stage: 2*ref_rec (+ 2*res_rec)
 };
 
-constexpr int kChunkStages = 4;               // ring depth: three pages in flight while one is used
+constexpr int kChunkStages = 6;               // ring depth in pages: two pairs in flight while one is used
 constexpr int kChunkMaxSplit = 1024;          // pages per split (block ids preloaded into LDS)
 
 // 16x16x32 products: a lane's eight k values of A and of B are two 16x16x16
 // operands side by side (the matrix cores pair element e of A with element e
 // of B within a lane group, so any split of k between the halves works)
 typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
-__device__ __forceinline__ floatx4 mfma_f16k32(uint2 a0, uint2 a1, uint2 b0, uint2 b1, floatx4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(halfx8, make_uint4(a0.x, a0.y, a1.x, a1.y)),
-                                                  __builtin_bit_cast(halfx8, make_uint4(b0.x, b0.y, b1.x, b1.y)), c,
-                                                  0, 0, 0);
+__device__ __forceinline__ floatx4 mfma_f16x32(uint4 a, uint4 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(halfx8, a), __builtin_bit_cast(halfx8, b), c, 0,
+                                                  0, 0);
 }
 
 // This lane's K codes of one token: D*BITS/32 bytes (channels kb*D/4 ..
@@ -348,29 +347,34 @@ __device__ __forceinline__ void split4(const float *win, uint2 &hi, uint2 &lo, f
     used = (w[0] + w[1]) + (w[2] + w[3]);
 }
 
-// acc[m] += Ahi x B_m + Alo x B_m for every column group m, one operand
-// expansion and one 16x16x32 product for both terms (k: the tokens' hi
-// weights, then their lo weights against the same codes)
+// acc[m] += Ahi x B_m + Alo x B_m for every column group m of a page pair:
+// B_m = the fp16 (16 + c) codes of this lane group's four tokens of the first
+// page, then of the second (the order of the A operands' weights); two
+// 16x16x32 products per group against the same operand
 template <int WP, int BITS, int I>
-__device__ __forceinline__ void v_mfma2_word(floatx4 *acc, uint32_t w, uint2 ahi, uint2 alo, uint32_t vmask,
-                                             uint32_t exp16) {
+__device__ __forceinline__ void v_mfma_pair_word(floatx4 *acc, uint32_t w0, uint32_t w1, uint4 ahi, uint4 alo,
+                                                 uint32_t vmask, uint32_t exp16) {
     if constexpr (I < WP) {
-        const uint32_t b0 = vpair<BITS * I>(w, vmask, exp16);
-        const uint32_t b1 = vpair<BITS * (WP + I)>(w, vmask, exp16);
-        acc[I] = mfma_f16k32(ahi, alo, make_uint2(b0, b1), make_uint2(b0, b1), acc[I]);
-        v_mfma2_word<WP, BITS, I + 1>(acc, w, ahi, alo, vmask, exp16);
+        const uint4 bv = make_uint4(vpair<BITS * I>(w0, vmask, exp16), vpair<BITS * (WP + I)>(w0, vmask, exp16),
+                                    vpair<BITS * I>(w1, vmask, exp16), vpair<BITS * (WP + I)>(w1, vmask, exp16));
+        acc[I] = mfma_f16x32(ahi, bv, acc[I]);
+        acc[I] = mfma_f16x32(alo, bv, acc[I]);
+        v_mfma_pair_word<WP, BITS, I + 1>(acc, w0, w1, ahi, alo, vmask, exp16);
     }
 }
 
 template <int D, int BITS>
-__device__ __forceinline__ void v_mfma2(floatx4 *acc, const VWords<D, BITS> &v, uint2 ahi, uint2 alo) {
+__device__ __forceinline__ void v_mfma_pair(floatx4 *acc, const VWords<D, BITS> &va, const VWords<D, BITS> &vb,
+                                            uint4 ahi, uint4 alo) {
     using V = VWords<D, BITS>;
     uint32_t vmask, exp16;
     vpair_consts<BITS>(vmask, exp16);
 #pragma unroll
-    for (int p = 0; p < V::NFULL; ++p) v_mfma2_word<V::W, BITS, 0>(acc + V::W * p, v.w[p], ahi, alo, vmask, exp16);
+    for (int p = 0; p < V::NFULL; ++p)
+        v_mfma_pair_word<V::W, BITS, 0>(acc + V::W * p, va.w[p], vb.w[p], ahi, alo, vmask, exp16);
     if constexpr (V::REM > 0)
-        v_mfma2_word<V::REM, BITS, 0>(acc + V::W * V::NFULL, v.w[V::NFULL], ahi, alo, vmask, exp16);
+        v_mfma_pair_word<V::REM, BITS, 0>(acc + V::W * V::NFULL, va.w[V::NFULL], vb.w[V::NFULL], ahi, alo, vmask,
+                                          exp16);
 }
 
 // One workgroup per (head, split, sequence x group of 64 queries); wave w
@@ -380,17 +384,18 @@ __device__ __forceinline__ void v_mfma2(floatx4 *acc, const VWords<D, BITS> &v, 
 // score product it holds tokens 4*kb..4*kb+3 of query x; in the output
 // accumulators queries 4*kb..4*kb+3 at channel 16m + x.
 //
-// The four waves share every page: each stage of an LDS ring holds the page's
+// The four waves share every page: each slot of an LDS ring holds one page's
 // reference K and V records and the loop's residual K and V records as
 // stored (two runs of the slab; only the K code areas transposed, see KSwz),
-// filled by direct-to-LDS loads that the
-// waves issue in equal shares kChunkStages-1 pages ahead; one barrier per
-// page publishes the landed stage and frees the oldest one. The split's block
-// ids are preloaded into LDS. Three waves per SIMD (at most 168 registers):
-// with two, the per-page chains of loads, products and softmax left the SIMDs
-// idle; the residual widths then keep a few values in scratch.
+// filled by direct-to-LDS loads that the waves issue in equal shares. Pages
+// go in pairs (the V product takes k = four tokens of each page of a pair, so
+// its operand is never duplicated), two pairs ahead; one barrier per pair
+// publishes the landed slots and frees the oldest ones. The split's block ids
+// are preloaded into LDS. Two waves per SIMD: with three (at most 168
+// registers) the pair's scores, weights and operands spill to scratch, which
+// measured slower.
 template <int D, int RB, bool MF, int NI>
-__global__ __launch_bounds__(256, 3) void rq_chunk_split_kernel(ChunkArgs a) {
+__global__ __launch_bounds__(256, 2) void rq_chunk_split_kernel(ChunkArgs a) {
     constexpr int NK = D / 16;                 // k-steps of the score product = column groups of V
     constexpr int PF = partial_floats(D);
     constexpr int MSZ = MF ? 4 : 2;
@@ -493,77 +498,99 @@ __global__ __launch_bounds__(256, 3) void rq_chunk_split_kernel(ChunkArgs a) {
     }
     const int code_ref = 16 * D / 2, code_res = 16 * D * (RB ? RB : 2) / 8;
 
+    // pages in pairs: pair i = split pages 2i, 2i+1 in slots 2i % NST,
+    // (2i+1) % NST, issued two pairs ahead; a split with an odd page count
+    // loads its last page twice (the copy is masked)
+    const int npair = (steps + 1) >> 1;
+    auto issue_pair = [&](int i) {
+        issue(2 * i, (2 * i) % NST);
+        issue(min(2 * i + 1, steps - 1), (2 * i + 1) % NST);
+    };
+    if (npair > 0) issue_pair(0);
+    if (npair > 1) issue_pair(1);
+
+    // scores (log2 domain, masked: -inf) of the four tokens 4kb..4kb+3 of
+    // split page c held by this lane, for query x
+    auto page_scores = [&](int c, const uint8_t *S, float *sc) {
+        const uint8_t *rk = S, *sk = S + 2 * a.ref_rec;
+        KChunk<D, 4> kr;
+        load_k<D, 4>(kr, rk + KR::off(x, kb));
+        float skr[4], zkr[4];
+        load_sz4<MF>(rk + code_ref + 4 * kb * 2 * MSZ, skr, zkr);
+        intx4 dr[3] = {}, ds[3] = {};
 #pragma unroll
-    for (int j = 0; j < NST - 1; ++j)
-        if (j < steps) issue(j, j);
-    // pages in blocks of kChunkFold; the zero terms are folded into the
-    // accumulators after each block (see below)
-    for (int cb = 0; cb < steps; cb += kChunkFold) {
-        const int ce = min(steps, cb + kChunkFold);
-        for (int cur = cb; cur < ce; ++cur) {
-            // this wave's loads of page `cur` have landed ...
-            wait_steps<NST - 2, NI>(min(NST - 2, steps - 1 - cur));
-            // ... and every other wave's; all waves are done with page cur-1
-            __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-            if (cur + NST - 1 < steps) issue(cur + NST - 1, (cur + NST - 1) % NST);
-            if (q0 >= C) continue;                 // a wave without queries only loads
-            const int p = p0 + cur;
-            const bool bok = tbl[cur] >= 0;
-            const uint8_t *S = ring + (cur % NST) * stage;
-            const uint8_t *rk = S, *rv = S + a.ref_rec;
-            const uint8_t *sk = S + 2 * a.ref_rec, *sv = sk + a.res_rec;
-            // ---- loads: K codes of token x (operand role), metadata of tokens 4kb..4kb+3, V codes
-            KChunk<D, 4> kr;
-            load_k<D, 4>(kr, rk + KR::off(x, kb));
-            float skr[4], zkr[4], svr[4], zvr[4];
-            load_sz4<MF>(rk + code_ref + 4 * kb * 2 * MSZ, skr, zkr);
-            load_sz4<MF>(rv + code_ref + 4 * kb * 2 * MSZ, svr, zvr);
-            VWords<D, 4> vr;
-            load_v<D, 4>(vr, rv, lane);
-            KChunk<D, RB ? RB : 2> ks;
-            VWords<D, RB ? RB : 2> vs;
-            float sks[4], zks[4], aks[4], svs[4], zvs[4], avs[4];
-            if constexpr (RB != 0) {
-                load_k<D, RB>(ks, sk + KS::off(x, kb));
-                load_sz4<MF>(sk + code_res + 4 * kb * 2 * MSZ, sks, zks);
-                load_a4<MF>(sk + code_res + a.meta_bytes + 4 * kb * MSZ, aks);
-                load_sz4<MF>(sv + code_res + 4 * kb * 2 * MSZ, svs, zvs);
-                load_a4<MF>(sv + code_res + a.meta_bytes + 4 * kb * MSZ, avs);
-                load_v<D, RB>(vs, sv, lane);
-            }
-            // ---- scores^T: rows = tokens, columns = queries; one integer
-            // accumulator per digit
-            intx4 dr[3] = {}, ds[3] = {};
-    #pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const uint4 kk = chunk_kbytes<D, 4>(kr.w, s);
+#pragma unroll
+            for (int l = 0; l < 3; ++l) dr[l] = mfma_i8(kk, qd[s][l], dr[l]);
+        }
+        float sks[4], zks[4], aks[4];
+        if constexpr (RB != 0) {
+            KChunk<D, RB> ks;
+            load_k<D, RB>(ks, sk + KS::off(x, kb));
+            load_sz4<MF>(sk + code_res + 4 * kb * 2 * MSZ, sks, zks);
+            load_a4<MF>(sk + code_res + a.meta_bytes + 4 * kb * MSZ, aks);
+#pragma unroll
             for (int s = 0; s < NS; ++s) {
-                const uint4 kk = chunk_kbytes<D, 4>(kr.w, s);
-    #pragma unroll
-                for (int l = 0; l < 3; ++l) dr[l] = mfma_i8(kk, qd[s][l], dr[l]);
+                const uint4 kk = chunk_kbytes<D, RB>(ks.w, s);
+#pragma unroll
+                for (int l = 0; l < 3; ++l) ds[l] = mfma_i8(kk, qlds[(s * 3 + l) * 64 + lane], ds[l]);
             }
+        }
+        const bool ok = c < steps && tbl[c] >= 0 && qok;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * (p0 + c) + 4 * kb + r;
+            // sum q c = 65536 S2 + 256 S1 + S0 (256 S2 + S1 is exact in int32)
+            const float sr = fmaf((float)((dr[2][r] << 8) + dr[1][r]), 256.f, (float)dr[0][r]);
+            float v = fmaf(skr[r] * teq, sr, zkr[r] * tsq);
             if constexpr (RB != 0) {
-    #pragma unroll
-                for (int s = 0; s < NS; ++s) {
-                    const uint4 kk = chunk_kbytes<D, RB>(ks.w, s);
-    #pragma unroll
-                    for (int l = 0; l < 3; ++l) ds[l] = mfma_i8(kk, qlds[(s * 3 + l) * 64 + lane], ds[l]);
-                }
+                const float ss = fmaf((float)((ds[2][r] << 8) + ds[1][r]), 256.f, (float)ds[0][r]);
+                v = fmaf(aks[r], v, fmaf(sks[r] * ter, ss, zks[r] * tsr));
             }
-            float sc[4];
-            float pmax = kNegInf;
-    #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * p + 4 * kb + r;
-                // sum q c = 65536 S2 + 256 S1 + S0 (256 S2 + S1 is exact in int32)
-                const float sr = fmaf((float)((dr[2][r] << 8) + dr[1][r]), 256.f, (float)dr[0][r]);
-                float v = fmaf(skr[r] * teq, sr, zkr[r] * tsq);
-                if constexpr (RB != 0) {
-                    const float ss = fmaf((float)((ds[2][r] << 8) + ds[1][r]), 256.f, (float)ds[0][r]);
-                    v = fmaf(aks[r], v, fmaf(sks[r] * ter, ss, zks[r] * tsr));
-                }
-                sc[r] = (bok && t < seq && qok) ? v : kNegInf;
-                pmax = fmaxf(pmax, sc[r]);
+            sc[r] = (ok && t < seq) ? v : kNegInf;
+        }
+    };
+    // the weights of the four tokens: reference (p alpha s_v, p alpha z_v)
+    // and residual (p s_v, p z_v); zero for masked tokens
+    auto page_weights = [&](const uint8_t *S, const float *pr, float *wr, float *ws, float &zsr, float &zss) {
+        const uint8_t *rv = S + a.ref_rec, *sv = S + 2 * a.ref_rec + a.res_rec;
+        float svr[4], zvr[4], svs[4], zvs[4], avs[4];
+        load_sz4<MF>(rv + code_ref + 4 * kb * 2 * MSZ, svr, zvr);
+        if constexpr (RB != 0) {
+            load_sz4<MF>(sv + code_res + 4 * kb * 2 * MSZ, svs, zvs);
+            load_a4<MF>(sv + code_res + a.meta_bytes + 4 * kb * MSZ, avs);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float pa = RB != 0 ? pr[r] * avs[r] : pr[r];
+            wr[r] = pa * svr[r];
+            zsr = fmaf(pa, zvr[r], zsr);
+            if constexpr (RB != 0) {
+                ws[r] = pr[r] * svs[r];
+                zss = fmaf(pr[r], zvs[r], zss);
             }
+        }
+    };
+
+    // pairs in blocks of kChunkFold/2; the zero terms are folded into the
+    // accumulators after each block (see below)
+    for (int cb = 0; cb < npair; cb += kChunkFold / 2) {
+        const int ce = min(npair, cb + kChunkFold / 2);
+        for (int ci = cb; ci < ce; ++ci) {
+            // this wave's loads of pair ci have landed ...
+            wait_steps<1, 2 * NI>(min(1, npair - 1 - ci));
+            // ... and every other wave's; all waves are done with pair ci-1
+            __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            if (ci + 2 < npair) issue_pair(ci + 2);
+            if (q0 >= C) continue;                 // a wave without queries only loads
+            const uint8_t *S0 = ring + ((2 * ci) % NST) * stage, *S1 = ring + ((2 * ci + 1) % NST) * stage;
+            float sc0[4], sc1[4];
+            page_scores(2 * ci, S0, sc0);
+            page_scores(2 * ci + 1, S1, sc1);
             // ---- online softmax per query (lanes x, x+16, x+32, x+48 share query x)
+            float pmax = fmaxf(fmaxf(fmaxf(sc0[0], sc0[1]), fmaxf(sc0[2], sc0[3])),
+                               fmaxf(fmaxf(sc1[0], sc1[1]), fmaxf(sc1[2], sc1[3])));
             pmax = fmaxf(pmax, __shfl_xor(pmax, 16, 64));
             pmax = fmaxf(pmax, __shfl_xor(pmax, 32, 64));
             if (__any(pmax > m + kThreshC)) {
@@ -572,39 +599,51 @@ __global__ __launch_bounds__(256, 3) void rq_chunk_split_kernel(ChunkArgs a) {
                 lsum *= f; zr *= f; zs *= f;
                 m = mn;
                 // accumulator rows are queries 4kb + v: their factors come from lanes 4kb + v
-    #pragma unroll
+#pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const float fv = __shfl(f, 4 * kb + v, 64);
-    #pragma unroll
+#pragma unroll
                     for (int i = 0; i < NK; ++i) {
                         vacc_r[i][v] *= fv;
                         if constexpr (RB != 0) vacc_s[i][v] *= fv;
                     }
                 }
             }
-            float wr[4], ws[4];
-            float zsum_r = 0.f, zsum_s = 0.f;
-    #pragma unroll
+            float p0w[4], p1w[4];
+#pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float pr = (sc[r] == kNegInf) ? 0.f : fast_exp2(sc[r] - m);
-                lsum += pr;
-                const float av = RB != 0 ? avs[r] : 1.f;
-                wr[r] = pr * av * svr[r];
-                zsum_r = fmaf(pr * av, zvr[r], zsum_r);
-                if constexpr (RB != 0) {
-                    ws[r] = pr * svs[r];
-                    zsum_s = fmaf(pr, zvs[r], zsum_s);
-                }
+                p0w[r] = (sc0[r] == kNegInf) ? 0.f : fast_exp2(sc0[r] - m);
+                p1w[r] = (sc1[r] == kNegInf) ? 0.f : fast_exp2(sc1[r] - m);
+                lsum += p0w[r] + p1w[r];
             }
-            uint2 ahi, alo;
-            float used;
-            split4(wr, ahi, alo, used);
-            zr += zsum_r - 16.f * used;
-            v_mfma2<D, 4>(vacc_r, vr, ahi, alo);
+            float wr0[4], ws0[4], wr1[4], ws1[4];
+            float zsum_r = 0.f, zsum_s = 0.f;
+            page_weights(S0, p0w, wr0, ws0, zsum_r, zsum_s);
+            page_weights(S1, p1w, wr1, ws1, zsum_r, zsum_s);
+            // ---- out += P x V: k = this lane group's four tokens of page
+            // 2ci, then the same four of page 2ci+1; hi and lo weights in two
+            // products against the same V operand
+            const uint8_t *rv0 = S0 + a.ref_rec, *rv1 = S1 + a.ref_rec;
+            uint2 h0, l0, h1, l1;
+            float u0, u1;
+            split4(wr0, h0, l0, u0);
+            split4(wr1, h1, l1, u1);
+            zr += zsum_r - 16.f * (u0 + u1);
+            {
+                VWords<D, 4> va, vb;
+                load_v<D, 4>(va, rv0, lane);
+                load_v<D, 4>(vb, rv1, lane);
+                v_mfma_pair<D, 4>(vacc_r, va, vb, make_uint4(h0.x, h0.y, h1.x, h1.y), make_uint4(l0.x, l0.y, l1.x, l1.y));
+            }
             if constexpr (RB != 0) {
-                split4(ws, ahi, alo, used);
-                zs += zsum_s - 16.f * used;
-                v_mfma2<D, RB>(vacc_s, vs, ahi, alo);
+                const uint8_t *sv0 = S0 + 2 * a.ref_rec + a.res_rec, *sv1 = S1 + 2 * a.ref_rec + a.res_rec;
+                split4(ws0, h0, l0, u0);
+                split4(ws1, h1, l1, u1);
+                zs += zsum_s - 16.f * (u0 + u1);
+                VWords<D, RB> va, vb;
+                load_v<D, RB>(va, sv0, lane);
+                load_v<D, RB>(vb, sv1, lane);
+                v_mfma_pair<D, RB>(vacc_s, va, vb, make_uint4(h0.x, h0.y, h1.x, h1.y), make_uint4(l0.x, l0.y, l1.x, l1.y));
             }
         }
         // After every block of kChunkFold pages the zero terms go into the
