@@ -47,11 +47,13 @@ namespace {
 
 constexpr float kLog2eC = 1.4426950408889634f;
 constexpr float kThreshC = 8.0f;         // rescale when a score beats the running max by 2^8
-// LDS offset of the q' operand area: after the ring (ring_bytes), the padding
-// slots and the split's block ids, 16-byte aligned
-__host__ __device__ constexpr int chunk_qlds_offset(int ring_bytes, int split_pages) {
+// LDS offset of the per-page token tables: after the ring (ring_bytes), the
+// padding slots and the split's block ids, 16-byte aligned; two buffers of two
+// pages x 8 entries x 16 tokens (floats)
+__host__ __device__ constexpr int chunk_tab_offset(int ring_bytes, int split_pages) {
     return (ring_bytes + 64 + 4 * split_pages + 15) & ~15;
 }
+constexpr int kChunkTabBytes = 2 * 2 * 8 * 16 * 4;
 constexpr int kChunkFold = 16;           // pages between folds of the zero terms into the accumulators
 
 // ---------------------------------------------------- int8 score operands
@@ -232,7 +234,7 @@ struct ChunkArgs {
     int stage;                                // bytes of one ring stage: 2*ref_rec (+ 2*res_rec)
 };
 
-constexpr int kChunkStages = 6;               // ring depth in pages: two pairs in flight while one is used
+constexpr int kChunkStages = 8;               // ring depth in pages: two pairs in flight, one tabulated, one used
 constexpr int kChunkMaxSplit = 1024;          // pages per split (block ids preloaded into LDS)
 
 // 16x16x32 products: a lane's eight k values of A and of B are two 16x16x16
@@ -377,6 +379,13 @@ __device__ __forceinline__ void v_mfma_pair(floatx4 *acc, const VWords<D, BITS> 
                                           exp16);
 }
 
+// element i of a record's metadata area (fp16 or fp32 values)
+template <bool MF>
+__device__ __forceinline__ float meta_at(const uint8_t *p, int i) {
+    if constexpr (MF) return ((const float *)p)[i];
+    else return f16_to_f32(((const uint16_t *)p)[i]);
+}
+
 // One workgroup per (head, split, sequence x group of 64 queries); wave w
 // holds queries 16*(4*qg + w) + 0..15. Lane l = 16*kb + x: as the query
 // operand it holds the digits of query x's channels kb*D/4 + 16s + 0..15 of
@@ -389,11 +398,13 @@ __device__ __forceinline__ void v_mfma_pair(floatx4 *acc, const VWords<D, BITS> 
 // stored (two runs of the slab; only the K code areas transposed, see KSwz),
 // filled by direct-to-LDS loads that the waves issue in equal shares. Pages
 // go in pairs (the V product takes k = four tokens of each page of a pair, so
-// its operand is never duplicated), two pairs ahead; one barrier per pair
-// publishes the landed slots and frees the oldest ones. The split's block ids
-// are preloaded into LDS. Two waves per SIMD: with three (at most 168
-// registers) the pair's scores, weights and operands spill to scratch, which
-// measured slower.
+// its operand is never duplicated), three pairs ahead. The per-token factors
+// of a pair (metadata as f32, times alpha and the softmax scale where they
+// apply) are tabulated once per workgroup, each wave one record, one pair
+// ahead of their use. One barrier per pair publishes the landed slots and the
+// tables and frees the oldest ones. The split's block ids are preloaded into
+// LDS. Two waves per SIMD: with three (at most 168 registers) the pair's
+// scores, weights and operands spill to scratch, which measured slower.
 template <int D, int RB, bool MF, int NI>
 __global__ __launch_bounds__(256, 2) void rq_chunk_split_kernel(ChunkArgs a) {
     constexpr int NK = D / 16;                 // k-steps of the score product = column groups of V
@@ -461,11 +472,9 @@ __global__ __launch_bounds__(256, 2) void rq_chunk_split_kernel(ChunkArgs a) {
     const int qi = q0 + x;
     const bool qok = qi < C;
     const int64_t qrow = ((int64_t)b * C + (qok ? qi : 0)) * H + h;
-    // the digits of q in registers; those of q' in this wave's LDS area
-    // ([step][digit][64 lanes], read back per page: fewer registers)
+    // the digits of q and of q' in registers
     constexpr int NS = chunk_steps8<D>();
-    uint4 qd[NS][3];
-    uint4 *qlds = (uint4 *)(smem + chunk_qlds_offset(NST * stage, a.split_pages)) + wave * NS * 3 * 64;
+    uint4 qd[NS][3], qe[RB ? NS : 1][3];
     const uint8_t *qr = a.qrec + qrow * chunk_qrec_bytes(D);
     {
         const uint4 *dq = (const uint4 *)(qr + 16) + kb, *dr = dq + NS * 12;
@@ -474,19 +483,21 @@ __global__ __launch_bounds__(256, 2) void rq_chunk_split_kernel(ChunkArgs a) {
 #pragma unroll
             for (int l = 0; l < 3; ++l) {
                 qd[s][l] = qok ? dq[(s * 3 + l) * 4] : make_uint4(0u, 0u, 0u, 0u);
-                if constexpr (RB != 0) qlds[(s * 3 + l) * 64 + lane] = qok ? dr[(s * 3 + l) * 4] : make_uint4(0u, 0u, 0u, 0u);
+                if constexpr (RB != 0) qe[s][l] = qok ? dr[(s * 3 + l) * 4] : make_uint4(0u, 0u, 0u, 0u);
             }
     }
-    // softmax scale (log2 domain) times: sum q, sum q', 2^-e, 2^-e'
+    // sum q, sum q', 2^-e, 2^-e' (the softmax scale is in the token tables)
     const float4 hd = qok ? *(const float4 *)qr : make_float4(0.f, 0.f, 0.f, 0.f);
-    const float tsq = a.score_scale * hd.x, tsr = a.score_scale * hd.y;
-    const float teq = a.score_scale * hd.z, ter = a.score_scale * hd.w;
     // the query registers are complete before the ring's loads are counted
 #pragma unroll
     for (int s = 0; s < NS; ++s)
 #pragma unroll
-        for (int l = 0; l < 3; ++l) __asm__ volatile("" ::"v"(qd[s][l].x), "v"(qd[s][l].y), "v"(qd[s][l].z), "v"(qd[s][l].w));
-    __asm__ volatile("" ::"v"(tsq), "v"(tsr), "v"(teq), "v"(ter));
+        for (int l = 0; l < 3; ++l) {
+            __asm__ volatile("" ::"v"(qd[s][l].x), "v"(qd[s][l].y), "v"(qd[s][l].z), "v"(qd[s][l].w));
+            if constexpr (RB != 0)
+                __asm__ volatile("" ::"v"(qe[s][l].x), "v"(qe[s][l].y), "v"(qe[s][l].z), "v"(qe[s][l].w));
+        }
+    __asm__ volatile("" ::"v"(hd.x), "v"(hd.y), "v"(hd.z), "v"(hd.w));
     wait_vmcnt<0>();
 
     float m = kNegInf, lsum = 0.f, zr = 0.f, zs = 0.f;
@@ -496,27 +507,46 @@ __global__ __launch_bounds__(256, 2) void rq_chunk_split_kernel(ChunkArgs a) {
         vacc_r[i] = floatx4{0.f, 0.f, 0.f, 0.f};
         vacc_s[i] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
-    const int code_ref = 16 * D / 2, code_res = 16 * D * (RB ? RB : 2) / 8;
 
     // pages in pairs: pair i = split pages 2i, 2i+1 in slots 2i % NST,
-    // (2i+1) % NST, issued two pairs ahead; a split with an odd page count
+    // (2i+1) % NST, issued three pairs ahead; a split with an odd page count
     // loads its last page twice (the copy is masked)
     const int npair = (steps + 1) >> 1;
     auto issue_pair = [&](int i) {
         issue(2 * i, (2 * i) % NST);
         issue(min(2 * i + 1, steps - 1), (2 * i + 1) % NST);
     };
-    if (npair > 0) issue_pair(0);
-    if (npair > 1) issue_pair(1);
+
+    // token tables of pair i in buffer i % 2: [page][entry][token] with the
+    // entries (tau = softmax scale * log2 e; alpha from the residual record)
+    //   0, 1: tau alpha s, tau alpha z of the reference K record
+    //   2, 3: tau s, tau z of the residual K record
+    //   4, 5: alpha s, alpha z of the reference V record
+    //   6, 7: s, z of the residual V record
+    // wave w fills the entries of record w, lanes 0..31 = (page, token)
+    float *tabs = (float *)(smem + chunk_tab_offset(NST * stage, a.split_pages));
+    const int code_ref = 16 * D / 2, code_res = 16 * D * (RB ? RB : 2) / 8;
+    auto make_tables = [&](int i) {
+        if (lane < 32 && (RB != 0 || (wave & 1) == 0)) {
+            const int j = lane >> 4, t = lane & 15;
+            const uint8_t *S = ring + ((2 * i + j) % NST) * stage;
+            const bool vrec = wave >= 2, resrec = (wave & 1) != 0;
+            const uint8_t *rec = resrec ? S + 2 * a.ref_rec + (vrec ? a.res_rec : 0) : S + (vrec ? a.ref_rec : 0);
+            const uint8_t *meta = rec + (resrec ? code_res : code_ref);
+            float f = vrec ? 1.f : a.score_scale;
+            if (RB != 0 && !resrec) f *= meta_at<MF>(S + 2 * a.ref_rec + (vrec ? a.res_rec : 0) + code_res + a.meta_bytes, t);
+            float *T = tabs + ((i & 1) * 2 + j) * 128 + 2 * wave * 16 + t;
+            T[0] = f * meta_at<MF>(meta, 2 * t);
+            T[16] = f * meta_at<MF>(meta, 2 * t + 1);
+        }
+    };
 
     // scores (log2 domain, masked: -inf) of the four tokens 4kb..4kb+3 of
     // split page c held by this lane, for query x
-    auto page_scores = [&](int c, const uint8_t *S, float *sc) {
+    auto page_scores = [&](int c, const uint8_t *S, const float *T, float *sc) {
         const uint8_t *rk = S, *sk = S + 2 * a.ref_rec;
         KChunk<D, 4> kr;
         load_k<D, 4>(kr, rk + KR::off(x, kb));
-        float skr[4], zkr[4];
-        load_sz4<MF>(rk + code_ref + 4 * kb * 2 * MSZ, skr, zkr);
         intx4 dr[3] = {}, ds[3] = {};
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
@@ -524,70 +554,87 @@ __global__ __launch_bounds__(256, 2) void rq_chunk_split_kernel(ChunkArgs a) {
 #pragma unroll
             for (int l = 0; l < 3; ++l) dr[l] = mfma_i8(kk, qd[s][l], dr[l]);
         }
-        float sks[4], zks[4], aks[4];
         if constexpr (RB != 0) {
             KChunk<D, RB> ks;
             load_k<D, RB>(ks, sk + KS::off(x, kb));
-            load_sz4<MF>(sk + code_res + 4 * kb * 2 * MSZ, sks, zks);
-            load_a4<MF>(sk + code_res + a.meta_bytes + 4 * kb * MSZ, aks);
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
                 const uint4 kk = chunk_kbytes<D, RB>(ks.w, s);
 #pragma unroll
-                for (int l = 0; l < 3; ++l) ds[l] = mfma_i8(kk, qlds[(s * 3 + l) * 64 + lane], ds[l]);
+                for (int l = 0; l < 3; ++l) ds[l] = mfma_i8(kk, qe[s][l], ds[l]);
             }
         }
-        const bool ok = c < steps && tbl[c] >= 0 && qok;
+        const float *tt = T + 4 * kb;
+        const float4 e0 = *(const float4 *)tt, e1 = *(const float4 *)(tt + 16);
+        float4 e2 = {0.f, 0.f, 0.f, 0.f}, e3 = e2;
+        if constexpr (RB != 0) {
+            e2 = *(const float4 *)(tt + 32);
+            e3 = *(const float4 *)(tt + 48);
+        }
+        const float a0[4] = {e0.x, e0.y, e0.z, e0.w}, a1[4] = {e1.x, e1.y, e1.z, e1.w};
+        const float a2[4] = {e2.x, e2.y, e2.z, e2.w}, a3[4] = {e3.x, e3.y, e3.z, e3.w};
+        const bool ok = (c < steps) & (tbl[min(c, steps - 1)] >= 0) & qok;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = 16 * (p0 + c) + 4 * kb + r;
             // sum q c = 65536 S2 + 256 S1 + S0 (256 S2 + S1 is exact in int32)
             const float sr = fmaf((float)((dr[2][r] << 8) + dr[1][r]), 256.f, (float)dr[0][r]);
-            float v = fmaf(skr[r] * teq, sr, zkr[r] * tsq);
+            float v = fmaf(a0[r], sr * hd.z, a1[r] * hd.x);
             if constexpr (RB != 0) {
                 const float ss = fmaf((float)((ds[2][r] << 8) + ds[1][r]), 256.f, (float)ds[0][r]);
-                v = fmaf(aks[r], v, fmaf(sks[r] * ter, ss, zks[r] * tsr));
+                v += fmaf(a2[r], ss * hd.w, a3[r] * hd.y);
             }
-            sc[r] = (ok && t < seq) ? v : kNegInf;
+            sc[r] = (ok & (t < seq)) ? v : kNegInf;
         }
     };
     // the weights of the four tokens: reference (p alpha s_v, p alpha z_v)
     // and residual (p s_v, p z_v); zero for masked tokens
-    auto page_weights = [&](const uint8_t *S, const float *pr, float *wr, float *ws, float &zsr, float &zss) {
-        const uint8_t *rv = S + a.ref_rec, *sv = S + 2 * a.ref_rec + a.res_rec;
-        float svr[4], zvr[4], svs[4], zvs[4], avs[4];
-        load_sz4<MF>(rv + code_ref + 4 * kb * 2 * MSZ, svr, zvr);
+    auto page_weights = [&](const float *T, const float *pr, float *wr, float *ws, float &zsr, float &zss) {
+        const float *tt = T + 64 + 4 * kb;
+        const float4 e4 = *(const float4 *)tt, e5 = *(const float4 *)(tt + 16);
+        float4 e6 = {0.f, 0.f, 0.f, 0.f}, e7 = e6;
         if constexpr (RB != 0) {
-            load_sz4<MF>(sv + code_res + 4 * kb * 2 * MSZ, svs, zvs);
-            load_a4<MF>(sv + code_res + a.meta_bytes + 4 * kb * MSZ, avs);
+            e6 = *(const float4 *)(tt + 32);
+            e7 = *(const float4 *)(tt + 48);
         }
+        const float a4[4] = {e4.x, e4.y, e4.z, e4.w}, a5[4] = {e5.x, e5.y, e5.z, e5.w};
+        const float a6[4] = {e6.x, e6.y, e6.z, e6.w}, a7[4] = {e7.x, e7.y, e7.z, e7.w};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float pa = RB != 0 ? pr[r] * avs[r] : pr[r];
-            wr[r] = pa * svr[r];
-            zsr = fmaf(pa, zvr[r], zsr);
+            wr[r] = pr[r] * a4[r];
+            zsr = fmaf(pr[r], a5[r], zsr);
             if constexpr (RB != 0) {
-                ws[r] = pr[r] * svs[r];
-                zss = fmaf(pr[r], zvs[r], zss);
+                ws[r] = pr[r] * a6[r];
+                zss = fmaf(pr[r], a7[r], zss);
             }
         }
     };
 
+    for (int i = 0; i < 3; ++i)
+        if (i < npair) issue_pair(i);
+    if (npair > 0) {
+        wait_steps<2, 2 * NI>(min(2, npair - 1));          // this wave's loads of pair 0
+        __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        make_tables(0);
+    }
     // pairs in blocks of kChunkFold/2; the zero terms are folded into the
     // accumulators after each block (see below)
     for (int cb = 0; cb < npair; cb += kChunkFold / 2) {
         const int ce = min(npair, cb + kChunkFold / 2);
         for (int ci = cb; ci < ce; ++ci) {
-            // this wave's loads of pair ci have landed ...
-            wait_steps<1, 2 * NI>(min(1, npair - 1 - ci));
-            // ... and every other wave's; all waves are done with pair ci-1
+            // this wave's loads of pair ci+1 have landed (of pair ci, the last) ...
+            wait_steps<1, 2 * NI>(min(ci + 2, npair - 1) - min(ci + 1, npair - 1));
+            // ... and every other wave's; the tables of pair ci are complete;
+            // all waves are done with pair ci-1 and its tables
             __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-            if (ci + 2 < npair) issue_pair(ci + 2);
-            if (q0 >= C) continue;                 // a wave without queries only loads
+            if (ci + 3 < npair) issue_pair(ci + 3);
+            if (ci + 1 < npair) make_tables(ci + 1);
+            if (q0 >= C) continue;                 // a wave without queries only loads and tabulates
             const uint8_t *S0 = ring + ((2 * ci) % NST) * stage, *S1 = ring + ((2 * ci + 1) % NST) * stage;
+            const float *T0 = tabs + (ci & 1) * 256, *T1 = T0 + 128;
             float sc0[4], sc1[4];
-            page_scores(2 * ci, S0, sc0);
-            page_scores(2 * ci + 1, S1, sc1);
+            page_scores(2 * ci, S0, T0, sc0);
+            page_scores(2 * ci + 1, S1, T1, sc1);
             // ---- online softmax per query (lanes x, x+16, x+32, x+48 share query x)
             float pmax = fmaxf(fmaxf(fmaxf(sc0[0], sc0[1]), fmaxf(sc0[2], sc0[3])),
                                fmaxf(fmaxf(sc1[0], sc1[1]), fmaxf(sc1[2], sc1[3])));
@@ -618,8 +665,8 @@ __global__ __launch_bounds__(256, 2) void rq_chunk_split_kernel(ChunkArgs a) {
             }
             float wr0[4], ws0[4], wr1[4], ws1[4];
             float zsum_r = 0.f, zsum_s = 0.f;
-            page_weights(S0, p0w, wr0, ws0, zsum_r, zsum_s);
-            page_weights(S1, p1w, wr1, ws1, zsum_r, zsum_s);
+            page_weights(T0, p0w, wr0, ws0, zsum_r, zsum_s);
+            page_weights(T1, p1w, wr1, ws1, zsum_r, zsum_s);
             // ---- out += P x V: k = this lane group's four tokens of page
             // 2ci, then the same four of page 2ci+1; hi and lo weights in two
             // products against the same V operand
@@ -860,10 +907,10 @@ __global__ __launch_bounds__(1024) void rq_chunk_combine_kernel(ChunkCombineArgs
 
 template <int D, int RB>
 hipError_t launch_chunk_split(const ChunkArgs &s, bool mf, dim3 grid, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
-    // ring, padding slots, block ids of one split, and for a residual loop the
-    // four waves' q' operands
-    const size_t lds = (size_t)chunk_qlds_offset(kChunkStages * s.stage, s.split_pages) +
-                       (RB != 0 ? 4 * chunk_steps8<D>() * 3 * 64 * 16 : 0);
+    // ring, padding slots, block ids of one split, token tables (<= 64 KB:
+    // stage <= 4736 bytes for the supported layouts, split_pages <= 1024)
+    const size_t lds = (size_t)chunk_tab_offset(kChunkStages * s.stage, s.split_pages) + kChunkTabBytes;
+    if (lds > 65536) return hipErrorInvalidValue;
     const bool two = s.stage > 4096;           // two direct-to-LDS instructions per wave and page
     if (mf) {
         if (two) hipExtLaunchKernelGGL((rq_chunk_split_kernel<D, RB, true, 2>), grid, dim3(256), (uint32_t)lds, st, e0, e1, 0, s);
