@@ -628,12 +628,29 @@ def traffic_from_profiles(kernel_src_hash):
     return d
 
 
-def kernel_src_hash():
+def kernel_src_hash(files=("rq_decode.hip", "rq_device.h", "rq_internal.h", "rq_vmfma.h")):
     import hashlib
     h = hashlib.sha256()
-    for f in ("rq_decode.hip", "rq_device.h", "rq_internal.h", "rq_vmfma.h"):
+    for f in files:
         h.update(open(os.path.join(ROOT, "looped_transformer_decode_rq_amd", "csrc", f), "rb").read())
     return h.hexdigest()
+
+
+def chunk_src_hash():
+    return kernel_src_hash(("rq_chunk.hip", "rq_device.h", "rq_internal.h", "rq_vmfma.h"))
+
+
+def chunk_traffic_from_profiles():
+    """HBM bytes per launch of the residual-loop chunked-prefill split kernel
+    from the committed counter summary, valid only for the chunk kernel source
+    it was taken on (else None)."""
+    try:
+        d = json.load(open(os.path.join(ROOT, "profiles", "split_kernel_traffic.json")))
+    except Exception:
+        return None
+    if d.get("chunk_src_sha256") != chunk_src_hash():
+        return None
+    return d.get("chunk_residual", {}).get("hbm_bytes_per_launch")
 
 
 def main():
@@ -809,6 +826,10 @@ def main():
                    "residual_split_kernel_ms": ch_res_ms,
                    "residual_split_kernel_gbs": ch_bytes / (ch_res_ms * 1e-3) / 1e9,
                    "residual_split_kernel_tflops": ch_flops / (ch_res_ms * 1e-3) / 1e12,
+                   "residual_split_kernel_traffic": (chunk_traffic_from_profiles()
+                                                     if w.name == DEFAULT_WORKLOAD and C == 64 else None),
+                   "residual_split_kernel_bound": "valu (per query-token score, softmax and weight work; "
+                                                  "matrix cores about a quarter busy)",
                    "reference_split_kernel_ms": float(np.mean(cms[L - 1]))}
         log(f"chunked prefill step {t_ch * 1e3:.3f} ms; residual chunk kernel {ch_res_ms:.3f} ms "
             f"({chunked['residual_split_kernel_gbs']:.0f} GB/s packed, {chunked['residual_split_kernel_tflops']:.1f} TFLOP/s)")
