@@ -472,8 +472,22 @@ def bf16_step(w, rq, b, split_pages, events=None):
         R.bf16_write(b["kc"][l], b["vc"][l], b["new"][l], rq["slots_new"])
 
 
+SETTLE_S = 0.1
+
+
 def timed(fn, steps, warmup):
+    """Seconds per step over `steps` timed steps. The GPU's clocks ramp up
+    over the first ~40 ms of sustained load after an idle spell (measured on
+    MI355X: a per-loop step of the benchmark layer takes ~2.0 ms cold, 1.19 ms
+    10 ms later, ~1.15 ms from ~40 ms on), so each leg first runs its step
+    untimed for SETTLE_S seconds, then the `warmup` steps, then the timed
+    ones, all back to back."""
     import torch
+    t_end = time.perf_counter() + SETTLE_S
+    while time.perf_counter() < t_end:
+        fn(None)
+        fn(None)
+        torch.cuda.synchronize()
     for _ in range(warmup):
         fn(None)
     torch.cuda.synchronize()
