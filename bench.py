@@ -591,7 +591,9 @@ def cpu_baseline(w, pools, budget_s=12.0):
     CPU share. For the benchmark workload, waves of one unit per worker run
     until the time budget is spent and the step time is extrapolated from the
     mean unit time; the tiny and the Ouro-like 4096-token workloads run in
-    full. A single worker gives the 1-core figure."""
+    full; the Huginn-like layer and the 24-layer cache time one unit per
+    worker and are extrapolated to their full step (all layers' units and
+    encodes). A single worker gives the 1-core figure."""
     import workloads as W
     cores, pool, pool1 = pools
     B, H = w.batch, w.heads
@@ -625,6 +627,18 @@ def cpu_baseline(w, pools, budget_s=12.0):
                          "step_s_on_cores": float(np.sum(ut)) / cores + te,
                          "tokens_per_s": wf.batch / (float(np.sum(ut)) / cores + te)}
     out["full_workloads"] = full
+    # the Huginn-like layer and the 24-layer cache: one wave of units per worker, extrapolated
+    sampled = {}
+    for key in (3, 4):
+        ws = W.get(key)
+        layers = getattr(ws, "layers", 1)
+        te = _oracle_encode_step(ws)
+        ut = pool.map(_oracle_unit, [(ws.name, 3000 + i) for i in range(cores)])
+        units = layers * ws.batch * ws.heads
+        st = units * float(np.mean(ut)) / cores + layers * te
+        sampled[ws.name] = {"units_timed": len(ut), "units_per_step": units, "layers": layers,
+                            "step_s_on_cores": st, "tokens_per_s": ws.batch / st, "extrapolated": True}
+    out["sampled_workloads"] = sampled
     return out
 
 
