@@ -848,16 +848,15 @@ __global__ __launch_bounds__(256, 4) void rq_split_kernel(SplitArgs a) {
     const int page_in_step = tok_i >> 4, tok = tok_i & 15;
     const int g = (q4 * CPL) / G;
 
+    // the split's block-table entries, one per lane (at most 64 pages per
+    // split), loaded together with the query (one memory latency, not two,
+    // before the first page's loads can be issued)
+    int tbl = -1;
+    if (lane < cnt) tbl = a.block_table[(int64_t)b * a.max_blocks + p0 + lane];
     QueryRegs<D> q;
     const uint8_t *qp = a.qpack + ((int64_t)b * H + h) * qpack_bytes(D);
     load_query<D, RB != 0>(qp, q4, q);
-
-    // the split's block-table entries, one per lane (at most 64 pages per split)
-    int tbl = -1;
-    if (lane < cnt) {
-        tbl = a.block_table[(int64_t)b * a.max_blocks + p0 + lane];
-        if (tbl < 0 || tbl >= a.nblk) tbl = -1;
-    }
+    if (tbl < 0 || tbl >= a.nblk) tbl = -1;
 
     // this lane's piece of each direct-to-LDS instruction: (page of the step, byte offset in the slab)
     int doff[NI], dpg[NI];
@@ -1116,14 +1115,12 @@ __global__ __launch_bounds__(64 * kMaxMultiLoops) void rq_multi_kernel(MultiArgs
     const int page_in_step = tok_i >> 4, tok = tok_i & 15;
     const int g = (q4 * CPL) / G;
 
+    // the split's block ids, loaded together with the query (one memory latency)
+    int tbl = -1;
+    if (lane < cnt) tbl = a.block_table[(int64_t)b * a.max_blocks + p0 + lane];
     QueryRegs<D> q;
     load_query<D, true>(a.qpack + (((int64_t)call * a.B + b) * H + h) * qpack_bytes(D), q4, q);
-
-    int tbl = -1;
-    if (lane < cnt) {
-        tbl = a.block_table[(int64_t)b * a.max_blocks + p0 + lane];
-        if (tbl < 0 || tbl >= a.nblk) tbl = -1;
-    }
+    if (tbl < 0 || tbl >= a.nblk) tbl = -1;
 
     // LDS: nst shared reference stages, then nst private residual stages per
     // wave, then one 16-byte scratch slot per wave for the padding loads, the
