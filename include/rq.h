@@ -75,7 +75,7 @@ typedef int32_t rq_status;
 #define RQ_OK               0
 #define RQ_ERR_NULL        -1   /* a required pointer is NULL */
 #define RQ_ERR_SHAPE       -2   /* inconsistent or out-of-range sizes / indices */
-#define RQ_ERR_UNSUPPORTED -3   /* a valid request this build has no kernel for */
+#define RQ_ERR_UNSUPPORTED -3   /* a valid request the library has no kernel for */
 #define RQ_ERR_WORKSPACE   -4   /* workspace smaller than the *_workspace_bytes figure */
 #define RQ_ERR_HIP         -5   /* a HIP runtime call or kernel launch failed */
 #define RQ_ERR_SCRATCH     -6   /* request needs more than RQ_NOALLOC_SCRATCH_BYTES */
