@@ -342,10 +342,15 @@ __device__ __forceinline__ void split4(const float *win, uint2 &hi, uint2 &lo, f
         __asm__ volatile("" : "+v"(w[i]));
     }
     halfx2 h01 = {(_Float16)w[0], (_Float16)w[1]}, h23 = {(_Float16)w[2], (_Float16)w[3]};
-    halfx2 l01 = {(_Float16)(w[0] - (float)h01.x), (_Float16)(w[1] - (float)h01.y)};
-    halfx2 l23 = {(_Float16)(w[2] - (float)h23.x), (_Float16)(w[3] - (float)h23.y)};
     hi = make_uint2(__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23));
-    lo = make_uint2(__builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23));
+    // lo = RNE_f16(w - hi), one mixed-precision FMA per weight (-1 * hi + w in
+    // fp32, exact, rounded once to fp16 into the low or the high half)
+    uint32_t l01, l23;
+    __asm__("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(l01) : "v"(hi.x), "v"(w[0]));
+    __asm__("v_fma_mixhi_f16 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(l01) : "v"(hi.x), "v"(w[1]));
+    __asm__("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(l23) : "v"(hi.y), "v"(w[2]));
+    __asm__("v_fma_mixhi_f16 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(l23) : "v"(hi.y), "v"(w[3]));
+    lo = make_uint2(l01, l23);
     used = (w[0] + w[1]) + (w[2] + w[3]);
 }
 

@@ -564,8 +564,12 @@ __device__ __forceinline__ void token_step(const uint8_t *ck, const uint8_t *mkr
     __asm__ volatile("" : "+v"(wr), "+v"(ws));
     // fp16 terms, both rounded to nearest (unbiased): hi = RNE(w), lo = RNE(w - hi)
     const halfx2 hi = {(_Float16)wr, (_Float16)ws};
-    const halfx2 lo = {(_Float16)(wr - (float)hi.x), (_Float16)(ws - (float)hi.y)};
-    const uint32_t hib = __builtin_bit_cast(uint32_t, hi), lob = __builtin_bit_cast(uint32_t, lo);
+    const uint32_t hib = __builtin_bit_cast(uint32_t, hi);
+    // lo: one mixed-precision FMA per weight (-1 * hi + w in fp32, exact,
+    // rounded once to fp16 into the low or the high half)
+    uint32_t lob;
+    __asm__("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(lob) : "v"(hib), "v"(wr));
+    __asm__("v_fma_mixhi_f16 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(lob) : "v"(hib), "v"(ws));
     // zero terms: p*alpha*z minus the offset 16 times the weight. The matrix
     // cores see hi + lo instead of w: the offset then leaves 16 (hi + lo - w)
     // per token, an unbiased rounding error of the same size as the one the
