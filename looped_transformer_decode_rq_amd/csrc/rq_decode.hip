@@ -80,53 +80,72 @@ __device__ __forceinline__ int limb_channel(int q4, int k, int n, int rb) {
     return q4 * CPL + 8 * k + n;
 }
 
-// One workgroup per (head, loop call, 16 sequences); one wave per sequence.
+// Sequences per workgroup of the query prep and of the combine (one wave
+// each): small workgroups spread these latency-bound kernels over more CUs.
+constexpr int kPrepRows = 4;
+
+// One workgroup per (head, loop call, kPrepRows sequences); one wave per sequence.
 template <int D, bool KV_F32>
-__global__ __launch_bounds__(1024) void rq_qprep_kernel(QPrepArgs a) {
+__global__ __launch_bounds__(64 * kPrepRows) void rq_qprep_kernel(QPrepArgs a) {
     using Ln = Lanes<D>;
-    constexpr int QS = D + 1;
-    __shared__ float Q[16 * QS];
-    __shared__ float QR[16 * QS];
-    __shared__ int QI[16][2][D];
+    constexpr int QS = D + 1, RW = kPrepRows;
+    constexpr int NT = (D / 16 + RW - 1) / RW;    // column tiles of the rotation per wave
+    __shared__ float Q[16 * QS];                  // rows RW..15 zero: the A operand has 16 rows
+    __shared__ float QR[RW * QS];
+    __shared__ int QI[RW][2][D];
 
     const int lane = threadIdx.x & 63, r = threadIdx.x >> 6;
     const int h = blockIdx.x, i = blockIdx.y, tile = blockIdx.z;
     const int rb = a.rb[i];
     const int B = a.B, H = a.H;
-    const int b = tile * 16 + r;
+    const int b = tile * RW + r;
     const bool row_ok = b < B;
 
-    // q' = R_K q for the 16 rows: [16 x D] x R_K^T. v_mfma_f32_16x16x4f32:
+    // q' = R_K q for the RW rows: [16 x D] x R_K^T. v_mfma_f32_16x16x4f32:
     // lane l supplies A[l%16][k], B[k][l%16] for its k-slot l/16 and receives
-    // D[4*(l/16)+v][l%16]; wave r computes columns 16r..16r+15. Step kk gives
-    // slot k0 = l/16 the channel k = (D/4) k0 + kk, so that a lane's B
-    // operands are D/4 consecutive floats of row n of R_K (vector loads).
-    // They are loaded first, so that their latency overlaps the query loads.
-    const bool rot_wave = rb != 0 && r < D / 16;
-    const int n = r * 16 + (lane & 15);
-    float rk[D / 4];
-    if (rot_wave) {
-        const float4 *RK = (const float4 *)(a.rot + ((int64_t)h * 2 + 0) * D * D + (int64_t)n * D +
-                                            (lane >> 4) * (D / 4));
+    // D[4*(l/16)+v][l%16]; wave r computes the column tiles r, r + RW, ...
+    // Step kk gives slot k0 = l/16 the channel k = (D/4) k0 + kk, so that a
+    // lane's B operands are D/4 consecutive floats of row n of R_K (vector
+    // loads). They are loaded first, so that their latency overlaps the
+    // query loads.
+    float rk[NT][D / 4];
+    if (rb != 0) {
 #pragma unroll
-        for (int k4 = 0; k4 < D / 16; ++k4) {
-            const float4 v = RK[k4];
-            rk[4 * k4] = v.x; rk[4 * k4 + 1] = v.y; rk[4 * k4 + 2] = v.z; rk[4 * k4 + 3] = v.w;
+        for (int j = 0; j < NT; ++j) {
+            const int ct = r + RW * j;
+            if (ct < D / 16) {
+                const float4 *RK = (const float4 *)(a.rot + ((int64_t)h * 2 + 0) * D * D +
+                                                    (int64_t)(ct * 16 + (lane & 15)) * D + (lane >> 4) * (D / 4));
+#pragma unroll
+                for (int k4 = 0; k4 < D / 16; ++k4) {
+                    const float4 v = RK[k4];
+                    rk[j][4 * k4] = v.x; rk[j][4 * k4 + 1] = v.y; rk[j][4 * k4 + 2] = v.z; rk[j][4 * k4 + 3] = v.w;
+                }
+            }
         }
     }
     for (int c = lane; c < D; c += 64)
         Q[r * QS + c] = row_ok ? load_kv<KV_F32>(a.q, (((int64_t)i * B + b) * H + h) * D + c) : 0.0f;
+    for (int e = threadIdx.x; e < (16 - RW) * QS; e += 64 * RW) Q[RW * QS + e] = 0.0f;
     __syncthreads();
-    if (rot_wave) {
-        // four independent accumulation chains (the products' latency overlaps)
-        floatx4 c4[4] = {};
+    if (rb != 0) {
 #pragma unroll
-        for (int kk = 0; kk < D / 4; ++kk) {
-            const int k = (lane >> 4) * (D / 4) + kk;
-            c4[kk & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(Q[(lane & 15) * QS + k], rk[kk], c4[kk & 3], 0, 0, 0);
+        for (int j = 0; j < NT; ++j) {
+            const int ct = r + RW * j;
+            if (ct < D / 16) {
+                // four independent accumulation chains (the products' latency overlaps)
+                floatx4 c4[4] = {};
+#pragma unroll
+                for (int kk = 0; kk < D / 4; ++kk) {
+                    const int k = (lane >> 4) * (D / 4) + kk;
+                    c4[kk & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(Q[(lane & 15) * QS + k], rk[j][kk], c4[kk & 3],
+                                                                      0, 0, 0);
+                }
+                const floatx4 c = (c4[0] + c4[1]) + (c4[2] + c4[3]);
+                for (int v = 0; v < 4; ++v)
+                    if (4 * (lane >> 4) + v < RW) QR[(4 * (lane >> 4) + v) * QS + ct * 16 + (lane & 15)] = c[v];
+            }
         }
-        const floatx4 c = (c4[0] + c4[1]) + (c4[2] + c4[3]);
-        for (int v = 0; v < 4; ++v) QR[(4 * (lane >> 4) + v) * QS + n] = c[v];
     }
     __syncthreads();
 
@@ -136,21 +155,31 @@ __global__ __launch_bounds__(1024) void rq_qprep_kernel(QPrepArgs a) {
     // coarsens only its own slice, and 24 bits (q) / 20 bits (q') keep the
     // small channels of that slice: bf16 values of q are exact down to
     // 2^-15 of their slice's largest magnitude.
-    int S[2][4] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+    // All 2 LPT maxima (q and q' per slice) in one reduction, likewise the
+    // slices' sums of the fixed-point values below.
+    constexpr int LPT = Ln::LPT;
+    const int t0 = lane / Ln::CPL, t1 = (lane + 64) / Ln::CPL;
+    float x[2][2], am[2 * LPT];
+#pragma unroll
     for (int which = 0; which < 2; ++which) {
         const float *src = which == 0 ? Q : QR;
         const bool on = which == 0 || rb != 0;
+        x[which][0] = (on && lane < D) ? src[r * QS + lane] : 0.f;
+        x[which][1] = (on && lane + 64 < D) ? src[r * QS + lane + 64] : 0.f;
+#pragma unroll
+        for (int t = 0; t < LPT; ++t)
+            am[which * LPT + t] = fmaxf(t0 == t ? fabsf(x[which][0]) : 0.f, t1 == t ? fabsf(x[which][1]) : 0.f);
+    }
+    wave_max_n(am);
+    int S[2][4] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+    int ps[2 * LPT];
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
         const int qmax = qmax_fixed(which == 0 ? kQueryLimbs : kRotLimbs);
-        float x0 = 0.f, x1 = 0.f;
-        if (on) {
-            x0 = (lane < D) ? src[r * QS + lane] : 0.f;
-            x1 = (lane + 64 < D) ? src[r * QS + lane + 64] : 0.f;
-        }
-        const int t0 = lane / Ln::CPL, t1 = (lane + 64) / Ln::CPL;
         int s0 = 0, s1 = 0;
 #pragma unroll
-        for (int t = 0; t < Ln::LPT; ++t) {
-            const float amax = wave_max(fmaxf(t0 == t ? fabsf(x0) : 0.f, t1 == t ? fabsf(x1) : 0.f));
+        for (int t = 0; t < LPT; ++t) {
+            const float amax = am[which * LPT + t];
             int sh = 0;
             if (amax > 0.f) {
                 int e;
@@ -162,12 +191,29 @@ __global__ __launch_bounds__(1024) void rq_qprep_kernel(QPrepArgs a) {
             s0 = t0 == t ? sh : s0;
             s1 = t1 == t ? sh : s1;
         }
-        if (lane < D) QI[r][which][lane] = (int)rintf(ldexpf(x0, s0));
-        if (lane + 64 < D) QI[r][which][lane + 64] = (int)rintf(ldexpf(x1, s1));
+        const int v0 = (int)rintf(ldexpf(x[which][0], s0)), v1 = (int)rintf(ldexpf(x[which][1], s1));
+        if (lane < D) QI[r][which][lane] = v0;
+        if (lane + 64 < D) QI[r][which][lane + 64] = v1;
+#pragma unroll
+        for (int t = 0; t < LPT; ++t) ps[which * LPT + t] = (t0 == t ? v0 : 0) + (t1 == t ? v1 : 0);
     }
+    wave_sum_n(ps);                                     // |sum| < 2^31
     __syncthreads();
     if (!row_ok) return;
     uint8_t *qp = a.qpack + (((int64_t)i * B + b) * H + h) * qpack_bytes(D);
+    // per (which, slice): the sum of the slice's fixed-point values and the
+    // slice's scale 2^-s
+    if (lane == 0) {
+#pragma unroll
+        for (int which = 0; which < 2; ++which) {
+            const bool on = which == 0 || rb != 0;
+#pragma unroll
+            for (int t = 0; t < LPT; ++t) {
+                ((int *)(qp + 16 + 16 * which))[t] = ps[which * LPT + t];
+                ((float *)(qp + 48 * which))[t] = on ? ldexpf(1.0f, -S[which][t]) : 0.0f;
+            }
+        }
+    }
     // Limb words. Per quantity (q, then q'), plane A holds limbs 0..3 as one
     // 16-byte entry per (slice q4, dword k) and plane B the remaining limbs
     // (2 for q, 1 for q') as one 8- or 4-byte entry per (q4, k). Nibble n of
@@ -193,23 +239,6 @@ __global__ __launch_bounds__(1024) void rq_qprep_kernel(QPrepArgs a) {
                 word |= (((u >> (4 * limb)) & 15u) ^ 8u) << (4 * nn);
             }
             base[dw] = word;
-        }
-    }
-    // per (which, slice): the sum of the slice's fixed-point values (|sum| <
-    // 2^31), and the slice's scale 2^-s
-    for (int which = 0; which < 2; ++which) {
-        const bool on = which == 0 || rb != 0;
-        const int v0 = (on && lane < D) ? QI[r][which][lane] : 0;
-        const int v1 = (on && lane + 64 < D) ? QI[r][which][lane + 64] : 0;
-#pragma unroll
-        for (int t = 0; t < Ln::LPT; ++t) {
-            int part = (lane / Ln::CPL == t ? v0 : 0) + ((lane + 64) / Ln::CPL == t ? v1 : 0);
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
-            if (lane == 0) {
-                ((int *)(qp + 16 + 16 * which))[t] = part;
-                ((float *)(qp + 48 * which))[t] = on ? ldexpf(1.0f, -S[which][t]) : 0.0f;
-            }
         }
     }
 }
@@ -1338,29 +1367,36 @@ __device__ __forceinline__ float readlane_f(float v, int l) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
-// One workgroup per (head, loop call, 16 sequences); one wave per sequence.
+// One workgroup per (head, loop call, kPrepRows sequences); one wave per sequence.
 template <int D, bool KV_F32>
-__global__ __launch_bounds__(1024) void rq_combine_kernel(CombineArgs a) {
-    constexpr int QS = D + 1;
+__global__ __launch_bounds__(64 * kPrepRows) void rq_combine_kernel(CombineArgs a) {
+    constexpr int QS = D + 1, RW = kPrepRows;
+    constexpr int NT = (D / 16 + RW - 1) / RW;    // column tiles of the rotation per wave
     constexpr int PF = partial_floats(D);
-    __shared__ float A[16 * QS];
-    __shared__ float O[16 * QS];
+    __shared__ float A[16 * QS];                  // rows RW..15 zero: the A operand has 16 rows
+    __shared__ float O[RW * QS];
     const int lane = threadIdx.x & 63, r = threadIdx.x >> 6;
     const int h = blockIdx.x, i = blockIdx.y, tile = blockIdx.z;
     const int B = a.B, H = a.H;
     const bool has_res = a.is_res[i] != 0;
-    const int b = tile * 16 + r;
+    const int b = tile * RW + r;
     const int c0 = lane, c1 = lane + 64;
     float ar0 = 0.f, ar1 = 0.f, as0 = 0.f, as1 = 0.f;
-    // this lane's R_V operands of the output rotation, loaded before the
-    // partials so that the two latencies overlap (see the MFMA below)
-    const bool rot_wave = has_res && r < D / 16;
-    const int n = r * 16 + (lane & 15);
-    float rv[D / 4];
-    if (rot_wave) {
-        const float *RV = a.rot + ((int64_t)h * 2 + 1) * D * D + (int64_t)(lane >> 4) * D + n;
+    // this lane's R_V operands of the output rotation (column tiles r, r +
+    // RW, ...), loaded before the partials so that the two latencies overlap
+    // (see the MFMA below)
+    float rv[NT][D / 4];
+    if (has_res) {
 #pragma unroll
-        for (int kk = 0; kk < D / 4; ++kk) rv[kk] = RV[(int64_t)4 * kk * D];
+        for (int j = 0; j < NT; ++j) {
+            const int ct = r + RW * j;
+            if (ct < D / 16) {
+                const float *RV = a.rot + ((int64_t)h * 2 + 1) * D * D + (int64_t)(lane >> 4) * D + ct * 16 + (lane & 15);
+#pragma unroll
+                for (int kk = 0; kk < D / 4; ++kk) rv[j][kk] = RV[(int64_t)4 * kk * D];
+            }
+        }
+        for (int e = threadIdx.x; e < (16 - RW) * QS; e += 64 * RW) A[RW * QS + e] = 0.0f;
     }
     if (b < B) {
         int seq = a.seq_lens[b];
@@ -1370,30 +1406,60 @@ __global__ __launch_bounds__(1024) void rq_combine_kernel(CombineArgs a) {
         const int ns = (nsw + a.spp - 1) / a.spp;                        // their partials
         const int64_t row = ((int64_t)i * B + b) * H + h;
         const float *P = a.partials + row * a.nparts * PF;
-        float st = kNegInf;
+        float st = kNegInf, tv0 = 0.f, tv1 = 0.f;
         if (a.tail_k) {
             float d = 0.f;
             if (c0 < D) d += load_kv<KV_F32>(a.q, row * D + c0) * load_kv<KV_F32>(a.tail_k, row * D + c0);
             if (c1 < D) d += load_kv<KV_F32>(a.q, row * D + c1) * load_kv<KV_F32>(a.tail_k, row * D + c1);
+            if (c0 < D) tv0 = load_kv<KV_F32>(a.tail_v, row * D + c0);
+            if (c1 < D) tv1 = load_kv<KV_F32>(a.tail_v, row * D + c1);
             st = wave_sum(d) * a.score_scale;
         }
-        float mloc = kNegInf;
-        for (int s = lane; s < ns; s += 64) mloc = fmaxf(mloc, P[(int64_t)s * PF]);
+        // One round of loads for what the merge needs first: (m, l) of the
+        // partials lane, lane + 64, ... and this lane's columns c0 and c1
+        // (clamped: the weight of a column beyond D is never used) of the
+        // first NPRE partials (indices past the last partial re-read it with
+        // weight 0)
+        constexpr int NPRE = 24;
+        const int k0 = min(c0, D - 1), k1 = min(c1, D - 1);
+        const float m_l = lane < ns ? P[(int64_t)lane * PF] : kNegInf;
+        const float l_l = lane < ns ? P[(int64_t)lane * PF + 1] : 0.f;
+        float pv0[NPRE], pv1[NPRE], pw0[NPRE], pw1[NPRE];
+        if (ns > 0) {
+#pragma unroll
+            for (int j = 0; j < NPRE; ++j) {
+                const float *ps = P + (int64_t)min(j, ns - 1) * PF + 2;
+                pv0[j] = ps[k0];
+                pv1[j] = D > 64 ? ps[k1] : 0.f;
+                pw0[j] = has_res ? ps[D + k0] : 0.f;
+                pw1[j] = (has_res && D > 64) ? ps[D + k1] : 0.f;
+            }
+        }
+        float mloc = m_l;
+        for (int s = lane + 64; s < ns; s += 64) mloc = fmaxf(mloc, P[(int64_t)s * PF]);
         const float M = fmaxf(wave_max(mloc), st);
         if (M != kNegInf) {
             float lloc = 0.f;
-            // columns c0 and c1 of this lane (clamped: the weight of a column
-            // beyond D is never used)
-            const int k0 = min(c0, D - 1), k1 = min(c1, D - 1);
             for (int cb = 0; cb < ns; cb += 64) {
                 const int s = cb + lane;
-                const float e_l = s < ns ? fast_exp2(P[(int64_t)s * PF] - M) : 0.f;
-                if (s < ns) lloc = fmaf(e_l, P[(int64_t)s * PF + 1], lloc);
+                const float e_l = s < ns ? fast_exp2((cb == 0 ? m_l : P[(int64_t)s * PF]) - M) : 0.f;
+                if (s < ns) lloc = fmaf(e_l, cb == 0 ? l_l : P[(int64_t)s * PF + 1], lloc);
                 const int cnt = min(64, ns - cb);
-                // groups of 8 partials with unconditional loads (indices past
-                // the last partial re-read it with weight 0), so that all the
-                // group's loads are in flight together
-                for (int j0 = 0; j0 < cnt; j0 += 8) {
+                int j0 = 0;
+                if (cb == 0) {
+#pragma unroll
+                    for (int j = 0; j < NPRE; ++j) {
+                        const float e = j < cnt ? readlane_f(e_l, j) : 0.f;
+                        ar0 = fmaf(e, pv0[j], ar0);
+                        ar1 = fmaf(e, pv1[j], ar1);
+                        as0 = fmaf(e, pw0[j], as0);
+                        as1 = fmaf(e, pw1[j], as1);
+                    }
+                    j0 = NPRE;
+                }
+                // the rest in groups of 8 partials with unconditional loads,
+                // so that all the group's loads are in flight together
+                for (; j0 < cnt; j0 += 8) {
                     float e[8], v0[8], v1[8], w0[8], w1[8];
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
@@ -1418,8 +1484,8 @@ __global__ __launch_bounds__(1024) void rq_combine_kernel(CombineArgs a) {
             if (a.tail_k) {
                 const float pt = fast_exp2(st - M);
                 lsum += pt;
-                if (c0 < D) ar0 = fmaf(pt, load_kv<KV_F32>(a.tail_v, row * D + c0), ar0);
-                if (c1 < D) ar1 = fmaf(pt, load_kv<KV_F32>(a.tail_v, row * D + c1), ar1);
+                if (c0 < D) ar0 = fmaf(pt, tv0, ar0);
+                if (c1 < D) ar1 = fmaf(pt, tv1, ar1);
             }
             const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
             ar0 *= inv; ar1 *= inv; as0 *= inv; as1 *= inv;
@@ -1432,20 +1498,27 @@ __global__ __launch_bounds__(1024) void rq_combine_kernel(CombineArgs a) {
     if (has_res) {
         // out = O + A * R_V (row vector times R_V = R_V^T applied to the column),
         // v_mfma_f32_16x16x4f32: lane l supplies A[l%16][k0 + l/16], B[k0 + l/16][l%16]
-        // and receives D[4*(l/16)+v][l%16]; wave r computes output columns 16r..16r+15.
-        if (rot_wave) {
-            // four independent accumulation chains (the products' latency overlaps)
-            floatx4 c4[4] = {};
+        // and receives D[4*(l/16)+v][l%16]; wave r computes the output column
+        // tiles r, r + RW, ...
 #pragma unroll
-            for (int kk = 0; kk < D / 4; ++kk) {
-                const int k = 4 * kk + (lane >> 4);
-                c4[kk & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(A[(lane & 15) * QS + k], rv[kk], c4[kk & 3], 0, 0, 0);
-            }
-            const floatx4 c = (c4[0] + c4[1]) + (c4[2] + c4[3]);
-            for (int v = 0; v < 4; ++v) {
-                const int rr = 4 * (lane >> 4) + v;
-                const int bb = tile * 16 + rr;
-                if (bb < B) a.out[(((int64_t)i * B + bb) * H + h) * D + n] = c[v] + O[rr * QS + n];
+        for (int j = 0; j < NT; ++j) {
+            const int ct = r + RW * j;
+            if (ct < D / 16) {
+                const int n = ct * 16 + (lane & 15);
+                // four independent accumulation chains (the products' latency overlaps)
+                floatx4 c4[4] = {};
+#pragma unroll
+                for (int kk = 0; kk < D / 4; ++kk) {
+                    const int k = 4 * kk + (lane >> 4);
+                    c4[kk & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(A[(lane & 15) * QS + k], rv[j][kk], c4[kk & 3],
+                                                                      0, 0, 0);
+                }
+                const floatx4 c = (c4[0] + c4[1]) + (c4[2] + c4[3]);
+                for (int v = 0; v < 4; ++v) {
+                    const int rr = 4 * (lane >> 4) + v;
+                    const int bb = tile * RW + rr;
+                    if (rr < RW && bb < B) a.out[(((int64_t)i * B + bb) * H + h) * D + n] = c[v] + O[rr * QS + n];
+                }
             }
         }
     } else if (b < B) {
@@ -1631,7 +1704,7 @@ template <int D>
 hipError_t launch_decode_d(const DecodeCall &c) {
     const Geom &g = *c.g;
     const bool kvf = g.kvdt == RQ_DTYPE_F32, mf = g.meta == RQ_DTYPE_F32;
-    const int tiles = (c.B + 15) / 16;
+    const int tiles = (c.B + kPrepRows - 1) / kPrepRows;
 
     QPrepArgs qa;
     qa.q = c.q; qa.rot = c.rot; qa.qpack = c.qpack; qa.B = c.B; qa.H = g.H;
@@ -1645,8 +1718,8 @@ hipError_t launch_decode_d(const DecodeCall &c) {
     dim3 pgrid(g.H, c.n, tiles);
     hipError_t err = hipSuccess;
     if (!c.stream_probe) {
-        if (kvf) hipLaunchKernelGGL((rq_qprep_kernel<D, true>), pgrid, dim3(1024), 0, c.stream, qa);
-        else hipLaunchKernelGGL((rq_qprep_kernel<D, false>), pgrid, dim3(1024), 0, c.stream, qa);
+        if (kvf) hipLaunchKernelGGL((rq_qprep_kernel<D, true>), pgrid, dim3(64 * kPrepRows), 0, c.stream, qa);
+        else hipLaunchKernelGGL((rq_qprep_kernel<D, false>), pgrid, dim3(64 * kPrepRows), 0, c.stream, qa);
         err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
@@ -1779,8 +1852,8 @@ hipError_t launch_decode_d(const DecodeCall &c) {
     ca.max_blocks = c.max_blocks; ca.seq_lens = c.seq_lens;
     ca.q = c.q; ca.tail_k = c.tail_k; ca.tail_v = c.tail_v; ca.rot = c.rot; ca.out = c.out;
     ca.B = c.B; ca.H = g.H; ca.score_scale = score_scale;
-    if (kvf) hipLaunchKernelGGL((rq_combine_kernel<D, true>), pgrid, dim3(1024), 0, c.stream, ca);
-    else hipLaunchKernelGGL((rq_combine_kernel<D, false>), pgrid, dim3(1024), 0, c.stream, ca);
+    if (kvf) hipLaunchKernelGGL((rq_combine_kernel<D, true>), pgrid, dim3(64 * kPrepRows), 0, c.stream, ca);
+    else hipLaunchKernelGGL((rq_combine_kernel<D, false>), pgrid, dim3(64 * kPrepRows), 0, c.stream, ca);
     return hipGetLastError();
 }
 

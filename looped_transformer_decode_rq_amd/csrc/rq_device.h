@@ -83,6 +83,30 @@ __device__ __forceinline__ float wave_sum(float v) {
     for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
     return v;
 }
+// The same butterflies over N values at once: the N shuffles of each step
+// are issued together, so the latency is that of one reduction.
+template <int N>
+__device__ __forceinline__ void wave_max_n(float (&v)[N]) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        float o[N];
+#pragma unroll
+        for (int j = 0; j < N; ++j) o[j] = __shfl_xor(v[j], off, 64);
+#pragma unroll
+        for (int j = 0; j < N; ++j) v[j] = fmaxf(v[j], o[j]);
+    }
+}
+template <int N>
+__device__ __forceinline__ void wave_sum_n(int (&v)[N]) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        int o[N];
+#pragma unroll
+        for (int j = 0; j < N; ++j) o[j] = __shfl_xor(v[j], off, 64);
+#pragma unroll
+        for (int j = 0; j < N; ++j) v[j] += o[j];
+    }
+}
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
