@@ -16,7 +16,9 @@
 //     B = a fixed-point copy of each query, round(q 2^e) with one power of
 //     two per query row and |round(q 2^e)| < 2^22, as three signed base-256
 //     digits in the same channel order (q' = R_K q likewise for the
-//     residual): exact integer dot products per digit, joined in fp32. The
+//     residual, under the same power of two): exact integer dot products per
+//     digit, joined in fp32. The scores stay in units of 2^-e until the
+//     exponent, where the scale joins the subtraction of the running max. The
 //     output leaves each lane with four tokens of one query, which is exactly
 //     the A operand of the next product, so no transpose is needed;
 //   out = P x Vcodes on the fp16 matrix cores (v_mfma_f32_16x16x32_f16):
@@ -27,9 +29,9 @@
 // head_dim).
 //
 // Three kernels per call:
-//   rq_chunk_qprep    per (head, 16 query rows): the digits and scale of q
-//                     and sum q; for a residual loop likewise for q' = R_K q
-//                     (computed on the f32 matrix cores)
+//   rq_chunk_qprep    per (head, 16 query rows): the digits of q and of
+//                     q' = R_K q (computed on the f32 matrix cores) under one
+//                     scale 2^-e per row, and their sums
 //   rq_chunk_split    per (head, split of pages, sequence x 64 queries): four
 //                     waves of 16 queries walk the split's pages, online
 //                     softmax per query, one partial per (split, query)
@@ -47,6 +49,9 @@ namespace {
 
 constexpr float kLog2eC = 1.4426950408889634f;
 constexpr float kThreshC = 8.0f;         // rescale when a score beats the running max by 2^8
+// The running max before the first unmasked score: finite, so that a masked
+// score's weight exp2(-inf - m) is 0 without a test; written out as -inf.
+constexpr float kFloorC = -1e30f;
 // LDS offset of the per-page token tables: after the ring (ring_bytes), the
 // padding slots and the split's block ids, 16-byte aligned; two buffers of two
 // pages x 8 entries x 16 tokens (floats)
@@ -178,8 +183,9 @@ __global__ __launch_bounds__(1024) void rq_chunk_qprep_kernel(ChunkPrepArgs a) {
     }
     __syncthreads();
     if (!row_ok) return;
-    // record: sum q, sum q', 2^-e, 2^-e' (floats), then the digit words of q
-    // and of q' in operand order [step][digit][lane slot kb][4 words]
+    // record: sum round(q 2^e), sum round(q' 2^e), 2^-e, 2^-e (floats), then
+    // the digit words of q and of q' in operand order [step][digit][lane
+    // slot kb][4 words]
     uint8_t *rec = a.qrec + ((int64_t)row * a.H + h) * chunk_qrec_bytes(D);
     const float *qrow = Q + r * QS, *rrow = QR + r * QS;
     float mq = 0.f, mr = 0.f;
@@ -187,7 +193,10 @@ __global__ __launch_bounds__(1024) void rq_chunk_qprep_kernel(ChunkPrepArgs a) {
         mq = fmaxf(mq, fabsf(qrow[c]));
         if (a.res) mr = fmaxf(mr, fabsf(rrow[c]));
     }
-    const int eq = fix_exp(wave_max(mq)), er = fix_exp(wave_max(mr));
+    // one exponent for q and q' (that of the larger magnitude), so that the
+    // two sums of a score share the scale 2^-e
+    const int eq0 = fix_exp(wave_max(mq)), er0 = fix_exp(wave_max(mr));
+    const int eq = a.res ? min(eq0, er0) : eq0, er = eq;
     // sums of the fixed-point values the products see (exact: |sum| < 2^29)
     int sq = 0, sr = 0;
     for (int c = lane; c < D; c += 64) {
@@ -209,10 +218,10 @@ __global__ __launch_bounds__(1024) void rq_chunk_qprep_kernel(ChunkPrepArgs a) {
     }
     if (lane == 0) {
         float *hd = (float *)rec;
-        hd[0] = ldexpf((float)sq, -eq);
-        hd[1] = ldexpf((float)sr, -er);
+        hd[0] = (float)sq;
+        hd[1] = (float)sr;
         hd[2] = ldexpf(1.f, -eq);
-        hd[3] = ldexpf(1.f, -er);
+        hd[3] = hd[2];
     }
 }
 
@@ -491,8 +500,9 @@ __global__ __launch_bounds__(256, 2) void rq_chunk_split_kernel(ChunkArgs a) {
                 if constexpr (RB != 0) qe[s][l] = qok ? dr[(s * 3 + l) * 4] : make_uint4(0u, 0u, 0u, 0u);
             }
     }
-    // sum q, sum q', 2^-e, 2^-e' (the softmax scale is in the token tables)
-    const float4 hd = qok ? *(const float4 *)qr : make_float4(0.f, 0.f, 0.f, 0.f);
+    // sums of the fixed-point q and q', 2^-e twice (the softmax scale is in
+    // the token tables); a missing query: zero sums, scale 1 (no NaN from -inf * 0)
+    const float4 hd = qok ? *(const float4 *)qr : make_float4(0.f, 0.f, 1.f, 1.f);
     // the query registers are complete before the ring's loads are counted
 #pragma unroll
     for (int s = 0; s < NS; ++s)
@@ -505,7 +515,7 @@ __global__ __launch_bounds__(256, 2) void rq_chunk_split_kernel(ChunkArgs a) {
     __asm__ volatile("" ::"v"(hd.x), "v"(hd.y), "v"(hd.z), "v"(hd.w));
     wait_vmcnt<0>();
 
-    float m = kNegInf, lsum = 0.f, zr = 0.f, zs = 0.f;
+    float m = kFloorC, lsum = 0.f, zr = 0.f, zs = 0.f;
     floatx4 vacc_r[NK], vacc_s[NK];
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
@@ -546,8 +556,8 @@ __global__ __launch_bounds__(256, 2) void rq_chunk_split_kernel(ChunkArgs a) {
         }
     };
 
-    // scores (log2 domain, masked: -inf) of the four tokens 4kb..4kb+3 of
-    // split page c held by this lane, for query x
+    // scores (log2 domain, in units of 2^-e; masked: -inf) of the four
+    // tokens 4kb..4kb+3 of split page c held by this lane, for query x
     auto page_scores = [&](int c, const uint8_t *S, const float *T, float *sc) {
         const uint8_t *rk = S, *sk = S + 2 * a.ref_rec;
         KChunk<D, 4> kr;
@@ -578,18 +588,27 @@ __global__ __launch_bounds__(256, 2) void rq_chunk_split_kernel(ChunkArgs a) {
         }
         const float a0[4] = {e0.x, e0.y, e0.z, e0.w}, a1[4] = {e1.x, e1.y, e1.z, e1.w};
         const float a2[4] = {e2.x, e2.y, e2.z, e2.w}, a3[4] = {e3.x, e3.y, e3.z, e3.w};
-        const bool ok = (c < steps) & (tbl[min(c, steps - 1)] >= 0) & qok;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int t = 16 * (p0 + c) + 4 * kb + r;
             // sum q c = 65536 S2 + 256 S1 + S0 (256 S2 + S1 is exact in int32)
             const float sr = fmaf((float)((dr[2][r] << 8) + dr[1][r]), 256.f, (float)dr[0][r]);
-            float v = fmaf(a0[r], sr * hd.z, a1[r] * hd.x);
+            float u = fmaf(a0[r], sr, a1[r] * hd.x);
             if constexpr (RB != 0) {
                 const float ss = fmaf((float)((ds[2][r] << 8) + ds[1][r]), 256.f, (float)ds[0][r]);
-                v += fmaf(a2[r], ss * hd.w, a3[r] * hd.y);
+                u = fmaf(a2[r], ss, fmaf(a3[r], hd.y, u));
             }
-            sc[r] = (ok & (t < seq)) ? v : kNegInf;
+            sc[r] = u;
+        }
+        // masks only on a page not wholly valid for the wave's 16 queries
+        const int blk = __builtin_amdgcn_readfirstlane(tbl[min(c, steps - 1)]);
+        const bool whole = c < steps && blk >= 0 && 16 * (p0 + c) + 16 <= seq && q0 + 16 <= C;
+        if (!whole) {
+            const bool ok = (c < steps) & (blk >= 0) & qok;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * (p0 + c) + 4 * kb + r;
+                sc[r] = (ok & (t < seq)) ? sc[r] : kNegInf;
+            }
         }
     };
     // the weights of the four tokens: reference (p alpha s_v, p alpha z_v)
@@ -645,9 +664,10 @@ __global__ __launch_bounds__(256, 2) void rq_chunk_split_kernel(ChunkArgs a) {
                                fmaxf(fmaxf(sc1[0], sc1[1]), fmaxf(sc1[2], sc1[3])));
             pmax = fmaxf(pmax, __shfl_xor(pmax, 16, 64));
             pmax = fmaxf(pmax, __shfl_xor(pmax, 32, 64));
+            pmax *= hd.z;                          // log2 units
             if (__any(pmax > m + kThreshC)) {
                 const float mn = fmaxf(m, pmax);
-                const float f = (mn == kNegInf) ? 1.f : fast_exp2(m - mn);
+                const float f = fast_exp2(m - mn);
                 lsum *= f; zr *= f; zs *= f;
                 m = mn;
                 // accumulator rows are queries 4kb + v: their factors come from lanes 4kb + v
@@ -661,11 +681,13 @@ __global__ __launch_bounds__(256, 2) void rq_chunk_split_kernel(ChunkArgs a) {
                     }
                 }
             }
+            // weights exp2(score - m), the scale 2^-e joined with the subtraction
             float p0w[4], p1w[4];
+            const float nm = -m;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                p0w[r] = (sc0[r] == kNegInf) ? 0.f : fast_exp2(sc0[r] - m);
-                p1w[r] = (sc1[r] == kNegInf) ? 0.f : fast_exp2(sc1[r] - m);
+                p0w[r] = fast_exp2(fmaf(sc0[r], hd.z, nm));
+                p1w[r] = fast_exp2(fmaf(sc1[r], hd.z, nm));
                 lsum += p0w[r] + p1w[r];
             }
             float wr0[4], ws0[4], wr1[4], ws1[4];
@@ -735,7 +757,7 @@ __global__ __launch_bounds__(256, 2) void rq_chunk_split_kernel(ChunkArgs a) {
     zs += __shfl_xor(zs, 32, 64);
     if (kb == 0 && qok) {
         float *o = a.partials + (qrow * a.nsplit + split) * PF;
-        o[0] = m;
+        o[0] = m == kFloorC ? kNegInf : m;
         o[1] = lsum;
     }
 #pragma unroll

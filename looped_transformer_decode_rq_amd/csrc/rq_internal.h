@@ -34,9 +34,10 @@ constexpr int kQueryLimbs = 6;
 constexpr int kRotLimbs = 5;
 __host__ __device__ constexpr int qpack_bytes(int D) { return 64 + (kQueryLimbs + kRotLimbs) * D / 2; }
 __host__ __device__ constexpr int partial_floats(int D) { return 2 + 2 * D; }
-// Per-(query row, head) record of the chunked-prefill query prep: sum q,
-// sum q', 2^-e, 2^-e' (floats), then the three base-256 digits of the fixed
-// point q and of q' = R_K q, (D/4 + 15)/16 steps of 4 lane slots x 16 bytes each
+// Per-(query row, head) record of the chunked-prefill query prep: the sums
+// of round(q 2^e) and of round(q' 2^e), 2^-e twice (floats), then the three
+// base-256 digits of the fixed point q and of q' = R_K q, (D/4 + 15)/16 steps
+// of 4 lane slots x 16 bytes each
 __host__ __device__ constexpr int chunk_qrec_bytes(int D) { return 16 + 2 * 3 * 64 * ((D / 4 + 15) / 16); }
 
 // Pages per split chosen when the caller passes 0: sized so that a launch
