@@ -472,22 +472,38 @@ def bf16_step(w, rq, b, split_pages, events=None):
         R.bf16_write(b["kc"][l], b["vc"][l], b["new"][l], rq["slots_new"])
 
 
-SETTLE_S = 0.1
+SETTLE_S = 0.1          # minimum untimed run of a leg's step before its timed steps
+SETTLE_MAX_S = 1.0      # at most this long: then the clocks are taken as settled
+SETTLE_BATCH = 5        # steps per settle batch
+SETTLE_TOL = 0.01       # settled: two batches in a row within 1% of each other
 
 
 def timed(fn, steps, warmup):
     """Seconds per step over `steps` timed steps. The GPU's clocks ramp up
     over the first ~40 ms of sustained load after an idle spell (measured on
     MI355X: a per-loop step of the benchmark layer takes ~2.0 ms cold, 1.19 ms
-    10 ms later, ~1.15 ms from ~40 ms on), so each leg first runs its step
-    untimed for SETTLE_S seconds, then the `warmup` steps, then the timed
-    ones, all back to back."""
+    10 ms later, ~1.15 ms from ~40 ms on; on some boxes the ramp takes
+    longer), so each leg first runs its step untimed for at least SETTLE_S
+    seconds and until two consecutive batches of SETTLE_BATCH steps agree
+    within SETTLE_TOL (at most SETTLE_MAX_S), then the `warmup` steps, then
+    the timed ones, all back to back."""
     import torch
-    t_end = time.perf_counter() + SETTLE_S
-    while time.perf_counter() < t_end:
-        fn(None)
-        fn(None)
+    t_start = time.perf_counter()
+    prev = None
+    nb = 0
+    while True:
+        t0 = time.perf_counter()
+        for _ in range(SETTLE_BATCH):
+            fn(None)
         torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        cur = t1 - t0
+        settled = prev is not None and abs(cur - prev) <= SETTLE_TOL * prev
+        prev = cur
+        nb += 1
+        if t1 - t_start >= SETTLE_MAX_S or (settled and t1 - t_start >= SETTLE_S):
+            log(f"settle: {nb} batches in {t1 - t_start:.2f} s, last batch {cur / SETTLE_BATCH * 1e3:.3f} ms per step")
+            break
     for _ in range(warmup):
         fn(None)
     torch.cuda.synchronize()
