@@ -179,6 +179,12 @@ rq_status rq_encode_pack(const rq_layout *layout, void *pool, const void *kv_new
                          const float *rot, const int64_t *slot_mapping,
                          int32_t num_tokens, void *stream);
 
+/* Device workspace bytes rq_encode_pack needs for num_tokens tokens: 0 for a
+ * valid layout and num_tokens >= 0 (the encoder keeps its scratch in LDS, so
+ * rq_encode_pack takes no workspace argument); SIZE_MAX for an invalid
+ * layout or a negative num_tokens. */
+size_t rq_encode_workspace_bytes(const rq_layout *layout, int32_t num_tokens);
+
 /* Workspace bytes for rq_decode_attention(_ex) with these sizes. */
 size_t rq_decode_workspace_bytes(const rq_layout *layout, int32_t n_loops,
                                  int32_t batch, int32_t max_blocks_per_seq,
@@ -374,8 +380,12 @@ rq_status rq_chunk_attention(const rq_layout *layout, const void *pool, int32_t 
                              void *stream);
 
 /* Uncompressed baseline (for the speed ratio): the same decode attention over
- * a paged bf16 cache of ONE loop.
- *   k_cache, v_cache  [num_blocks][H][16][D] bf16
+ * a paged bf16 cache of ONE loop, the cache against which the arXiv
+ * 2610.10381 abstract states the method's accuracy (close to BF16) and its
+ * fixed-batch and peak decode throughput gains.
+ *   k_cache, v_cache  [num_blocks][H][16][D] bf16; num_blocks bounds the
+ *                     block ids as in the packed path (an id < 0 or >=
+ *                     num_blocks masks its page)
  *   q, tail_k, tail_v [B][H][D] bf16 (tails may both be NULL); out [B][H][D] fp32
  * head_dim in {64, 96, 128}; block_size must be 16. */
 size_t rq_bf16_workspace_bytes(int32_t num_heads, int32_t head_dim, int32_t batch,

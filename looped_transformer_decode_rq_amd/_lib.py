@@ -24,7 +24,7 @@ EXPORTED = [
     "rq_decode_attention_ex", "rq_decode_attention_encode", "rq_fit_rotation", "rq_bf16_workspace_bytes",
     "rq_bf16_auto_split_pages", "rq_bf16_decode_attention", "rq_bf16_decode_attention_ex", "rq_bf16_write",
     "rq_chunk_workspace_bytes", "rq_chunk_attention", "rq_decode_attention_noalloc",
-    "rq_fit_rotation_device", "rq_fit_workspace_bytes", "rq_decode_stream_probe",
+    "rq_fit_rotation_device", "rq_fit_workspace_bytes", "rq_decode_stream_probe", "rq_encode_workspace_bytes",
 ]
 RQ_NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -66,6 +66,7 @@ def lib():
             "rq_record_bytes": (c_size_t, [POINTER(RqLayout), c_int32]),
             "rq_record_offset": (c_int64, [POINTER(RqLayout), c_int32, c_int32, c_int32, c_int32]),
             "rq_encode_pack": (c_int32, [POINTER(RqLayout), P, P, P, P, c_int32, P]),
+            "rq_encode_workspace_bytes": (c_size_t, [POINTER(RqLayout), c_int32]),
             "rq_decode_workspace_bytes": (c_size_t, [POINTER(RqLayout), c_int32, c_int32, c_int32, c_int32]),
             "rq_decode_auto_split_pages": (c_int32, [POINTER(RqLayout), c_int32, c_int32, c_int32]),
             "rq_decode_attention": (c_int32, [POINTER(RqLayout), P, P, c_int32, P, P, P, P, c_int32, c_int32,
@@ -193,6 +194,11 @@ def encode_pack(layout, pool, kv_new, rot, slot_mapping, stream=None):
             _check_rot(layout, rot)
     _check("rq_encode_pack", lib().rq_encode_pack(
         ctypes.byref(layout), _ptr(pool), _ptr(kv_new), _ptr(rot), _ptr(slot_mapping), T, _stream(stream)))
+
+
+def encode_workspace_bytes(layout, num_tokens) -> int:
+    """rq_encode_workspace_bytes: 0 for a valid layout (the encoder needs no device workspace)."""
+    return lib().rq_encode_workspace_bytes(ctypes.byref(layout), num_tokens)
 
 
 def decode_workspace_bytes(layout, n_loops, batch, max_blocks_per_seq, split_pages=0) -> int:

@@ -1,6 +1,7 @@
 // C ABI of librq: argument validation, pool geometry, workspace carving and
 // kernel launches. Nothing here allocates, frees or synchronizes.
 #include <math.h>
+#include <stdint.h>
 #include <string.h>
 
 #include <algorithm>
@@ -197,6 +198,12 @@ int64_t rq_record_offset(const rq_layout *layout, int32_t block, int32_t head, i
     if (block < 0 || block >= g.nblk || head < 0 || head >= g.H || loop < 0 || loop >= g.L || kv < 0 || kv > 1)
         return -1;
     return ((int64_t)block * g.H + head) * g.slab + g.loop_off[loop] + (int64_t)kv * g.rec[loop];
+}
+
+size_t rq_encode_workspace_bytes(const rq_layout *layout, int32_t num_tokens) {
+    Geom g;
+    if (num_tokens < 0 || make_geom(layout, &g) != RQ_OK) return SIZE_MAX;
+    return 0;
 }
 
 rq_status rq_encode_pack(const rq_layout *layout, void *pool, const void *kv_new, const float *rot,

@@ -220,6 +220,16 @@ def test_workspace_sizes_monotone(L):
     assert R.decode_workspace_bytes(lay, 1, 16, 2049, 65) == 0      # at most 64 pages per split
 
 
+def test_encode_needs_no_workspace(L):
+    lay = _lay(LAYOUTS[1])
+    assert R.encode_workspace_bytes(lay, 0) == 0
+    assert R.encode_workspace_bytes(lay, 1 << 20) == 0
+    size_max = (1 << (8 * ctypes.sizeof(ctypes.c_size_t))) - 1
+    assert R.encode_workspace_bytes(lay, -1) == size_max
+    bad = _lay(LAYOUTS[1]); bad.head_dim = 80
+    assert R.encode_workspace_bytes(bad, 4) == size_max
+
+
 def test_binding_refuses_host_tensors(L):
     torch = pytest.importorskip("torch")
     lay = _lay(LAYOUTS[0])
