@@ -400,9 +400,10 @@ rq_status rq_chunk_attention(const rq_layout *layout, const void *pool, int32_t 
         return RQ_ERR_SHAPE;
     if ((int64_t)max_blocks_per_seq * 16 > (int64_t)1 << 30) return RQ_ERR_SHAPE;
     const int sp = sp_req > 0 ? sp_req : chunk_split_pages(batch, g.H, chunk, max_blocks_per_seq);
-    // launch grids: splits, sequences x 64-query groups and 16-row tiles each within 65535
+    // launch grids: splits, sequences x 64-query groups, 16-row tiles and
+    // sequences x 16-query tiles each within 65535
     if (nsplit_of(max_blocks_per_seq, sp) > 65535 || (int64_t)batch * ((chunk + 63) / 64) > 65535 ||
-        ((int64_t)batch * chunk + 15) / 16 > 65535)
+        ((int64_t)batch * chunk + 15) / 16 > 65535 || (int64_t)batch * ((chunk + 15) / 16) > 65535)
         return RQ_ERR_UNSUPPORTED;
     if (!workspace) return RQ_ERR_NULL;
     if (workspace_bytes < chunk_ws(g, batch, chunk, max_blocks_per_seq, sp)) return RQ_ERR_WORKSPACE;

@@ -788,59 +788,85 @@ struct ChunkCombineArgs {
     float score_scale;
 };
 
-// One workgroup per (head, 16 query rows); one wave per row.
+// bf16 RNE of a float, and the bf16 hi/lo pair of a weight (hi = RNE(w),
+// lo = RNE(w - hi): relative error <= 2^-16)
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+    const uint32_t u = __float_as_uint(x);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ floatx4 mfma_bf16x32(uint4 a, uint4 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+}
+
+// One workgroup per (head, sequence, 16 consecutive queries of the chunk);
+// wave r holds query i = 16t + r. The chunk's own causal part runs on the
+// bf16 matrix cores (v_mfma_f32_16x16x32_bf16: lane l supplies row l%16 of A
+// and column l%16 of B for its eight k values 8(l/16)..8(l/16)+7, and
+// receives rows 4(l/16)..4(l/16)+3 of column l%16):
+//   scores S = Q K^T of the tile's 16 queries and its tokens j < 16t + 16,
+//     one 16-token tile per wave (exact bf16 products, fp32 sums);
+//   after each wave has merged its row's split partials and turned its
+//     scores into weights, O += P V_chunk, one 16-channel tile per wave,
+//     with the weights as bf16 hi/lo terms and the V rows as stored.
 template <int D>
 __global__ __launch_bounds__(1024) void rq_chunk_combine_kernel(ChunkCombineArgs a) {
     constexpr int QS = D + 1;
     constexpr int PF = partial_floats(D);
+    constexpr int SS = kMaxChunk + 4;              // row stride of the score / weight tile
     __shared__ float A[16 * QS];
     __shared__ float O[16 * QS];
-    __shared__ float QV[16 * QS];
+    __shared__ float S[16 * SS];
     const int lane = threadIdx.x & 63, r = threadIdx.x >> 6;
-    const int h = blockIdx.x, tile = blockIdx.y;
-    const int row = tile * 16 + r;
+    const int h = blockIdx.x;
     const int H = a.H, C = a.C;
+    const int nt = (C + 15) >> 4;
+    const int b = blockIdx.y / nt, t = blockIdx.y % nt;
+    const int i = 16 * t + r;
+    const bool row_ok = i < C;
+    const int64_t qrow = ((int64_t)b * C + (row_ok ? i : 0)) * H + h;
+    // the tile's chunk tokens (causal: up to its last query) in 16-token tiles
+    const int jmax = a.chunk_k ? min(C, 16 * t + 16) : 0;
+    const int ntt = (jmax + 15) >> 4;
+    if (r < ntt) {
+        const int qi = 16 * t + (lane & 15), tj = 16 * r + (lane & 15);
+        const uint16_t *qa = a.q + (((int64_t)b * C + min(qi, C - 1)) * H + h) * D + 8 * (lane >> 4);
+        const uint16_t *kb = a.chunk_k + (((int64_t)b * C + min(tj, jmax - 1)) * H + h) * D + 8 * (lane >> 4);
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk) {
+            const uint4 av = *(const uint4 *)(qa + 32 * kk), bv = *(const uint4 *)(kb + 32 * kk);
+            acc = mfma_bf16x32(av, bv, acc);
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) S[(4 * (lane >> 4) + v) * SS + tj] = acc[v] * a.score_scale;
+    }
+    __syncthreads();
+
     const int c0 = lane, c1 = lane + 64;
-    float ar0 = 0.f, ar1 = 0.f, as0 = 0.f, as1 = 0.f;
-    const bool rot_wave = a.res && r < D / 16;
-    const int n = r * 16 + (lane & 15);
-    if (row < a.R) {
-        const int b = row / C, i = row % C;
-        const int64_t qrow = (int64_t)row * H + h;
-        for (int c = lane; c < D; c += 64) QV[r * QS + c] = bf16_to_f32(a.q[qrow * D + c]);
+    float ar0 = 0.f, ar1 = 0.f, as0 = 0.f, as1 = 0.f, inv = 0.f;
+    if (row_ok) {
         int seq = a.seq_lens[b];
         seq = seq < 0 ? 0 : (seq > a.max_blocks * 16 ? a.max_blocks * 16 : seq);
         const int npages = (seq + 15) >> 4;
         const int ns = (npages + a.split_pages - 1) / a.split_pages;     // splits with pages
         const float *P = a.partials + qrow * a.nsplit * PF;
-        // chunk tokens 0..i: one lane per token (i < C), score over the whole row
+        // this row's chunk scores (tokens 0..i), lanes lane + 64k
         const int nj = a.chunk_k ? i + 1 : 0;
         float mloc = kNegInf;
         for (int s = lane; s < ns; s += 64) mloc = fmaxf(mloc, P[(int64_t)s * PF]);
-        float sj[4];                                     // chunk scores of tokens lane + 64k (C <= 256)
+        float sj[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int j = lane + 64 * k;
-            sj[k] = kNegInf;
-            if (j < nj) {
-                const uint16_t *kr = a.chunk_k + (((int64_t)b * C + j) * H + h) * D;
-                float d = 0.f;
-                for (int c = 0; c < D; c += 8) {
-                    const uint4 v = *(const uint4 *)(kr + c);
-                    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        d = fmaf(QV[r * QS + c + 2 * e], __uint_as_float(w[e] << 16), d);
-                        d = fmaf(QV[r * QS + c + 2 * e + 1], __uint_as_float(w[e] & 0xFFFF0000u), d);
-                    }
-                }
-                sj[k] = d * a.score_scale;
-                mloc = fmaxf(mloc, sj[k]);
-            }
+            sj[k] = j < nj ? S[r * SS + j] : kNegInf;
+            mloc = fmaxf(mloc, sj[k]);
         }
         const float M = wave_max(mloc);
+        float lloc = 0.f;
+        float pj[4] = {0.f, 0.f, 0.f, 0.f};
         if (M != kNegInf) {
-            float lloc = 0.f;
             const int k0 = min(c0, D - 1), k1 = min(c1, D - 1);
             // four partials per round with their loads in flight together
             // (indices past the last partial re-read it with weight 0)
@@ -866,51 +892,72 @@ __global__ __launch_bounds__(1024) void rq_chunk_combine_kernel(ChunkCombineArgs
                     as1 = fmaf(e[u], w1[u], as1);
                 }
             }
-            // chunk part: weights of tokens lane + 64k, then the V rows token by token
-            float pj[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 pj[k] = sj[k] == kNegInf ? 0.f : fast_exp2(sj[k] - M);
                 lloc += pj[k];
             }
-            // eight tokens per round with their loads in flight together
-            // (indices past the last token re-read it with weight 0; columns
-            // beyond D read column D-1 and are never stored)
-            const int k0v = min(c0, D - 1), k1v = min(c1, D - 1);
-            for (int j0 = 0; j0 < nj; j0 += 8) {
-                float pw[8], v0[8], v1[8];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int j = min(j0 + u, nj - 1);
-                    const float p = __shfl(pj[j >> 6], j & 63, 64);
-                    pw[u] = j0 + u < nj ? p : 0.f;
-                    const uint16_t *vr = a.chunk_v + (((int64_t)b * C + j) * H + h) * D;
-                    v0[u] = bf16_to_f32(vr[k0v]);
-                    v1[u] = bf16_to_f32(vr[k1v]);
-                }
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    ar0 = fmaf(pw[u], v0[u], ar0);
-                    ar1 = fmaf(pw[u], v1[u], ar1);
-                }
-            }
             const float lsum = wave_sum(lloc);
-            const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
-            ar0 *= inv; ar1 *= inv; as0 *= inv; as1 *= inv;
+            inv = lsum > 0.f ? 1.0f / lsum : 0.f;
         }
+        as0 *= inv; as1 *= inv;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) pj[k] *= inv;        // normalized weights of the chunk tokens
+        // this row's weights for the P V product (0 past token i)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (lane + 64 * k < 16 * ntt) S[r * SS + lane + 64 * k] = pj[k];
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (lane + 64 * k < 16 * ntt) S[r * SS + lane + 64 * k] = 0.f;
     }
+    // merged partials: O (reference sums, normalized below), A (residual, normalized)
+    if (c0 < D) { O[r * QS + c0] = ar0 * inv; A[r * QS + c0] = as0; }
+    if (c1 < D) { O[r * QS + c1] = ar1 * inv; A[r * QS + c1] = as1; }
     // this lane's R_V operands of the output rotation: loaded after the
     // merge (their registers would otherwise spill there), ahead of the
     // barrier that their latency overlaps
+    const bool rot_wave = a.res && r < D / 16;
+    const int n = r * 16 + (lane & 15);
     float rv[D / 4];
     if (rot_wave) {
         const float *RV = a.rot + ((int64_t)h * 2 + 1) * D * D + (int64_t)(lane >> 4) * D + n;
 #pragma unroll
         for (int kk = 0; kk < D / 4; ++kk) rv[kk] = RV[(int64_t)4 * kk * D];
     }
-    if (c0 < D) { O[r * QS + c0] = ar0; A[r * QS + c0] = as0; }
-    if (c1 < D) { O[r * QS + c1] = ar1; A[r * QS + c1] = as1; }
     __syncthreads();
+
+    // O += P V_chunk: wave r computes channels 16r..16r+15 over the tile's
+    // tokens, 32 per product (tokens past the tile's last one weigh 0)
+    if (ntt > 0 && r < D / 16) {
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        const uint16_t *vcol = a.chunk_v + ((int64_t)b * C * H + h) * D + n;
+        for (int j0 = 0; j0 < 16 * ntt; j0 += 32) {
+            const int jb = j0 + 8 * (lane >> 4);
+            uint32_t hi[4], lo[4], vv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int ja = jb + 2 * e, jc = ja + 1;
+                const float wa = ja < 16 * ntt ? S[(lane & 15) * SS + ja] : 0.f;
+                const float wc = jc < 16 * ntt ? S[(lane & 15) * SS + jc] : 0.f;
+                const uint32_t ha = bf16_rne(wa), hc = bf16_rne(wc);
+                const uint32_t la = bf16_rne(wa - __uint_as_float(ha << 16)), lc = bf16_rne(wc - __uint_as_float(hc << 16));
+                hi[e] = ha | (hc << 16);
+                lo[e] = la | (lc << 16);
+                const uint32_t va = ja < jmax ? vcol[(int64_t)ja * H * D] : 0u;
+                const uint32_t vc = jc < jmax ? vcol[(int64_t)jc * H * D] : 0u;
+                vv[e] = va | (vc << 16);
+            }
+            const uint4 bv = make_uint4(vv[0], vv[1], vv[2], vv[3]);
+            acc = mfma_bf16x32(make_uint4(hi[0], hi[1], hi[2], hi[3]), bv, acc);
+            acc = mfma_bf16x32(make_uint4(lo[0], lo[1], lo[2], lo[3]), bv, acc);
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) O[(4 * (lane >> 4) + v) * QS + n] += acc[v];
+    }
+    __syncthreads();
+
     if (a.res) {
         // out = O + A * R_V (R_V^T applied to each row's residual sum), as in decode
         if (rot_wave) {
@@ -922,13 +969,13 @@ __global__ __launch_bounds__(1024) void rq_chunk_combine_kernel(ChunkCombineArgs
             }
             for (int v = 0; v < 4; ++v) {
                 const int rr = 4 * (lane >> 4) + v;
-                const int rw = tile * 16 + rr;
-                if (rw < a.R) a.out[((int64_t)rw * H + h) * D + n] = c[v] + O[rr * QS + n];
+                const int ir = 16 * t + rr;
+                if (ir < C) a.out[(((int64_t)b * C + ir) * H + h) * D + n] = c[v] + O[rr * QS + n];
             }
         }
-    } else if (row < a.R) {
-        if (c0 < D) a.out[((int64_t)row * H + h) * D + c0] = O[r * QS + c0];
-        if (c1 < D) a.out[((int64_t)row * H + h) * D + c1] = O[r * QS + c1];
+    } else if (row_ok) {
+        if (c0 < D) a.out[qrow * D + c0] = O[r * QS + c0];
+        if (c1 < D) a.out[qrow * D + c1] = O[r * QS + c1];
     }
 }
 
@@ -988,7 +1035,7 @@ hipError_t launch_chunk_d(const ChunkCall &c) {
     ca.chunk_k = (const uint16_t *)c.chunk_k; ca.chunk_v = (const uint16_t *)c.chunk_v;
     ca.rot = c.rot; ca.out = c.out; ca.R = R; ca.C = c.C; ca.H = g.H; ca.res = res ? 1 : 0;
     ca.score_scale = s.score_scale;
-    hipLaunchKernelGGL((rq_chunk_combine_kernel<D>), dim3(g.H, tiles), dim3(1024), 0, c.stream, ca);
+    hipLaunchKernelGGL((rq_chunk_combine_kernel<D>), dim3(g.H, c.B * ((c.C + 15) / 16)), dim3(1024), 0, c.stream, ca);
     return hipGetLastError();
 }
 
