@@ -75,12 +75,6 @@ constexpr int kChunkFold = 16;           // pages between folds of the zero term
 template <int D>
 __host__ __device__ constexpr int chunk_steps8() { return (D / 4 + 15) / 16; }
 
-template <int BITS>
-__device__ __forceinline__ int chunk_byte_channel(int s, int e) {
-    const int d = e >> 2, i = e & 3;
-    return BITS == 4 ? 16 * s + 8 * (d >> 1) + 2 * i + (d & 1) : 16 * s + 4 * i + d;
-}
-
 template <int D, int BITS>
 __device__ __forceinline__ uint4 chunk_kbytes(const uint32_t *w, int s) {
     if constexpr (BITS == 4) {
@@ -119,17 +113,17 @@ __device__ __forceinline__ int fix_digit(int v, int l) {
     return l == 0 ? d0 : (l == 1 ? d1 : (v1 - d1) >> 8);
 }
 
-// word d of digit l, step s, lane slot kb of a row's operand
+// Byte of channel c (0..D-1) in the digit words of a query row: the words
+// are [step s][digit l][lane slot kb][4 words d], byte i of word d holding
+// the slot's channel 16s + 8 (d / 2) + 2 i + d % 2 (INT4 operand order) or
+// 16s + 4 i + d (INT2), slot kb covering channels kb D/4 ..; this returns
+// the byte of digit 0 (digit l: + 64 l).
 template <int D, int BITS>
-__device__ __forceinline__ uint32_t digit_word(const float *row, int e, int s, int l, int kb, int d) {
-    uint32_t w = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int ch = chunk_byte_channel<BITS>(s, 4 * d + i);
-        const int v = ch < D / 4 ? fix_digit(fix_int(row[kb * (D / 4) + ch], e), l) : 0;
-        w |= (uint32_t)(v & 0xFF) << (8 * i);
-    }
-    return w;
+__device__ __forceinline__ int digit_byte(int c) {
+    const int kb = c / (D / 4), ch = c % (D / 4), st = ch >> 4, rem = ch & 15;
+    const int d = BITS == 4 ? 2 * (rem >> 3) + (rem & 1) : rem & 3;
+    const int i = BITS == 4 ? (rem & 7) >> 1 : rem >> 2;
+    return st * 192 + kb * 16 + d * 4 + i;
 }
 
 // ------------------------------------------------------------------ qprep
@@ -146,6 +140,7 @@ __global__ __launch_bounds__(1024) void rq_chunk_qprep_kernel(ChunkPrepArgs a) {
     constexpr int QS = D + 1;
     __shared__ float Q[16 * QS];
     __shared__ float QR[16 * QS];
+    __shared__ uint32_t DW[16 * 2 * chunk_steps8<D>() * 48];   // per row: the digit words of q and q'
     const int lane = threadIdx.x & 63, r = threadIdx.x >> 6;
     const int h = blockIdx.x, tile = blockIdx.y;
     const int row = tile * 16 + r;
@@ -188,34 +183,51 @@ __global__ __launch_bounds__(1024) void rq_chunk_qprep_kernel(ChunkPrepArgs a) {
     // slot kb][4 words]
     uint8_t *rec = a.qrec + ((int64_t)row * a.H + h) * chunk_qrec_bytes(D);
     const float *qrow = Q + r * QS, *rrow = QR + r * QS;
-    float mq = 0.f, mr = 0.f;
-    for (int c = lane; c < D; c += 64) {
-        mq = fmaxf(mq, fabsf(qrow[c]));
-        if (a.res) mr = fmaxf(mr, fabsf(rrow[c]));
-    }
+    const bool has1 = lane + 64 < D;
+    const float x0 = qrow[lane], x1 = has1 ? qrow[lane + 64] : 0.f;
+    const float y0 = a.res ? rrow[lane] : 0.f, y1 = (a.res && has1) ? rrow[lane + 64] : 0.f;
     // one exponent for q and q' (that of the larger magnitude), so that the
     // two sums of a score share the scale 2^-e
-    const int eq0 = fix_exp(wave_max(mq)), er0 = fix_exp(wave_max(mr));
-    const int eq = a.res ? min(eq0, er0) : eq0, er = eq;
-    // sums of the fixed-point values the products see (exact: |sum| < 2^29)
-    int sq = 0, sr = 0;
-    for (int c = lane; c < D; c += 64) {
-        sq += fix_int(qrow[c], eq);
-        if (a.res) sr += fix_int(rrow[c], er);
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        sq += __shfl_xor(sq, o, 64);
-        sr += __shfl_xor(sr, o, 64);
-    }
+    float mx[2] = {fmaxf(fabsf(x0), fabsf(x1)), fmaxf(fabsf(y0), fabsf(y1))};
+    wave_max_n(mx);
+    const int eq0 = fix_exp(mx[0]), er0 = fix_exp(mx[1]);
+    const int eq = a.res ? min(eq0, er0) : eq0;
+    // the fixed-point values (each channel converted once) and their sums
+    // (exact: |sum| < 2^29)
+    const int vq0 = fix_int(x0, eq), vq1 = has1 ? fix_int(x1, eq) : 0;
+    const int vr0 = fix_int(y0, eq), vr1 = has1 ? fix_int(y1, eq) : 0;
+    int sums[2] = {vq0 + vq1, vr0 + vr1};
+    wave_sum_n(sums);
+    // the digit words of this row, assembled byte by byte in LDS (zero
+    // bytes for the padding channels), then stored as words
     constexpr int NS = chunk_steps8<D>();
-    uint32_t *wq = (uint32_t *)(rec + 16), *wr = wq + NS * 48;
-    for (int j = lane; j < NS * 48; j += 64) {
-        const int s = j / 48, l = (j / 16) % 3, kb = (j / 4) % 4, d = j % 4;
-        wq[j] = digit_word<D, 4>(qrow, eq, s, l, kb, d);
-        if (a.res == 4) wr[j] = digit_word<D, 4>(rrow, er, s, l, kb, d);
-        else if (a.res) wr[j] = digit_word<D, 2>(rrow, er, s, l, kb, d);
+    constexpr int NW = NS * 48;                 // words per quantity
+    uint32_t *img = DW + r * 2 * NW;
+    for (int j = lane; j < 2 * NW; j += 64) img[j] = 0u;
+    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's zeros land before its bytes
+    uint8_t *bq = (uint8_t *)img, *br = (uint8_t *)(img + NW);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int c = lane + 64 * u;
+        if (c < D) {
+            const int vq = u ? vq1 : vq0, vr = u ? vr1 : vr0;
+            const int oq = digit_byte<D, 4>(c);
+#pragma unroll
+            for (int l = 0; l < 3; ++l) bq[oq + 64 * l] = (uint8_t)fix_digit(vq, l);
+            if (a.res) {
+                const int orr = a.res == 4 ? digit_byte<D, 4>(c) : digit_byte<D, 2>(c);
+#pragma unroll
+                for (int l = 0; l < 3; ++l) br[orr + 64 * l] = (uint8_t)fix_digit(vr, l);
+            }
+        }
     }
+    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // LDS keeps one wave's accesses in order
+    uint32_t *wq = (uint32_t *)(rec + 16), *wr = wq + NW;
+    for (int j = lane; j < NW; j += 64) {
+        wq[j] = img[j];
+        if (a.res) wr[j] = img[NW + j];
+    }
+    const int sq = sums[0], sr = sums[1];
     if (lane == 0) {
         float *hd = (float *)rec;
         hd[0] = (float)sq;
