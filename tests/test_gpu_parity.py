@@ -141,6 +141,25 @@ def test_shuffled_table_is_bitwise_invariant():
                                       b.run_decode(b.device_pool_from_oracle(), [l]))
 
 
+def test_many_partials_per_row():
+    """Rows with many split partials: 4500 cached tokens (282 pages) in one
+    sequence, 1800 in the other, splits of 1, 2 and 3 pages. The per-loop
+    combine then merges 71, 36 and 24 workgroup partials per row (more than
+    one round of 64 lanes, and around its first round of 24 prefetched
+    partials); the multi-loop call up to 282 per row and loop."""
+    c = SmallCase(W.get(1).replace(batch=2, heads=2, context=4500), shuffled=True, seq_lens=[4500, 1800])
+    pool = c.device_pool_from_oracle()
+    L = c.w.loops
+    want = [c.oracle_out(l) for l in range(L)]
+    for sp in (1, 2, 3):
+        multi = c.run_decode(pool, list(range(L)), tail=True, split_pages=sp)
+        for l in range(L):
+            got = c.run_decode(pool, [l], tail=True, split_pages=sp)[0]
+            e, r = check_attention(f"long rows loop {l} sp {sp}", got, want[l])
+            check_attention(f"long rows multi-loop loop {l} sp {sp}", multi[l], want[l])
+            print(f"[long rows loop {l} sp {sp}] max-abs {e:.2e} rel-L2 {r:.2e}", flush=True)
+
+
 def test_split_count_changes_only_rounding():
     c = case("ouro_small")
     pool = c.device_pool_from_oracle()
