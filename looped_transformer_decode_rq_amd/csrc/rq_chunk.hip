@@ -35,9 +35,9 @@
 //   rq_chunk_split    per (head, split of pages, sequence x 64 queries): four
 //                     waves of 16 queries walk the split's pages, online
 //                     softmax per query, one partial per (split, query)
-//   rq_chunk_combine  per (head, 16 query rows): merge the partials, the
-//                     chunk's causal part in bf16, out = acc_ref/l + R_V^T
-//                     acc_res/l on the f32 matrix cores
+//   rq_chunk_combine  per (head, sequence, 16 queries): merge the partials,
+//                     the chunk's causal part on the bf16 matrix cores,
+//                     out = acc_ref/l + R_V^T acc_res/l on the f32 matrix cores
 #include <hip/hip_ext.h>
 
 #include "rq_device.h"
@@ -924,7 +924,8 @@ __global__ __launch_bounds__(1024) void rq_chunk_combine_kernel(ChunkCombineArgs
         for (int k = 0; k < 4; ++k)
             if (lane + 64 * k < 16 * ntt) S[r * SS + lane + 64 * k] = 0.f;
     }
-    // merged partials: O (reference sums, normalized below), A (residual, normalized)
+    // merged partials, normalized: O (reference sums; the chunk's part is
+    // added below) and A (residual sums)
     if (c0 < D) { O[r * QS + c0] = ar0 * inv; A[r * QS + c0] = as0; }
     if (c1 < D) { O[r * QS + c1] = ar1 * inv; A[r * QS + c1] = as1; }
     // this lane's R_V operands of the output rotation: loaded after the
