@@ -669,8 +669,15 @@ __global__ __launch_bounds__(256, 2) void rq_chunk_split_kernel(ChunkArgs a) {
             const uint8_t *S0 = ring + ((2 * ci) % NST) * stage, *S1 = ring + ((2 * ci + 1) % NST) * stage;
             const float *T0 = tabs + (ci & 1) * 256, *T1 = T0 + 128;
             float sc0[4], sc1[4];
+            // The two workgroups on a CU run out of phase: each SIMD holds one
+            // wave of each. Raising this wave's priority over its matrix-core
+            // sections (the score products here, the V products below) lets
+            // the other wave's VALU work fill the cycles around them
+            // (measured: residual 1.300 -> 1.278 ms, reference 0.672 -> 0.624 ms).
+            __builtin_amdgcn_s_setprio(1);
             page_scores(2 * ci, S0, T0, sc0);
             page_scores(2 * ci + 1, S1, T1, sc1);
+            __builtin_amdgcn_s_setprio(0);
             // ---- online softmax per query (lanes x, x+16, x+32, x+48 share query x)
             float pmax = fmaxf(fmaxf(fmaxf(sc0[0], sc0[1]), fmaxf(sc0[2], sc0[3])),
                                fmaxf(fmaxf(sc1[0], sc1[1]), fmaxf(sc1[2], sc1[3])));
@@ -709,6 +716,7 @@ __global__ __launch_bounds__(256, 2) void rq_chunk_split_kernel(ChunkArgs a) {
             // ---- out += P x V: k = this lane group's four tokens of page
             // 2ci, then the same four of page 2ci+1; hi and lo weights in two
             // products against the same V operand
+            __builtin_amdgcn_s_setprio(1);
             const uint8_t *rv0 = S0 + a.ref_rec, *rv1 = S1 + a.ref_rec;
             uint2 h0, l0, h1, l1;
             float u0, u1;
@@ -731,6 +739,7 @@ __global__ __launch_bounds__(256, 2) void rq_chunk_split_kernel(ChunkArgs a) {
                 load_v<D, RB>(vb, sv1, lane);
                 v_mfma_pair<D, RB>(vacc_s, va, vb, make_uint4(h0.x, h0.y, h1.x, h1.y), make_uint4(l0.x, l0.y, l1.x, l1.y));
             }
+            __builtin_amdgcn_s_setprio(0);
         }
         // After every block of kChunkFold pages the zero terms go into the
         // accumulators. The products carry the offset 16 of every code, so the
