@@ -87,6 +87,38 @@ __device__ __forceinline__ uint4 chunk_kbytes(const uint32_t *w, int s) {
     }
 }
 
+// Maxima of scores, which are never NaN: the plain instructions. (fmaxf
+// makes the compiler quiet possible signaling NaNs first, one extra
+// instruction per operand it cannot prove canonical.)
+__device__ __forceinline__ float vmax2(float a, float b) {
+    float r;
+    __asm__("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+    float r;
+    __asm__("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
+// Max of x over lanes l, l^16, l^32, l^48 (the four lanes that share a query)
+// with the gfx950 row and half swaps (v_permlane16_swap, v_permlane32_swap):
+// no LDS round trip, unlike a bpermute shuffle
+__device__ __forceinline__ float max_lanes4(float x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float y = vmax2(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+    return vmax2(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Sum of x over the same four lanes, as (x_l + x_l^16) + (x_l^32 + x_l^48)
+__device__ __forceinline__ float sum_lanes4(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 typedef int intx4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ intx4 mfma_i8(uint4 a, uint4 b, intx4 c) {
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(intx4, a), __builtin_bit_cast(intx4, b), c, 0, 0,
@@ -679,11 +711,9 @@ __global__ __launch_bounds__(256, 2) void rq_chunk_split_kernel(ChunkArgs a) {
             page_scores(2 * ci + 1, S1, T1, sc1);
             __builtin_amdgcn_s_setprio(0);
             // ---- online softmax per query (lanes x, x+16, x+32, x+48 share query x)
-            float pmax = fmaxf(fmaxf(fmaxf(sc0[0], sc0[1]), fmaxf(sc0[2], sc0[3])),
-                               fmaxf(fmaxf(sc1[0], sc1[1]), fmaxf(sc1[2], sc1[3])));
-            pmax = fmaxf(pmax, __shfl_xor(pmax, 16, 64));
-            pmax = fmaxf(pmax, __shfl_xor(pmax, 32, 64));
-            pmax *= hd.z;                          // log2 units
+            float pmax = vmax2(vmax3(sc0[0], sc0[1], sc0[2]),
+                               vmax3(sc0[3], sc1[0], vmax3(sc1[1], sc1[2], sc1[3])));
+            pmax = max_lanes4(pmax) * hd.z;        // log2 units
             if (__any(pmax > m + kThreshC)) {
                 const float mn = fmaxf(m, pmax);
                 const float f = fast_exp2(m - mn);
@@ -750,13 +780,8 @@ __global__ __launch_bounds__(256, 2) void rq_chunk_split_kernel(ChunkArgs a) {
         // and their fp32 rounding would otherwise build up over the whole split
         // (thousands of tokens); folded, it builds up over one block only.
         if (q0 < C) {
-            float zq = zr + __shfl_xor(zr, 16, 64);
-            zq += __shfl_xor(zq, 32, 64);
-            float zsq = 0.f;
-            if constexpr (RB != 0) {
-                zsq = zs + __shfl_xor(zs, 16, 64);
-                zsq += __shfl_xor(zsq, 32, 64);
-            }
+            const float zq = sum_lanes4(zr);
+            const float zsq = RB != 0 ? sum_lanes4(zs) : 0.f;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const float zrv = __shfl(zq, 4 * kb + v, 64);       // accumulator row v: query 4kb + v
