@@ -73,39 +73,59 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
-__device__ __forceinline__ float wave_max(float v) {
+// Butterfly partners of a whole-wave reduction without LDS: quad xor 1 and
+// xor 2 and row rotations by 4 and 8 (DPP) leave the row's reduction in each
+// of its 16 lanes; the gfx950 row swap (v_permlane16_swap) then pairs rows
+// 0-1 and 2-3, the half swap (v_permlane32_swap) the two halves. A bpermute
+// shuffle per step would cost an LDS round trip and its address arithmetic.
+__device__ __forceinline__ uint32_t dpp_row_ror4(uint32_t v) { return __builtin_amdgcn_mov_dpp(v, 0x124, 0xF, 0xF, false); }
+__device__ __forceinline__ uint32_t dpp_row_ror8(uint32_t v) { return __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false); }
+__device__ __forceinline__ uint32_t dpp_xor1(uint32_t v) { return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false); }
+__device__ __forceinline__ uint32_t dpp_xor2(uint32_t v) { return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false); }
+
+template <int N, typename T, typename Op>
+__device__ __forceinline__ void wave_reduce_n(T (&v)[N], Op op) {
+    static_assert(sizeof(T) == 4, "32-bit values");
+    auto u = [](T x) { return __builtin_bit_cast(uint32_t, x); };
+    auto t = [](uint32_t x) { return __builtin_bit_cast(T, x); };
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-    return v;
+    for (int j = 0; j < N; ++j) v[j] = op(v[j], t(dpp_xor1(u(v[j]))));
+#pragma unroll
+    for (int j = 0; j < N; ++j) v[j] = op(v[j], t(dpp_xor2(u(v[j]))));
+#pragma unroll
+    for (int j = 0; j < N; ++j) v[j] = op(v[j], t(dpp_row_ror4(u(v[j]))));
+#pragma unroll
+    for (int j = 0; j < N; ++j) v[j] = op(v[j], t(dpp_row_ror8(u(v[j]))));
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+        const auto a = __builtin_amdgcn_permlane16_swap(u(v[j]), u(v[j]), false, false);
+        v[j] = op(t(a[0]), t(a[1]));
+    }
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+        const auto a = __builtin_amdgcn_permlane32_swap(u(v[j]), u(v[j]), false, false);
+        v[j] = op(t(a[0]), t(a[1]));
+    }
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+    float a[1] = {v};
+    wave_reduce_n<1>(a, [](float x, float y) { return fmaxf(x, y); });
+    return a[0];
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
+    float a[1] = {v};
+    wave_reduce_n<1>(a, [](float x, float y) { return x + y; });
+    return a[0];
 }
-// The same butterflies over N values at once: the N shuffles of each step
-// are issued together, so the latency is that of one reduction.
+// The same over N values at once (independent chains, issued together).
 template <int N>
 __device__ __forceinline__ void wave_max_n(float (&v)[N]) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        float o[N];
-#pragma unroll
-        for (int j = 0; j < N; ++j) o[j] = __shfl_xor(v[j], off, 64);
-#pragma unroll
-        for (int j = 0; j < N; ++j) v[j] = fmaxf(v[j], o[j]);
-    }
+    wave_reduce_n<N>(v, [](float x, float y) { return fmaxf(x, y); });
 }
 template <int N>
 __device__ __forceinline__ void wave_sum_n(int (&v)[N]) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        int o[N];
-#pragma unroll
-        for (int j = 0; j < N; ++j) o[j] = __shfl_xor(v[j], off, 64);
-#pragma unroll
-        for (int j = 0; j < N; ++j) v[j] += o[j];
-    }
+    wave_reduce_n<N>(v, [](int x, int y) { return x + y; });
 }
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
