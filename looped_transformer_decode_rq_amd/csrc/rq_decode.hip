@@ -650,11 +650,10 @@ __device__ __forceinline__ void token_step(const uint8_t *ck, const uint8_t *mkr
 template <int D, bool RES, int G>
 __device__ __forceinline__ void finish_split(SplitState<D> &s, int lane, float *out) {
     constexpr int LPT = Lanes<D>::LPT, CPL = Lanes<D>::CPL, NPG = G / CPL;
-#pragma unroll
-    for (int off = LPT; off < 64; off <<= 1) {
-        s.zr += __shfl_xor(s.zr, off, 64);
-        if constexpr (RES) s.zs += __shfl_xor(s.zs, off, 64);
-        s.lsum += __shfl_xor(s.lsum, off, 64);
+    {
+        float t[3] = {s.zr, RES ? s.zs : 0.f, s.lsum};
+        strided_sum_n<LPT>(t);
+        s.zr = t[0]; s.zs = t[1]; s.lsum = t[2];
     }
     // lane q4 = g*NPG (token slot 0) holds group g's zero terms
     const int gl = lane >> 4, col = lane & 15;
@@ -736,11 +735,10 @@ __device__ __forceinline__ void shared_ref_gather(const SplitState<D> &s, float 
 template <int D, bool RES, int G>
 __device__ __forceinline__ void finish_split_shared(SplitState<D> &s, int lane, const float *gref, float *out) {
     constexpr int LPT = Lanes<D>::LPT, CPL = Lanes<D>::CPL, NPG = G / CPL;
-#pragma unroll
-    for (int off = LPT; off < 64; off <<= 1) {
-        s.zr += __shfl_xor(s.zr, off, 64);
-        if constexpr (RES) s.zs += __shfl_xor(s.zs, off, 64);
-        s.lsum += __shfl_xor(s.lsum, off, 64);
+    {
+        float t[3] = {s.zr, RES ? s.zs : 0.f, s.lsum};
+        strided_sum_n<LPT>(t);
+        s.zr = t[0]; s.zs = t[1]; s.lsum = t[2];
     }
     const int gl = lane >> 4, col = lane & 15;
     const float zr = __shfl(s.zr, gl * NPG, 64);

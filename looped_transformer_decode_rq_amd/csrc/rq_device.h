@@ -108,6 +108,37 @@ __device__ __forceinline__ void wave_reduce_n(T (&v)[N], Op op) {
     }
 }
 
+// Sums over the lanes that share lane % LPT (LPT in {1, 2, 4}), every such
+// lane receiving its sum: the steps of wave_reduce_n from the first partner
+// distance LPT on.
+template <int LPT, int N>
+__device__ __forceinline__ void strided_sum_n(float (&v)[N]) {
+    auto u = [](float x) { return __builtin_bit_cast(uint32_t, x); };
+    auto f = [](uint32_t x) { return __builtin_bit_cast(float, x); };
+    if constexpr (LPT == 1) {
+#pragma unroll
+        for (int j = 0; j < N; ++j) v[j] += f(dpp_xor1(u(v[j])));
+    }
+    if constexpr (LPT <= 2) {
+#pragma unroll
+        for (int j = 0; j < N; ++j) v[j] += f(dpp_xor2(u(v[j])));
+    }
+#pragma unroll
+    for (int j = 0; j < N; ++j) v[j] += f(dpp_row_ror4(u(v[j])));
+#pragma unroll
+    for (int j = 0; j < N; ++j) v[j] += f(dpp_row_ror8(u(v[j])));
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+        const auto a = __builtin_amdgcn_permlane16_swap(u(v[j]), u(v[j]), false, false);
+        v[j] = f(a[0]) + f(a[1]);
+    }
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+        const auto a = __builtin_amdgcn_permlane32_swap(u(v[j]), u(v[j]), false, false);
+        v[j] = f(a[0]) + f(a[1]);
+    }
+}
+
 __device__ __forceinline__ float wave_max(float v) {
     float a[1] = {v};
     wave_reduce_n<1>(a, [](float x, float y) { return fmaxf(x, y); });
