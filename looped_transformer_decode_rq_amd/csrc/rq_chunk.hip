@@ -860,7 +860,7 @@ __device__ __forceinline__ floatx4 mfma_bf16x32(uint4 a, uint4 b, floatx4 c) {
 //     scores into weights, O += P V_chunk, one 16-channel tile per wave,
 //     with the weights as bf16 hi/lo terms and the V rows as stored.
 template <int D>
-__global__ __launch_bounds__(1024) void rq_chunk_combine_kernel(ChunkCombineArgs a) {
+__global__ __launch_bounds__(1024, 8) void rq_chunk_combine_kernel(ChunkCombineArgs a) {
     constexpr int QS = D + 1;
     constexpr int PF = partial_floats(D);
     constexpr int SS = kMaxChunk + 4;              // row stride of the score / weight tile
@@ -965,17 +965,8 @@ __global__ __launch_bounds__(1024) void rq_chunk_combine_kernel(ChunkCombineArgs
     // added below) and A (residual sums)
     if (c0 < D) { O[r * QS + c0] = ar0 * inv; A[r * QS + c0] = as0; }
     if (c1 < D) { O[r * QS + c1] = ar1 * inv; A[r * QS + c1] = as1; }
-    // this lane's R_V operands of the output rotation: loaded after the
-    // merge (their registers would otherwise spill there), ahead of the
-    // barrier that their latency overlaps
     const bool rot_wave = a.res && r < D / 16;
     const int n = r * 16 + (lane & 15);
-    float rv[D / 4];
-    if (rot_wave) {
-        const float *RV = a.rot + ((int64_t)h * 2 + 1) * D * D + (int64_t)(lane >> 4) * D + n;
-#pragma unroll
-        for (int kk = 0; kk < D / 4; ++kk) rv[kk] = RV[(int64_t)4 * kk * D];
-    }
     __syncthreads();
 
     // O += P V_chunk: wave r computes channels 16r..16r+15 over the tile's
@@ -1011,6 +1002,11 @@ __global__ __launch_bounds__(1024) void rq_chunk_combine_kernel(ChunkCombineArgs
     if (a.res) {
         // out = O + A * R_V (R_V^T applied to each row's residual sum), as in decode
         if (rot_wave) {
+            // this lane's R_V operands (rows 4kk + lane/16 of column n)
+            float rv[D / 4];
+            const float *RV = a.rot + ((int64_t)h * 2 + 1) * D * D + (int64_t)(lane >> 4) * D + n;
+#pragma unroll
+            for (int kk = 0; kk < D / 4; ++kk) rv[kk] = RV[(int64_t)4 * kk * D];
             floatx4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < D / 4; ++kk) {
