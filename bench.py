@@ -673,10 +673,18 @@ def traffic_from_profiles(kernel_src_hash):
 
 
 def kernel_src_hash(files=("rq_decode.hip", "rq_device.h", "rq_internal.h", "rq_vmfma.h")):
+    """sha256 of the kernel sources' code: comments and blank lines are left
+    out, so that a comment edit does not void the counter summaries taken on
+    the same code."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in files:
-        h.update(open(os.path.join(ROOT, "looped_transformer_decode_rq_amd", "csrc", f), "rb").read())
+        src = open(os.path.join(ROOT, "looped_transformer_decode_rq_amd", "csrc", f)).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", "", src)
+        code = "\n".join(line.rstrip() for line in src.splitlines() if line.strip())
+        h.update(code.encode())
     return h.hexdigest()
 
 

@@ -78,6 +78,8 @@ __device__ __forceinline__ float group_sum(float v) {
 // of its 16 lanes; the gfx950 row swap (v_permlane16_swap) then pairs rows
 // 0-1 and 2-3, the half swap (v_permlane32_swap) the two halves. A bpermute
 // shuffle per step would cost an LDS round trip and its address arithmetic.
+// These read other lanes' registers unconditionally: call them with every
+// lane of the wave active (all call sites are wave-uniform).
 __device__ __forceinline__ uint32_t dpp_row_ror4(uint32_t v) { return __builtin_amdgcn_mov_dpp(v, 0x124, 0xF, 0xF, false); }
 __device__ __forceinline__ uint32_t dpp_row_ror8(uint32_t v) { return __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false); }
 __device__ __forceinline__ uint32_t dpp_xor1(uint32_t v) { return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false); }
