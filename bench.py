@@ -814,9 +814,30 @@ def main():
     stream_ref["split_kernel_frac_of_reference"] = {
         "residual": (res_bytes / (res_ms * 1e-3) / 1e9) / stream_ref["residual"]["gbs"],
         "reference": (ref_bytes / (ref_ms * 1e-3) / 1e9) / stream_ref["reference"]["gbs"]}
+    # the roof of any access pattern: a plain contiguous read of a 4 GiB buffer
+    cbytes = 4 << 30
+    cbuf = torch.empty(cbytes, dtype=torch.uint8, device=dev)
+    csink = torch.zeros(32 * 256, dtype=torch.int32, device=dev)   # one word per wave
+    c_ev = [(ev.create(), ev.create()) for _ in range(args.steps)]
+
+    def cread_fn(k):
+        R.read_probe(cbuf, csink, events=None if k is None else c_ev[k])
+
+    timed(cread_fn, args.steps, args.warmup)
+    cms = float(np.mean([ev.ms(a, b) for a, b in c_ev]))
+    for a, b in c_ev:
+        ev.destroy(a)
+        ev.destroy(b)
+    del cbuf
+    c_gbs = cbytes / (cms * 1e-3) / 1e9
+    stream_ref["contiguous_read"] = {"kernel_ms": cms, "bytes_per_launch": cbytes, "gbs": c_gbs,
+                                     "frac_of_peak": c_gbs / HBM_PEAK_GBS}
+    stream_ref["split_kernel_frac_of_contiguous_read"] = {
+        "residual": (res_bytes / (res_ms * 1e-3) / 1e9) / c_gbs,
+        "reference": (ref_bytes / (ref_ms * 1e-3) / 1e9) / c_gbs}
     log(f"streaming reference (same loads, no arithmetic): residual {stream_ref['residual']['kernel_ms']:.3f} ms "
         f"({stream_ref['residual']['gbs']:.0f} GB/s), reference {stream_ref['reference']['kernel_ms']:.3f} ms "
-        f"({stream_ref['reference']['gbs']:.0f} GB/s)")
+        f"({stream_ref['reference']['gbs']:.0f} GB/s); contiguous read {c_gbs:.0f} GB/s")
 
     # multi-loop mode: the same step with the 4 loops' queries in one call
     mpairs = {k: (ev.create(), ev.create()) for k in range(args.steps)}

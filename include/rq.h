@@ -255,6 +255,25 @@ rq_status rq_decode_stream_probe(const rq_layout *layout, const void *pool, int3
                                  int32_t max_blocks_per_seq, void *workspace, size_t workspace_bytes,
                                  const rq_decode_opts *opts, void *stream);
 
+/* Bandwidth reference of a plain contiguous read: streams `bytes` bytes of
+ * device memory at `buf` (16-byte aligned, bytes a multiple of 16) with
+ * 16-byte non-temporal vector loads, eight in flight per lane, over eight
+ * 256-thread workgroups per compute unit, and folds them into checksum words:
+ * `sink` is a device array of `sink_words` uint32 that the caller zeroes
+ * first; each wave XORs its share into one word, so that on completion the
+ * XOR of all sink words is the XOR of all 32-bit words of the buffer (every
+ * byte read once). Give one word per wave, 32 per compute unit (fewer words
+ * are allowed; waves then share them and their atomics queue). Its duration
+ * is the rate at which HBM streams contiguous reads, the roof against which
+ * the decode kernels and their page pattern (rq_decode_stream_probe) are
+ * compared, ResidualQuant decode being bound by the bytes it reads (arXiv
+ * 2610.10381, abstract). opts may be NULL; its timing events bracket the
+ * kernel when set (split_pages is ignored). RQ_ERR_NULL for a null sink (or a
+ * null buf with bytes > 0), RQ_ERR_SHAPE for a misaligned buffer or size or
+ * sink_words < 1. */
+rq_status rq_read_probe(const void *buf, size_t bytes, uint32_t *sink, int32_t sink_words,
+                        const rq_decode_opts *opts, void *stream);
+
 /* rq_decode_attention_ex without a caller workspace, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation). The query records and split partials go

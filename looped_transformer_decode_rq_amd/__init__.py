@@ -12,5 +12,5 @@ from ._lib import (  # noqa: F401
     RQ_NOALLOC_SCRATCH_BYTES, bf16_workspace_bytes,
     bf16_auto_split_pages, chunk_workspace_bytes, chunk_attention,
     bf16_decode_attention, bf16_write, status_string, fit_rotation, fit_rotation_device, fit_workspace_bytes,
-    decode_stream_probe, EXPORTED,
+    decode_stream_probe, read_probe, EXPORTED,
 )

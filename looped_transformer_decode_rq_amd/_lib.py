@@ -25,6 +25,7 @@ EXPORTED = [
     "rq_bf16_auto_split_pages", "rq_bf16_decode_attention", "rq_bf16_decode_attention_ex", "rq_bf16_write",
     "rq_chunk_workspace_bytes", "rq_chunk_attention", "rq_decode_attention_noalloc",
     "rq_fit_rotation_device", "rq_fit_workspace_bytes", "rq_decode_stream_probe", "rq_encode_workspace_bytes",
+    "rq_read_probe",
 ]
 RQ_NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -87,6 +88,7 @@ def lib():
             "rq_fit_workspace_bytes": (c_size_t, [c_int32]),
             "rq_decode_stream_probe": (c_int32, [POINTER(RqLayout), P, c_int32, P, P, c_int32, c_int32, P, c_size_t,
                                                  POINTER(RqDecodeOpts), P]),
+            "rq_read_probe": (c_int32, [P, c_size_t, P, c_int32, POINTER(RqDecodeOpts), P]),
             "rq_bf16_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32]),
             "rq_bf16_auto_split_pages": (c_int32, [c_int32, c_int32, c_int32]),
             "rq_bf16_decode_attention": (c_int32, [c_int32, c_int32, c_int32, c_int32, P, P, P, P, P, c_int32,
@@ -420,3 +422,16 @@ def decode_stream_probe(layout, pool, loop, block_table, seq_lens, workspace, sp
     _check("rq_decode_stream_probe", lib().rq_decode_stream_probe(
         ctypes.byref(layout), _ptr(pool), int(loop), _ptr(block_table), _ptr(seq_lens), B, mb, _ptr(workspace),
         workspace.numel() * workspace.element_size(), ctypes.byref(o), _stream(stream)))
+
+
+def read_probe(buf, sink, events=None, stream=None):
+    """rq_read_probe: a plain contiguous read of the device tensor `buf` (an
+    HBM-rate reference). sink: a contiguous 32-bit device tensor zeroed by the
+    caller (one word per wave: 32 per compute unit); the XOR of its words
+    becomes the XOR of the buffer's 32-bit words."""
+    _need(buf.is_cuda and buf.is_contiguous(), "buf must be a contiguous device tensor")
+    _need(sink.is_cuda and sink.is_contiguous() and sink.element_size() == 4 and sink.numel() >= 1,
+          "sink must be a contiguous 32-bit device tensor")
+    o = _opts(0, events)
+    _check("rq_read_probe", lib().rq_read_probe(_ptr(buf), _nbytes(buf), _ptr(sink), int(sink.numel()),
+                                                ctypes.byref(o), _stream(stream)))

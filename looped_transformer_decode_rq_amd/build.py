@@ -16,7 +16,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "librq.so")
-SOURCES = ["rq_api.cpp", "rq_encode.hip", "rq_decode.hip", "rq_chunk.hip", "rq_bf16.hip", "rq_fit.cpp", "rq_fit.hip"]
+SOURCES = ["rq_api.cpp", "rq_encode.hip", "rq_decode.hip", "rq_chunk.hip", "rq_bf16.hip", "rq_fit.cpp", "rq_fit.hip",
+           "rq_probe.hip"]
 ARCH = os.environ.get("RQ_OFFLOAD_ARCH", "gfx950")
 
 # Packed-fp32 VALU forms are kept out of the device code on purpose: the

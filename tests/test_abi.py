@@ -310,3 +310,12 @@ def test_chunk_validation(L):
         a[0] = ctypes.byref(bad)
         assert L.rq_chunk_attention(*a) == -3
         assert R.chunk_workspace_bytes(bad, C, B, mb) == 0
+
+
+def test_read_probe_validation(L):
+    f = L.rq_read_probe
+    assert f(_fake(0), 4096, None, 1, None, None) == -1            # no sink
+    assert f(None, 4096, _fake(1), 1, None, None) == -1            # no buffer for a non-empty read
+    assert f(_fake(0), 4100, _fake(1), 1, None, None) == -2        # size not a multiple of 16
+    assert f(c_void_p(0x1008), 4096, _fake(1), 1, None, None) == -2  # buffer not 16-byte aligned
+    assert f(_fake(0), 4096, _fake(1), 0, None, None) == -2        # no sink words
