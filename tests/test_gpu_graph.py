@@ -73,3 +73,50 @@ def test_graph_replay_equals_eager():
         assert T.equal(multi, want_m), f"replay {rep}: multi-loop outputs differ"
         for i in range(layers):
             assert T.equal(pools[i], want_p[i]), f"replay {rep}: pool of layer {i} differs"
+
+
+def test_chunk_graph_replay_equals_eager():
+    """Chunked prefill of every loop (a ragged 37-query chunk: partial query
+    tiles) captured in one graph replays to the eager outputs bit for bit."""
+    import looped_transformer_decode_rq_amd as R
+    T = torch()
+    c = SmallCase(W.get(1).replace(batch=2, heads=3, context=150), shuffled=True, seq_lens=[150, 33])
+    w = c.w
+    L, B, H, D, C = w.loops, w.batch, w.heads, w.head_dim, 37
+    rng = np.random.default_rng(7)
+    shp = (L, B, C, H, D)
+    q = to_dev(W.bf16_round(rng.normal(size=shp) / np.sqrt(D)), "bf16")
+    ck = to_dev(W.bf16_round(rng.normal(size=shp)), "bf16")
+    cv = to_dev(W.bf16_round(rng.normal(size=shp)), "bf16")
+    pool = c.device_pool_from_oracle()
+    ws = T.empty(R.chunk_workspace_bytes(c.lay, C, B, c.table.shape[1]), dtype=T.uint8, device=dev())
+    out = T.empty((L, B, C, H, D), device=dev())
+
+    def step():
+        for l in range(L):
+            R.chunk_attention(c.lay, pool, l, q[l], c.d_rot, c.d_table, c.d_seq, ck[l], cv[l], c.tau, out[l], ws)
+
+    step()
+    T.cuda.synchronize()
+    want = out.clone()
+    assert T.isfinite(want).all()
+    side = T.cuda.Stream()
+    side.wait_stream(T.cuda.current_stream())
+    with T.cuda.stream(side):
+        step()
+    T.cuda.current_stream().wait_stream(side)
+    T.cuda.synchronize()
+    g = T.cuda.CUDAGraph()
+    with T.cuda.graph(g):
+        step()
+    T.cuda.synchronize()
+    scratch = T.empty((B, C, H, D), device=dev())
+    for rep in range(3):
+        out.fill_(float("nan"))
+        # the program's own eager work between replays
+        R.chunk_attention(c.lay, pool, 0, q[1], c.d_rot, c.d_table, c.d_seq, ck[1], cv[1], c.tau, scratch, ws)
+        T.cuda.synchronize()
+        g.replay()
+        T.cuda.synchronize()
+        print(f"[chunk graph] replay {rep}", flush=True)
+        assert T.equal(out, want), f"replay {rep}: chunk outputs differ"
