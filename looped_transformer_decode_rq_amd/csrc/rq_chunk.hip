@@ -859,6 +859,9 @@ __device__ __forceinline__ floatx4 mfma_bf16x32(uint4 a, uint4 b, floatx4 c) {
 //   after each wave has merged its row's split partials and turned its
 //     scores into weights, O += P V_chunk, one 16-channel tile per wave,
 //     with the weights as bf16 hi/lo terms and the V rows as stored.
+// At most 64 registers (eight waves per SIMD), so that two workgroups share a
+// CU and one's loads overlap the other's work: the rotation's R_V operands are
+// therefore loaded in the rotation phase, not held across the merge.
 template <int D>
 __global__ __launch_bounds__(1024, 8) void rq_chunk_combine_kernel(ChunkCombineArgs a) {
     constexpr int QS = D + 1;
